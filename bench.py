@@ -1,0 +1,200 @@
+"""Throughput of the fused Single-Pass mHC step on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+pack the next sublayer's projection (mhc_pack_wmix) and run mhc_fused_step on
+all tokens (hc_post, hc_mixes with its 4x4 Sinkhorn, hc_pre and RMSNorm, in
+one pass over the streams). Inputs are drawn by the seeded generators of
+``stream_hyper_connections_amd.workloads`` and are resident in HBM before the
+timed region starts; the prior coefficients come from the library's own
+mhc_mixes on the same streams.
+
+Prints one JSON line. ``value`` is tokens/s; ``roofline`` reports the fused
+kernel's achieved HBM bandwidth (algorithmic bytes per launch / average
+launch duration, from HIP events on the launch stream) against 8 TB/s;
+``cpu_baseline`` times the float64 oracle on a bounded sample of the same
+workload on the host cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+N = 4
+
+
+def algorithmic_bytes(tokens: int, d: int, elem: int) -> int:
+    """Bytes one fused-step launch must move: read x [T,4,d] and f [T,d], write
+    x_out and y ((2n+2)*d elements per token), read the 24 prior coefficients
+    and write the 24 new ones (float32), plus the float32 parameters once
+    (W [24,4d], base [24], scale [3], gamma [d])."""
+    per_token = (2 * N + 2) * d * elem + 2 * 24 * 4
+    per_call = (24 * N * d + 24 + 3 + d) * 4
+    return tokens * per_token + per_call
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="large_prefill")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
+    return ap.parse_args()
+
+
+def upload_tokens(w, tensor, step, dev, dtype_t):
+    """Draw a token-indexed tensor chunk by chunk straight into device memory."""
+    import torch
+    from stream_hyper_connections_amd import workloads as wl
+    width = N * w.d if tensor == wl.X else w.d
+    out = torch.empty((w.tokens, width), dtype=dtype_t, device=dev)
+    for t0, blk in wl.token_tensor_chunks(w, tensor, step):
+        out[t0:t0 + len(blk)].copy_(wl.to_dtype(blk, w.dtype))
+    return out
+
+
+def cpu_baseline(w, sample_tokens):
+    """The float64 oracle on the first ``sample_tokens`` tokens of the same
+    workload (inputs and prior drawn/computed outside the timed region)."""
+    import oracle
+    from threadpoolctl import threadpool_info
+    from stream_hyper_connections_amd import workloads as wl
+
+    idx = np.arange(min(sample_tokens, w.tokens))
+    x = wl.streams(w, 0, idx).double().numpy()
+    f = wl.sublayer_out(w, 0, idx).double().numpy()
+    prev, cur = wl.params(w, prev=True), wl.params(w)
+    _, pre, post, comb = oracle.mixes(x, prev["w_mix"], prev["base"], prev["scale"], w.iters,
+                                      w.norm_eps, w.hc_eps)
+    pre, post, comb = (a.astype(np.float32) for a in (pre, post, comb))
+    t0 = time.perf_counter()
+    chunk = 1024
+    for c0 in range(0, len(idx), chunk):
+        sl = slice(c0, c0 + chunk)
+        oracle.fused_step(x[sl], f[sl], pre[sl], post[sl], comb[sl], cur["w_mix"], cur["base"],
+                          cur["scale"], cur["gamma"], w.iters, w.norm_eps, w.hc_eps, w.dtype)
+    secs = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": len(idx) / secs, "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"float64 NumPy oracle, full step on the first {len(idx)} tokens of "
+                      f"{w.name} (chunks of {chunk}), {secs:.2f} s, host CPUs {os.cpu_count()}"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the step shards over "
+              "tokens with no communication, so a multi-GPU figure would be N independent "
+              "copies of the one-GPU run.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import stream_hyper_connections_amd as mhc
+    from stream_hyper_connections_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    mhc.load()
+    w = wl.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    elem = 2 if w.dtype == "bf16" else 4
+
+    t_prep = time.time()
+    x = upload_tokens(w, wl.X, 0, dev, dt).view(w.tokens, N, w.d)
+    f = upload_tokens(w, wl.F, 0, dev, dt)
+    prev = {k: torch.as_tensor(v).to(dev) for k, v in wl.params(w, prev=True).items()}
+    cur = {k: torch.as_tensor(v).to(dev) for k, v in wl.params(w).items()}
+    wp_prev = mhc.pack_wmix(prev["w_mix"], w.dtype)
+    prior = mhc.mixes(x, wp_prev, prev["base"], prev["scale"], w.iters, w.norm_eps, w.hc_eps)
+    wp = torch.empty(mhc.wmix_packed_bytes(w.d, w.dtype), dtype=torch.uint8, device=dev)
+    outs = dict(x_out=torch.empty_like(x), y_out=torch.empty_like(f),
+                pre_out=torch.empty_like(prior["pre"]), post_out=torch.empty_like(prior["post"]),
+                comb_out=torch.empty_like(prior["comb"]))
+    torch.cuda.synchronize()
+    print(f"[bench] inputs resident after {time.time() - t_prep:.1f}s: {w.name} T={w.tokens} "
+          f"d={w.d} {w.dtype}", file=sys.stderr, flush=True)
+
+    def step():
+        mhc.pack_wmix(cur["w_mix"], w.dtype, out=wp)
+        e1.record()
+        mhc.fused_step(x, f, prior["pre"], prior["post"], prior["comb"], wp, cur["base"],
+                       cur["scale"], cur["gamma"], w.iters, w.norm_eps, w.hc_eps, **outs)
+
+    e1 = torch.cuda.Event(enable_timing=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    mids = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record()
+        e1 = mids[i]
+        step()
+        ends[i].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    step_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    kern_ms = np.array([m.elapsed_time(e) for m, e in zip(mids, ends)])
+    total_ms = starts[0].elapsed_time(ends[-1])
+    ms_per_step = total_ms / args.steps
+    value = w.tokens / (ms_per_step / 1e3)
+    alg = algorithmic_bytes(w.tokens, w.d, elem)
+    kern_avg_s = kern_ms.mean() / 1e3
+    achieved = alg / kern_avg_s / 1e9
+
+    result = {
+        "metric": "tokens/s and achieved HBM GB/s (% of peak) for fused mHC step, n=4 d=5120",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "tokens": w.tokens, "batch": w.batch,
+                   "seq_len": w.tokens // w.batch, "n_streams": N, "d": w.d,
+                   "sinkhorn_iters": w.iters, "stream_dtype": w.dtype},
+        "step_ms_p50": round(float(np.percentile(step_ms, 50)), 5),
+        "step_ms_p95": round(float(np.percentile(step_ms, 95)), 5),
+        "step_ms_p99": round(float(np.percentile(step_ms, 99)), 5),
+        "fused_kernel_ms_avg": round(float(kern_ms.mean()), 5),
+        "fused_kernel_ms_p50": round(float(np.percentile(kern_ms, 50)), 5),
+        "wall_s": round(wall, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None,
+                     "algorithmic_bytes_per_launch": alg,
+                     "kernel": "step_kernel<bf16, fused, h in registers>"},
+        "device": torch.cuda.get_device_name(0),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_tokens)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

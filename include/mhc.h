@@ -1,0 +1,153 @@
+/*
+ * mhc.h -- C ABI of libmhc, the MI355X (gfx950) implementation of the
+ * Single-Pass mHC residual step with n = 4 residual streams.
+ *
+ * Pages this interface follows (cited by title and section):
+ *   [SW] "DeepSeek V4.1 · Stream weights for the feed-forward": the formula list
+ *        "All 5 steps", the "Why" paragraph (traffic of the fused single pass)
+ *        and the Code excerpts hc_mixes, hc_pre, hc_post and the split/Sinkhorn
+ *        kernel with its wrapper.
+ *   [RN] "DeepSeek V4.1 · MoE RMSNorm": the RMSNorm formula and the Code
+ *        excerpts RMSNorm and Block.forward.
+ *
+ * Conventions shared by every entry point
+ *   - All data pointers are DEVICE pointers, contiguous, row-major, and must be
+ *     16-byte aligned. The caller owns all memory; the library allocates
+ *     nothing and keeps no state between calls.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *     and the call returns without synchronising.
+ *   - `dtype` (an mhc_dtype value) is the dtype of the stream tensors x, f,
+ *     x_out and y_out. Coefficients, mixes and all parameters are float32.
+ *   - Layouts: x [T][4][d]; f [T][d]; pre, post [T][4]; comb [T][4][4] indexed
+ *     [j][k]; mixes [T][24] with slots 0-3 pre, 4-7 post, 8+4j+k comb; w_mix
+ *     float32 [24][4*d] whose column k*d+f multiplies stream k, feature f.
+ *   - Errors: argument problems return MHC_ERR_INVALID_ARG and configurations
+ *     the kernels do not cover return MHC_ERR_UNSUPPORTED, both before any HIP
+ *     call. A failing HIP launch returns MHC_ERR_HIP. mhc_last_error() then
+ *     describes the failure (per calling thread). tokens == 0 returns MHC_OK
+ *     and launches nothing. NaN/Inf in the data propagate; they are not
+ *     detected.
+ *   - Outputs must not overlap each other or any input, except that x_out may
+ *     be exactly x (in-place stream update).
+ */
+#ifndef MHC_H
+#define MHC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MHC_ABI_VERSION 1
+#define MHC_N_STREAMS 4
+#define MHC_N_MIX 24
+
+typedef enum mhc_status {
+  MHC_OK = 0,
+  MHC_ERR_INVALID_ARG = 1,
+  MHC_ERR_UNSUPPORTED = 2,
+  MHC_ERR_HIP = 3
+} mhc_status;
+
+typedef enum mhc_dtype { MHC_F32 = 0, MHC_BF16 = 1 } mhc_dtype;
+
+typedef void* mhc_stream_t;
+
+/* Version of this ABI (MHC_ABI_VERSION). */
+int32_t mhc_abi_version(void);
+
+/* Static name of a status code; "unknown status" for other values. */
+const char* mhc_status_string(int32_t status);
+
+/* Detail of the last non-OK status returned to the calling thread ("" if none).
+ * The string belongs to the library and stays valid until the next call. */
+const char* mhc_last_error(void);
+
+/* d must be a positive multiple of this many features (32). */
+int32_t mhc_d_granule(void);
+
+/* Bytes of the packed projection for width d and stream dtype, or -1 for a bad
+ * d or dtype. */
+int64_t mhc_wmix_packed_bytes(int32_t d, int32_t dtype);
+
+/*
+ * mhc_pack_wmix -- lay the float32 mix projection W [24][4*d] ([SW] Code,
+ * hc_mixes: the weight of F.linear; "All 5 steps": W_mix) out in the operand
+ * order of the gfx950 matrix instructions the step kernels use.
+ *   - MHC_BF16: every weight is split into three bfloat16 terms hi + mid + lo
+ *     whose sum is the float32 weight exactly; the 72 terms per column are
+ *     padded to 80 rows.
+ *   - MHC_F32: float32 copy, rows padded to 32.
+ * The packed buffer depends only on (W, d, dtype): pack once per weight and
+ * reuse it for every call of mhc_fused_step / mhc_mixes with that dtype.
+ * w_packed must hold mhc_wmix_packed_bytes(d, dtype) bytes (packed_bytes is
+ * the caller's buffer size, checked).
+ */
+mhc_status mhc_pack_wmix(const float* w_mix, int32_t d, int32_t dtype, void* w_packed,
+                         int64_t packed_bytes, mhc_stream_t stream);
+
+/*
+ * mhc_fused_step -- one Single-Pass mHC step at the boundary between sublayer
+ * i and sublayer i+1, in one pass over the streams ([SW] "Why": the fused form
+ * moves (2n+2)*d elements per token instead of (4n+4)*d; [RN] Code,
+ * Block.forward: hc_post, then hc_mixes on the new streams, hc_pre with the
+ * read weights of the previous sublayer, then the norm).
+ *
+ * Per token t, with S the stream dtype and every sum in float32:
+ *   x_out[k] = S( sum_j comb_in[j][k] * x[j] + post_in[k] * f )      ([SW] Code, hc_post)
+ *   r        = 1 / sqrt( mean over all 4*d of x_out^2 + norm_eps )
+ *   mix      = r * (W . flatten(x_out))                              ([SW] Code, hc_mixes)
+ *   pre_out, post_out, comb_out = split + Sinkhorn of mix            (as mhc_sinkhorn4)
+ *   h        = S( sum_k pre_in[k] * x_out[k] )                       ([SW] Code, hc_pre)
+ *   y_out    = S( gamma * (h / sqrt(mean(h^2) + norm_eps)) )         ([RN] RMSNorm)
+ *
+ * Inputs:  x [T][4][d] (streams entering sublayer i), f [T][d] (sublayer i
+ *          output), pre_in/post_in/comb_in (coefficients sublayer i computed
+ *          from x), w_packed (mhc_pack_wmix of sublayer i+1's W, same dtype),
+ *          base [24], scale [3] (sublayer i+1), gamma [d] (sublayer i+1's
+ *          RMSNorm gain), sinkhorn_iters >= 1, norm_eps >= 0, hc_eps >= 0.
+ * Outputs: x_out [T][4][d] (may be x), y_out [T][d], pre_out/post_out
+ *          [T][4], comb_out [T][4][4], mix_out [T][24] (optional, NULL to skip).
+ */
+mhc_status mhc_fused_step(const void* x, const void* f, int32_t dtype, int64_t tokens,
+                          int32_t d, const float* pre_in, const float* post_in,
+                          const float* comb_in, const void* w_packed, const float* base,
+                          const float* scale, const float* gamma, int32_t sinkhorn_iters,
+                          float norm_eps, float hc_eps, void* x_out, void* y_out,
+                          float* pre_out, float* post_out, float* comb_out, float* mix_out,
+                          mhc_stream_t stream);
+
+/*
+ * mhc_mixes -- hc_mixes alone ([SW] Code, hc_mixes and "All 5 steps"): one RMS
+ * statistic over the flattened 4*d streams, the 24-wide projection, then the
+ * split and Sinkhorn of mhc_sinkhorn4. Reads x [T][4][d]; writes pre_out,
+ * post_out [T][4], comb_out [T][4][4] and, if not NULL, mix_out [T][24].
+ * w_packed as for mhc_fused_step.
+ */
+mhc_status mhc_mixes(const void* x, int32_t dtype, int64_t tokens, int32_t d,
+                     const void* w_packed, const float* base, const float* scale,
+                     int32_t sinkhorn_iters, float norm_eps, float hc_eps, float* pre_out,
+                     float* post_out, float* comb_out, float* mix_out, mhc_stream_t stream);
+
+/*
+ * mhc_sinkhorn4 -- split float32 mixes [T][24] into the three coefficient sets
+ * ([SW] Code, the split/Sinkhorn kernel; "All 5 steps", the formulas for p,
+ * u and C):
+ *   pre[j]  = sigmoid(scale[0]*m[j] + base[j]) + hc_eps
+ *   post[k] = 2*sigmoid(scale[1]*m[4+k] + base[4+k])
+ *   comb    = row-softmax(scale[2]*m[8+4j+k] + base[8+4j+k]) + hc_eps, divided
+ *             by (column sum + hc_eps); then sinkhorn_iters-1 rounds of
+ *             division by (row sum + hc_eps) and by (column sum + hc_eps).
+ */
+mhc_status mhc_sinkhorn4(const float* mixes, int64_t tokens, const float* base,
+                         const float* scale, int32_t sinkhorn_iters, float hc_eps,
+                         float* pre_out, float* post_out, float* comb_out,
+                         mhc_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MHC_H */

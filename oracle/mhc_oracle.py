@@ -91,7 +91,11 @@ def round_bf16(x) -> np.ndarray:
 
 
 def round_to(x, dtype: str) -> np.ndarray:
-    """Round exact values to the stream dtype (``"bf16"`` or ``"f32"``), RNE."""
+    """Round exact values to the stream dtype (``"bf16"`` or ``"f32"``), RNE.
+    ``"f64"`` returns the values unrounded (for checks that need the exact
+    value before the cast)."""
+    if dtype == "f64":
+        return np.asarray(x, dtype=np.float64)
     if dtype == "bf16":
         return round_bf16(x)
     if dtype == "f32":

@@ -1,0 +1,21 @@
+"""MI355X (gfx950) implementation of the Single-Pass mHC residual step.
+
+The step runs in hand-written HIP kernels behind the C ABI of
+``include/mhc.h`` (``libmhc.so``, built in-tree by
+``stream_hyper_connections_amd.build``); ``binding`` is a thin ctypes layer
+for torch tensors, and ``workloads`` holds the seeded synthetic inputs.
+"""
+
+from .binding import (  # noqa: F401
+    MhcError,
+    abi_version,
+    d_granule,
+    fused_step,
+    last_error,
+    load,
+    mixes,
+    pack_wmix,
+    sinkhorn4,
+    status_string,
+    wmix_packed_bytes,
+)

@@ -1,0 +1,196 @@
+"""Thin ctypes binding of libmhc (include/mhc.h) for torch tensors.
+
+Argument marshalling only: every computation runs in the HIP kernels of
+libmhc.so. Tensors must be CUDA (HIP) tensors, contiguous, with the layouts of
+mhc.h; outputs are allocated with torch when not given. Work is enqueued on
+torch's current stream. There is no CPU fallback: if the library is missing
+the first call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmhc.so")
+
+MHC_OK, MHC_ERR_INVALID_ARG, MHC_ERR_UNSUPPORTED, MHC_ERR_HIP = 0, 1, 2, 3
+MHC_F32, MHC_BF16 = 0, 1
+N_STREAMS, N_MIX = 4, 24
+
+_c_void_p, _i32, _i64, _f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+
+_SIGS = {
+    "mhc_abi_version": ([], _i32),
+    "mhc_status_string": ([_i32], ctypes.c_char_p),
+    "mhc_last_error": ([], ctypes.c_char_p),
+    "mhc_d_granule": ([], _i32),
+    "mhc_wmix_packed_bytes": ([_i32, _i32], _i64),
+    "mhc_pack_wmix": ([_c_void_p, _i32, _i32, _c_void_p, _i64, _c_void_p], _i32),
+    "mhc_fused_step": ([_c_void_p, _c_void_p, _i32, _i64, _i32, _c_void_p, _c_void_p, _c_void_p,
+                        _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _f32, _f32,
+                        _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                        _c_void_p], _i32),
+    "mhc_mixes": ([_c_void_p, _i32, _i64, _i32, _c_void_p, _c_void_p, _c_void_p, _i32, _f32, _f32,
+                   _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p], _i32),
+    "mhc_sinkhorn4": ([_c_void_p, _i64, _c_void_p, _c_void_p, _i32, _f32, _c_void_p, _c_void_p,
+                       _c_void_p, _c_void_p], _i32),
+}
+
+_lib = None
+
+
+class MhcError(RuntimeError):
+    def __init__(self, fn, status, detail):
+        self.status = status
+        super().__init__(f"{fn}: {status_string(status)}: {detail}")
+
+
+def load():
+    """Load libmhc.so (once) and declare the C signatures."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; build it with "
+                               "`python -m stream_hyper_connections_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = lib
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return load().mhc_status_string(status).decode()
+
+
+def last_error() -> str:
+    return load().mhc_last_error().decode()
+
+
+def abi_version() -> int:
+    return load().mhc_abi_version()
+
+
+def d_granule() -> int:
+    return load().mhc_d_granule()
+
+
+def _check(fn, status):
+    if status != MHC_OK:
+        raise MhcError(fn, status, last_error())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return MHC_BF16
+    if t.dtype == torch.float32:
+        return MHC_F32
+    raise TypeError(f"stream tensors must be bfloat16 or float32, got {t.dtype}")
+
+
+def _dtype_name_code(dtype) -> int:
+    if dtype in ("bf16", torch.bfloat16, MHC_BF16):
+        return MHC_BF16
+    if dtype in ("f32", torch.float32, MHC_F32):
+        return MHC_F32
+    raise TypeError(f"unknown stream dtype {dtype!r}")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _f32_out(shape, like, out):
+    if out is not None:
+        return out
+    return torch.empty(shape, dtype=torch.float32, device=like.device)
+
+
+def wmix_packed_bytes(d: int, dtype) -> int:
+    return load().mhc_wmix_packed_bytes(d, _dtype_name_code(dtype))
+
+
+def pack_wmix(w_mix: torch.Tensor, dtype, out: torch.Tensor | None = None) -> torch.Tensor:
+    """mhc_pack_wmix: float32 W [24, 4d] -> packed operand buffer (uint8)."""
+    code = _dtype_name_code(dtype)
+    d = w_mix.shape[1] // N_STREAMS
+    nbytes = load().mhc_wmix_packed_bytes(d, code)
+    if nbytes < 0:
+        raise ValueError(f"width {d} is not a positive multiple of {d_granule()}")
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=w_mix.device)
+    _check("mhc_pack_wmix", load().mhc_pack_wmix(_ptr(w_mix), d, code, _ptr(out),
+                                                 out.numel() * out.element_size(), _stream()))
+    return out
+
+
+def fused_step(x, f, pre_in, post_in, comb_in, w_packed, base, scale, gamma, iters=20,
+               norm_eps=1e-6, hc_eps=1e-6, x_out=None, y_out=None, pre_out=None, post_out=None,
+               comb_out=None, mix_out=None, want_mix=False) -> dict:
+    """mhc_fused_step on tensors. x [T,4,d], f [T,d] (bf16 or f32); coefficients
+    and parameters float32. Returns dict(x_out, y, pre, post, comb, mix)."""
+    t, n, d = x.shape
+    if n != N_STREAMS:
+        raise ValueError("x must be [T, 4, d]")
+    x_out = torch.empty_like(x) if x_out is None else x_out
+    y_out = torch.empty_like(f) if y_out is None else y_out
+    pre_out = _f32_out((t, N_STREAMS), x, pre_out)
+    post_out = _f32_out((t, N_STREAMS), x, post_out)
+    comb_out = _f32_out((t, N_STREAMS, N_STREAMS), x, comb_out)
+    if want_mix and mix_out is None:
+        mix_out = _f32_out((t, N_MIX), x, None)
+    st = load().mhc_fused_step(
+        _ptr(x), _ptr(f), _dtype_code(x), t, d, _ptr(pre_in), _ptr(post_in), _ptr(comb_in),
+        _ptr(w_packed), _ptr(base), _ptr(scale), _ptr(gamma), iters, norm_eps, hc_eps,
+        _ptr(x_out), _ptr(y_out), _ptr(pre_out), _ptr(post_out), _ptr(comb_out), _ptr(mix_out),
+        _stream())
+    _check("mhc_fused_step", st)
+    return {"x_out": x_out, "y": y_out, "pre": pre_out, "post": post_out, "comb": comb_out,
+            "mix": mix_out}
+
+
+def mixes(x, w_packed, base, scale, iters=20, norm_eps=1e-6, hc_eps=1e-6, pre_out=None,
+          post_out=None, comb_out=None, mix_out=None, want_mix=False) -> dict:
+    """mhc_mixes on tensors. Returns dict(pre, post, comb, mix)."""
+    t, n, d = x.shape
+    if n != N_STREAMS:
+        raise ValueError("x must be [T, 4, d]")
+    pre_out = _f32_out((t, N_STREAMS), x, pre_out)
+    post_out = _f32_out((t, N_STREAMS), x, post_out)
+    comb_out = _f32_out((t, N_STREAMS, N_STREAMS), x, comb_out)
+    if want_mix and mix_out is None:
+        mix_out = _f32_out((t, N_MIX), x, None)
+    st = load().mhc_mixes(_ptr(x), _dtype_code(x), t, d, _ptr(w_packed), _ptr(base), _ptr(scale),
+                          iters, norm_eps, hc_eps, _ptr(pre_out), _ptr(post_out), _ptr(comb_out),
+                          _ptr(mix_out), _stream())
+    _check("mhc_mixes", st)
+    return {"pre": pre_out, "post": post_out, "comb": comb_out, "mix": mix_out}
+
+
+def sinkhorn4(mix, base, scale, iters=20, hc_eps=1e-6, pre_out=None, post_out=None,
+              comb_out=None) -> dict:
+    """mhc_sinkhorn4 on tensors: mix [T, 24] float32. Returns dict(pre, post, comb)."""
+    t = mix.shape[0]
+    pre_out = _f32_out((t, N_STREAMS), mix, pre_out)
+    post_out = _f32_out((t, N_STREAMS), mix, post_out)
+    comb_out = _f32_out((t, N_STREAMS, N_STREAMS), mix, comb_out)
+    st = load().mhc_sinkhorn4(_ptr(mix), t, _ptr(base), _ptr(scale), iters, hc_eps,
+                              _ptr(pre_out), _ptr(post_out), _ptr(comb_out), _stream())
+    _check("mhc_sinkhorn4", st)
+    return {"pre": pre_out, "post": post_out, "comb": comb_out}

@@ -1,0 +1,956 @@
+// libmhc: gfx950 (MI355X, CDNA4) kernels and C ABI of the Single-Pass mHC step.
+//
+// Pages followed (by title and section):
+//   [SW] "DeepSeek V4.1 · Stream weights for the feed-forward": "Why" (one fused
+//        pass over the streams, (2n+2)*d traffic), "All 5 steps" and the Code
+//        excerpts hc_mixes / hc_pre / hc_post and the split/Sinkhorn kernel.
+//   [RN] "DeepSeek V4.1 · MoE RMSNorm": RMSNorm formula and Code (RMSNorm,
+//        Block.forward).
+//
+// Design (one pass per token; every HBM byte of the streams is touched once):
+//   * A workgroup owns a tile of 16 tokens and all d features of them. Its 8
+//     waves split the features: wave w takes the 32-feature steps w, w+8, ...
+//     Lane l works on token l%16 and on 8 consecutive features (one 16-byte
+//     bf16 load per stream), so the four lanes of a token read 64 contiguous
+//     bytes per stream and step.
+//   * That lane layout IS the A-operand layout of v_mfma_f32_16x16x32_bf16
+//     (row = token, 8 K values per lane), so the freshly rounded new streams
+//     feed the 24-wide projection without any reshuffle. The projection
+//     weights are pre-split into three exact bf16 terms (mhc_pack_wmix) and
+//     packed in B-operand order; 72 columns (3 x 24) padded to 5 tiles of 16.
+//   * The rounded hc_pre result h (bf16, 8 values per lane and step) stays in
+//     registers until the token's sum of squares is complete, then the
+//     normalised y is written: streams are read once and written once.
+//   * The per-token tail (RMS, split, 4x4 Sinkhorn) runs after one LDS
+//     reduction of the per-wave partials.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "mhc.h"
+
+namespace {
+
+constexpr int kStreams = 4;
+constexpr int kMix = 24;
+constexpr int kTok = 16;              // tokens per workgroup = rows of one MFMA tile
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kStep = 32;             // features per wave step (4 lane groups x 8)
+constexpr int kMaxSpw = 20;           // steps per wave with h held in registers
+constexpr int kTilesBf = 5;           // bf16 path: 80 packed columns (hi/mid/lo x 24 + pad)
+constexpr int kTilesF = 2;            // f32 path: 32 packed columns (24 + pad)
+constexpr int kColsMax = 16 * kTilesBf;
+
+enum Mode { kFused = 0, kMixesOnly = 1 };
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two floats -> two bf16 (round to nearest even), `a` in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+__device__ __forceinline__ float sigmoidf(float z) { return 1.0f / (1.0f + expf(-z)); }
+
+// Split one token's mixes into (pre, post, comb): [SW] Code, the split/Sinkhorn
+// kernel, and "All 5 steps" (p, u, C). The 4x4 lives in registers; the first row
+// normalisation is the max-subtracted softmax, every later division is by
+// (sum + hc_eps); the schedule ends with a column division.
+__device__ void split_sinkhorn_token(const float* m, const float* base, const float* scale,
+                                     int iters, float eps, float* pre, float* post,
+                                     float* comb) {
+  const float s0 = scale[0], s1 = scale[1], s2 = scale[2];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) pre[j] = sigmoidf(m[j] * s0 + base[j]) + eps;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) post[k] = 2.0f * sigmoidf(m[4 + k] * s1 + base[4 + k]);
+  float c[4][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) c[j][k] = m[8 + 4 * j + k] * s2 + base[8 + 4 * j + k];
+    const float mx = fmaxf(fmaxf(c[j][0], c[j][1]), fmaxf(c[j][2], c[j][3]));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) c[j][k] = expf(c[j][k] - mx);
+    const float rs = (c[j][0] + c[j][1]) + (c[j][2] + c[j][3]);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) c[j][k] = c[j][k] / rs + eps;
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float cs = ((c[0][k] + c[1][k]) + (c[2][k] + c[3][k])) + eps;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) c[j][k] = c[j][k] / cs;
+  }
+  for (int it = 1; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float rs = ((c[j][0] + c[j][1]) + (c[j][2] + c[j][3])) + eps;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) c[j][k] = c[j][k] / rs;
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float cs = ((c[0][k] + c[1][k]) + (c[2][k] + c[3][k])) + eps;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) c[j][k] = c[j][k] / cs;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) comb[4 * j + k] = c[j][k];
+}
+
+struct StepArgs {
+  const void* x;
+  const void* f;
+  const float* pre_in;
+  const float* post_in;
+  const float* comb_in;
+  const void* wpk;
+  const float* base;
+  const float* scale;
+  const float* gamma;
+  void* x_out;
+  void* y_out;
+  float* pre_out;
+  float* post_out;
+  float* comb_out;
+  float* mix_out;
+  int64_t tokens;
+  int d;
+  int iters;
+  float norm_eps;
+  float hc_eps;
+};
+
+// Per-lane state carried through a tile.
+template <int kTiles>
+struct LaneState {
+  float C[4][4];   // comb_in of the lane's token, [j][k]
+  float U[4];      // post_in
+  float P[4];      // pre_in
+  f32x4 acc[kTiles];
+  float ss;        // partial sum of squares of the new streams
+  float hs;        // partial sum of squares of h
+};
+
+// ----- bf16 streams ---------------------------------------------------------------------
+
+struct InBf {
+  u32x4 x[4];
+  u32x4 f;
+};
+
+template <int MODE>
+__device__ __forceinline__ void load_bf(InBf& in, const uint16_t* xrow, const uint16_t* frow,
+                                        int d, int f0, bool valid) {
+  if (valid) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) in.x[j] = ld16(xrow + (size_t)j * d + f0);
+    in.f = MODE == kFused ? ld16(frow + f0) : u32x4{0, 0, 0, 0};
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) in.x[j] = u32x4{0, 0, 0, 0};
+    in.f = u32x4{0, 0, 0, 0};
+  }
+}
+
+// One 32-feature step of one wave for 16 tokens: hc_post, the running sums,
+// hc_pre, the store of the new streams and 20 MFMAs of the projection.
+// Returns the packed bf16 h of the lane's 8 features.
+template <int MODE>
+__device__ __forceinline__ u32x4 step_bf(const InBf& in, LaneState<kTilesBf>& st,
+                                         const u32x4* __restrict__ wstep, int lane,
+                                         uint16_t* xorow, int d, int f0, bool valid) {
+  u32x4 xo[4];
+  if (MODE == kFused) {
+    // hc_post ([SW] Code): new stream k = sum_j comb[j][k] * x_j + post[k] * f, fp32,
+    // then rounded to bf16.
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      float a0[4], a1[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        a0[j] = bf_lo(in.x[j][w]);
+        a1[j] = bf_hi(in.x[j][w]);
+      }
+      const float f0v = bf_lo(in.f[w]), f1v = bf_hi(in.f[w]);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        float v0 = a0[0] * st.C[0][k];
+        float v1 = a1[0] * st.C[0][k];
+#pragma unroll
+        for (int j = 1; j < 4; ++j) {
+          v0 = fmaf(a0[j], st.C[j][k], v0);
+          v1 = fmaf(a1[j], st.C[j][k], v1);
+        }
+        v0 = fmaf(f0v, st.U[k], v0);
+        v1 = fmaf(f1v, st.U[k], v1);
+        xo[k][w] = pack_bf16x2(v0, v1);
+      }
+    }
+    if (valid) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) st16(xorow + (size_t)k * d + f0, xo[k]);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) xo[k] = in.x[k];
+  }
+
+  // projection partials: A = new stream k (8 features of the lane's token),
+  // B = packed weight terms for the same features.
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const bf16x8 A = __builtin_bit_cast(bf16x8, xo[k]);
+#pragma unroll
+    for (int q = 0; q < kTilesBf; ++q) {
+      const u32x4 B = wstep[(k * kTilesBf + q) * 64 + lane];
+      st.acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8, B),
+                                                          st.acc[q], 0, 0, 0);
+    }
+  }
+
+  // sums of squares of the rounded new streams, and hc_pre
+  u32x4 hpk = {0, 0, 0, 0};
+  float ssa = 0.f, ssb = 0.f, hsa = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    float r0[4], r1[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      r0[k] = bf_lo(xo[k][w]);
+      r1[k] = bf_hi(xo[k][w]);
+      ssa = fmaf(r0[k], r0[k], ssa);
+      ssb = fmaf(r1[k], r1[k], ssb);
+    }
+    if (MODE == kFused) {
+      float h0 = st.P[0] * r0[0], h1 = st.P[0] * r1[0];
+#pragma unroll
+      for (int k = 1; k < 4; ++k) {
+        h0 = fmaf(st.P[k], r0[k], h0);
+        h1 = fmaf(st.P[k], r1[k], h1);
+      }
+      const uint32_t hp = pack_bf16x2(h0, h1);
+      hpk[w] = hp;
+      const float q0 = bf_lo(hp), q1 = bf_hi(hp);
+      hsa = fmaf(q0, q0, hsa);
+      hsa = fmaf(q1, q1, hsa);
+    }
+  }
+  st.ss += ssa + ssb;
+  st.hs += hsa;
+  return hpk;
+}
+
+// y = bf16(gamma * (h * rh)) for the lane's 8 features ([RN] RMSNorm: the
+// normalised value first, then the gain).
+__device__ __forceinline__ u32x4 norm_bf(u32x4 hpk, const float* gamma, int f0, float rh) {
+  const f32x4 g0 = *reinterpret_cast<const f32x4*>(gamma + f0);
+  const f32x4 g1 = *reinterpret_cast<const f32x4*>(gamma + f0 + 4);
+  const float gv[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
+  u32x4 y;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float a = gv[2 * w] * (bf_lo(hpk[w]) * rh);
+    const float b = gv[2 * w + 1] * (bf_hi(hpk[w]) * rh);
+    y[w] = pack_bf16x2(a, b);
+  }
+  return y;
+}
+
+// ----- f32 streams ----------------------------------------------------------------------
+
+struct InF {
+  u32x4 x[4][2];
+  u32x4 f[2];
+};
+
+template <int MODE>
+__device__ __forceinline__ void load_f(InF& in, const float* xrow, const float* frow, int d,
+                                       int f0, bool valid) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    if (valid) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) in.x[j][h] = ld16(xrow + (size_t)j * d + f0 + 4 * h);
+      in.f[h] = MODE == kFused ? ld16(frow + f0 + 4 * h) : u32x4{0, 0, 0, 0};
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) in.x[j][h] = u32x4{0, 0, 0, 0};
+      in.f[h] = u32x4{0, 0, 0, 0};
+    }
+  }
+}
+
+// f32 variant of step_bf: the projection uses v_mfma_f32_16x16x4_f32 (one K
+// value per lane per instruction, eight instructions per stream and tile) on
+// the float32 weights; h goes to the y buffer as scratch.
+template <int MODE>
+__device__ __forceinline__ void step_f(const InF& in, LaneState<kTilesF>& st,
+                                       const u32x4* __restrict__ wstep, int lane, float* xorow,
+                                       float* hrow, int d, int f0, bool valid) {
+  float xr[4][8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float a[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a[j] = __uint_as_float(in.x[j][e >> 2][e & 3]);
+    if (MODE == kFused) {
+      const float fv = __uint_as_float(in.f[e >> 2][e & 3]);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        float v = a[0] * st.C[0][k];
+#pragma unroll
+        for (int j = 1; j < 4; ++j) v = fmaf(a[j], st.C[j][k], v);
+        xr[k][e] = fmaf(fv, st.U[k], v);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) xr[k][e] = a[k];
+    }
+  }
+  if (MODE == kFused && valid) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        st16(xorow + (size_t)k * d + f0 + 4 * h,
+             u32x4{__float_as_uint(xr[k][4 * h]), __float_as_uint(xr[k][4 * h + 1]),
+                   __float_as_uint(xr[k][4 * h + 2]), __float_as_uint(xr[k][4 * h + 3])});
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+#pragma unroll
+    for (int q = 0; q < kTilesF; ++q) {
+      const u32x4* wp = wstep + ((k * kTilesF + q) * 64 + lane) * 2;
+      const u32x4 b0 = wp[0], b1 = wp[1];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float B = __uint_as_float(e < 4 ? b0[e] : b1[e - 4]);
+        st.acc[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(xr[k][e], B, st.acc[q], 0, 0, 0);
+      }
+    }
+  }
+  float ss = 0.f, hs = 0.f;
+  float hv[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) ss = fmaf(xr[k][e], xr[k][e], ss);
+    if (MODE == kFused) {
+      float h = st.P[0] * xr[0][e];
+#pragma unroll
+      for (int k = 1; k < 4; ++k) h = fmaf(st.P[k], xr[k][e], h);
+      hv[e] = h;
+      hs = fmaf(h, h, hs);
+    }
+  }
+  if (MODE == kFused && valid) {
+    st16(hrow + f0, u32x4{__float_as_uint(hv[0]), __float_as_uint(hv[1]), __float_as_uint(hv[2]),
+                          __float_as_uint(hv[3])});
+    st16(hrow + f0 + 4, u32x4{__float_as_uint(hv[4]), __float_as_uint(hv[5]),
+                              __float_as_uint(hv[6]), __float_as_uint(hv[7])});
+  }
+  st.ss += ss;
+  st.hs += hs;
+}
+
+// ----- the step kernel ------------------------------------------------------------------
+
+template <int DT, int MODE, bool HREG>
+__global__ __launch_bounds__(kThreads) void step_kernel(StepArgs a) {
+  constexpr bool kBf = (DT == MHC_BF16);
+  constexpr int kTiles = kBf ? kTilesBf : kTilesF;
+
+  __shared__ float red_acc[kWaves][kTok][kColsMax];
+  __shared__ float red_ss[kWaves][kTok];
+  __shared__ float red_hs[kWaves][kTok];
+  __shared__ float m_lds[kTok][kMix];
+  __shared__ float rh_lds[kTok];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int tr = lane & 15;
+  const int g = lane >> 4;
+  const int64_t t0 = (int64_t)blockIdx.x * kTok;
+  const int64_t t = t0 + tr;
+  const bool valid = t < a.tokens;
+  const int d = a.d;
+  const int nsteps = d / kStep;
+  const int cnt = wave < nsteps ? (nsteps - wave + kWaves - 1) / kWaves : 0;
+
+  LaneState<kTiles> st;
+#pragma unroll
+  for (int q = 0; q < kTiles; ++q) st.acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.ss = 0.f;
+  st.hs = 0.f;
+  if (MODE == kFused) {
+    if (valid) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 c = *reinterpret_cast<const f32x4*>(a.comb_in + t * 16 + 4 * j);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) st.C[j][k] = c[k];
+      }
+      const f32x4 u = *reinterpret_cast<const f32x4*>(a.post_in + t * 4);
+      const f32x4 p = *reinterpret_cast<const f32x4*>(a.pre_in + t * 4);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        st.U[k] = u[k];
+        st.P[k] = p[k];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) st.C[j][k] = 0.f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) st.U[k] = st.P[k] = 0.f;
+    }
+  }
+
+  const float rh_unused = 0.f;
+  (void)rh_unused;
+
+  if constexpr (kBf) {
+    const uint16_t* xrow = static_cast<const uint16_t*>(a.x) + t * kStreams * (int64_t)d;
+    const uint16_t* frow = static_cast<const uint16_t*>(a.f) + t * (int64_t)d;
+    uint16_t* xorow = static_cast<uint16_t*>(a.x_out) + t * kStreams * (int64_t)d;
+    uint16_t* yrow = static_cast<uint16_t*>(a.y_out) + t * (int64_t)d;
+    const u32x4* wpk = static_cast<const u32x4*>(a.wpk);
+    const size_t wstride = (size_t)kStreams * kTilesBf * 64;   // u32x4 per step
+
+    InBf cur, nxt;
+    if (cnt > 0) load_bf<MODE>(cur, xrow, frow, d, wave * kStep + g * 8, valid);
+    if constexpr (HREG) {
+      u32x4 hb[kMaxSpw];
+#pragma unroll
+      for (int i = 0; i < kMaxSpw; ++i) {
+        if (i < cnt) {
+          const int s = wave + kWaves * i;
+          const int f0 = s * kStep + g * 8;
+          if (i + 1 < cnt) load_bf<MODE>(nxt, xrow, frow, d, f0 + kWaves * kStep, valid);
+          hb[i] = step_bf<MODE>(cur, st, wpk + (size_t)s * wstride, lane, xorow, d, f0, valid);
+          cur = nxt;
+        }
+      }
+      // ---- reduction + tail (shared code below via lambda-free duplication) ----
+      float ss = st.ss, hs = st.hs;
+      ss += __shfl_xor(ss, 16);
+      ss += __shfl_xor(ss, 32);
+      hs += __shfl_xor(hs, 16);
+      hs += __shfl_xor(hs, 32);
+      if (g == 0) {
+        red_ss[wave][tr] = ss;
+        red_hs[wave][tr] = hs;
+      }
+#pragma unroll
+      for (int q = 0; q < kTiles; ++q)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red_acc[wave][4 * g + r][16 * q + tr] = st.acc[q][r];
+      __syncthreads();
+      if (tid < kTok) {
+        float hsum = 0.f;
+        for (int w = 0; w < kWaves; ++w) hsum += red_hs[w][tid];
+        rh_lds[tid] = rsqrtf(hsum / (float)d + a.norm_eps);
+      }
+      __syncthreads();
+      if (MODE == kFused) {
+        const float rh = rh_lds[tr];
+#pragma unroll
+        for (int i = 0; i < kMaxSpw; ++i) {
+          if (i < cnt && valid) {
+            const int f0 = (wave + kWaves * i) * kStep + g * 8;
+            st16(yrow + f0, norm_bf(hb[i], a.gamma, f0, rh));
+          }
+        }
+      }
+    } else {
+      for (int i = 0; i < cnt; ++i) {
+        const int s = wave + kWaves * i;
+        const int f0 = s * kStep + g * 8;
+        if (i + 1 < cnt) load_bf<MODE>(nxt, xrow, frow, d, f0 + kWaves * kStep, valid);
+        const u32x4 h = step_bf<MODE>(cur, st, wpk + (size_t)s * wstride, lane, xorow, d, f0, valid);
+        if (MODE == kFused && valid) st16(yrow + f0, h);   // h parked in y until rh is known
+        cur = nxt;
+      }
+      float ss = st.ss, hs = st.hs;
+      ss += __shfl_xor(ss, 16);
+      ss += __shfl_xor(ss, 32);
+      hs += __shfl_xor(hs, 16);
+      hs += __shfl_xor(hs, 32);
+      if (g == 0) {
+        red_ss[wave][tr] = ss;
+        red_hs[wave][tr] = hs;
+      }
+#pragma unroll
+      for (int q = 0; q < kTiles; ++q)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red_acc[wave][4 * g + r][16 * q + tr] = st.acc[q][r];
+      __syncthreads();
+      if (tid < kTok) {
+        float hsum = 0.f;
+        for (int w = 0; w < kWaves; ++w) hsum += red_hs[w][tid];
+        rh_lds[tid] = rsqrtf(hsum / (float)d + a.norm_eps);
+      }
+      __syncthreads();
+      if (MODE == kFused) {
+        const float rh = rh_lds[tr];
+        for (int i = 0; i < cnt; ++i) {
+          if (valid) {
+            const int f0 = (wave + kWaves * i) * kStep + g * 8;
+            st16(yrow + f0, norm_bf(ld16(yrow + f0), a.gamma, f0, rh));
+          }
+        }
+      }
+    }
+  } else {
+    const float* xrow = static_cast<const float*>(a.x) + t * kStreams * (int64_t)d;
+    const float* frow = static_cast<const float*>(a.f) + t * (int64_t)d;
+    float* xorow = static_cast<float*>(a.x_out) + t * kStreams * (int64_t)d;
+    float* yrow = static_cast<float*>(a.y_out) + t * (int64_t)d;
+    const u32x4* wpk = static_cast<const u32x4*>(a.wpk);
+    const size_t wstride = (size_t)kStreams * kTilesF * 64 * 2;   // u32x4 per step
+
+    InF cur, nxt;
+    if (cnt > 0) load_f<MODE>(cur, xrow, frow, d, wave * kStep + g * 8, valid);
+    for (int i = 0; i < cnt; ++i) {
+      const int s = wave + kWaves * i;
+      const int f0 = s * kStep + g * 8;
+      if (i + 1 < cnt) load_f<MODE>(nxt, xrow, frow, d, f0 + kWaves * kStep, valid);
+      step_f<MODE>(cur, st, wpk + (size_t)s * wstride, lane, xorow, yrow, d, f0, valid);
+      cur = nxt;
+    }
+    float ss = st.ss, hs = st.hs;
+    ss += __shfl_xor(ss, 16);
+    ss += __shfl_xor(ss, 32);
+    hs += __shfl_xor(hs, 16);
+    hs += __shfl_xor(hs, 32);
+    if (g == 0) {
+      red_ss[wave][tr] = ss;
+      red_hs[wave][tr] = hs;
+    }
+#pragma unroll
+    for (int q = 0; q < kTiles; ++q)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red_acc[wave][4 * g + r][16 * q + tr] = st.acc[q][r];
+    __syncthreads();
+    if (tid < kTok) {
+      float hsum = 0.f;
+      for (int w = 0; w < kWaves; ++w) hsum += red_hs[w][tid];
+      rh_lds[tid] = rsqrtf(hsum / (float)d + a.norm_eps);
+    }
+    __syncthreads();
+    if (MODE == kFused) {
+      const float rh = rh_lds[tr];
+      for (int i = 0; i < cnt; ++i) {
+        if (valid) {
+          const int f0 = (wave + kWaves * i) * kStep + g * 8;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const u32x4 hv = ld16(yrow + f0 + 4 * h);
+            const f32x4 gv = *reinterpret_cast<const f32x4*>(a.gamma + f0 + 4 * h);
+            u32x4 y;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[e] = __float_as_uint(gv[e] * (__uint_as_float(hv[e]) * rh));
+            st16(yrow + f0 + 4 * h, y);
+          }
+        }
+      }
+    }
+  }
+
+  // ---- mixes: total over waves, the three weight terms, times the RMS factor ----
+  if (tid < kTok * kMix) {
+    const int tt = tid / kMix;
+    const int j = tid - tt * kMix;
+    float ssum = 0.f;
+    for (int w = 0; w < kWaves; ++w) ssum += red_ss[w][tt];
+    const float r = rsqrtf(ssum / (float)(kStreams * d) + a.norm_eps);
+    float mv;
+    if (kBf) {
+      float hi = 0.f, mid = 0.f, lo = 0.f;
+      for (int w = 0; w < kWaves; ++w) {
+        hi += red_acc[w][tt][j];
+        mid += red_acc[w][tt][kMix + j];
+        lo += red_acc[w][tt][2 * kMix + j];
+      }
+      mv = ((hi + mid) + lo) * r;
+    } else {
+      float s = 0.f;
+      for (int w = 0; w < kWaves; ++w) s += red_acc[w][tt][j];
+      mv = s * r;
+    }
+    m_lds[tt][j] = mv;
+    if (a.mix_out != nullptr && t0 + tt < a.tokens) a.mix_out[(t0 + tt) * kMix + j] = mv;
+  }
+  __syncthreads();
+  if (tid < kTok && t0 + tid < a.tokens) {
+    const int64_t tt = t0 + tid;
+    float pre[4], post[4], comb[16];
+    split_sinkhorn_token(m_lds[tid], a.base, a.scale, a.iters, a.hc_eps, pre, post, comb);
+    *reinterpret_cast<f32x4*>(a.pre_out + tt * 4) = f32x4{pre[0], pre[1], pre[2], pre[3]};
+    *reinterpret_cast<f32x4*>(a.post_out + tt * 4) = f32x4{post[0], post[1], post[2], post[3]};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<f32x4*>(a.comb_out + tt * 16 + 4 * j) =
+          f32x4{comb[4 * j], comb[4 * j + 1], comb[4 * j + 2], comb[4 * j + 3]};
+  }
+}
+
+// ----- split / Sinkhorn on given mixes -------------------------------------------------
+
+__global__ __launch_bounds__(256) void sinkhorn4_kernel(const float* __restrict__ mixes,
+                                                        int64_t tokens, const float* base,
+                                                        const float* scale, int iters,
+                                                        float eps, float* pre_out,
+                                                        float* post_out, float* comb_out) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= tokens) return;
+  float m[kMix];
+#pragma unroll
+  for (int i = 0; i < kMix / 4; ++i) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(mixes + t * kMix + 4 * i);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) m[4 * i + e] = v[e];
+  }
+  float pre[4], post[4], comb[16];
+  split_sinkhorn_token(m, base, scale, iters, eps, pre, post, comb);
+  *reinterpret_cast<f32x4*>(pre_out + t * 4) = f32x4{pre[0], pre[1], pre[2], pre[3]};
+  *reinterpret_cast<f32x4*>(post_out + t * 4) = f32x4{post[0], post[1], post[2], post[3]};
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    *reinterpret_cast<f32x4*>(comb_out + t * 16 + 4 * j) =
+        f32x4{comb[4 * j], comb[4 * j + 1], comb[4 * j + 2], comb[4 * j + 3]};
+}
+
+// ----- packing of the projection --------------------------------------------------------
+
+// bf16: one thread per (step s, stream k, tile q, lane) writes the lane's 8
+// B-operand values: column n = 16q + lane%16 is term n/24 (hi, mid, lo) of
+// projection row n%24; K slots are features 32s + 8(lane/16) + 0..7 of stream k.
+// hi = bf16(w), mid = bf16(w - hi), lo = bf16(w - hi - mid); both differences
+// are exact in float32 and hi + mid + lo == w.
+__global__ __launch_bounds__(256) void pack_bf16_kernel(const float* __restrict__ w, int d,
+                                                        int64_t total, u32x4* __restrict__ out) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= total) return;
+  const int lane = (int)(idx & 63);
+  int64_t r = idx >> 6;
+  const int q = (int)(r % kTilesBf);
+  r /= kTilesBf;
+  const int k = (int)(r % kStreams);
+  const int64_t s = r / kStreams;
+  const int n = 16 * q + (lane & 15);
+  const int g = lane >> 4;
+  const int64_t c0 = (int64_t)k * d + s * kStep + 8 * g;
+  float v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = 0.f;
+  if (n < 3 * kMix) {
+    const int row = n % kMix;
+    const int part = n / kMix;
+    const float* src = w + (int64_t)row * kStreams * d + c0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = src[e];
+      const float hi = __uint_as_float(pack_bf16x2(x, 0.f) << 16);
+      const float r1 = x - hi;
+      const float mid = __uint_as_float(pack_bf16x2(r1, 0.f) << 16);
+      const float r2 = r1 - mid;
+      v[e] = part == 0 ? hi : (part == 1 ? mid : r2);
+    }
+  }
+  out[idx] = u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                   pack_bf16x2(v[6], v[7])};
+}
+
+// f32: one thread per (s, k, q, lane) copies the lane's 8 float32 weights
+// (row n = 16q + lane%16, zero for n >= 24).
+__global__ __launch_bounds__(256) void pack_f32_kernel(const float* __restrict__ w, int d,
+                                                       int64_t total, u32x4* __restrict__ out) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= total) return;
+  const int lane = (int)(idx & 63);
+  int64_t r = idx >> 6;
+  const int q = (int)(r % kTilesF);
+  r /= kTilesF;
+  const int k = (int)(r % kStreams);
+  const int64_t s = r / kStreams;
+  const int n = 16 * q + (lane & 15);
+  const int g = lane >> 4;
+  const int64_t c0 = (int64_t)k * d + s * kStep + 8 * g;
+  u32x4 o0 = {0, 0, 0, 0}, o1 = {0, 0, 0, 0};
+  if (n < kMix) {
+    const float* src = w + (int64_t)n * kStreams * d + c0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      o0[e] = __float_as_uint(src[e]);
+      o1[e] = __float_as_uint(src[4 + e]);
+    }
+  }
+  out[2 * idx] = o0;
+  out[2 * idx + 1] = o1;
+}
+
+// ----- host side ------------------------------------------------------------------------
+
+thread_local char g_last_error[512] = "";
+
+mhc_status fail(mhc_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+mhc_status ok() {
+  g_last_error[0] = '\0';
+  return MHC_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Span {
+  const char* name;
+  const void* p;
+  uint64_t bytes;
+};
+
+bool overlaps(const Span& a, const Span& b) {
+  if (a.p == nullptr || b.p == nullptr || a.bytes == 0 || b.bytes == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+int elem_size(int32_t dtype) { return dtype == MHC_BF16 ? 2 : (dtype == MHC_F32 ? 4 : 0); }
+
+mhc_status check_common(int32_t dtype, int64_t tokens, int32_t d, int32_t iters, float norm_eps,
+                        float hc_eps) {
+  if (dtype != MHC_BF16 && dtype != MHC_F32) return fail(MHC_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (tokens < 0) return fail(MHC_ERR_INVALID_ARG, "tokens must be >= 0 (got %lld)", (long long)tokens);
+  if (d <= 0 || d % kStep != 0)
+    return fail(MHC_ERR_INVALID_ARG, "d must be a positive multiple of %d (got %d)", kStep, d);
+  if (iters < 1) return fail(MHC_ERR_INVALID_ARG, "sinkhorn_iters must be >= 1 (got %d)", iters);
+  if (!(norm_eps >= 0.f) || !isfinite(norm_eps))
+    return fail(MHC_ERR_INVALID_ARG, "norm_eps must be finite and >= 0");
+  if (!(hc_eps >= 0.f) || !isfinite(hc_eps))
+    return fail(MHC_ERR_INVALID_ARG, "hc_eps must be finite and >= 0");
+  // element offsets of the stream tensors are computed in 64 bits; the grid
+  // has one workgroup per 16 tokens
+  if (tokens > ((int64_t)1 << 35))
+    return fail(MHC_ERR_UNSUPPORTED, "tokens beyond 2^35 are not supported");
+  return MHC_OK;
+}
+
+mhc_status check_spans(const Span* in, int nin, const Span* out, int nout, const void* inplace_a,
+                       const void* inplace_b) {
+  for (int i = 0; i < nin; ++i)
+    if (in[i].p == nullptr) return fail(MHC_ERR_INVALID_ARG, "%s is NULL", in[i].name);
+  for (int i = 0; i < nout; ++i)
+    if (out[i].p == nullptr) return fail(MHC_ERR_INVALID_ARG, "%s is NULL", out[i].name);
+  for (int i = 0; i < nin; ++i)
+    if (!aligned16(in[i].p)) return fail(MHC_ERR_INVALID_ARG, "%s is not 16-byte aligned", in[i].name);
+  for (int i = 0; i < nout; ++i)
+    if (!aligned16(out[i].p))
+      return fail(MHC_ERR_INVALID_ARG, "%s is not 16-byte aligned", out[i].name);
+  for (int i = 0; i < nout; ++i) {
+    for (int j = i + 1; j < nout; ++j)
+      if (overlaps(out[i], out[j]))
+        return fail(MHC_ERR_INVALID_ARG, "outputs %s and %s overlap", out[i].name, out[j].name);
+    for (int j = 0; j < nin; ++j) {
+      if (out[i].p == inplace_a && in[j].p == inplace_b && out[i].bytes == in[j].bytes) continue;
+      if (overlaps(out[i], in[j]))
+        return fail(MHC_ERR_INVALID_ARG, "output %s overlaps input %s", out[i].name, in[j].name);
+    }
+  }
+  return MHC_OK;
+}
+
+mhc_status launch_status(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(MHC_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+int64_t packed_bytes(int32_t d, int32_t dtype) {
+  if (d <= 0 || d % kStep != 0) return -1;
+  const int64_t steps = d / kStep;
+  if (dtype == MHC_BF16) return steps * kStreams * kTilesBf * 64 * 16;
+  if (dtype == MHC_F32) return steps * kStreams * kTilesF * 64 * 32;
+  return -1;
+}
+
+typedef void (*StepKernel)(StepArgs);
+
+StepKernel pick_step_kernel(int32_t dtype, int mode, int32_t d) {
+  const int nsteps = d / kStep;
+  const bool hreg = (nsteps + kWaves - 1) / kWaves <= kMaxSpw;
+  if (dtype == MHC_BF16) {
+    if (mode == kMixesOnly) return step_kernel<MHC_BF16, kMixesOnly, false>;
+    return hreg ? step_kernel<MHC_BF16, kFused, true> : step_kernel<MHC_BF16, kFused, false>;
+  }
+  if (mode == kMixesOnly) return step_kernel<MHC_F32, kMixesOnly, false>;
+  return step_kernel<MHC_F32, kFused, false>;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t mhc_abi_version(void) { return MHC_ABI_VERSION; }
+
+const char* mhc_status_string(int32_t status) {
+  switch (status) {
+    case MHC_OK: return "MHC_OK";
+    case MHC_ERR_INVALID_ARG: return "MHC_ERR_INVALID_ARG";
+    case MHC_ERR_UNSUPPORTED: return "MHC_ERR_UNSUPPORTED";
+    case MHC_ERR_HIP: return "MHC_ERR_HIP";
+    default: return "unknown status";
+  }
+}
+
+const char* mhc_last_error(void) { return g_last_error; }
+
+int32_t mhc_d_granule(void) { return kStep; }
+
+int64_t mhc_wmix_packed_bytes(int32_t d, int32_t dtype) { return packed_bytes(d, dtype); }
+
+mhc_status mhc_pack_wmix(const float* w_mix, int32_t d, int32_t dtype, void* w_packed,
+                         int64_t packed_bytes_given, mhc_stream_t stream) {
+  const int64_t need = packed_bytes(d, dtype);
+  if (need < 0) return fail(MHC_ERR_INVALID_ARG, "bad d (%d) or dtype (%d)", d, dtype);
+  if (packed_bytes_given < need)
+    return fail(MHC_ERR_INVALID_ARG, "w_packed holds %lld bytes, %lld needed",
+                (long long)packed_bytes_given, (long long)need);
+  const Span in[] = {{"w_mix", w_mix, (uint64_t)kMix * kStreams * d * 4}};
+  const Span out[] = {{"w_packed", w_packed, (uint64_t)need}};
+  mhc_status s = check_spans(in, 1, out, 1, nullptr, nullptr);
+  if (s != MHC_OK) return s;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t total = (dtype == MHC_BF16 ? need / 16 : need / 32);
+  const unsigned blocks = (unsigned)((total + 255) / 256);
+  if (dtype == MHC_BF16)
+    hipLaunchKernelGGL(pack_bf16_kernel, dim3(blocks), dim3(256), 0, st, w_mix, d, total,
+                       static_cast<u32x4*>(w_packed));
+  else
+    hipLaunchKernelGGL(pack_f32_kernel, dim3(blocks), dim3(256), 0, st, w_mix, d, total,
+                       static_cast<u32x4*>(w_packed));
+  return launch_status("pack kernel launch");
+}
+
+mhc_status mhc_fused_step(const void* x, const void* f, int32_t dtype, int64_t tokens, int32_t d,
+                          const float* pre_in, const float* post_in, const float* comb_in,
+                          const void* w_packed, const float* base, const float* scale,
+                          const float* gamma, int32_t sinkhorn_iters, float norm_eps,
+                          float hc_eps, void* x_out, void* y_out, float* pre_out,
+                          float* post_out, float* comb_out, float* mix_out,
+                          mhc_stream_t stream) {
+  mhc_status s = check_common(dtype, tokens, d, sinkhorn_iters, norm_eps, hc_eps);
+  if (s != MHC_OK) return s;
+  const uint64_t es = elem_size(dtype), T = (uint64_t)tokens;
+  const Span in[] = {
+      {"x", x, T * kStreams * d * es},     {"f", f, T * d * es},
+      {"pre_in", pre_in, T * 16},          {"post_in", post_in, T * 16},
+      {"comb_in", comb_in, T * 64},        {"w_packed", w_packed, (uint64_t)packed_bytes(d, dtype)},
+      {"base", base, kMix * 4},            {"scale", scale, 12},
+      {"gamma", gamma, (uint64_t)d * 4},
+  };
+  const Span out[] = {
+      {"x_out", x_out, T * kStreams * d * es}, {"y_out", y_out, T * d * es},
+      {"pre_out", pre_out, T * 16},            {"post_out", post_out, T * 16},
+      {"comb_out", comb_out, T * 64},
+  };
+  s = check_spans(in, 9, out, 5, x_out, x);
+  if (s != MHC_OK) return s;
+  if (mix_out != nullptr) {
+    const Span mo[] = {{"mix_out", mix_out, T * kMix * 4}};
+    Span all[14];
+    for (int i = 0; i < 9; ++i) all[i] = in[i];
+    for (int i = 0; i < 5; ++i) all[9 + i] = out[i];
+    s = check_spans(all, 14, mo, 1, nullptr, nullptr);
+    if (s != MHC_OK) return s;
+  }
+  if (tokens == 0) return ok();
+  StepArgs a{x, f, pre_in, post_in, comb_in, w_packed, base, scale, gamma, x_out, y_out,
+             pre_out, post_out, comb_out, mix_out, tokens, d, sinkhorn_iters, norm_eps, hc_eps};
+  const unsigned blocks = (unsigned)((tokens + kTok - 1) / kTok);
+  hipLaunchKernelGGL(pick_step_kernel(dtype, kFused, d), dim3(blocks), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), a);
+  return launch_status("fused step kernel launch");
+}
+
+mhc_status mhc_mixes(const void* x, int32_t dtype, int64_t tokens, int32_t d,
+                     const void* w_packed, const float* base, const float* scale,
+                     int32_t sinkhorn_iters, float norm_eps, float hc_eps, float* pre_out,
+                     float* post_out, float* comb_out, float* mix_out, mhc_stream_t stream) {
+  mhc_status s = check_common(dtype, tokens, d, sinkhorn_iters, norm_eps, hc_eps);
+  if (s != MHC_OK) return s;
+  const uint64_t es = elem_size(dtype), T = (uint64_t)tokens;
+  const Span in[] = {
+      {"x", x, T * kStreams * d * es},
+      {"w_packed", w_packed, (uint64_t)packed_bytes(d, dtype)},
+      {"base", base, kMix * 4},
+      {"scale", scale, 12},
+  };
+  const Span out[] = {
+      {"pre_out", pre_out, T * 16}, {"post_out", post_out, T * 16},
+      {"comb_out", comb_out, T * 64}, {"mix_out", mix_out, T * kMix * 4},
+  };
+  s = check_spans(in, 4, out, mix_out ? 4 : 3, nullptr, nullptr);
+  if (s != MHC_OK) return s;
+  if (tokens == 0) return ok();
+  StepArgs a{x, nullptr, nullptr, nullptr, nullptr, w_packed, base, scale, nullptr, nullptr,
+             nullptr, pre_out, post_out, comb_out, mix_out, tokens, d, sinkhorn_iters, norm_eps,
+             hc_eps};
+  const unsigned blocks = (unsigned)((tokens + kTok - 1) / kTok);
+  hipLaunchKernelGGL(pick_step_kernel(dtype, kMixesOnly, d), dim3(blocks), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), a);
+  return launch_status("mixes kernel launch");
+}
+
+mhc_status mhc_sinkhorn4(const float* mixes, int64_t tokens, const float* base,
+                         const float* scale, int32_t sinkhorn_iters, float hc_eps,
+                         float* pre_out, float* post_out, float* comb_out,
+                         mhc_stream_t stream) {
+  if (tokens < 0) return fail(MHC_ERR_INVALID_ARG, "tokens must be >= 0");
+  if (sinkhorn_iters < 1) return fail(MHC_ERR_INVALID_ARG, "sinkhorn_iters must be >= 1");
+  if (!(hc_eps >= 0.f) || !isfinite(hc_eps))
+    return fail(MHC_ERR_INVALID_ARG, "hc_eps must be finite and >= 0");
+  if (tokens > ((int64_t)1 << 35)) return fail(MHC_ERR_UNSUPPORTED, "too many tokens");
+  const uint64_t T = (uint64_t)tokens;
+  const Span in[] = {{"mixes", mixes, T * kMix * 4}, {"base", base, kMix * 4}, {"scale", scale, 12}};
+  const Span out[] = {{"pre_out", pre_out, T * 16}, {"post_out", post_out, T * 16},
+                      {"comb_out", comb_out, T * 64}};
+  mhc_status s = check_spans(in, 3, out, 3, nullptr, nullptr);
+  if (s != MHC_OK) return s;
+  if (tokens == 0) return ok();
+  const unsigned blocks = (unsigned)((tokens + 255) / 256);
+  hipLaunchKernelGGL(sinkhorn4_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     mixes, tokens, base, scale, sinkhorn_iters, hc_eps, pre_out, post_out,
+                     comb_out);
+  return launch_status("sinkhorn4 kernel launch");
+}
+
+}  // extern "C"

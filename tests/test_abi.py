@@ -1,0 +1,160 @@
+"""CPU-side checks of the C ABI: the library loads, exports every function that
+include/mhc.h declares, and rejects bad arguments before any HIP call (fake,
+never dereferenced device addresses are used; nothing is launched)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from stream_hyper_connections_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mhc.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(binding.LIB_PATH),
+                                reason="libmhc.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mhc_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for fn in ("mhc_fused_step", "mhc_mixes", "mhc_sinkhorn4", "mhc_pack_wmix",
+               "mhc_wmix_packed_bytes", "mhc_status_string", "mhc_last_error",
+               "mhc_abi_version", "mhc_d_granule"):
+        assert fn in names
+
+
+def test_library_exports_every_declared_function():
+    lib = ctypes.CDLL(binding.LIB_PATH)
+    for fn in declared_functions():
+        assert hasattr(lib, fn), fn
+    assert set(declared_functions()) == set(binding._SIGS)
+
+
+def test_version_granule_and_status_strings():
+    assert binding.abi_version() == 1
+    assert binding.d_granule() == 32
+    lib = binding.load()
+    assert lib.mhc_status_string(0) == b"MHC_OK"
+    assert lib.mhc_status_string(1) == b"MHC_ERR_INVALID_ARG"
+    assert lib.mhc_status_string(2) == b"MHC_ERR_UNSUPPORTED"
+    assert lib.mhc_status_string(3) == b"MHC_ERR_HIP"
+    assert lib.mhc_status_string(99) == b"unknown status"
+
+
+def test_packed_bytes():
+    lib = binding.load()
+    assert lib.mhc_wmix_packed_bytes(5120, binding.MHC_BF16) == 160 * 4 * 5 * 64 * 16
+    assert lib.mhc_wmix_packed_bytes(5120, binding.MHC_F32) == 160 * 4 * 2 * 64 * 32
+    assert lib.mhc_wmix_packed_bytes(100, binding.MHC_BF16) == -1
+    assert lib.mhc_wmix_packed_bytes(0, binding.MHC_BF16) == -1
+    assert lib.mhc_wmix_packed_bytes(64, 7) == -1
+
+
+# ---- validation of mhc_fused_step with fake addresses ----------------------------------
+
+T, D = 64, 256
+ES = 2
+A = 1 << 40          # fake, aligned, never dereferenced
+
+
+def _layout():
+    """Non-overlapping fake buffers for every argument."""
+    sizes = {
+        "x": T * 4 * D * ES, "f": T * D * ES, "pre_in": T * 16, "post_in": T * 16,
+        "comb_in": T * 64, "w_packed": (D // 32) * 4 * 5 * 64 * 16, "base": 96, "scale": 12,
+        "gamma": D * 4, "x_out": T * 4 * D * ES, "y_out": T * D * ES, "pre_out": T * 16,
+        "post_out": T * 16, "comb_out": T * 64, "mix_out": T * 96,
+    }
+    addr, p = A, {}
+    for k, n in sizes.items():
+        p[k] = addr
+        addr += (n + 4095) // 4096 * 4096
+    return p
+
+
+def _call(**over):
+    p = _layout()
+    args = dict(x=p["x"], f=p["f"], dtype=binding.MHC_BF16, tokens=T, d=D, pre_in=p["pre_in"],
+                post_in=p["post_in"], comb_in=p["comb_in"], w_packed=p["w_packed"],
+                base=p["base"], scale=p["scale"], gamma=p["gamma"], iters=20, norm_eps=1e-6,
+                hc_eps=1e-6, x_out=p["x_out"], y_out=p["y_out"], pre_out=p["pre_out"],
+                post_out=p["post_out"], comb_out=p["comb_out"], mix_out=p["mix_out"],
+                stream=None)
+    args.update(over)
+    lib = binding.load()
+    return lib.mhc_fused_step(*args.values())
+
+
+@pytest.mark.parametrize("over,needle", [
+    (dict(dtype=5), "dtype"),
+    (dict(tokens=-1), "tokens"),
+    (dict(d=0), "multiple"),
+    (dict(d=48), "multiple"),
+    (dict(iters=0), "sinkhorn_iters"),
+    (dict(norm_eps=-1.0), "norm_eps"),
+    (dict(norm_eps=float("nan")), "norm_eps"),
+    (dict(hc_eps=float("inf")), "hc_eps"),
+    (dict(x=None), "x is NULL"),
+    (dict(gamma=None), "gamma is NULL"),
+    (dict(comb_out=None), "comb_out is NULL"),
+    (dict(f=A + 8), "not 16-byte aligned"),
+    (dict(y_out=_layout()["x_out"] + 64), "overlap"),
+    (dict(x_out=_layout()["x"] + 16), "overlaps input"),
+    (dict(pre_out=_layout()["pre_in"]), "overlaps input"),
+    (dict(mix_out=_layout()["comb_out"]), "overlap"),
+])
+def test_fused_step_rejects_bad_arguments(over, needle):
+    st = _call(**over)
+    assert st == binding.MHC_ERR_INVALID_ARG
+    assert needle in binding.last_error()
+
+
+def test_fused_step_zero_tokens_is_a_no_op():
+    assert _call(tokens=0) == binding.MHC_OK
+    assert binding.last_error() == ""
+
+
+def test_fused_step_in_place_streams_pass_validation_with_zero_tokens():
+    p = _layout()
+    assert _call(tokens=0, x_out=p["x"]) == binding.MHC_OK
+
+
+def test_mixes_and_sinkhorn_validation():
+    lib = binding.load()
+    p = _layout()
+    st = lib.mhc_mixes(p["x"], binding.MHC_BF16, T, D, p["w_packed"], p["base"], p["scale"], 0,
+                       1e-6, 1e-6, p["pre_out"], p["post_out"], p["comb_out"], None, None)
+    assert st == binding.MHC_ERR_INVALID_ARG
+    st = lib.mhc_mixes(p["x"], binding.MHC_BF16, 0, D, p["w_packed"], p["base"], p["scale"], 20,
+                       1e-6, 1e-6, p["pre_out"], p["post_out"], p["comb_out"], None, None)
+    assert st == binding.MHC_OK
+    st = lib.mhc_sinkhorn4(p["mix_out"], T, p["base"], p["scale"], 20, -1.0, p["pre_out"],
+                           p["post_out"], p["comb_out"], None)
+    assert st == binding.MHC_ERR_INVALID_ARG
+    st = lib.mhc_sinkhorn4(p["mix_out"], T, p["base"], p["scale"], 20, 1e-6, p["pre_out"],
+                           p["pre_out"], p["comb_out"], None)
+    assert st == binding.MHC_ERR_INVALID_ARG and "overlap" in binding.last_error()
+    st = lib.mhc_sinkhorn4(p["mix_out"], 0, p["base"], p["scale"], 20, 1e-6, p["pre_out"],
+                           p["post_out"], p["comb_out"], None)
+    assert st == binding.MHC_OK
+
+
+def test_pack_validation():
+    lib = binding.load()
+    p = _layout()
+    need = lib.mhc_wmix_packed_bytes(D, binding.MHC_BF16)
+    assert lib.mhc_pack_wmix(p["x"], D, binding.MHC_BF16, p["w_packed"], need - 16,
+                             None) == binding.MHC_ERR_INVALID_ARG
+    assert "bytes" in binding.last_error()
+    assert lib.mhc_pack_wmix(p["x"], 40, binding.MHC_BF16, p["w_packed"], need,
+                             None) == binding.MHC_ERR_INVALID_ARG
+    assert lib.mhc_pack_wmix(None, D, binding.MHC_BF16, p["w_packed"], need,
+                             None) == binding.MHC_ERR_INVALID_ARG
