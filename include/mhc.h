@@ -25,7 +25,8 @@
  *     the kernels do not cover return MHC_ERR_UNSUPPORTED, both before any HIP
  *     call. A failing HIP launch returns MHC_ERR_HIP. mhc_last_error() then
  *     describes the failure (per calling thread). tokens == 0 returns MHC_OK
- *     and launches nothing. NaN/Inf in the data propagate; they are not
+ *     after the scalar checks, without examining pointers and without
+ *     launching anything. NaN/Inf in the data propagate; they are not
  *     detected.
  *   - Outputs must not overlap each other or any input, except that x_out may
  *     be exactly x (in-place stream update).

@@ -869,6 +869,7 @@ mhc_status mhc_fused_step(const void* x, const void* f, int32_t dtype, int64_t t
                           mhc_stream_t stream) {
   mhc_status s = check_common(dtype, tokens, d, sinkhorn_iters, norm_eps, hc_eps);
   if (s != MHC_OK) return s;
+  if (tokens == 0) return ok();
   const uint64_t es = elem_size(dtype), T = (uint64_t)tokens;
   const Span in[] = {
       {"x", x, T * kStreams * d * es},     {"f", f, T * d * es},
@@ -892,7 +893,6 @@ mhc_status mhc_fused_step(const void* x, const void* f, int32_t dtype, int64_t t
     s = check_spans(all, 14, mo, 1, nullptr, nullptr);
     if (s != MHC_OK) return s;
   }
-  if (tokens == 0) return ok();
   StepArgs a{x, f, pre_in, post_in, comb_in, w_packed, base, scale, gamma, x_out, y_out,
              pre_out, post_out, comb_out, mix_out, tokens, d, sinkhorn_iters, norm_eps, hc_eps};
   const unsigned blocks = (unsigned)((tokens + kTok - 1) / kTok);
@@ -907,6 +907,7 @@ mhc_status mhc_mixes(const void* x, int32_t dtype, int64_t tokens, int32_t d,
                      float* post_out, float* comb_out, float* mix_out, mhc_stream_t stream) {
   mhc_status s = check_common(dtype, tokens, d, sinkhorn_iters, norm_eps, hc_eps);
   if (s != MHC_OK) return s;
+  if (tokens == 0) return ok();
   const uint64_t es = elem_size(dtype), T = (uint64_t)tokens;
   const Span in[] = {
       {"x", x, T * kStreams * d * es},
@@ -920,7 +921,6 @@ mhc_status mhc_mixes(const void* x, int32_t dtype, int64_t tokens, int32_t d,
   };
   s = check_spans(in, 4, out, mix_out ? 4 : 3, nullptr, nullptr);
   if (s != MHC_OK) return s;
-  if (tokens == 0) return ok();
   StepArgs a{x, nullptr, nullptr, nullptr, nullptr, w_packed, base, scale, nullptr, nullptr,
              nullptr, pre_out, post_out, comb_out, mix_out, tokens, d, sinkhorn_iters, norm_eps,
              hc_eps};
@@ -939,13 +939,13 @@ mhc_status mhc_sinkhorn4(const float* mixes, int64_t tokens, const float* base,
   if (!(hc_eps >= 0.f) || !isfinite(hc_eps))
     return fail(MHC_ERR_INVALID_ARG, "hc_eps must be finite and >= 0");
   if (tokens > ((int64_t)1 << 35)) return fail(MHC_ERR_UNSUPPORTED, "too many tokens");
+  if (tokens == 0) return ok();
   const uint64_t T = (uint64_t)tokens;
   const Span in[] = {{"mixes", mixes, T * kMix * 4}, {"base", base, kMix * 4}, {"scale", scale, 12}};
   const Span out[] = {{"pre_out", pre_out, T * 16}, {"post_out", post_out, T * 16},
                       {"comb_out", comb_out, T * 64}};
   mhc_status s = check_spans(in, 3, out, 3, nullptr, nullptr);
   if (s != MHC_OK) return s;
-  if (tokens == 0) return ok();
   const unsigned blocks = (unsigned)((tokens + 255) / 256);
   hipLaunchKernelGGL(sinkhorn4_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
                      mixes, tokens, base, scale, sinkhorn_iters, hc_eps, pre_out, post_out,

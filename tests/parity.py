@@ -4,20 +4,22 @@ Tolerances (the parity bar of this implementation):
 
 * mixes m, pre, post and every comb entry (float32): |g - o| <= 1e-4 * max(|o|, 1).
 * comb row and column sums: within 1e-5 of the oracle's same sums, and every
-  column sum within 1e-5 of 1 (the schedule ends with a column division).
+  column sum within 1e-5 + hc_eps of 1 (the schedule ends with a column
+  division, which leaves each column short of 1 by eps/(s + eps)).
 * bf16 stream outputs (new streams, y): |g - o| <= ulp_bf16(o) + 1e-3; the new
   streams are held to the stricter rule below.
 * f32 stream outputs: |g - o| <= 1e-5 * max(|o|, 1).
 
 Roundings with more than one correct result. The kernels (like the code on
 the pages) evaluate the new streams and h in float32 and then round to bf16.
-Where the exact value lies within the float32 evaluation error of a bf16
-rounding boundary, both neighbouring bf16 values are correct. For such an
-element the check accepts either neighbour; everywhere else it demands the
-oracle's rounding bit for bit. The stages after the rounding are then
-evaluated by the oracle on the oracle's own candidate value that matches the
-choice made on the GPU (never on a value taken from the GPU), so that a
-correct tie choice is not reported as a mixes error.
+Every bf16 value between the roundings of (exact - b) and (exact + b), with b
+the float32 evaluation error bound of that element, is a correct result; near
+a rounding boundary that is two neighbours, under cancellation it can be a
+few. The check demands that every element lies in its oracle-computed
+interval (a single value almost everywhere). Because the later stages depend
+on which correct rounding was taken, they are compared against the oracle
+evaluated on the new streams as validated (each element inside its
+interval), so that a correct tie choice is not reported as a mixes error.
 """
 
 from __future__ import annotations
@@ -69,7 +71,10 @@ def check_mix_like(what, got, want):
         _fail(what, bad, got, want)
 
 
-def check_comb(got, want):
+def check_comb(got, want, hc_eps=1e-6):
+    """Entries, row and column sums against the oracle's; column sums against
+    1 within the tolerance plus the shortfall eps/(s + eps) the final column
+    division leaves."""
     got, want = _np(got), _np(want)
     check_mix_like("comb", got, want)
     for axis, name in ((1, "column"), (2, "row")):
@@ -78,7 +83,7 @@ def check_comb(got, want):
         if bad.any():
             _fail(f"comb {name} sums", bad, gs, ws)
     cs = got.sum(axis=1)
-    bad = ~(np.abs(cs - 1.0) <= SUM_TOL)
+    bad = ~(np.abs(cs - 1.0) <= SUM_TOL + hc_eps)
     if bad.any():
         _fail("comb column sums vs 1", bad, cs, np.ones_like(cs))
 
@@ -94,15 +99,16 @@ def check_stream(what, got, want, dtype):
 
 
 def resolve_rounding(got, exact, bound, dtype, what):
-    """Check bf16 ``got`` against the roundings of ``exact`` +- ``bound`` and
-    return the oracle candidate equal to it (raises if it is neither)."""
+    """Check that every element of ``got`` is a rounding (to ``dtype``) of some
+    value within ``exact`` +- ``bound``; return it as validated, with the count
+    of elements whose interval holds more than one value."""
     lo = oracle.round_to(exact - bound, dtype)
     hi = oracle.round_to(exact + bound, dtype)
     nearest = oracle.round_to(exact, dtype)
-    ok = (got == lo) | (got == hi)
+    ok = (got >= lo) & (got <= hi) & (got == oracle.round_to(got, dtype))
     if not ok.all():
         _fail(what, ~ok, got, nearest, "(not a correct rounding of the exact value)")
-    return np.where(got == hi, hi, lo), int((lo != hi).sum())
+    return np.where(ok, got, nearest), int((lo != hi).sum())
 
 
 def check_mixes(inputs, gpu, dtype):
@@ -115,7 +121,7 @@ def check_mixes(inputs, gpu, dtype):
         check_mix_like("mix", gpu["mix"], m)
     check_mix_like("pre", gpu["pre"], pre)
     check_mix_like("post", gpu["post"], post)
-    check_comb(gpu["comb"], comb)
+    check_comb(gpu["comb"], comb, inputs.get("hc_eps", 1e-6))
     return {"m": m, "pre": pre, "post": post, "comb": comb}
 
 
@@ -157,7 +163,7 @@ def check_step(inputs, gpu, dtype, coef_abs=0.0):
         check_mix_like("mix", gpu["mix"], o["m"])
     check_mix_like("pre", gpu["pre"], o["pre"])
     check_mix_like("post", gpu["post"], o["post"])
-    check_comb(gpu["comb"], o["comb"])
+    check_comb(gpu["comb"], o["comb"], hc_eps)
 
     gy = _np(gpu["y"])
     if dtype == "bf16":
@@ -168,9 +174,8 @@ def check_step(inputs, gpu, dtype, coef_abs=0.0):
         h_hi = oracle.round_to(h_exact + h_band, dtype)
         y_lo = oracle.rmsnorm(h_lo, inputs["gamma"], norm_eps, dtype)
         y_hi = oracle.rmsnorm(h_hi, inputs["gamma"], norm_eps, dtype)
-        tol_lo = ulp_bf16(y_lo) + BF16_ABS
-        tol_hi = ulp_bf16(y_hi) + BF16_ABS
-        ok = (np.abs(gy - y_lo) <= tol_lo) | (np.abs(gy - y_hi) <= tol_hi)
+        tol = np.maximum(ulp_bf16(y_lo), ulp_bf16(y_hi)) + BF16_ABS
+        ok = (gy >= np.minimum(y_lo, y_hi) - tol) & (gy <= np.maximum(y_lo, y_hi) + tol)
         if not ok.all():
             _fail("y", ~ok, gy, o["y"])
     else:

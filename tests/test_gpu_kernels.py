@@ -37,7 +37,7 @@ def test_sinkhorn4_random(t, iters, eps):
     check_mix_like("pre", out["pre"].cpu(), pre)
     check_mix_like("post", out["post"].cpu(), post)
     if iters >= 5:
-        check_comb(out["comb"].cpu(), comb)
+        check_comb(out["comb"].cpu(), comb, eps)
     else:
         check_mix_like("comb", out["comb"].cpu(), comb)
 
