@@ -51,7 +51,30 @@ def parse():
     ap.add_argument("--workload", default="large_prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="time a plain device-to-device copy of 2 GiB instead (the reference "
+                         "kernel for scaling the HBM byte counters)")
     return ap.parse_args()
+
+
+def copy_calibration(steps):
+    """A plain copy of known size: 2 GiB read + 2 GiB written per launch."""
+    import torch
+    n = 1 << 31
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms_per_copy": round(ms, 4),
+                      "GBps_read_plus_write": round(2 * n / ms / 1e6, 1)}), flush=True)
 
 
 def upload_tokens(w, tensor, step, dev, dtype_t):
@@ -108,6 +131,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration(args.steps)
+        return
     mhc.load()
     w = wl.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")

@@ -31,6 +31,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "mhc.h"
 
 namespace {
@@ -49,22 +51,56 @@ constexpr int kColsMax = 16 * kTilesBf;
 enum Mode { kFused = 0, kMixesOnly = 1 };
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 // Two floats -> two bf16 (round to nearest even), `a` in the low half.
+// float -> bf16 bits, round to nearest even, placed in the HIGH half of the
+// returned word (low half is garbage); every NaN becomes the quiet NaN 0x7fc0.
+// Integer arithmetic on purpose: the hardware packed conversion instruction
+// returned wrong halves for some lanes now and then inside the pipelined
+// kernel, which this form avoids.
+__device__ __forceinline__ uint32_t rne_bf16_hi(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t r = u + 0x7fffu + ((u >> 16) & 1u);
+  return x != x ? 0x7fc00000u : r;
+}
+
+// Two floats -> two bf16 (round to nearest even), `a` in the low half.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  f32x2 v = {a, b};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+  return __builtin_amdgcn_perm(rne_bf16_hi(b), rne_bf16_hi(a), 0x07060302u);
 }
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+#ifndef MHC_STREAM_NT
+#define MHC_STREAM_NT 0
+#endif
+#ifndef MHC_SKIP_PAD
+#define MHC_SKIP_PAD 0
+#endif
+#ifndef MHC_FORCE_HMEM
+#define MHC_FORCE_HMEM 0
+#endif
+#ifndef MHC_HWRITE
+#define MHC_HWRITE 0   // 0: h to LDS before the MFMAs, 1: after them, 2: as two 8-byte writes
+#endif
+
+
+// Stream tensors are touched once: optionally load/store them non-temporally so
+// they do not push the packed projection out of L2.
+__device__ __forceinline__ u32x4 lds16(const void* p) {
+  if (MHC_STREAM_NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return ld16(p);
+}
+__device__ __forceinline__ void sts16(void* p, u32x4 v) {
+  if (MHC_STREAM_NT) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+  else st16(p, v);
+}
 
 __device__ __forceinline__ float sigmoidf(float z) { return 1.0f / (1.0f + expf(-z)); }
 
@@ -164,8 +200,8 @@ __device__ __forceinline__ void load_bf(InBf& in, const uint16_t* xrow, const ui
                                         int d, int f0, bool valid) {
   if (valid) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) in.x[j] = ld16(xrow + (size_t)j * d + f0);
-    in.f = MODE == kFused ? ld16(frow + f0) : u32x4{0, 0, 0, 0};
+    for (int j = 0; j < 4; ++j) in.x[j] = lds16(xrow + (size_t)j * d + f0);
+    in.f = MODE == kFused ? lds16(frow + f0) : u32x4{0, 0, 0, 0};
   } else {
 #pragma unroll
     for (int j = 0; j < 4; ++j) in.x[j] = u32x4{0, 0, 0, 0};
@@ -209,7 +245,7 @@ __device__ __forceinline__ u32x4 step_bf(const InBf& in, LaneState<kTilesBf>& st
     }
     if (valid) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) st16(xorow + (size_t)k * d + f0, xo[k]);
+      for (int k = 0; k < 4; ++k) sts16(xorow + (size_t)k * d + f0, xo[k]);
     }
   } else {
 #pragma unroll
@@ -223,7 +259,9 @@ __device__ __forceinline__ u32x4 step_bf(const InBf& in, LaneState<kTilesBf>& st
     const bf16x8 A = __builtin_bit_cast(bf16x8, xo[k]);
 #pragma unroll
     for (int q = 0; q < kTilesBf; ++q) {
-      const u32x4 B = wstep[(k * kTilesBf + q) * 64 + lane];
+      // the last tile holds columns 64..79 of which 72..79 are padding
+      const bool pad = MHC_SKIP_PAD && q == kTilesBf - 1 && (lane & 15) >= 3 * kMix - 64;
+      const u32x4 B = pad ? u32x4{0, 0, 0, 0} : wstep[(k * kTilesBf + q) * 64 + lane];
       st.acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8, B),
                                                           st.acc[q], 0, 0, 0);
     }
@@ -481,7 +519,7 @@ __global__ __launch_bounds__(kThreads) void step_kernel(StepArgs a) {
         for (int i = 0; i < kMaxSpw; ++i) {
           if (i < cnt && valid) {
             const int f0 = (wave + kWaves * i) * kStep + g * 8;
-            st16(yrow + f0, norm_bf(hb[i], a.gamma, f0, rh));
+            sts16(yrow + f0, norm_bf(hb[i], a.gamma, f0, rh));
           }
         }
       }
@@ -617,6 +655,406 @@ __global__ __launch_bounds__(kThreads) void step_kernel(StepArgs a) {
           f32x4{comb[4 * j], comb[4 * j + 1], comb[4 * j + 2], comb[4 * j + 3]};
   }
 }
+
+// ----- pipelined bf16 kernel (d <= 5120) ------------------------------------------------
+//
+// Persistent workgroups of 8 waves (two per SIMD), at most one per CU because
+// h fills the LDS, walk over 16-token tiles. Wave w takes the 32-feature steps
+// w, w+8, ... of the tile. The memory streams are software-pipelined by hand,
+// because the vector-memory counter retires in issue order and a wait on a
+// late-issued load would otherwise drain every earlier prefetch. Each step i
+// issues, in this order:
+//   1. the 20 packed-projection loads of step i (served by L2),
+//   2. the stream loads of step i+kAhead (kAhead+1 rotating register buffers),
+//   3. [wait for step i's streams] hc_post, the new-stream stores, the sums of
+//      squares and hc_pre, h into LDS,
+//   4. [wait for step i's projection operands] 20 MFMAs.
+// The other wave of the SIMD runs while one waits for its operands. The loop is
+// unrolled by the period of the stream-buffer rotation so no register copies
+// are needed. Stream tensors use buffer instructions whose range check
+// drops the lanes of tokens past the end of the tensor (no branches), and the
+// padding half of the last operand tile is read from outside the range, which
+// returns zeros without memory traffic. h is kept in LDS (one 1 KB slot per
+// wave step; the last step of the waves that would overflow stays in
+// registers) until the token's sum of squares is known.
+
+namespace pipe {
+
+#ifndef MHC_PREFETCH
+#define MHC_PREFETCH 1
+#endif
+constexpr int kAhead = MHC_PREFETCH;        // stream prefetch distance in steps (1 or 2)
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kMaxSteps = 160;              // d <= 5120
+constexpr int kSlots = kMaxSteps - kWaves;  // LDS slots for h
+constexpr int kCols = 3 * kMix;             // real packed columns (hi/mid/lo x 24)
+constexpr int kTiles = kTilesBf;
+constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw buffer, 32-bit data format (gfx9)
+constexpr int kNT = 2;                         // cache-policy bit: non-temporal
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+struct __align__(16) Smem {
+  union {
+    u32x4 h[kSlots][64];
+    float acc[kWaves][kTok][kCols];
+  } u;
+  float ss[kWaves][kTok];
+  float hs[kWaves][kTok];
+};
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, (int)kRsrcWord3);
+}
+template <int AUX>
+__device__ __forceinline__ u32x4 bload(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, AUX));
+}
+template <int AUX>
+__device__ __forceinline__ void bstore(rsrc_t r, uint32_t voff, uint32_t soff, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(
+      __builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b128(r, 0, 0, 0)), v), r,
+      (int)voff, (int)soff, AUX);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// DPP controls: quad permutations and rotations inside a 16-lane row
+constexpr int kQuadSwap1 = 0xB1;   // [1,0,3,2]
+constexpr int kQuadSwap2 = 0x4E;   // [2,3,0,1]
+constexpr int kRowRor4 = 0x124;
+constexpr int kRowRor8 = 0x128;
+
+__device__ __forceinline__ float quad_sum(float v) {
+  v += dpp<kQuadSwap1>(v);
+  return v + dpp<kQuadSwap2>(v);
+}
+__device__ __forceinline__ float quad_max(float v) {
+  v = fmaxf(v, dpp<kQuadSwap1>(v));
+  return fmaxf(v, dpp<kQuadSwap2>(v));
+}
+// sum over lanes e, e+4, e+8, e+12 of a 16-lane row
+__device__ __forceinline__ float col_sum(float v) {
+  v += dpp<kRowRor8>(v);
+  return v + dpp<kRowRor4>(v);
+}
+
+struct SBuf {
+  u32x4 x[4];
+  u32x4 f;
+};
+
+struct Ctx {
+  rsrc_t xr, fr, xor_, yr, wr;
+  uint32_t xoff, foff;   // lane byte offsets inside the tile's stream rows
+  uint32_t woff, woff_last;
+  int d2;                // d * 2 bytes (stream stride)
+  float C[4][4], U[4], P[4];
+  f32x4 acc[kTiles];
+  float ss, hs;
+  u32x4 hlast;
+};
+
+template <int MODE>
+__device__ __forceinline__ void load_s(SBuf& sb, const Ctx& c, int s) {
+  const uint32_t col = (uint32_t)s * 64;   // 32 features x 2 bytes
+#pragma unroll
+  for (int j = 0; j < 4; ++j) sb.x[j] = bload<kNT>(c.xr, c.xoff, col + (uint32_t)j * c.d2);
+  sb.f = MODE == kFused ? bload<kNT>(c.fr, c.foff, col) : u32x4{0, 0, 0, 0};
+}
+
+// One pipelined step on stream buffer `sc`, prefetching step i+2 into `s2`.
+// The arithmetic per element is that of step_bf.
+template <int MODE, bool GUARD>
+__device__ __forceinline__ void body(int i, int cnt, int wave, Ctx& c, Smem& sm, int lane,
+                                     const SBuf& sc, SBuf& s2) {
+  if (GUARD && i >= cnt) return;
+  const int s = wave + kWaves * i;
+  u32x4 w[4][kTiles];
+  {
+    const uint32_t base = (uint32_t)s * (kStreams * kTiles * 1024);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int q = 0; q < kTiles; ++q)
+        w[k][q] = bload<0>(c.wr, q == kTiles - 1 ? c.woff_last : c.woff,
+                           base + (uint32_t)(k * kTiles + q) * 1024);
+  }
+  load_s<MODE>(s2, c, i + kAhead < cnt ? s + kAhead * kWaves : s);
+  __builtin_amdgcn_sched_barrier(0);
+
+  u32x4 xo[4];
+  if (MODE == kFused) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float a0[4], a1[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        a0[j] = bf_lo(sc.x[j][q]);
+        a1[j] = bf_hi(sc.x[j][q]);
+      }
+      const float f0v = bf_lo(sc.f[q]), f1v = bf_hi(sc.f[q]);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        float v0 = a0[0] * c.C[0][k];
+        float v1 = a1[0] * c.C[0][k];
+#pragma unroll
+        for (int j = 1; j < 4; ++j) {
+          v0 = fmaf(a0[j], c.C[j][k], v0);
+          v1 = fmaf(a1[j], c.C[j][k], v1);
+        }
+        v0 = fmaf(f0v, c.U[k], v0);
+        v1 = fmaf(f1v, c.U[k], v1);
+        xo[k][q] = pack_bf16x2(v0, v1);
+      }
+    }
+    const uint32_t col = (uint32_t)s * 64;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) bstore<0>(c.xor_, c.xoff, col + (uint32_t)k * c.d2, xo[k]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) xo[k] = sc.x[k];
+  }
+
+  u32x4 hpk = {0, 0, 0, 0};
+  float ssa = 0.f, ssb = 0.f, hsa = 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float r0[4], r1[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      r0[k] = bf_lo(xo[k][q]);
+      r1[k] = bf_hi(xo[k][q]);
+      ssa = fmaf(r0[k], r0[k], ssa);
+      ssb = fmaf(r1[k], r1[k], ssb);
+    }
+    if (MODE == kFused) {
+      float h0 = c.P[0] * r0[0], h1 = c.P[0] * r1[0];
+#pragma unroll
+      for (int k = 1; k < 4; ++k) {
+        h0 = fmaf(c.P[k], r0[k], h0);
+        h1 = fmaf(c.P[k], r1[k], h1);
+      }
+      const uint32_t hp = pack_bf16x2(h0, h1);
+      hpk[q] = hp;
+      const float q0 = bf_lo(hp), q1 = bf_hi(hp);
+      hsa = fmaf(q0, q0, hsa);
+      hsa = fmaf(q1, q1, hsa);
+    }
+  }
+  c.ss += ssa + ssb;
+  c.hs += hsa;
+  if (MODE == kFused && MHC_HWRITE != 1) {
+    if (s < kSlots) {
+      if (MHC_HWRITE == 2) {
+        uint2* p = reinterpret_cast<uint2*>(&sm.u.h[s][lane]);
+        p[0] = make_uint2(hpk[0], hpk[1]);
+        p[1] = make_uint2(hpk[2], hpk[3]);
+      } else {
+        sm.u.h[s][lane] = hpk;
+      }
+    } else {
+      c.hlast = hpk;
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const bf16x8 A = __builtin_bit_cast(bf16x8, xo[k]);
+#pragma unroll
+    for (int q = 0; q < kTiles; ++q)
+      c.acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8, w[k][q]),
+                                                         c.acc[q], 0, 0, 0);
+  }
+  if (MODE == kFused && MHC_HWRITE == 1) {
+    if (s < kSlots) sm.u.h[s][lane] = hpk;
+    else c.hlast = hpk;
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kThreads) void fused_bf16_kernel(StepArgs a, int ntiles) {
+  __shared__ Smem sm;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tr = lane & 15;
+  const int g = lane >> 4;
+  const int d = a.d;
+  const int nsteps = d / kStep;
+  const int cnt = wave < nsteps ? (nsteps - wave + kWaves - 1) / kWaves : 0;
+
+  Ctx c;
+  c.d2 = d * 2;
+  c.wr = make_rsrc(a.wpk, (uint32_t)nsteps * kStreams * kTiles * 1024);
+  c.woff = (uint32_t)lane * 16;
+  c.woff_last = (tr < kCols - 16 * (kTiles - 1)) ? (uint32_t)lane * 16 : kOutOfRange;
+
+  SBuf sa, sb, sx;
+
+  auto setup = [&](int tile) {
+    const int64_t t0 = (int64_t)tile * kTok;
+    const int ntok = (int)min((int64_t)kTok, a.tokens - t0);
+    const uint32_t rowx = (uint32_t)(kStreams * d * 2), rowf = (uint32_t)(d * 2);
+    c.xr = make_rsrc(static_cast<const char*>(a.x) + t0 * rowx, ntok * rowx);
+    if (MODE == kFused) {
+      c.fr = make_rsrc(static_cast<const char*>(a.f) + t0 * rowf, ntok * rowf);
+      c.xor_ = make_rsrc(static_cast<char*>(a.x_out) + t0 * rowx, ntok * rowx);
+      c.yr = make_rsrc(static_cast<char*>(a.y_out) + t0 * rowf, ntok * rowf);
+    }
+    c.xoff = (uint32_t)tr * rowx + (uint32_t)g * 16;
+    c.foff = (uint32_t)tr * rowf + (uint32_t)g * 16;
+    if (MODE == kFused) {
+      const int64_t tc = t0 + min(tr, ntok - 1);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 cv = *reinterpret_cast<const f32x4*>(a.comb_in + tc * 16 + 4 * j);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) c.C[j][k] = cv[k];
+      }
+      const f32x4 u = *reinterpret_cast<const f32x4*>(a.post_in + tc * 4);
+      const f32x4 p = *reinterpret_cast<const f32x4*>(a.pre_in + tc * 4);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        c.U[k] = u[k];
+        c.P[k] = p[k];
+      }
+    }
+    if (cnt > 0) {
+      load_s<MODE>(sa, c, wave);
+      if (kAhead == 2) load_s<MODE>(sb, c, cnt > 1 ? wave + kWaves : wave);
+    }
+  };
+
+  int tile = blockIdx.x;
+  if (tile < ntiles) setup(tile);
+  for (; tile < ntiles; tile += gridDim.x) {
+    const int64_t t0 = (int64_t)tile * kTok;
+    const int ntok = (int)min((int64_t)kTok, a.tokens - t0);
+#pragma unroll
+    for (int q = 0; q < kTiles; ++q) c.acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    c.ss = 0.f;
+    c.hs = 0.f;
+    c.hlast = u32x4{0, 0, 0, 0};
+
+    int i = 0;
+    if (kAhead == 2) {
+      for (; i + 3 <= cnt; i += 3) {
+        body<MODE, false>(i + 0, cnt, wave, c, sm, lane, sa, sx);
+        body<MODE, false>(i + 1, cnt, wave, c, sm, lane, sb, sa);
+        body<MODE, false>(i + 2, cnt, wave, c, sm, lane, sx, sb);
+      }
+      body<MODE, true>(i + 0, cnt, wave, c, sm, lane, sa, sx);
+      body<MODE, true>(i + 1, cnt, wave, c, sm, lane, sb, sa);
+    } else {
+      for (; i + 2 <= cnt; i += 2) {
+        body<MODE, false>(i + 0, cnt, wave, c, sm, lane, sa, sb);
+        body<MODE, false>(i + 1, cnt, wave, c, sm, lane, sb, sa);
+      }
+      body<MODE, true>(i + 0, cnt, wave, c, sm, lane, sa, sb);
+    }
+
+    // keep what the tail needs; start the next tile's loads so they fly while
+    // this tile's y, reductions and Sinkhorn run
+    const rsrc_t yr = c.yr;
+    const float hsum_part = c.hs, ssum_part = c.ss;
+    f32x4 acc[kTiles];
+#pragma unroll
+    for (int q = 0; q < kTiles; ++q) acc[q] = c.acc[q];
+    const u32x4 hlast = c.hlast;
+    const uint32_t foff = c.foff;
+    if (tile + (int)gridDim.x < ntiles) setup(tile + gridDim.x);
+
+    // ---- sums of squares: over the four lane groups, then across waves ----
+    float ss = ssum_part, hs = hsum_part;
+    ss += __shfl_xor(ss, 16);
+    ss += __shfl_xor(ss, 32);
+    hs += __shfl_xor(hs, 16);
+    hs += __shfl_xor(hs, 32);
+    if (g == 0) {
+      sm.ss[wave][tr] = ss;
+      sm.hs[wave][tr] = hs;
+    }
+    __syncthreads();
+
+    // ---- y = bf16(gamma * (h * rh)) ([RN] RMSNorm) ----
+    if (MODE == kFused) {
+      float hsum = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) hsum += sm.hs[w][tr];
+      const float rh = rsqrtf(hsum / (float)d + a.norm_eps);
+      for (int ii = 0; ii < cnt; ++ii) {
+        const int s = wave + kWaves * ii;
+        const u32x4 h = s < kSlots ? sm.u.h[s][lane] : hlast;
+        const int f0 = s * kStep + g * 8;
+        bstore<kNT>(yr, foff, (uint32_t)s * 64, norm_bf(h, a.gamma, f0, rh));
+      }
+      __syncthreads();
+    }
+
+    // ---- projection partials across waves ----
+#pragma unroll
+    for (int q = 0; q < kTiles; ++q) {
+      const int col = 16 * q + tr;
+      if (col < kCols) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sm.u.acc[wave][4 * g + r][col] = acc[q][r];
+      }
+    }
+    __syncthreads();
+
+    // ---- per-token tail: one token per 16-lane row, one comb entry per lane ----
+    if (tid < kTok * 16) {
+      const int tt = tid >> 4;
+      const int e = tid & 15;
+      float ssum = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) ssum += sm.ss[w][tt];
+      const float r = rsqrtf(ssum / (float)(kStreams * d) + a.norm_eps);
+      auto mix_at = [&](int j) {
+        float hi = 0.f, mid = 0.f, lo = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          hi += sm.u.acc[w][tt][j];
+          mid += sm.u.acc[w][tt][kMix + j];
+          lo += sm.u.acc[w][tt][2 * kMix + j];
+        }
+        return ((hi + mid) + lo) * r;
+      };
+      const float mc = mix_at(8 + e);                 // comb logit slot of (j, k) = (e/4, e%4)
+      const float mp = mix_at(e < 8 ? e : 0);         // pre / post slot for e < 8
+      const bool tok_ok = tt < ntok;
+      const int64_t t = t0 + tt;
+      if (tok_ok && a.mix_out != nullptr) {
+        a.mix_out[t * kMix + 8 + e] = mc;
+        if (e < 8) a.mix_out[t * kMix + e] = mp;
+      }
+      const float s0 = a.scale[0], s1 = a.scale[1], s2 = a.scale[2];
+      const float eps = a.hc_eps;
+      if (tok_ok && e < 4) a.pre_out[t * 4 + e] = sigmoidf(mp * s0 + a.base[e]) + eps;
+      if (tok_ok && e >= 4 && e < 8)
+        a.post_out[t * 4 + (e - 4)] = 2.0f * sigmoidf(mp * s1 + a.base[e]);
+      float cv = mc * s2 + a.base[8 + e];
+      cv = expf(cv - quad_max(cv));
+      cv = cv / quad_sum(cv) + eps;
+      cv = cv * __builtin_amdgcn_rcpf(col_sum(cv) + eps);
+      for (int it = 1; it < a.iters; ++it) {
+        cv = cv * __builtin_amdgcn_rcpf(quad_sum(cv) + eps);
+        cv = cv * __builtin_amdgcn_rcpf(col_sum(cv) + eps);
+      }
+      if (tok_ok) a.comb_out[t * 16 + e] = cv;
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace pipe
 
 // ----- split / Sinkhorn on given mixes -------------------------------------------------
 
@@ -806,13 +1244,58 @@ typedef void (*StepKernel)(StepArgs);
 
 StepKernel pick_step_kernel(int32_t dtype, int mode, int32_t d) {
   const int nsteps = d / kStep;
-  const bool hreg = (nsteps + kWaves - 1) / kWaves <= kMaxSpw;
+  const bool hreg = !MHC_FORCE_HMEM && (nsteps + kWaves - 1) / kWaves <= kMaxSpw;
   if (dtype == MHC_BF16) {
     if (mode == kMixesOnly) return step_kernel<MHC_BF16, kMixesOnly, false>;
     return hreg ? step_kernel<MHC_BF16, kFused, true> : step_kernel<MHC_BF16, kFused, false>;
   }
   if (mode == kMixesOnly) return step_kernel<MHC_F32, kMixesOnly, false>;
   return step_kernel<MHC_F32, kFused, false>;
+}
+
+#ifndef MHC_FORCE_GENERIC
+#define MHC_FORCE_GENERIC 0
+#endif
+
+// Compute units of the current device (cached per device ordinal).
+mhc_status device_cu_count(int* out) {
+  static int cache[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MHC_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev >= 0 && dev < 64 && cache[dev] > 0) {
+    *out = cache[dev];
+    return MHC_OK;
+  }
+  int n = 0;
+  e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess || n <= 0)
+    return fail(MHC_ERR_HIP, "hipDeviceGetAttribute(multiprocessor count): %s", hipGetErrorString(e));
+  if (dev >= 0 && dev < 64) cache[dev] = n;
+  *out = n;
+  return MHC_OK;
+}
+
+mhc_status launch_step(const StepArgs& a, int32_t dtype, int mode, hipStream_t stream,
+                       const char* what) {
+  const int nsteps = a.d / kStep;
+  const int64_t ntiles = (a.tokens + kTok - 1) / kTok;
+  if (!MHC_FORCE_GENERIC && dtype == MHC_BF16 && nsteps <= pipe::kMaxSteps) {
+    int cus = 0;
+    const mhc_status s = device_cu_count(&cus);
+    if (s != MHC_OK) return s;
+    const unsigned grid = (unsigned)std::min<int64_t>(ntiles, cus);
+    if (mode == kFused)
+      hipLaunchKernelGGL(pipe::fused_bf16_kernel<kFused>, dim3(grid), dim3(pipe::kThreads), 0,
+                         stream, a, (int)ntiles);
+    else
+      hipLaunchKernelGGL(pipe::fused_bf16_kernel<kMixesOnly>, dim3(grid), dim3(pipe::kThreads), 0,
+                         stream, a, (int)ntiles);
+    return launch_status(what);
+  }
+  hipLaunchKernelGGL(pick_step_kernel(dtype, mode, a.d), dim3((unsigned)ntiles), dim3(kThreads), 0,
+                     stream, a);
+  return launch_status(what);
 }
 
 }  // namespace
@@ -895,10 +1378,7 @@ mhc_status mhc_fused_step(const void* x, const void* f, int32_t dtype, int64_t t
   }
   StepArgs a{x, f, pre_in, post_in, comb_in, w_packed, base, scale, gamma, x_out, y_out,
              pre_out, post_out, comb_out, mix_out, tokens, d, sinkhorn_iters, norm_eps, hc_eps};
-  const unsigned blocks = (unsigned)((tokens + kTok - 1) / kTok);
-  hipLaunchKernelGGL(pick_step_kernel(dtype, kFused, d), dim3(blocks), dim3(kThreads), 0,
-                     static_cast<hipStream_t>(stream), a);
-  return launch_status("fused step kernel launch");
+  return launch_step(a, dtype, kFused, static_cast<hipStream_t>(stream), "fused step kernel launch");
 }
 
 mhc_status mhc_mixes(const void* x, int32_t dtype, int64_t tokens, int32_t d,
@@ -924,10 +1404,7 @@ mhc_status mhc_mixes(const void* x, int32_t dtype, int64_t tokens, int32_t d,
   StepArgs a{x, nullptr, nullptr, nullptr, nullptr, w_packed, base, scale, nullptr, nullptr,
              nullptr, pre_out, post_out, comb_out, mix_out, tokens, d, sinkhorn_iters, norm_eps,
              hc_eps};
-  const unsigned blocks = (unsigned)((tokens + kTok - 1) / kTok);
-  hipLaunchKernelGGL(pick_step_kernel(dtype, kMixesOnly, d), dim3(blocks), dim3(kThreads), 0,
-                     static_cast<hipStream_t>(stream), a);
-  return launch_status("mixes kernel launch");
+  return launch_step(a, dtype, kMixesOnly, static_cast<hipStream_t>(stream), "mixes kernel launch");
 }
 
 mhc_status mhc_sinkhorn4(const float* mixes, int64_t tokens, const float* base,

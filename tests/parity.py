@@ -60,8 +60,15 @@ class ParityError(AssertionError):
 def _fail(what, mask, got, want, extra=""):
     idx = np.argwhere(mask)
     first = tuple(idx[0]) if len(idx) else ()
+    where = ""
+    if mask.ndim >= 2:
+        toks = np.unique(idx[:, 0])
+        where = f"; tokens {toks[:12].tolist()}{' ...' if len(toks) > 12 else ''}"
+        if mask.ndim == 2:
+            steps = np.unique(idx[:, 1] // 32)
+            where += f"; 32-feature blocks {steps[:12].tolist()}"
     raise ParityError(f"{what}: {int(mask.sum())} of {mask.size} elements out of tolerance; "
-                      f"first at {first}: got {got[first]!r} want {want[first]!r} {extra}")
+                      f"first at {first}: got {got[first]!r} want {want[first]!r} {extra}{where}")
 
 
 def check_mix_like(what, got, want):
