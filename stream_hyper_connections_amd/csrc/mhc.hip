@@ -78,16 +78,13 @@ __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 #ifndef MHC_STREAM_NT
-#define MHC_STREAM_NT 0
+#define MHC_STREAM_NT 1
 #endif
 #ifndef MHC_SKIP_PAD
-#define MHC_SKIP_PAD 0
+#define MHC_SKIP_PAD 1
 #endif
 #ifndef MHC_FORCE_HMEM
 #define MHC_FORCE_HMEM 0
-#endif
-#ifndef MHC_HWRITE
-#define MHC_HWRITE 0   // 0: h to LDS before the MFMAs, 1: after them, 2: as two 8-byte writes
 #endif
 
 
@@ -658,32 +655,32 @@ __global__ __launch_bounds__(kThreads) void step_kernel(StepArgs a) {
 
 // ----- pipelined bf16 kernel (d <= 5120) ------------------------------------------------
 //
-// Persistent workgroups of 8 waves (two per SIMD), at most one per CU because
-// h fills the LDS, walk over 16-token tiles. Wave w takes the 32-feature steps
-// w, w+8, ... of the tile. The memory streams are software-pipelined by hand,
-// because the vector-memory counter retires in issue order and a wait on a
-// late-issued load would otherwise drain every earlier prefetch. Each step i
-// issues, in this order:
-//   1. the 20 packed-projection loads of step i (served by L2),
-//   2. the stream loads of step i+kAhead (kAhead+1 rotating register buffers),
-//   3. [wait for step i's streams] hc_post, the new-stream stores, the sums of
-//      squares and hc_pre, h into LDS,
-//   4. [wait for step i's projection operands] 20 MFMAs.
-// The other wave of the SIMD runs while one waits for its operands. The loop is
-// unrolled by the period of the stream-buffer rotation so no register copies
-// are needed. Stream tensors use buffer instructions whose range check
-// drops the lanes of tokens past the end of the tensor (no branches), and the
-// padding half of the last operand tile is read from outside the range, which
-// returns zeros without memory traffic. h is kept in LDS (one 1 KB slot per
-// wave step; the last step of the waves that would overflow stays in
-// registers) until the token's sum of squares is known.
+// Persistent workgroups of 8 waves (two per SIMD; one workgroup per CU because
+// h fills the LDS) walk over 16-token tiles. The unit of work of a wave is a
+// PAIR of adjacent 32-feature steps (64 features = one 128-byte line of every
+// token row): wave w takes the pairs w, w+8, ... of the tile, so both halves of
+// each line are loaded and stored by the same wave, back to back. The memory
+// streams are software-pipelined by hand, because the vector-memory counter
+// retires in issue order and a wait on a late-issued load would otherwise drain
+// every earlier prefetch. Per pair (steps A and B):
+//   1. projection operands of A (20 loads, L2)
+//   2. [wait streams of A] hc_post, sums of squares, hc_pre for A; h to LDS
+//   3. stream loads of the NEXT pair's A into the freed registers
+//   4. [wait operands of A] 20 MFMAs
+//   5. projection operands of B
+//   6. [wait streams of B] VALU work of B
+//   7. stream loads of the next pair's B; stores of A and B interleaved, so
+//      every 128-byte line of the new streams is written by two adjacent
+//      instructions
+//   8. [wait operands of B] 20 MFMAs
+// Stream tensors use buffer instructions whose range check drops the lanes of
+// tokens past the end of the tensor (no branches), and the padding half of the
+// last operand tile is read from outside the range, which returns zeros without
+// memory traffic. h is kept in LDS (one 1 KB slot per step; the steps beyond the
+// LDS capacity stay in registers) until the token's sum of squares is known.
 
 namespace pipe {
 
-#ifndef MHC_PREFETCH
-#define MHC_PREFETCH 1
-#endif
-constexpr int kAhead = MHC_PREFETCH;        // stream prefetch distance in steps (1 or 2)
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kMaxSteps = 160;              // d <= 5120
@@ -693,6 +690,10 @@ constexpr int kTiles = kTilesBf;
 constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw buffer, 32-bit data format (gfx9)
 constexpr int kNT = 2;                         // cache-policy bit: non-temporal
 constexpr uint32_t kOutOfRange = 0x80000000u;
+
+#ifndef MHC_STORE_AUX
+#define MHC_STORE_AUX 0
+#endif
 
 struct __align__(16) Smem {
   union {
@@ -743,7 +744,7 @@ __device__ __forceinline__ float col_sum(float v) {
   return v + dpp<kRowRor4>(v);
 }
 
-struct SBuf {
+struct Half {   // stream inputs of one 32-feature step
   u32x4 x[4];
   u32x4 f;
 };
@@ -756,48 +757,42 @@ struct Ctx {
   float C[4][4], U[4], P[4];
   f32x4 acc[kTiles];
   float ss, hs;
-  u32x4 hlast;
+  u32x4 hlast[2];
 };
 
 template <int MODE>
-__device__ __forceinline__ void load_s(SBuf& sb, const Ctx& c, int s) {
+__device__ __forceinline__ void load_half(Half& hf, const Ctx& c, int s) {
   const uint32_t col = (uint32_t)s * 64;   // 32 features x 2 bytes
 #pragma unroll
-  for (int j = 0; j < 4; ++j) sb.x[j] = bload<kNT>(c.xr, c.xoff, col + (uint32_t)j * c.d2);
-  sb.f = MODE == kFused ? bload<kNT>(c.fr, c.foff, col) : u32x4{0, 0, 0, 0};
+  for (int j = 0; j < 4; ++j) hf.x[j] = bload<kNT>(c.xr, c.xoff, col + (uint32_t)j * c.d2);
+  hf.f = MODE == kFused ? bload<kNT>(c.fr, c.foff, col) : u32x4{0, 0, 0, 0};
 }
 
-// One pipelined step on stream buffer `sc`, prefetching step i+2 into `s2`.
-// The arithmetic per element is that of step_bf.
-template <int MODE, bool GUARD>
-__device__ __forceinline__ void body(int i, int cnt, int wave, Ctx& c, Smem& sm, int lane,
-                                     const SBuf& sc, SBuf& s2) {
-  if (GUARD && i >= cnt) return;
-  const int s = wave + kWaves * i;
-  u32x4 w[4][kTiles];
-  {
-    const uint32_t base = (uint32_t)s * (kStreams * kTiles * 1024);
+__device__ __forceinline__ void load_w(u32x4 (&w)[4][kTiles], const Ctx& c, int s) {
+  const uint32_t base = (uint32_t)s * (kStreams * kTiles * 1024);
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
+  for (int k = 0; k < 4; ++k)
 #pragma unroll
-      for (int q = 0; q < kTiles; ++q)
-        w[k][q] = bload<0>(c.wr, q == kTiles - 1 ? c.woff_last : c.woff,
-                           base + (uint32_t)(k * kTiles + q) * 1024);
-  }
-  load_s<MODE>(s2, c, i + kAhead < cnt ? s + kAhead * kWaves : s);
-  __builtin_amdgcn_sched_barrier(0);
+    for (int q = 0; q < kTiles; ++q)
+      w[k][q] = bload<0>(c.wr, q == kTiles - 1 ? c.woff_last : c.woff,
+                         base + (uint32_t)(k * kTiles + q) * 1024);
+}
 
-  u32x4 xo[4];
+// hc_post, the sums of squares and hc_pre of one step (the arithmetic per
+// element is that of step_bf); h goes to LDS slot s (or a register).
+template <int MODE>
+__device__ __forceinline__ void valu_step(const Half& in, u32x4 (&xo)[4], Ctx& c, Smem& sm, int s,
+                                          int lane, int half) {
   if (MODE == kFused) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       float a0[4], a1[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        a0[j] = bf_lo(sc.x[j][q]);
-        a1[j] = bf_hi(sc.x[j][q]);
+        a0[j] = bf_lo(in.x[j][q]);
+        a1[j] = bf_hi(in.x[j][q]);
       }
-      const float f0v = bf_lo(sc.f[q]), f1v = bf_hi(sc.f[q]);
+      const float f0v = bf_lo(in.f[q]), f1v = bf_hi(in.f[q]);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         float v0 = a0[0] * c.C[0][k];
@@ -812,12 +807,9 @@ __device__ __forceinline__ void body(int i, int cnt, int wave, Ctx& c, Smem& sm,
         xo[k][q] = pack_bf16x2(v0, v1);
       }
     }
-    const uint32_t col = (uint32_t)s * 64;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) bstore<0>(c.xor_, c.xoff, col + (uint32_t)k * c.d2, xo[k]);
   } else {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) xo[k] = sc.x[k];
+    for (int k = 0; k < 4; ++k) xo[k] = in.x[k];
   }
 
   u32x4 hpk = {0, 0, 0, 0};
@@ -848,21 +840,14 @@ __device__ __forceinline__ void body(int i, int cnt, int wave, Ctx& c, Smem& sm,
   }
   c.ss += ssa + ssb;
   c.hs += hsa;
-  if (MODE == kFused && MHC_HWRITE != 1) {
-    if (s < kSlots) {
-      if (MHC_HWRITE == 2) {
-        uint2* p = reinterpret_cast<uint2*>(&sm.u.h[s][lane]);
-        p[0] = make_uint2(hpk[0], hpk[1]);
-        p[1] = make_uint2(hpk[2], hpk[3]);
-      } else {
-        sm.u.h[s][lane] = hpk;
-      }
-    } else {
-      c.hlast = hpk;
-    }
+  if (MODE == kFused) {
+    if (s < kSlots) sm.u.h[s][lane] = hpk;
+    else c.hlast[half] = hpk;
   }
-  __builtin_amdgcn_sched_barrier(0);
+}
 
+__device__ __forceinline__ void mfma_step(const u32x4 (&xo)[4], const u32x4 (&w)[4][kTiles],
+                                          Ctx& c) {
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const bf16x8 A = __builtin_bit_cast(bf16x8, xo[k]);
@@ -871,10 +856,41 @@ __device__ __forceinline__ void body(int i, int cnt, int wave, Ctx& c, Smem& sm,
       c.acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8, w[k][q]),
                                                          c.acc[q], 0, 0, 0);
   }
-  if (MODE == kFused && MHC_HWRITE == 1) {
-    if (s < kSlots) sm.u.h[s][lane] = hpk;
-    else c.hlast = hpk;
+}
+
+// One pair of steps (A = 2P, B = 2P + 1), prefetching the next pair's streams.
+template <int MODE>
+__device__ __forceinline__ void pair_body(int p, int cnt, int wave, Ctx& c, Smem& sm, int lane,
+                                          Half& ha, Half& hb) {
+  const int sa = 2 * (wave + kWaves * p);
+  const int sn = p + 1 < cnt ? sa + 2 * kWaves : sa;   // next pair (clamped to this one)
+  u32x4 w[4][kTiles];
+  u32x4 xa[4], xb[4];
+
+  load_w(w, c, sa);
+  __builtin_amdgcn_sched_barrier(0);
+  valu_step<MODE>(ha, xa, c, sm, sa, lane, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  load_half<MODE>(ha, c, sn);
+  __builtin_amdgcn_sched_barrier(0);
+  mfma_step(xa, w, c);
+  __builtin_amdgcn_sched_barrier(0);
+
+  load_w(w, c, sa + 1);
+  __builtin_amdgcn_sched_barrier(0);
+  valu_step<MODE>(hb, xb, c, sm, sa + 1, lane, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  load_half<MODE>(hb, c, sn + 1);
+  if (MODE == kFused) {
+    const uint32_t col = (uint32_t)sa * 64;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      bstore<MHC_STORE_AUX>(c.xor_, c.xoff, col + (uint32_t)k * c.d2, xa[k]);
+      bstore<MHC_STORE_AUX>(c.xor_, c.xoff, col + 64 + (uint32_t)k * c.d2, xb[k]);
+    }
   }
+  __builtin_amdgcn_sched_barrier(0);
+  mfma_step(xb, w, c);
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -888,7 +904,8 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_kernel(StepArgs a, int nt
   const int g = lane >> 4;
   const int d = a.d;
   const int nsteps = d / kStep;
-  const int cnt = wave < nsteps ? (nsteps - wave + kWaves - 1) / kWaves : 0;
+  const int npairs = nsteps / 2;
+  const int cnt = wave < npairs ? (npairs - wave + kWaves - 1) / kWaves : 0;
 
   Ctx c;
   c.d2 = d * 2;
@@ -896,7 +913,7 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_kernel(StepArgs a, int nt
   c.woff = (uint32_t)lane * 16;
   c.woff_last = (tr < kCols - 16 * (kTiles - 1)) ? (uint32_t)lane * 16 : kOutOfRange;
 
-  SBuf sa, sb, sx;
+  Half ha, hb;
 
   auto setup = [&](int tile) {
     const int64_t t0 = (int64_t)tile * kTok;
@@ -927,8 +944,8 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_kernel(StepArgs a, int nt
       }
     }
     if (cnt > 0) {
-      load_s<MODE>(sa, c, wave);
-      if (kAhead == 2) load_s<MODE>(sb, c, cnt > 1 ? wave + kWaves : wave);
+      load_half<MODE>(ha, c, 2 * wave);
+      load_half<MODE>(hb, c, 2 * wave + 1);
     }
   };
 
@@ -941,24 +958,9 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_kernel(StepArgs a, int nt
     for (int q = 0; q < kTiles; ++q) c.acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
     c.ss = 0.f;
     c.hs = 0.f;
-    c.hlast = u32x4{0, 0, 0, 0};
+    c.hlast[0] = c.hlast[1] = u32x4{0, 0, 0, 0};
 
-    int i = 0;
-    if (kAhead == 2) {
-      for (; i + 3 <= cnt; i += 3) {
-        body<MODE, false>(i + 0, cnt, wave, c, sm, lane, sa, sx);
-        body<MODE, false>(i + 1, cnt, wave, c, sm, lane, sb, sa);
-        body<MODE, false>(i + 2, cnt, wave, c, sm, lane, sx, sb);
-      }
-      body<MODE, true>(i + 0, cnt, wave, c, sm, lane, sa, sx);
-      body<MODE, true>(i + 1, cnt, wave, c, sm, lane, sb, sa);
-    } else {
-      for (; i + 2 <= cnt; i += 2) {
-        body<MODE, false>(i + 0, cnt, wave, c, sm, lane, sa, sb);
-        body<MODE, false>(i + 1, cnt, wave, c, sm, lane, sb, sa);
-      }
-      body<MODE, true>(i + 0, cnt, wave, c, sm, lane, sa, sb);
-    }
+    for (int p = 0; p < cnt; ++p) pair_body<MODE>(p, cnt, wave, c, sm, lane, ha, hb);
 
     // keep what the tail needs; start the next tile's loads so they fly while
     // this tile's y, reductions and Sinkhorn run
@@ -967,7 +969,7 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_kernel(StepArgs a, int nt
     f32x4 acc[kTiles];
 #pragma unroll
     for (int q = 0; q < kTiles; ++q) acc[q] = c.acc[q];
-    const u32x4 hlast = c.hlast;
+    const u32x4 hlast0 = c.hlast[0], hlast1 = c.hlast[1];
     const uint32_t foff = c.foff;
     if (tile + (int)gridDim.x < ntiles) setup(tile + gridDim.x);
 
@@ -983,17 +985,21 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_kernel(StepArgs a, int nt
     }
     __syncthreads();
 
-    // ---- y = bf16(gamma * (h * rh)) ([RN] RMSNorm) ----
+    // ---- y = bf16(gamma * (h * rh)) ([RN] RMSNorm), both halves of each line together ----
     if (MODE == kFused) {
       float hsum = 0.f;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) hsum += sm.hs[w][tr];
       const float rh = rsqrtf(hsum / (float)d + a.norm_eps);
-      for (int ii = 0; ii < cnt; ++ii) {
-        const int s = wave + kWaves * ii;
-        const u32x4 h = s < kSlots ? sm.u.h[s][lane] : hlast;
-        const int f0 = s * kStep + g * 8;
-        bstore<kNT>(yr, foff, (uint32_t)s * 64, norm_bf(h, a.gamma, f0, rh));
+      for (int pp = 0; pp < cnt; ++pp) {
+        const int sa = 2 * (wave + kWaves * pp);
+        const u32x4 h0 = sa < kSlots ? sm.u.h[sa][lane] : hlast0;
+        const u32x4 h1 = sa + 1 < kSlots ? sm.u.h[sa + 1][lane] : hlast1;
+        const int f0 = sa * kStep + g * 8;
+        const u32x4 y0 = norm_bf(h0, a.gamma, f0, rh);
+        const u32x4 y1 = norm_bf(h1, a.gamma, f0 + kStep, rh);
+        bstore<kNT>(yr, foff, (uint32_t)sa * 64, y0);
+        bstore<kNT>(yr, foff, (uint32_t)sa * 64 + 64, y1);
       }
       __syncthreads();
     }
@@ -1280,7 +1286,7 @@ mhc_status launch_step(const StepArgs& a, int32_t dtype, int mode, hipStream_t s
                        const char* what) {
   const int nsteps = a.d / kStep;
   const int64_t ntiles = (a.tokens + kTok - 1) / kTok;
-  if (!MHC_FORCE_GENERIC && dtype == MHC_BF16 && nsteps <= pipe::kMaxSteps) {
+  if (!MHC_FORCE_GENERIC && dtype == MHC_BF16 && nsteps <= pipe::kMaxSteps && nsteps % 2 == 0) {
     int cus = 0;
     const mhc_status s = device_cu_count(&cus);
     if (s != MHC_OK) return s;
