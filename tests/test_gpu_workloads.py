@@ -51,6 +51,7 @@ def test_workload_full(name):
     _log(f"  comb sums: {comb_sum_stats(out['comb'])}")
 
 
+@pytest.mark.timeout(900)
 def test_workload_large_prefill_sampled():
     w = wl.WORKLOADS["large_prefill"]
     t = w.tokens
@@ -75,6 +76,7 @@ def test_workload_large_prefill_sampled():
     _log(f"large_prefill: {len(idx)} sampled tokens match; comb sums {stats}")
 
 
+@pytest.mark.timeout(900)
 def test_workload_chain():
     w = wl.WORKLOADS["chain"]
     t = w.tokens
