@@ -32,7 +32,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 N = 4
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_step_large_prefill_traffic.txt")
-KERNEL_SRC = os.path.join(ROOT, "stream_hyper_connections_amd", "csrc", "mhc.hip")
+KERNEL_DIR = os.path.join(ROOT, "stream_hyper_connections_amd", "csrc")
 
 
 def measured_traffic(workload: str):
@@ -44,12 +44,22 @@ def measured_traffic(workload: str):
     import json as _json
     try:
         rec = _json.load(open(TRAFFIC_FILE))
-        src = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+        src = kernel_source_hash()
     except (OSError, ValueError):
         return None
     if rec.get("source_sha256") != src or rec.get("workload") != workload:
         return None
     return int(rec["traffic_bytes"])
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the kernel sources (file names and contents, sorted)."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(KERNEL_DIR)):
+        h.update(name.encode())
+        h.update(open(os.path.join(KERNEL_DIR, name), "rb").read())
+    return h.hexdigest()
 
 
 def algorithmic_bytes(tokens: int, d: int, elem: int) -> int:
@@ -173,6 +183,10 @@ def main():
     outs = dict(x_out=torch.empty_like(x), y_out=torch.empty_like(f),
                 pre_out=torch.empty_like(prior["pre"]), post_out=torch.empty_like(prior["post"]),
                 comb_out=torch.empty_like(prior["comb"]))
+    split = (w.tokens >= mhc.SPLIT_MIN_TOKENS and
+             mhc.fused_step_workspace_bytes(w.tokens, w.d, w.dtype) > 0)
+    kernel_name = ("fsplit::split_kernel (feature-split fused step)" if split
+                   else "pipe::fused_bf16_kernel (tile fused step)")
     torch.cuda.synchronize()
     print(f"[bench] inputs resident after {time.time() - t_prep:.1f}s: {w.name} T={w.tokens} "
           f"d={w.d} {w.dtype}", file=sys.stderr, flush=True)
@@ -200,6 +214,13 @@ def main():
         ends[i].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+
+    if split:
+        ws = mhc.workspace_for(dev, mhc.fused_step_workspace_bytes(w.tokens, w.d, w.dtype))
+        if mhc.split_status(ws) != 0:
+            print("bench.py: a cross-workgroup wait of the feature-split kernel gave up; the "
+                  "outputs and the timing are invalid", file=sys.stderr)
+            sys.exit(1)
 
     step_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
     kern_ms = np.array([m.elapsed_time(e) for m, e in zip(mids, ends)])
@@ -236,7 +257,7 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(w.name),
                      "algorithmic_bytes_per_launch": alg,
-                     "kernel": "pipe::fused_bf16_kernel (fused step, bf16 streams)"},
+                     "kernel": kernel_name},
         "device": torch.cuda.get_device_name(0),
     }
     if not args.no_cpu_baseline:

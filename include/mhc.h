@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define MHC_ABI_VERSION 1
+#define MHC_ABI_VERSION 2
 #define MHC_N_STREAMS 4
 #define MHC_N_MIX 24
 
@@ -90,6 +90,18 @@ mhc_status mhc_pack_wmix(const float* w_mix, int32_t d, int32_t dtype, void* w_p
                          int64_t packed_bytes, mhc_stream_t stream);
 
 /*
+ * mhc_fused_step_workspace_bytes -- bytes of device workspace that
+ * mhc_fused_step needs to run its feature-split kernel for these arguments on
+ * the current device: 0 when that kernel does not apply (then the workspace
+ * argument is ignored), -1 for bad arguments or a failing HIP query (see
+ * mhc_last_error). The feature-split kernel applies to MHC_BF16 streams with
+ * d in {2048, 3072, 4096, 5120} on a device with at least 32 compute units and
+ * cooperative launch support; the size depends only on the device's compute
+ * unit count (about 15 MB for 256 CUs), not on tokens.
+ */
+int64_t mhc_fused_step_workspace_bytes(int64_t tokens, int32_t d, int32_t dtype);
+
+/*
  * mhc_fused_step -- one Single-Pass mHC step at the boundary between sublayer
  * i and sublayer i+1, in one pass over the streams ([SW] "Why": the fused form
  * moves (2n+2)*d elements per token instead of (4n+4)*d; [RN] Code,
@@ -111,6 +123,20 @@ mhc_status mhc_pack_wmix(const float* w_mix, int32_t d, int32_t dtype, void* w_p
  *          RMSNorm gain), sinkhorn_iters >= 1, norm_eps >= 0, hc_eps >= 0.
  * Outputs: x_out [T][4][d] (may be x), y_out [T][d], pre_out/post_out
  *          [T][4], comb_out [T][4][4], mix_out [T][24] (optional, NULL to skip).
+ * Workspace (optional): NULL, or device memory of workspace_bytes bytes,
+ *          256-byte aligned, overlapping no other argument. When it is given and
+ *          mhc_fused_step_workspace_bytes() > 0, the step runs the feature-split
+ *          kernel (each compute unit keeps 1/32 of the features and of W on chip;
+ *          workgroups exchange per-token partial sums through the workspace),
+ *          which needs the whole device: it is launched cooperatively, one
+ *          workgroup per compute unit, and fails with MHC_ERR_HIP when that
+ *          launch is refused. workspace_bytes below the required size is
+ *          MHC_ERR_INVALID_ARG. Otherwise the tile kernel runs (no workspace).
+ *          Calls that share a workspace must be ordered (same stream or
+ *          synchronised). After the call has completed, the 32-bit word at
+ *          workspace offset 0 is 0; it is 1 if a cross-workgroup wait gave up
+ *          after its bounded number of polls, in which case the outputs are
+ *          invalid.
  */
 mhc_status mhc_fused_step(const void* x, const void* f, int32_t dtype, int64_t tokens,
                           int32_t d, const float* pre_in, const float* post_in,
@@ -118,7 +144,7 @@ mhc_status mhc_fused_step(const void* x, const void* f, int32_t dtype, int64_t t
                           const float* scale, const float* gamma, int32_t sinkhorn_iters,
                           float norm_eps, float hc_eps, void* x_out, void* y_out,
                           float* pre_out, float* post_out, float* comb_out, float* mix_out,
-                          mhc_stream_t stream);
+                          void* workspace, int64_t workspace_bytes, mhc_stream_t stream);
 
 /*
  * mhc_mixes -- hc_mixes alone ([SW] Code, hc_mixes and "All 5 steps"): one RMS

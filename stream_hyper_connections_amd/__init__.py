@@ -10,12 +10,16 @@ from .binding import (  # noqa: F401
     MhcError,
     abi_version,
     d_granule,
+    SPLIT_MIN_TOKENS,
     fused_step,
+    fused_step_workspace_bytes,
     last_error,
     load,
     mixes,
     pack_wmix,
     sinkhorn4,
+    split_status,
     status_string,
     wmix_packed_bytes,
+    workspace_for,
 )

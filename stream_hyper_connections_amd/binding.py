@@ -30,10 +30,11 @@ _SIGS = {
     "mhc_d_granule": ([], _i32),
     "mhc_wmix_packed_bytes": ([_i32, _i32], _i64),
     "mhc_pack_wmix": ([_c_void_p, _i32, _i32, _c_void_p, _i64, _c_void_p], _i32),
+    "mhc_fused_step_workspace_bytes": ([_i64, _i32, _i32], _i64),
     "mhc_fused_step": ([_c_void_p, _c_void_p, _i32, _i64, _i32, _c_void_p, _c_void_p, _c_void_p,
                         _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _f32, _f32,
                         _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
-                        _c_void_p], _i32),
+                        _c_void_p, _i64, _c_void_p], _i32),
     "mhc_mixes": ([_c_void_p, _i32, _i64, _i32, _c_void_p, _c_void_p, _c_void_p, _i32, _f32, _f32,
                    _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p], _i32),
     "mhc_sinkhorn4": ([_c_void_p, _i64, _c_void_p, _c_void_p, _i32, _f32, _c_void_p, _c_void_p,
@@ -140,14 +141,64 @@ def pack_wmix(w_mix: torch.Tensor, dtype, out: torch.Tensor | None = None) -> to
     return out
 
 
+# token count from which path="auto" takes the feature-split kernel: below it
+# the cooperative whole-device launch and the per-call load of the projection
+# slices do not pay off
+SPLIT_MIN_TOKENS = 4096
+
+_workspaces = {}
+
+
+def fused_step_workspace_bytes(tokens: int, d: int, dtype) -> int:
+    """mhc_fused_step_workspace_bytes: 0 when the feature-split kernel does not
+    apply to (d, dtype) on the current device."""
+    n = load().mhc_fused_step_workspace_bytes(tokens, d, _dtype_name_code(dtype))
+    if n < 0:
+        raise MhcError("mhc_fused_step_workspace_bytes", MHC_ERR_INVALID_ARG, last_error())
+    return n
+
+
+def workspace_for(device, nbytes: int) -> torch.Tensor:
+    """A workspace of at least nbytes, cached per (device, current stream):
+    calls that share it are ordered by their stream."""
+    key = (torch.device(device).index, torch.cuda.current_stream(device).cuda_stream)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def split_status(workspace: torch.Tensor) -> int:
+    """The status word of a feature-split call (synchronises): 0, or 1 if a
+    cross-workgroup wait gave up."""
+    return int(workspace[:4].view(torch.int32).item())
+
+
 def fused_step(x, f, pre_in, post_in, comb_in, w_packed, base, scale, gamma, iters=20,
                norm_eps=1e-6, hc_eps=1e-6, x_out=None, y_out=None, pre_out=None, post_out=None,
-               comb_out=None, mix_out=None, want_mix=False) -> dict:
+               comb_out=None, mix_out=None, want_mix=False, path="auto", workspace=None) -> dict:
     """mhc_fused_step on tensors. x [T,4,d], f [T,d] (bf16 or f32); coefficients
-    and parameters float32. Returns dict(x_out, y, pre, post, comb, mix)."""
+    and parameters float32. Returns dict(x_out, y, pre, post, comb, mix).
+
+    path: "tile" (no workspace), "split" (feature-split kernel; raises if it does
+    not apply), or "auto" (split for at least SPLIT_MIN_TOKENS tokens when it
+    applies). workspace: optional uint8 tensor for the split kernel (a cached
+    one is used otherwise)."""
     t, n, d = x.shape
     if n != N_STREAMS:
         raise ValueError("x must be [T, 4, d]")
+    if path not in ("auto", "tile", "split"):
+        raise ValueError(f"unknown path {path!r}")
+    ws_ptr, ws_bytes = None, 0
+    if path != "tile":
+        need = fused_step_workspace_bytes(t, d, _dtype_code(x))
+        if path == "split" and need == 0:
+            raise ValueError(f"the feature-split kernel does not apply to d={d}, {x.dtype}")
+        if need > 0 and (path == "split" or t >= SPLIT_MIN_TOKENS):
+            if workspace is None:
+                workspace = workspace_for(x.device, need)
+            ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
     x_out = torch.empty_like(x) if x_out is None else x_out
     y_out = torch.empty_like(f) if y_out is None else y_out
     pre_out = _f32_out((t, N_STREAMS), x, pre_out)
@@ -159,7 +210,7 @@ def fused_step(x, f, pre_in, post_in, comb_in, w_packed, base, scale, gamma, ite
         _ptr(x), _ptr(f), _dtype_code(x), t, d, _ptr(pre_in), _ptr(post_in), _ptr(comb_in),
         _ptr(w_packed), _ptr(base), _ptr(scale), _ptr(gamma), iters, norm_eps, hc_eps,
         _ptr(x_out), _ptr(y_out), _ptr(pre_out), _ptr(post_out), _ptr(comb_out), _ptr(mix_out),
-        _stream())
+        ws_ptr, ws_bytes, _stream())
     _check("mhc_fused_step", st)
     return {"x_out": x_out, "y": y_out, "pre": pre_out, "post": post_out, "comb": comb_out,
             "mix": mix_out}

@@ -74,8 +74,31 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_amdgcn_perm(rne_bf16_hi(b), rne_bf16_hi(a), 0x07060302u);
 }
 
+// Every vector store of more than 64 bits is followed by this guard. On gfx950
+// the compiler may overwrite a store's data registers with the very next VALU
+// instruction (no wait state), and such stores have written wrong data for
+// some lanes (lanes 12-15 of each 16-lane row, the words rewritten first,
+// intermittently). A few wait states right after the store, with the
+// scheduler kept from moving anything across, avoid it.
+__device__ __forceinline__ void store_guard() {
+  __builtin_amdgcn_sched_barrier(0);
+  __asm__ volatile("s_nop 4");
+  __builtin_amdgcn_sched_barrier(0);
+}
+// pins the store that follows in place (nothing is scheduled across it)
+__device__ __forceinline__ void store_pin() { __builtin_amdgcn_sched_barrier(0); }
+
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
-__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+__device__ __forceinline__ void st16(void* p, u32x4 v) {
+  store_pin();
+  *reinterpret_cast<u32x4*>(p) = v;
+  store_guard();
+}
+__device__ __forceinline__ void st4f(float* p, f32x4 v) {
+  store_pin();
+  *reinterpret_cast<f32x4*>(p) = v;
+  store_guard();
+}
 
 #ifndef MHC_STREAM_NT
 #define MHC_STREAM_NT 1
@@ -95,8 +118,13 @@ __device__ __forceinline__ u32x4 lds16(const void* p) {
   return ld16(p);
 }
 __device__ __forceinline__ void sts16(void* p, u32x4 v) {
-  if (MHC_STREAM_NT) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
-  else st16(p, v);
+  if (MHC_STREAM_NT) {
+    store_pin();
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+    store_guard();
+  } else {
+    st16(p, v);
+  }
 }
 
 __device__ __forceinline__ float sigmoidf(float z) { return 1.0f / (1.0f + expf(-z)); }
@@ -644,12 +672,12 @@ __global__ __launch_bounds__(kThreads) void step_kernel(StepArgs a) {
     const int64_t tt = t0 + tid;
     float pre[4], post[4], comb[16];
     split_sinkhorn_token(m_lds[tid], a.base, a.scale, a.iters, a.hc_eps, pre, post, comb);
-    *reinterpret_cast<f32x4*>(a.pre_out + tt * 4) = f32x4{pre[0], pre[1], pre[2], pre[3]};
-    *reinterpret_cast<f32x4*>(a.post_out + tt * 4) = f32x4{post[0], post[1], post[2], post[3]};
+    st4f(a.pre_out + tt * 4, f32x4{pre[0], pre[1], pre[2], pre[3]});
+    st4f(a.post_out + tt * 4, f32x4{post[0], post[1], post[2], post[3]});
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<f32x4*>(a.comb_out + tt * 16 + 4 * j) =
-          f32x4{comb[4 * j], comb[4 * j + 1], comb[4 * j + 2], comb[4 * j + 3]};
+      st4f(a.comb_out + tt * 16 + 4 * j,
+           f32x4{comb[4 * j], comb[4 * j + 1], comb[4 * j + 2], comb[4 * j + 3]});
   }
 }
 
@@ -715,9 +743,11 @@ __device__ __forceinline__ u32x4 bload(rsrc_t r, uint32_t voff, uint32_t soff) {
 }
 template <int AUX>
 __device__ __forceinline__ void bstore(rsrc_t r, uint32_t voff, uint32_t soff, u32x4 v) {
+  store_pin();
   __builtin_amdgcn_raw_buffer_store_b128(
       __builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b128(r, 0, 0, 0)), v), r,
       (int)voff, (int)soff, AUX);
+  store_guard();
 }
 
 template <int CTRL>
@@ -1062,6 +1092,8 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_kernel(StepArgs a, int nt
 
 }  // namespace pipe
 
+#include "split_kernel.h"
+
 // ----- split / Sinkhorn on given mixes -------------------------------------------------
 
 __global__ __launch_bounds__(256) void sinkhorn4_kernel(const float* __restrict__ mixes,
@@ -1080,12 +1112,12 @@ __global__ __launch_bounds__(256) void sinkhorn4_kernel(const float* __restrict_
   }
   float pre[4], post[4], comb[16];
   split_sinkhorn_token(m, base, scale, iters, eps, pre, post, comb);
-  *reinterpret_cast<f32x4*>(pre_out + t * 4) = f32x4{pre[0], pre[1], pre[2], pre[3]};
-  *reinterpret_cast<f32x4*>(post_out + t * 4) = f32x4{post[0], post[1], post[2], post[3]};
+  st4f(pre_out + t * 4, f32x4{pre[0], pre[1], pre[2], pre[3]});
+  st4f(post_out + t * 4, f32x4{post[0], post[1], post[2], post[3]});
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    *reinterpret_cast<f32x4*>(comb_out + t * 16 + 4 * j) =
-        f32x4{comb[4 * j], comb[4 * j + 1], comb[4 * j + 2], comb[4 * j + 3]};
+    st4f(comb_out + t * 16 + 4 * j,
+         f32x4{comb[4 * j], comb[4 * j + 1], comb[4 * j + 2], comb[4 * j + 3]});
 }
 
 // ----- packing of the projection --------------------------------------------------------
@@ -1282,6 +1314,49 @@ mhc_status device_cu_count(int* out) {
   return MHC_OK;
 }
 
+// Feature-split kernel: applicable to bf16 streams with d in {2048, 3072, 4096,
+// 5120} on a device with at least 32 CUs that supports cooperative launches.
+// groups = 0 when not applicable.
+mhc_status split_groups(int32_t dtype, int32_t d, int* groups) {
+  *groups = 0;
+  if (dtype != MHC_BF16 || d % 1024 != 0 || d < 2048 || d > 32 * fsplit::kMaxS) return MHC_OK;
+  int cus = 0;
+  mhc_status s = device_cu_count(&cus);
+  if (s != MHC_OK) return s;
+  if (cus < fsplit::kSlices) return MHC_OK;
+  int dev = 0, coop = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev);
+  if (e != hipSuccess) return fail(MHC_ERR_HIP, "cooperative-launch attribute: %s", hipGetErrorString(e));
+  if (!coop) return MHC_OK;
+  *groups = cus / fsplit::kSlices;
+  return MHC_OK;
+}
+
+mhc_status launch_split(const StepArgs& a, void* ws, int groups, hipStream_t stream) {
+  const int words = (int)(fsplit::mp_off(groups) / 4);
+  hipLaunchKernelGGL(fsplit::clear_kernel, dim3(1), dim3(256), 0, stream,
+                     static_cast<uint32_t*>(ws), words);
+  mhc_status s = launch_status("workspace clear kernel launch");
+  if (s != MHC_OK) return s;
+  fsplit::Args fs{static_cast<char*>(ws), groups, (int)((a.tokens + fsplit::kBatch - 1) / fsplit::kBatch)};
+  StepArgs args = a;
+  void* params[] = {&args, &fs};
+  const void* fn = nullptr;
+  switch (a.d / 32) {
+    case 64: fn = reinterpret_cast<const void*>(fsplit::split_kernel<1, false>); break;
+    case 96: fn = reinterpret_cast<const void*>(fsplit::split_kernel<1, true>); break;
+    case 128: fn = reinterpret_cast<const void*>(fsplit::split_kernel<2, false>); break;
+    case 160: fn = reinterpret_cast<const void*>(fsplit::split_kernel<2, true>); break;
+    default: return fail(MHC_ERR_UNSUPPORTED, "feature-split kernel: d = %d", a.d);
+  }
+  const hipError_t e = hipLaunchCooperativeKernel(fn, dim3((unsigned)(groups * fsplit::kSlices)),
+                                                  dim3(fsplit::kThreads), params, 0, stream);
+  if (e != hipSuccess)
+    return fail(MHC_ERR_HIP, "feature-split kernel cooperative launch: %s", hipGetErrorString(e));
+  return launch_status("feature-split kernel launch");
+}
+
 mhc_status launch_step(const StepArgs& a, int32_t dtype, int mode, hipStream_t stream,
                        const char* what) {
   const int nsteps = a.d / kStep;
@@ -1326,6 +1401,16 @@ int32_t mhc_d_granule(void) { return kStep; }
 
 int64_t mhc_wmix_packed_bytes(int32_t d, int32_t dtype) { return packed_bytes(d, dtype); }
 
+int64_t mhc_fused_step_workspace_bytes(int64_t tokens, int32_t d, int32_t dtype) {
+  if (tokens < 0 || d <= 0 || d % kStep != 0 || elem_size(dtype) == 0) {
+    fail(MHC_ERR_INVALID_ARG, "bad tokens (%lld), d (%d) or dtype (%d)", (long long)tokens, d, dtype);
+    return -1;
+  }
+  int groups = 0;
+  if (split_groups(dtype, d, &groups) != MHC_OK) return -1;
+  return groups > 0 ? fsplit::workspace_bytes(groups) : 0;
+}
+
 mhc_status mhc_pack_wmix(const float* w_mix, int32_t d, int32_t dtype, void* w_packed,
                          int64_t packed_bytes_given, mhc_stream_t stream) {
   const int64_t need = packed_bytes(d, dtype);
@@ -1354,8 +1439,8 @@ mhc_status mhc_fused_step(const void* x, const void* f, int32_t dtype, int64_t t
                           const void* w_packed, const float* base, const float* scale,
                           const float* gamma, int32_t sinkhorn_iters, float norm_eps,
                           float hc_eps, void* x_out, void* y_out, float* pre_out,
-                          float* post_out, float* comb_out, float* mix_out,
-                          mhc_stream_t stream) {
+                          float* post_out, float* comb_out, float* mix_out, void* workspace,
+                          int64_t workspace_bytes, mhc_stream_t stream) {
   mhc_status s = check_common(dtype, tokens, d, sinkhorn_iters, norm_eps, hc_eps);
   if (s != MHC_OK) return s;
   if (tokens == 0) return ok();
@@ -1382,8 +1467,30 @@ mhc_status mhc_fused_step(const void* x, const void* f, int32_t dtype, int64_t t
     s = check_spans(all, 14, mo, 1, nullptr, nullptr);
     if (s != MHC_OK) return s;
   }
+  int groups = 0;
+  if (workspace != nullptr) {
+    s = split_groups(dtype, d, &groups);
+    if (s != MHC_OK) return s;
+  }
+  if (groups > 0) {
+    const int64_t need = fsplit::workspace_bytes(groups);
+    if (workspace_bytes < need)
+      return fail(MHC_ERR_INVALID_ARG, "workspace holds %lld bytes, %lld needed",
+                  (long long)workspace_bytes, (long long)need);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+      return fail(MHC_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+    const Span wsp[] = {{"workspace", workspace, (uint64_t)need}};
+    Span all[15];
+    for (int i = 0; i < 9; ++i) all[i] = in[i];
+    for (int i = 0; i < 5; ++i) all[9 + i] = out[i];
+    int nall = 14;
+    if (mix_out != nullptr) all[nall++] = {"mix_out", mix_out, T * kMix * 4};
+    s = check_spans(all, nall, wsp, 1, nullptr, nullptr);
+    if (s != MHC_OK) return s;
+  }
   StepArgs a{x, f, pre_in, post_in, comb_in, w_packed, base, scale, gamma, x_out, y_out,
              pre_out, post_out, comb_out, mix_out, tokens, d, sinkhorn_iters, norm_eps, hc_eps};
+  if (groups > 0) return launch_split(a, workspace, groups, static_cast<hipStream_t>(stream));
   return launch_step(a, dtype, kFused, static_cast<hipStream_t>(stream), "fused step kernel launch");
 }
 

@@ -1,0 +1,601 @@
+// Feature-split fused step (bf16 streams, d = 32 * S with S = 64 * NR + 32 * TAIL,
+// NR >= 1, S <= 160): the kernel behind mhc_fused_step when a workspace is given.
+//
+// Included by mhc.hip (one translation unit); uses its helpers and the pipe::
+// buffer-instruction wrappers.
+//
+// Why a second kernel. The tile kernel re-reads the packed projection (three
+// bf16 terms of W, 20 KB per 32 features) from L2 for every 16-token tile:
+// twice the stream bytes through each CU's vector-memory path. Its lane layout
+// (16 token rows x 64 bytes per load instruction, the MFMA operand order) also
+// moves at most ~3 TB/s even as a plain copy, against ~4.3 TB/s for 4-8 rows x
+// 128-256 bytes. Here every CU owns one 32nd of the features for good:
+//
+//   * Workgroup (group g, slice c): g = blockIdx % G, c = blockIdx / G, with G
+//     groups of 32 workgroups. Slice c is features [c*S, (c+1)*S) of every
+//     stream row, F row, new-stream row and y row; its W slice (S/32 packed
+//     steps, 100 KB for S = 160) is loaded into LDS once and used for every
+//     token the group processes. Groups take 128-token batches b = g, g+G, ...;
+//     wave w of a workgroup owns tokens 16w .. 16w+15 of each batch.
+//   * Loads and stores move 8 token rows x 128 bytes per instruction ("half
+//     rounds" of 64 features); the S % 64 = 32 remainder ("tail", 16 rows x 64
+//     bytes) sits at the 128-byte-aligned end of the slice (first for odd c).
+//     New streams pass through a 2 KB per-wave LDS buffer per stream to reach
+//     the MFMA A-operand order (row = token, 8 consecutive features per lane).
+//   * Per token the slice yields 24 projection partials, sum x'^2 and sum h^2.
+//     They go to a workspace ring (kRing slots per group) with device-scope
+//     (sc1) stores; the last wave of a workgroup to finish a batch bumps the
+//     group's counter for that slot (one device-scope atomic per workgroup).
+//   * One batch later each wave waits for all 32 slices of the batch, sums the
+//     32 partial sums of h^2 of its 16 tokens and writes y for its slice from h
+//     kept in registers; one wave per workgroup (rotating) sums the partials of
+//     4 tokens of the batch and runs RMS scaling, split and the 4x4 Sinkhorn.
+//
+// Cross-workgroup protocol (correct wherever the workgroups run; the group ->
+// XCD mapping only matters for speed):
+//   * writer: exchange stores carry sc1, so they are written through to the
+//     device-coherent level; s_waitcnt vmcnt makes them complete before the
+//     wave's LDS increment; the wave that completes the workgroup's count
+//     issues a device-scope atomic add on the counter.
+//   * reader: polls the counter with device-scope loads until it reaches
+//     32 * (generation + 1), then reads the exchange with sc1 loads.
+//   * slots: a workgroup writes batch i's slot only after it has seen every
+//     workgroup of the group finish batch i-2, whose waves had all finished
+//     reading batch i-4 before that; four slots are therefore never read and
+//     written at once.
+//   * every wait is bounded: after kSpinLimit polls the wave sets the status
+//     word at workspace offset 0 and stops waiting (outputs are then invalid);
+//     later waits return at once once the status word is set.
+// All workgroups must be resident together: the host launches the kernel
+// cooperatively with one workgroup per CU.
+
+namespace fsplit {
+
+using pipe::bload;
+using pipe::bstore;
+using pipe::col_sum;
+using pipe::dpp;
+using pipe::kNT;
+using pipe::kOutOfRange;
+using pipe::make_rsrc;
+using pipe::quad_max;
+using pipe::quad_sum;
+using pipe::rsrc_t;
+
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kSlices = 32;                    // workgroups per group = feature slices
+constexpr int kBatch = kWaves * kTok;          // 128 tokens per batch
+constexpr int kRing = 4;                       // exchange slots per group
+constexpr int kRow = 28;                       // floats per token and slice: 24 mixes, x'^2, h^2, pad
+constexpr int kTiles = kTilesBf;
+constexpr int kCols = 3 * kMix;                // 72 packed columns in use
+constexpr int kMaxS = 160;                     // features per slice (d <= 5120)
+constexpr int kStepBytes = kStreams * kTiles * 1024;   // packed bytes per 32 features
+constexpr int kSC1 = 16;                       // cache-policy bit: device scope
+constexpr uint32_t kSpinLimit = 1u << 20;
+constexpr int kCtrStride = 128;                // bytes between counters
+constexpr int64_t kHdr = 256;                  // status word + padding
+
+constexpr int kRowRor2 = 0x122;                // DPP row rotate right by 2
+
+__host__ __device__ constexpr int64_t ctr_off(int g, int slot) {
+  return kHdr + ((int64_t)g * kRing + slot) * kCtrStride;
+}
+__host__ __device__ constexpr int64_t mp_off(int groups) {
+  return kHdr + (((int64_t)groups * kRing * kCtrStride + 255) / 256) * 256;
+}
+__host__ __device__ constexpr int64_t mp_slot_bytes() { return (int64_t)kSlices * kBatch * kRow * 4; }
+__host__ __device__ constexpr int64_t hs_off(int groups) {
+  return mp_off(groups) + (int64_t)groups * kRing * mp_slot_bytes();
+}
+__host__ __device__ constexpr int64_t hs_slot_bytes() { return (int64_t)kSlices * kBatch * 4; }
+__host__ __device__ constexpr int64_t workspace_bytes(int groups) {
+  return hs_off(groups) + (int64_t)groups * kRing * hs_slot_bytes();
+}
+
+// s_waitcnt with only vmcnt limited (gfx9 encoding: vmcnt[3:0], expcnt[6:4],
+// lgkmcnt[11:8], vmcnt[5:4] in [15:14]).
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+struct __align__(16) WaveSmem {
+  union {
+    struct {
+      u32x4 xs[2][kTok * 8];      // A-operand staging: [token][8 chunks of 16 B], swizzled
+      float coef[kTok][24];       // comb_in (16), post_in (4), pre_in (4) of the wave's tokens
+    } e;
+    float cst[kTok][kCols];       // projection partials before the hi/mid/lo sums
+  } u;
+  float rh[kTok];                 // 1/rms(h) of the wave's tokens
+};
+
+struct __align__(16) Smem {
+  u32x4 w[kMaxS / 32 * kStepBytes / 16];   // W slice, packed B-operand order
+  WaveSmem wv[kWaves];
+  float gamma[kMaxS];
+  uint32_t lcount[kRing];
+};
+
+struct Args {
+  char* ws;      // workspace (mhc_fused_step_workspace_bytes)
+  int groups;    // G
+  int nbatch;    // ceil(tokens / 128)
+};
+
+struct Items {   // one load group: 4 stream rows + the F row, 16 B per lane each
+  u32x4 x[4];
+  u32x4 f;
+};
+
+struct Rs {      // buffer resources of one wave's 16 tokens of one batch
+  rsrc_t x, f, xo, y, cb, po, pr;
+  int64_t t0;
+};
+
+struct Cf {      // raw coefficient loads of one batch (see store_coef)
+  u32x4 cb, po, pr;
+};
+
+__device__ __forceinline__ void bstore64(rsrc_t r, uint32_t voff, uint32_t soff, float a, float b) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 v = {__float_as_uint(a), __float_as_uint(b)};
+  store_pin();
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)voff, (int)soff, kSC1);
+  store_guard();
+}
+__device__ __forceinline__ void bstore32(rsrc_t r, uint32_t voff, uint32_t soff, float a) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(a), r, (int)voff, (int)soff, kSC1);
+}
+__device__ __forceinline__ f32x4 bload_sc1(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(f32x4, bload<kSC1>(r, voff, soff));
+}
+
+// Sum over the lanes l' == l (mod 2) of the wave (32 lanes).
+__device__ __forceinline__ float sum_same_parity(float v) {
+  v += dpp<pipe::kRowRor8>(v);
+  v += dpp<pipe::kRowRor4>(v);
+  v += dpp<kRowRor2>(v);
+  v += __shfl_xor(v, 16);
+  return v + __shfl_xor(v, 32);
+}
+
+// hc_post, sums of squares and hc_pre for the 8 features of one lane (the
+// arithmetic of the tile kernels): xo[k] = bf16(sum_j C[j][k] x_j + U[k] f),
+// h = bf16(sum_k P[k] xo[k]).
+__device__ __forceinline__ void elementwise(const Items& in, const float (&C)[4][4],
+                                            const float (&U)[4], const float (&P)[4],
+                                            u32x4 (&xo)[4], u32x4& hp, float& ss, float& hs) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float a0[4], a1[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      a0[j] = bf_lo(in.x[j][q]);
+      a1[j] = bf_hi(in.x[j][q]);
+    }
+    const float f0v = bf_lo(in.f[q]), f1v = bf_hi(in.f[q]);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float v0 = a0[0] * C[0][k];
+      float v1 = a1[0] * C[0][k];
+#pragma unroll
+      for (int j = 1; j < 4; ++j) {
+        v0 = fmaf(a0[j], C[j][k], v0);
+        v1 = fmaf(a1[j], C[j][k], v1);
+      }
+      v0 = fmaf(f0v, U[k], v0);
+      v1 = fmaf(f1v, U[k], v1);
+      xo[k][q] = pack_bf16x2(v0, v1);
+    }
+  }
+  float ssa = 0.f, ssb = 0.f, hsa = 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float r0[4], r1[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      r0[k] = bf_lo(xo[k][q]);
+      r1[k] = bf_hi(xo[k][q]);
+      ssa = fmaf(r0[k], r0[k], ssa);
+      ssb = fmaf(r1[k], r1[k], ssb);
+    }
+    float h0 = P[0] * r0[0], h1 = P[0] * r1[0];
+#pragma unroll
+    for (int k = 1; k < 4; ++k) {
+      h0 = fmaf(P[k], r0[k], h0);
+      h1 = fmaf(P[k], r1[k], h1);
+    }
+    const uint32_t w = pack_bf16x2(h0, h1);
+    hp[q] = w;
+    const float q0 = bf_lo(w), q1 = bf_hi(w);
+    hsa = fmaf(q0, q0, hsa);
+    hsa = fmaf(q1, q1, hsa);
+  }
+  ss += ssa + ssb;
+  hs += hsa;
+}
+
+// Bounded wait until the counter reaches `target`; false after a time-out or
+// when another wave has already timed out.
+__device__ __forceinline__ bool wait_count(char* ws, int64_t off, uint32_t target) {
+  uint32_t* status = reinterpret_cast<uint32_t*>(ws);
+  const uint32_t* ctr = reinterpret_cast<const uint32_t*>(ws + off);
+  for (uint32_t n = 0;; ++n) {
+    const uint32_t v = __builtin_amdgcn_readfirstlane(
+        __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    if (v >= target) return true;
+    const uint32_t st = __builtin_amdgcn_readfirstlane(
+        __hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    if (st != 0) return false;
+    if (n >= kSpinLimit) {
+      __hip_atomic_store(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
+template <int NR, bool TAIL>
+__global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
+  __shared__ Smem sm;
+  constexpr int S = 64 * NR + (TAIL ? 32 : 0);   // features per slice
+  constexpr int KS = S / 32;                      // packed steps per slice
+  constexpr int NI = 2 * NR + (TAIL ? 1 : 0);     // load groups per wave and batch
+  static_assert(NR >= 1 && S <= kMaxS, "slice shape");
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = fs.groups;
+  const int g = blockIdx.x % G;
+  const int c = blockIdx.x / G;
+  const int d = a.d;
+  const uint32_t d2 = (uint32_t)d * 2;
+  const uint32_t rowx = kStreams * d2, rowf = d2;
+  const bool odd = (c & 1) != 0;
+  const int fr0 = (TAIL && odd) ? 32 : 0;        // slice feature where the rounds start
+  const int ftl = odd ? 0 : S - 32;              // slice feature of the tail
+  const int f0 = c * S;                          // first feature of the slice
+  WaveSmem& wsm = sm.wv[wave];
+  char* const ws = fs.ws;
+  const rsrc_t wsr = make_rsrc(ws, (uint32_t)workspace_bytes(G));
+
+  {
+    const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.wpk) +
+                                                      (size_t)c * KS * kStepBytes);
+    for (int i = tid; i < KS * kStepBytes / 16; i += kThreads) sm.w[i] = src[i];
+    for (int i = tid; i < S; i += kThreads) sm.gamma[i] = a.gamma[f0 + i];
+    if (tid < kRing) sm.lcount[tid] = 0;
+  }
+  __syncthreads();
+
+  // lane maps: half rounds (token 8h + m8, 16 B chunk x8 of 64 features) and
+  // tail (token t16, chunk g16 of 32 features: the MFMA A-operand order)
+  const int m8 = lane >> 3, x8 = lane & 7;
+  const int t16 = lane & 15, g16 = lane >> 4;
+  uint32_t vxh[2], vfh[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    vxh[h] = (uint32_t)(8 * h + m8) * rowx + (uint32_t)(f0 + fr0) * 2 + 16u * x8;
+    vfh[h] = (uint32_t)(8 * h + m8) * rowf + (uint32_t)(f0 + fr0) * 2 + 16u * x8;
+  }
+  const uint32_t vxt = (uint32_t)t16 * rowx + (uint32_t)(f0 + ftl) * 2 + 16u * g16;
+  const uint32_t vft = (uint32_t)t16 * rowf + (uint32_t)(f0 + ftl) * 2 + 16u * g16;
+
+  auto batch_rs = [&](int i) {
+    const int64_t b = g + (int64_t)i * G;
+    const int64_t t0 = b * kBatch + (int64_t)wave * kTok;
+    const int ntok = (int)max<int64_t>(0, min<int64_t>(kTok, a.tokens - t0));
+    Rs r;
+    r.t0 = t0;
+    r.x = make_rsrc(static_cast<const char*>(a.x) + t0 * rowx, ntok * rowx);
+    r.f = make_rsrc(static_cast<const char*>(a.f) + t0 * rowf, ntok * rowf);
+    r.xo = make_rsrc(static_cast<char*>(a.x_out) + t0 * rowx, ntok * rowx);
+    r.y = make_rsrc(static_cast<char*>(a.y_out) + t0 * rowf, ntok * rowf);
+    r.cb = make_rsrc(a.comb_in + t0 * 16, ntok * 64);
+    r.po = make_rsrc(a.post_in + t0 * 4, ntok * 16);
+    r.pr = make_rsrc(a.pre_in + t0 * 4, ntok * 16);
+    return r;
+  };
+  auto load_half = [&](Items& it, const Rs& r, int rr, int h) {
+    const uint32_t col = 128u * rr;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) it.x[k] = bload<kNT>(r.x, vxh[h], col + k * d2);
+    it.f = bload<kNT>(r.f, vfh[h], col);
+  };
+  auto load_tail = [&](Items& it, const Rs& r) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) it.x[k] = bload<kNT>(r.x, vxt, k * d2);
+    it.f = bload<kNT>(r.f, vft, 0);
+  };
+  auto load_coef = [&](Cf& cf, const Rs& r) {
+    cf.cb = bload<0>(r.cb, 16u * lane, 0);
+    cf.po = bload<0>(r.po, lane < kTok ? 16u * lane : kOutOfRange, 0);
+    cf.pr = bload<0>(r.pr, lane < kTok ? 16u * lane : kOutOfRange, 0);
+  };
+  auto store_coef = [&](const Cf& cf) {
+    *reinterpret_cast<u32x4*>(&wsm.u.e.coef[lane >> 2][4 * (lane & 3)]) = cf.cb;
+    if (lane < kTok) {
+      *reinterpret_cast<u32x4*>(&wsm.u.e.coef[lane][16]) = cf.po;
+      *reinterpret_cast<u32x4*>(&wsm.u.e.coef[lane][20]) = cf.pr;
+    }
+  };
+  auto get_coef = [&](int tau, float (&C)[4][4], float (&U)[4], float (&P)[4]) {
+    const f32x4* row = reinterpret_cast<const f32x4*>(wsm.u.e.coef[tau]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 v = row[j];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) C[j][k] = v[k];
+    }
+    const f32x4 u = row[4], p = row[5];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      U[k] = u[k];
+      P[k] = p[k];
+    }
+  };
+  auto wlds = [&](int step, int k, int q) -> bf16x8 {
+    return __builtin_bit_cast(bf16x8, sm.w[((step * kStreams + k) * kTiles + q) * 64 + lane]);
+  };
+  // staging index of (token, 16-byte chunk) with the XOR swizzle that keeps
+  // both the row writes and the operand reads free of bank conflicts
+  auto sidx = [](int tok, int chunk) { return tok * 8 + (chunk ^ ((tok >> 1) & 7)); };
+
+  const int nbg = g < fs.nbatch ? (fs.nbatch - g + G - 1) / G : 0;
+
+  // ---- finish batch i: y of the wave's tokens, Sinkhorn of 4 tokens ----
+  auto finish = [&](int i, const Rs& r, const u32x4 (&hk)[NI]) {
+    const int slot = i % kRing;
+    const uint32_t target = (uint32_t)kSlices * (uint32_t)(i / kRing + 1);
+    wait_count(ws, ctr_off(g, slot), target);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);   // exchange loads stay behind the wait
+    __builtin_amdgcn_sched_barrier(0);
+    const int64_t slot_id = (int64_t)g * kRing + slot;
+    // sum of h^2 over the 32 slices for the wave's 16 tokens
+    {
+      const uint32_t off = (uint32_t)(hs_off(G) + slot_id * hs_slot_bytes()) +
+                           (uint32_t)(((lane >> 1) * kBatch + wave * kTok + 8 * (lane & 1)) * 4);
+      const f32x4 p0 = bload_sc1(wsr, off, 0), p1 = bload_sc1(wsr, off, 16);
+      float rh[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        rh[e] = rsqrtf(sum_same_parity(p0[e]) / (float)d + a.norm_eps);
+        rh[4 + e] = rsqrtf(sum_same_parity(p1[e]) / (float)d + a.norm_eps);
+      }
+      if (lane < 2) {
+        *reinterpret_cast<f32x4*>(&wsm.rh[8 * lane]) = f32x4{rh[0], rh[1], rh[2], rh[3]};
+        *reinterpret_cast<f32x4*>(&wsm.rh[8 * lane + 4]) = f32x4{rh[4], rh[5], rh[6], rh[7]};
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+    // y = bf16(gamma * (h * rh)) ([RN] RMSNorm) for the slice
+#pragma unroll
+    for (int j = 0; j < 2 * NR; ++j) {
+      const int rr = j >> 1, h = j & 1;
+      const float rhv = wsm.rh[8 * h + m8];
+      const u32x4 y = norm_bf(hk[j], sm.gamma, fr0 + 64 * rr + 8 * x8, rhv);
+      bstore<kNT>(r.y, vfh[h], 128u * rr, y);
+    }
+    if (TAIL) {
+      const u32x4 y = norm_bf(hk[NI - 1], sm.gamma, ftl + 8 * g16, wsm.rh[t16]);
+      bstore<kNT>(r.y, vft, 0, y);
+    }
+    // split + Sinkhorn of tokens 4c .. 4c+3 of the batch
+    if (wave == i % kWaves) {
+      const int sh = lane / 28, q = lane % 28;
+      const uint32_t base = (uint32_t)(mp_off(G) + slot_id * mp_slot_bytes()) +
+                            (uint32_t)((4 * c) * kRow * 4 + 16 * q);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+      for (int jj = 0; jj < 16; ++jj) {
+        const int s = 16 * sh + jj;
+        const uint32_t off = lane < 56 ? base + (uint32_t)(s * kBatch * kRow * 4) : kOutOfRange;
+        acc += bload_sc1(wsr, off, 0);
+      }
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = acc[e] + __shfl(acc[e], min(lane + 28, 63));
+      // lane q < 28 now holds floats 4(q%7) .. 4(q%7)+3 of token q/7
+      const int tt = lane >> 4, e = lane & 15;
+      auto pick = [&](int src, int el) {
+        const float w0 = __shfl(v[0], src), w1 = __shfl(v[1], src);
+        const float w2 = __shfl(v[2], src), w3 = __shfl(v[3], src);
+        return el == 0 ? w0 : (el == 1 ? w1 : (el == 2 ? w2 : w3));
+      };
+      const float msum_c = pick(7 * tt + 2 + (e >> 2), e & 3);   // mixes slot 8 + e
+      const float msum_p = pick(7 * tt + ((e & 7) >> 2), e & 3); // mixes slot e (e < 8)
+      const float ssum = __shfl(v[0], 7 * tt + 6);                // sum of x'^2
+      const float rr = rsqrtf(ssum / (float)(kStreams * d) + a.norm_eps);
+      const float mc = msum_c * rr, mp = msum_p * rr;
+      const int64_t t = (g + (int64_t)i * G) * kBatch + 4 * c + tt;
+      const bool tok_ok = t < a.tokens;
+      if (tok_ok && a.mix_out != nullptr) {
+        a.mix_out[t * kMix + 8 + e] = mc;
+        if (e < 8) a.mix_out[t * kMix + e] = mp;
+      }
+      const float s0 = a.scale[0], s1 = a.scale[1], s2 = a.scale[2];
+      const float eps = a.hc_eps;
+      if (tok_ok && e < 4) a.pre_out[t * 4 + e] = sigmoidf(mp * s0 + a.base[e]) + eps;
+      if (tok_ok && e >= 4 && e < 8)
+        a.post_out[t * 4 + (e - 4)] = 2.0f * sigmoidf(mp * s1 + a.base[e]);
+      float cv = mc * s2 + a.base[8 + e];
+      cv = expf(cv - quad_max(cv));
+      cv = cv / quad_sum(cv) + eps;
+      cv = cv * __builtin_amdgcn_rcpf(col_sum(cv) + eps);
+      for (int it = 1; it < a.iters; ++it) {
+        cv = cv * __builtin_amdgcn_rcpf(quad_sum(cv) + eps);
+        cv = cv * __builtin_amdgcn_rcpf(col_sum(cv) + eps);
+      }
+      if (tok_ok) a.comb_out[t * 16 + e] = cv;
+    }
+  };
+
+  Rs rcur = batch_rs(0), rprev = rcur;
+  Cf cf;
+  Items bufA, bufB, bufT;
+  u32x4 hcur[NI], hprev[NI];
+  if (nbg > 0) {
+    load_coef(cf, rcur);
+    load_half(bufA, rcur, 0, 0);
+  }
+
+  for (int i = 0; i < nbg; ++i) {
+    store_coef(cf);
+    __builtin_amdgcn_wave_barrier();
+    f32x4 acc[kTiles];
+#pragma unroll
+    for (int q = 0; q < kTiles; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float ssA[2] = {0.f, 0.f}, hsA[2] = {0.f, 0.f}, ssT = 0.f, hsT = 0.f;
+
+#pragma unroll
+    for (int rr = 0; rr < NR; ++rr) {
+      u32x4 xo0[4], xo1[4];
+      float C[4][4], U[4], P[4];
+      // phases are fenced so the compiler keeps every load group's wait at
+      // its consumer (vmcnt retires in order)
+      load_half(bufB, rcur, rr, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      get_coef(m8, C, U, P);
+      elementwise(bufA, C, U, P, xo0, hcur[2 * rr], ssA[0], hsA[0]);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) bstore<0>(rcur.xo, vxh[0], 128u * rr + k * d2, xo0[k]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (rr + 1 < NR) load_half(bufA, rcur, rr + 1, 0);
+      else if (TAIL) load_tail(bufT, rcur);
+      __builtin_amdgcn_sched_barrier(0);
+      get_coef(8 + m8, C, U, P);
+      elementwise(bufB, C, U, P, xo1, hcur[2 * rr + 1], ssA[1], hsA[1]);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) bstore<0>(rcur.xo, vxh[1], 128u * rr + k * d2, xo1[k]);
+      __builtin_amdgcn_sched_barrier(0);
+      // new streams of the two halves -> A operands, 2 K-steps x 4 streams
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        u32x4* buf = wsm.u.e.xs[k & 1];
+        buf[sidx(m8, x8)] = xo0[k];
+        buf[sidx(8 + m8, x8)] = xo1[k];
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int q2 = 0; q2 < 2; ++q2) {
+          const bf16x8 A = __builtin_bit_cast(bf16x8, buf[sidx(t16, 4 * q2 + g16)]);
+          const int step = fr0 / 32 + 2 * rr + q2;
+#pragma unroll
+          for (int q = 0; q < kTiles; ++q)
+            acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, wlds(step, k, q), acc[q], 0, 0, 0);
+        }
+        __builtin_amdgcn_wave_barrier();
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (TAIL) {
+      u32x4 xot[4];
+      float C[4][4], U[4], P[4];
+      get_coef(t16, C, U, P);
+      elementwise(bufT, C, U, P, xot, hcur[NI - 1], ssT, hsT);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) bstore<0>(rcur.xo, vxt, k * d2, xot[k]);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const bf16x8 A = __builtin_bit_cast(bf16x8, xot[k]);
+#pragma unroll
+        for (int q = 0; q < kTiles; ++q)
+          acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, wlds(ftl / 32, k, q), acc[q], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // ---- publish the slice's per-token partials of batch i ----
+    {
+      // sums of squares: half rounds over the 8 lanes of a token, tail over
+      // the 4 lanes of a token
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        ssA[h] = quad_sum(ssA[h]);
+        ssA[h] += __shfl_xor(ssA[h], 4);
+        hsA[h] = quad_sum(hsA[h]);
+        hsA[h] += __shfl_xor(hsA[h], 4);
+      }
+      if (TAIL) {
+        ssT += __shfl_xor(ssT, 16);
+        ssT += __shfl_xor(ssT, 32);
+        hsT += __shfl_xor(hsT, 16);
+        hsT += __shfl_xor(hsT, 32);
+      }
+      const int u = lane >> 2;   // token this lane publishes
+      const int src = 8 * (u & 7);
+      const float s0 = __shfl(ssA[0], src), s1 = __shfl(ssA[1], src);
+      const float h0 = __shfl(hsA[0], src), h1 = __shfl(hsA[1], src);
+      float ssu = u < 8 ? s0 : s1, hsu = u < 8 ? h0 : h1;
+      if (TAIL) {
+        ssu += __shfl(ssT, u);
+        hsu += __shfl(hsT, u);
+      }
+      // projection partials -> per-token rows, hi + mid + lo
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int q = 0; q < kTiles; ++q) {
+        const int col = 16 * q + t16;
+        if (col < kCols) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) wsm.u.cst[4 * g16 + e][col] = acc[q][e];
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+      float mv[6];
+#pragma unroll
+      for (int jj = 0; jj < 6; ++jj) {
+        const int row = 6 * (lane & 3) + jj;
+        mv[jj] = (wsm.u.cst[u][row] + wsm.u.cst[u][kMix + row]) + wsm.u.cst[u][2 * kMix + row];
+      }
+      __builtin_amdgcn_wave_barrier();
+      const int slot = i % kRing;
+      const int64_t slot_id = (int64_t)g * kRing + slot;
+      const uint32_t row_off = (uint32_t)(mp_off(G) + slot_id * mp_slot_bytes()) +
+                               (uint32_t)(((c * kBatch) + wave * kTok + u) * kRow * 4);
+      const uint32_t lo = 24u * (lane & 3);
+      bstore64(wsr, row_off + lo, 0, mv[0], mv[1]);
+      bstore64(wsr, row_off + lo + 8, 0, mv[2], mv[3]);
+      bstore64(wsr, row_off + lo + 16, 0, mv[4], mv[5]);
+      if ((lane & 3) == 0) {
+        bstore64(wsr, row_off + 96, 0, ssu, hsu);
+        bstore32(wsr, (uint32_t)(hs_off(G) + slot_id * hs_slot_bytes()) +
+                          (uint32_t)((c * kBatch + wave * kTok + u) * 4),
+                 0, hsu);
+      }
+
+      // next batch's first loads (8 of them, empty ranges past the end), then
+      // wait for everything issued before them: the exchange stores included
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_sched_barrier(0);
+      const Rs rnext = batch_rs(i + 1);
+      load_coef(cf, rnext);
+      load_half(bufA, rnext, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(8));
+      __builtin_amdgcn_sched_barrier(0);
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      uint32_t old = 0;
+      if (lane == 0)
+        old = __hip_atomic_fetch_add(&sm.lcount[slot], 1u, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_WORKGROUP);
+      old = __builtin_amdgcn_readfirstlane(old);
+      if (old % kWaves == kWaves - 1 && lane == 0)
+        __hip_atomic_fetch_add(reinterpret_cast<uint32_t*>(ws + ctr_off(g, slot)), 1u,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+      if (i > 0) finish(i - 1, rprev, hprev);
+      rprev = rcur;
+      rcur = rnext;
+#pragma unroll
+      for (int j = 0; j < NI; ++j) hprev[j] = hcur[j];
+    }
+  }
+  if (nbg > 0) finish(nbg - 1, rprev, hprev);
+}
+
+__global__ __launch_bounds__(256) void clear_kernel(uint32_t* p, int words) {
+  for (int i = threadIdx.x; i < words; i += 256) p[i] = 0u;
+}
+
+}  // namespace fsplit

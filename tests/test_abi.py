@@ -27,7 +27,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for fn in ("mhc_fused_step", "mhc_mixes", "mhc_sinkhorn4", "mhc_pack_wmix",
                "mhc_wmix_packed_bytes", "mhc_status_string", "mhc_last_error",
-               "mhc_abi_version", "mhc_d_granule"):
+               "mhc_abi_version", "mhc_d_granule", "mhc_fused_step_workspace_bytes"):
         assert fn in names
 
 
@@ -39,7 +39,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_granule_and_status_strings():
-    assert binding.abi_version() == 1
+    assert binding.abi_version() == 2
     assert binding.d_granule() == 32
     lib = binding.load()
     assert lib.mhc_status_string(0) == b"MHC_OK"
@@ -87,7 +87,7 @@ def _call(**over):
                 base=p["base"], scale=p["scale"], gamma=p["gamma"], iters=20, norm_eps=1e-6,
                 hc_eps=1e-6, x_out=p["x_out"], y_out=p["y_out"], pre_out=p["pre_out"],
                 post_out=p["post_out"], comb_out=p["comb_out"], mix_out=p["mix_out"],
-                stream=None)
+                workspace=None, workspace_bytes=0, stream=None)
     args.update(over)
     lib = binding.load()
     return lib.mhc_fused_step(*args.values())
@@ -115,6 +115,13 @@ def test_fused_step_rejects_bad_arguments(over, needle):
     st = _call(**over)
     assert st == binding.MHC_ERR_INVALID_ARG
     assert needle in binding.last_error()
+
+
+def test_workspace_bytes_rejects_bad_arguments():
+    lib = binding.load()
+    for args in ((-1, 5120, binding.MHC_BF16), (64, 48, binding.MHC_BF16), (64, 5120, 9)):
+        assert lib.mhc_fused_step_workspace_bytes(*args) == -1
+        assert "bad tokens" in binding.last_error()
 
 
 def test_fused_step_zero_tokens_is_a_no_op():

@@ -1,0 +1,156 @@
+"""GPU parity of the feature-split fused-step kernel (path="split").
+
+Each compute unit owns 1/32 of the features; workgroups exchange per-token
+partial sums through a workspace ring. The cases cover every slice shape the
+kernel is built for (d = 2048, 3072, 4096, 5120), token counts from one token
+to enough batches that every exchange slot is reused several times, ragged
+batches, in-place updates, guard bands, repeated calls on one workspace, and
+agreement with the tile kernel (the new streams must match bit for bit: their
+arithmetic is the same; y and the coefficients differ only in summation
+order). Every call's status word must read 0 (no wait gave up).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import stream_hyper_connections_amd as mhc
+from stream_hyper_connections_amd import workloads as wl
+from tests.cases import make_case, run_step, to_dev
+from tests.parity import check_step
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def _run(case, **kw):
+    ws = torch.empty(mhc.fused_step_workspace_bytes(len(case["x"]), case["x"].shape[2], "bf16"),
+                     dtype=torch.uint8, device="cuda")
+    assert ws.numel() > 0
+    out, dev = run_step(case, path="split", workspace=ws, **kw)
+    assert mhc.split_status(ws) == 0, "a cross-workgroup wait gave up"
+    return out, dev
+
+
+SPLIT_CASES = [
+    (5120, 1),       # one token: one wave of one group works
+    (5120, 37),      # ragged first batch
+    (5120, 128),     # exactly one batch
+    (5120, 1000),    # fewer batches than groups for some groups
+    (5120, 4133),    # every group, ring not yet wrapped, ragged
+    (5120, 9000),    # ring slots reused, ragged last batch
+    (4096, 300),     # no tail
+    (3072, 257),     # one round + tail
+    (2048, 513),     # one round, no tail
+]
+
+
+@pytest.mark.parametrize("d,t", SPLIT_CASES)
+def test_split_parity(d, t):
+    _log(f"split d={d} T={t}")
+    w = wl.Workload(400 + d % 89 + t % 7, "split", t, d, "bf16")
+    case = make_case(w)
+    out, _ = _run(case)
+    o = check_step(case, out, "bf16")
+    _log(f"  ties in new streams: {o['n_ties']}")
+
+
+def test_split_matches_tile_kernel():
+    w = wl.Workload(450, "split_vs_tile", 700, 5120, "bf16")
+    case = make_case(w)
+    a, _ = _run(case)
+    b, _ = run_step(case, path="tile")
+    assert torch.equal(a["x_out"], b["x_out"])
+    ya, yb = a["y"].float(), b["y"].float()
+    ulp = torch.maximum(ya.abs(), yb.abs()) * 2.0 ** -7 + 1e-30
+    assert ((ya - yb).abs() <= ulp).all()
+    for k in ("pre", "post", "comb", "mix"):
+        np.testing.assert_allclose(a[k].numpy(), b[k].numpy(), rtol=0, atol=2e-5)
+
+
+def test_split_in_place_and_deterministic():
+    w = wl.Workload(451, "split_inplace", 555, 5120, "bf16")
+    case = make_case(w)
+    ref, dev = _run(case)
+    again, _ = _run(case)
+    for k in ref:
+        if ref[k] is not None:
+            assert torch.equal(ref[k], again[k]), k
+    x_dev = dev["x"].clone()
+    wp = mhc.pack_wmix(dev["w_mix"], "bf16")
+    ws = torch.empty(mhc.fused_step_workspace_bytes(555, 5120, "bf16"), dtype=torch.uint8,
+                     device="cuda")
+    out = mhc.fused_step(x_dev, dev["f"], dev["pre"], dev["post"], dev["comb"], wp, dev["base"],
+                         dev["scale"], dev["gamma"], x_out=x_dev, want_mix=True, path="split",
+                         workspace=ws)
+    torch.cuda.synchronize()
+    assert mhc.split_status(ws) == 0
+    for k in ("x_out", "y", "pre", "post", "comb", "mix"):
+        assert torch.equal(out[k].cpu(), ref[k]), k
+
+
+def test_split_guard_bands_untouched():
+    t, d, gpad = 21, 2048, 64
+    w = wl.Workload(452, "split_guard", t, d, "bf16")
+    case = make_case(w)
+    dev = {k: to_dev(case[k]) for k in ("x", "f", "pre", "post", "comb", "w_mix", "base",
+                                        "scale", "gamma")}
+    wp = mhc.pack_wmix(dev["w_mix"], "bf16")
+
+    def guarded(n, dtype):
+        buf = torch.full((n + 2 * gpad,), float("nan"), dtype=dtype, device="cuda")
+        return buf, buf[gpad:gpad + n]
+
+    bx, vx = guarded(t * 4 * d, torch.bfloat16)
+    by, vy = guarded(t * d, torch.bfloat16)
+    bp, vp = guarded(t * 4, torch.float32)
+    bu, vu = guarded(t * 4, torch.float32)
+    bc, vc = guarded(t * 16, torch.float32)
+    bm, vm = guarded(t * 24, torch.float32)
+    ws = torch.empty(mhc.fused_step_workspace_bytes(t, d, "bf16"), dtype=torch.uint8,
+                     device="cuda")
+    out = mhc.fused_step(dev["x"], dev["f"], dev["pre"], dev["post"], dev["comb"], wp, dev["base"],
+                         dev["scale"], dev["gamma"], x_out=vx.view(t, 4, d), y_out=vy.view(t, d),
+                         pre_out=vp.view(t, 4), post_out=vu.view(t, 4), comb_out=vc.view(t, 4, 4),
+                         mix_out=vm.view(t, 24), path="split", workspace=ws)
+    torch.cuda.synchronize()
+    assert mhc.split_status(ws) == 0
+    for buf, view in ((bx, vx), (by, vy), (bp, vp), (bu, vu), (bc, vc), (bm, vm)):
+        assert torch.isnan(buf[:gpad].float()).all() and torch.isnan(buf[-gpad:].float()).all()
+        assert not torch.isnan(view.float()).any()
+    check_step(case, {k: (v.cpu() if v is not None else None) for k, v in out.items()}, "bf16")
+
+
+def test_split_repeated_calls_share_a_workspace():
+    """Two calls in a row on one workspace, the second smaller: counters and the
+    status word are reset by every call."""
+    ws = torch.empty(mhc.fused_step_workspace_bytes(1, 5120, "bf16"), dtype=torch.uint8,
+                     device="cuda")
+    for t, seed in ((3000, 453), (200, 454)):
+        case = make_case(wl.Workload(seed, "split_repeat", t, 5120, "bf16"))
+        out, _ = run_step(case, path="split", workspace=ws)
+        assert mhc.split_status(ws) == 0
+        check_step(case, out, "bf16")
+
+
+def test_split_workspace_validation():
+    t, d = 64, 2048
+    x = torch.zeros((t, 4, d), dtype=torch.bfloat16, device="cuda")
+    f = torch.zeros((t, d), dtype=torch.bfloat16, device="cuda")
+    wp = mhc.pack_wmix(torch.zeros((24, 4 * d), device="cuda"), "bf16")
+    z = torch.zeros((t, 4), device="cuda")
+    need = mhc.fused_step_workspace_bytes(t, d, "bf16")
+    args = (x, f, z, z, torch.zeros((t, 4, 4), device="cuda"), wp, torch.zeros(24, device="cuda"),
+            torch.ones(3, device="cuda"), torch.ones(d, device="cuda"))
+    small = torch.empty(need - 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(mhc.MhcError, match="workspace holds"):
+        mhc.fused_step(*args, path="split", workspace=small)
+    big = torch.empty(need + 512, dtype=torch.uint8, device="cuda")
+    with pytest.raises(mhc.MhcError, match="256-byte aligned"):
+        mhc.fused_step(*args, path="split", workspace=big[16:])
+    assert mhc.fused_step_workspace_bytes(t, 5120, "f32") == 0
+    assert mhc.fused_step_workspace_bytes(t, 1024, "bf16") == 0
+    assert mhc.fused_step_workspace_bytes(t, 6144, "bf16") == 0
