@@ -60,17 +60,26 @@ __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 
 // Two floats -> two bf16 (round to nearest even), `a` in the low half.
 // float -> bf16 bits, round to nearest even, placed in the HIGH half of the
 // returned word (low half is garbage); every NaN becomes the quiet NaN 0x7fc0.
-// Integer arithmetic on purpose: the hardware packed conversion instruction
-// returned wrong halves for some lanes now and then inside the pipelined
-// kernel, which this form avoids.
 __device__ __forceinline__ uint32_t rne_bf16_hi(float x) {
   const uint32_t u = __float_as_uint(x);
   const uint32_t r = u + 0x7fffu + ((u >> 16) & 1u);
   return x != x ? 0x7fc00000u : r;
 }
 
-// Two floats -> two bf16 (round to nearest even), `a` in the low half.
+#ifndef MHC_HW_BF16
+#define MHC_HW_BF16 1
+#endif
+
+// Two floats -> two bf16 (round to nearest even), `a` in the low half: the
+// packed hardware conversion (v_cvt_pk_bf16_f32, round to nearest even in the
+// default mode), or the integer form above.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  if (MHC_HW_BF16) {
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const f32x2_t v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+  }
   return __builtin_amdgcn_perm(rne_bf16_hi(b), rne_bf16_hi(a), 0x07060302u);
 }
 
@@ -80,9 +89,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 // some lanes (lanes 12-15 of each 16-lane row, the words rewritten first,
 // intermittently). A few wait states right after the store, with the
 // scheduler kept from moving anything across, avoid it.
+#ifndef MHC_GUARD_NOP
+#define MHC_GUARD_NOP 4
+#endif
+#define MHC_STR2(x) #x
+#define MHC_STR(x) MHC_STR2(x)
 __device__ __forceinline__ void store_guard() {
   __builtin_amdgcn_sched_barrier(0);
-  __asm__ volatile("s_nop 4");
+  __asm__ volatile("s_nop " MHC_STR(MHC_GUARD_NOP));
   __builtin_amdgcn_sched_barrier(0);
 }
 // pins the store that follows in place (nothing is scheduled across it)

@@ -28,8 +28,9 @@
 //     group's counter for that slot (one device-scope atomic per workgroup).
 //   * One batch later each wave waits for all 32 slices of the batch, sums the
 //     32 partial sums of h^2 of its 16 tokens and writes y for its slice from h
-//     kept in registers; one wave per workgroup (rotating) sums the partials of
-//     4 tokens of the batch and runs RMS scaling, split and the 4x4 Sinkhorn.
+//     kept in registers; four waves per workgroup (alternating halves) each sum
+//     the 32 partial rows of one of the workgroup's 4 tokens of the batch and
+//     run RMS scaling, split and the 4x4 Sinkhorn for it.
 //
 // Cross-workgroup protocol (correct wherever the workgroups run; the group ->
 // XCD mapping only matters for speed):
@@ -67,7 +68,7 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kSlices = 32;                    // workgroups per group = feature slices
 constexpr int kBatch = kWaves * kTok;          // 128 tokens per batch
 constexpr int kRing = 4;                       // exchange slots per group
-constexpr int kRow = 28;                       // floats per token and slice: 24 mixes, x'^2, h^2, pad
+constexpr int kRow = 32;                       // floats per token and slice: 24 mixes, x'^2, h^2, pad
 constexpr int kTiles = kTilesBf;
 constexpr int kCols = 3 * kMix;                // 72 packed columns in use
 constexpr int kMaxS = 160;                     // features per slice (d <= 5120)
@@ -78,6 +79,22 @@ constexpr int kCtrStride = 128;                // bytes between counters
 constexpr int64_t kHdr = 256;                  // status word + padding
 
 constexpr int kRowRor2 = 0x122;                // DPP row rotate right by 2
+
+// cache policies: stream loads, new-stream stores, y stores
+// raise the batch count right after the exchange stores (1) or after the
+// next batch's wait, which covers them for free (0)
+#ifndef FS_COUNT_EARLY
+#define FS_COUNT_EARLY 1
+#endif
+#ifndef FS_LOAD_AUX
+#define FS_LOAD_AUX 2
+#endif
+#ifndef FS_XO_AUX
+#define FS_XO_AUX 0
+#endif
+#ifndef FS_Y_AUX
+#define FS_Y_AUX 2
+#endif
 
 __host__ __device__ constexpr int64_t ctr_off(int g, int slot) {
   return kHdr + ((int64_t)g * kRing + slot) * kCtrStride;
@@ -224,9 +241,11 @@ __device__ __forceinline__ bool wait_count(char* ws, int64_t off, uint32_t targe
     const uint32_t v = __builtin_amdgcn_readfirstlane(
         __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
     if (v >= target) return true;
-    const uint32_t st = __builtin_amdgcn_readfirstlane(
-        __hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-    if (st != 0) return false;
+    if ((n & 31) == 31) {
+      const uint32_t st = __builtin_amdgcn_readfirstlane(
+          __hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      if (st != 0) return false;
+    }
     if (n >= kSpinLimit) {
       __hip_atomic_store(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       return false;
@@ -300,13 +319,13 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
   auto load_half = [&](Items& it, const Rs& r, int rr, int h) {
     const uint32_t col = 128u * rr;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) it.x[k] = bload<kNT>(r.x, vxh[h], col + k * d2);
-    it.f = bload<kNT>(r.f, vfh[h], col);
+    for (int k = 0; k < 4; ++k) it.x[k] = bload<FS_LOAD_AUX>(r.x, vxh[h], col + k * d2);
+    it.f = bload<FS_LOAD_AUX>(r.f, vfh[h], col);
   };
   auto load_tail = [&](Items& it, const Rs& r) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) it.x[k] = bload<kNT>(r.x, vxt, k * d2);
-    it.f = bload<kNT>(r.f, vft, 0);
+    for (int k = 0; k < 4; ++k) it.x[k] = bload<FS_LOAD_AUX>(r.x, vxt, k * d2);
+    it.f = bload<FS_LOAD_AUX>(r.f, vft, 0);
   };
   auto load_coef = [&](Cf& cf, const Rs& r) {
     cf.cb = bload<0>(r.cb, 16u * lane, 0);
@@ -345,18 +364,57 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
   const int nbg = g < fs.nbatch ? (fs.nbatch - g + G - 1) / G : 0;
 
   // ---- finish batch i: y of the wave's tokens, Sinkhorn of 4 tokens ----
-  auto finish = [&](int i, const Rs& r, const u32x4 (&hk)[NI]) {
+  // The wave's exchange stores of batch i are complete: count them in LDS; the
+  // workgroup's eighth count raises the group counter of the slot.
+  auto count_batch = [&](int i) {
+    const int slot = i % kRing;
+    uint32_t old = 0;
+    if (lane == 0)
+      old = __hip_atomic_fetch_add(&sm.lcount[slot], 1u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+    old = __builtin_amdgcn_readfirstlane(old);
+    if (old % kWaves == kWaves - 1 && lane == 0)
+      __hip_atomic_fetch_add(reinterpret_cast<uint32_t*>(ws + ctr_off(g, slot)), 1u,
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+
+  // finish(i, ...) also counts batch i+1 (count_next): its exchange stores were
+  // issued before the loads of sum h^2 below, so once those loads have
+  // returned (vector memory retires in order) the stores are complete too.
+  auto finish = [&](int i, const Rs& r, const u32x4 (&hk)[NI], bool count_next) {
     const int slot = i % kRing;
     const uint32_t target = (uint32_t)kSlices * (uint32_t)(i / kRing + 1);
     wait_count(ws, ctr_off(g, slot), target);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);   // exchange loads stay behind the wait
     __builtin_amdgcn_sched_barrier(0);
     const int64_t slot_id = (int64_t)g * kRing + slot;
-    // sum of h^2 over the 32 slices for the wave's 16 tokens
+    // sum of h^2 over the 32 slices for the wave's 16 tokens: lane l reads
+    // slice l/2, tokens 8(l&1) .. 8(l&1)+7
+    const uint32_t hoff = (uint32_t)(hs_off(G) + slot_id * hs_slot_bytes()) +
+                          (uint32_t)(((lane >> 1) * kBatch + wave * kTok + 8 * (lane & 1)) * 4);
+    const f32x4 p0 = bload_sc1(wsr, hoff, 0), p1 = bload_sc1(wsr, hoff, 16);
+    // waves 4(i&1) .. 4(i&1)+3 each take one of the workgroup's 4 tokens of
+    // the batch for the split and Sinkhorn; their 4 partial loads per lane
+    // (lane: 16-byte chunk l&7 of the token row, slices l>>3 + 8j) follow at
+    // once so their latency hides behind the y work (empty for other waves)
+    const bool sk = (wave >> 2) == (i & 1);
+    f32x4 sk_part[4];
     {
-      const uint32_t off = (uint32_t)(hs_off(G) + slot_id * hs_slot_bytes()) +
-                           (uint32_t)(((lane >> 1) * kBatch + wave * kTok + 8 * (lane & 1)) * 4);
-      const f32x4 p0 = bload_sc1(wsr, off, 0), p1 = bload_sc1(wsr, off, 16);
+      const uint32_t base = (uint32_t)(mp_off(G) + slot_id * mp_slot_bytes()) +
+                            (uint32_t)(((4 * c + (wave & 3)) * kRow + 4 * (lane & 7)) * 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        sk_part[j] = bload_sc1(
+            wsr, sk ? base + (uint32_t)(((lane >> 3) + 8 * j) * kBatch * kRow * 4) : kOutOfRange, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    {
+      if (count_next) {
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(4));
+        __builtin_amdgcn_sched_barrier(0);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        count_batch(i + 1);
+      }
       float rh[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -375,49 +433,46 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
       const int rr = j >> 1, h = j & 1;
       const float rhv = wsm.rh[8 * h + m8];
       const u32x4 y = norm_bf(hk[j], sm.gamma, fr0 + 64 * rr + 8 * x8, rhv);
-      bstore<kNT>(r.y, vfh[h], 128u * rr, y);
+      bstore<FS_Y_AUX>(r.y, vfh[h], 128u * rr, y);
     }
     if (TAIL) {
       const u32x4 y = norm_bf(hk[NI - 1], sm.gamma, ftl + 8 * g16, wsm.rh[t16]);
-      bstore<kNT>(r.y, vft, 0, y);
+      bstore<FS_Y_AUX>(r.y, vft, 0, y);
     }
-    // split + Sinkhorn of tokens 4c .. 4c+3 of the batch
-    if (wave == i % kWaves) {
-      const int sh = lane / 28, q = lane % 28;
-      const uint32_t base = (uint32_t)(mp_off(G) + slot_id * mp_slot_bytes()) +
-                            (uint32_t)((4 * c) * kRow * 4 + 16 * q);
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-      for (int jj = 0; jj < 16; ++jj) {
-        const int s = 16 * sh + jj;
-        const uint32_t off = lane < 56 ? base + (uint32_t)(s * kBatch * kRow * 4) : kOutOfRange;
-        acc += bload_sc1(wsr, off, 0);
-      }
+    // split + Sinkhorn: token 4c + tt of the batch by wave 4 * (i & 1) + tt
+    if (sk) {
+      f32x4 acc = sk_part[0];
+#pragma unroll
+      for (int j = 1; j < 4; ++j) acc += sk_part[j];
       float v[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = acc[e] + __shfl(acc[e], min(lane + 28, 63));
-      // lane q < 28 now holds floats 4(q%7) .. 4(q%7)+3 of token q/7
-      const int tt = lane >> 4, e = lane & 15;
-      auto pick = [&](int src, int el) {
-        const float w0 = __shfl(v[0], src), w1 = __shfl(v[1], src);
-        const float w2 = __shfl(v[2], src), w3 = __shfl(v[3], src);
+      for (int e = 0; e < 4; ++e) {   // sum over the 8 slice groups (lanes l ^ 8, 16, 32)
+        float x = acc[e] + dpp<pipe::kRowRor8>(acc[e]);
+        x += __shfl_xor(x, 16);
+        v[e] = x + __shfl_xor(x, 32);
+      }
+      // every lane now holds floats 4(l&7) .. 4(l&7)+3 of the token's row
+      const int e = lane & 15;
+      auto pick = [&](int chunk, int el) {
+        const float w0 = __shfl(v[0], chunk), w1 = __shfl(v[1], chunk);
+        const float w2 = __shfl(v[2], chunk), w3 = __shfl(v[3], chunk);
         return el == 0 ? w0 : (el == 1 ? w1 : (el == 2 ? w2 : w3));
       };
-      const float msum_c = pick(7 * tt + 2 + (e >> 2), e & 3);   // mixes slot 8 + e
-      const float msum_p = pick(7 * tt + ((e & 7) >> 2), e & 3); // mixes slot e (e < 8)
-      const float ssum = __shfl(v[0], 7 * tt + 6);                // sum of x'^2
+      const float msum_c = pick(2 + (e >> 2), e & 3);   // mixes slot 8 + e
+      const float msum_p = pick((e & 7) >> 2, e & 3);   // mixes slot e (e < 8)
+      const float ssum = __shfl(v[0], 6);               // sum of x'^2
       const float rr = rsqrtf(ssum / (float)(kStreams * d) + a.norm_eps);
       const float mc = msum_c * rr, mp = msum_p * rr;
-      const int64_t t = (g + (int64_t)i * G) * kBatch + 4 * c + tt;
-      const bool tok_ok = t < a.tokens;
-      if (tok_ok && a.mix_out != nullptr) {
+      const int64_t t = (g + (int64_t)i * G) * kBatch + 4 * c + (wave & 3);
+      const bool st_ok = t < a.tokens && lane < 16;
+      if (st_ok && a.mix_out != nullptr) {
         a.mix_out[t * kMix + 8 + e] = mc;
         if (e < 8) a.mix_out[t * kMix + e] = mp;
       }
       const float s0 = a.scale[0], s1 = a.scale[1], s2 = a.scale[2];
       const float eps = a.hc_eps;
-      if (tok_ok && e < 4) a.pre_out[t * 4 + e] = sigmoidf(mp * s0 + a.base[e]) + eps;
-      if (tok_ok && e >= 4 && e < 8)
+      if (st_ok && e < 4) a.pre_out[t * 4 + e] = sigmoidf(mp * s0 + a.base[e]) + eps;
+      if (st_ok && e >= 4 && e < 8)
         a.post_out[t * 4 + (e - 4)] = 2.0f * sigmoidf(mp * s1 + a.base[e]);
       float cv = mc * s2 + a.base[8 + e];
       cv = expf(cv - quad_max(cv));
@@ -427,7 +482,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
         cv = cv * __builtin_amdgcn_rcpf(quad_sum(cv) + eps);
         cv = cv * __builtin_amdgcn_rcpf(col_sum(cv) + eps);
       }
-      if (tok_ok) a.comb_out[t * 16 + e] = cv;
+      if (st_ok) a.comb_out[t * 16 + e] = cv;
     }
   };
 
@@ -438,6 +493,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
   if (nbg > 0) {
     load_coef(cf, rcur);
     load_half(bufA, rcur, 0, 0);
+    load_half(bufB, rcur, 0, 1);
   }
 
   for (int i = 0; i < nbg; ++i) {
@@ -448,18 +504,18 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
     for (int q = 0; q < kTiles; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
     float ssA[2] = {0.f, 0.f}, hsA[2] = {0.f, 0.f}, ssT = 0.f, hsT = 0.f;
 
+    // both halves of round rr are in flight on entry; each half's buffer is
+    // refilled with the next round's half (or the tail) once consumed. Phases
+    // are fenced so every wait stays at its consumer (vmcnt retires in order).
 #pragma unroll
     for (int rr = 0; rr < NR; ++rr) {
       u32x4 xo0[4], xo1[4];
       float C[4][4], U[4], P[4];
-      // phases are fenced so the compiler keeps every load group's wait at
-      // its consumer (vmcnt retires in order)
-      load_half(bufB, rcur, rr, 1);
       __builtin_amdgcn_sched_barrier(0);
       get_coef(m8, C, U, P);
       elementwise(bufA, C, U, P, xo0, hcur[2 * rr], ssA[0], hsA[0]);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) bstore<0>(rcur.xo, vxh[0], 128u * rr + k * d2, xo0[k]);
+      for (int k = 0; k < 4; ++k) bstore<FS_XO_AUX>(rcur.xo, vxh[0], 128u * rr + k * d2, xo0[k]);
       __builtin_amdgcn_sched_barrier(0);
       if (rr + 1 < NR) load_half(bufA, rcur, rr + 1, 0);
       else if (TAIL) load_tail(bufT, rcur);
@@ -467,7 +523,9 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
       get_coef(8 + m8, C, U, P);
       elementwise(bufB, C, U, P, xo1, hcur[2 * rr + 1], ssA[1], hsA[1]);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) bstore<0>(rcur.xo, vxh[1], 128u * rr + k * d2, xo1[k]);
+      for (int k = 0; k < 4; ++k) bstore<FS_XO_AUX>(rcur.xo, vxh[1], 128u * rr + k * d2, xo1[k]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (rr + 1 < NR) load_half(bufB, rcur, rr + 1, 1);
       __builtin_amdgcn_sched_barrier(0);
       // new streams of the two halves -> A operands, 2 K-steps x 4 streams
 #pragma unroll
@@ -494,7 +552,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
       get_coef(t16, C, U, P);
       elementwise(bufT, C, U, P, xot, hcur[NI - 1], ssT, hsT);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) bstore<0>(rcur.xo, vxt, k * d2, xot[k]);
+      for (int k = 0; k < 4; ++k) bstore<FS_XO_AUX>(rcur.xo, vxt, k * d2, xot[k]);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const bf16x8 A = __builtin_bit_cast(bf16x8, xot[k]);
@@ -563,35 +621,32 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
                           (uint32_t)((c * kBatch + wave * kTok + u) * 4),
                  0, hsu);
       }
-
-      // next batch's first loads (8 of them, empty ranges past the end), then
-      // wait for everything issued before them: the exchange stores included
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       __builtin_amdgcn_sched_barrier(0);
+
+      // next batch's first round (both halves) and coefficients, empty ranges
+      // past the end: they fly while batch i-1 is finished
       const Rs rnext = batch_rs(i + 1);
       load_coef(cf, rnext);
       load_half(bufA, rnext, 0, 0);
+      load_half(bufB, rnext, 0, 1);
       __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(8));
-      __builtin_amdgcn_sched_barrier(0);
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      uint32_t old = 0;
-      if (lane == 0)
-        old = __hip_atomic_fetch_add(&sm.lcount[slot], 1u, __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_WORKGROUP);
-      old = __builtin_amdgcn_readfirstlane(old);
-      if (old % kWaves == kWaves - 1 && lane == 0)
-        __hip_atomic_fetch_add(reinterpret_cast<uint32_t*>(ws + ctr_off(g, slot)), 1u,
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-
-      if (i > 0) finish(i - 1, rprev, hprev);
+      if (i == 0 || FS_COUNT_EARLY) {
+        // wait for the exchange stores directly (13 loads were issued after
+        // them) and count the batch now
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(13));
+        __builtin_amdgcn_sched_barrier(0);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        count_batch(i);
+      }
+      if (i > 0) finish(i - 1, rprev, hprev, !FS_COUNT_EARLY);
       rprev = rcur;
       rcur = rnext;
 #pragma unroll
       for (int j = 0; j < NI; ++j) hprev[j] = hcur[j];
     }
   }
-  if (nbg > 0) finish(nbg - 1, rprev, hprev);
+  if (nbg > 0) finish(nbg - 1, rprev, hprev, false);
 }
 
 __global__ __launch_bounds__(256) void clear_kernel(uint32_t* p, int words) {
