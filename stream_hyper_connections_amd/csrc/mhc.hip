@@ -1328,43 +1328,70 @@ mhc_status device_cu_count(int* out) {
   return MHC_OK;
 }
 
-// Feature-split kernel: applicable to bf16 streams with d in {2048, 3072, 4096,
-// 5120} on a device with at least 32 CUs that supports cooperative launches.
-// groups = 0 when not applicable.
-mhc_status split_groups(int32_t dtype, int32_t d, int* groups) {
-  *groups = 0;
-  if (dtype != MHC_BF16 || d % 1024 != 0 || d < 2048 || d > 32 * fsplit::kMaxS) return MHC_OK;
+// Feature-split kernel geometry: `ns` workgroups per group, each owning S = d/ns
+// features, and `groups` groups (one workgroup per compute unit). Slices of a
+// multiple of 64 features (128-byte aligned rows, no 32-feature tail) are
+// preferred, then the most compute units in use, then fewer slices (less
+// exchange traffic). groups = 0 when the kernel does not apply: bf16 streams,
+// S in {64, 96, 128, 160}, at least `ns` compute units and cooperative launch
+// support are required.
+#ifndef MHC_SPLIT_NS
+#define MHC_SPLIT_NS 0   // 0: choose; otherwise only this slice count is considered
+#endif
+
+struct SplitCfg {
+  int groups = 0;
+  int ns = 0;
+  int S = 0;
+};
+
+mhc_status split_config(int32_t dtype, int32_t d, SplitCfg* cfg) {
+  *cfg = SplitCfg{};
+  if (dtype != MHC_BF16) return MHC_OK;
   int cus = 0;
   mhc_status s = device_cu_count(&cus);
   if (s != MHC_OK) return s;
-  if (cus < fsplit::kSlices) return MHC_OK;
+  int best_score = -1;
+  for (int ns : {32, 40, 48, 64}) {
+    if (MHC_SPLIT_NS != 0 && ns != MHC_SPLIT_NS) continue;
+    if (d % ns != 0 || ns > cus) continue;
+    const int S = d / ns;
+    if (S % 32 != 0 || S < 64 || S > fsplit::kMaxS) continue;
+    const int used = (cus / ns) * ns;
+    const int score = (S % 64 == 0 ? 1 << 20 : 0) + used * 64 + (64 - ns);
+    if (score > best_score) {
+      best_score = score;
+      *cfg = SplitCfg{cus / ns, ns, S};
+    }
+  }
+  if (cfg->groups == 0) return MHC_OK;
   int dev = 0, coop = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev);
   if (e != hipSuccess) return fail(MHC_ERR_HIP, "cooperative-launch attribute: %s", hipGetErrorString(e));
-  if (!coop) return MHC_OK;
-  *groups = cus / fsplit::kSlices;
+  if (!coop) *cfg = SplitCfg{};
   return MHC_OK;
 }
 
-mhc_status launch_split(const StepArgs& a, void* ws, int groups, hipStream_t stream) {
-  const int words = (int)(fsplit::mp_off(groups) / 4);
+mhc_status launch_split(const StepArgs& a, void* ws, const SplitCfg& cfg, hipStream_t stream) {
+  const int words = (int)(fsplit::mp_off(cfg.groups) / 4);
   hipLaunchKernelGGL(fsplit::clear_kernel, dim3(1), dim3(256), 0, stream,
                      static_cast<uint32_t*>(ws), words);
   mhc_status s = launch_status("workspace clear kernel launch");
   if (s != MHC_OK) return s;
-  fsplit::Args fs{static_cast<char*>(ws), groups, (int)((a.tokens + fsplit::kBatch - 1) / fsplit::kBatch)};
+  fsplit::Args fs{static_cast<char*>(ws), cfg.groups, cfg.ns,
+                  (int)((a.tokens + fsplit::kBatch - 1) / fsplit::kBatch)};
   StepArgs args = a;
   void* params[] = {&args, &fs};
   const void* fn = nullptr;
-  switch (a.d / 32) {
+  switch (cfg.S) {
     case 64: fn = reinterpret_cast<const void*>(fsplit::split_kernel<1, false>); break;
     case 96: fn = reinterpret_cast<const void*>(fsplit::split_kernel<1, true>); break;
     case 128: fn = reinterpret_cast<const void*>(fsplit::split_kernel<2, false>); break;
     case 160: fn = reinterpret_cast<const void*>(fsplit::split_kernel<2, true>); break;
-    default: return fail(MHC_ERR_UNSUPPORTED, "feature-split kernel: d = %d", a.d);
+    default: return fail(MHC_ERR_UNSUPPORTED, "feature-split kernel: slice of %d features", cfg.S);
   }
-  const hipError_t e = hipLaunchCooperativeKernel(fn, dim3((unsigned)(groups * fsplit::kSlices)),
+  const hipError_t e = hipLaunchCooperativeKernel(fn, dim3((unsigned)(cfg.groups * cfg.ns)),
                                                   dim3(fsplit::kThreads), params, 0, stream);
   if (e != hipSuccess)
     return fail(MHC_ERR_HIP, "feature-split kernel cooperative launch: %s", hipGetErrorString(e));
@@ -1420,9 +1447,9 @@ int64_t mhc_fused_step_workspace_bytes(int64_t tokens, int32_t d, int32_t dtype)
     fail(MHC_ERR_INVALID_ARG, "bad tokens (%lld), d (%d) or dtype (%d)", (long long)tokens, d, dtype);
     return -1;
   }
-  int groups = 0;
-  if (split_groups(dtype, d, &groups) != MHC_OK) return -1;
-  return groups > 0 ? fsplit::workspace_bytes(groups) : 0;
+  SplitCfg cfg;
+  if (split_config(dtype, d, &cfg) != MHC_OK) return -1;
+  return cfg.groups > 0 ? fsplit::workspace_bytes(cfg.groups, cfg.ns) : 0;
 }
 
 mhc_status mhc_pack_wmix(const float* w_mix, int32_t d, int32_t dtype, void* w_packed,
@@ -1481,13 +1508,13 @@ mhc_status mhc_fused_step(const void* x, const void* f, int32_t dtype, int64_t t
     s = check_spans(all, 14, mo, 1, nullptr, nullptr);
     if (s != MHC_OK) return s;
   }
-  int groups = 0;
+  SplitCfg cfg;
   if (workspace != nullptr) {
-    s = split_groups(dtype, d, &groups);
+    s = split_config(dtype, d, &cfg);
     if (s != MHC_OK) return s;
   }
-  if (groups > 0) {
-    const int64_t need = fsplit::workspace_bytes(groups);
+  if (cfg.groups > 0) {
+    const int64_t need = fsplit::workspace_bytes(cfg.groups, cfg.ns);
     if (workspace_bytes < need)
       return fail(MHC_ERR_INVALID_ARG, "workspace holds %lld bytes, %lld needed",
                   (long long)workspace_bytes, (long long)need);
@@ -1504,7 +1531,7 @@ mhc_status mhc_fused_step(const void* x, const void* f, int32_t dtype, int64_t t
   }
   StepArgs a{x, f, pre_in, post_in, comb_in, w_packed, base, scale, gamma, x_out, y_out,
              pre_out, post_out, comb_out, mix_out, tokens, d, sinkhorn_iters, norm_eps, hc_eps};
-  if (groups > 0) return launch_split(a, workspace, groups, static_cast<hipStream_t>(stream));
+  if (cfg.groups > 0) return launch_split(a, workspace, cfg, static_cast<hipStream_t>(stream));
   return launch_step(a, dtype, kFused, static_cast<hipStream_t>(stream), "fused step kernel launch");
 }
 

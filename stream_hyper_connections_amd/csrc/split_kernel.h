@@ -65,7 +65,7 @@ using pipe::rsrc_t;
 
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-constexpr int kSlices = 32;                    // workgroups per group = feature slices
+constexpr int kMaxSlices = 64;                 // workgroups per group = feature slices (at most)
 constexpr int kBatch = kWaves * kTok;          // 128 tokens per batch
 constexpr int kRing = 4;                       // exchange slots per group
 constexpr int kRow = 32;                       // floats per token and slice: 24 mixes, x'^2, h^2, pad
@@ -80,12 +80,13 @@ constexpr int64_t kHdr = 256;                  // status word + padding
 
 constexpr int kRowRor2 = 0x122;                // DPP row rotate right by 2
 
-// cache policies: stream loads, new-stream stores, y stores
-// raise the batch count right after the exchange stores (1) or after the
-// next batch's wait, which covers them for free (0)
+// raise a batch's count right after its exchange stores (1), or after the
+// next wait, whose loads were issued behind those stores (0)
 #ifndef FS_COUNT_EARLY
 #define FS_COUNT_EARLY 1
 #endif
+
+// cache policies: stream loads, new-stream stores, y stores
 #ifndef FS_LOAD_AUX
 #define FS_LOAD_AUX 2
 #endif
@@ -96,19 +97,22 @@ constexpr int kRowRor2 = 0x122;                // DPP row rotate right by 2
 #define FS_Y_AUX 2
 #endif
 
+// workspace layout for `groups` groups of `ns` slices: status word, one
+// counter per (group, slot), then per (group, slot) the mixes rows
+// [slice][token][kRow] and the h^2 partials [slice][token]
 __host__ __device__ constexpr int64_t ctr_off(int g, int slot) {
   return kHdr + ((int64_t)g * kRing + slot) * kCtrStride;
 }
 __host__ __device__ constexpr int64_t mp_off(int groups) {
   return kHdr + (((int64_t)groups * kRing * kCtrStride + 255) / 256) * 256;
 }
-__host__ __device__ constexpr int64_t mp_slot_bytes() { return (int64_t)kSlices * kBatch * kRow * 4; }
-__host__ __device__ constexpr int64_t hs_off(int groups) {
-  return mp_off(groups) + (int64_t)groups * kRing * mp_slot_bytes();
+__host__ __device__ constexpr int64_t mp_slot_bytes(int ns) { return (int64_t)ns * kBatch * kRow * 4; }
+__host__ __device__ constexpr int64_t hs_off(int groups, int ns) {
+  return mp_off(groups) + (int64_t)groups * kRing * mp_slot_bytes(ns);
 }
-__host__ __device__ constexpr int64_t hs_slot_bytes() { return (int64_t)kSlices * kBatch * 4; }
-__host__ __device__ constexpr int64_t workspace_bytes(int groups) {
-  return hs_off(groups) + (int64_t)groups * kRing * hs_slot_bytes();
+__host__ __device__ constexpr int64_t hs_slot_bytes(int ns) { return (int64_t)ns * kBatch * 4; }
+__host__ __device__ constexpr int64_t workspace_bytes(int groups, int ns) {
+  return hs_off(groups, ns) + (int64_t)groups * kRing * hs_slot_bytes(ns);
 }
 
 // s_waitcnt with only vmcnt limited (gfx9 encoding: vmcnt[3:0], expcnt[6:4],
@@ -136,6 +140,7 @@ struct __align__(16) Smem {
 struct Args {
   char* ws;      // workspace (mhc_fused_step_workspace_bytes)
   int groups;    // G
+  int ns;        // slices per group (d = ns * S)
   int nbatch;    // ceil(tokens / 128)
 };
 
@@ -277,7 +282,8 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
   const int f0 = c * S;                          // first feature of the slice
   WaveSmem& wsm = sm.wv[wave];
   char* const ws = fs.ws;
-  const rsrc_t wsr = make_rsrc(ws, (uint32_t)workspace_bytes(G));
+  const int ns = fs.ns;
+  const rsrc_t wsr = make_rsrc(ws, (uint32_t)workspace_bytes(G, ns));
 
   {
     const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.wpk) +
@@ -383,34 +389,46 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
   // returned (vector memory retires in order) the stores are complete too.
   auto finish = [&](int i, const Rs& r, const u32x4 (&hk)[NI], bool count_next) {
     const int slot = i % kRing;
-    const uint32_t target = (uint32_t)kSlices * (uint32_t)(i / kRing + 1);
+    const uint32_t target = (uint32_t)ns * (uint32_t)(i / kRing + 1);
     wait_count(ws, ctr_off(g, slot), target);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);   // exchange loads stay behind the wait
     __builtin_amdgcn_sched_barrier(0);
     const int64_t slot_id = (int64_t)g * kRing + slot;
-    // sum of h^2 over the 32 slices for the wave's 16 tokens: lane l reads
-    // slice l/2, tokens 8(l&1) .. 8(l&1)+7
-    const uint32_t hoff = (uint32_t)(hs_off(G) + slot_id * hs_slot_bytes()) +
-                          (uint32_t)(((lane >> 1) * kBatch + wave * kTok + 8 * (lane & 1)) * 4);
-    const f32x4 p0 = bload_sc1(wsr, hoff, 0), p1 = bload_sc1(wsr, hoff, 16);
-    // waves 4(i&1) .. 4(i&1)+3 each take one of the workgroup's 4 tokens of
-    // the batch for the split and Sinkhorn; their 4 partial loads per lane
-    // (lane: 16-byte chunk l&7 of the token row, slices l>>3 + 8j) follow at
-    // once so their latency hides behind the y work (empty for other waves)
-    const bool sk = (wave >> 2) == (i & 1);
-    f32x4 sk_part[4];
+    // sum of h^2 over the ns slices for the wave's 16 tokens: lane l reads
+    // slices l/2 and l/2 + 32, tokens 8(l&1) .. 8(l&1)+7
+    f32x4 p0, p1;
     {
-      const uint32_t base = (uint32_t)(mp_off(G) + slot_id * mp_slot_bytes()) +
-                            (uint32_t)(((4 * c + (wave & 3)) * kRow + 4 * (lane & 7)) * 4);
+      const uint32_t hbase = (uint32_t)(hs_off(G, ns) + slot_id * hs_slot_bytes(ns)) +
+                             (uint32_t)((wave * kTok + 8 * (lane & 1)) * 4);
+      const int s0 = lane >> 1, s1 = 32 + (lane >> 1);
+      const uint32_t o0 = hbase + (uint32_t)(s0 * kBatch * 4);
+      const uint32_t o1 = s1 < ns ? hbase + (uint32_t)(s1 * kBatch * 4) : kOutOfRange;
+      p0 = bload_sc1(wsr, s0 < ns ? o0 : kOutOfRange, 0);
+      p1 = bload_sc1(wsr, s0 < ns ? o0 : kOutOfRange, 16);
+      p0 += bload_sc1(wsr, o1, 0);
+      p1 += bload_sc1(wsr, o1, 16);
+    }
+    // waves 4(i&1) + j, j = 0..3, take the batch's token c + ns*j (when it
+    // exists) for the split and Sinkhorn; their partial loads (lane: 16-byte
+    // chunk l&7 of the token row, slices l>>3 + 8k) follow at once so their
+    // latency hides behind the y work
+    const int tb = c + ns * (wave & 3);
+    const bool sk = (wave >> 2) == (i & 1) && tb < kBatch;
+    f32x4 sk_part[kMaxSlices / 8];
+    {
+      const uint32_t base = (uint32_t)(mp_off(G) + slot_id * mp_slot_bytes(ns)) +
+                            (uint32_t)((tb * kRow + 4 * (lane & 7)) * 4);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < kMaxSlices / 8; ++j) {
+        const int sl = (lane >> 3) + 8 * j;
         sk_part[j] = bload_sc1(
-            wsr, sk ? base + (uint32_t)(((lane >> 3) + 8 * j) * kBatch * kRow * 4) : kOutOfRange, 0);
+            wsr, sk && sl < ns ? base + (uint32_t)(sl * kBatch * kRow * 4) : kOutOfRange, 0);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
     {
       if (count_next) {
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(4));
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(kMaxSlices / 8));
         __builtin_amdgcn_sched_barrier(0);
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         count_batch(i + 1);
@@ -439,11 +457,11 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
       const u32x4 y = norm_bf(hk[NI - 1], sm.gamma, ftl + 8 * g16, wsm.rh[t16]);
       bstore<FS_Y_AUX>(r.y, vft, 0, y);
     }
-    // split + Sinkhorn: token 4c + tt of the batch by wave 4 * (i & 1) + tt
+    // split + Sinkhorn of token tb of the batch
     if (sk) {
       f32x4 acc = sk_part[0];
 #pragma unroll
-      for (int j = 1; j < 4; ++j) acc += sk_part[j];
+      for (int j = 1; j < kMaxSlices / 8; ++j) acc += sk_part[j];
       float v[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {   // sum over the 8 slice groups (lanes l ^ 8, 16, 32)
@@ -463,7 +481,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
       const float ssum = __shfl(v[0], 6);               // sum of x'^2
       const float rr = rsqrtf(ssum / (float)(kStreams * d) + a.norm_eps);
       const float mc = msum_c * rr, mp = msum_p * rr;
-      const int64_t t = (g + (int64_t)i * G) * kBatch + 4 * c + (wave & 3);
+      const int64_t t = (g + (int64_t)i * G) * kBatch + tb;
       const bool st_ok = t < a.tokens && lane < 16;
       if (st_ok && a.mix_out != nullptr) {
         a.mix_out[t * kMix + 8 + e] = mc;
@@ -609,7 +627,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
       __builtin_amdgcn_wave_barrier();
       const int slot = i % kRing;
       const int64_t slot_id = (int64_t)g * kRing + slot;
-      const uint32_t row_off = (uint32_t)(mp_off(G) + slot_id * mp_slot_bytes()) +
+      const uint32_t row_off = (uint32_t)(mp_off(G) + slot_id * mp_slot_bytes(ns)) +
                                (uint32_t)(((c * kBatch) + wave * kTok + u) * kRow * 4);
       const uint32_t lo = 24u * (lane & 3);
       bstore64(wsr, row_off + lo, 0, mv[0], mv[1]);
@@ -617,7 +635,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
       bstore64(wsr, row_off + lo + 16, 0, mv[4], mv[5]);
       if ((lane & 3) == 0) {
         bstore64(wsr, row_off + 96, 0, ssu, hsu);
-        bstore32(wsr, (uint32_t)(hs_off(G) + slot_id * hs_slot_bytes()) +
+        bstore32(wsr, (uint32_t)(hs_off(G, ns) + slot_id * hs_slot_bytes(ns)) +
                           (uint32_t)((c * kBatch + wave * kTok + u) * 4),
                  0, hsu);
       }

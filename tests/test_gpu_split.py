@@ -1,8 +1,9 @@
 """GPU parity of the feature-split fused-step kernel (path="split").
 
 Each compute unit owns 1/32 of the features; workgroups exchange per-token
-partial sums through a workspace ring. The cases cover every slice shape the
-kernel is built for (d = 2048, 3072, 4096, 5120), token counts from one token
+partial sums through a workspace ring. The cases cover every slice geometry the
+host picks on a 256-CU device (32, 40, 48 and 64 slices of 64 or 128
+features), token counts from one token
 to enough batches that every exchange slot is reused several times, ragged
 batches, in-place updates, guard bands, repeated calls on one workspace, and
 agreement with the tile kernel (the new streams must match bit for bit: their
@@ -35,6 +36,9 @@ def _run(case, **kw):
     return out, dev
 
 
+# slice geometry chosen on a 256-CU device: d=5120 -> 40 slices of 128
+# features, 4096 -> 32 x 128, 3072 -> 48 x 64, 2048 -> 32 x 64, 2560 -> 40 x 64,
+# 6144 -> 48 x 128, 8192 -> 64 x 128
 SPLIT_CASES = [
     (5120, 1),       # one token: one wave of one group works
     (5120, 37),      # ragged first batch
@@ -42,9 +46,12 @@ SPLIT_CASES = [
     (5120, 1000),    # fewer batches than groups for some groups
     (5120, 4133),    # every group, ring not yet wrapped, ragged
     (5120, 9000),    # ring slots reused, ragged last batch
-    (4096, 300),     # no tail
-    (3072, 257),     # one round + tail
-    (2048, 513),     # one round, no tail
+    (4096, 300),
+    (3072, 257),
+    (2048, 513),
+    (2560, 130),
+    (6144, 700),
+    (8192, 260),
 ]
 
 
@@ -153,4 +160,4 @@ def test_split_workspace_validation():
         mhc.fused_step(*args, path="split", workspace=big[16:])
     assert mhc.fused_step_workspace_bytes(t, 5120, "f32") == 0
     assert mhc.fused_step_workspace_bytes(t, 1024, "bf16") == 0
-    assert mhc.fused_step_workspace_bytes(t, 6144, "bf16") == 0
+    assert mhc.fused_step_workspace_bytes(t, 7168, "bf16") == 0
