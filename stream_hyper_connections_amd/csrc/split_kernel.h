@@ -134,6 +134,8 @@ struct __align__(16) Smem {
   u32x4 w[kMaxS / 32 * kStepBytes / 16];   // W slice, packed B-operand order
   WaveSmem wv[kWaves];
   float gamma[kMaxS];
+  float base[kMix];
+  float scale[4];
   uint32_t lcount[kRing];
 };
 
@@ -158,16 +160,6 @@ struct Cf {      // raw coefficient loads of one batch (see store_coef)
   u32x4 cb, po, pr;
 };
 
-__device__ __forceinline__ void bstore64(rsrc_t r, uint32_t voff, uint32_t soff, float a, float b) {
-  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-  const u32x2 v = {__float_as_uint(a), __float_as_uint(b)};
-  store_pin();
-  __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)voff, (int)soff, kSC1);
-  store_guard();
-}
-__device__ __forceinline__ void bstore32(rsrc_t r, uint32_t voff, uint32_t soff, float a) {
-  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(a), r, (int)voff, (int)soff, kSC1);
-}
 __device__ __forceinline__ f32x4 bload_sc1(rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_bit_cast(f32x4, bload<kSC1>(r, voff, soff));
 }
@@ -290,6 +282,8 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
                                                       (size_t)c * KS * kStepBytes);
     for (int i = tid; i < KS * kStepBytes / 16; i += kThreads) sm.w[i] = src[i];
     for (int i = tid; i < S; i += kThreads) sm.gamma[i] = a.gamma[f0 + i];
+    if (tid < kMix) sm.base[tid] = a.base[tid];
+    if (tid < 3) sm.scale[tid] = a.scale[tid];
     if (tid < kRing) sm.lcount[tid] = 0;
   }
   __syncthreads();
@@ -487,12 +481,12 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
         a.mix_out[t * kMix + 8 + e] = mc;
         if (e < 8) a.mix_out[t * kMix + e] = mp;
       }
-      const float s0 = a.scale[0], s1 = a.scale[1], s2 = a.scale[2];
+      const float s0 = sm.scale[0], s1 = sm.scale[1], s2 = sm.scale[2];
       const float eps = a.hc_eps;
-      if (st_ok && e < 4) a.pre_out[t * 4 + e] = sigmoidf(mp * s0 + a.base[e]) + eps;
+      if (st_ok && e < 4) a.pre_out[t * 4 + e] = sigmoidf(mp * s0 + sm.base[e]) + eps;
       if (st_ok && e >= 4 && e < 8)
-        a.post_out[t * 4 + (e - 4)] = 2.0f * sigmoidf(mp * s1 + a.base[e]);
-      float cv = mc * s2 + a.base[8 + e];
+        a.post_out[t * 4 + (e - 4)] = 2.0f * sigmoidf(mp * s1 + sm.base[e]);
+      float cv = mc * s2 + sm.base[8 + e];
       cv = expf(cv - quad_max(cv));
       cv = cv / quad_sum(cv) + eps;
       cv = cv * __builtin_amdgcn_rcpf(col_sum(cv) + eps);
@@ -625,20 +619,36 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
         mv[jj] = (wsm.u.cst[u][row] + wsm.u.cst[u][kMix + row]) + wsm.u.cst[u][2 * kMix + row];
       }
       __builtin_amdgcn_wave_barrier();
+      // assemble the 16 token rows (24 mixes, x'^2, h^2, zero pad) in LDS, then
+      // write each row as 8 lanes x 16 bytes: whole 128-byte lines
+      float(*rows)[kRow] = reinterpret_cast<float(*)[kRow]>(&wsm.u.cst[0][0]);
+#pragma unroll
+      for (int jj = 0; jj < 6; ++jj) rows[u][6 * (lane & 3) + jj] = mv[jj];
+      if ((lane & 3) == 0) {
+        *reinterpret_cast<f32x4*>(&rows[u][24]) = f32x4{ssu, hsu, 0.f, 0.f};
+        *reinterpret_cast<f32x4*>(&rows[u][28]) = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      __builtin_amdgcn_wave_barrier();
       const int slot = i % kRing;
       const int64_t slot_id = (int64_t)g * kRing + slot;
-      const uint32_t row_off = (uint32_t)(mp_off(G) + slot_id * mp_slot_bytes(ns)) +
-                               (uint32_t)(((c * kBatch) + wave * kTok + u) * kRow * 4);
-      const uint32_t lo = 24u * (lane & 3);
-      bstore64(wsr, row_off + lo, 0, mv[0], mv[1]);
-      bstore64(wsr, row_off + lo + 8, 0, mv[2], mv[3]);
-      bstore64(wsr, row_off + lo + 16, 0, mv[4], mv[5]);
-      if ((lane & 3) == 0) {
-        bstore64(wsr, row_off + 96, 0, ssu, hsu);
-        bstore32(wsr, (uint32_t)(hs_off(G, ns) + slot_id * hs_slot_bytes(ns)) +
-                          (uint32_t)((c * kBatch + wave * kTok + u) * 4),
-                 0, hsu);
+      const uint32_t rows_off = (uint32_t)(mp_off(G) + slot_id * mp_slot_bytes(ns)) +
+                                (uint32_t)((c * kBatch + wave * kTok) * kRow * 4);
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int tk = 8 * hh + (lane >> 3);
+        const u32x4 v = *reinterpret_cast<const u32x4*>(&rows[tk][4 * (lane & 7)]);
+        bstore<kSC1>(wsr, rows_off + (uint32_t)(tk * kRow * 4 + 16 * (lane & 7)), 0, v);
       }
+      {
+        // sum of h^2 of the 16 tokens: 4 lanes x 4 tokens
+        const int t0 = 4 * (lane & 3);
+        const u32x4 v = {__float_as_uint(rows[t0][25]), __float_as_uint(rows[t0 + 1][25]),
+                         __float_as_uint(rows[t0 + 2][25]), __float_as_uint(rows[t0 + 3][25])};
+        const uint32_t hoff = (uint32_t)(hs_off(G, ns) + slot_id * hs_slot_bytes(ns)) +
+                              (uint32_t)((c * kBatch + wave * kTok + t0) * 4);
+        bstore<kSC1>(wsr, lane < 4 ? hoff : kOutOfRange, 0, v);
+      }
+      __builtin_amdgcn_wave_barrier();
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       __builtin_amdgcn_sched_barrier(0);
 
