@@ -94,10 +94,12 @@ mhc_status mhc_pack_wmix(const float* w_mix, int32_t d, int32_t dtype, void* w_p
  * mhc_fused_step needs to run its feature-split kernel for these arguments on
  * the current device: 0 when that kernel does not apply (then the workspace
  * argument is ignored), -1 for bad arguments or a failing HIP query (see
- * mhc_last_error). The feature-split kernel applies to MHC_BF16 streams with
- * d in {2048, 3072, 4096, 5120} on a device with at least 32 compute units and
- * cooperative launch support; the size depends only on the device's compute
- * unit count (about 15 MB for 256 CUs), not on tokens.
+ * mhc_last_error). The feature-split kernel applies to MHC_BF16 streams whose
+ * width splits into ns slices of S features, ns in {32, 40, 48, 64} and S in
+ * {64, 96, 128, 160} (d = 2048 ... 10240, e.g. 5120 = 40 x 128), on a device
+ * with at least ns compute units and cooperative launch support. The size
+ * depends on the device's compute unit count and d, not on tokens (about
+ * 17 MB for d = 5120 on 256 CUs).
  */
 int64_t mhc_fused_step_workspace_bytes(int64_t tokens, int32_t d, int32_t dtype);
 
@@ -126,8 +128,8 @@ int64_t mhc_fused_step_workspace_bytes(int64_t tokens, int32_t d, int32_t dtype)
  * Workspace (optional): NULL, or device memory of workspace_bytes bytes,
  *          256-byte aligned, overlapping no other argument. When it is given and
  *          mhc_fused_step_workspace_bytes() > 0, the step runs the feature-split
- *          kernel (each compute unit keeps 1/32 of the features and of W on chip;
- *          workgroups exchange per-token partial sums through the workspace),
+ *          kernel (each compute unit keeps one slice of the features and of W on
+ *          chip; workgroups exchange per-token partial sums through the workspace),
  *          which needs the whole device: it is launched cooperatively, one
  *          workgroup per compute unit, and fails with MHC_ERR_HIP when that
  *          launch is refused. workspace_bytes below the required size is

@@ -1,5 +1,6 @@
-// Feature-split fused step (bf16 streams, d = 32 * S with S = 64 * NR + 32 * TAIL,
-// NR >= 1, S <= 160): the kernel behind mhc_fused_step when a workspace is given.
+// Feature-split fused step (bf16 streams, d = ns * S with S = 64 * NR + 32 * TAIL,
+// NR >= 1, S <= 160, ns <= 64 slices): the kernel behind mhc_fused_step when a
+// workspace is given.
 //
 // Included by mhc.hip (one translation unit); uses its helpers and the pipe::
 // buffer-instruction wrappers.
@@ -8,29 +9,31 @@
 // bf16 terms of W, 20 KB per 32 features) from L2 for every 16-token tile:
 // twice the stream bytes through each CU's vector-memory path. Its lane layout
 // (16 token rows x 64 bytes per load instruction, the MFMA operand order) also
-// moves at most ~3 TB/s even as a plain copy, against ~4.3 TB/s for 4-8 rows x
-// 128-256 bytes. Here every CU owns one 32nd of the features for good:
+// moves at most ~3 TB/s even as a plain copy, against 4.3-4.8 TB/s for 4-8 rows
+// x 128-256 bytes. Here every CU owns one slice of the features for good:
 //
 //   * Workgroup (group g, slice c): g = blockIdx % G, c = blockIdx / G, with G
-//     groups of 32 workgroups. Slice c is features [c*S, (c+1)*S) of every
-//     stream row, F row, new-stream row and y row; its W slice (S/32 packed
-//     steps, 100 KB for S = 160) is loaded into LDS once and used for every
-//     token the group processes. Groups take 128-token batches b = g, g+G, ...;
-//     wave w of a workgroup owns tokens 16w .. 16w+15 of each batch.
+//     groups of ns workgroups (the host picks ns; d = 5120 runs 40 slices of
+//     128 features). Slice c is features [c*S, (c+1)*S) of every stream row,
+//     F row, new-stream row and y row; its W slice (S/32 packed steps, 80 KB
+//     for S = 128) is loaded into LDS once and used for every token the group
+//     processes. Groups take 128-token batches b = g, g+G, ...; wave w of a
+//     workgroup owns tokens 16w .. 16w+15 of each batch.
 //   * Loads and stores move 8 token rows x 128 bytes per instruction ("half
-//     rounds" of 64 features); the S % 64 = 32 remainder ("tail", 16 rows x 64
+//     rounds" of 64 features); an S % 64 = 32 remainder ("tail", 16 rows x 64
 //     bytes) sits at the 128-byte-aligned end of the slice (first for odd c).
 //     New streams pass through a 2 KB per-wave LDS buffer per stream to reach
 //     the MFMA A-operand order (row = token, 8 consecutive features per lane).
 //   * Per token the slice yields 24 projection partials, sum x'^2 and sum h^2.
-//     They go to a workspace ring (kRing slots per group) with device-scope
-//     (sc1) stores; the last wave of a workgroup to finish a batch bumps the
-//     group's counter for that slot (one device-scope atomic per workgroup).
-//   * One batch later each wave waits for all 32 slices of the batch, sums the
-//     32 partial sums of h^2 of its 16 tokens and writes y for its slice from h
+//     They go to a workspace ring (kRing slots per group) as whole 128-byte
+//     rows with device-scope (sc1) stores; the last wave of a workgroup to
+//     finish a batch bumps the group's counter for that slot (one device-scope
+//     atomic per workgroup and batch).
+//   * One batch later each wave waits for all ns slices of the batch, sums the
+//     ns partial sums of h^2 of its 16 tokens and writes y for its slice from h
 //     kept in registers; four waves per workgroup (alternating halves) each sum
-//     the 32 partial rows of one of the workgroup's 4 tokens of the batch and
-//     run RMS scaling, split and the 4x4 Sinkhorn for it.
+//     the ns partial rows of one token of the batch (token c + ns*j) and run RMS
+//     scaling, split and the 4x4 Sinkhorn for it.
 //
 // Cross-workgroup protocol (correct wherever the workgroups run; the group ->
 // XCD mapping only matters for speed):
@@ -39,7 +42,7 @@
 //     wave's LDS increment; the wave that completes the workgroup's count
 //     issues a device-scope atomic add on the counter.
 //   * reader: polls the counter with device-scope loads until it reaches
-//     32 * (generation + 1), then reads the exchange with sc1 loads.
+//     ns * (generation + 1), then reads the exchange with sc1 loads.
 //   * slots: a workgroup writes batch i's slot only after it has seen every
 //     workgroup of the group finish batch i-2, whose waves had all finished
 //     reading batch i-4 before that; four slots are therefore never read and

@@ -1,9 +1,9 @@
 """GPU parity of the feature-split fused-step kernel (path="split").
 
-Each compute unit owns 1/32 of the features; workgroups exchange per-token
+Each compute unit owns one slice of the features; workgroups exchange per-token
 partial sums through a workspace ring. The cases cover every slice geometry the
-host picks on a 256-CU device (32, 40, 48 and 64 slices of 64 or 128
-features), token counts from one token
+host picks on a 256-CU device (32, 40, 48 and 64 slices of 64, 96, 128 or
+160 features), token counts from one token
 to enough batches that every exchange slot is reused several times, ragged
 batches, in-place updates, guard bands, repeated calls on one workspace, and
 agreement with the tile kernel (the new streams must match bit for bit: their
@@ -38,7 +38,8 @@ def _run(case, **kw):
 
 # slice geometry chosen on a 256-CU device: d=5120 -> 40 slices of 128
 # features, 4096 -> 32 x 128, 3072 -> 48 x 64, 2048 -> 32 x 64, 2560 -> 40 x 64,
-# 6144 -> 48 x 128, 8192 -> 64 x 128
+# 6144 -> 48 x 128, 8192 -> 64 x 128; no 128-byte aligned choice exists for
+# 3840 (40 x 96) and 6400 (40 x 160), which take the 32-feature tail
 SPLIT_CASES = [
     (5120, 1),       # one token: one wave of one group works
     (5120, 37),      # ragged first batch
@@ -52,6 +53,8 @@ SPLIT_CASES = [
     (2560, 130),
     (6144, 700),
     (8192, 260),
+    (3840, 300),     # 40 x 96: one round + a 32-feature tail
+    (6400, 200),     # 40 x 160: two rounds + tail
 ]
 
 
