@@ -98,8 +98,8 @@ mhc_status mhc_pack_wmix(const float* w_mix, int32_t d, int32_t dtype, void* w_p
  * width splits into ns slices of S features, ns in {32, 40, 48, 64} and S in
  * {64, 96, 128, 160} (d = 2048 ... 10240, e.g. 5120 = 40 x 128), on a device
  * with at least ns compute units and cooperative launch support. The size
- * depends on the device's compute unit count and d, not on tokens (about
- * 17 MB for d = 5120 on 256 CUs).
+ * depends on the device's compute unit count, d and tokens (about 17 MB for
+ * d = 5120 on 256 CUs, plus 96 bytes per token for the mixes rows).
  */
 int64_t mhc_fused_step_workspace_bytes(int64_t tokens, int32_t d, int32_t dtype);
 

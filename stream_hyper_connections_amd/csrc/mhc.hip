@@ -1379,7 +1379,10 @@ mhc_status launch_split(const StepArgs& a, void* ws, const SplitCfg& cfg, hipStr
                      static_cast<uint32_t*>(ws), words);
   mhc_status s = launch_status("workspace clear kernel launch");
   if (s != MHC_OK) return s;
-  fsplit::Args fs{static_cast<char*>(ws), cfg.groups, cfg.ns,
+  float* mix = a.mix_out != nullptr
+                   ? a.mix_out
+                   : reinterpret_cast<float*>(static_cast<char*>(ws) + fsplit::mix_off(cfg.groups, cfg.ns));
+  fsplit::Args fs{static_cast<char*>(ws), mix, cfg.groups, cfg.ns,
                   (int)((a.tokens + fsplit::kBatch - 1) / fsplit::kBatch)};
   StepArgs args = a;
   void* params[] = {&args, &fs};
@@ -1395,7 +1398,12 @@ mhc_status launch_split(const StepArgs& a, void* ws, const SplitCfg& cfg, hipStr
                                                   dim3(fsplit::kThreads), params, 0, stream);
   if (e != hipSuccess)
     return fail(MHC_ERR_HIP, "feature-split kernel cooperative launch: %s", hipGetErrorString(e));
-  return launch_status("feature-split kernel launch");
+  s = launch_status("feature-split kernel launch");
+  if (s != MHC_OK) return s;
+  hipLaunchKernelGGL(fsplit::tail_kernel, dim3((unsigned)((a.tokens + 15) / 16)), dim3(256), 0,
+                     stream, mix, a.tokens, a.base, a.scale, a.iters, a.hc_eps, a.pre_out,
+                     a.post_out, a.comb_out);
+  return launch_status("split/Sinkhorn tail kernel launch");
 }
 
 mhc_status launch_step(const StepArgs& a, int32_t dtype, int mode, hipStream_t stream,
@@ -1449,7 +1457,7 @@ int64_t mhc_fused_step_workspace_bytes(int64_t tokens, int32_t d, int32_t dtype)
   }
   SplitCfg cfg;
   if (split_config(dtype, d, &cfg) != MHC_OK) return -1;
-  return cfg.groups > 0 ? fsplit::workspace_bytes(cfg.groups, cfg.ns) : 0;
+  return cfg.groups > 0 ? fsplit::workspace_bytes(cfg.groups, cfg.ns, tokens) : 0;
 }
 
 mhc_status mhc_pack_wmix(const float* w_mix, int32_t d, int32_t dtype, void* w_packed,
@@ -1514,7 +1522,7 @@ mhc_status mhc_fused_step(const void* x, const void* f, int32_t dtype, int64_t t
     if (s != MHC_OK) return s;
   }
   if (cfg.groups > 0) {
-    const int64_t need = fsplit::workspace_bytes(cfg.groups, cfg.ns);
+    const int64_t need = fsplit::workspace_bytes(cfg.groups, cfg.ns, tokens);
     if (workspace_bytes < need)
       return fail(MHC_ERR_INVALID_ARG, "workspace holds %lld bytes, %lld needed",
                   (long long)workspace_bytes, (long long)need);

@@ -32,8 +32,9 @@
 //   * One batch later each wave waits for all ns slices of the batch, sums the
 //     ns partial sums of h^2 of its 16 tokens and writes y for its slice from h
 //     kept in registers; four waves per workgroup (alternating halves) each sum
-//     the ns partial rows of one token of the batch (token c + ns*j) and run RMS
-//     scaling, split and the 4x4 Sinkhorn for it.
+//     the ns partial rows of one token of the batch (token c + ns*j), apply the
+//     RMS scaling and write its 24 mixes; tail_kernel then runs the split and
+//     the 4x4 Sinkhorn on all tokens (16 lanes per token).
 //
 // Cross-workgroup protocol (correct wherever the workgroups run; the group ->
 // XCD mapping only matters for speed):
@@ -114,8 +115,12 @@ __host__ __device__ constexpr int64_t hs_off(int groups, int ns) {
   return mp_off(groups) + (int64_t)groups * kRing * mp_slot_bytes(ns);
 }
 __host__ __device__ constexpr int64_t hs_slot_bytes(int ns) { return (int64_t)ns * kBatch * 4; }
-__host__ __device__ constexpr int64_t workspace_bytes(int groups, int ns) {
+__host__ __device__ constexpr int64_t mix_off(int groups, int ns) {
   return hs_off(groups, ns) + (int64_t)groups * kRing * hs_slot_bytes(ns);
+}
+// the mixes region [T][24] follows (used when the caller passes no mix_out)
+__host__ __device__ constexpr int64_t workspace_bytes(int groups, int ns, int64_t tokens) {
+  return mix_off(groups, ns) + ((tokens * kMix * 4 + 255) / 256) * 256;
 }
 
 // s_waitcnt with only vmcnt limited (gfx9 encoding: vmcnt[3:0], expcnt[6:4],
@@ -144,6 +149,7 @@ struct __align__(16) Smem {
 
 struct Args {
   char* ws;      // workspace (mhc_fused_step_workspace_bytes)
+  float* mix;    // [T][24] mixes (mix_out, or a workspace region)
   int groups;    // G
   int ns;        // slices per group (d = ns * S)
   int nbatch;    // ceil(tokens / 128)
@@ -278,7 +284,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
   WaveSmem& wsm = sm.wv[wave];
   char* const ws = fs.ws;
   const int ns = fs.ns;
-  const rsrc_t wsr = make_rsrc(ws, (uint32_t)workspace_bytes(G, ns));
+  const rsrc_t wsr = make_rsrc(ws, (uint32_t)mix_off(G, ns));
 
   {
     const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.wpk) +
@@ -479,25 +485,11 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
       const float rr = rsqrtf(ssum / (float)(kStreams * d) + a.norm_eps);
       const float mc = msum_c * rr, mp = msum_p * rr;
       const int64_t t = (g + (int64_t)i * G) * kBatch + tb;
-      const bool st_ok = t < a.tokens && lane < 16;
-      if (st_ok && a.mix_out != nullptr) {
-        a.mix_out[t * kMix + 8 + e] = mc;
-        if (e < 8) a.mix_out[t * kMix + e] = mp;
+      // the mixes row; split and Sinkhorn run in tail_kernel
+      if (t < a.tokens && lane < 16) {
+        fs.mix[t * kMix + 8 + e] = mc;
+        if (e < 8) fs.mix[t * kMix + e] = mp;
       }
-      const float s0 = sm.scale[0], s1 = sm.scale[1], s2 = sm.scale[2];
-      const float eps = a.hc_eps;
-      if (st_ok && e < 4) a.pre_out[t * 4 + e] = sigmoidf(mp * s0 + sm.base[e]) + eps;
-      if (st_ok && e >= 4 && e < 8)
-        a.post_out[t * 4 + (e - 4)] = 2.0f * sigmoidf(mp * s1 + sm.base[e]);
-      float cv = mc * s2 + sm.base[8 + e];
-      cv = expf(cv - quad_max(cv));
-      cv = cv / quad_sum(cv) + eps;
-      cv = cv * __builtin_amdgcn_rcpf(col_sum(cv) + eps);
-      for (int it = 1; it < a.iters; ++it) {
-        cv = cv * __builtin_amdgcn_rcpf(quad_sum(cv) + eps);
-        cv = cv * __builtin_amdgcn_rcpf(col_sum(cv) + eps);
-      }
-      if (st_ok) a.comb_out[t * 16 + e] = cv;
     }
   };
 
@@ -678,6 +670,36 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
     }
   }
   if (nbg > 0) finish(nbg - 1, rprev, hprev, false);
+}
+
+// Split and Sinkhorn of the mixes rows [T][24] the feature-split kernel wrote:
+// 16 lanes per token, lane e holds comb entry (e/4, e%4) and, for e < 8, the
+// pre (e < 4) or post slot e ([SW] Code, the split/Sinkhorn kernel; "All 5
+// steps"): row sums over quads, column sums over lanes e, e+4, e+8, e+12.
+__global__ __launch_bounds__(256) void tail_kernel(const float* __restrict__ mix, int64_t tokens,
+                                                   const float* __restrict__ base,
+                                                   const float* __restrict__ scale, int iters,
+                                                   float eps, float* __restrict__ pre_out,
+                                                   float* __restrict__ post_out,
+                                                   float* __restrict__ comb_out) {
+  const int e = threadIdx.x & 15;
+  const int64_t t = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const bool ok = t < tokens;
+  const int64_t tc = ok ? t : 0;
+  const float mc = mix[tc * kMix + 8 + e];
+  const float mp = mix[tc * kMix + (e & 7)];
+  const float s0 = scale[0], s1 = scale[1], s2 = scale[2];
+  if (ok && e < 4) pre_out[t * 4 + e] = sigmoidf(mp * s0 + base[e]) + eps;
+  if (ok && e >= 4 && e < 8) post_out[t * 4 + (e - 4)] = 2.0f * sigmoidf(mp * s1 + base[e]);
+  float cv = mc * s2 + base[8 + e];
+  cv = expf(cv - quad_max(cv));
+  cv = cv / quad_sum(cv) + eps;
+  cv = cv * __builtin_amdgcn_rcpf(col_sum(cv) + eps);
+  for (int it = 1; it < iters; ++it) {
+    cv = cv * __builtin_amdgcn_rcpf(quad_sum(cv) + eps);
+    cv = cv * __builtin_amdgcn_rcpf(col_sum(cv) + eps);
+  }
+  if (ok) comb_out[t * 16 + e] = cv;
 }
 
 __global__ __launch_bounds__(256) void clear_kernel(uint32_t* p, int words) {

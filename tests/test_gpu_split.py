@@ -137,7 +137,7 @@ def test_split_guard_bands_untouched():
 def test_split_repeated_calls_share_a_workspace():
     """Two calls in a row on one workspace, the second smaller: counters and the
     status word are reset by every call."""
-    ws = torch.empty(mhc.fused_step_workspace_bytes(1, 5120, "bf16"), dtype=torch.uint8,
+    ws = torch.empty(mhc.fused_step_workspace_bytes(3000, 5120, "bf16"), dtype=torch.uint8,
                      device="cuda")
     for t, seed in ((3000, 453), (200, 454)):
         case = make_case(wl.Workload(seed, "split_repeat", t, 5120, "bf16"))
