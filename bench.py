@@ -62,6 +62,16 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
+def algorithmic_bytes_three_kernel(tokens: int, d: int, elem: int) -> int:
+    """Bytes the separate kernels must move: hc_post reads x, f and writes x'
+    (9d), hc_mixes reads x' (4d), hc_pre reads x' and writes h (5d), RMSNorm
+    reads h and writes y (2d): (4n+4)*d elements per token, plus the same 192 B
+    of coefficients and the per-call parameters."""
+    per_token = (4 * N + 4) * d * elem + 2 * 24 * 4
+    per_call = (24 * N * d + 24 + 3 + d) * 4
+    return tokens * per_token + per_call
+
+
 def algorithmic_bytes(tokens: int, d: int, elem: int) -> int:
     """Bytes one fused-step launch must move: read x [T,4,d] and f [T,d], write
     x_out and y ((2n+2)*d elements per token), read the 24 prior coefficients
@@ -81,6 +91,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="minimum oracle time for the cpu_baseline sample")
+    ap.add_argument("--form", choices=("fused", "three-kernel"), default="fused",
+                    help="fused: the single-pass step (the headline); three-kernel: hc_post, "
+                         "hc_mixes, hc_pre and RMSNorm as separate kernels (the comparison)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain device-to-device copy of 2 GiB instead (the reference "
                          "kernel for scaling the HBM byte counters)")
@@ -187,15 +200,24 @@ def main():
              mhc.fused_step_workspace_bytes(w.tokens, w.d, w.dtype) > 0)
     kernel_name = ("fsplit::split_kernel (feature-split fused step)" if split
                    else "pipe::fused_bf16_kernel (tile fused step)")
+    if args.form != "fused":
+        kernel_name = "hc_post + hc_mixes + hc_pre + RMSNorm kernels (three-kernel form)"
     torch.cuda.synchronize()
     print(f"[bench] inputs resident after {time.time() - t_prep:.1f}s: {w.name} T={w.tokens} "
           f"d={w.d} {w.dtype}", file=sys.stderr, flush=True)
 
+    h_buf = torch.empty_like(f)
+
     def step():
         mhc.pack_wmix(cur["w_mix"], w.dtype, out=wp)
         e1.record()
-        mhc.fused_step(x, f, prior["pre"], prior["post"], prior["comb"], wp, cur["base"],
-                       cur["scale"], cur["gamma"], w.iters, w.norm_eps, w.hc_eps, **outs)
+        if args.form == "fused":
+            mhc.fused_step(x, f, prior["pre"], prior["post"], prior["comb"], wp, cur["base"],
+                           cur["scale"], cur["gamma"], w.iters, w.norm_eps, w.hc_eps, **outs)
+        else:
+            mhc.three_kernel_step(x, f, prior["pre"], prior["post"], prior["comb"], wp,
+                                  cur["base"], cur["scale"], cur["gamma"], w.iters, w.norm_eps,
+                                  w.hc_eps, x_out=outs["x_out"], h_out=h_buf, y_out=outs["y_out"])
 
     e1 = torch.cuda.Event(enable_timing=True)
     for _ in range(args.warmup):
@@ -227,7 +249,8 @@ def main():
     total_ms = starts[0].elapsed_time(ends[-1])
     ms_per_step = total_ms / args.steps
     value = w.tokens / (ms_per_step / 1e3)
-    alg = algorithmic_bytes(w.tokens, w.d, elem)
+    alg = (algorithmic_bytes(w.tokens, w.d, elem) if args.form == "fused"
+           else algorithmic_bytes_three_kernel(w.tokens, w.d, elem))
     kern_avg_s = kern_ms.mean() / 1e3
     achieved = alg / kern_avg_s / 1e9
 
@@ -246,7 +269,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "tokens": w.tokens, "batch": w.batch,
                    "seq_len": w.tokens // w.batch, "n_streams": N, "d": w.d,
-                   "sinkhorn_iters": w.iters, "stream_dtype": w.dtype},
+                   "sinkhorn_iters": w.iters, "stream_dtype": w.dtype, "form": args.form},
         "step_ms_p50": round(float(np.percentile(step_ms, 50)), 5),
         "step_ms_p95": round(float(np.percentile(step_ms, 95)), 5),
         "step_ms_p99": round(float(np.percentile(step_ms, 99)), 5),
@@ -255,7 +278,7 @@ def main():
         "wall_s": round(wall, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(w.name),
+                     "traffic": measured_traffic(w.name) if args.form == "fused" else None,
                      "algorithmic_bytes_per_launch": alg,
                      "kernel": kernel_name},
         "device": torch.cuda.get_device_name(0),

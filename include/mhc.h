@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define MHC_ABI_VERSION 2
+#define MHC_ABI_VERSION 3
 #define MHC_N_STREAMS 4
 #define MHC_N_MIX 24
 
@@ -153,12 +153,40 @@ mhc_status mhc_fused_step(const void* x, const void* f, int32_t dtype, int64_t t
  * statistic over the flattened 4*d streams, the 24-wide projection, then the
  * split and Sinkhorn of mhc_sinkhorn4. Reads x [T][4][d]; writes pre_out,
  * post_out [T][4], comb_out [T][4][4] and, if not NULL, mix_out [T][24].
- * w_packed as for mhc_fused_step.
+ * w_packed as for mhc_fused_step. workspace / workspace_bytes as for
+ * mhc_fused_step (same size, mhc_fused_step_workspace_bytes): with it, the
+ * feature-split kernel runs in its mixes-only mode.
  */
 mhc_status mhc_mixes(const void* x, int32_t dtype, int64_t tokens, int32_t d,
                      const void* w_packed, const float* base, const float* scale,
                      int32_t sinkhorn_iters, float norm_eps, float hc_eps, float* pre_out,
-                     float* post_out, float* comb_out, float* mix_out, mhc_stream_t stream);
+                     float* post_out, float* comb_out, float* mix_out, void* workspace,
+                     int64_t workspace_bytes, mhc_stream_t stream);
+
+/*
+ * The step as separate kernels, in the order of [RN] Code, Block.forward:
+ * mhc_hc_post, mhc_mixes, mhc_hc_pre, mhc_rmsnorm. Each reads its inputs from
+ * memory and writes its outputs back, so the streams move (4n+4)*d elements
+ * per token against the fused step's (2n+2)*d ([SW] "Why"); the per-element
+ * arithmetic and rounding points are those of mhc_fused_step. Same argument
+ * rules as mhc_fused_step; d a multiple of mhc_d_granule().
+ *
+ * mhc_hc_post -- [SW] Code, hc_post: x_out[t][k] = S(sum_j comb_in[t][j][k] *
+ *   x[t][j] + post_in[t][k] * f[t]). x_out may be exactly x.
+ */
+mhc_status mhc_hc_post(const void* x, const void* f, int32_t dtype, int64_t tokens, int32_t d,
+                       const float* post_in, const float* comb_in, void* x_out,
+                       mhc_stream_t stream);
+
+/* mhc_hc_pre -- [SW] Code, hc_pre: h_out[t] = S(sum_k pre_in[t][k] * x[t][k]);
+ * x [T][4][d], h_out [T][d]. */
+mhc_status mhc_hc_pre(const void* x, int32_t dtype, int64_t tokens, int32_t d,
+                      const float* pre_in, void* h_out, mhc_stream_t stream);
+
+/* mhc_rmsnorm -- [RN] RMSNorm: y_out[t] = S(gamma * (h[t] / sqrt(mean(h[t]^2) +
+ * norm_eps))); h, y_out [T][d] (y_out may be exactly h), gamma [d] float32. */
+mhc_status mhc_rmsnorm(const void* h, int32_t dtype, int64_t tokens, int32_t d,
+                       const float* gamma, float norm_eps, void* y_out, mhc_stream_t stream);
 
 /*
  * mhc_sinkhorn4 -- split float32 mixes [T][24] into the three coefficient sets

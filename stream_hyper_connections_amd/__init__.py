@@ -13,13 +13,17 @@ from .binding import (  # noqa: F401
     SPLIT_MIN_TOKENS,
     fused_step,
     fused_step_workspace_bytes,
+    hc_post,
+    hc_pre,
     last_error,
     load,
     mixes,
     pack_wmix,
+    rmsnorm,
     sinkhorn4,
     split_status,
     status_string,
+    three_kernel_step,
     wmix_packed_bytes,
     workspace_for,
 )

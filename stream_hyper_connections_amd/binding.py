@@ -36,7 +36,11 @@ _SIGS = {
                         _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                         _c_void_p, _i64, _c_void_p], _i32),
     "mhc_mixes": ([_c_void_p, _i32, _i64, _i32, _c_void_p, _c_void_p, _c_void_p, _i32, _f32, _f32,
-                   _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p], _i32),
+                   _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _c_void_p], _i32),
+    "mhc_hc_post": ([_c_void_p, _c_void_p, _i32, _i64, _i32, _c_void_p, _c_void_p, _c_void_p,
+                     _c_void_p], _i32),
+    "mhc_hc_pre": ([_c_void_p, _i32, _i64, _i32, _c_void_p, _c_void_p, _c_void_p], _i32),
+    "mhc_rmsnorm": ([_c_void_p, _i32, _i64, _i32, _c_void_p, _f32, _c_void_p, _c_void_p], _i32),
     "mhc_sinkhorn4": ([_c_void_p, _i64, _c_void_p, _c_void_p, _i32, _f32, _c_void_p, _c_void_p,
                        _c_void_p, _c_void_p], _i32),
 }
@@ -188,17 +192,7 @@ def fused_step(x, f, pre_in, post_in, comb_in, w_packed, base, scale, gamma, ite
     t, n, d = x.shape
     if n != N_STREAMS:
         raise ValueError("x must be [T, 4, d]")
-    if path not in ("auto", "tile", "split"):
-        raise ValueError(f"unknown path {path!r}")
-    ws_ptr, ws_bytes = None, 0
-    if path != "tile":
-        need = fused_step_workspace_bytes(t, d, _dtype_code(x))
-        if path == "split" and need == 0:
-            raise ValueError(f"the feature-split kernel does not apply to d={d}, {x.dtype}")
-        if need > 0 and (path == "split" or t >= SPLIT_MIN_TOKENS):
-            if workspace is None:
-                workspace = workspace_for(x.device, need)
-            ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    ws_ptr, ws_bytes = _workspace_arg(x, t, d, path, workspace)
     x_out = torch.empty_like(x) if x_out is None else x_out
     y_out = torch.empty_like(f) if y_out is None else y_out
     pre_out = _f32_out((t, N_STREAMS), x, pre_out)
@@ -216,12 +210,31 @@ def fused_step(x, f, pre_in, post_in, comb_in, w_packed, base, scale, gamma, ite
             "mix": mix_out}
 
 
+def _workspace_arg(x, t, d, path, workspace):
+    """(pointer, bytes) of the workspace for path "tile" / "split" / "auto"."""
+    if path not in ("auto", "tile", "split"):
+        raise ValueError(f"unknown path {path!r}")
+    if path == "tile":
+        return None, 0
+    need = fused_step_workspace_bytes(t, d, _dtype_code(x))
+    if path == "split" and need == 0:
+        raise ValueError(f"the feature-split kernel does not apply to d={d}, {x.dtype}")
+    if need > 0 and (path == "split" or t >= SPLIT_MIN_TOKENS):
+        if workspace is None:
+            workspace = workspace_for(x.device, need)
+        return _ptr(workspace), workspace.numel() * workspace.element_size()
+    return None, 0
+
+
 def mixes(x, w_packed, base, scale, iters=20, norm_eps=1e-6, hc_eps=1e-6, pre_out=None,
-          post_out=None, comb_out=None, mix_out=None, want_mix=False) -> dict:
-    """mhc_mixes on tensors. Returns dict(pre, post, comb, mix)."""
+          post_out=None, comb_out=None, mix_out=None, want_mix=False, path="auto",
+          workspace=None) -> dict:
+    """mhc_mixes on tensors. Returns dict(pre, post, comb, mix). path and
+    workspace as for fused_step."""
     t, n, d = x.shape
     if n != N_STREAMS:
         raise ValueError("x must be [T, 4, d]")
+    ws_ptr, ws_bytes = _workspace_arg(x, t, d, path, workspace)
     pre_out = _f32_out((t, N_STREAMS), x, pre_out)
     post_out = _f32_out((t, N_STREAMS), x, post_out)
     comb_out = _f32_out((t, N_STREAMS, N_STREAMS), x, comb_out)
@@ -229,7 +242,7 @@ def mixes(x, w_packed, base, scale, iters=20, norm_eps=1e-6, hc_eps=1e-6, pre_ou
         mix_out = _f32_out((t, N_MIX), x, None)
     st = load().mhc_mixes(_ptr(x), _dtype_code(x), t, d, _ptr(w_packed), _ptr(base), _ptr(scale),
                           iters, norm_eps, hc_eps, _ptr(pre_out), _ptr(post_out), _ptr(comb_out),
-                          _ptr(mix_out), _stream())
+                          _ptr(mix_out), ws_ptr, ws_bytes, _stream())
     _check("mhc_mixes", st)
     return {"pre": pre_out, "post": post_out, "comb": comb_out, "mix": mix_out}
 
@@ -245,3 +258,44 @@ def sinkhorn4(mix, base, scale, iters=20, hc_eps=1e-6, pre_out=None, post_out=No
                               _ptr(pre_out), _ptr(post_out), _ptr(comb_out), _stream())
     _check("mhc_sinkhorn4", st)
     return {"pre": pre_out, "post": post_out, "comb": comb_out}
+
+
+def hc_post(x, f, post_in, comb_in, x_out=None):
+    """mhc_hc_post: new streams x_out [T,4,d] = S(comb^T x + post * f)."""
+    t, n, d = x.shape
+    x_out = torch.empty_like(x) if x_out is None else x_out
+    _check("mhc_hc_post", load().mhc_hc_post(_ptr(x), _ptr(f), _dtype_code(x), t, d, _ptr(post_in),
+                                             _ptr(comb_in), _ptr(x_out), _stream()))
+    return x_out
+
+
+def hc_pre(x, pre_in, h_out=None):
+    """mhc_hc_pre: h [T,d] = S(sum_k pre_k x_k)."""
+    t, n, d = x.shape
+    h_out = torch.empty((t, d), dtype=x.dtype, device=x.device) if h_out is None else h_out
+    _check("mhc_hc_pre", load().mhc_hc_pre(_ptr(x), _dtype_code(x), t, d, _ptr(pre_in),
+                                           _ptr(h_out), _stream()))
+    return h_out
+
+
+def rmsnorm(h, gamma, norm_eps=1e-6, y_out=None):
+    """mhc_rmsnorm: y [T,d] = S(gamma * h / rms(h))."""
+    t, d = h.shape
+    y_out = torch.empty_like(h) if y_out is None else y_out
+    _check("mhc_rmsnorm", load().mhc_rmsnorm(_ptr(h), _dtype_code(h), t, d, _ptr(gamma), norm_eps,
+                                             _ptr(y_out), _stream()))
+    return y_out
+
+
+def three_kernel_step(x, f, pre_in, post_in, comb_in, w_packed, base, scale, gamma, iters=20,
+                      norm_eps=1e-6, hc_eps=1e-6, want_mix=False, path="auto", workspace=None,
+                      x_out=None, h_out=None, y_out=None) -> dict:
+    """The step as the pages run it, one kernel per operation: hc_post, hc_mixes,
+    hc_pre, RMSNorm. Same outputs as fused_step (plus h)."""
+    xo = hc_post(x, f, post_in, comb_in, x_out=x_out)
+    m = mixes(xo, w_packed, base, scale, iters, norm_eps, hc_eps, want_mix=want_mix, path=path,
+              workspace=workspace)
+    h = hc_pre(xo, pre_in, h_out=h_out)
+    y = rmsnorm(h, gamma, norm_eps, y_out=y_out)
+    return {"x_out": xo, "y": y, "pre": m["pre"], "post": m["post"], "comb": m["comb"],
+            "mix": m["mix"], "h": h}

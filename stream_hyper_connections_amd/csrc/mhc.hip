@@ -1107,6 +1107,7 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_kernel(StepArgs a, int nt
 }  // namespace pipe
 
 #include "split_kernel.h"
+#include "unfused.h"
 
 // ----- split / Sinkhorn on given mixes -------------------------------------------------
 
@@ -1373,7 +1374,8 @@ mhc_status split_config(int32_t dtype, int32_t d, SplitCfg* cfg) {
   return MHC_OK;
 }
 
-mhc_status launch_split(const StepArgs& a, void* ws, const SplitCfg& cfg, hipStream_t stream) {
+mhc_status launch_split(const StepArgs& a, void* ws, const SplitCfg& cfg, int mode,
+                        hipStream_t stream) {
   const int words = (int)(fsplit::mp_off(cfg.groups) / 4);
   hipLaunchKernelGGL(fsplit::clear_kernel, dim3(1), dim3(256), 0, stream,
                      static_cast<uint32_t*>(ws), words);
@@ -1387,11 +1389,24 @@ mhc_status launch_split(const StepArgs& a, void* ws, const SplitCfg& cfg, hipStr
   StepArgs args = a;
   void* params[] = {&args, &fs};
   const void* fn = nullptr;
+  const bool full = mode == kFused;
   switch (cfg.S) {
-    case 64: fn = reinterpret_cast<const void*>(fsplit::split_kernel<1, false>); break;
-    case 96: fn = reinterpret_cast<const void*>(fsplit::split_kernel<1, true>); break;
-    case 128: fn = reinterpret_cast<const void*>(fsplit::split_kernel<2, false>); break;
-    case 160: fn = reinterpret_cast<const void*>(fsplit::split_kernel<2, true>); break;
+    case 64:
+      fn = full ? reinterpret_cast<const void*>(fsplit::split_kernel<1, false, kFused>)
+                : reinterpret_cast<const void*>(fsplit::split_kernel<1, false, kMixesOnly>);
+      break;
+    case 96:
+      fn = full ? reinterpret_cast<const void*>(fsplit::split_kernel<1, true, kFused>)
+                : reinterpret_cast<const void*>(fsplit::split_kernel<1, true, kMixesOnly>);
+      break;
+    case 128:
+      fn = full ? reinterpret_cast<const void*>(fsplit::split_kernel<2, false, kFused>)
+                : reinterpret_cast<const void*>(fsplit::split_kernel<2, false, kMixesOnly>);
+      break;
+    case 160:
+      fn = full ? reinterpret_cast<const void*>(fsplit::split_kernel<2, true, kFused>)
+                : reinterpret_cast<const void*>(fsplit::split_kernel<2, true, kMixesOnly>);
+      break;
     default: return fail(MHC_ERR_UNSUPPORTED, "feature-split kernel: slice of %d features", cfg.S);
   }
   const hipError_t e = hipLaunchCooperativeKernel(fn, dim3((unsigned)(cfg.groups * cfg.ns)),
@@ -1539,14 +1554,16 @@ mhc_status mhc_fused_step(const void* x, const void* f, int32_t dtype, int64_t t
   }
   StepArgs a{x, f, pre_in, post_in, comb_in, w_packed, base, scale, gamma, x_out, y_out,
              pre_out, post_out, comb_out, mix_out, tokens, d, sinkhorn_iters, norm_eps, hc_eps};
-  if (cfg.groups > 0) return launch_split(a, workspace, cfg, static_cast<hipStream_t>(stream));
+  if (cfg.groups > 0)
+    return launch_split(a, workspace, cfg, kFused, static_cast<hipStream_t>(stream));
   return launch_step(a, dtype, kFused, static_cast<hipStream_t>(stream), "fused step kernel launch");
 }
 
 mhc_status mhc_mixes(const void* x, int32_t dtype, int64_t tokens, int32_t d,
                      const void* w_packed, const float* base, const float* scale,
                      int32_t sinkhorn_iters, float norm_eps, float hc_eps, float* pre_out,
-                     float* post_out, float* comb_out, float* mix_out, mhc_stream_t stream) {
+                     float* post_out, float* comb_out, float* mix_out, void* workspace,
+                     int64_t workspace_bytes, mhc_stream_t stream) {
   mhc_status s = check_common(dtype, tokens, d, sinkhorn_iters, norm_eps, hc_eps);
   if (s != MHC_OK) return s;
   if (tokens == 0) return ok();
@@ -1563,10 +1580,96 @@ mhc_status mhc_mixes(const void* x, int32_t dtype, int64_t tokens, int32_t d,
   };
   s = check_spans(in, 4, out, mix_out ? 4 : 3, nullptr, nullptr);
   if (s != MHC_OK) return s;
+  SplitCfg cfg;
+  if (workspace != nullptr) {
+    s = split_config(dtype, d, &cfg);
+    if (s != MHC_OK) return s;
+  }
+  if (cfg.groups > 0) {
+    const int64_t need = fsplit::workspace_bytes(cfg.groups, cfg.ns, tokens);
+    if (workspace_bytes < need)
+      return fail(MHC_ERR_INVALID_ARG, "workspace holds %lld bytes, %lld needed",
+                  (long long)workspace_bytes, (long long)need);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+      return fail(MHC_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+    const Span wsp[] = {{"workspace", workspace, (uint64_t)need}};
+    Span all[8];
+    for (int i = 0; i < 4; ++i) all[i] = in[i];
+    for (int i = 0; i < (mix_out ? 4 : 3); ++i) all[4 + i] = out[i];
+    s = check_spans(all, mix_out ? 8 : 7, wsp, 1, nullptr, nullptr);
+    if (s != MHC_OK) return s;
+  }
   StepArgs a{x, nullptr, nullptr, nullptr, nullptr, w_packed, base, scale, nullptr, nullptr,
              nullptr, pre_out, post_out, comb_out, mix_out, tokens, d, sinkhorn_iters, norm_eps,
              hc_eps};
+  if (cfg.groups > 0)
+    return launch_split(a, workspace, cfg, kMixesOnly, static_cast<hipStream_t>(stream));
   return launch_step(a, dtype, kMixesOnly, static_cast<hipStream_t>(stream), "mixes kernel launch");
+}
+
+mhc_status mhc_hc_post(const void* x, const void* f, int32_t dtype, int64_t tokens, int32_t d,
+                       const float* post_in, const float* comb_in, void* x_out,
+                       mhc_stream_t stream) {
+  mhc_status s = check_common(dtype, tokens, d, 1, 0.f, 0.f);
+  if (s != MHC_OK) return s;
+  if (tokens == 0) return ok();
+  const uint64_t es = elem_size(dtype), T = (uint64_t)tokens;
+  const Span in[] = {{"x", x, T * kStreams * d * es}, {"f", f, T * d * es},
+                     {"post_in", post_in, T * 16}, {"comb_in", comb_in, T * 64}};
+  const Span out[] = {{"x_out", x_out, T * kStreams * d * es}};
+  s = check_spans(in, 4, out, 1, x_out, x);
+  if (s != MHC_OK) return s;
+  const unsigned blocks = (unsigned)((tokens * (d / 8) + unfused::kThreads - 1) / unfused::kThreads);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (dtype == MHC_BF16)
+    hipLaunchKernelGGL(unfused::hc_post_kernel<MHC_BF16>, dim3(blocks), dim3(unfused::kThreads), 0,
+                       st, x, f, post_in, comb_in, tokens, d, x_out);
+  else
+    hipLaunchKernelGGL(unfused::hc_post_kernel<MHC_F32>, dim3(blocks), dim3(unfused::kThreads), 0,
+                       st, x, f, post_in, comb_in, tokens, d, x_out);
+  return launch_status("hc_post kernel launch");
+}
+
+mhc_status mhc_hc_pre(const void* x, int32_t dtype, int64_t tokens, int32_t d,
+                      const float* pre_in, void* h_out, mhc_stream_t stream) {
+  mhc_status s = check_common(dtype, tokens, d, 1, 0.f, 0.f);
+  if (s != MHC_OK) return s;
+  if (tokens == 0) return ok();
+  const uint64_t es = elem_size(dtype), T = (uint64_t)tokens;
+  const Span in[] = {{"x", x, T * kStreams * d * es}, {"pre_in", pre_in, T * 16}};
+  const Span out[] = {{"h_out", h_out, T * d * es}};
+  s = check_spans(in, 2, out, 1, nullptr, nullptr);
+  if (s != MHC_OK) return s;
+  const unsigned blocks = (unsigned)((tokens * (d / 8) + unfused::kThreads - 1) / unfused::kThreads);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (dtype == MHC_BF16)
+    hipLaunchKernelGGL(unfused::hc_pre_kernel<MHC_BF16>, dim3(blocks), dim3(unfused::kThreads), 0,
+                       st, x, pre_in, tokens, d, h_out);
+  else
+    hipLaunchKernelGGL(unfused::hc_pre_kernel<MHC_F32>, dim3(blocks), dim3(unfused::kThreads), 0,
+                       st, x, pre_in, tokens, d, h_out);
+  return launch_status("hc_pre kernel launch");
+}
+
+mhc_status mhc_rmsnorm(const void* h, int32_t dtype, int64_t tokens, int32_t d,
+                       const float* gamma, float norm_eps, void* y_out, mhc_stream_t stream) {
+  mhc_status s = check_common(dtype, tokens, d, 1, norm_eps, 0.f);
+  if (s != MHC_OK) return s;
+  if (tokens == 0) return ok();
+  const uint64_t es = elem_size(dtype), T = (uint64_t)tokens;
+  const Span in[] = {{"h", h, T * d * es}, {"gamma", gamma, (uint64_t)d * 4}};
+  const Span out[] = {{"y_out", y_out, T * d * es}};
+  s = check_spans(in, 2, out, 1, y_out, h);
+  if (s != MHC_OK) return s;
+  const unsigned blocks = (unsigned)((tokens + 3) / 4);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (dtype == MHC_BF16)
+    hipLaunchKernelGGL(unfused::rmsnorm_kernel<MHC_BF16>, dim3(blocks), dim3(unfused::kThreads), 0,
+                       st, h, gamma, tokens, d, norm_eps, y_out);
+  else
+    hipLaunchKernelGGL(unfused::rmsnorm_kernel<MHC_F32>, dim3(blocks), dim3(unfused::kThreads), 0,
+                       st, h, gamma, tokens, d, norm_eps, y_out);
+  return launch_status("rmsnorm kernel launch");
 }
 
 mhc_status mhc_sinkhorn4(const float* mixes, int64_t tokens, const float* base,

@@ -238,6 +238,23 @@ __device__ __forceinline__ void elementwise(const Items& in, const float (&C)[4]
   hs += hsa;
 }
 
+// hc_mixes alone: the input streams are the new streams; only their sum of
+// squares is needed here.
+__device__ __forceinline__ void streams_only(const Items& in, u32x4 (&xo)[4], float& ss) {
+  float ssa = 0.f, ssb = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    xo[k] = in.x[k];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float r0 = bf_lo(in.x[k][q]), r1 = bf_hi(in.x[k][q]);
+      ssa = fmaf(r0, r0, ssa);
+      ssb = fmaf(r1, r1, ssb);
+    }
+  }
+  ss += ssa + ssb;
+}
+
 // Bounded wait until the counter reaches `target`; false after a time-out or
 // when another wave has already timed out.
 __device__ __forceinline__ bool wait_count(char* ws, int64_t off, uint32_t target) {
@@ -260,8 +277,9 @@ __device__ __forceinline__ bool wait_count(char* ws, int64_t off, uint32_t targe
   }
 }
 
-template <int NR, bool TAIL>
+template <int NR, bool TAIL, int MODE>
 __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
+  constexpr bool kFull = MODE == kFused;   // else mixes only (hc_mixes)
   __shared__ Smem sm;
   constexpr int S = 64 * NR + (TAIL ? 32 : 0);   // features per slice
   constexpr int KS = S / 32;                      // packed steps per slice
@@ -290,7 +308,8 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
     const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.wpk) +
                                                       (size_t)c * KS * kStepBytes);
     for (int i = tid; i < KS * kStepBytes / 16; i += kThreads) sm.w[i] = src[i];
-    for (int i = tid; i < S; i += kThreads) sm.gamma[i] = a.gamma[f0 + i];
+    if constexpr (kFull)
+      for (int i = tid; i < S; i += kThreads) sm.gamma[i] = a.gamma[f0 + i];
     if (tid < kMix) sm.base[tid] = a.base[tid];
     if (tid < 3) sm.scale[tid] = a.scale[tid];
     if (tid < kRing) sm.lcount[tid] = 0;
@@ -317,31 +336,39 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
     Rs r;
     r.t0 = t0;
     r.x = make_rsrc(static_cast<const char*>(a.x) + t0 * rowx, ntok * rowx);
-    r.f = make_rsrc(static_cast<const char*>(a.f) + t0 * rowf, ntok * rowf);
-    r.xo = make_rsrc(static_cast<char*>(a.x_out) + t0 * rowx, ntok * rowx);
-    r.y = make_rsrc(static_cast<char*>(a.y_out) + t0 * rowf, ntok * rowf);
-    r.cb = make_rsrc(a.comb_in + t0 * 16, ntok * 64);
-    r.po = make_rsrc(a.post_in + t0 * 4, ntok * 16);
-    r.pr = make_rsrc(a.pre_in + t0 * 4, ntok * 16);
+    if constexpr (kFull) {
+      r.f = make_rsrc(static_cast<const char*>(a.f) + t0 * rowf, ntok * rowf);
+      r.xo = make_rsrc(static_cast<char*>(a.x_out) + t0 * rowx, ntok * rowx);
+      r.y = make_rsrc(static_cast<char*>(a.y_out) + t0 * rowf, ntok * rowf);
+      r.cb = make_rsrc(a.comb_in + t0 * 16, ntok * 64);
+      r.po = make_rsrc(a.post_in + t0 * 4, ntok * 16);
+      r.pr = make_rsrc(a.pre_in + t0 * 4, ntok * 16);
+    } else {
+      r.f = r.xo = r.y = r.cb = r.po = r.pr = r.x;   // unused
+    }
     return r;
   };
   auto load_half = [&](Items& it, const Rs& r, int rr, int h) {
     const uint32_t col = 128u * rr;
 #pragma unroll
     for (int k = 0; k < 4; ++k) it.x[k] = bload<FS_LOAD_AUX>(r.x, vxh[h], col + k * d2);
-    it.f = bload<FS_LOAD_AUX>(r.f, vfh[h], col);
+    if constexpr (kFull) it.f = bload<FS_LOAD_AUX>(r.f, vfh[h], col);
+    else it.f = u32x4{0, 0, 0, 0};
   };
   auto load_tail = [&](Items& it, const Rs& r) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) it.x[k] = bload<FS_LOAD_AUX>(r.x, vxt, k * d2);
-    it.f = bload<FS_LOAD_AUX>(r.f, vft, 0);
+    if constexpr (kFull) it.f = bload<FS_LOAD_AUX>(r.f, vft, 0);
+    else it.f = u32x4{0, 0, 0, 0};
   };
   auto load_coef = [&](Cf& cf, const Rs& r) {
+    if constexpr (!kFull) return;
     cf.cb = bload<0>(r.cb, 16u * lane, 0);
     cf.po = bload<0>(r.po, lane < kTok ? 16u * lane : kOutOfRange, 0);
     cf.pr = bload<0>(r.pr, lane < kTok ? 16u * lane : kOutOfRange, 0);
   };
   auto store_coef = [&](const Cf& cf) {
+    if constexpr (!kFull) return;
     *reinterpret_cast<u32x4*>(&wsm.u.e.coef[lane >> 2][4 * (lane & 3)]) = cf.cb;
     if (lane < kTok) {
       *reinterpret_cast<u32x4*>(&wsm.u.e.coef[lane][16]) = cf.po;
@@ -399,8 +426,8 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
     const int64_t slot_id = (int64_t)g * kRing + slot;
     // sum of h^2 over the ns slices for the wave's 16 tokens: lane l reads
     // slices l/2 and l/2 + 32, tokens 8(l&1) .. 8(l&1)+7
-    f32x4 p0, p1;
-    {
+    f32x4 p0 = {0.f, 0.f, 0.f, 0.f}, p1 = p0;
+    if constexpr (kFull) {
       const uint32_t hbase = (uint32_t)(hs_off(G, ns) + slot_id * hs_slot_bytes(ns)) +
                              (uint32_t)((wave * kTok + 8 * (lane & 1)) * 4);
       const int s0 = lane >> 1, s1 = 32 + (lane >> 1);
@@ -436,6 +463,8 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         count_batch(i + 1);
       }
+    }
+    if constexpr (kFull) {
       float rh[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -447,18 +476,18 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
         *reinterpret_cast<f32x4*>(&wsm.rh[8 * lane + 4]) = f32x4{rh[4], rh[5], rh[6], rh[7]};
       }
       __builtin_amdgcn_wave_barrier();
-    }
-    // y = bf16(gamma * (h * rh)) ([RN] RMSNorm) for the slice
+      // y = bf16(gamma * (h * rh)) ([RN] RMSNorm) for the slice
 #pragma unroll
-    for (int j = 0; j < 2 * NR; ++j) {
-      const int rr = j >> 1, h = j & 1;
-      const float rhv = wsm.rh[8 * h + m8];
-      const u32x4 y = norm_bf(hk[j], sm.gamma, fr0 + 64 * rr + 8 * x8, rhv);
-      bstore<FS_Y_AUX>(r.y, vfh[h], 128u * rr, y);
-    }
-    if (TAIL) {
-      const u32x4 y = norm_bf(hk[NI - 1], sm.gamma, ftl + 8 * g16, wsm.rh[t16]);
-      bstore<FS_Y_AUX>(r.y, vft, 0, y);
+      for (int j = 0; j < 2 * NR; ++j) {
+        const int rr = j >> 1, h = j & 1;
+        const float rhv = wsm.rh[8 * h + m8];
+        const u32x4 y = norm_bf(hk[j], sm.gamma, fr0 + 64 * rr + 8 * x8, rhv);
+        bstore<FS_Y_AUX>(r.y, vfh[h], 128u * rr, y);
+      }
+      if (TAIL) {
+        const u32x4 y = norm_bf(hk[NI - 1], sm.gamma, ftl + 8 * g16, wsm.rh[t16]);
+        bstore<FS_Y_AUX>(r.y, vft, 0, y);
+      }
     }
     // split + Sinkhorn of token tb of the batch
     if (sk) {
@@ -519,18 +548,22 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
       u32x4 xo0[4], xo1[4];
       float C[4][4], U[4], P[4];
       __builtin_amdgcn_sched_barrier(0);
-      get_coef(m8, C, U, P);
-      elementwise(bufA, C, U, P, xo0, hcur[2 * rr], ssA[0], hsA[0]);
+      if constexpr (kFull) get_coef(m8, C, U, P);
+      if constexpr (kFull) elementwise(bufA, C, U, P, xo0, hcur[2 * rr], ssA[0], hsA[0]);
+      else streams_only(bufA, xo0, ssA[0]);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) bstore<FS_XO_AUX>(rcur.xo, vxh[0], 128u * rr + k * d2, xo0[k]);
+      for (int k = 0; k < 4; ++k)
+        if constexpr (kFull) bstore<FS_XO_AUX>(rcur.xo, vxh[0], 128u * rr + k * d2, xo0[k]);
       __builtin_amdgcn_sched_barrier(0);
       if (rr + 1 < NR) load_half(bufA, rcur, rr + 1, 0);
       else if (TAIL) load_tail(bufT, rcur);
       __builtin_amdgcn_sched_barrier(0);
-      get_coef(8 + m8, C, U, P);
-      elementwise(bufB, C, U, P, xo1, hcur[2 * rr + 1], ssA[1], hsA[1]);
+      if constexpr (kFull) get_coef(8 + m8, C, U, P);
+      if constexpr (kFull) elementwise(bufB, C, U, P, xo1, hcur[2 * rr + 1], ssA[1], hsA[1]);
+      else streams_only(bufB, xo1, ssA[1]);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) bstore<FS_XO_AUX>(rcur.xo, vxh[1], 128u * rr + k * d2, xo1[k]);
+      for (int k = 0; k < 4; ++k)
+        if constexpr (kFull) bstore<FS_XO_AUX>(rcur.xo, vxh[1], 128u * rr + k * d2, xo1[k]);
       __builtin_amdgcn_sched_barrier(0);
       if (rr + 1 < NR) load_half(bufB, rcur, rr + 1, 1);
       __builtin_amdgcn_sched_barrier(0);
@@ -556,10 +589,12 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
     if (TAIL) {
       u32x4 xot[4];
       float C[4][4], U[4], P[4];
-      get_coef(t16, C, U, P);
-      elementwise(bufT, C, U, P, xot, hcur[NI - 1], ssT, hsT);
+      if constexpr (kFull) get_coef(t16, C, U, P);
+      if constexpr (kFull) elementwise(bufT, C, U, P, xot, hcur[NI - 1], ssT, hsT);
+      else streams_only(bufT, xot, ssT);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) bstore<FS_XO_AUX>(rcur.xo, vxt, k * d2, xot[k]);
+      for (int k = 0; k < 4; ++k)
+        if constexpr (kFull) bstore<FS_XO_AUX>(rcur.xo, vxt, k * d2, xot[k]);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const bf16x8 A = __builtin_bit_cast(bf16x8, xot[k]);
@@ -641,7 +676,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
                          __float_as_uint(rows[t0 + 2][25]), __float_as_uint(rows[t0 + 3][25])};
         const uint32_t hoff = (uint32_t)(hs_off(G, ns) + slot_id * hs_slot_bytes(ns)) +
                               (uint32_t)((c * kBatch + wave * kTok + t0) * 4);
-        bstore<kSC1>(wsr, lane < 4 ? hoff : kOutOfRange, 0, v);
+        if constexpr (kFull) bstore<kSC1>(wsr, lane < 4 ? hoff : kOutOfRange, 0, v);
       }
       __builtin_amdgcn_wave_barrier();
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -657,7 +692,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
       if (i == 0 || FS_COUNT_EARLY) {
         // wait for the exchange stores directly (13 loads were issued after
         // them) and count the batch now
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(13));
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(kFull ? 13 : 8));
         __builtin_amdgcn_sched_barrier(0);
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         count_batch(i);

@@ -27,7 +27,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for fn in ("mhc_fused_step", "mhc_mixes", "mhc_sinkhorn4", "mhc_pack_wmix",
                "mhc_wmix_packed_bytes", "mhc_status_string", "mhc_last_error",
-               "mhc_abi_version", "mhc_d_granule", "mhc_fused_step_workspace_bytes"):
+               "mhc_abi_version", "mhc_d_granule", "mhc_fused_step_workspace_bytes",
+               "mhc_hc_post", "mhc_hc_pre", "mhc_rmsnorm"):
         assert fn in names
 
 
@@ -39,7 +40,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_granule_and_status_strings():
-    assert binding.abi_version() == 2
+    assert binding.abi_version() == 3
     assert binding.d_granule() == 32
     lib = binding.load()
     assert lib.mhc_status_string(0) == b"MHC_OK"
@@ -138,10 +139,10 @@ def test_mixes_and_sinkhorn_validation():
     lib = binding.load()
     p = _layout()
     st = lib.mhc_mixes(p["x"], binding.MHC_BF16, T, D, p["w_packed"], p["base"], p["scale"], 0,
-                       1e-6, 1e-6, p["pre_out"], p["post_out"], p["comb_out"], None, None)
+                       1e-6, 1e-6, p["pre_out"], p["post_out"], p["comb_out"], None, None, 0, None)
     assert st == binding.MHC_ERR_INVALID_ARG
     st = lib.mhc_mixes(p["x"], binding.MHC_BF16, 0, D, p["w_packed"], p["base"], p["scale"], 20,
-                       1e-6, 1e-6, p["pre_out"], p["post_out"], p["comb_out"], None, None)
+                       1e-6, 1e-6, p["pre_out"], p["post_out"], p["comb_out"], None, None, 0, None)
     assert st == binding.MHC_OK
     st = lib.mhc_sinkhorn4(p["mix_out"], T, p["base"], p["scale"], 20, -1.0, p["pre_out"],
                            p["post_out"], p["comb_out"], None)
@@ -165,3 +166,29 @@ def test_pack_validation():
                              None) == binding.MHC_ERR_INVALID_ARG
     assert lib.mhc_pack_wmix(None, D, binding.MHC_BF16, p["w_packed"], need,
                              None) == binding.MHC_ERR_INVALID_ARG
+
+
+def test_unfused_entry_points_validate():
+    lib = binding.load()
+    p = _layout()
+    # NULL input, bad width, overlapping output, zero tokens
+    assert lib.mhc_hc_post(None, p["f"], binding.MHC_BF16, T, D, p["post_in"], p["comb_in"],
+                           p["x_out"], None) == binding.MHC_ERR_INVALID_ARG
+    assert "x is NULL" in binding.last_error()
+    assert lib.mhc_hc_post(p["x"], p["f"], binding.MHC_BF16, T, 48, p["post_in"], p["comb_in"],
+                           p["x_out"], None) == binding.MHC_ERR_INVALID_ARG
+    assert lib.mhc_hc_post(p["x"], p["f"], binding.MHC_BF16, T, D, p["post_in"], p["comb_in"],
+                           p["f"], None) == binding.MHC_ERR_INVALID_ARG
+    assert "overlaps" in binding.last_error()
+    assert lib.mhc_hc_post(p["x"], p["f"], binding.MHC_BF16, 0, D, p["post_in"], p["comb_in"],
+                           p["x"], None) == binding.MHC_OK
+    assert lib.mhc_hc_pre(p["x"], binding.MHC_BF16, T, D, p["pre_in"], p["x"] + 64,
+                          None) == binding.MHC_ERR_INVALID_ARG
+    assert lib.mhc_hc_pre(p["x"], 3, T, D, p["pre_in"], p["y_out"], None) == binding.MHC_ERR_INVALID_ARG
+    assert lib.mhc_rmsnorm(p["y_out"], binding.MHC_BF16, T, D, None, 1e-6, p["y_out"],
+                           None) == binding.MHC_ERR_INVALID_ARG
+    assert "gamma is NULL" in binding.last_error()
+    assert lib.mhc_rmsnorm(p["y_out"], binding.MHC_BF16, T, D, p["gamma"], -1.0, p["y_out"],
+                           None) == binding.MHC_ERR_INVALID_ARG
+    assert lib.mhc_rmsnorm(p["y_out"], binding.MHC_BF16, 0, D, p["gamma"], 1e-6, p["y_out"],
+                           None) == binding.MHC_OK
