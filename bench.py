@@ -94,6 +94,10 @@ def parse():
     ap.add_argument("--form", choices=("fused", "three-kernel"), default="fused",
                     help="fused: the single-pass step (the headline); three-kernel: hc_post, "
                          "hc_mixes, hc_pre and RMSNorm as separate kernels (the comparison)")
+    ap.add_argument("--sinkhorn-sweep", action="store_true",
+                    help="time the split/Sinkhorn kernel (mhc_sinkhorn4) on the workload's mixes "
+                         "for a range of iteration counts and report row-sum convergence; one "
+                         "JSON line per count")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain device-to-device copy of 2 GiB instead (the reference "
                          "kernel for scaling the HBM byte counters)")
@@ -118,6 +122,36 @@ def copy_calibration(steps):
     ms = a.elapsed_time(b) / steps
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms_per_copy": round(ms, 4),
                       "GBps_read_plus_write": round(2 * n / ms / 1e6, 1)}), flush=True)
+
+
+SWEEP_ITERS = (1, 2, 3, 5, 10, 20, 50, 100, 200)
+
+
+def sinkhorn_sweep(w, mix, base, scale, steps, warmup):
+    """mhc_sinkhorn4 on the mixes [T, 24] for every count in SWEEP_ITERS: time
+    (HIP events over `steps` calls) and row-sum deviation of the output comb."""
+    import torch
+    import stream_hyper_connections_amd as mhc
+    t = mix.shape[0]
+    for iters in SWEEP_ITERS:
+        for _ in range(warmup):
+            out = mhc.sinkhorn4(mix, base, scale, iters, w.hc_eps)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            out = mhc.sinkhorn4(mix, base, scale, iters, w.hc_eps)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / steps
+        rdev = (out["comb"].double().sum(dim=2) - 1).abs().amax(dim=1)
+        cdev = (out["comb"].double().sum(dim=1) - 1).abs().amax()
+        print(json.dumps({
+            "metric": "split + Sinkhorn kernel time and comb row-sum deviation vs iterations",
+            "sinkhorn_iters": iters, "tokens": t, "ms": round(ms, 5),
+            "tokens_per_s": round(t / ms * 1e3, 1),
+            "row_dev_median": float(rdev.median()), "row_dev_p99": float(rdev.quantile(0.99)),
+            "row_dev_max": float(rdev.max()), "col_dev_max": float(cdev),
+            "config": {"workload": w.name, "hc_eps": w.hc_eps}}), flush=True)
 
 
 def upload_tokens(w, tensor, step, dev, dtype_t):
@@ -202,6 +236,12 @@ def main():
                    else "pipe::fused_bf16_kernel (tile fused step)")
     if args.form != "fused":
         kernel_name = "hc_post + hc_mixes + hc_pre + RMSNorm kernels (three-kernel form)"
+    if args.sinkhorn_sweep:
+        cur_mix = mhc.mixes(x, mhc.pack_wmix(cur["w_mix"], w.dtype), cur["base"], cur["scale"],
+                            w.iters, w.norm_eps, w.hc_eps, want_mix=True)["mix"]
+        torch.cuda.synchronize()
+        sinkhorn_sweep(w, cur_mix, cur["base"], cur["scale"], args.steps, args.warmup)
+        return
     torch.cuda.synchronize()
     print(f"[bench] inputs resident after {time.time() - t_prep:.1f}s: {w.name} T={w.tokens} "
           f"d={w.d} {w.dtype}", file=sys.stderr, flush=True)

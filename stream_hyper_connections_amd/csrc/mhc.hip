@@ -1109,32 +1109,6 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_kernel(StepArgs a, int nt
 #include "split_kernel.h"
 #include "unfused.h"
 
-// ----- split / Sinkhorn on given mixes -------------------------------------------------
-
-__global__ __launch_bounds__(256) void sinkhorn4_kernel(const float* __restrict__ mixes,
-                                                        int64_t tokens, const float* base,
-                                                        const float* scale, int iters,
-                                                        float eps, float* pre_out,
-                                                        float* post_out, float* comb_out) {
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (t >= tokens) return;
-  float m[kMix];
-#pragma unroll
-  for (int i = 0; i < kMix / 4; ++i) {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(mixes + t * kMix + 4 * i);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) m[4 * i + e] = v[e];
-  }
-  float pre[4], post[4], comb[16];
-  split_sinkhorn_token(m, base, scale, iters, eps, pre, post, comb);
-  st4f(pre_out + t * 4, f32x4{pre[0], pre[1], pre[2], pre[3]});
-  st4f(post_out + t * 4, f32x4{post[0], post[1], post[2], post[3]});
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    st4f(comb_out + t * 16 + 4 * j,
-         f32x4{comb[4 * j], comb[4 * j + 1], comb[4 * j + 2], comb[4 * j + 3]});
-}
-
 // ----- packing of the projection --------------------------------------------------------
 
 // bf16: one thread per (step s, stream k, tile q, lane) writes the lane's 8
@@ -1688,11 +1662,10 @@ mhc_status mhc_sinkhorn4(const float* mixes, int64_t tokens, const float* base,
                       {"comb_out", comb_out, T * 64}};
   mhc_status s = check_spans(in, 3, out, 3, nullptr, nullptr);
   if (s != MHC_OK) return s;
-  const unsigned blocks = (unsigned)((tokens + 255) / 256);
-  hipLaunchKernelGGL(sinkhorn4_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
-                     mixes, tokens, base, scale, sinkhorn_iters, hc_eps, pre_out, post_out,
-                     comb_out);
-  return launch_status("sinkhorn4 kernel launch");
+  hipLaunchKernelGGL(fsplit::tail_kernel, dim3((unsigned)((tokens + 15) / 16)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), mixes, tokens, base, scale, sinkhorn_iters,
+                     hc_eps, pre_out, post_out, comb_out);
+  return launch_status("split/Sinkhorn kernel launch");
 }
 
 }  // extern "C"

@@ -78,10 +78,12 @@ def check_mix_like(what, got, want):
         _fail(what, bad, got, want)
 
 
-def check_comb(got, want, hc_eps=1e-6):
+def check_comb(got, want, hc_eps=1e-6, iters=20):
     """Entries, row and column sums against the oracle's; column sums against
     1 within the tolerance plus the shortfall eps/(s + eps) the final column
-    division leaves."""
+    division leaves. That shortfall is below hc_eps only once a full round has
+    run (iters >= 2): after the softmax alone a column can hold little more
+    than the eps floor, so the check against 1 is skipped for iters = 1."""
     got, want = _np(got), _np(want)
     check_mix_like("comb", got, want)
     for axis, name in ((1, "column"), (2, "row")):
@@ -89,6 +91,8 @@ def check_comb(got, want, hc_eps=1e-6):
         bad = ~(np.abs(gs - ws) <= SUM_TOL)
         if bad.any():
             _fail(f"comb {name} sums", bad, gs, ws)
+    if iters < 2:
+        return
     cs = got.sum(axis=1)
     bad = ~(np.abs(cs - 1.0) <= SUM_TOL + hc_eps)
     if bad.any():
@@ -128,7 +132,7 @@ def check_mixes(inputs, gpu, dtype):
         check_mix_like("mix", gpu["mix"], m)
     check_mix_like("pre", gpu["pre"], pre)
     check_mix_like("post", gpu["post"], post)
-    check_comb(gpu["comb"], comb, inputs.get("hc_eps", 1e-6))
+    check_comb(gpu["comb"], comb, inputs.get("hc_eps", 1e-6), inputs.get("iters", 20))
     return {"m": m, "pre": pre, "post": post, "comb": comb}
 
 
@@ -170,7 +174,7 @@ def check_step(inputs, gpu, dtype, coef_abs=0.0):
         check_mix_like("mix", gpu["mix"], o["m"])
     check_mix_like("pre", gpu["pre"], o["pre"])
     check_mix_like("post", gpu["post"], o["post"])
-    check_comb(gpu["comb"], o["comb"], hc_eps)
+    check_comb(gpu["comb"], o["comb"], hc_eps, iters)
 
     gy = _np(gpu["y"])
     if dtype == "bf16":
