@@ -19,8 +19,11 @@ id    name               tokens      dtype   notes
 4     chain              8192 x 80   bf16    80 sublayer steps, fresh params per step
 ====  =================  ==========  ======  =========================================
 
-Distributions: streams X and sublayer output F ~ N(0, 1); W_mix [24, 4d] ~
-N(0, 0.02); base [24] ~ N(0, 0.1); scale [3] ~ U(0.5, 2); gamma [d] ~ 1 +
+Other stream counts n (2 or 8) use the same recipe with n streams and
+(2+n)*n mixes; at n = 4 the draws are those of the table above.
+
+Distributions: streams X and sublayer output F ~ N(0, 1); W_mix [(2+n)n, nd]
+~ N(0, 0.02); base [(2+n)n] ~ N(0, 0.1); scale [3] ~ U(0.5, 2); gamma [d] ~ 1 +
 N(0, 0.05). N(mu, s) names the standard deviation s. Values are drawn in
 float32 and rounded to bf16 (round-to-nearest-even) where the workload is bf16.
 """
@@ -54,6 +57,11 @@ class Workload:
     norm_eps: float = 1e-6
     hc_eps: float = 1e-6
     batch: int = 1
+    n: int = N_STREAMS
+
+    @property
+    def n_mix(self) -> int:
+        return (2 + self.n) * self.n
 
     @property
     def n_outliers(self) -> int:
@@ -105,9 +113,9 @@ def _token_chunk(wl: Workload, tensor: int, step: int, c: int, width: int) -> np
 
 
 def token_rows(wl: Workload, tensor: int, tokens, step: int = 0) -> np.ndarray:
-    """float32 rows of a token-indexed tensor (X: width 4d, F: width d) for the
+    """float32 rows of a token-indexed tensor (X: width n*d, F: width d) for the
     given token indices, drawn exactly as the full tensor would be."""
-    width = N_STREAMS * wl.d if tensor == X else wl.d
+    width = wl.n * wl.d if tensor == X else wl.d
     tokens = np.asarray(tokens, dtype=np.int64)
     out = np.empty((len(tokens), width), dtype=np.float32)
     for c in np.unique(tokens // CHUNK):
@@ -119,18 +127,18 @@ def token_rows(wl: Workload, tensor: int, tokens, step: int = 0) -> np.ndarray:
 
 def token_tensor_chunks(wl: Workload, tensor: int, step: int = 0):
     """Yield (t0, float32 block) over the whole token range."""
-    width = N_STREAMS * wl.d if tensor == X else wl.d
+    width = wl.n * wl.d if tensor == X else wl.d
     nchunks = (wl.tokens + CHUNK - 1) // CHUNK
     for c in range(nchunks):
         yield c * CHUNK, _token_chunk(wl, tensor, step, c, width)
 
 
 def streams(wl: Workload, step: int = 0, tokens=None):
-    """X as a torch CPU tensor [T, 4, d] in the workload dtype."""
+    """X as a torch CPU tensor [T, n, d] in the workload dtype."""
     if tokens is None:
         tokens = np.arange(wl.tokens)
     a = token_rows(wl, X, tokens, step)
-    return to_dtype(a, wl.dtype).reshape(len(tokens), N_STREAMS, wl.d)
+    return to_dtype(a, wl.dtype).reshape(len(tokens), wl.n, wl.d)
 
 
 def sublayer_out(wl: Workload, step: int = 0, tokens=None):
@@ -142,14 +150,14 @@ def sublayer_out(wl: Workload, step: int = 0, tokens=None):
 
 
 def params(wl: Workload, step: int = 0, prev: bool = False) -> dict:
-    """fp32 parameters (numpy) of one sublayer: w_mix [24, 4d], base [24],
-    scale [3], gamma [d]. ``prev`` selects the independent set used to make the
+    """fp32 parameters (numpy) of one sublayer: w_mix [(2+n)n, nd], base
+    [(2+n)n], scale [3], gamma [d]. ``prev`` selects the independent set used to make the
     prior coefficients."""
     tw, tb, ts = (W_PREV, BASE_PREV, SCALE_PREV) if prev else (W, BASE, SCALE)
     d = wl.d
-    w = (_rng(wl.wid, tw, step).standard_normal((N_MIX, N_STREAMS * d), dtype=np.float32)
+    w = (_rng(wl.wid, tw, step).standard_normal((wl.n_mix, wl.n * d), dtype=np.float32)
          * np.float32(0.02))
-    b = _rng(wl.wid, tb, step).standard_normal(N_MIX, dtype=np.float32) * np.float32(0.1)
+    b = _rng(wl.wid, tb, step).standard_normal(wl.n_mix, dtype=np.float32) * np.float32(0.1)
     s = _rng(wl.wid, ts, step).uniform(0.5, 2.0, size=3).astype(np.float32)
     g = (np.float32(1.0)
          + _rng(wl.wid, GAMMA, step).standard_normal(d, dtype=np.float32) * np.float32(0.05))

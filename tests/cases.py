@@ -17,10 +17,10 @@ from stream_hyper_connections_amd import workloads as wl
 
 def oracle_prior(x_cpu, prev, iters=20, norm_eps=1e-6, hc_eps=1e-6, chunk=1024):
     """Oracle mixes of the streams with parameters ``prev``, as float32 numpy."""
-    t = x_cpu.shape[0]
-    pre = np.empty((t, 4), np.float32)
-    post = np.empty((t, 4), np.float32)
-    comb = np.empty((t, 4, 4), np.float32)
+    t, n = x_cpu.shape[0], x_cpu.shape[1]
+    pre = np.empty((t, n), np.float32)
+    post = np.empty((t, n), np.float32)
+    comb = np.empty((t, n, n), np.float32)
     for t0 in range(0, t, chunk):
         xs = x_cpu[t0:t0 + chunk].double().numpy()
         _, p, u, c = oracle.mixes(xs, prev["w_mix"], prev["base"], prev["scale"], iters,

@@ -67,24 +67,29 @@ def test_worked_example_through_split_sinkhorn_n2(iters, key):
     np.testing.assert_allclose(comb[0], _mat(G[key]), rtol=0, atol=1e-15)
 
 
+@pytest.mark.parametrize("n", [4, 8])
 @pytest.mark.parametrize("iters,key", [(1, "round1"), (2, "round2")])
-def test_worked_example_kronecker_into_4x4(iters, key):
-    """A (x) J2 has Sinkhorn iterates (iterates of A) (x) J2 / 2; this drives the
-    n = 4 path with the course's example."""
+def test_worked_example_kronecker(iters, key, n):
+    """A (x) J_b (b = n/2) has Sinkhorn iterates (iterates of A) (x) J_b / b;
+    this drives the n = 4 and n = 8 schedules with the course's example."""
+    b = n // 2
     a = _mat(G["input"])
-    big = np.kron(a, np.ones((2, 2)))
-    m = _logits_to_m(np.log(big)[None], 4)
-    _, _, comb = split_sinkhorn(m, [1, 1, 1], np.zeros(24), iters=iters, hc_eps=0.0, n=4)
-    want = np.kron(_mat(G[key]), np.ones((2, 2)) / 2)
+    big = np.kron(a, np.ones((b, b)))
+    m = _logits_to_m(np.log(big)[None], n)
+    _, _, comb = split_sinkhorn(m, [1, 1, 1], np.zeros((2 + n) * n), iters=iters, hc_eps=0.0,
+                                n=n)
+    want = np.kron(_mat(G[key]), np.ones((b, b)) / b)
     np.testing.assert_allclose(comb[0], want, rtol=0, atol=1e-15)
 
 
-def test_worked_example_kronecker_20_rounds():
+@pytest.mark.parametrize("n", [4, 8])
+def test_worked_example_kronecker_20_rounds(n):
+    b = n // 2
     a = _mat(G["input"])
-    m = _logits_to_m(np.log(np.kron(a, np.ones((2, 2))))[None], 4)
-    _, _, comb = split_sinkhorn(m, [1, 1, 1], np.zeros(24), iters=20, hc_eps=0.0, n=4)
+    m = _logits_to_m(np.log(np.kron(a, np.ones((b, b))))[None], n)
+    _, _, comb = split_sinkhorn(m, [1, 1, 1], np.zeros((2 + n) * n), iters=20, hc_eps=0.0, n=n)
     t = G["limit_t"]
-    want = np.kron(np.array([[t, 1 - t], [1 - t, t]]), np.ones((2, 2)) / 2)
+    want = np.kron(np.array([[t, 1 - t], [1 - t, t]]), np.ones((b, b)) / b)
     np.testing.assert_allclose(comb[0], want, rtol=0, atol=1e-12)
     assert np.all(np.abs(comb.sum(axis=1) - 1) < G["sum_tol_after_20"])
     assert np.all(np.abs(comb.sum(axis=2) - 1) < G["sum_tol_after_20"])
@@ -177,24 +182,26 @@ def test_zero_mixes():
     np.testing.assert_allclose(post[0], 2 * expit(base[4:8]), rtol=1e-15)
 
 
-@pytest.mark.parametrize("slot", range(24))
-def test_each_slot_moves_only_its_own_output(slot):
-    """Slots 0-3 feed pre[j], 4-7 post[k], 8-23 comb row (slot-8)//4."""
-    base = np.zeros(24)
-    p0, u0, c0 = split_sinkhorn(np.zeros((1, 24)), [1, 1, 1], base, iters=1, hc_eps=0.0)
-    m = np.zeros((1, 24))
+@pytest.mark.parametrize("n,slot", [(4, s) for s in range(24)] + [(2, s) for s in range(8)]
+                         + [(8, s) for s in (0, 7, 8, 15, 16, 17, 23, 42, 79)])
+def test_each_slot_moves_only_its_own_output(n, slot):
+    """Slots 0..n-1 feed pre[j], n..2n-1 post[k], 2n + j*n + k comb entry (j, k)."""
+    nm = (2 + n) * n
+    base = np.zeros(nm)
+    p0, u0, c0 = split_sinkhorn(np.zeros((1, nm)), [1, 1, 1], base, iters=1, hc_eps=0.0, n=n)
+    m = np.zeros((1, nm))
     m[0, slot] = 1.0
-    p1, u1, c1 = split_sinkhorn(m, [1, 1, 1], base, iters=1, hc_eps=0.0)
+    p1, u1, c1 = split_sinkhorn(m, [1, 1, 1], base, iters=1, hc_eps=0.0, n=n)
     dp = np.nonzero(np.abs(p1 - p0)[0] > 1e-12)[0].tolist()
     du = np.nonzero(np.abs(u1 - u0)[0] > 1e-12)[0].tolist()
     # with iters = 1 and eps = 0 the column division spreads a row change over the
     # whole matrix, so look at the softmax row instead: the largest entry moves to k
-    if slot < 4:
+    if slot < n:
         assert dp == [slot] and du == []
-    elif slot < 8:
-        assert dp == [] and du == [slot - 4]
+    elif slot < 2 * n:
+        assert dp == [] and du == [slot - n]
     else:
-        j, k = divmod(slot - 8, 4)
+        j, k = divmod(slot - 2 * n, n)
         assert dp == [] and du == []
         assert np.argmax(c1[0, j]) == k
         assert np.argmax(c1[0, :, k]) == j

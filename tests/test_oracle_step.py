@@ -22,15 +22,15 @@ def _bf16_values(rng, shape, scale=1.0):
     return round_bf16(rng.standard_normal(shape) * scale)
 
 
-def _inputs(rng, t, d, dtype="bf16"):
-    xs = rng.standard_normal((t, N, d))
+def _inputs(rng, t, d, dtype="bf16", n=N):
+    xs = rng.standard_normal((t, n, d))
     f = rng.standard_normal((t, d))
     xs, f = round_to(xs, dtype), round_to(f, dtype)
-    pre = rng.uniform(0.1, 1.0, (t, N))
-    post = rng.uniform(0.1, 2.0, (t, N))
-    comb = rng.dirichlet(np.ones(N), size=(t, N))
-    w = rng.normal(0, 0.02, (24, N * d))
-    base = rng.normal(0, 0.1, 24)
+    pre = rng.uniform(0.1, 1.0, (t, n))
+    post = rng.uniform(0.1, 2.0, (t, n))
+    comb = rng.dirichlet(np.ones(n), size=(t, n))
+    w = rng.normal(0, 0.02, ((2 + n) * n, n * d))
+    base = rng.normal(0, 0.1, (2 + n) * n)
     scale = rng.uniform(0.5, 2, 3)
     gamma = 1 + rng.normal(0, 0.05, d)
     return xs, f, pre, post, comb, w, base, scale, gamma
@@ -234,12 +234,14 @@ def _brute_step(xs, f, pre, post, comb, w, base, scale, gamma, iters, norm_eps, 
     return xp, m, p_next, u_next, c, h, y
 
 
-@pytest.mark.parametrize("d", [1, 2, 8])
+@pytest.mark.parametrize("n,d", [(4, 1), (4, 2), (4, 8), (2, 1), (2, 8), (8, 1), (8, 2)])
 @pytest.mark.parametrize("dtype,bits", [("bf16", 8), ("f32", 24)])
-def test_step_brute_force_tiny_d(d, dtype, bits):
-    rng = np.random.default_rng(100 + d)
-    t = 3
-    xs, f, pre, post, comb, w, base, scale, gamma = _inputs(rng, t, d, dtype)
+def test_step_brute_force_tiny_d(n, d, dtype, bits):
+    """Every stream count the pages' shapes allow (hc_mult = 2, 4, 8): the
+    mixes vector has (2+n)*n slots over n*d flattened columns."""
+    rng = np.random.default_rng(100 + d + 1000 * (n != 4) * n)
+    t = 3 if n == 4 else 2
+    xs, f, pre, post, comb, w, base, scale, gamma = _inputs(rng, t, d, dtype, n)
     iters, norm_eps, hc_eps = 20, 1e-6, 1e-6
     o = fused_step(xs, f, pre, post, comb, w, base, scale, gamma, iters, norm_eps, hc_eps, dtype)
     with mpmath.workdps(60):
