@@ -82,6 +82,78 @@ def algorithmic_bytes(tokens: int, d: int, elem: int) -> int:
     return tokens * per_token + per_call
 
 
+def algorithmic_bytes_n(tokens: int, d: int, elem: int, n: int) -> int:
+    """Bytes one call of the general-n step must move: the streams ((2n+2)*d
+    elements per token), the prior coefficients read and the new ones written
+    ((2n + n^2) floats each way), the mixes written ((2+n)n floats, an output
+    of that entry point), plus the float32 parameters once."""
+    nm = (2 + n) * n
+    per_token = (2 * n + 2) * d * elem + (2 * (2 * n + n * n) + nm) * 4
+    per_call = (nm * n * d + nm + 3 + d) * 4
+    return tokens * per_token + per_call
+
+
+N_SWEEP = (2, 4, 8)
+
+
+def general_n_bench(w0, steps, warmup):
+    """mhc_fused_step_n at the workload's shape for n = 2, 4, 8: one JSON line
+    each (HIP events around the call, which runs the block kernel and the
+    split/Sinkhorn kernel)."""
+    import dataclasses
+    import torch
+    import stream_hyper_connections_amd as mhc
+    from stream_hyper_connections_amd import workloads as wl
+    dev = torch.device("cuda:0")
+    for n in N_SWEEP:
+        w = dataclasses.replace(w0, name=f"{w0.name}_n{n}", n=n)
+        dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        elem = 2 if w.dtype == "bf16" else 4
+        x = upload_tokens(w, wl.X, 0, dev, dt).view(w.tokens, n, w.d)
+        f = upload_tokens(w, wl.F, 0, dev, dt)
+        prev = {k: torch.as_tensor(v).to(dev) for k, v in wl.params(w, prev=True).items()}
+        cur = {k: torch.as_tensor(v).to(dev) for k, v in wl.params(w).items()}
+        prior = mhc.mixes_n(x, mhc.pack_wmix_n(prev["w_mix"], w.dtype), prev["base"],
+                            prev["scale"], w.iters, w.norm_eps, w.hc_eps)
+        wp = mhc.pack_wmix_n(cur["w_mix"], w.dtype)
+        outs = dict(x_out=torch.empty_like(x), y_out=torch.empty_like(f),
+                    pre_out=torch.empty_like(prior["pre"]),
+                    post_out=torch.empty_like(prior["post"]),
+                    comb_out=torch.empty_like(prior["comb"]),
+                    mix_out=torch.empty_like(prior["mix"]))
+
+        def call():
+            mhc.fused_step_n(x, f, prior["pre"], prior["post"], prior["comb"], wp, cur["base"],
+                             cur["scale"], cur["gamma"], w.iters, w.norm_eps, w.hc_eps, **outs)
+
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        a = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        b = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        for i in range(steps):
+            a[i].record()
+            call()
+            b[i].record()
+        torch.cuda.synchronize()
+        ms = np.array([x0.elapsed_time(x1) for x0, x1 in zip(a, b)])
+        alg = algorithmic_bytes_n(w.tokens, w.d, elem, n)
+        achieved = alg / (ms.mean() / 1e3) / 1e9
+        print(json.dumps({
+            "metric": f"tokens/s of the general-n fused step, n={n} d={w.d}",
+            "value": round(w.tokens / (ms.mean() / 1e3), 1), "unit": "tokens/s",
+            "n_streams": n, "tokens": w.tokens, "d": w.d, "dtype": w.dtype,
+            "call_ms_avg": round(float(ms.mean()), 5),
+            "call_ms_p50": round(float(np.percentile(ms, 50)), 5),
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                         "traffic": None, "algorithmic_bytes_per_launch": alg,
+                         "kernel": "gen::block_kernel + gen::sinkhorn_kernel"},
+            "config": {"workload": w.name, "sinkhorn_iters": w.iters}}), flush=True)
+        del x, f, prior, outs
+        torch.cuda.empty_cache()
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -98,6 +170,9 @@ def parse():
                     help="time the split/Sinkhorn kernel (mhc_sinkhorn4) on the workload's mixes "
                          "for a range of iteration counts and report row-sum convergence; one "
                          "JSON line per count")
+    ap.add_argument("--n-sweep", action="store_true",
+                    help="time the general stream-count step (mhc_fused_step_n) at the "
+                         "workload's shape for n = 2, 4, 8; one JSON line per n")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain device-to-device copy of 2 GiB instead (the reference "
                          "kernel for scaling the HBM byte counters)")
@@ -158,7 +233,7 @@ def upload_tokens(w, tensor, step, dev, dtype_t):
     """Draw a token-indexed tensor chunk by chunk straight into device memory."""
     import torch
     from stream_hyper_connections_amd import workloads as wl
-    width = N * w.d if tensor == wl.X else w.d
+    width = w.n * w.d if tensor == wl.X else w.d
     out = torch.empty((w.tokens, width), dtype=dtype_t, device=dev)
     for t0, blk in wl.token_tensor_chunks(w, tensor, step):
         out[t0:t0 + len(blk)].copy_(wl.to_dtype(blk, w.dtype))
@@ -215,6 +290,9 @@ def main():
         return
     mhc.load()
     w = wl.WORKLOADS[args.workload]
+    if args.n_sweep:
+        general_n_bench(w, args.steps, args.warmup)
+        return
     dev = torch.device("cuda:0")
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     elem = 2 if w.dtype == "bf16" else 4

@@ -1,6 +1,7 @@
 /*
  * mhc.h -- C ABI of libmhc, the MI355X (gfx950) implementation of the
- * Single-Pass mHC residual step with n = 4 residual streams.
+ * Single-Pass mHC residual step: tuned kernels for n = 4 residual streams and
+ * a general family (the *_n entry points) for n in {2, 4, 8}.
  *
  * Pages this interface follows (cited by title and section):
  *   [SW] "DeepSeek V4.1 · Stream weights for the feed-forward": the formula list
@@ -41,7 +42,7 @@
 extern "C" {
 #endif
 
-#define MHC_ABI_VERSION 3
+#define MHC_ABI_VERSION 4
 #define MHC_N_STREAMS 4
 #define MHC_N_MIX 24
 
@@ -202,6 +203,60 @@ mhc_status mhc_sinkhorn4(const float* mixes, int64_t tokens, const float* base,
                          const float* scale, int32_t sinkhorn_iters, float hc_eps,
                          float* pre_out, float* post_out, float* comb_out,
                          mhc_stream_t stream);
+
+/*
+ * Any stream count n in {2, 4, 8} ([SW] Code: the Block constructor sizes the
+ * projection as (2+n)*n rows over n*d columns -- mixes slots 0..n-1 pre,
+ * n..2n-1 post, 2n+n*j+k comb -- and hc_pre, hc_post and the split kernel take
+ * hc_mult as a parameter). Same conventions as above with 4 replaced by n:
+ * x [T][n][d], pre/post [T][n], comb [T][n][n], mixes [T][(2+n)n], w_mix
+ * float32 [(2+n)n][n*d], base [(2+n)n]. n outside {2, 4, 8} is
+ * MHC_ERR_UNSUPPORTED. The packed projection of this family has its own
+ * layout (each of the three bf16 terms padded to whole 16-column tiles) and
+ * is not interchangeable with mhc_pack_wmix's.
+ */
+
+/* Bytes of the packed projection for n streams, width d and stream dtype, or
+ * -1 for a bad argument. */
+int64_t mhc_wmix_packed_bytes_n(int32_t n, int32_t d, int32_t dtype);
+
+/* Pack w_mix [(2+n)n][n*d] (float32) for mhc_fused_step_n / mhc_mixes_n; same
+ * rules as mhc_pack_wmix. */
+mhc_status mhc_pack_wmix_n(int32_t n, const float* w_mix, int32_t d, int32_t dtype,
+                           void* w_packed, int64_t packed_bytes, mhc_stream_t stream);
+
+/*
+ * mhc_fused_step_n -- mhc_fused_step for n streams: the same six formulas with
+ * sums over n streams and the RMS statistic over n*d values. Runs two kernels:
+ * one pass over the streams (hc_post, RMS statistic, projection, hc_pre,
+ * RMSNorm) that writes the mixes to mix_out, then the split/Sinkhorn of
+ * mhc_sinkhorn_n reading them back. mix_out [T][(2+n)n] is therefore
+ * REQUIRED (NULL is MHC_ERR_INVALID_ARG). No workspace.
+ */
+mhc_status mhc_fused_step_n(int32_t n, const void* x, const void* f, int32_t dtype,
+                            int64_t tokens, int32_t d, const float* pre_in,
+                            const float* post_in, const float* comb_in, const void* w_packed,
+                            const float* base, const float* scale, const float* gamma,
+                            int32_t sinkhorn_iters, float norm_eps, float hc_eps, void* x_out,
+                            void* y_out, float* pre_out, float* post_out, float* comb_out,
+                            float* mix_out, mhc_stream_t stream);
+
+/* mhc_mixes_n -- mhc_mixes for n streams; mix_out is required (as above). */
+mhc_status mhc_mixes_n(int32_t n, const void* x, int32_t dtype, int64_t tokens, int32_t d,
+                       const void* w_packed, const float* base, const float* scale,
+                       int32_t sinkhorn_iters, float norm_eps, float hc_eps, float* pre_out,
+                       float* post_out, float* comb_out, float* mix_out, mhc_stream_t stream);
+
+/*
+ * mhc_sinkhorn_n -- mhc_sinkhorn4 for n streams: mixes [T][(2+n)n] to pre,
+ * post [T][n] and comb [T][n][n], with m[n+k] for post and m[2n+n*j+k] for the
+ * comb logits. Each division by (sum + hc_eps) is a multiplication by the
+ * correctly rounded reciprocal.
+ */
+mhc_status mhc_sinkhorn_n(int32_t n, const float* mixes, int64_t tokens, const float* base,
+                          const float* scale, int32_t sinkhorn_iters, float hc_eps,
+                          float* pre_out, float* post_out, float* comb_out,
+                          mhc_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -12,18 +12,24 @@ from .binding import (  # noqa: F401
     d_granule,
     SPLIT_MIN_TOKENS,
     fused_step,
+    fused_step_n,
     fused_step_workspace_bytes,
     hc_post,
     hc_pre,
     last_error,
     load,
     mixes,
+    mixes_n,
+    n_mix,
     pack_wmix,
+    pack_wmix_n,
     rmsnorm,
     sinkhorn4,
+    sinkhorn_n,
     split_status,
     status_string,
     three_kernel_step,
     wmix_packed_bytes,
+    wmix_packed_bytes_n,
     workspace_for,
 )

@@ -43,6 +43,16 @@ _SIGS = {
     "mhc_rmsnorm": ([_c_void_p, _i32, _i64, _i32, _c_void_p, _f32, _c_void_p, _c_void_p], _i32),
     "mhc_sinkhorn4": ([_c_void_p, _i64, _c_void_p, _c_void_p, _i32, _f32, _c_void_p, _c_void_p,
                        _c_void_p, _c_void_p], _i32),
+    "mhc_wmix_packed_bytes_n": ([_i32, _i32, _i32], _i64),
+    "mhc_pack_wmix_n": ([_i32, _c_void_p, _i32, _i32, _c_void_p, _i64, _c_void_p], _i32),
+    "mhc_fused_step_n": ([_i32, _c_void_p, _c_void_p, _i32, _i64, _i32, _c_void_p, _c_void_p,
+                          _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _f32, _f32,
+                          _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                          _c_void_p], _i32),
+    "mhc_mixes_n": ([_i32, _c_void_p, _i32, _i64, _i32, _c_void_p, _c_void_p, _c_void_p, _i32,
+                     _f32, _f32, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p], _i32),
+    "mhc_sinkhorn_n": ([_i32, _c_void_p, _i64, _c_void_p, _c_void_p, _i32, _f32, _c_void_p,
+                        _c_void_p, _c_void_p, _c_void_p], _i32),
 }
 
 _lib = None
@@ -299,3 +309,81 @@ def three_kernel_step(x, f, pre_in, post_in, comb_in, w_packed, base, scale, gam
     y = rmsnorm(h, gamma, norm_eps, y_out=y_out)
     return {"x_out": xo, "y": y, "pre": m["pre"], "post": m["post"], "comb": m["comb"],
             "mix": m["mix"], "h": h}
+
+
+# ----- any stream count n in {2, 4, 8} (the *_n entry points) -----------------------------
+
+def n_mix(n: int) -> int:
+    return (2 + n) * n
+
+
+def wmix_packed_bytes_n(n: int, d: int, dtype) -> int:
+    return load().mhc_wmix_packed_bytes_n(n, d, _dtype_name_code(dtype))
+
+
+def pack_wmix_n(w_mix: torch.Tensor, dtype, out: torch.Tensor | None = None) -> torch.Tensor:
+    """mhc_pack_wmix_n: float32 W [(2+n)n, n*d] -> packed operand buffer (uint8)."""
+    code = _dtype_name_code(dtype)
+    rows, cols = w_mix.shape
+    n = next((k for k in (2, 4, 8) if n_mix(k) == rows), None)
+    if n is None or cols % n:
+        raise ValueError(f"w_mix shape {tuple(w_mix.shape)} is not [(2+n)n, n*d] for n in 2, 4, 8")
+    d = cols // n
+    nbytes = load().mhc_wmix_packed_bytes_n(n, d, code)
+    if nbytes < 0:
+        raise ValueError(f"width {d} is not a positive multiple of {d_granule()}")
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=w_mix.device)
+    _check("mhc_pack_wmix_n", load().mhc_pack_wmix_n(n, _ptr(w_mix), d, code, _ptr(out),
+                                                     out.numel() * out.element_size(), _stream()))
+    return out
+
+
+def fused_step_n(x, f, pre_in, post_in, comb_in, w_packed, base, scale, gamma, iters=20,
+                 norm_eps=1e-6, hc_eps=1e-6, x_out=None, y_out=None, pre_out=None, post_out=None,
+                 comb_out=None, mix_out=None) -> dict:
+    """mhc_fused_step_n on tensors: x [T,n,d], f [T,d]; w_packed from pack_wmix_n.
+    Returns dict(x_out, y, pre, post, comb, mix) (mix is always produced)."""
+    t, n, d = x.shape
+    x_out = torch.empty_like(x) if x_out is None else x_out
+    y_out = torch.empty_like(f) if y_out is None else y_out
+    pre_out = _f32_out((t, n), x, pre_out)
+    post_out = _f32_out((t, n), x, post_out)
+    comb_out = _f32_out((t, n, n), x, comb_out)
+    mix_out = _f32_out((t, n_mix(n)), x, mix_out)
+    st = load().mhc_fused_step_n(
+        n, _ptr(x), _ptr(f), _dtype_code(x), t, d, _ptr(pre_in), _ptr(post_in), _ptr(comb_in),
+        _ptr(w_packed), _ptr(base), _ptr(scale), _ptr(gamma), iters, norm_eps, hc_eps,
+        _ptr(x_out), _ptr(y_out), _ptr(pre_out), _ptr(post_out), _ptr(comb_out), _ptr(mix_out),
+        _stream())
+    _check("mhc_fused_step_n", st)
+    return {"x_out": x_out, "y": y_out, "pre": pre_out, "post": post_out, "comb": comb_out,
+            "mix": mix_out}
+
+
+def mixes_n(x, w_packed, base, scale, iters=20, norm_eps=1e-6, hc_eps=1e-6, pre_out=None,
+            post_out=None, comb_out=None, mix_out=None) -> dict:
+    """mhc_mixes_n on tensors: x [T,n,d]. Returns dict(pre, post, comb, mix)."""
+    t, n, d = x.shape
+    pre_out = _f32_out((t, n), x, pre_out)
+    post_out = _f32_out((t, n), x, post_out)
+    comb_out = _f32_out((t, n, n), x, comb_out)
+    mix_out = _f32_out((t, n_mix(n)), x, mix_out)
+    st = load().mhc_mixes_n(n, _ptr(x), _dtype_code(x), t, d, _ptr(w_packed), _ptr(base),
+                            _ptr(scale), iters, norm_eps, hc_eps, _ptr(pre_out), _ptr(post_out),
+                            _ptr(comb_out), _ptr(mix_out), _stream())
+    _check("mhc_mixes_n", st)
+    return {"pre": pre_out, "post": post_out, "comb": comb_out, "mix": mix_out}
+
+
+def sinkhorn_n(n, mix, base, scale, iters=20, hc_eps=1e-6, pre_out=None, post_out=None,
+               comb_out=None) -> dict:
+    """mhc_sinkhorn_n on tensors: mix [T, (2+n)n] float32. Returns dict(pre, post, comb)."""
+    t = mix.shape[0]
+    pre_out = _f32_out((t, n), mix, pre_out)
+    post_out = _f32_out((t, n), mix, post_out)
+    comb_out = _f32_out((t, n, n), mix, comb_out)
+    st = load().mhc_sinkhorn_n(n, _ptr(mix), t, _ptr(base), _ptr(scale), iters, hc_eps,
+                               _ptr(pre_out), _ptr(post_out), _ptr(comb_out), _stream())
+    _check("mhc_sinkhorn_n", st)
+    return {"pre": pre_out, "post": post_out, "comb": comb_out}

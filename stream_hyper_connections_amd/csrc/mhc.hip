@@ -32,6 +32,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "mhc.h"
 
@@ -1108,6 +1109,7 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_kernel(StepArgs a, int nt
 
 #include "split_kernel.h"
 #include "unfused.h"
+#include "general_n.h"
 
 // ----- packing of the projection --------------------------------------------------------
 
@@ -1417,6 +1419,99 @@ mhc_status launch_step(const StepArgs& a, int32_t dtype, int mode, hipStream_t s
   return launch_status(what);
 }
 
+// ----- the general-n family ------------------------------------------------------------
+
+bool n_supported(int32_t n) { return n == 2 || n == 4 || n == 8; }
+
+int n_mix(int32_t n) { return (2 + n) * n; }
+
+int64_t packed_bytes_n(int32_t n, int32_t d, int32_t dtype) {
+  if (!n_supported(n) || d <= 0 || d % kStep != 0) return -1;
+  const int64_t steps = d / kStep;
+  auto vecs = [&](auto tag) -> int64_t {
+    constexpr int N = decltype(tag)::value;
+    return dtype == MHC_BF16 ? gen::Slice<N, MHC_BF16>::kVecs : gen::Slice<N, MHC_F32>::kVecs;
+  };
+  if (dtype != MHC_BF16 && dtype != MHC_F32) return -1;
+  int64_t v = 0;
+  switch (n) {
+    case 2: v = vecs(std::integral_constant<int, 2>{}); break;
+    case 4: v = vecs(std::integral_constant<int, 4>{}); break;
+    default: v = vecs(std::integral_constant<int, 8>{}); break;
+  }
+  return steps * v * 16;
+}
+
+template <int N>
+void launch_pack_n(const float* w, int d, int32_t dtype, int64_t total, void* out, hipStream_t st) {
+  const unsigned blocks = (unsigned)((total + 255) / 256);
+  if (dtype == MHC_BF16)
+    hipLaunchKernelGGL((gen::pack_kernel<N, MHC_BF16>), dim3(blocks), dim3(256), 0, st, w, d, total,
+                       static_cast<u32x4*>(out));
+  else
+    hipLaunchKernelGGL((gen::pack_kernel<N, MHC_F32>), dim3(blocks), dim3(256), 0, st, w, d, total,
+                       static_cast<u32x4*>(out));
+}
+
+template <int N, int DT, int SPI>
+void launch_block(const StepArgs& a, int mode, hipStream_t st) {
+  const unsigned grid = (unsigned)((a.tokens + gen::kBlock - 1) / gen::kBlock);
+  if (mode == kFused)
+    hipLaunchKernelGGL((gen::block_kernel<N, DT, kFused, SPI>), dim3(grid), dim3(gen::kThreads), 0,
+                       st, a);
+  else
+    hipLaunchKernelGGL((gen::block_kernel<N, DT, kMixesOnly, SPI>), dim3(grid),
+                       dim3(gen::kThreads), 0, st, a);
+}
+
+// bf16 streams with n <= 4 and an even step count run two steps per unit
+// (both halves of each 128-byte line of a token row loaded back to back)
+#ifndef MHC_GEN_UNIT2
+#define MHC_GEN_UNIT2 1
+#endif
+template <int N>
+void launch_block_n(const StepArgs& a, int32_t dtype, int mode, hipStream_t st) {
+  if (dtype == MHC_F32) {
+    launch_block<N, MHC_F32, 1>(a, mode, st);
+    return;
+  }
+  if constexpr (N <= 4) {
+    if (MHC_GEN_UNIT2 && (a.d / kStep) % 2 == 0) {
+      launch_block<N, MHC_BF16, 2>(a, mode, st);
+      return;
+    }
+  }
+  launch_block<N, MHC_BF16, 1>(a, mode, st);
+}
+
+template <int N>
+void launch_sinkhorn_n(const float* mix, int64_t tokens, const float* base, const float* scale,
+                       int iters, float eps, float* pre, float* post, float* comb, hipStream_t st) {
+  hipLaunchKernelGGL(gen::sinkhorn_kernel<N>, dim3((unsigned)((tokens + 255) / 256)), dim3(256), 0,
+                     st, mix, tokens, base, scale, iters, eps, pre, post, comb);
+}
+
+// The two kernels of the general step: one pass over the streams, then the
+// split/Sinkhorn of the mixes it wrote.
+mhc_status run_n(int32_t n, const StepArgs& a, int32_t dtype, int mode, hipStream_t st) {
+  switch (n) {
+    case 2: launch_block_n<2>(a, dtype, mode, st); break;
+    case 4: launch_block_n<4>(a, dtype, mode, st); break;
+    default: launch_block_n<8>(a, dtype, mode, st); break;
+  }
+  mhc_status s = launch_status("general-n step kernel launch");
+  if (s != MHC_OK) return s;
+  switch (n) {
+    case 2: launch_sinkhorn_n<2>(a.mix_out, a.tokens, a.base, a.scale, a.iters, a.hc_eps,
+                                 a.pre_out, a.post_out, a.comb_out, st); break;
+    case 4: launch_sinkhorn_n<4>(a.mix_out, a.tokens, a.base, a.scale, a.iters, a.hc_eps,
+                                 a.pre_out, a.post_out, a.comb_out, st); break;
+    default: launch_sinkhorn_n<8>(a.mix_out, a.tokens, a.base, a.scale, a.iters, a.hc_eps,
+                                  a.pre_out, a.post_out, a.comb_out, st); break;
+  }
+  return launch_status("general-n split/Sinkhorn kernel launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -1666,6 +1761,122 @@ mhc_status mhc_sinkhorn4(const float* mixes, int64_t tokens, const float* base,
                      static_cast<hipStream_t>(stream), mixes, tokens, base, scale, sinkhorn_iters,
                      hc_eps, pre_out, post_out, comb_out);
   return launch_status("split/Sinkhorn kernel launch");
+}
+
+int64_t mhc_wmix_packed_bytes_n(int32_t n, int32_t d, int32_t dtype) {
+  const int64_t b = packed_bytes_n(n, d, dtype);
+  if (b < 0) fail(MHC_ERR_INVALID_ARG, "bad n (%d), d (%d) or dtype (%d)", n, d, dtype);
+  return b;
+}
+
+mhc_status mhc_pack_wmix_n(int32_t n, const float* w_mix, int32_t d, int32_t dtype,
+                           void* w_packed, int64_t packed_bytes_given, mhc_stream_t stream) {
+  if (!n_supported(n)) return fail(MHC_ERR_UNSUPPORTED, "n = %d streams (2, 4 or 8 supported)", n);
+  const int64_t need = packed_bytes_n(n, d, dtype);
+  if (need < 0) return fail(MHC_ERR_INVALID_ARG, "bad d (%d) or dtype (%d)", d, dtype);
+  if (packed_bytes_given < need)
+    return fail(MHC_ERR_INVALID_ARG, "w_packed holds %lld bytes, %lld needed",
+                (long long)packed_bytes_given, (long long)need);
+  const Span in[] = {{"w_mix", w_mix, (uint64_t)n_mix(n) * n * d * 4}};
+  const Span out[] = {{"w_packed", w_packed, (uint64_t)need}};
+  mhc_status s = check_spans(in, 1, out, 1, nullptr, nullptr);
+  if (s != MHC_OK) return s;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t total = need / (dtype == MHC_BF16 ? 16 : 32);
+  switch (n) {
+    case 2: launch_pack_n<2>(w_mix, d, dtype, total, w_packed, st); break;
+    case 4: launch_pack_n<4>(w_mix, d, dtype, total, w_packed, st); break;
+    default: launch_pack_n<8>(w_mix, d, dtype, total, w_packed, st); break;
+  }
+  return launch_status("general-n pack kernel launch");
+}
+
+mhc_status mhc_fused_step_n(int32_t n, const void* x, const void* f, int32_t dtype,
+                            int64_t tokens, int32_t d, const float* pre_in,
+                            const float* post_in, const float* comb_in, const void* w_packed,
+                            const float* base, const float* scale, const float* gamma,
+                            int32_t sinkhorn_iters, float norm_eps, float hc_eps, void* x_out,
+                            void* y_out, float* pre_out, float* post_out, float* comb_out,
+                            float* mix_out, mhc_stream_t stream) {
+  if (!n_supported(n)) return fail(MHC_ERR_UNSUPPORTED, "n = %d streams (2, 4 or 8 supported)", n);
+  mhc_status s = check_common(dtype, tokens, d, sinkhorn_iters, norm_eps, hc_eps);
+  if (s != MHC_OK) return s;
+  if (tokens == 0) return ok();
+  const uint64_t es = elem_size(dtype), T = (uint64_t)tokens, nn = (uint64_t)n, nm = n_mix(n);
+  const Span in[] = {
+      {"x", x, T * nn * d * es},           {"f", f, T * d * es},
+      {"pre_in", pre_in, T * nn * 4},      {"post_in", post_in, T * nn * 4},
+      {"comb_in", comb_in, T * nn * nn * 4},
+      {"w_packed", w_packed, (uint64_t)packed_bytes_n(n, d, dtype)},
+      {"base", base, nm * 4},              {"scale", scale, 12},
+      {"gamma", gamma, (uint64_t)d * 4},
+  };
+  const Span out[] = {
+      {"x_out", x_out, T * nn * d * es},   {"y_out", y_out, T * d * es},
+      {"pre_out", pre_out, T * nn * 4},    {"post_out", post_out, T * nn * 4},
+      {"comb_out", comb_out, T * nn * nn * 4}, {"mix_out", mix_out, T * nm * 4},
+  };
+  s = check_spans(in, 9, out, 6, x_out, x);
+  if (s != MHC_OK) return s;
+  StepArgs a{x, f, pre_in, post_in, comb_in, w_packed, base, scale, gamma, x_out, y_out,
+             pre_out, post_out, comb_out, mix_out, tokens, d, sinkhorn_iters, norm_eps, hc_eps};
+  return run_n(n, a, dtype, kFused, static_cast<hipStream_t>(stream));
+}
+
+mhc_status mhc_mixes_n(int32_t n, const void* x, int32_t dtype, int64_t tokens, int32_t d,
+                       const void* w_packed, const float* base, const float* scale,
+                       int32_t sinkhorn_iters, float norm_eps, float hc_eps, float* pre_out,
+                       float* post_out, float* comb_out, float* mix_out, mhc_stream_t stream) {
+  if (!n_supported(n)) return fail(MHC_ERR_UNSUPPORTED, "n = %d streams (2, 4 or 8 supported)", n);
+  mhc_status s = check_common(dtype, tokens, d, sinkhorn_iters, norm_eps, hc_eps);
+  if (s != MHC_OK) return s;
+  if (tokens == 0) return ok();
+  const uint64_t es = elem_size(dtype), T = (uint64_t)tokens, nn = (uint64_t)n, nm = n_mix(n);
+  const Span in[] = {
+      {"x", x, T * nn * d * es},
+      {"w_packed", w_packed, (uint64_t)packed_bytes_n(n, d, dtype)},
+      {"base", base, nm * 4},
+      {"scale", scale, 12},
+  };
+  const Span out[] = {
+      {"pre_out", pre_out, T * nn * 4}, {"post_out", post_out, T * nn * 4},
+      {"comb_out", comb_out, T * nn * nn * 4}, {"mix_out", mix_out, T * nm * 4},
+  };
+  s = check_spans(in, 4, out, 4, nullptr, nullptr);
+  if (s != MHC_OK) return s;
+  StepArgs a{x, nullptr, nullptr, nullptr, nullptr, w_packed, base, scale, nullptr, nullptr,
+             nullptr, pre_out, post_out, comb_out, mix_out, tokens, d, sinkhorn_iters, norm_eps,
+             hc_eps};
+  return run_n(n, a, dtype, kMixesOnly, static_cast<hipStream_t>(stream));
+}
+
+mhc_status mhc_sinkhorn_n(int32_t n, const float* mixes, int64_t tokens, const float* base,
+                          const float* scale, int32_t sinkhorn_iters, float hc_eps,
+                          float* pre_out, float* post_out, float* comb_out,
+                          mhc_stream_t stream) {
+  if (!n_supported(n)) return fail(MHC_ERR_UNSUPPORTED, "n = %d streams (2, 4 or 8 supported)", n);
+  if (tokens < 0) return fail(MHC_ERR_INVALID_ARG, "tokens must be >= 0");
+  if (sinkhorn_iters < 1) return fail(MHC_ERR_INVALID_ARG, "sinkhorn_iters must be >= 1");
+  if (!(hc_eps >= 0.f) || !isfinite(hc_eps))
+    return fail(MHC_ERR_INVALID_ARG, "hc_eps must be finite and >= 0");
+  if (tokens > ((int64_t)1 << 35)) return fail(MHC_ERR_UNSUPPORTED, "too many tokens");
+  if (tokens == 0) return ok();
+  const uint64_t T = (uint64_t)tokens, nn = (uint64_t)n, nm = n_mix(n);
+  const Span in[] = {{"mixes", mixes, T * nm * 4}, {"base", base, nm * 4}, {"scale", scale, 12}};
+  const Span out[] = {{"pre_out", pre_out, T * nn * 4}, {"post_out", post_out, T * nn * 4},
+                      {"comb_out", comb_out, T * nn * nn * 4}};
+  mhc_status s = check_spans(in, 3, out, 3, nullptr, nullptr);
+  if (s != MHC_OK) return s;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  switch (n) {
+    case 2: launch_sinkhorn_n<2>(mixes, tokens, base, scale, sinkhorn_iters, hc_eps, pre_out,
+                                 post_out, comb_out, st); break;
+    case 4: launch_sinkhorn_n<4>(mixes, tokens, base, scale, sinkhorn_iters, hc_eps, pre_out,
+                                 post_out, comb_out, st); break;
+    default: launch_sinkhorn_n<8>(mixes, tokens, base, scale, sinkhorn_iters, hc_eps, pre_out,
+                                  post_out, comb_out, st); break;
+  }
+  return launch_status("general-n split/Sinkhorn kernel launch");
 }
 
 }  // extern "C"

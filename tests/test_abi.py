@@ -28,7 +28,8 @@ def test_header_declares_the_entry_points():
     for fn in ("mhc_fused_step", "mhc_mixes", "mhc_sinkhorn4", "mhc_pack_wmix",
                "mhc_wmix_packed_bytes", "mhc_status_string", "mhc_last_error",
                "mhc_abi_version", "mhc_d_granule", "mhc_fused_step_workspace_bytes",
-               "mhc_hc_post", "mhc_hc_pre", "mhc_rmsnorm"):
+               "mhc_hc_post", "mhc_hc_pre", "mhc_rmsnorm", "mhc_wmix_packed_bytes_n",
+               "mhc_pack_wmix_n", "mhc_fused_step_n", "mhc_mixes_n", "mhc_sinkhorn_n"):
         assert fn in names
 
 
@@ -40,7 +41,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_granule_and_status_strings():
-    assert binding.abi_version() == 3
+    assert binding.abi_version() == 4
     assert binding.d_granule() == 32
     lib = binding.load()
     assert lib.mhc_status_string(0) == b"MHC_OK"
@@ -192,3 +193,96 @@ def test_unfused_entry_points_validate():
                            None) == binding.MHC_ERR_INVALID_ARG
     assert lib.mhc_rmsnorm(p["y_out"], binding.MHC_BF16, 0, D, p["gamma"], 1e-6, p["y_out"],
                            None) == binding.MHC_OK
+
+
+# ---- the general-n family --------------------------------------------------------------
+
+def test_packed_bytes_n():
+    lib = binding.load()
+    # bf16: three terms, each padded to ceil((2+n)n / 16) tiles of 16 columns
+    for n, tiles in ((2, 3), (4, 6), (8, 15)):
+        assert lib.mhc_wmix_packed_bytes_n(n, 5120, binding.MHC_BF16) == 160 * n * tiles * 64 * 16
+    for n, tiles in ((2, 1), (4, 2), (8, 5)):
+        assert lib.mhc_wmix_packed_bytes_n(n, 5120, binding.MHC_F32) == 160 * n * tiles * 64 * 32
+    for args in ((3, 5120, binding.MHC_BF16), (8, 40, binding.MHC_BF16), (2, 64, 5)):
+        assert lib.mhc_wmix_packed_bytes_n(*args) == -1
+
+
+def _layout_n(n):
+    nm = (2 + n) * n
+    sizes = {
+        "x": T * n * D * ES, "f": T * D * ES, "pre_in": T * n * 4, "post_in": T * n * 4,
+        "comb_in": T * n * n * 4, "w_packed": 1 << 24, "base": nm * 4, "scale": 12,
+        "gamma": D * 4, "x_out": T * n * D * ES, "y_out": T * D * ES, "pre_out": T * n * 4,
+        "post_out": T * n * 4, "comb_out": T * n * n * 4, "mix_out": T * nm * 4,
+    }
+    addr, p = A, {}
+    for k, sz in sizes.items():
+        p[k] = addr
+        addr += (sz + 4095) // 4096 * 4096
+    return p
+
+
+def _call_n(n_layout, **over):
+    p = _layout_n(n_layout)
+    args = dict(n=n_layout, x=p["x"], f=p["f"], dtype=binding.MHC_BF16, tokens=T, d=D,
+                pre_in=p["pre_in"], post_in=p["post_in"], comb_in=p["comb_in"],
+                w_packed=p["w_packed"], base=p["base"], scale=p["scale"], gamma=p["gamma"],
+                iters=20, norm_eps=1e-6, hc_eps=1e-6, x_out=p["x_out"], y_out=p["y_out"],
+                pre_out=p["pre_out"], post_out=p["post_out"], comb_out=p["comb_out"],
+                mix_out=p["mix_out"], stream=None)
+    args.update(over)
+    return binding.load().mhc_fused_step_n(*args.values())
+
+
+@pytest.mark.parametrize("n", [2, 4, 8])
+@pytest.mark.parametrize("over,needle", [
+    (dict(d=48), "multiple"),
+    (dict(iters=0), "sinkhorn_iters"),
+    (dict(mix_out=None), "mix_out is NULL"),
+    (dict(comb_in=None), "comb_in is NULL"),
+    (dict(post_out=A + 4), "not 16-byte aligned"),
+    (dict(x_out="x+16"), "overlaps input"),
+    (dict(mix_out="comb_out"), "overlap"),
+])
+def test_fused_step_n_rejects_bad_arguments(n, over, needle):
+    p = _layout_n(n)
+    over = {k: (p[v.split("+")[0]] + int(v.split("+")[1]) if isinstance(v, str) and "+" in v
+                else p[v] if isinstance(v, str) else v) for k, v in over.items()}
+    assert _call_n(n, **over) == binding.MHC_ERR_INVALID_ARG
+    assert needle in binding.last_error()
+
+
+def test_fused_step_n_stream_counts_and_zero_tokens():
+    for n in (1, 3, 5, 16):
+        assert _call_n(4, n=n) == binding.MHC_ERR_UNSUPPORTED
+        assert "streams" in binding.last_error()
+    for n in (2, 4, 8):
+        assert _call_n(n, tokens=0) == binding.MHC_OK
+        assert _call_n(n, tokens=0, x_out=_layout_n(n)["x"]) == binding.MHC_OK
+
+
+def test_mixes_n_sinkhorn_n_pack_n_validation():
+    lib = binding.load()
+    p = _layout_n(8)
+    st = lib.mhc_mixes_n(8, p["x"], binding.MHC_BF16, T, D, p["w_packed"], p["base"], p["scale"],
+                         20, 1e-6, 1e-6, p["pre_out"], p["post_out"], p["comb_out"], None, None)
+    assert st == binding.MHC_ERR_INVALID_ARG and "mix_out is NULL" in binding.last_error()
+    st = lib.mhc_mixes_n(6, p["x"], binding.MHC_BF16, T, D, p["w_packed"], p["base"], p["scale"],
+                         20, 1e-6, 1e-6, p["pre_out"], p["post_out"], p["comb_out"], p["mix_out"],
+                         None)
+    assert st == binding.MHC_ERR_UNSUPPORTED
+    st = lib.mhc_sinkhorn_n(8, p["mix_out"], T, p["base"], p["scale"], 20, 1e-6, p["pre_out"],
+                            p["pre_out"], p["comb_out"], None)
+    assert st == binding.MHC_ERR_INVALID_ARG and "overlap" in binding.last_error()
+    st = lib.mhc_sinkhorn_n(2, p["mix_out"], T, p["base"], p["scale"], 0, 1e-6, p["pre_out"],
+                            p["post_out"], p["comb_out"], None)
+    assert st == binding.MHC_ERR_INVALID_ARG
+    st = lib.mhc_sinkhorn_n(4, p["mix_out"], 0, p["base"], p["scale"], 20, 1e-6, p["pre_out"],
+                            p["post_out"], p["comb_out"], None)
+    assert st == binding.MHC_OK
+    need = lib.mhc_wmix_packed_bytes_n(8, D, binding.MHC_BF16)
+    assert lib.mhc_pack_wmix_n(8, p["x"], D, binding.MHC_BF16, p["w_packed"], need - 16,
+                               None) == binding.MHC_ERR_INVALID_ARG
+    assert lib.mhc_pack_wmix_n(5, p["x"], D, binding.MHC_BF16, p["w_packed"], need,
+                               None) == binding.MHC_ERR_UNSUPPORTED

@@ -1,0 +1,222 @@
+"""GPU parity of the general stream-count family (mhc_*_n, n in {2, 4, 8}).
+
+Every case is checked against the float64 oracle with the rules of
+tests/parity.py (new streams as correct roundings, everything after them
+teacher-forced on the validated new streams). Cases cover n = 2, 4, 8, bf16
+and f32 streams, widths from one 32-feature step to d = 5120, odd step counts,
+token counts from one token to several 128-token blocks with a ragged last
+block, in-place updates, guard bands around every output, and, at n = 4,
+agreement with the tuned n = 4 kernels (same per-element arithmetic, so the
+new streams must match bit for bit). The largest case runs n = 8 at the
+throughput shape (65,536 tokens, d = 5120) exactly as the benchmark launches
+it, with sampled tokens checked in full.
+"""
+
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import stream_hyper_connections_amd as mhc
+from stream_hyper_connections_amd import workloads as wl
+from tests.cases import make_case, oracle_prior, run_step, to_dev
+from tests.conftest import load_golden
+from tests.parity import check_comb, check_mix_like, check_mixes, check_step, comb_sum_stats
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def _dev(case):
+    return {k: to_dev(case[k]) for k in ("x", "f", "pre", "post", "comb", "w_mix", "base",
+                                         "scale", "gamma")}
+
+
+def run_step_n(case, dtype, **kw):
+    dev = _dev(case)
+    wp = mhc.pack_wmix_n(dev["w_mix"], dtype)
+    out = mhc.fused_step_n(dev["x"], dev["f"], dev["pre"], dev["post"], dev["comb"], wp,
+                           dev["base"], dev["scale"], dev["gamma"], case["iters"],
+                           case["norm_eps"], case["hc_eps"], **kw)
+    torch.cuda.synchronize()
+    return {k: v.cpu() for k, v in out.items()}, dev
+
+
+CASES = [
+    # n, dtype, d, tokens
+    (2, "bf16", 5120, 300),
+    (2, "bf16", 256, 129),
+    (2, "f32", 64, 17),
+    (4, "bf16", 5120, 257),
+    (4, "bf16", 2080, 100),     # 65 steps: odd count
+    (4, "f32", 96, 33),
+    (8, "bf16", 5120, 200),
+    (8, "bf16", 32, 130),       # a single step
+    (8, "bf16", 1024, 1),       # one token: one lane of one wave works
+    (8, "f32", 128, 40),
+]
+
+
+@pytest.mark.parametrize("n,dtype,d,t", CASES)
+def test_general_n_parity(n, dtype, d, t):
+    _log(f"general n={n} {dtype} d={d} T={t}")
+    case = make_case(wl.Workload(700 + 10 * n + d % 7 + t % 5, "general_n", t, d, dtype, n=n))
+    out, _ = run_step_n(case, dtype)
+    o = check_step(case, out, dtype)
+    _log(f"  ties in new streams: {o['n_ties']}; comb sums {comb_sum_stats(out['comb'])}")
+
+
+def test_general_n4_matches_tuned_kernels():
+    case = make_case(wl.Workload(760, "general_n4", 700, 5120, "bf16"))
+    a, _ = run_step_n(case, "bf16")
+    for path in ("split", "tile"):
+        b, _ = run_step(case, path=path)
+        assert torch.equal(a["x_out"], b["x_out"]), path
+        ya, yb = a["y"].float(), b["y"].float()
+        assert ((ya - yb).abs() <= torch.maximum(ya.abs(), yb.abs()) * 2.0 ** -7 + 1e-30).all()
+        # the mixes are summed in another order (|m| up to ~10 here)
+        for k in ("pre", "post", "comb", "mix"):
+            np.testing.assert_allclose(a[k].numpy(), b[k].numpy(), rtol=1e-5, atol=2e-5)
+
+
+@pytest.mark.parametrize("n,dtype,d,t", [(2, "bf16", 5120, 1000), (8, "bf16", 2048, 300),
+                                         (8, "f32", 64, 129)])
+def test_mixes_n_parity(n, dtype, d, t):
+    w = wl.Workload(770 + n, "mixes_n", t, d, dtype, n=n)
+    x = wl.streams(w)
+    p = wl.params(w)
+    out = mhc.mixes_n(to_dev(x), mhc.pack_wmix_n(to_dev(p["w_mix"]), dtype), to_dev(p["base"]),
+                      to_dev(p["scale"]))
+    torch.cuda.synchronize()
+    check_mixes(dict(x=x, **p), {k: v.cpu() for k, v in out.items()}, dtype)
+
+
+@pytest.mark.parametrize("n", [2, 4, 8])
+@pytest.mark.parametrize("iters", [1, 2, 20])
+def test_sinkhorn_n_parity(n, iters):
+    rng = np.random.default_rng(780 + n + iters)
+    nm = (2 + n) * n
+    m = rng.normal(0, 3.0, (517, nm)).astype(np.float32)
+    base = rng.normal(0, 0.1, nm).astype(np.float32)
+    scale = rng.uniform(0.5, 2.0, 3).astype(np.float32)
+    out = mhc.sinkhorn_n(n, to_dev(m), to_dev(base), to_dev(scale), iters, 1e-6)
+    torch.cuda.synchronize()
+    pre, post, comb = oracle.split_sinkhorn(m, scale, base, iters, 1e-6, n)
+    check_mix_like("pre", out["pre"].cpu(), pre)
+    check_mix_like("post", out["post"].cpu(), post)
+    check_comb(out["comb"].cpu(), comb, 1e-6, iters)
+
+
+@pytest.mark.parametrize("n", [4, 8])
+def test_sinkhorn_n_worked_example(n):
+    """The course page's hand-checked 2x2 example ("2A · Single-Pass mHC", §4)
+    through A (x) J_b (b = n/2) with logits log of it, base 0, scale 1, eps 0:
+    after one and two rounds the blocks are the printed matrices divided by b."""
+    from fractions import Fraction
+    g = load_golden("sinkhorn_2x2_worked_example.txt")
+
+    def mat(key):
+        return np.array([float(Fraction(v)) for v in g[key]]).reshape(2, 2)
+
+    b = n // 2
+    big = np.kron(mat("input"), np.ones((b, b)))
+    nm = (2 + n) * n
+    m = np.zeros((1, nm), np.float32)
+    m[0, 2 * n:] = np.log(big).reshape(-1)
+    for iters, key in ((1, "round1"), (2, "round2")):
+        out = mhc.sinkhorn_n(n, to_dev(m), to_dev(np.zeros(nm, np.float32)),
+                             to_dev(np.ones(3, np.float32)), iters, 0.0)
+        torch.cuda.synchronize()
+        want = np.kron(mat(key), np.ones((b, b)) / b)
+        np.testing.assert_allclose(out["comb"].cpu().numpy()[0], want, rtol=0, atol=2e-7)
+
+
+def test_general_n_in_place_and_repeatable():
+    case = make_case(wl.Workload(790, "general_n_inplace", 300, 1024, "bf16", n=8))
+    ref, dev = run_step_n(case, "bf16")
+    again, _ = run_step_n(case, "bf16")
+    for k in ref:
+        assert torch.equal(ref[k], again[k]), k
+    x = dev["x"].clone()
+    wp = mhc.pack_wmix_n(dev["w_mix"], "bf16")
+    out = mhc.fused_step_n(x, dev["f"], dev["pre"], dev["post"], dev["comb"], wp, dev["base"],
+                           dev["scale"], dev["gamma"], x_out=x)
+    torch.cuda.synchronize()
+    for k in ("x_out", "y", "pre", "post", "comb", "mix"):
+        assert torch.equal(out[k].cpu(), ref[k]), k
+
+
+@pytest.mark.parametrize("n", [2, 8])
+def test_general_n_guard_bands_untouched(n):
+    t, d, gpad = 21, 256, 64
+    case = make_case(wl.Workload(795 + n, "general_n_guard", t, d, "bf16", n=n))
+    dev = _dev(case)
+    wp = mhc.pack_wmix_n(dev["w_mix"], "bf16")
+
+    def guarded(count, dtype):
+        buf = torch.full((count + 2 * gpad,), float("nan"), dtype=dtype, device="cuda")
+        return buf, buf[gpad:gpad + count]
+
+    nm = (2 + n) * n
+    bx, vx = guarded(t * n * d, torch.bfloat16)
+    by, vy = guarded(t * d, torch.bfloat16)
+    bp, vp = guarded(t * n, torch.float32)
+    bu, vu = guarded(t * n, torch.float32)
+    bc, vc = guarded(t * n * n, torch.float32)
+    bm, vm = guarded(t * nm, torch.float32)
+    out = mhc.fused_step_n(dev["x"], dev["f"], dev["pre"], dev["post"], dev["comb"], wp,
+                           dev["base"], dev["scale"], dev["gamma"], x_out=vx.view(t, n, d),
+                           y_out=vy.view(t, d), pre_out=vp.view(t, n), post_out=vu.view(t, n),
+                           comb_out=vc.view(t, n, n), mix_out=vm.view(t, nm))
+    torch.cuda.synchronize()
+    for buf, view in ((bx, vx), (by, vy), (bp, vp), (bu, vu), (bc, vc), (bm, vm)):
+        assert torch.isnan(buf[:gpad].float()).all() and torch.isnan(buf[-gpad:].float()).all()
+        assert not torch.isnan(view.float()).any()
+    check_step(case, {k: v.cpu() for k, v in out.items()}, "bf16")
+
+
+def test_general_n_zero_tokens():
+    x = torch.zeros((0, 8, 64), dtype=torch.bfloat16, device="cuda")
+    f = torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda")
+    z = torch.zeros((0, 8), device="cuda")
+    wp = mhc.pack_wmix_n(torch.zeros((80, 8 * 64), device="cuda"), "bf16")
+    out = mhc.fused_step_n(x, f, z, z, torch.zeros((0, 8, 8), device="cuda"), wp,
+                           torch.zeros(80, device="cuda"), torch.ones(3, device="cuda"),
+                           torch.ones(64, device="cuda"))
+    torch.cuda.synchronize()
+    assert out["y"].shape == (0, 64)
+
+
+@pytest.mark.timeout(900)
+def test_general_n8_throughput_shape_sampled():
+    """n = 8 at 65,536 tokens x d = 5120, launched as the benchmark launches it
+    (prior coefficients from the oracle on the CPU); first and last blocks plus
+    a seeded random sample of tokens checked in full."""
+    w = wl.Workload(3, "large_prefill_n8", 65536, 5120, "bf16", batch=4, n=8)
+    t_start = time.time()
+    x = wl.streams(w)
+    f = wl.sublayer_out(w)
+    prev, cur = wl.params(w, prev=True), wl.params(w)
+    _log(f"n8 large: inputs drawn in {time.time() - t_start:.1f}s")
+    pre, post, comb = oracle_prior(x, prev)
+    _log(f"n8 large: oracle prior done at {time.time() - t_start:.1f}s")
+    case = dict(x=x, f=f, pre=pre, post=post, comb=comb, iters=w.iters, norm_eps=w.norm_eps,
+                hc_eps=w.hc_eps, **cur)
+    out, _ = run_step_n(case, "bf16")
+    _log(f"n8 large: GPU step done at {time.time() - t_start:.1f}s")
+    t = w.tokens
+    rng = np.random.default_rng(54321)
+    idx = np.unique(np.concatenate([np.arange(128), np.arange(t - 128, t),
+                                    rng.choice(t, 256, replace=False)]))
+    sub = dict(case)
+    for k in ("x", "f", "pre", "post", "comb"):
+        sub[k] = case[k][idx]
+    check_step(sub, {k: v[idx] for k, v in out.items()}, "bf16")
+    stats = comb_sum_stats(out["comb"])
+    assert stats["col_dev_max"] <= 1e-5
+    _log(f"n8 large: {len(idx)} sampled tokens match; comb sums {stats}")
