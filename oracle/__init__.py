@@ -20,6 +20,10 @@ Pages cited (by title and section):
   and ``Block.forward``).
 * "2A · Single-Pass mHC" (openarchlab course page): §1 definition, §3 solution
   and §4 profiling (the hand-checked Sinkhorn example).
+
+``mhc_backward`` derives the gradient of the step from these forward
+definitions (the pages give no backward); its pins are finite differences of
+the forward and automatic differentiation of an independent transcription.
 """
 
 from .mhc_oracle import (  # noqa: F401
@@ -37,4 +41,8 @@ from .mhc_oracle import (  # noqa: F401
     rmsnorm,
     fused_step,
     fused_step_from_xprime,
+)
+from .mhc_backward import (  # noqa: F401
+    fused_step_backward,
+    split_sinkhorn_backward,
 )
