@@ -154,6 +154,75 @@ def general_n_bench(w0, steps, warmup):
         torch.cuda.empty_cache()
 
 
+def algorithmic_bytes_backward(tokens: int, d: int, elem: int, n: int) -> int:
+    """Bytes the backward must move at least: read X, F and the upstream dX',
+    dy, write dX and dF ((3n+3)*d elements per token; the new streams and h are
+    recomputable from X and F), the per-token coefficients (forward's pre, post,
+    comb in, mixes out, upstream coefficient gradients, and the coefficient
+    gradients written), plus the parameters read and their gradients written."""
+    nm = (2 + n) * n
+    per_token = (3 * n + 3) * d * elem + (3 * (2 * n + n * n) + nm + (2 * n + n * n)) * 4
+    per_call = 2 * (nm * n * d + nm + 3 + d) * 4
+    return tokens * per_token + per_call
+
+
+def backward_bench(w, steps, warmup):
+    """mhc_fused_step_backward_n at the workload's shape (n = 4): one JSON
+    line, HIP events around the call (all backward kernels)."""
+    import torch
+    import stream_hyper_connections_amd as mhc
+    from stream_hyper_connections_amd import workloads as wl
+    dev = torch.device("cuda:0")
+    n = w.n
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    elem = 2 if w.dtype == "bf16" else 4
+    x = upload_tokens(w, wl.X, 0, dev, dt).view(w.tokens, n, w.d)
+    f = upload_tokens(w, wl.F, 0, dev, dt)
+    prev = {k: torch.as_tensor(v).to(dev) for k, v in wl.params(w, prev=True).items()}
+    cur = {k: torch.as_tensor(v).to(dev) for k, v in wl.params(w).items()}
+    prior = mhc.mixes_n(x, mhc.pack_wmix_n(prev["w_mix"], w.dtype), prev["base"], prev["scale"],
+                        w.iters, w.norm_eps, w.hc_eps)
+    fwd = mhc.fused_step_n(x, f, prior["pre"], prior["post"], prior["comb"],
+                           mhc.pack_wmix_n(cur["w_mix"], w.dtype), cur["base"], cur["scale"],
+                           cur["gamma"], w.iters, w.norm_eps, w.hc_eps)
+    # upstream gradients: the forward's own outputs serve as seeded, finite data
+    d_x_out, d_y = fwd["x_out"].clone(), fwd["y"].clone()
+    d_pre, d_post, d_comb = fwd["pre"].clone(), fwd["post"].clone(), fwd["comb"].clone()
+    ws = torch.empty(mhc.fused_step_backward_workspace_bytes_n(n, w.tokens, w.d),
+                     dtype=torch.uint8, device=dev)
+
+    def call():
+        mhc.fused_step_backward_n(x, f, prior["pre"], prior["post"], prior["comb"], fwd["x_out"],
+                                  fwd["mix"], cur["w_mix"], cur["base"], cur["scale"],
+                                  cur["gamma"], d_x_out, d_y, d_pre, d_post, d_comb, w.iters,
+                                  w.norm_eps, w.hc_eps, workspace=ws)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    a = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    b = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for i in range(steps):
+        a[i].record()
+        call()
+        b[i].record()
+    torch.cuda.synchronize()
+    ms = np.array([x0.elapsed_time(x1) for x0, x1 in zip(a, b)])
+    alg = algorithmic_bytes_backward(w.tokens, w.d, elem, n)
+    achieved = alg / (ms.mean() / 1e3) / 1e9
+    print(json.dumps({
+        "metric": f"tokens/s of the fused-step backward, n={n} d={w.d}",
+        "value": round(w.tokens / (ms.mean() / 1e3), 1), "unit": "tokens/s",
+        "n_streams": n, "tokens": w.tokens, "d": w.d, "dtype": w.dtype,
+        "call_ms_avg": round(float(ms.mean()), 5),
+        "call_ms_p50": round(float(np.percentile(ms, 50)), 5),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": alg,
+                     "kernel": "bwd:: split + stats + stream + param + reductions"},
+        "config": {"workload": w.name, "sinkhorn_iters": w.iters}}), flush=True)
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -173,6 +242,9 @@ def parse():
     ap.add_argument("--n-sweep", action="store_true",
                     help="time the general stream-count step (mhc_fused_step_n) at the "
                          "workload's shape for n = 2, 4, 8; one JSON line per n")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward of the step (mhc_fused_step_backward_n) at the "
+                         "workload's shape; one JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain device-to-device copy of 2 GiB instead (the reference "
                          "kernel for scaling the HBM byte counters)")
@@ -292,6 +364,9 @@ def main():
     w = wl.WORKLOADS[args.workload]
     if args.n_sweep:
         general_n_bench(w, args.steps, args.warmup)
+        return
+    if args.backward:
+        backward_bench(w, args.steps, args.warmup)
         return
     dev = torch.device("cuda:0")
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32

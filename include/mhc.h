@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define MHC_ABI_VERSION 4
+#define MHC_ABI_VERSION 5
 #define MHC_N_STREAMS 4
 #define MHC_N_MIX 24
 
@@ -257,6 +257,41 @@ mhc_status mhc_sinkhorn_n(int32_t n, const float* mixes, int64_t tokens, const f
                           const float* scale, int32_t sinkhorn_iters, float hc_eps,
                           float* pre_out, float* post_out, float* comb_out,
                           mhc_stream_t stream);
+
+/*
+ * Backward of the fused step, n in {2, 4} (n = 8 is MHC_ERR_UNSUPPORTED). The
+ * pages give the forward only; the gradient follows from its definitions
+ * ([SW] "All 5 steps" and Code; [RN] formula and Code) by the chain rule, with
+ * the casts to the stream dtype passing gradients through unchanged (as
+ * automatic differentiation treats a dtype conversion).
+ *
+ * Inputs: the forward's inputs x, f, pre_in, post_in, comb_in; its saved
+ *   outputs x_out [T][n][d] (the new streams) and mix [T][(2+n)n] (the mixes
+ *   it wrote to mix_out); the float32 parameters w_mix [(2+n)n][n*d]
+ *   (unpacked), base, scale, gamma; sinkhorn_iters, norm_eps, hc_eps as in the
+ *   forward; the upstream gradients d_x_out [T][n][d] and d_y [T][d] (stream
+ *   dtype) and d_pre, d_post [T][n], d_comb [T][n][n] (float32).
+ * Outputs: d_x [T][n][d], d_f [T][d] (stream dtype, rounded to nearest even);
+ *   d_pre_in, d_post_in [T][n], d_comb_in [T][n][n], d_w_mix [(2+n)n][n*d],
+ *   d_base [(2+n)n], d_scale [3], d_gamma [d] (float32, overwritten, not
+ *   accumulated). Sums over tokens are taken in a fixed order: repeated calls
+ *   give identical results.
+ * Workspace: REQUIRED, mhc_fused_step_backward_workspace_bytes_n() bytes,
+ *   256-byte aligned, overlapping no other argument; calls sharing one must be
+ *   ordered. Its contents need no initialisation.
+ * Same conventions as above otherwise (no output may overlap an input).
+ */
+int64_t mhc_fused_step_backward_workspace_bytes_n(int32_t n, int64_t tokens, int32_t d);
+
+mhc_status mhc_fused_step_backward_n(
+    int32_t n, const void* x, const void* f, int32_t dtype, int64_t tokens, int32_t d,
+    const float* pre_in, const float* post_in, const float* comb_in, const void* x_out,
+    const float* mix, const float* w_mix, const float* base, const float* scale,
+    const float* gamma, int32_t sinkhorn_iters, float norm_eps, float hc_eps, const void* d_x_out,
+    const void* d_y, const float* d_pre, const float* d_post, const float* d_comb, void* d_x,
+    void* d_f, float* d_pre_in, float* d_post_in, float* d_comb_in, float* d_w_mix,
+    float* d_base, float* d_scale, float* d_gamma, void* workspace, int64_t workspace_bytes,
+    mhc_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -90,7 +90,7 @@ def split_sinkhorn_backward(m, scale, base, iters, hc_eps, n, d_pre, d_post, d_c
 
 def fused_step_backward(xs, f, pre_in, post_in, comb_in, w_mix, base, scale, gamma, d_xprime,
                         d_y, d_pre, d_post, d_comb, iters: int = 20, norm_eps: float = 1e-6,
-                        hc_eps: float = 1e-6, dtype: str = "bf16"):
+                        hc_eps: float = 1e-6, dtype: str = "bf16", xprime=None):
     """Gradients of one fused step (``mhc_oracle.fused_step``) with respect to
     all its inputs and parameters.
 
@@ -112,8 +112,11 @@ def fused_step_backward(xs, f, pre_in, post_in, comb_in, w_mix, base, scale, gam
       d comb_in[j,k] = sum_f X_j dA_k; d post_in_k = sum_f F dA_k
 
     Shapes as ``fused_step``; upstream d_xprime [T,n,d], d_y [T,d], d_pre,
-    d_post [T,n], d_comb [T,n,n]. Returns a dict of float64 arrays (d_x and
-    d_f unrounded).
+    d_post [T,n], d_comb [T,n,n]. ``xprime``: the new streams the forward
+    stored, if given (a backward receives the forward's saved output; any
+    correct rounding of it is a valid forward); otherwise recomputed. Returns
+    a dict of float64 arrays (d_x and d_f unrounded) with the intermediate
+    gradients da (of the new streams), dx_mix and dh.
     """
     xs = np.asarray(xs, dtype=np.float64)
     f = np.asarray(f, dtype=np.float64)
@@ -128,7 +131,9 @@ def fused_step_backward(xs, f, pre_in, post_in, comb_in, w_mix, base, scale, gam
     t, n, d = xs.shape
 
     # forward values the gradient uses
-    xprime = hc_post(xs, f, post_in, comb_in, dtype)
+    if xprime is None:
+        xprime = hc_post(xs, f, post_in, comb_in, dtype)
+    xprime = np.asarray(xprime, dtype=np.float64)
     x = xprime.reshape(t, n * d)
     r = 1.0 / np.sqrt(np.mean(x * x, axis=1) + norm_eps)
     z = x @ w.T
@@ -169,4 +174,4 @@ def fused_step_backward(xs, f, pre_in, post_in, comb_in, w_mix, base, scale, gam
     return {"d_x": d_x, "d_f": d_f, "d_pre_in": d_pre_in, "d_post_in": d_post_in,
             "d_comb_in": d_comb_in, "d_w_mix": d_w, "d_base": d_base, "d_scale": d_scale,
             "d_gamma": d_gamma, "m": m, "r": r, "rho": rho, "s": s_sum, "g": g,
-            "xprime": xprime, "h": h}
+            "xprime": xprime, "h": h, "da": da, "dx_mix": dx_mix, "dh": dh}

@@ -12,6 +12,8 @@ from .binding import (  # noqa: F401
     d_granule,
     SPLIT_MIN_TOKENS,
     fused_step,
+    fused_step_backward_n,
+    fused_step_backward_workspace_bytes_n,
     fused_step_n,
     fused_step_workspace_bytes,
     hc_post,

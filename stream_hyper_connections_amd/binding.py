@@ -53,6 +53,10 @@ _SIGS = {
                      _f32, _f32, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p], _i32),
     "mhc_sinkhorn_n": ([_i32, _c_void_p, _i64, _c_void_p, _c_void_p, _i32, _f32, _c_void_p,
                         _c_void_p, _c_void_p, _c_void_p], _i32),
+    "mhc_fused_step_backward_workspace_bytes_n": ([_i32, _i64, _i32], _i64),
+    "mhc_fused_step_backward_n": ([_i32, _c_void_p, _c_void_p, _i32, _i64, _i32]
+                                  + [_c_void_p] * 9 + [_i32, _f32, _f32]
+                                  + [_c_void_p] * 15 + [_i64, _c_void_p], _i32),
 }
 
 _lib = None
@@ -387,3 +391,45 @@ def sinkhorn_n(n, mix, base, scale, iters=20, hc_eps=1e-6, pre_out=None, post_ou
                                _ptr(pre_out), _ptr(post_out), _ptr(comb_out), _stream())
     _check("mhc_sinkhorn_n", st)
     return {"pre": pre_out, "post": post_out, "comb": comb_out}
+
+
+# ----- backward of the step (n in {2, 4}) --------------------------------------------------
+
+def fused_step_backward_workspace_bytes_n(n: int, tokens: int, d: int) -> int:
+    b = load().mhc_fused_step_backward_workspace_bytes_n(n, tokens, d)
+    if b < 0:
+        raise MhcError("mhc_fused_step_backward_workspace_bytes_n", MHC_ERR_INVALID_ARG,
+                       last_error())
+    return b
+
+
+def fused_step_backward_n(x, f, pre_in, post_in, comb_in, x_out, mix, w_mix, base, scale, gamma,
+                          d_x_out, d_y, d_pre, d_post, d_comb, iters=20, norm_eps=1e-6,
+                          hc_eps=1e-6, workspace=None) -> dict:
+    """mhc_fused_step_backward_n on tensors. Forward inputs (x [T,n,d], f,
+    pre_in, post_in, comb_in), the forward's saved outputs (x_out, mix), the
+    float32 parameters (w_mix [(2+n)n, nd] unpacked, base, scale, gamma) and
+    the upstream gradients (d_x_out, d_y in the stream dtype; d_pre, d_post,
+    d_comb float32). Returns the gradients d_x, d_f (stream dtype), d_pre_in,
+    d_post_in, d_comb_in, d_w_mix, d_base, d_scale, d_gamma (float32)."""
+    t, n, d = x.shape
+    nm = n_mix(n)
+    dev = x.device
+    need = fused_step_backward_workspace_bytes_n(n, t, d)
+    if workspace is None:
+        workspace = workspace_for(dev, need)
+    out = {"d_x": torch.empty_like(x), "d_f": torch.empty_like(f),
+           "d_pre_in": torch.empty((t, n), device=dev), "d_post_in": torch.empty((t, n), device=dev),
+           "d_comb_in": torch.empty((t, n, n), device=dev),
+           "d_w_mix": torch.empty((nm, n * d), device=dev), "d_base": torch.empty(nm, device=dev),
+           "d_scale": torch.empty(3, device=dev), "d_gamma": torch.empty(d, device=dev)}
+    st = load().mhc_fused_step_backward_n(
+        n, _ptr(x), _ptr(f), _dtype_code(x), t, d, _ptr(pre_in), _ptr(post_in), _ptr(comb_in),
+        _ptr(x_out), _ptr(mix), _ptr(w_mix), _ptr(base), _ptr(scale), _ptr(gamma), iters,
+        norm_eps, hc_eps, _ptr(d_x_out), _ptr(d_y), _ptr(d_pre), _ptr(d_post), _ptr(d_comb),
+        _ptr(out["d_x"]), _ptr(out["d_f"]), _ptr(out["d_pre_in"]), _ptr(out["d_post_in"]),
+        _ptr(out["d_comb_in"]), _ptr(out["d_w_mix"]), _ptr(out["d_base"]), _ptr(out["d_scale"]),
+        _ptr(out["d_gamma"]), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream())
+    _check("mhc_fused_step_backward_n", st)
+    return out

@@ -1,0 +1,670 @@
+// Backward of the fused step, for n in {2, 4} streams. The pages define the
+// forward only ([SW] "All 5 steps" and Code; [RN] formula and Code); the
+// gradient follows from those definitions by the chain rule, with the casts to
+// the stream dtype passing gradients through unchanged. Per token, with
+// forward values X' (the stored new streams), h = S(sum_k p_k X'_k),
+// r = (mean X'^2 + eps)^-1/2, rho = (mean h^2 + eps)^-1/2 and m (the mixes):
+//
+//   g      = gradient at the split's pre-activations a = scale * m + base
+//            (sigmoid derivatives; the unrolled Sinkhorn in reverse; the
+//            row softmax)                                  split_kernel
+//   r, rho, S = sum_f dy gamma h                             stats_kernel
+//   V = r * scale * g, dr = (scale * g) . m / r, c = dr r^3 / (n d),
+//   kappa = rho^3 S / d
+//   dh     = rho gamma dy - kappa h
+//   dA_k   = dX'_k + (W^T V)_k - c X'_k + p_k dh
+//   dX_j   = S(sum_k C[j][k] dA_k), dF = S(sum_k u_k dA_k)
+//   d comb_in[j][k] = sum_f X_j dA_k, d post_in_k = sum_f F dA_k,
+//   d pre_in_k = sum_f dh X'_k                               stream_kernel
+//   d gamma[f] = sum_t dy h rho (per-workgroup partials)    stream_kernel
+//   dW[i][k d + f] = sum_t V_i X'_k[f]                       param_kernel
+//   d base_i = sum_t g_i, d scale = sums of g_i m_i per group  slot_kernel
+//
+// Layout of the stream kernel follows the general-n block kernel: a
+// workgroup owns 128 tokens, each wave 16 of them over all features. W^T V is
+// a product over the (2+n)n slots, computed with v_mfma_f32_16x16x4_f32 on
+// float32 weights staged in LDS one step at a time, with the weights as the A
+// operand (rows = features) and V as the B operand (columns = tokens), so the
+// result lands in the lane that holds the token's features. Reductions over
+// tokens (dW, d gamma, d base, d scale) are written as per-chunk partial sums
+// and added in a fixed order: the results are deterministic.
+//
+// Included by mhc.hip after general_n.h.
+
+namespace bwd {
+
+constexpr int kTok = gen::kTok;
+constexpr int kWaves = gen::kWaves;
+constexpr int kThreads = gen::kThreads;
+constexpr int kBlock = gen::kBlock;
+constexpr int kStep = gen::kStep;
+constexpr int kParamChunks = 16;   // token chunks of the parameter kernel
+
+template <int N>
+struct Dims {
+  static constexpr int kMix = (2 + N) * N;
+  static constexpr int kSlots = (kMix + 15) / 16 * 16;   // padded to whole u32x4 groups of K
+  static constexpr int kKc = kSlots / 4;                  // K chunks of the f32 MFMA
+  static constexpr int kVecs = N * 2 * (kSlots / 16) * 64;   // u32x4 of one step's W^T
+  static constexpr int kItems = N * kSlots * 8;               // f32x4 loads staging one step
+  static constexpr int kStage = (kItems + kThreads - 1) / kThreads;
+};
+
+// Workspace (floats, each region 256-byte aligned).
+__host__ __device__ constexpr int64_t al64(int64_t v) { return (v + 63) / 64 * 64; }
+template <int N>
+struct Ws {
+  int64_t tokens;
+  int d;
+  __host__ __device__ int64_t g_off() const { return 0; }
+  __host__ __device__ int64_t v_off() const { return g_off() + al64(tokens * Dims<N>::kMix); }
+  __host__ __device__ int64_t st_off() const { return v_off() + al64(tokens * Dims<N>::kSlots); }
+  __host__ __device__ int64_t pw_off() const { return st_off() + al64(tokens * 4); }
+  __host__ __device__ int64_t groups() const { return (tokens + kBlock - 1) / kBlock; }
+  __host__ __device__ int64_t pg_off() const {
+    return pw_off() + al64((int64_t)kParamChunks * Dims<N>::kMix * N * d);
+  }
+  __host__ __device__ int64_t e_off() const { return pg_off() + al64(groups() * d); }
+  __host__ __device__ int64_t floats() const { return e_off() + al64(Dims<N>::kMix); }
+};
+
+struct Args {
+  const void* x;
+  const void* f;
+  const float* pre_in;
+  const float* post_in;
+  const float* comb_in;
+  const void* x_out;
+  const float* mix;
+  const float* w;
+  const float* base;
+  const float* scale;
+  const float* gamma;
+  const void* dxo;
+  const void* dy;
+  const float* d_pre;
+  const float* d_post;
+  const float* d_comb;
+  void* dx;
+  void* df;
+  float* d_pre_in;
+  float* d_post_in;
+  float* d_comb_in;
+  float* d_w;
+  float* d_base;
+  float* d_scale;
+  float* d_gamma;
+  float* ws;
+  int64_t tokens;
+  int d;
+  int iters;
+  float norm_eps;
+  float hc_eps;
+};
+
+// ----- split / Sinkhorn backward, one thread per token ---------------------------------
+
+// In-place normalisation of the NxN matrix c (rows when ROW, columns
+// otherwise) by (sum + eps); the divisors go to s.
+template <int N, bool ROW>
+__device__ __forceinline__ void normalise(float (&c)[N][N], float (&s)[N], float eps) {
+#pragma unroll
+  for (int a = 0; a < N; ++a) {
+    float sum = 0.f;
+#pragma unroll
+    for (int b = 0; b < N; ++b) sum += ROW ? c[a][b] : c[b][a];
+    s[a] = sum + eps;
+#pragma unroll
+    for (int b = 0; b < N; ++b) {
+      if (ROW)
+        c[a][b] = c[a][b] / s[a];
+      else
+        c[b][a] = c[b][a] / s[a];
+    }
+  }
+}
+
+// Step k of the comb's normalisations (k = 0: the first column division,
+// then rows at odd k and columns at even k).
+template <int N>
+__device__ __forceinline__ void sk_step(float (&c)[N][N], float (&s)[N], int k, float eps) {
+  if (k == 0 || (k & 1) == 0)
+    normalise<N, false>(c, s, eps);
+  else
+    normalise<N, true>(c, s, eps);
+}
+
+// The reverse pass recomputes the forward up to each normalisation (memory
+// stays O(N^2) per thread; the work is O(iters^2 N^2), small at the pages'
+// 20 rounds). For Y = X / (sum + eps) along an axis,
+// dX = (dY - sum_axis(dY * Y)) / (sum + eps); for P = softmax(L) along rows,
+// dL = P * (dP - sum_row(dP * P)).
+template <int N>
+__global__ __launch_bounds__(256) void split_kernel(Args a) {
+  constexpr int kMix = Dims<N>::kMix;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= a.tokens) return;
+  const float* m = a.mix + t * kMix;
+  float* g = a.ws + t * kMix;   // region g at offset 0
+  const float s0 = a.scale[0], s1 = a.scale[1], s2 = a.scale[2];
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    const float sp = sigmoidf(m[j] * s0 + a.base[j]);
+    g[j] = a.d_pre[t * N + j] * sp * (1.0f - sp);
+    const float sq = sigmoidf(m[N + j] * s1 + a.base[N + j]);
+    g[N + j] = a.d_post[t * N + j] * 2.0f * sq * (1.0f - sq);
+  }
+  float p[N][N];
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+      p[j][k] = m[2 * N + N * j + k] * s2 + a.base[2 * N + N * j + k];
+      mx = fmaxf(mx, p[j][k]);
+    }
+    float rs = 0.f;
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+      p[j][k] = expf(p[j][k] - mx);
+      rs += p[j][k];
+    }
+#pragma unroll
+    for (int k = 0; k < N; ++k) p[j][k] = p[j][k] / rs;
+  }
+  float dc[N][N];
+#pragma unroll
+  for (int j = 0; j < N; ++j)
+#pragma unroll
+    for (int k = 0; k < N; ++k) dc[j][k] = a.d_comb[(t * N + j) * N + k];
+  const float eps = a.hc_eps;
+  const int nsteps = 2 * a.iters - 1;
+  for (int step = nsteps - 1; step >= 0; --step) {
+    float c[N][N], s[N];
+#pragma unroll
+    for (int j = 0; j < N; ++j)
+#pragma unroll
+      for (int k = 0; k < N; ++k) c[j][k] = p[j][k] + eps;
+    for (int q = 0; q <= step; ++q) sk_step<N>(c, s, q, eps);   // c = output of `step`
+    const bool row = step != 0 && (step & 1);
+#pragma unroll
+    for (int a2 = 0; a2 < N; ++a2) {
+      float dot = 0.f;
+#pragma unroll
+      for (int b = 0; b < N; ++b) dot += row ? dc[a2][b] * c[a2][b] : dc[b][a2] * c[b][a2];
+#pragma unroll
+      for (int b = 0; b < N; ++b) {
+        if (row)
+          dc[a2][b] = (dc[a2][b] - dot) / s[a2];
+        else
+          dc[b][a2] = (dc[b][a2] - dot) / s[a2];
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    float dot = 0.f;
+#pragma unroll
+    for (int k = 0; k < N; ++k) dot += dc[j][k] * p[j][k];
+#pragma unroll
+    for (int k = 0; k < N; ++k) g[2 * N + N * j + k] = p[j][k] * (dc[j][k] - dot);
+  }
+}
+
+// ----- per-token statistics, one wave per token ----------------------------------------
+
+// 8 consecutive stream elements as floats.
+template <int DT>
+__device__ __forceinline__ void load8(const void* base, int64_t elem, float (&v)[8]) {
+  if constexpr (DT == MHC_BF16) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + elem);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf_lo(w[i]);
+      v[2 * i + 1] = bf_hi(w[i]);
+    }
+  } else {
+    const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(base) + elem);
+    const f32x4 lo = p[0], hi = p[1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = lo[i];
+      v[4 + i] = hi[i];
+    }
+  }
+}
+
+// Round to the stream dtype (RNE), as the forward does.
+template <int DT>
+__device__ __forceinline__ void round8(float (&v)[8]) {
+  if constexpr (DT == MHC_BF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+      v[2 * i] = bf_lo(w);
+      v[2 * i + 1] = bf_hi(w);
+    }
+  }
+}
+
+// r, rho and S = sum_f dy gamma h of each token, from the stored new streams
+// (h is recomputed with the forward's operation order and rounding).
+template <int N, int DT>
+__global__ __launch_bounds__(256) void stats_kernel(Args a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= a.tokens) return;
+  const int d = a.d;
+  float P[N];
+#pragma unroll
+  for (int k = 0; k < N; ++k) P[k] = a.pre_in[t * N + k];
+  float sx = 0.f, sh = 0.f, sd = 0.f;
+  for (int f0 = 8 * lane; f0 < d; f0 += 512) {
+    float xp[N][8], dy[8];
+#pragma unroll
+    for (int k = 0; k < N; ++k) load8<DT>(a.x_out, (t * N + k) * (int64_t)d + f0, xp[k]);
+    load8<DT>(a.dy, t * (int64_t)d + f0, dy);
+    float h[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float v = P[0] * xp[0][e];
+#pragma unroll
+      for (int k = 1; k < N; ++k) v = fmaf(P[k], xp[k][e], v);
+      h[e] = v;
+#pragma unroll
+      for (int k = 0; k < N; ++k) sx = fmaf(xp[k][e], xp[k][e], sx);
+    }
+    round8<DT>(h);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      sh = fmaf(h[e], h[e], sh);
+      sd = fmaf(dy[e] * a.gamma[f0 + e], h[e], sd);
+    }
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    sx += __shfl_xor(sx, o);
+    sh += __shfl_xor(sh, o);
+    sd += __shfl_xor(sd, o);
+  }
+  if (lane == 0) {
+    Ws<N> w{a.tokens, d};
+    float* st = a.ws + w.st_off() + t * 4;
+    st[0] = rsqrtf(sx / (float)(N * d) + a.norm_eps);
+    st[1] = rsqrtf(sh / (float)d + a.norm_eps);
+    st[2] = sd;
+    st[3] = 0.f;
+  }
+}
+
+// ----- the stream kernel ----------------------------------------------------------------
+
+// One step's W^T in the A-operand order of v_mfma_f32_16x16x4_f32: u32x4
+// index ((k * 2 + q) * (kSlots / 16) + c4) * 64 + lane holds, in element e,
+// W[16 c4 + 4 e + lane / 16][k d + 32 s + feat(q, lane % 16)] with
+// feat(q, rho) = 8 (rho / 4) + 4 q + rho % 4, so that the product's rows
+// 4g..4g+3 are features 8g + 4q + 0..3 (the lane's own features).
+// Staging item i = ((k * kSlots) + slot) * 8 + c8 covers features 4 c8..4 c8+3.
+template <int N>
+__device__ __forceinline__ void stage_load(f32x4 (&st)[Dims<N>::kStage], const float* w, int d,
+                                           int s, int tid) {
+  using D = Dims<N>;
+#pragma unroll
+  for (int r = 0; r < D::kStage; ++r) {
+    const int i = tid + r * kThreads;
+    const int c8 = i & 7;
+    const int slot = (i >> 3) % D::kSlots;
+    const int k = (i >> 3) / D::kSlots;
+    st[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (i < D::kItems && slot < D::kMix)
+      st[r] = *reinterpret_cast<const f32x4*>(w + (int64_t)slot * N * d + (int64_t)k * d +
+                                              s * kStep + 4 * c8);
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void stage_store(float* wl, const f32x4 (&st)[Dims<N>::kStage],
+                                            int tid) {
+  using D = Dims<N>;
+#pragma unroll
+  for (int r = 0; r < D::kStage; ++r) {
+    const int i = tid + r * kThreads;
+    if (i >= D::kItems) continue;
+    const int c8 = i & 7;
+    const int slot = (i >> 3) % D::kSlots;
+    const int k = (i >> 3) / D::kSlots;
+    const int q = c8 & 1;                 // features 4 c8 .. 4 c8 + 3: 8 (c8 / 2) + 4 q + 0..3
+    const int rho0 = 4 * (c8 >> 1);       // rows rho0 .. rho0 + 3
+    const int c4 = slot >> 4, e = (slot >> 2) & 3, gq = slot & 3;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int lane = rho0 + u + 16 * gq;
+      wl[((((k * 2 + q) * (D::kSlots / 16) + c4) * 64 + lane) << 2) + e] = st[r][u];
+    }
+  }
+}
+
+template <int N, int DT>
+__global__ __launch_bounds__(kThreads) void stream_kernel(Args a) {
+  using D = Dims<N>;
+  constexpr int kMix = D::kMix;
+  constexpr int es = DT == MHC_BF16 ? 2 : 4;
+  __shared__ __align__(16) float wl[2][D::kVecs * 4];
+  __shared__ float red[2][kWaves][kStep];   // per-wave d gamma sums of one step
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tr = lane & 15;
+  const int g = lane >> 4;
+  const int64_t tw = (int64_t)blockIdx.x * kBlock + wave * kTok;
+  const int64_t t = tw + tr;
+  const bool valid = t < a.tokens;
+  const int64_t tc = valid ? t : 0;   // a valid row for the per-token loads
+  const int d = a.d;
+  const int nsteps = d / kStep;
+  Ws<N> wsl{a.tokens, d};
+
+  f32x4 st[D::kStage];
+  stage_load<N>(st, a.w, d, 0, tid);
+
+  // per-token constants
+  float C[N][N], U[N], P[N];
+#pragma unroll
+  for (int j = 0; j < N; ++j)
+#pragma unroll
+    for (int k = 0; k < N; ++k) C[j][k] = a.comb_in[(tc * N + j) * N + k];
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    U[k] = a.post_in[tc * N + k];
+    P[k] = a.pre_in[tc * N + k];
+  }
+  const float* stt = a.ws + wsl.st_off() + tc * 4;
+  const float r = stt[0], rho = stt[1], ssum = stt[2];
+  const float* gr = a.ws + wsl.g_off() + tc * kMix;
+  const float* mr = a.mix + tc * kMix;
+  float dmm = 0.f;   // (scale * g) . m
+#pragma unroll
+  for (int i = 0; i < kMix; ++i) {
+    const float sc = i < N ? a.scale[0] : (i < 2 * N ? a.scale[1] : a.scale[2]);
+    dmm = fmaf(sc * gr[i], mr[i], dmm);
+  }
+  const float cr = dmm * r * r / (float)(N * d);       // dr r^3 / (n d), dr = dmm / r
+  const float kappa = rho * rho * rho * ssum / (float)d;
+  // B operand: V[slot 4 kc + g] of the lane's token
+  float vb[D::kKc];
+#pragma unroll
+  for (int kc = 0; kc < D::kKc; ++kc) {
+    const int i = 4 * kc + g;
+    const float sc = i < N ? a.scale[0] : (i < 2 * N ? a.scale[1] : a.scale[2]);
+    vb[kc] = i < kMix ? r * sc * gr[i] : 0.f;
+  }
+  // V for the parameter kernel: lane g writes the slots it holds
+  if (valid) {
+#pragma unroll
+    for (int kc = 0; kc < D::kKc; ++kc) a.ws[wsl.v_off() + t * D::kSlots + 4 * kc + g] = vb[kc];
+  }
+
+  stage_store<N>(wl[0], st, tid);
+  __syncthreads();
+
+  float dC[N][N], du[N], dp[N];
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    du[k] = dp[k] = 0.f;
+#pragma unroll
+    for (int j = 0; j < N; ++j) dC[j][k] = 0.f;
+  }
+
+  const int64_t xrow = (int64_t)N * d, frow = d;
+  for (int s = 0; s < nsteps; ++s) {
+    const int f0 = s * kStep + 8 * g;
+    if (s + 1 < nsteps) stage_load<N>(st, a.w, d, s + 1, tid);
+    // lane inputs (8 features of the token)
+    float xv[N][8], dxo[N][8], fv[8], dyv[8];
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      load8<DT>(a.x, tc * xrow + j * (int64_t)d + f0, xv[j]);
+      load8<DT>(a.dxo, tc * xrow + j * (int64_t)d + f0, dxo[j]);
+    }
+    load8<DT>(a.f, tc * frow + f0, fv);
+    load8<DT>(a.dy, tc * frow + f0, dyv);
+    const f32x4 g0 = *reinterpret_cast<const f32x4*>(a.gamma + f0);
+    const f32x4 g1 = *reinterpret_cast<const f32x4*>(a.gamma + f0 + 4);
+    const float gv[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
+
+    // W^T V for the lane's features: tile q gives features 8g + 4q + 0..3
+    const float* wb = wl[s & 1];
+    float dxm[N][8];
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c4 = 0; c4 < D::kSlots / 16; ++c4) {
+          const f32x4 av = *reinterpret_cast<const f32x4*>(
+              wb + ((((k * 2 + q) * (D::kSlots / 16) + c4) * 64 + lane) << 2));
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[e], vb[4 * c4 + e], acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dxm[k][4 * q + i] = acc[i];
+      }
+    }
+
+    // recompute X' and h exactly as the forward did
+    float xp[N][8], h[8];
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float v = xv[0][e] * C[0][k];
+#pragma unroll
+        for (int j = 1; j < N; ++j) v = fmaf(xv[j][e], C[j][k], v);
+        xp[k][e] = fmaf(fv[e], U[k], v);
+      }
+      round8<DT>(xp[k]);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float v = P[0] * xp[0][e];
+#pragma unroll
+      for (int k = 1; k < N; ++k) v = fmaf(P[k], xp[k][e], v);
+      h[e] = v;
+    }
+    round8<DT>(h);
+
+    float dxj[N][8], dfv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      // d gamma: sum over the wave's 16 tokens (lanes of one 16-lane row)
+      float dg = valid ? dyv[e] * h[e] * rho : 0.f;
+      dg += __shfl_xor(dg, 1);
+      dg += __shfl_xor(dg, 2);
+      dg += __shfl_xor(dg, 4);
+      dg += __shfl_xor(dg, 8);
+      if (tr == 0) red[s & 1][wave][8 * g + e] = dg;
+      const float dh = rho * (gv[e] * dyv[e]) - kappa * h[e];
+      float da[N];
+#pragma unroll
+      for (int k = 0; k < N; ++k) {
+        da[k] = dxo[k][e] + (dxm[k][e] - cr * xp[k][e]) + P[k] * dh;
+        dp[k] = fmaf(dh, xp[k][e], dp[k]);
+        du[k] = fmaf(fv[e], da[k], du[k]);
+#pragma unroll
+        for (int j = 0; j < N; ++j) dC[j][k] = fmaf(xv[j][e], da[k], dC[j][k]);
+      }
+#pragma unroll
+      for (int j = 0; j < N; ++j) {
+        float v = C[j][0] * da[0];
+#pragma unroll
+        for (int k = 1; k < N; ++k) v = fmaf(C[j][k], da[k], v);
+        dxj[j][e] = v;
+      }
+      float v = U[0] * da[0];
+#pragma unroll
+      for (int k = 1; k < N; ++k) v = fmaf(U[k], da[k], v);
+      dfv[e] = v;
+    }
+    if (valid) {
+#pragma unroll
+      for (int j = 0; j < N; ++j)
+        unfused::put8<DT>(a.dx, tc * xrow + j * (int64_t)d + f0, dxj[j]);
+      unfused::put8<DT>(a.df, tc * frow + f0, dfv);
+    }
+
+    // next step's W^T into the other buffer (read two steps ago; every wave
+    // passed the barrier at the end of the previous step since)
+    if (s + 1 < nsteps) stage_store<N>(wl[(s + 1) & 1], st, tid);
+    __syncthreads();
+    // the workgroup's d gamma partial of this step's features (red[s & 1] is
+    // rewritten two steps later, after the next barrier)
+    if (wave == 0 && lane < kStep) {
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) v += red[s & 1][w][lane];
+      a.ws[wsl.pg_off() + (int64_t)blockIdx.x * d + s * kStep + lane] = v;
+    }
+  }
+
+  // per-token sums over the 4 lanes of a token
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    dp[k] += __shfl_xor(dp[k], 16);
+    dp[k] += __shfl_xor(dp[k], 32);
+    du[k] += __shfl_xor(du[k], 16);
+    du[k] += __shfl_xor(du[k], 32);
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      dC[j][k] += __shfl_xor(dC[j][k], 16);
+      dC[j][k] += __shfl_xor(dC[j][k], 32);
+    }
+  }
+  if (valid && g == 0) {
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+      a.d_pre_in[t * N + k] = dp[k];
+      a.d_post_in[t * N + k] = du[k];
+#pragma unroll
+      for (int j = 0; j < N; ++j) a.d_comb_in[(t * N + j) * N + k] = dC[j][k];
+    }
+  }
+}
+
+// ----- parameter gradients: features across threads, tokens in chunks ----------------
+
+// Thread (feature f, stream k, chunk c) accumulates
+// dW[i][k d + f] = sum_t V_t[i] X'_t[k][f] over the chunk's tokens (V_t from
+// the stream kernel; X' the stored new streams). Tokens are taken kBatch at a
+// time so that their loads are in flight together. Partial sums per chunk go
+// to the workspace.
+template <int N, int DT>
+__global__ __launch_bounds__(256) void param_kernel(Args a) {
+  constexpr int kMix = Dims<N>::kMix;
+  constexpr int kBatch = 8;
+  const int d = a.d;
+  const int64_t f = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int k = blockIdx.y;
+  const int chunk = blockIdx.z;
+  if (f >= d) return;
+  Ws<N> wsl{a.tokens, d};
+  const int64_t per = (a.tokens + kParamChunks - 1) / kParamChunks;
+  const int64_t t0 = chunk * per;
+  const int64_t t1 = t0 + per < a.tokens ? t0 + per : a.tokens;
+  const float* v = a.ws + wsl.v_off();
+  float acc[kMix];
+#pragma unroll
+  for (int i = 0; i < kMix; ++i) acc[i] = 0.f;
+  for (int64_t tb = t0; tb < t1; tb += kBatch) {
+    float xp[kBatch];
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int64_t t = tb + b < t1 ? tb + b : t1 - 1;
+      const int64_t idx = (t * N + k) * d + f;
+      if constexpr (DT == MHC_BF16)
+        xp[b] = __uint_as_float((uint32_t) static_cast<const uint16_t*>(a.x_out)[idx] << 16);
+      else
+        xp[b] = static_cast<const float*>(a.x_out)[idx];
+      if (tb + b >= t1) xp[b] = 0.f;
+    }
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int64_t t = tb + b < t1 ? tb + b : t1 - 1;
+      const float* vt = v + t * Dims<N>::kSlots;
+#pragma unroll
+      for (int i = 0; i < kMix; ++i) acc[i] = fmaf(vt[i], xp[b], acc[i]);
+    }
+  }
+  float* pw = a.ws + wsl.pw_off() + (int64_t)chunk * kMix * N * d;
+#pragma unroll
+  for (int i = 0; i < kMix; ++i) pw[(int64_t)i * N * d + (int64_t)k * d + f] = acc[i];
+}
+
+// Sum of the per-chunk partials, in chunk order.
+template <int N>
+__global__ __launch_bounds__(256) void param_reduce_kernel(Args a) {
+  const int d = a.d;
+  const int64_t nw = (int64_t)Dims<N>::kMix * N * d;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  Ws<N> wsl{a.tokens, d};
+  if (i < nw) {
+    const float* pw = a.ws + wsl.pw_off();
+    float s = 0.f;
+    for (int c = 0; c < kParamChunks; ++c) s += pw[(int64_t)c * nw + i];
+    a.d_w[i] = s;
+  } else if (i < nw + d) {
+    const int64_t f = i - nw;
+    const float* pg = a.ws + wsl.pg_off();
+    float s = 0.f;
+    for (int64_t c = 0; c < wsl.groups(); ++c) s += pg[c * d + f];
+    a.d_gamma[f] = s;
+  }
+}
+
+// d base and the per-slot sums of g * m: one workgroup per slot, a fixed-order
+// tree over the tokens; the last step folds the slot sums into d scale.
+template <int N>
+__global__ __launch_bounds__(256) void slot_kernel(Args a) {
+  constexpr int kMix = Dims<N>::kMix;
+  __shared__ float sg[256], sm[256];
+  const int i = blockIdx.x;
+  Ws<N> wsl{a.tokens, a.d};
+  const float* g = a.ws + wsl.g_off();
+  float s1 = 0.f, s2 = 0.f;
+  for (int64_t t = threadIdx.x; t < a.tokens; t += 256) {
+    const float gv = g[t * kMix + i];
+    s1 += gv;
+    s2 = fmaf(gv, a.mix[t * kMix + i], s2);
+  }
+  sg[threadIdx.x] = s1;
+  sm[threadIdx.x] = s2;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) {
+      sg[threadIdx.x] += sg[threadIdx.x + w];
+      sm[threadIdx.x] += sm[threadIdx.x + w];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    a.d_base[i] = sg[0];
+    a.ws[wsl.e_off() + i] = sm[0];
+  }
+}
+
+template <int N>
+__global__ __launch_bounds__(64) void scale_kernel(Args a) {
+  constexpr int kMix = Dims<N>::kMix;
+  if (threadIdx.x != 0) return;
+  Ws<N> wsl{a.tokens, a.d};
+  const float* e = a.ws + wsl.e_off();
+  float s[3] = {0.f, 0.f, 0.f};
+  for (int i = 0; i < kMix; ++i) s[i < N ? 0 : (i < 2 * N ? 1 : 2)] += e[i];
+  a.d_scale[0] = s[0];
+  a.d_scale[1] = s[1];
+  a.d_scale[2] = s[2];
+}
+
+}  // namespace bwd

@@ -1110,6 +1110,7 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_kernel(StepArgs a, int nt
 #include "split_kernel.h"
 #include "unfused.h"
 #include "general_n.h"
+#include "backward.h"
 
 // ----- packing of the projection --------------------------------------------------------
 
@@ -1512,6 +1513,41 @@ mhc_status run_n(int32_t n, const StepArgs& a, int32_t dtype, int mode, hipStrea
   return launch_status("general-n split/Sinkhorn kernel launch");
 }
 
+// ----- backward ------------------------------------------------------------------------
+
+bool bwd_supported(int32_t n) { return n == 2 || n == 4; }
+
+int64_t bwd_workspace_floats(int32_t n, int64_t tokens, int32_t d) {
+  if (n == 2) return bwd::Ws<2>{tokens, d}.floats();
+  return bwd::Ws<4>{tokens, d}.floats();
+}
+
+template <int N, int DT>
+mhc_status run_backward(const bwd::Args& a, hipStream_t st) {
+  const unsigned tok256 = (unsigned)((a.tokens + 255) / 256);
+  hipLaunchKernelGGL((bwd::split_kernel<N>), dim3(tok256), dim3(256), 0, st, a);
+  mhc_status s = launch_status("backward split/Sinkhorn kernel launch");
+  if (s != MHC_OK) return s;
+  hipLaunchKernelGGL((bwd::stats_kernel<N, DT>), dim3((unsigned)((a.tokens + 3) / 4)), dim3(256),
+                     0, st, a);
+  if ((s = launch_status("backward statistics kernel launch")) != MHC_OK) return s;
+  hipLaunchKernelGGL((bwd::stream_kernel<N, DT>),
+                     dim3((unsigned)((a.tokens + bwd::kBlock - 1) / bwd::kBlock)),
+                     dim3(bwd::kThreads), 0, st, a);
+  if ((s = launch_status("backward stream kernel launch")) != MHC_OK) return s;
+  hipLaunchKernelGGL((bwd::param_kernel<N, DT>),
+                     dim3((unsigned)((a.d + 255) / 256), N, bwd::kParamChunks), dim3(256), 0, st, a);
+  if ((s = launch_status("backward parameter kernel launch")) != MHC_OK) return s;
+  const int64_t nred = (int64_t)bwd::Dims<N>::kMix * N * a.d + a.d;
+  hipLaunchKernelGGL((bwd::param_reduce_kernel<N>), dim3((unsigned)((nred + 255) / 256)),
+                     dim3(256), 0, st, a);
+  if ((s = launch_status("backward parameter reduction launch")) != MHC_OK) return s;
+  hipLaunchKernelGGL((bwd::slot_kernel<N>), dim3(bwd::Dims<N>::kMix), dim3(256), 0, st, a);
+  if ((s = launch_status("backward slot reduction launch")) != MHC_OK) return s;
+  hipLaunchKernelGGL((bwd::scale_kernel<N>), dim3(1), dim3(64), 0, st, a);
+  return launch_status("backward scale reduction launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -1877,6 +1913,64 @@ mhc_status mhc_sinkhorn_n(int32_t n, const float* mixes, int64_t tokens, const f
                                   post_out, comb_out, st); break;
   }
   return launch_status("general-n split/Sinkhorn kernel launch");
+}
+
+int64_t mhc_fused_step_backward_workspace_bytes_n(int32_t n, int64_t tokens, int32_t d) {
+  if (!bwd_supported(n) || tokens < 0 || d <= 0 || d % kStep != 0) {
+    fail(MHC_ERR_INVALID_ARG, "bad n (%d), tokens (%lld) or d (%d)", n, (long long)tokens, d);
+    return -1;
+  }
+  return bwd_workspace_floats(n, tokens, d) * 4;
+}
+
+mhc_status mhc_fused_step_backward_n(
+    int32_t n, const void* x, const void* f, int32_t dtype, int64_t tokens, int32_t d,
+    const float* pre_in, const float* post_in, const float* comb_in, const void* x_out,
+    const float* mix, const float* w_mix, const float* base, const float* scale,
+    const float* gamma, int32_t sinkhorn_iters, float norm_eps, float hc_eps, const void* d_x_out,
+    const void* d_y, const float* d_pre, const float* d_post, const float* d_comb, void* d_x,
+    void* d_f, float* d_pre_in, float* d_post_in, float* d_comb_in, float* d_w_mix,
+    float* d_base, float* d_scale, float* d_gamma, void* workspace, int64_t workspace_bytes,
+    mhc_stream_t stream) {
+  if (!bwd_supported(n))
+    return fail(MHC_ERR_UNSUPPORTED, "backward: n = %d streams (2 or 4 supported)", n);
+  mhc_status s = check_common(dtype, tokens, d, sinkhorn_iters, norm_eps, hc_eps);
+  if (s != MHC_OK) return s;
+  if (tokens == 0) return ok();
+  const uint64_t es = elem_size(dtype), T = (uint64_t)tokens, nn = (uint64_t)n, nm = n_mix(n);
+  const int64_t need = bwd_workspace_floats(n, tokens, d) * 4;
+  if (workspace_bytes < need)
+    return fail(MHC_ERR_INVALID_ARG, "workspace holds %lld bytes, %lld needed",
+                (long long)workspace_bytes, (long long)need);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(MHC_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+  const Span in[] = {
+      {"x", x, T * nn * d * es},            {"f", f, T * d * es},
+      {"pre_in", pre_in, T * nn * 4},       {"post_in", post_in, T * nn * 4},
+      {"comb_in", comb_in, T * nn * nn * 4}, {"x_out", x_out, T * nn * d * es},
+      {"mix", mix, T * nm * 4},             {"w_mix", w_mix, nm * nn * d * 4},
+      {"base", base, nm * 4},               {"scale", scale, 12},
+      {"gamma", gamma, (uint64_t)d * 4},    {"d_x_out", d_x_out, T * nn * d * es},
+      {"d_y", d_y, T * d * es},             {"d_pre", d_pre, T * nn * 4},
+      {"d_post", d_post, T * nn * 4},       {"d_comb", d_comb, T * nn * nn * 4},
+  };
+  const Span out[] = {
+      {"d_x", d_x, T * nn * d * es},        {"d_f", d_f, T * d * es},
+      {"d_pre_in", d_pre_in, T * nn * 4},   {"d_post_in", d_post_in, T * nn * 4},
+      {"d_comb_in", d_comb_in, T * nn * nn * 4}, {"d_w_mix", d_w_mix, nm * nn * d * 4},
+      {"d_base", d_base, nm * 4},           {"d_scale", d_scale, 12},
+      {"d_gamma", d_gamma, (uint64_t)d * 4}, {"workspace", workspace, (uint64_t)need},
+  };
+  s = check_spans(in, 16, out, 10, nullptr, nullptr);
+  if (s != MHC_OK) return s;
+  bwd::Args a{x, f, pre_in, post_in, comb_in, x_out, mix, w_mix, base, scale, gamma, d_x_out,
+              d_y, d_pre, d_post, d_comb, d_x, d_f, d_pre_in, d_post_in, d_comb_in, d_w_mix,
+              d_base, d_scale, d_gamma, static_cast<float*>(workspace), tokens, d,
+              sinkhorn_iters, norm_eps, hc_eps};
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (n == 2)
+    return dtype == MHC_BF16 ? run_backward<2, MHC_BF16>(a, st) : run_backward<2, MHC_F32>(a, st);
+  return dtype == MHC_BF16 ? run_backward<4, MHC_BF16>(a, st) : run_backward<4, MHC_F32>(a, st);
 }
 
 }  // extern "C"

@@ -29,7 +29,8 @@ def test_header_declares_the_entry_points():
                "mhc_wmix_packed_bytes", "mhc_status_string", "mhc_last_error",
                "mhc_abi_version", "mhc_d_granule", "mhc_fused_step_workspace_bytes",
                "mhc_hc_post", "mhc_hc_pre", "mhc_rmsnorm", "mhc_wmix_packed_bytes_n",
-               "mhc_pack_wmix_n", "mhc_fused_step_n", "mhc_mixes_n", "mhc_sinkhorn_n"):
+               "mhc_pack_wmix_n", "mhc_fused_step_n", "mhc_mixes_n", "mhc_sinkhorn_n",
+               "mhc_fused_step_backward_n", "mhc_fused_step_backward_workspace_bytes_n"):
         assert fn in names
 
 
@@ -41,7 +42,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_granule_and_status_strings():
-    assert binding.abi_version() == 4
+    assert binding.abi_version() == 5
     assert binding.d_granule() == 32
     lib = binding.load()
     assert lib.mhc_status_string(0) == b"MHC_OK"
@@ -286,3 +287,53 @@ def test_mixes_n_sinkhorn_n_pack_n_validation():
                                None) == binding.MHC_ERR_INVALID_ARG
     assert lib.mhc_pack_wmix_n(5, p["x"], D, binding.MHC_BF16, p["w_packed"], need,
                                None) == binding.MHC_ERR_UNSUPPORTED
+
+
+# ---- backward --------------------------------------------------------------------------
+
+def _call_bwd(n=4, **over):
+    p = _layout_n(n)
+    ws_addr = A + (1 << 36)
+    args = dict(n=n, x=p["x"], f=p["f"], dtype=binding.MHC_BF16, tokens=T, d=D,
+                pre_in=p["pre_in"], post_in=p["post_in"], comb_in=p["comb_in"],
+                x_out=p["x_out"], mix=p["mix_out"], w_mix=p["w_packed"], base=p["base"],
+                scale=p["scale"], gamma=p["gamma"], iters=20, norm_eps=1e-6, hc_eps=1e-6,
+                d_x_out=A + (1 << 37), d_y=A + (1 << 37) + (1 << 30), d_pre=p["pre_out"],
+                d_post=p["post_out"], d_comb=p["comb_out"], d_x=A + (1 << 38),
+                d_f=A + (1 << 38) + (1 << 30), d_pre_in=A + (1 << 39),
+                d_post_in=A + (1 << 39) + (1 << 20), d_comb_in=A + (1 << 39) + (2 << 20),
+                d_w_mix=A + (1 << 39) + (4 << 20), d_base=A + (1 << 39) + (64 << 20),
+                d_scale=A + (1 << 39) + (65 << 20), d_gamma=A + (1 << 39) + (66 << 20),
+                workspace=ws_addr,
+                workspace_bytes=binding.load().mhc_fused_step_backward_workspace_bytes_n(n, T, D),
+                stream=None)
+    args.update(over)
+    return binding.load().mhc_fused_step_backward_n(*args.values())
+
+
+def test_backward_workspace_bytes():
+    lib = binding.load()
+    assert lib.mhc_fused_step_backward_workspace_bytes_n(4, 1000, 5120) > 0
+    assert lib.mhc_fused_step_backward_workspace_bytes_n(8, 1000, 5120) == -1
+    assert lib.mhc_fused_step_backward_workspace_bytes_n(4, -1, 5120) == -1
+    assert lib.mhc_fused_step_backward_workspace_bytes_n(2, 10, 48) == -1
+
+
+@pytest.mark.parametrize("over,status,needle", [
+    (dict(n=8), binding.MHC_ERR_UNSUPPORTED, "streams"),
+    (dict(iters=0), binding.MHC_ERR_INVALID_ARG, "sinkhorn_iters"),
+    (dict(workspace_bytes=1024), binding.MHC_ERR_INVALID_ARG, "workspace holds"),
+    (dict(workspace=A + (1 << 36) + 16), binding.MHC_ERR_INVALID_ARG, "256-byte"),
+    (dict(mix=None), binding.MHC_ERR_INVALID_ARG, "mix is NULL"),
+    (dict(d_gamma=None), binding.MHC_ERR_INVALID_ARG, "d_gamma is NULL"),
+    (dict(d_x="x"), binding.MHC_ERR_INVALID_ARG, "overlaps input"),
+])
+def test_backward_rejects_bad_arguments(over, status, needle):
+    p = _layout_n(4)
+    over = {k: (p[v] if isinstance(v, str) else v) for k, v in over.items()}
+    assert _call_bwd(**over) == status
+    assert needle in binding.last_error()
+
+
+def test_backward_zero_tokens():
+    assert _call_bwd(tokens=0) == binding.MHC_OK
