@@ -134,14 +134,15 @@ __device__ __forceinline__ void sk_step(float (&c)[N][N], float (&s)[N], int k, 
     normalise<N, true>(c, s, eps);
 }
 
-// The reverse pass recomputes the forward up to each normalisation (memory
-// stays O(N^2) per thread; the work is O(iters^2 N^2), small at the pages'
-// 20 rounds). For Y = X / (sum + eps) along an axis,
+// The reverse pass recomputes the forward up to each normalisation from the
+// nearest of kCp checkpoints (the matrices entering every seg-th step), so
+// the state stays O(kCp N^2) registers and the work O(iters^2 / kCp). For Y = X / (sum + eps) along an axis,
 // dX = (dY - sum_axis(dY * Y)) / (sum + eps); for P = softmax(L) along rows,
 // dL = P * (dP - sum_row(dP * P)).
 template <int N>
 __global__ __launch_bounds__(256) void split_kernel(Args a) {
   constexpr int kMix = Dims<N>::kMix;
+  constexpr int kCp = 8;
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (t >= a.tokens) return;
   const float* m = a.mix + t * kMix;
@@ -178,26 +179,50 @@ __global__ __launch_bounds__(256) void split_kernel(Args a) {
 #pragma unroll
     for (int k = 0; k < N; ++k) dc[j][k] = a.d_comb[(t * N + j) * N + k];
   const float eps = a.hc_eps;
+  // checkpoints: the input of step cp * seg, kept for kCp segments
   const int nsteps = 2 * a.iters - 1;
-  for (int step = nsteps - 1; step >= 0; --step) {
+  const int seg = (nsteps + kCp - 1) / kCp;
+  float ck[kCp][N][N];
+  {
     float c[N][N], s[N];
 #pragma unroll
     for (int j = 0; j < N; ++j)
 #pragma unroll
       for (int k = 0; k < N; ++k) c[j][k] = p[j][k] + eps;
-    for (int q = 0; q <= step; ++q) sk_step<N>(c, s, q, eps);   // c = output of `step`
-    const bool row = step != 0 && (step & 1);
 #pragma unroll
-    for (int a2 = 0; a2 < N; ++a2) {
-      float dot = 0.f;
+    for (int cp = 0; cp < kCp; ++cp) {
 #pragma unroll
-      for (int b = 0; b < N; ++b) dot += row ? dc[a2][b] * c[a2][b] : dc[b][a2] * c[b][a2];
+      for (int j = 0; j < N; ++j)
 #pragma unroll
-      for (int b = 0; b < N; ++b) {
-        if (row)
-          dc[a2][b] = (dc[a2][b] - dot) / s[a2];
-        else
-          dc[b][a2] = (dc[b][a2] - dot) / s[a2];
+        for (int k = 0; k < N; ++k) ck[cp][j][k] = c[j][k];
+      const int hi = (cp + 1) * seg < nsteps ? (cp + 1) * seg : nsteps;
+      for (int q = cp * seg; q < hi; ++q) sk_step<N>(c, s, q, eps);
+    }
+  }
+#pragma unroll
+  for (int cp = kCp - 1; cp >= 0; --cp) {
+    const int lo = cp * seg;
+    const int hi = lo + seg < nsteps ? lo + seg : nsteps;
+    for (int step = hi - 1; step >= lo; --step) {
+      float c[N][N], s[N];
+#pragma unroll
+      for (int j = 0; j < N; ++j)
+#pragma unroll
+        for (int k = 0; k < N; ++k) c[j][k] = ck[cp][j][k];
+      for (int q = lo; q <= step; ++q) sk_step<N>(c, s, q, eps);   // c = output of `step`
+      const bool row = step != 0 && (step & 1);
+#pragma unroll
+      for (int a2 = 0; a2 < N; ++a2) {
+        float dot = 0.f;
+#pragma unroll
+        for (int b = 0; b < N; ++b) dot += row ? dc[a2][b] * c[a2][b] : dc[b][a2] * c[b][a2];
+#pragma unroll
+        for (int b = 0; b < N; ++b) {
+          if (row)
+            dc[a2][b] = (dc[a2][b] - dot) / s[a2];
+          else
+            dc[b][a2] = (dc[b][a2] - dot) / s[a2];
+        }
       }
     }
   }
