@@ -18,7 +18,8 @@
 //   d pre_in_k = sum_f dh X'_k                               stream_kernel
 //   d gamma[f] = sum_t dy h rho (per-workgroup partials)    stream_kernel
 //   dW[i][k d + f] = sum_t V_i X'_k[f]                       param_kernel
-//   d base_i = sum_t g_i, d scale = sums of g_i m_i per group  slot_kernel
+//   d base_i = sum_t g_i, d scale = sums of g_i m_i per group
+//                                                slot_kernel, scale_kernel
 //
 // Layout of the stream kernel follows the general-n block kernel: a
 // workgroup owns 128 tokens, each wave 16 of them over all features. W^T V is
@@ -39,6 +40,7 @@ constexpr int kThreads = gen::kThreads;
 constexpr int kBlock = gen::kBlock;
 constexpr int kStep = gen::kStep;
 constexpr int kParamChunks = 16;   // token chunks of the parameter kernel
+constexpr int kSlotChunks = 256;   // token chunks of the slot sums
 
 template <int N>
 struct Dims {
@@ -65,7 +67,9 @@ struct Ws {
     return pw_off() + al64((int64_t)kParamChunks * Dims<N>::kMix * N * d);
   }
   __host__ __device__ int64_t e_off() const { return pg_off() + al64(groups() * d); }
-  __host__ __device__ int64_t floats() const { return e_off() + al64(Dims<N>::kMix); }
+  __host__ __device__ int64_t floats() const {
+    return e_off() + al64((int64_t)kSlotChunks * 2 * Dims<N>::kMix);
+  }
 };
 
 struct Args {
@@ -627,69 +631,220 @@ __global__ __launch_bounds__(256) void param_kernel(Args a) {
   for (int i = 0; i < kMix; ++i) pw[(int64_t)i * N * d + (int64_t)k * d + f] = acc[i];
 }
 
-// Sum of the per-chunk partials, in chunk order.
+// bf16 streams: the same partial sums on v_mfma_f32_16x16x32_bf16. A wave
+// owns 64 features of one stream and the chunk's tokens, 32 at a time:
+//   D[slot][feature] += V^T[slot][token] X'[token][feature]
+// with A = V^T (slots 16 st + lane % 16, tokens 8 (lane / 16) + 0..7) split
+// into three exact bf16 terms (hi, mid, lo) accumulated into the same tile,
+// and B = X' (exact in bf16), where column c of feature tile tau is feature
+// 4c + tau, so that a lane loads 4 adjacent features of a token row (8 bytes)
+// and the 16 lanes of a row group cover 128 contiguous bytes.
+template <int N>
+__global__ __launch_bounds__(256) void param_mfma_kernel(Args a) {
+  constexpr int kMix = Dims<N>::kMix;
+  constexpr int kST = Dims<N>::kSlots / 16;   // slot tiles
+  typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+  const int d = a.d;
+  const int lane = threadIdx.x & 63;
+  const int c = lane & 15, g = lane >> 4;
+  const int64_t f0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 64;   // 64 features
+  const int k = blockIdx.y;
+  const int chunk = blockIdx.z;
+  if (f0 >= d) return;
+  Ws<N> wsl{a.tokens, d};
+  const int64_t per = (a.tokens + kParamChunks - 1) / kParamChunks;
+  const int64_t t0 = chunk * per;
+  const int64_t t1 = t0 + per < a.tokens ? t0 + per : a.tokens;
+  const float* v = a.ws + wsl.v_off();
+  const uint16_t* xo = static_cast<const uint16_t*>(a.x_out);
+  f32x4 acc[kST][4];
+#pragma unroll
+  for (int st = 0; st < kST; ++st)
+#pragma unroll
+    for (int tau = 0; tau < 4; ++tau) acc[st][tau] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int64_t tb = t0; tb < t1; tb += 32) {
+    // B: X'[tb + 8g + e][k][f0 + 4c .. +3], e = 0..7
+    uint32_t xw[8][2];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int64_t t = tb + 8 * g + e;
+      const int64_t tc = t < t1 ? t : t1 - 1;
+      const uint32_t* p =
+          reinterpret_cast<const uint32_t*>(xo + (tc * N + k) * (int64_t)d + f0 + 4 * c);
+      xw[e][0] = t < t1 ? p[0] : 0u;
+      xw[e][1] = t < t1 ? p[1] : 0u;
+    }
+    bf16x8_t B[4];   // feature tile tau: feature 4c + tau of the 8 tokens
+#pragma unroll
+    for (int tau = 0; tau < 4; ++tau) {
+      u32x4 w;
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const uint32_t a0 = xw[2 * e2][tau >> 1], a1 = xw[2 * e2 + 1][tau >> 1];
+        const uint32_t lo = (tau & 1) ? (a0 >> 16) : (a0 & 0xffffu);
+        const uint32_t hi = (tau & 1) ? (a1 & 0xffff0000u) : (a1 << 16);
+        w[e2] = lo | hi;
+      }
+      B[tau] = __builtin_bit_cast(bf16x8_t, w);
+    }
+#pragma unroll
+    for (int st = 0; st < kST; ++st) {
+      // A: V[tb + 8g + e][16 st + c], split into three bf16 terms
+      float vv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int64_t t = tb + 8 * g + e;
+        vv[e] = t < t1 ? v[t * Dims<N>::kSlots + 16 * st + c] : 0.f;
+      }
+      u32x4 th, tm, tl;
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        float h2[2], m2[2], l2[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const float x = vv[2 * e2 + u];
+          h2[u] = __uint_as_float(pack_bf16x2(x, 0.f) << 16);
+          const float r1 = x - h2[u];
+          m2[u] = __uint_as_float(pack_bf16x2(r1, 0.f) << 16);
+          l2[u] = r1 - m2[u];
+        }
+        th[e2] = pack_bf16x2(h2[0], h2[1]);
+        tm[e2] = pack_bf16x2(m2[0], m2[1]);
+        tl[e2] = pack_bf16x2(l2[0], l2[1]);
+      }
+      const bf16x8_t Ah = __builtin_bit_cast(bf16x8_t, th);
+      const bf16x8_t Am = __builtin_bit_cast(bf16x8_t, tm);
+      const bf16x8_t Al = __builtin_bit_cast(bf16x8_t, tl);
+#pragma unroll
+      for (int tau = 0; tau < 4; ++tau) {
+        acc[st][tau] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ah, B[tau], acc[st][tau], 0, 0, 0);
+        acc[st][tau] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Am, B[tau], acc[st][tau], 0, 0, 0);
+        acc[st][tau] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Al, B[tau], acc[st][tau], 0, 0, 0);
+      }
+    }
+  }
+  // D[slot 16 st + 4g + i][feature 4c + tau] = acc[st][tau][i]
+  float* pw = a.ws + wsl.pw_off() + (int64_t)chunk * kMix * N * d;
+#pragma unroll
+  for (int st = 0; st < kST; ++st)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int slot = 16 * st + 4 * g + i;
+      if (slot < kMix)
+        st4f(pw + (int64_t)slot * N * d + (int64_t)k * d + f0 + 4 * c,
+             f32x4{acc[st][0][i], acc[st][1][i], acc[st][2][i], acc[st][3][i]});
+    }
+}
+
+// dW: sum of the per-chunk partials, in chunk order.
 template <int N>
 __global__ __launch_bounds__(256) void param_reduce_kernel(Args a) {
   const int d = a.d;
   const int64_t nw = (int64_t)Dims<N>::kMix * N * d;
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= nw) return;
   Ws<N> wsl{a.tokens, d};
-  if (i < nw) {
-    const float* pw = a.ws + wsl.pw_off();
-    float s = 0.f;
-    for (int c = 0; c < kParamChunks; ++c) s += pw[(int64_t)c * nw + i];
-    a.d_w[i] = s;
-  } else if (i < nw + d) {
-    const int64_t f = i - nw;
-    const float* pg = a.ws + wsl.pg_off();
-    float s = 0.f;
-    for (int64_t c = 0; c < wsl.groups(); ++c) s += pg[c * d + f];
-    a.d_gamma[f] = s;
-  }
+  const float* pw = a.ws + wsl.pw_off();
+  float s = 0.f;
+  for (int c = 0; c < kParamChunks; ++c) s += pw[(int64_t)c * nw + i];
+  a.d_w[i] = s;
 }
 
-// d base and the per-slot sums of g * m: one workgroup per slot, a fixed-order
-// tree over the tokens; the last step folds the slot sums into d scale.
+// d gamma: the per-workgroup partials summed in a fixed order. A block owns
+// 64 features; its 4 waves sum the workgroups w = slice, slice + 4, ... (8 at
+// a time, so that their loads are in flight together), then the 4 slice sums
+// are added in slice order.
+template <int N>
+__global__ __launch_bounds__(256) void gamma_reduce_kernel(Args a) {
+  __shared__ float part[4][64];
+  const int d = a.d;
+  const int lane = threadIdx.x & 63, slice = threadIdx.x >> 6;
+  const int64_t f = (int64_t)blockIdx.x * 64 + lane;
+  Ws<N> wsl{a.tokens, d};
+  const int64_t groups = wsl.groups();
+  const float* pg = a.ws + wsl.pg_off();
+  float s = 0.f;
+  if (f < d) {
+    for (int64_t w0 = slice; w0 < groups; w0 += 32) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t w = w0 + 4 * u;
+        v[u] = w < groups ? pg[w * d + f] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += v[u];
+    }
+  }
+  part[slice][lane] = s;
+  __syncthreads();
+  if (slice == 0 && f < d)
+    a.d_gamma[f] = ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
+}
+
+// d base and the per-slot sums of g * m, stage 1: each block sums a chunk of
+// consecutive tokens (contiguous rows of g and of the mixes) per slot, with a
+// fixed-order tree.
 template <int N>
 __global__ __launch_bounds__(256) void slot_kernel(Args a) {
   constexpr int kMix = Dims<N>::kMix;
+  constexpr int kRows = 256 / kMix;   // token rows per pass of the block
   __shared__ float sg[256], sm[256];
-  const int i = blockIdx.x;
   Ws<N> wsl{a.tokens, a.d};
   const float* g = a.ws + wsl.g_off();
+  const int64_t per = (a.tokens + kSlotChunks - 1) / kSlotChunks;
+  const int64_t t0 = blockIdx.x * per;
+  const int64_t t1 = t0 + per < a.tokens ? t0 + per : a.tokens;
+  const int i = threadIdx.x % kMix, r = threadIdx.x / kMix;
   float s1 = 0.f, s2 = 0.f;
-  for (int64_t t = threadIdx.x; t < a.tokens; t += 256) {
-    const float gv = g[t * kMix + i];
-    s1 += gv;
-    s2 = fmaf(gv, a.mix[t * kMix + i], s2);
+  if (r < kRows) {
+    for (int64_t t = t0 + r; t < t1; t += kRows) {
+      const float gv = g[t * kMix + i];
+      s1 += gv;
+      s2 = fmaf(gv, a.mix[t * kMix + i], s2);
+    }
   }
   sg[threadIdx.x] = s1;
   sm[threadIdx.x] = s2;
   __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if ((int)threadIdx.x < w) {
-      sg[threadIdx.x] += sg[threadIdx.x + w];
-      sm[threadIdx.x] += sm[threadIdx.x + w];
+  if (threadIdx.x < kMix) {
+    float a1 = 0.f, a2 = 0.f;
+    for (int rr = 0; rr < kRows; ++rr) {
+      a1 += sg[rr * kMix + threadIdx.x];
+      a2 += sm[rr * kMix + threadIdx.x];
     }
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) {
-    a.d_base[i] = sg[0];
-    a.ws[wsl.e_off() + i] = sm[0];
+    float* e = a.ws + wsl.e_off() + (int64_t)blockIdx.x * 2 * kMix;
+    e[threadIdx.x] = a1;
+    e[kMix + threadIdx.x] = a2;
   }
 }
 
+// Stage 2: chunk sums in chunk order; d scale folds the slot sums of g * m
+// per group.
 template <int N>
 __global__ __launch_bounds__(64) void scale_kernel(Args a) {
   constexpr int kMix = Dims<N>::kMix;
-  if (threadIdx.x != 0) return;
+  __shared__ float em[kMix];
   Ws<N> wsl{a.tokens, a.d};
   const float* e = a.ws + wsl.e_off();
-  float s[3] = {0.f, 0.f, 0.f};
-  for (int i = 0; i < kMix; ++i) s[i < N ? 0 : (i < 2 * N ? 1 : 2)] += e[i];
-  a.d_scale[0] = s[0];
-  a.d_scale[1] = s[1];
-  a.d_scale[2] = s[2];
+  const int i = threadIdx.x;
+  if (i < kMix) {
+    float s1 = 0.f, s2 = 0.f;
+    for (int c = 0; c < kSlotChunks; ++c) {
+      s1 += e[(int64_t)c * 2 * kMix + i];
+      s2 += e[(int64_t)c * 2 * kMix + kMix + i];
+    }
+    a.d_base[i] = s1;
+    em[i] = s2;
+  }
+  __syncthreads();
+  if (i == 0) {
+    float s[3] = {0.f, 0.f, 0.f};
+    for (int j = 0; j < kMix; ++j) s[j < N ? 0 : (j < 2 * N ? 1 : 2)] += em[j];
+    a.d_scale[0] = s[0];
+    a.d_scale[1] = s[1];
+    a.d_scale[2] = s[2];
+  }
 }
 
 }  // namespace bwd

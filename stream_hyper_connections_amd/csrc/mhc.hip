@@ -1522,6 +1522,10 @@ int64_t bwd_workspace_floats(int32_t n, int64_t tokens, int32_t d) {
   return bwd::Ws<4>{tokens, d}.floats();
 }
 
+#ifndef MHC_BWD_MFMA_DW
+#define MHC_BWD_MFMA_DW 1   // dW on bf16 MFMA for bf16 streams with d % 64 == 0
+#endif
+
 template <int N, int DT>
 mhc_status run_backward(const bwd::Args& a, hipStream_t st) {
   const unsigned tok256 = (unsigned)((a.tokens + 255) / 256);
@@ -1535,14 +1539,23 @@ mhc_status run_backward(const bwd::Args& a, hipStream_t st) {
                      dim3((unsigned)((a.tokens + bwd::kBlock - 1) / bwd::kBlock)),
                      dim3(bwd::kThreads), 0, st, a);
   if ((s = launch_status("backward stream kernel launch")) != MHC_OK) return s;
-  hipLaunchKernelGGL((bwd::param_kernel<N, DT>),
-                     dim3((unsigned)((a.d + 255) / 256), N, bwd::kParamChunks), dim3(256), 0, st, a);
+  if (DT == MHC_BF16 && MHC_BWD_MFMA_DW && a.d % 64 == 0)
+    hipLaunchKernelGGL((bwd::param_mfma_kernel<N>),
+                       dim3((unsigned)((a.d / 64 + 3) / 4), N, bwd::kParamChunks), dim3(256), 0, st,
+                       a);
+  else
+    hipLaunchKernelGGL((bwd::param_kernel<N, DT>),
+                       dim3((unsigned)((a.d + 255) / 256), N, bwd::kParamChunks), dim3(256), 0, st,
+                       a);
   if ((s = launch_status("backward parameter kernel launch")) != MHC_OK) return s;
-  const int64_t nred = (int64_t)bwd::Dims<N>::kMix * N * a.d + a.d;
-  hipLaunchKernelGGL((bwd::param_reduce_kernel<N>), dim3((unsigned)((nred + 255) / 256)),
+  const int64_t nw = (int64_t)bwd::Dims<N>::kMix * N * a.d;
+  hipLaunchKernelGGL((bwd::param_reduce_kernel<N>), dim3((unsigned)((nw + 255) / 256)),
                      dim3(256), 0, st, a);
   if ((s = launch_status("backward parameter reduction launch")) != MHC_OK) return s;
-  hipLaunchKernelGGL((bwd::slot_kernel<N>), dim3(bwd::Dims<N>::kMix), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((bwd::gamma_reduce_kernel<N>), dim3((unsigned)((a.d + 63) / 64)), dim3(256),
+                     0, st, a);
+  if ((s = launch_status("backward gain reduction launch")) != MHC_OK) return s;
+  hipLaunchKernelGGL((bwd::slot_kernel<N>), dim3(bwd::kSlotChunks), dim3(256), 0, st, a);
   if ((s = launch_status("backward slot reduction launch")) != MHC_OK) return s;
   hipLaunchKernelGGL((bwd::scale_kernel<N>), dim3(1), dim3(64), 0, st, a);
   return launch_status("backward scale reduction launch");
