@@ -23,10 +23,11 @@
 //
 // Layout of the stream kernel follows the general-n block kernel: a
 // workgroup owns 128 tokens, each wave 16 of them over all features. W^T V is
-// a product over the (2+n)n slots, computed with v_mfma_f32_16x16x4_f32 on
-// float32 weights staged in LDS one step at a time, with the weights as the A
-// operand (rows = features) and V as the B operand (columns = tokens), so the
-// result lands in the lane that holds the token's features. Reductions over
+// a product over the (2+n)n slots, computed with v_mfma_f32_16x16x32_bf16 on
+// exact three-term bf16 splits of W (staged in LDS one step at a time) and of
+// V, with the weights as the A operand (rows = features) and V as the B
+// operand (columns = tokens), so the result lands in the lane that holds the
+// token's features. Reductions over
 // tokens (dW, d gamma, d base, d scale) are written as per-chunk partial sums
 // and added in a fixed order: the results are deterministic.
 //
@@ -45,10 +46,10 @@ constexpr int kSlotChunks = 256;   // token chunks of the slot sums
 template <int N>
 struct Dims {
   static constexpr int kMix = (2 + N) * N;
-  static constexpr int kSlots = (kMix + 15) / 16 * 16;   // padded to whole u32x4 groups of K
-  static constexpr int kKc = kSlots / 4;                  // K chunks of the f32 MFMA
-  static constexpr int kVecs = N * 2 * (kSlots / 16) * 64;   // u32x4 of one step's W^T
-  static constexpr int kItems = N * kSlots * 8;               // f32x4 loads staging one step
+  static constexpr int kSlots = 32;   // the K of one bf16 MFMA, (2+n)n padded
+  static_assert(kMix <= kSlots, "the backward covers n <= 4");
+  static constexpr int kVecs = N * 2 * 3 * 64;    // u32x4 of one step's W^T (3 terms)
+  static constexpr int kItems = N * kSlots * 8;   // f32x4 loads staging one step
   static constexpr int kStage = (kItems + kThreads - 1) / kThreads;
 };
 
@@ -328,9 +329,10 @@ __global__ __launch_bounds__(256) void stats_kernel(Args a) {
 
 // ----- the stream kernel ----------------------------------------------------------------
 
-// One step's W^T in the A-operand order of v_mfma_f32_16x16x4_f32: u32x4
-// index ((k * 2 + q) * (kSlots / 16) + c4) * 64 + lane holds, in element e,
-// W[16 c4 + 4 e + lane / 16][k d + 32 s + feat(q, lane % 16)] with
+// One step's W^T in the A-operand order of v_mfma_f32_16x16x32_bf16, as
+// three exact bf16 terms (hi, mid, lo): u32x4 index ((k * 2 + q) * 3 + term)
+// * 64 + lane holds, in bf16 element e, the term of
+// W[8 (lane / 16) + e][k d + 32 s + feat(q, lane % 16)] with
 // feat(q, rho) = 8 (rho / 4) + 4 q + rho % 4, so that the product's rows
 // 4g..4g+3 are features 8g + 4q + 0..3 (the lane's own features).
 // Staging item i = ((k * kSlots) + slot) * 8 + c8 covers features 4 c8..4 c8+3.
@@ -351,8 +353,19 @@ __device__ __forceinline__ void stage_load(f32x4 (&st)[Dims<N>::kStage], const f
   }
 }
 
+// The three bf16 terms of x: hi = bf16(x), mid = bf16(x - hi), lo = x - hi - mid
+// (both differences exact in float32; hi + mid + lo == x), as bits.
+__device__ __forceinline__ void split3(float x, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+  const float h = __uint_as_float(pack_bf16x2(x, 0.f) << 16);
+  const float r1 = x - h;
+  const float m = __uint_as_float(pack_bf16x2(r1, 0.f) << 16);
+  hi = pack_bf16x2(x, 0.f) & 0xffffu;
+  mid = pack_bf16x2(r1, 0.f) & 0xffffu;
+  lo = pack_bf16x2(r1 - m, 0.f) & 0xffffu;
+}
+
 template <int N>
-__device__ __forceinline__ void stage_store(float* wl, const f32x4 (&st)[Dims<N>::kStage],
+__device__ __forceinline__ void stage_store(uint16_t* wl, const f32x4 (&st)[Dims<N>::kStage],
                                             int tid) {
   using D = Dims<N>;
 #pragma unroll
@@ -364,11 +377,15 @@ __device__ __forceinline__ void stage_store(float* wl, const f32x4 (&st)[Dims<N>
     const int k = (i >> 3) / D::kSlots;
     const int q = c8 & 1;                 // features 4 c8 .. 4 c8 + 3: 8 (c8 / 2) + 4 q + 0..3
     const int rho0 = 4 * (c8 >> 1);       // rows rho0 .. rho0 + 3
-    const int c4 = slot >> 4, e = (slot >> 2) & 3, gq = slot & 3;
+    const int e = slot & 7, gq = slot >> 3;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int lane = rho0 + u + 16 * gq;
-      wl[((((k * 2 + q) * (D::kSlots / 16) + c4) * 64 + lane) << 2) + e] = st[r][u];
+      uint32_t t3[3];
+      split3(st[r][u], t3[0], t3[1], t3[2]);
+#pragma unroll
+      for (int term = 0; term < 3; ++term)
+        wl[((((k * 2 + q) * 3 + term) * 64 + lane) << 3) + e] = (uint16_t)t3[term];
     }
   }
 }
@@ -378,7 +395,7 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(Args a) {
   using D = Dims<N>;
   constexpr int kMix = D::kMix;
   constexpr int es = DT == MHC_BF16 ? 2 : 4;
-  __shared__ __align__(16) float wl[2][D::kVecs * 4];
+  __shared__ __align__(16) uint16_t wl[2][D::kVecs * 8];
   __shared__ float red[2][kWaves][kStep];   // per-wave d gamma sums of one step
 
   const int tid = threadIdx.x;
@@ -420,18 +437,28 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(Args a) {
   }
   const float cr = dmm * r * r / (float)(N * d);       // dr r^3 / (n d), dr = dmm / r
   const float kappa = rho * rho * rho * ssum / (float)d;
-  // B operand: V[slot 4 kc + g] of the lane's token
-  float vb[D::kKc];
+  // B operand: V[slot 8g + e] of the lane's token, as three bf16 terms
+  typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+  bf16x8_t vb[3];
+  {
+    u32x4 w3[3];
 #pragma unroll
-  for (int kc = 0; kc < D::kKc; ++kc) {
-    const int i = 4 * kc + g;
-    const float sc = i < N ? a.scale[0] : (i < 2 * N ? a.scale[1] : a.scale[2]);
-    vb[kc] = i < kMix ? r * sc * gr[i] : 0.f;
-  }
-  // V for the parameter kernel: lane g writes the slots it holds
-  if (valid) {
+    for (int e2 = 0; e2 < 4; ++e2) {
+      uint32_t tt[2][3];
 #pragma unroll
-    for (int kc = 0; kc < D::kKc; ++kc) a.ws[wsl.v_off() + t * D::kSlots + 4 * kc + g] = vb[kc];
+      for (int u = 0; u < 2; ++u) {
+        const int i = 8 * g + 2 * e2 + u;
+        const float sc = i < N ? a.scale[0] : (i < 2 * N ? a.scale[1] : a.scale[2]);
+        const float vi = i < kMix ? r * sc * gr[i < kMix ? i : 0] : 0.f;
+        split3(vi, tt[u][0], tt[u][1], tt[u][2]);
+        // V for the parameter kernel: lane g writes the slots it holds
+        if (valid) a.ws[wsl.v_off() + t * D::kSlots + i] = vi;
+      }
+#pragma unroll
+      for (int term = 0; term < 3; ++term) w3[term][e2] = tt[0][term] | (tt[1][term] << 16);
+    }
+#pragma unroll
+    for (int term = 0; term < 3; ++term) vb[term] = __builtin_bit_cast(bf16x8_t, w3[term]);
   }
 
   stage_store<N>(wl[0], st, tid);
@@ -462,22 +489,25 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(Args a) {
     const f32x4 g1 = *reinterpret_cast<const f32x4*>(a.gamma + f0 + 4);
     const float gv[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
 
-    // W^T V for the lane's features: tile q gives features 8g + 4q + 0..3
-    const float* wb = wl[s & 1];
+    // W^T V for the lane's features: tile q gives features 8g + 4q + 0..3.
+    // Six of the nine term products (the three dropped ones are below 2^-24
+    // of the product).
+    const u32x4* wb = reinterpret_cast<const u32x4*>(wl[s & 1]);
     float dxm[N][8];
 #pragma unroll
     for (int k = 0; k < N; ++k) {
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
+        const bf16x8_t w0 = __builtin_bit_cast(bf16x8_t, wb[((k * 2 + q) * 3 + 0) * 64 + lane]);
+        const bf16x8_t w1 = __builtin_bit_cast(bf16x8_t, wb[((k * 2 + q) * 3 + 1) * 64 + lane]);
+        const bf16x8_t w2 = __builtin_bit_cast(bf16x8_t, wb[((k * 2 + q) * 3 + 2) * 64 + lane]);
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int c4 = 0; c4 < D::kSlots / 16; ++c4) {
-          const f32x4 av = *reinterpret_cast<const f32x4*>(
-              wb + ((((k * 2 + q) * (D::kSlots / 16) + c4) * 64 + lane) << 2));
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[e], vb[4 * c4 + e], acc, 0, 0, 0);
-        }
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w2, vb[0], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w0, vb[2], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w1, vb[1], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w1, vb[0], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w0, vb[1], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w0, vb[0], acc, 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) dxm[k][4 * q + i] = acc[i];
       }
