@@ -223,6 +223,75 @@ def backward_bench(w, steps, warmup):
         "config": {"workload": w.name, "sinkhorn_iters": w.iters}}), flush=True)
 
 
+CONFIG_NAMES = ("tiny", "prefill", "decode", "large_prefill", "chain")
+
+
+def all_configs_bench(reps_min=50, min_ms=200.0, flush_bytes=512 << 20):
+    """mhc_fused_step alone on each workload (the chain: its first step), with
+    HIP events around the C-ABI call: warm (10 warm-up calls, then at least
+    `reps_min` calls or `min_ms` of calls) and cache-flushed (a write of
+    `flush_bytes` between calls, outside the timed events, so that the inputs
+    are not served from the 256 MB Infinity Cache). One JSON line per workload
+    with p50 / p95 / p99 in microseconds and tokens/s, GB/s and % of peak at
+    the p50."""
+    import torch
+    import stream_hyper_connections_amd as mhc
+    from stream_hyper_connections_amd import workloads as wl
+    dev = torch.device("cuda:0")
+    scratch = torch.empty(flush_bytes, dtype=torch.uint8, device=dev)
+    for name in CONFIG_NAMES:
+        w = wl.WORKLOADS[name]
+        dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        elem = 2 if w.dtype == "bf16" else 4
+        x = upload_tokens(w, wl.X, 0, dev, dt).view(w.tokens, N, w.d)
+        f = upload_tokens(w, wl.F, 0, dev, dt)
+        prev = {k: torch.as_tensor(v).to(dev) for k, v in wl.params(w, prev=True).items()}
+        cur = {k: torch.as_tensor(v).to(dev) for k, v in wl.params(w).items()}
+        prior = mhc.mixes(x, mhc.pack_wmix(prev["w_mix"], w.dtype), prev["base"], prev["scale"],
+                          w.iters, w.norm_eps, w.hc_eps)
+        wp = mhc.pack_wmix(cur["w_mix"], w.dtype)
+        outs = dict(x_out=torch.empty_like(x), y_out=torch.empty_like(f),
+                    pre_out=torch.empty_like(prior["pre"]),
+                    post_out=torch.empty_like(prior["post"]),
+                    comb_out=torch.empty_like(prior["comb"]))
+
+        def call():
+            mhc.fused_step(x, f, prior["pre"], prior["post"], prior["comb"], wp, cur["base"],
+                           cur["scale"], cur["gamma"], w.iters, w.norm_eps, w.hc_eps, **outs)
+
+        line = {"metric": "fused mHC step latency per workload, n=4", "workload": name,
+                "tokens": w.tokens, "d": w.d, "dtype": w.dtype}
+        alg = algorithmic_bytes(w.tokens, w.d, elem)
+        for mode in ("warm", "flushed"):
+            for _ in range(10):
+                call()
+            torch.cuda.synchronize()
+            times, total = [], 0.0
+            while len(times) < reps_min or total < min_ms:
+                if mode == "flushed":
+                    scratch.fill_(len(times) & 255)
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                call()
+                b.record()
+                b.synchronize()
+                ms = a.elapsed_time(b)
+                times.append(ms)
+                total += ms
+            us = np.array(times) * 1e3
+            p50 = float(np.percentile(us, 50))
+            line[mode] = {"reps": len(times), "p50_us": round(p50, 2),
+                          "p95_us": round(float(np.percentile(us, 95)), 2),
+                          "p99_us": round(float(np.percentile(us, 99)), 2),
+                          "tokens_per_s": round(w.tokens / (p50 / 1e6), 1),
+                          "GBps": round(alg / (p50 / 1e6) / 1e9, 1),
+                          "frac_of_peak": round(alg / (p50 / 1e6) / 1e9 / HBM_PEAK_GBS, 4)}
+        line["algorithmic_bytes"] = alg
+        print(json.dumps(line), flush=True)
+        del x, f, outs, prior
+        torch.cuda.empty_cache()
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -245,6 +314,9 @@ def parse():
     ap.add_argument("--backward", action="store_true",
                     help="time the backward of the step (mhc_fused_step_backward_n) at the "
                          "workload's shape; one JSON line")
+    ap.add_argument("--all-configs", action="store_true",
+                    help="latency of the fused step alone on every workload, warm and "
+                         "cache-flushed (p50/p95/p99); one JSON line per workload")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain device-to-device copy of 2 GiB instead (the reference "
                          "kernel for scaling the HBM byte counters)")
@@ -312,6 +384,16 @@ def upload_tokens(w, tensor, step, dev, dtype_t):
     return out
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, min_seconds):
     """The float64 oracle on consecutive 1,024-token chunks of the same
     workload until at least ``min_seconds`` of oracle time has accumulated.
@@ -336,10 +418,24 @@ def cpu_baseline(w, min_seconds):
         secs += time.perf_counter() - t0
         done += len(idx)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    # one core, on one chunk, for context
+    from threadpoolctl import threadpool_limits
+    idx = np.arange(0, min(chunk, w.tokens))
+    x = wl.streams(w, 0, idx).double().numpy()
+    f = wl.sublayer_out(w, 0, idx).double().numpy()
+    _, pre, post, comb = oracle.mixes(x, prev["w_mix"], prev["base"], prev["scale"], w.iters,
+                                      w.norm_eps, w.hc_eps)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        oracle.fused_step(x, f, pre.astype(np.float32), post.astype(np.float32),
+                          comb.astype(np.float32), cur["w_mix"], cur["base"], cur["scale"],
+                          cur["gamma"], w.iters, w.norm_eps, w.hc_eps, w.dtype)
+        one = len(idx) / (time.perf_counter() - t0)
     return {"value": done / secs, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"float64 NumPy oracle, full step on the first {done} tokens of {w.name} in "
                       f"chunks of {chunk} ({secs:.2f} s of oracle time; inputs and prior prepared "
-                      f"outside the timed region), host CPUs {os.cpu_count()}"}
+                      f"outside the timed region), host CPUs {os.cpu_count()}",
+            "cpu_model": cpu_model(), "single_core_value": round(one, 1)}
 
 
 def main():
@@ -367,6 +463,9 @@ def main():
         return
     if args.backward:
         backward_bench(w, args.steps, args.warmup)
+        return
+    if args.all_configs:
+        all_configs_bench()
         return
     dev = torch.device("cuda:0")
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32

@@ -159,10 +159,11 @@ def pack_wmix(w_mix: torch.Tensor, dtype, out: torch.Tensor | None = None) -> to
     return out
 
 
-# token count from which path="auto" takes the feature-split kernel: below it
-# the cooperative whole-device launch and the per-call load of the projection
-# slices do not pay off
-SPLIT_MIN_TOKENS = 4096
+# token count from which path="auto" takes the feature-split kernel (when it
+# applies to d and the dtype). Measured on 65,536-token down to 16-token calls
+# at d = 5120 it is faster than the tile kernel at every size (59 against 124
+# us at 256 tokens), so it is taken from the first token.
+SPLIT_MIN_TOKENS = 1
 
 _workspaces = {}
 

@@ -1343,10 +1343,19 @@ mhc_status split_config(int32_t dtype, int32_t d, SplitCfg* cfg) {
     }
   }
   if (cfg->groups == 0) return MHC_OK;
+  // cooperative-launch support, cached per device ordinal (1 = no, 2 = yes)
+  static int coop_cache[64];
   int dev = 0, coop = 0;
   hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev);
-  if (e != hipSuccess) return fail(MHC_ERR_HIP, "cooperative-launch attribute: %s", hipGetErrorString(e));
+  if (e == hipSuccess && dev >= 0 && dev < 64 && coop_cache[dev] != 0) {
+    coop = coop_cache[dev] - 1;
+  } else {
+    if (e == hipSuccess)
+      e = hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev);
+    if (e != hipSuccess)
+      return fail(MHC_ERR_HIP, "cooperative-launch attribute: %s", hipGetErrorString(e));
+    if (dev >= 0 && dev < 64) coop_cache[dev] = coop ? 2 : 1;
+  }
   if (!coop) *cfg = SplitCfg{};
   return MHC_OK;
 }

@@ -154,12 +154,15 @@ STEP_CASES = [
 ]
 
 
+# path "tile" always runs the tile kernels; "auto" takes the feature-split
+# kernel where it applies (bf16, d = 5120 here) and the tile kernels otherwise
+@pytest.mark.parametrize("path", ["tile", "auto"])
 @pytest.mark.parametrize("dtype,d,t", STEP_CASES)
-def test_fused_step_parity(dtype, d, t):
-    _log(f"fused dtype={dtype} d={d} T={t}")
+def test_fused_step_parity(dtype, d, t, path):
+    _log(f"fused dtype={dtype} d={d} T={t} path={path}")
     w = wl.Workload(200 + d % 97, "step", t, d, dtype)
     case = make_case(w)
-    out, _ = run_step(case, dtype=dtype)
+    out, _ = run_step(case, dtype=dtype, path=path)
     o = check_step(case, out, dtype)
     _log(f"  ties in new streams: {o['n_ties']}")
 
@@ -210,24 +213,26 @@ def test_zero_tokens_rows():
     assert not out["mix"][39].abs().max().item()
 
 
-def test_in_place_equals_out_of_place():
+@pytest.mark.parametrize("path", ["tile", "auto"])
+def test_in_place_equals_out_of_place(path):
     w = wl.Workload(303, "inplace", 33, 5120, "bf16")
     case = make_case(w)
-    ref, dev = run_step(case)
+    ref, dev = run_step(case, path=path)
     x_dev = dev["x"].clone()
     wp = mhc.pack_wmix(dev["w_mix"], "bf16")
     out = mhc.fused_step(x_dev, dev["f"], dev["pre"], dev["post"], dev["comb"], wp, dev["base"],
-                         dev["scale"], dev["gamma"], x_out=x_dev, want_mix=True)
+                         dev["scale"], dev["gamma"], x_out=x_dev, want_mix=True, path=path)
     torch.cuda.synchronize()
     for k in ("x_out", "y", "pre", "post", "comb", "mix"):
         assert torch.equal(out[k].cpu(), ref[k]), k
 
 
-def test_bitwise_deterministic():
+@pytest.mark.parametrize("path", ["tile", "auto"])
+def test_bitwise_deterministic(path):
     w = wl.Workload(304, "det", 70, 5120, "bf16")
     case = make_case(w)
-    a, _ = run_step(case)
-    b, _ = run_step(case)
+    a, _ = run_step(case, path=path)
+    b, _ = run_step(case, path=path)
     for k in a:
         if a[k] is not None:
             assert torch.equal(a[k], b[k]), k
