@@ -52,11 +52,17 @@ def measured_traffic(workload: str):
     return int(rec["traffic_bytes"])
 
 
+# the sources the measured fused-step kernels are built from (the feature-split
+# kernel, its clear and tail kernels, the packing kernel and their launch code);
+# the general-n, backward and three-kernel sources do not enter them
+FUSED_SOURCES = ("mhc.hip", "split_kernel.h")
+
+
 def kernel_source_hash() -> str:
-    """sha256 over the kernel sources (file names and contents, sorted)."""
+    """sha256 over the fused-step kernel sources (names and contents)."""
     import hashlib
     h = hashlib.sha256()
-    for name in sorted(os.listdir(KERNEL_DIR)):
+    for name in FUSED_SOURCES:
         h.update(name.encode())
         h.update(open(os.path.join(KERNEL_DIR, name), "rb").read())
     return h.hexdigest()
