@@ -61,7 +61,9 @@ struct Ws {
   int d;
   __host__ __device__ int64_t g_off() const { return 0; }
   __host__ __device__ int64_t v_off() const { return g_off() + al64(tokens * Dims<N>::kMix); }
-  __host__ __device__ int64_t st_off() const { return v_off() + al64(tokens * Dims<N>::kSlots); }
+  __host__ __device__ int64_t st_off() const {
+    return v_off() + al64((tokens + 31) / 32 * 32 * Dims<N>::kSlots);
+  }
   __host__ __device__ int64_t pw_off() const { return st_off() + al64(tokens * 4); }
   __host__ __device__ int64_t groups() const { return (tokens + kBlock - 1) / kBlock; }
   __host__ __device__ int64_t pg_off() const {
@@ -72,6 +74,18 @@ struct Ws {
     return e_off() + al64((int64_t)kSlotChunks * 2 * Dims<N>::kMix);
   }
 };
+
+// V[t][slot] in the workspace: blocks of 32 tokens, slot-major inside a block,
+// so that 8 consecutive tokens of one slot are 32 contiguous bytes.
+template <int N>
+__host__ __device__ __forceinline__ int64_t vidx(int64_t t, int slot) {
+  return ((t >> 5) * Dims<N>::kSlots + slot) * 32 + (t & 31);
+}
+
+// Tokens per chunk of the parameter kernels: a multiple of 32.
+__host__ __device__ __forceinline__ int64_t param_per(int64_t tokens) {
+  return ((tokens + kParamChunks - 1) / kParamChunks + 31) / 32 * 32;
+}
 
 struct Args {
   const void* x;
@@ -452,7 +466,7 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(Args a) {
         const float vi = i < kMix ? r * sc * gr[i < kMix ? i : 0] : 0.f;
         split3(vi, tt[u][0], tt[u][1], tt[u][2]);
         // V for the parameter kernel: lane g writes the slots it holds
-        if (valid) a.ws[wsl.v_off() + t * D::kSlots + i] = vi;
+        if (valid) a.ws[wsl.v_off() + vidx<N>(t, i)] = vi;
       }
 #pragma unroll
       for (int term = 0; term < 3; ++term) w3[term][e2] = tt[0][term] | (tt[1][term] << 16);
@@ -629,7 +643,7 @@ __global__ __launch_bounds__(256) void param_kernel(Args a) {
   const int chunk = blockIdx.z;
   if (f >= d) return;
   Ws<N> wsl{a.tokens, d};
-  const int64_t per = (a.tokens + kParamChunks - 1) / kParamChunks;
+  const int64_t per = param_per(a.tokens);
   const int64_t t0 = chunk * per;
   const int64_t t1 = t0 + per < a.tokens ? t0 + per : a.tokens;
   const float* v = a.ws + wsl.v_off();
@@ -651,9 +665,8 @@ __global__ __launch_bounds__(256) void param_kernel(Args a) {
 #pragma unroll
     for (int b = 0; b < kBatch; ++b) {
       const int64_t t = tb + b < t1 ? tb + b : t1 - 1;
-      const float* vt = v + t * Dims<N>::kSlots;
 #pragma unroll
-      for (int i = 0; i < kMix; ++i) acc[i] = fmaf(vt[i], xp[b], acc[i]);
+      for (int i = 0; i < kMix; ++i) acc[i] = fmaf(v[vidx<N>(t, i)], xp[b], acc[i]);
     }
   }
   float* pw = a.ws + wsl.pw_off() + (int64_t)chunk * kMix * N * d;
@@ -668,21 +681,28 @@ __global__ __launch_bounds__(256) void param_kernel(Args a) {
 // into three exact bf16 terms (hi, mid, lo) accumulated into the same tile,
 // and B = X' (exact in bf16), where column c of feature tile tau is feature
 // 4c + tau, so that a lane loads 4 adjacent features of a token row (8 bytes)
-// and the 16 lanes of a row group cover 128 contiguous bytes.
+// and the 16 lanes of a row group cover 128 contiguous bytes. The four waves
+// of a workgroup share the chunk's tokens: V of each 32-token step is staged
+// once in LDS (one 16-byte load per thread), and the next step's X' and V
+// loads are issued before the current step's products. Five waves per SIMD:
+// the d = 5120, n = 4 grid (5,120 waves) then runs in a single round.
 template <int N>
-__global__ __launch_bounds__(256) void param_mfma_kernel(Args a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5, 5))) void param_mfma_kernel(Args a) {
   constexpr int kMix = Dims<N>::kMix;
   constexpr int kST = Dims<N>::kSlots / 16;   // slot tiles
   typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
   const int d = a.d;
   const int lane = threadIdx.x & 63;
   const int c = lane & 15, g = lane >> 4;
-  const int64_t f0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 64;   // 64 features
+  // a wave past the last feature still stages V and meets every barrier; it
+  // reads features 0.. and writes nothing
+  const int64_t fw = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 64;   // 64 features
+  const bool active = fw < d;
+  const int64_t f0 = active ? fw : 0;
   const int k = blockIdx.y;
   const int chunk = blockIdx.z;
-  if (f0 >= d) return;
   Ws<N> wsl{a.tokens, d};
-  const int64_t per = (a.tokens + kParamChunks - 1) / kParamChunks;
+  const int64_t per = param_per(a.tokens);
   const int64_t t0 = chunk * per;
   const int64_t t1 = t0 + per < a.tokens ? t0 + per : a.tokens;
   const float* v = a.ws + wsl.v_off();
@@ -692,17 +712,47 @@ __global__ __launch_bounds__(256) void param_mfma_kernel(Args a) {
   for (int st = 0; st < kST; ++st)
 #pragma unroll
     for (int tau = 0; tau < 4; ++tau) acc[st][tau] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int64_t tb = t0; tb < t1; tb += 32) {
-    // B: X'[tb + 8g + e][k][f0 + 4c .. +3], e = 0..7
-    uint32_t xw[8][2];
+  // one step's X' rows: X'[tb + 8g + e][k][f0 + 4c .. +3] (e = 0..7); rows
+  // past the chunk are read clamped and zeroed before use
+  auto load = [&](uint2 (&xw)[8], int64_t tb) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int64_t t = tb + 8 * g + e;
       const int64_t tc = t < t1 ? t : t1 - 1;
-      const uint32_t* p =
-          reinterpret_cast<const uint32_t*>(xo + (tc * N + k) * (int64_t)d + f0 + 4 * c);
-      xw[e][0] = t < t1 ? p[0] : 0u;
-      xw[e][1] = t < t1 ? p[1] : 0u;
+      xw[e] = *reinterpret_cast<const uint2*>(xo + (tc * N + k) * (int64_t)d + f0 + 4 * c);
+    }
+  };
+  // V of one step (32 tokens x 32 slots, the workspace block) staged in LDS
+  // by the workgroup, rows of 36 floats: slot row, token column
+  __shared__ __align__(16) float vs[2][Dims<N>::kSlots * 36];
+  const int vi = threadIdx.x;   // f32x4 of the block: slot vi / 8, tokens 4 (vi % 8) ..
+  auto vload = [&](int64_t tb) {
+    return *reinterpret_cast<const f32x4*>(v + vidx<N>(tb, 0) + 4 * vi);
+  };
+  auto vstore = [&](int b, f32x4 x) {
+    *reinterpret_cast<f32x4*>(&vs[b][(vi >> 3) * 36 + 4 * (vi & 7)]) = x;
+  };
+  static_assert(Dims<N>::kSlots * 8 == 256, "one f32x4 per thread");
+  uint2 cur[8], nxt[8];
+  if (t0 < t1) {
+    load(cur, t0);
+    vstore(0, vload(t0));
+  }
+  __syncthreads();
+  int buf = 0;
+  for (int64_t tb = t0; tb < t1; tb += 32) {
+    const bool more = tb + 32 < t1;
+    f32x4 vn = {0.f, 0.f, 0.f, 0.f};
+    if (more) {
+      load(nxt, tb + 32);
+      vn = vload(tb + 32);
+    }
+    uint32_t xw[8][2];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const bool ok = tb + 8 * g + e < t1;
+      xw[e][0] = ok ? cur[e].x : 0u;
+      xw[e][1] = ok ? cur[e].y : 0u;
     }
     bf16x8_t B[4];   // feature tile tau: feature 4c + tau of the 8 tokens
 #pragma unroll
@@ -721,10 +771,12 @@ __global__ __launch_bounds__(256) void param_mfma_kernel(Args a) {
     for (int st = 0; st < kST; ++st) {
       // A: V[tb + 8g + e][16 st + c], split into three bf16 terms
       float vv[8];
+      const f32x4 v0 = *reinterpret_cast<const f32x4*>(&vs[buf][(16 * st + c) * 36 + 8 * g]);
+      const f32x4 v1 = *reinterpret_cast<const f32x4*>(&vs[buf][(16 * st + c) * 36 + 8 * g + 4]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int64_t t = tb + 8 * g + e;
-        vv[e] = t < t1 ? v[t * Dims<N>::kSlots + 16 * st + c] : 0.f;
+        const float x = e < 4 ? v0[e] : v1[e - 4];
+        vv[e] = tb + 8 * g + e < t1 ? x : 0.f;
       }
       u32x4 th, tm, tl;
 #pragma unroll
@@ -752,8 +804,14 @@ __global__ __launch_bounds__(256) void param_mfma_kernel(Args a) {
         acc[st][tau] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Al, B[tau], acc[st][tau], 0, 0, 0);
       }
     }
+    if (more) vstore(buf ^ 1, vn);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) cur[e] = nxt[e];
+    buf ^= 1;
+    __syncthreads();
   }
   // D[slot 16 st + 4g + i][feature 4c + tau] = acc[st][tau][i]
+  if (!active) return;
   float* pw = a.ws + wsl.pw_off() + (int64_t)chunk * kMix * N * d;
 #pragma unroll
   for (int st = 0; st < kST; ++st)
