@@ -15,19 +15,21 @@
 //   dA_k   = dX'_k + (W^T V)_k - c X'_k + p_k dh
 //   dX_j   = S(sum_k C[j][k] dA_k), dF = S(sum_k u_k dA_k)
 //   d comb_in[j][k] = sum_f X_j dA_k, d post_in_k = sum_f F dA_k,
-//   d pre_in_k = sum_f dh X'_k                               stream_kernel
-//   d gamma[f] = sum_t dy h rho (per-workgroup partials)    stream_kernel
+//   d pre_in_k = sum_f dh X'_k                    row_kernel / stream_kernel
+//   d gamma[f] = sum_t dy h rho (per-workgroup partials)    the same
 //   dW[i][k d + f] = sum_t V_i X'_k[f]                       param_kernel
 //   d base_i = sum_t g_i, d scale = sums of g_i m_i per group
 //                                                slot_kernel, scale_kernel
 //
-// Layout of the stream kernel follows the general-n block kernel: a
-// workgroup owns 128 tokens, each wave 16 of them over all features. W^T V is
-// a product over the (2+n)n slots, computed with v_mfma_f32_16x16x32_bf16 on
-// exact three-term bf16 splits of W (staged in LDS one step at a time) and of
-// V, with the weights as the A operand (rows = features) and V as the B
-// operand (columns = tokens), so the result lands in the lane that holds the
-// token's features. Reductions over
+// Two stream kernels compute the same arithmetic. row_kernel (bf16 streams,
+// d % 64 == 0) gives each wave 8 tokens and each lane 8 features of one
+// token, so that every load and store moves whole 128-byte row segments;
+// stream_kernel (the other cases) follows the general-n block kernel: a
+// workgroup owns 128 tokens, each wave 16 of them over all features. In both
+// W^T V is a product over the (2+n)n slots, computed with
+// v_mfma_f32_16x16x32_bf16 on exact three-term bf16 splits of W and of V, with
+// the weights as the A operand (rows = features) and V as the B operand
+// (columns = tokens). Reductions over
 // tokens (dW, d gamma, d base, d scale) are written as per-chunk partial sums
 // and added in a fixed order: the results are deterministic.
 //
@@ -41,6 +43,9 @@ constexpr int kThreads = gen::kThreads;
 constexpr int kBlock = gen::kBlock;
 constexpr int kStep = gen::kStep;
 constexpr int kParamChunks = 16;   // token chunks of the parameter kernel
+constexpr int kRowTok = 8;                      // tokens per wave of the row kernel
+constexpr int kRowBlock = kWaves * kRowTok;     // tokens per workgroup of the row kernel
+constexpr int kUnit = 64;                       // features per unit of the row kernel
 constexpr int kSlotChunks = 256;   // token chunks of the slot sums
 
 template <int N>
@@ -65,14 +70,18 @@ struct Ws {
     return v_off() + al64((tokens + 31) / 32 * 32 * Dims<N>::kSlots);
   }
   __host__ __device__ int64_t pw_off() const { return st_off() + al64(tokens * 4); }
-  __host__ __device__ int64_t groups() const { return (tokens + kBlock - 1) / kBlock; }
+  // d gamma partials: one row per workgroup of the stream kernel (64 or 128
+  // tokens); sized for the smaller blocks
+  __host__ __device__ int64_t groups() const { return (tokens + kRowBlock - 1) / kRowBlock; }
   __host__ __device__ int64_t pg_off() const {
     return pw_off() + al64((int64_t)kParamChunks * Dims<N>::kMix * N * d);
   }
   __host__ __device__ int64_t e_off() const { return pg_off() + al64(groups() * d); }
-  __host__ __device__ int64_t floats() const {
+  __host__ __device__ int64_t wt_off() const {
     return e_off() + al64((int64_t)kSlotChunks * 2 * Dims<N>::kMix);
   }
+  // packed W^T of the row kernel: 48 floats per feature and stream
+  __host__ __device__ int64_t floats() const { return wt_off() + al64((int64_t)d * N * 48); }
 };
 
 // V[t][slot] in the workspace: blocks of 32 tokens, slot-major inside a block,
@@ -115,6 +124,7 @@ struct Args {
   float* d_gamma;
   float* ws;
   int64_t tokens;
+  int64_t dg_groups;   // d gamma partial rows written by the stream kernel
   int d;
   int iters;
   float norm_eps;
@@ -626,6 +636,412 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(Args a) {
   }
 }
 
+// ----- the stream kernel on whole 128-byte rows (bf16, d % 64 == 0) -------------------
+//
+// Same arithmetic as stream_kernel, another layout. A workgroup owns 64
+// tokens, each wave 8 of them; features go in units of 64 (128 bytes of every
+// row). Lane l holds token l / 8 of the wave and features 8 (l % 8) .. +7 of
+// the unit, so that one load or store instruction moves 8 whole 128-byte row
+// segments (16 rows x 64 bytes, the MFMA result order, moves about a quarter
+// less).
+//
+// W^T V runs on v_mfma_f32_16x16x32_bf16 with W^T as A (rows = 16 features of
+// one stream, K = the 32 slots; three exact bf16 terms w0, w1, w2, packed once
+// per call in operand order by wt_pack_kernel) and V as B: columns 0-7 are the
+// wave's tokens with V's terms (v0 | v2), columns 8-15 the same tokens with
+// (v1 | 0). The products (w0 w1 w2) x (v0 | v1) and w0 x (v2 | 0) hold every
+// term pair above 2^-24 of the product; the two column halves are added
+// (DPP), and a 2 KB per-wave LDS buffer turns the result (4 features of one
+// token per lane) into the lane layout above. Each unit's packed W^T and
+// gamma are staged in LDS (double-buffered) one unit ahead, with the next
+// unit's stream loads issued after the product phase, ahead of the current
+// unit's elementwise arithmetic; the one barrier per unit waits for LDS
+// traffic only, so loads and stores stay in flight across it. Register
+// budget (n = 4: 256 VGPRs, none spilled): the coefficients are re-read from
+// LDS each unit, and empty asm statements keep the compiler from widening all
+// packed inputs at once or sinking the token sums to the end of the unit.
+
+using pipe::bload;
+using pipe::bstore;
+using pipe::kNT;
+using pipe::make_rsrc;
+using pipe::rsrc_t;
+
+template <int N>
+struct RowDims {
+  static constexpr int kWtVecs = N * 4 * 3 * 64;       // u32x4 of one unit's W^T
+  static constexpr int kWtPer = kWtVecs / kThreads;    // staged per thread
+  static_assert(kWtPer * kThreads == kWtVecs, "whole staging rounds");
+};
+
+// Packed W^T: u32x4 index (((u N + k) 4 + q) 3 + term) 64 + lane holds, in bf16
+// element e, the term of W[8 (lane / 16) + e][k d + 64 u + 16 q + lane % 16]
+// (zero for slots >= (2+n)n).
+template <int N>
+__global__ __launch_bounds__(256) void wt_pack_kernel(const float* __restrict__ w, int d,
+                                                      int64_t total, u32x4* __restrict__ out) {
+  constexpr int kMix = Dims<N>::kMix;
+  const int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (v >= total) return;
+  const int lane = (int)(v & 63);
+  const int term = (int)((v >> 6) % 3);
+  const int64_t uq = (v >> 6) / 3;   // (u N + k) 4 + q
+  const int q = (int)(uq & 3);
+  const int64_t uk = uq >> 2;
+  const int k = (int)(uk % N);
+  const int64_t u = uk / N;
+  const int64_t col = (int64_t)k * d + 64 * u + 16 * q + (lane & 15);
+  uint32_t h[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int slot = 8 * (lane >> 4) + e;
+    uint32_t t3[3] = {0u, 0u, 0u};
+    if (slot < kMix) split3(w[(int64_t)slot * N * d + col], t3[0], t3[1], t3[2]);
+    h[e] = term == 0 ? t3[0] : (term == 1 ? t3[1] : t3[2]);
+  }
+  out[v] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                 h[6] | (h[7] << 16)};
+}
+
+// Barrier for LDS traffic only: waits for the wave's LDS operations, not for
+// its outstanding global loads and stores.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+template <int N>
+__global__ __launch_bounds__(kThreads) void row_kernel(Args a) {
+  using D = Dims<N>;
+  using R = RowDims<N>;
+  constexpr int kMix = D::kMix;
+  typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+  __shared__ __align__(16) u32x4 wt[2][R::kWtVecs];
+  __shared__ __align__(16) float gm[2][kUnit];
+  __shared__ __align__(16) float tr[kWaves][kRowTok][kUnit + 4];
+  __shared__ float red[2][kWaves][kUnit];
+  constexpr int kCoef = N * N + 2 * N;   // comb_in, post_in, pre_in of a token
+  __shared__ __align__(16) float cst[kWaves][kRowTok][kCoef];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int m8 = lane >> 3, x8 = lane & 7;     // stream layout: token, 16-byte chunk
+  const int col = lane & 15, rg = lane >> 4;   // MFMA layout: column, row group
+  const int d = a.d;
+  const int nu = d / kUnit;
+  const int64_t tw = (int64_t)blockIdx.x * kRowBlock + wave * kRowTok;
+  const int64_t t = tw + m8;
+  const bool valid = t < a.tokens;
+  const int64_t tc = valid ? t : 0;
+  Ws<N> wsl{a.tokens, d};
+  const u32x4* wpk = reinterpret_cast<const u32x4*>(a.ws + wsl.wt_off());
+
+  // buffer resources over the wave's rows (rows past the end read zeros,
+  // stores to them are dropped)
+  const int ntok = (int)max<int64_t>(0, min<int64_t>(kRowTok, a.tokens - tw));
+  const uint32_t rowx = (uint32_t)(N * d * 2), rowf = (uint32_t)(d * 2), d2 = (uint32_t)(d * 2);
+  const int64_t tws = ntok > 0 ? tw : 0;
+  const rsrc_t rx = make_rsrc(static_cast<const char*>(a.x) + tws * rowx, ntok * rowx);
+  const rsrc_t rdxo = make_rsrc(static_cast<const char*>(a.dxo) + tws * rowx, ntok * rowx);
+  const rsrc_t rf = make_rsrc(static_cast<const char*>(a.f) + tws * rowf, ntok * rowf);
+  const rsrc_t rdy = make_rsrc(static_cast<const char*>(a.dy) + tws * rowf, ntok * rowf);
+  const rsrc_t rdx = make_rsrc(static_cast<char*>(a.dx) + tws * rowx, ntok * rowx);
+  const rsrc_t rdf = make_rsrc(static_cast<char*>(a.df) + tws * rowf, ntok * rowf);
+  const uint32_t vx = (uint32_t)m8 * rowx + 16u * x8;
+  const uint32_t vf = (uint32_t)m8 * rowf + 16u * x8;
+
+  struct Raw {
+    u32x4 x[N], dxo[N], f, dy;
+  };
+  auto load_raw = [&](Raw& r, int u) {
+    const uint32_t cu = 128u * u;
+#pragma unroll
+    for (int k = 0; k < N; ++k) r.x[k] = bload<kNT>(rx, vx + k * d2, cu);
+#pragma unroll
+    for (int k = 0; k < N; ++k) r.dxo[k] = bload<kNT>(rdxo, vx + k * d2, cu);
+    r.f = bload<kNT>(rf, vf, cu);
+    r.dy = bload<kNT>(rdy, vf, cu);
+  };
+  u32x4 wst[R::kWtPer];
+  f32x4 gst = {0.f, 0.f, 0.f, 0.f};
+  auto stage_load_w = [&](int u) {
+#pragma unroll
+    for (int r = 0; r < R::kWtPer; ++r) wst[r] = wpk[(int64_t)u * R::kWtVecs + tid + r * kThreads];
+    if (tid < kUnit / 4) gst = *reinterpret_cast<const f32x4*>(a.gamma + kUnit * u + 4 * tid);
+  };
+  auto stage_store_w = [&](int b) {
+#pragma unroll
+    for (int r = 0; r < R::kWtPer; ++r) wt[b][tid + r * kThreads] = wst[r];
+    if (tid < kUnit / 4) *reinterpret_cast<f32x4*>(&gm[b][4 * tid]) = gst;
+  };
+
+  Raw ra, rb;
+  stage_load_w(0);
+  load_raw(ra, 0);
+
+  // the coefficients of the wave's tokens go to LDS (re-read per unit, so
+  // that they hold no registers through the product phase)
+  if (x8 == 0) {
+#pragma unroll
+    for (int i = 0; i < N * N; ++i) cst[wave][m8][i] = a.comb_in[tc * N * N + i];
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+      cst[wave][m8][N * N + k] = a.post_in[tc * N + k];
+      cst[wave][m8][N * N + N + k] = a.pre_in[tc * N + k];
+    }
+  }
+  float cr, kappa, rho;
+  {
+    const float* stt = a.ws + wsl.st_off() + tc * 4;
+    const float r = stt[0];
+    rho = stt[1];
+    const float ssum = stt[2];
+    const float* gr = a.ws + wsl.g_off() + tc * kMix;
+    const float* mr = a.mix + tc * kMix;
+    float dmm = 0.f;   // (scale * g) . m
+#pragma unroll
+    for (int i = 0; i < kMix; ++i) {
+      const float sc = i < N ? a.scale[0] : (i < 2 * N ? a.scale[1] : a.scale[2]);
+      dmm = fmaf(sc * gr[i], mr[i], dmm);
+    }
+    cr = dmm * r * r / (float)(N * d);   // dr r^3 / (n d), dr = dmm / r
+    kappa = rho * rho * rho * ssum / (float)d;
+  }
+  // B operands (MFMA layout): V[slot 8 rg + e] of token col % 8, as bf16 terms;
+  // the lanes of columns 0-7 also write V for the parameter kernel
+  bf16x8_t ba, bb;
+  {
+    const int64_t tv = tw + (col & 7);
+    const bool vvalid = tv < a.tokens;
+    const int64_t tvc = vvalid ? tv : 0;
+    const float rv = a.ws[wsl.st_off() + tvc * 4];
+    const float* gr = a.ws + wsl.g_off() + tvc * kMix;
+    u32x4 wa, wb;
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      uint32_t tt[2][3];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int i = 8 * rg + 2 * e2 + u;
+        const float sc = i < N ? a.scale[0] : (i < 2 * N ? a.scale[1] : a.scale[2]);
+        const float vi = i < kMix ? rv * sc * gr[i < kMix ? i : 0] : 0.f;
+        split3(vi, tt[u][0], tt[u][1], tt[u][2]);
+        if (vvalid && col < 8) a.ws[wsl.v_off() + vidx<N>(tv, i)] = vi;
+      }
+      const uint32_t v0 = tt[0][0] | (tt[1][0] << 16), v1 = tt[0][1] | (tt[1][1] << 16);
+      const uint32_t v2 = tt[0][2] | (tt[1][2] << 16);
+      wa[e2] = col < 8 ? v0 : v1;
+      wb[e2] = col < 8 ? v2 : 0u;
+    }
+    ba = __builtin_bit_cast(bf16x8_t, wa);
+    bb = __builtin_bit_cast(bf16x8_t, wb);
+  }
+
+  stage_store_w(0);
+  lds_barrier();
+
+  float dC[N][N], du[N], dp[N];
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    du[k] = dp[k] = 0.f;
+#pragma unroll
+    for (int j = 0; j < N; ++j) dC[j][k] = 0.f;
+  }
+
+  Raw& cur = ra;
+  Raw& nxt = rb;
+  for (int u = 0; u < nu; ++u) {
+    const int b = u & 1;
+    const bool more = u + 1 < nu;
+    // the next unit's W^T and gamma, then its stream rows (vector memory
+    // retires in order: the staging loads complete first)
+    __builtin_amdgcn_sched_barrier(0);
+    if (more) stage_load_w(u + 1);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // W^T V of the unit, one stream at a time, through the wave's LDS buffer
+    float dxm[N][8];
+    const u32x4* wb = wt[b];
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int base = ((k * 4 + q) * 3) * 64 + lane;
+        const bf16x8_t w0 = __builtin_bit_cast(bf16x8_t, wb[base]);
+        const bf16x8_t w1 = __builtin_bit_cast(bf16x8_t, wb[base + 64]);
+        const bf16x8_t w2 = __builtin_bit_cast(bf16x8_t, wb[base + 128]);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w2, ba, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w0, bb, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w1, ba, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w0, ba, acc, 0, 0, 0);
+        f32x4 tot;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tot[i] = acc[i] + pipe::dpp<pipe::kRowRor8>(acc[i]);
+        if (col < 8) *reinterpret_cast<f32x4*>(&tr[wave][col][16 * q + 4 * rg]) = tot;
+        __builtin_amdgcn_sched_barrier(0);   // one tile's operands in flight at a time
+      }
+      __builtin_amdgcn_wave_barrier();
+      const f32x4 lo = *reinterpret_cast<const f32x4*>(&tr[wave][m8][8 * x8]);
+      const f32x4 hi = *reinterpret_cast<const f32x4*>(&tr[wave][m8][8 * x8 + 4]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        dxm[k][i] = lo[i];
+        dxm[k][4 + i] = hi[i];
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+
+    // the next unit's W^T and gamma into the other buffers (last read in the
+    // previous unit, before the barrier that ended it), then the next unit's
+    // stream rows, in flight through this unit's arithmetic
+    if (more) stage_store_w(b ^ 1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (more) load_raw(nxt, u + 1);
+
+    __builtin_amdgcn_sched_barrier(0);
+    const f32x4 g0 = *reinterpret_cast<const f32x4*>(&gm[b][8 * x8]);
+    const f32x4 g1 = *reinterpret_cast<const f32x4*>(&gm[b][8 * x8 + 4]);
+    const float gv[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
+    float C[N][N], U[N], P[N];
+    {
+      int ci = m8;
+      asm volatile("" : "+v"(ci));   // re-read every unit
+      const float* cp = cst[wave][ci];
+#pragma unroll
+      for (int j = 0; j < N; ++j)
+#pragma unroll
+        for (int k = 0; k < N; ++k) C[j][k] = cp[j * N + k];
+#pragma unroll
+      for (int k = 0; k < N; ++k) {
+        U[k] = cp[N * N + k];
+        P[k] = cp[N * N + N + k];
+      }
+    }
+
+    // dA (in place of W^T V), the token sums and the d gamma sums, two
+    // features at a time (the empty asm keeps the packed words from being
+    // widened to floats all at once ahead of their use)
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      uint32_t wx[N], wd[N], wf = cur.f[e2], wy = cur.dy[e2];
+#pragma unroll
+      for (int j = 0; j < N; ++j) {
+        wx[j] = cur.x[j][e2];
+        wd[j] = cur.dxo[j][e2];
+        asm volatile("" : "+v"(wx[j]), "+v"(wd[j]));
+      }
+      asm volatile("" : "+v"(wf), "+v"(wy));
+#pragma unroll
+      for (int hi = 0; hi < 2; ++hi) {
+        const int e = 2 * e2 + hi;
+        float xv[N];
+#pragma unroll
+        for (int j = 0; j < N; ++j) xv[j] = hi ? bf_hi(wx[j]) : bf_lo(wx[j]);
+        const float fv = hi ? bf_hi(wf) : bf_lo(wf);
+        const float dyv = hi ? bf_hi(wy) : bf_lo(wy);
+        // recompute X' and h exactly as the forward did
+        float xp[N];
+#pragma unroll
+        for (int k = 0; k < N; ++k) {
+          float v = xv[0] * C[0][k];
+#pragma unroll
+          for (int j = 1; j < N; ++j) v = fmaf(xv[j], C[j][k], v);
+          xp[k] = __uint_as_float(pack_bf16x2(fmaf(fv, U[k], v), 0.f) << 16);
+        }
+        float hv = P[0] * xp[0];
+#pragma unroll
+        for (int k = 1; k < N; ++k) hv = fmaf(P[k], xp[k], hv);
+        hv = __uint_as_float(pack_bf16x2(hv, 0.f) << 16);
+        // d gamma: sum over the wave's 8 tokens (lanes l ^ 8, ^ 16, ^ 32)
+        float dg = valid ? dyv * hv * rho : 0.f;
+        dg += pipe::dpp<pipe::kRowRor8>(dg);
+        dg += __shfl_xor(dg, 16);
+        dg += __shfl_xor(dg, 32);
+        if (m8 == 0) red[b][wave][8 * x8 + e] = dg;
+        const float dh = rho * (gv[e] * dyv) - kappa * hv;
+#pragma unroll
+        for (int k = 0; k < N; ++k) {
+          const float dxo = hi ? bf_hi(wd[k]) : bf_lo(wd[k]);
+          const float da = dxo + (dxm[k][e] - cr * xp[k]) + P[k] * dh;
+          dxm[k][e] = da;
+          dp[k] = fmaf(dh, xp[k], dp[k]);
+          du[k] = fmaf(fv, da, du[k]);
+#pragma unroll
+          for (int j = 0; j < N; ++j) dC[j][k] = fmaf(xv[j], da, dC[j][k]);
+        }
+      }
+      // the token sums are updated here, not sunk to the end of the unit
+#pragma unroll
+      for (int k = 0; k < N; ++k) {
+        asm volatile("" : "+v"(dp[k]), "+v"(du[k]));
+#pragma unroll
+        for (int j = 0; j < N; ++j) asm volatile("" : "+v"(dC[j][k]));
+      }
+      __builtin_amdgcn_sched_barrier(0);   // one pair's temporaries at a time
+    }
+    // dX_j = sum_k C[j][k] dA_k, dF = sum_k u_k dA_k, one row segment at a time
+    {
+      const uint32_t cu = 128u * u;
+#pragma unroll
+      for (int j = 0; j <= N; ++j) {
+        float o[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float* cj = j < N ? C[j] : U;
+          float v = cj[0] * dxm[0][e];
+#pragma unroll
+          for (int k = 1; k < N; ++k) v = fmaf(cj[k], dxm[k][e], v);
+          o[e] = v;
+        }
+        const u32x4 ov = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
+                          pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7])};
+        if (j < N)
+          bstore<0>(rdx, vx + j * d2, cu, ov);
+        else
+          bstore<0>(rdf, vf, cu, ov);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+
+    lds_barrier();
+    // the workgroup's d gamma partial of the unit's features (red[b] is
+    // rewritten two units later, after the next barrier)
+    if (wave == 0) {
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) v += red[b][w][lane];
+      a.ws[wsl.pg_off() + (int64_t)blockIdx.x * d + kUnit * u + lane] = v;
+    }
+    cur = nxt;
+  }
+
+  // per-token sums over the 8 lanes of a token
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    dp[k] = pipe::quad_sum(dp[k]);
+    dp[k] += __shfl_xor(dp[k], 4);
+    du[k] = pipe::quad_sum(du[k]);
+    du[k] += __shfl_xor(du[k], 4);
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      dC[j][k] = pipe::quad_sum(dC[j][k]);
+      dC[j][k] += __shfl_xor(dC[j][k], 4);
+    }
+  }
+  if (valid && x8 == 0) {
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+      a.d_pre_in[t * N + k] = dp[k];
+      a.d_post_in[t * N + k] = du[k];
+#pragma unroll
+      for (int j = 0; j < N; ++j) a.d_comb_in[(t * N + j) * N + k] = dC[j][k];
+    }
+  }
+}
+
 // ----- parameter gradients: features across threads, tokens in chunks ----------------
 
 // Thread (feature f, stream k, chunk c) accumulates
@@ -849,7 +1265,7 @@ __global__ __launch_bounds__(256) void gamma_reduce_kernel(Args a) {
   const int lane = threadIdx.x & 63, slice = threadIdx.x >> 6;
   const int64_t f = (int64_t)blockIdx.x * 64 + lane;
   Ws<N> wsl{a.tokens, d};
-  const int64_t groups = wsl.groups();
+  const int64_t groups = a.dg_groups;
   const float* pg = a.ws + wsl.pg_off();
   float s = 0.f;
   if (f < d) {

@@ -1536,7 +1536,13 @@ int64_t bwd_workspace_floats(int32_t n, int64_t tokens, int32_t d) {
 #endif
 
 template <int N, int DT>
-mhc_status run_backward(const bwd::Args& a, hipStream_t st) {
+mhc_status run_backward(const bwd::Args& args, hipStream_t st) {
+  // bf16 streams with d % 64 == 0 take the row kernel (64-token workgroups),
+  // the rest the MFMA-layout stream kernel (128-token workgroups)
+  const bool rows = DT == MHC_BF16 && args.d % bwd::kUnit == 0;
+  bwd::Args a = args;
+  const int64_t block = rows ? bwd::kRowBlock : bwd::kBlock;
+  a.dg_groups = (a.tokens + block - 1) / block;
   const unsigned tok256 = (unsigned)((a.tokens + 255) / 256);
   hipLaunchKernelGGL((bwd::split_kernel<N>), dim3(tok256), dim3(256), 0, st, a);
   mhc_status s = launch_status("backward split/Sinkhorn kernel launch");
@@ -1544,9 +1550,18 @@ mhc_status run_backward(const bwd::Args& a, hipStream_t st) {
   hipLaunchKernelGGL((bwd::stats_kernel<N, DT>), dim3((unsigned)((a.tokens + 3) / 4)), dim3(256),
                      0, st, a);
   if ((s = launch_status("backward statistics kernel launch")) != MHC_OK) return s;
-  hipLaunchKernelGGL((bwd::stream_kernel<N, DT>),
-                     dim3((unsigned)((a.tokens + bwd::kBlock - 1) / bwd::kBlock)),
-                     dim3(bwd::kThreads), 0, st, a);
+  if (rows) {
+    const bwd::Ws<N> wsl{a.tokens, a.d};
+    const int64_t vecs = (int64_t)(a.d / bwd::kUnit) * bwd::RowDims<N>::kWtVecs;
+    hipLaunchKernelGGL((bwd::wt_pack_kernel<N>), dim3((unsigned)((vecs + 255) / 256)), dim3(256),
+                       0, st, a.w, a.d, vecs, reinterpret_cast<u32x4*>(a.ws + wsl.wt_off()));
+    if ((s = launch_status("backward W^T packing kernel launch")) != MHC_OK) return s;
+    hipLaunchKernelGGL((bwd::row_kernel<N>), dim3((unsigned)a.dg_groups), dim3(bwd::kThreads), 0,
+                       st, a);
+  } else {
+    hipLaunchKernelGGL((bwd::stream_kernel<N, DT>), dim3((unsigned)a.dg_groups),
+                       dim3(bwd::kThreads), 0, st, a);
+  }
   if ((s = launch_status("backward stream kernel launch")) != MHC_OK) return s;
   if (DT == MHC_BF16 && MHC_BWD_MFMA_DW && a.d % 64 == 0)
     hipLaunchKernelGGL((bwd::param_mfma_kernel<N>),
@@ -1987,7 +2002,7 @@ mhc_status mhc_fused_step_backward_n(
   if (s != MHC_OK) return s;
   bwd::Args a{x, f, pre_in, post_in, comb_in, x_out, mix, w_mix, base, scale, gamma, d_x_out,
               d_y, d_pre, d_post, d_comb, d_x, d_f, d_pre_in, d_post_in, d_comb_in, d_w_mix,
-              d_base, d_scale, d_gamma, static_cast<float*>(workspace), tokens, d,
+              d_base, d_scale, d_gamma, static_cast<float*>(workspace), tokens, 0, d,
               sinkhorn_iters, norm_eps, hc_eps};
   const hipStream_t st = static_cast<hipStream_t>(stream);
   if (n == 2)

@@ -125,6 +125,7 @@ CASES = [
     (4, "f32", 128, 40, 20),
     (2, "f32", 64, 17, 1),
     (4, "bf16", 2080, 70, 3),
+    (4, "bf16", 64, 65, 20),      # one 64-feature unit; a second workgroup with one token
 ]
 
 
