@@ -1,4 +1,5 @@
-"""Build libmhc.so in-tree for gfx950 with hipcc.
+"""Build libmhc.so (and libmhc_probe.so, the copy kernels bench.py uses for
+the memory system's practical ceilings) in-tree for gfx950 with hipcc.
 
 ``python -m stream_hyper_connections_amd.build`` or ``build()`` from Python.
 The flags disable packed-fp32 instruction selection on the device side.
@@ -15,6 +16,8 @@ ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "mhc.hip")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmhc.so")
+PROBE_SRC = os.path.join(PKG, "csrc", "copy_probe.hip")
+PROBE_LIB = os.path.join(PKG, "libmhc_probe.so")
 ARCH = "gfx950"
 
 
@@ -24,20 +27,25 @@ def hipcc() -> str:
     return cand if os.path.exists(cand) else "hipcc"
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
+def _compile(src: str, lib: str, verbose: bool) -> None:
+    tmp = lib + ".tmp"
     cmd = [
         hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        "-I", INCLUDE, SRC, "-o", tmp,
+        "-I", INCLUDE, src, "-o", tmp,
     ]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed ({res.returncode}) building {LIB}")
-    os.replace(tmp, LIB)
+        raise RuntimeError(f"hipcc failed ({res.returncode}) building {lib}")
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    _compile(SRC, LIB, verbose)
+    _compile(PROBE_SRC, PROBE_LIB, verbose)
     return LIB
 
 

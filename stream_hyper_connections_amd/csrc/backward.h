@@ -642,8 +642,8 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(Args a) {
 // tokens, each wave 8 of them; features go in units of 64 (128 bytes of every
 // row). Lane l holds token l / 8 of the wave and features 8 (l % 8) .. +7 of
 // the unit, so that one load or store instruction moves 8 whole 128-byte row
-// segments (16 rows x 64 bytes, the MFMA result order, moves about a quarter
-// less).
+// segments (as a plain copy on the MI355X: 5.0 TB/s, against 2.8 TB/s for 16
+// rows x 64 bytes, the MFMA result order).
 //
 // W^T V runs on v_mfma_f32_16x16x32_bf16 with W^T as A (rows = 16 features of
 // one stream, K = the 32 slots; three exact bf16 terms w0, w1, w2, packed once
