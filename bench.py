@@ -104,8 +104,9 @@ N_SWEEP = (2, 4, 8)
 
 def general_n_bench(w0, steps, warmup):
     """mhc_fused_step_n at the workload's shape for n = 2, 4, 8: one JSON line
-    each (HIP events around the call, which runs the block kernel and the
-    split/Sinkhorn kernel)."""
+    per n and kernel (HIP events around the call): the token-block kernel
+    ("block") for every n, and the feature-split kernel ("split", with its
+    workspace) where it applies; each followed by the split/Sinkhorn kernel."""
     import dataclasses
     import torch
     import stream_hyper_connections_amd as mhc
@@ -128,34 +129,41 @@ def general_n_bench(w0, steps, warmup):
                     comb_out=torch.empty_like(prior["comb"]),
                     mix_out=torch.empty_like(prior["mix"]))
 
-        def call():
-            mhc.fused_step_n(x, f, prior["pre"], prior["post"], prior["comb"], wp, cur["base"],
-                             cur["scale"], cur["gamma"], w.iters, w.norm_eps, w.hc_eps, **outs)
+        paths = ["block"]
+        if mhc.fused_step_n_workspace_bytes(n, w.tokens, w.d, w.dtype) > 0:
+            paths.append("split")
+        kernels = {"block": "gen::block_kernel + gen::sinkhorn_kernel",
+                   "split": "fsn::split_kernel + gen::sinkhorn_kernel (feature-split)"}
+        for path in paths:
+            def call():
+                mhc.fused_step_n(x, f, prior["pre"], prior["post"], prior["comb"], wp,
+                                 cur["base"], cur["scale"], cur["gamma"], w.iters, w.norm_eps,
+                                 w.hc_eps, path=path, **outs)
 
-        for _ in range(warmup):
-            call()
-        torch.cuda.synchronize()
-        a = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-        b = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-        for i in range(steps):
-            a[i].record()
-            call()
-            b[i].record()
-        torch.cuda.synchronize()
-        ms = np.array([x0.elapsed_time(x1) for x0, x1 in zip(a, b)])
-        alg = algorithmic_bytes_n(w.tokens, w.d, elem, n)
-        achieved = alg / (ms.mean() / 1e3) / 1e9
-        print(json.dumps({
-            "metric": f"tokens/s of the general-n fused step, n={n} d={w.d}",
-            "value": round(w.tokens / (ms.mean() / 1e3), 1), "unit": "tokens/s",
-            "n_streams": n, "tokens": w.tokens, "d": w.d, "dtype": w.dtype,
-            "call_ms_avg": round(float(ms.mean()), 5),
-            "call_ms_p50": round(float(np.percentile(ms, 50)), 5),
-            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                         "traffic": None, "algorithmic_bytes_per_launch": alg,
-                         "kernel": "gen::block_kernel + gen::sinkhorn_kernel"},
-            "config": {"workload": w.name, "sinkhorn_iters": w.iters}}), flush=True)
+            for _ in range(warmup):
+                call()
+            torch.cuda.synchronize()
+            a = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+            b = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+            for i in range(steps):
+                a[i].record()
+                call()
+                b[i].record()
+            torch.cuda.synchronize()
+            ms = np.array([x0.elapsed_time(x1) for x0, x1 in zip(a, b)])
+            alg = algorithmic_bytes_n(w.tokens, w.d, elem, n)
+            achieved = alg / (ms.mean() / 1e3) / 1e9
+            print(json.dumps({
+                "metric": f"tokens/s of the general-n fused step, n={n} d={w.d}",
+                "value": round(w.tokens / (ms.mean() / 1e3), 1), "unit": "tokens/s",
+                "n_streams": n, "path": path, "tokens": w.tokens, "d": w.d, "dtype": w.dtype,
+                "call_ms_avg": round(float(ms.mean()), 5),
+                "call_ms_p50": round(float(np.percentile(ms, 50)), 5),
+                "roofline": {"bound": "hbm", "achieved": round(achieved, 1),
+                             "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                             "algorithmic_bytes_per_launch": alg, "kernel": kernels[path]},
+                "config": {"workload": w.name, "sinkhorn_iters": w.iters}}), flush=True)
         del x, f, prior, outs
         torch.cuda.empty_cache()
 

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define MHC_ABI_VERSION 5
+#define MHC_ABI_VERSION 6
 #define MHC_N_STREAMS 4
 #define MHC_N_MIX 24
 
@@ -226,12 +226,30 @@ mhc_status mhc_pack_wmix_n(int32_t n, const float* w_mix, int32_t d, int32_t dty
                            void* w_packed, int64_t packed_bytes, mhc_stream_t stream);
 
 /*
+ * Workspace bytes of the feature-split kernel of mhc_fused_step_n and
+ * mhc_mixes_n for (n, tokens, d, dtype) on the current device; 0 when that
+ * kernel does not apply (it covers n in {2, 4} with bf16 streams, d = ns * S
+ * with S a multiple of 64 of at most 256 (n = 2) or 128 (n = 4) features and
+ * 16 <= ns <= 64 slices, at most one per compute unit, on a device with
+ * cooperative launch); -1 for a bad argument.
+ */
+int64_t mhc_fused_step_n_workspace_bytes(int32_t n, int64_t tokens, int32_t d, int32_t dtype);
+
+/*
  * mhc_fused_step_n -- mhc_fused_step for n streams: the same six formulas with
- * sums over n streams and the RMS statistic over n*d values. Runs two kernels:
- * one pass over the streams (hc_post, RMS statistic, projection, hc_pre,
- * RMSNorm) that writes the mixes to mix_out, then the split/Sinkhorn of
+ * sums over n streams and the RMS statistic over n*d values. Two kernels: one
+ * pass over the streams (hc_post, RMS statistic, projection, hc_pre, RMSNorm)
+ * that writes the mixes to mix_out, then the split/Sinkhorn of
  * mhc_sinkhorn_n reading them back. mix_out [T][(2+n)n] is therefore
- * REQUIRED (NULL is MHC_ERR_INVALID_ARG). No workspace.
+ * REQUIRED (NULL is MHC_ERR_INVALID_ARG).
+ * Workspace (optional): NULL / 0 bytes, or device memory of at least
+ * mhc_fused_step_n_workspace_bytes() bytes, 256-byte aligned, overlapping no
+ * other argument. When it is given and that size is > 0, the pass over the
+ * streams is the feature-split kernel (as for mhc_fused_step: each compute
+ * unit keeps a slice of the features and of W; cooperative launch, one
+ * workgroup per compute unit; a smaller workspace is MHC_ERR_INVALID_ARG;
+ * the same status word at offset 0 and ordering rules). Otherwise, or with
+ * no workspace, the token-block kernel runs.
  */
 mhc_status mhc_fused_step_n(int32_t n, const void* x, const void* f, int32_t dtype,
                             int64_t tokens, int32_t d, const float* pre_in,
@@ -239,13 +257,16 @@ mhc_status mhc_fused_step_n(int32_t n, const void* x, const void* f, int32_t dty
                             const float* base, const float* scale, const float* gamma,
                             int32_t sinkhorn_iters, float norm_eps, float hc_eps, void* x_out,
                             void* y_out, float* pre_out, float* post_out, float* comb_out,
-                            float* mix_out, mhc_stream_t stream);
+                            float* mix_out, void* workspace, int64_t workspace_bytes,
+                            mhc_stream_t stream);
 
-/* mhc_mixes_n -- mhc_mixes for n streams; mix_out is required (as above). */
+/* mhc_mixes_n -- mhc_mixes for n streams; mix_out is required and the
+ * workspace optional (as above; same size). */
 mhc_status mhc_mixes_n(int32_t n, const void* x, int32_t dtype, int64_t tokens, int32_t d,
                        const void* w_packed, const float* base, const float* scale,
                        int32_t sinkhorn_iters, float norm_eps, float hc_eps, float* pre_out,
-                       float* post_out, float* comb_out, float* mix_out, mhc_stream_t stream);
+                       float* post_out, float* comb_out, float* mix_out, void* workspace,
+                       int64_t workspace_bytes, mhc_stream_t stream);
 
 /*
  * mhc_sinkhorn_n -- mhc_sinkhorn4 for n streams: mixes [T][(2+n)n] to pre,

@@ -1110,6 +1110,7 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_kernel(StepArgs a, int nt
 #include "split_kernel.h"
 #include "unfused.h"
 #include "general_n.h"
+#include "split_n.h"
 #include "backward.h"
 
 // ----- packing of the projection --------------------------------------------------------
@@ -1323,6 +1324,25 @@ struct SplitCfg {
   int S = 0;
 };
 
+// Cooperative-launch support of the current device, cached per device
+// ordinal (1 = no, 2 = yes).
+mhc_status coop_supported(bool* ok) {
+  static int coop_cache[64];
+  int dev = 0, coop = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess && dev >= 0 && dev < 64 && coop_cache[dev] != 0) {
+    coop = coop_cache[dev] - 1;
+  } else {
+    if (e == hipSuccess)
+      e = hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev);
+    if (e != hipSuccess)
+      return fail(MHC_ERR_HIP, "cooperative-launch attribute: %s", hipGetErrorString(e));
+    if (dev >= 0 && dev < 64) coop_cache[dev] = coop ? 2 : 1;
+  }
+  *ok = coop != 0;
+  return MHC_OK;
+}
+
 mhc_status split_config(int32_t dtype, int32_t d, SplitCfg* cfg) {
   *cfg = SplitCfg{};
   if (dtype != MHC_BF16) return MHC_OK;
@@ -1343,19 +1363,8 @@ mhc_status split_config(int32_t dtype, int32_t d, SplitCfg* cfg) {
     }
   }
   if (cfg->groups == 0) return MHC_OK;
-  // cooperative-launch support, cached per device ordinal (1 = no, 2 = yes)
-  static int coop_cache[64];
-  int dev = 0, coop = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess && dev >= 0 && dev < 64 && coop_cache[dev] != 0) {
-    coop = coop_cache[dev] - 1;
-  } else {
-    if (e == hipSuccess)
-      e = hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev);
-    if (e != hipSuccess)
-      return fail(MHC_ERR_HIP, "cooperative-launch attribute: %s", hipGetErrorString(e));
-    if (dev >= 0 && dev < 64) coop_cache[dev] = coop ? 2 : 1;
-  }
+  bool coop = false;
+  if ((s = coop_supported(&coop)) != MHC_OK) return s;
   if (!coop) *cfg = SplitCfg{};
   return MHC_OK;
 }
@@ -1520,6 +1529,117 @@ mhc_status run_n(int32_t n, const StepArgs& a, int32_t dtype, int mode, hipStrea
                                   a.pre_out, a.post_out, a.comb_out, st); break;
   }
   return launch_status("general-n split/Sinkhorn kernel launch");
+}
+
+// ----- the feature-split kernel of the n-family (n in {2, 4}, bf16) ---------------------
+
+struct SplitCfgN {
+  int groups = 0;
+  int ns = 0;
+  int nr = 0;   // slice = 64 * nr features
+};
+
+// The slice shape for (n, d) on this device: S = 64 * nr features per slice,
+// ns = d / S slices (16 <= ns <= 64 and at most one per CU); the most CUs in
+// use wins, then the widest slice. groups == 0: the kernel does not apply.
+mhc_status split_config_n(int32_t n, int32_t dtype, int32_t d, SplitCfgN* cfg) {
+  *cfg = SplitCfgN{};
+  if (dtype != MHC_BF16 || (n != 2 && n != 4) || d <= 0) return MHC_OK;
+  int cus = 0;
+  mhc_status s = device_cu_count(&cus);
+  if (s != MHC_OK) return s;
+  const int maxr = n == 2 ? fsn::max_rounds<2>() : fsn::max_rounds<4>();
+  int best = -1;
+  for (int nr = maxr; nr >= 1; --nr) {
+    const int S = 64 * nr;
+    if (d % S != 0) continue;
+    const int ns = d / S;
+    if (ns < 16 || ns > fsplit::kMaxSlices || ns > cus) continue;
+    const int score = (cus / ns) * ns * 8 + nr;
+    if (score > best) {
+      best = score;
+      *cfg = SplitCfgN{cus / ns, ns, nr};
+    }
+  }
+  if (cfg->groups == 0) return MHC_OK;
+  bool coop = false;
+  if ((s = coop_supported(&coop)) != MHC_OK) return s;
+  if (!coop) *cfg = SplitCfgN{};
+  return MHC_OK;
+}
+
+int64_t split_n_workspace_bytes(int32_t n, const SplitCfgN& c, int64_t tokens) {
+  if (c.groups == 0) return 0;
+  return n == 2 ? fsn::workspace_bytes<2>(c.groups, c.ns, tokens)
+                : fsn::workspace_bytes<4>(c.groups, c.ns, tokens);
+}
+
+// clear the workspace counters, the cooperative split kernel, then the
+// split/Sinkhorn of the mixes rows it wrote
+template <int N>
+mhc_status launch_split_n(const StepArgs& a, void* ws, const SplitCfgN& cfg, int mode,
+                          hipStream_t stream) {
+  const int words = (int)(fsn::mp_off<N>(cfg.groups) / 4);
+  hipLaunchKernelGGL(fsplit::clear_kernel, dim3(1), dim3(256), 0, stream,
+                     static_cast<uint32_t*>(ws), words);
+  mhc_status s = launch_status("workspace clear kernel launch");
+  if (s != MHC_OK) return s;
+  float* mix = a.mix_out != nullptr
+                   ? a.mix_out
+                   : reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                              fsn::mix_off<N>(cfg.groups, cfg.ns));
+  fsn::Args fs{static_cast<char*>(ws), mix, cfg.groups, cfg.ns,
+               (int)((a.tokens + fsplit::kBatch - 1) / fsplit::kBatch)};
+  StepArgs args = a;
+  void* params[] = {&args, &fs};
+  const bool full = mode == kFused;
+  const void* fn = nullptr;
+  switch (cfg.nr) {
+    case 1:
+      fn = full ? reinterpret_cast<const void*>(fsn::split_kernel<N, 1, kFused>)
+                : reinterpret_cast<const void*>(fsn::split_kernel<N, 1, kMixesOnly>);
+      break;
+    case 2:
+      fn = full ? reinterpret_cast<const void*>(fsn::split_kernel<N, 2, kFused>)
+                : reinterpret_cast<const void*>(fsn::split_kernel<N, 2, kMixesOnly>);
+      break;
+    case 4:
+      if constexpr (fsn::max_rounds<N>() >= 4)
+        fn = full ? reinterpret_cast<const void*>(fsn::split_kernel<N, 4, kFused>)
+                  : reinterpret_cast<const void*>(fsn::split_kernel<N, 4, kMixesOnly>);
+      break;
+    default: break;
+  }
+  if (fn == nullptr)
+    return fail(MHC_ERR_UNSUPPORTED, "feature-split kernel: n = %d, %d rounds", N, cfg.nr);
+  const hipError_t e = hipLaunchCooperativeKernel(fn, dim3((unsigned)(cfg.groups * cfg.ns)),
+                                                  dim3(fsplit::kThreads), params, 0, stream);
+  if (e != hipSuccess)
+    return fail(MHC_ERR_HIP, "feature-split kernel cooperative launch: %s", hipGetErrorString(e));
+  if ((s = launch_status("feature-split kernel launch")) != MHC_OK) return s;
+  launch_sinkhorn_n<N>(mix, a.tokens, a.base, a.scale, a.iters, a.hc_eps, a.pre_out, a.post_out,
+                       a.comb_out, stream);
+  return launch_status("general-n split/Sinkhorn kernel launch");
+}
+
+// Workspace argument of the n-family: (NULL or 0 bytes: the block kernel);
+// otherwise the feature-split kernel when it applies, after the checks of
+// mhc_fused_step.
+mhc_status pick_split_n(int32_t n, int32_t dtype, int64_t tokens, int32_t d, void* workspace,
+                        int64_t workspace_bytes, SplitCfgN* cfg, int64_t* need) {
+  *cfg = SplitCfgN{};
+  *need = 0;
+  if (workspace == nullptr || workspace_bytes <= 0) return MHC_OK;
+  mhc_status s = split_config_n(n, dtype, d, cfg);
+  if (s != MHC_OK) return s;
+  if (cfg->groups == 0) return MHC_OK;   // not applicable: the block kernel
+  *need = split_n_workspace_bytes(n, *cfg, tokens);
+  if (workspace_bytes < *need)
+    return fail(MHC_ERR_INVALID_ARG, "workspace holds %lld bytes, %lld needed",
+                (long long)workspace_bytes, (long long)*need);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(MHC_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+  return MHC_OK;
 }
 
 // ----- backward ------------------------------------------------------------------------
@@ -1864,17 +1984,33 @@ mhc_status mhc_pack_wmix_n(int32_t n, const float* w_mix, int32_t d, int32_t dty
   return launch_status("general-n pack kernel launch");
 }
 
+int64_t mhc_fused_step_n_workspace_bytes(int32_t n, int64_t tokens, int32_t d, int32_t dtype) {
+  if (!n_supported(n) || tokens < 0 || d <= 0 || d % kStep != 0 || elem_size(dtype) == 0) {
+    fail(MHC_ERR_INVALID_ARG, "bad n (%d), tokens (%lld), d (%d) or dtype (%d)", n,
+         (long long)tokens, d, dtype);
+    return -1;
+  }
+  SplitCfgN cfg;
+  if (split_config_n(n, dtype, d, &cfg) != MHC_OK) return -1;
+  return split_n_workspace_bytes(n, cfg, tokens);
+}
+
 mhc_status mhc_fused_step_n(int32_t n, const void* x, const void* f, int32_t dtype,
                             int64_t tokens, int32_t d, const float* pre_in,
                             const float* post_in, const float* comb_in, const void* w_packed,
                             const float* base, const float* scale, const float* gamma,
                             int32_t sinkhorn_iters, float norm_eps, float hc_eps, void* x_out,
                             void* y_out, float* pre_out, float* post_out, float* comb_out,
-                            float* mix_out, mhc_stream_t stream) {
+                            float* mix_out, void* workspace, int64_t workspace_bytes,
+                            mhc_stream_t stream) {
   if (!n_supported(n)) return fail(MHC_ERR_UNSUPPORTED, "n = %d streams (2, 4 or 8 supported)", n);
   mhc_status s = check_common(dtype, tokens, d, sinkhorn_iters, norm_eps, hc_eps);
   if (s != MHC_OK) return s;
   if (tokens == 0) return ok();
+  SplitCfgN cfg;
+  int64_t need = 0;
+  if ((s = pick_split_n(n, dtype, tokens, d, workspace, workspace_bytes, &cfg, &need)) != MHC_OK)
+    return s;
   const uint64_t es = elem_size(dtype), T = (uint64_t)tokens, nn = (uint64_t)n, nm = n_mix(n);
   const Span in[] = {
       {"x", x, T * nn * d * es},           {"f", f, T * d * es},
@@ -1888,22 +2024,32 @@ mhc_status mhc_fused_step_n(int32_t n, const void* x, const void* f, int32_t dty
       {"x_out", x_out, T * nn * d * es},   {"y_out", y_out, T * d * es},
       {"pre_out", pre_out, T * nn * 4},    {"post_out", post_out, T * nn * 4},
       {"comb_out", comb_out, T * nn * nn * 4}, {"mix_out", mix_out, T * nm * 4},
+      {"workspace", workspace, (uint64_t)need},
   };
-  s = check_spans(in, 9, out, 6, x_out, x);
+  s = check_spans(in, 9, out, cfg.groups > 0 ? 7 : 6, x_out, x);
   if (s != MHC_OK) return s;
   StepArgs a{x, f, pre_in, post_in, comb_in, w_packed, base, scale, gamma, x_out, y_out,
              pre_out, post_out, comb_out, mix_out, tokens, d, sinkhorn_iters, norm_eps, hc_eps};
-  return run_n(n, a, dtype, kFused, static_cast<hipStream_t>(stream));
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (cfg.groups > 0)
+    return n == 2 ? launch_split_n<2>(a, workspace, cfg, kFused, st)
+                  : launch_split_n<4>(a, workspace, cfg, kFused, st);
+  return run_n(n, a, dtype, kFused, st);
 }
 
 mhc_status mhc_mixes_n(int32_t n, const void* x, int32_t dtype, int64_t tokens, int32_t d,
                        const void* w_packed, const float* base, const float* scale,
                        int32_t sinkhorn_iters, float norm_eps, float hc_eps, float* pre_out,
-                       float* post_out, float* comb_out, float* mix_out, mhc_stream_t stream) {
+                       float* post_out, float* comb_out, float* mix_out, void* workspace,
+                       int64_t workspace_bytes, mhc_stream_t stream) {
   if (!n_supported(n)) return fail(MHC_ERR_UNSUPPORTED, "n = %d streams (2, 4 or 8 supported)", n);
   mhc_status s = check_common(dtype, tokens, d, sinkhorn_iters, norm_eps, hc_eps);
   if (s != MHC_OK) return s;
   if (tokens == 0) return ok();
+  SplitCfgN cfg;
+  int64_t need = 0;
+  if ((s = pick_split_n(n, dtype, tokens, d, workspace, workspace_bytes, &cfg, &need)) != MHC_OK)
+    return s;
   const uint64_t es = elem_size(dtype), T = (uint64_t)tokens, nn = (uint64_t)n, nm = n_mix(n);
   const Span in[] = {
       {"x", x, T * nn * d * es},
@@ -1914,13 +2060,18 @@ mhc_status mhc_mixes_n(int32_t n, const void* x, int32_t dtype, int64_t tokens, 
   const Span out[] = {
       {"pre_out", pre_out, T * nn * 4}, {"post_out", post_out, T * nn * 4},
       {"comb_out", comb_out, T * nn * nn * 4}, {"mix_out", mix_out, T * nm * 4},
+      {"workspace", workspace, (uint64_t)need},
   };
-  s = check_spans(in, 4, out, 4, nullptr, nullptr);
+  s = check_spans(in, 4, out, cfg.groups > 0 ? 5 : 4, nullptr, nullptr);
   if (s != MHC_OK) return s;
   StepArgs a{x, nullptr, nullptr, nullptr, nullptr, w_packed, base, scale, nullptr, nullptr,
              nullptr, pre_out, post_out, comb_out, mix_out, tokens, d, sinkhorn_iters, norm_eps,
              hc_eps};
-  return run_n(n, a, dtype, kMixesOnly, static_cast<hipStream_t>(stream));
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (cfg.groups > 0)
+    return n == 2 ? launch_split_n<2>(a, workspace, cfg, kMixesOnly, st)
+                  : launch_split_n<4>(a, workspace, cfg, kMixesOnly, st);
+  return run_n(n, a, dtype, kMixesOnly, st);
 }
 
 mhc_status mhc_sinkhorn_n(int32_t n, const float* mixes, int64_t tokens, const float* base,

@@ -30,6 +30,7 @@ def test_header_declares_the_entry_points():
                "mhc_abi_version", "mhc_d_granule", "mhc_fused_step_workspace_bytes",
                "mhc_hc_post", "mhc_hc_pre", "mhc_rmsnorm", "mhc_wmix_packed_bytes_n",
                "mhc_pack_wmix_n", "mhc_fused_step_n", "mhc_mixes_n", "mhc_sinkhorn_n",
+               "mhc_fused_step_n_workspace_bytes",
                "mhc_fused_step_backward_n", "mhc_fused_step_backward_workspace_bytes_n"):
         assert fn in names
 
@@ -42,7 +43,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_granule_and_status_strings():
-    assert binding.abi_version() == 5
+    assert binding.abi_version() == 6
     assert binding.d_granule() == 32
     lib = binding.load()
     assert lib.mhc_status_string(0) == b"MHC_OK"
@@ -231,7 +232,7 @@ def _call_n(n_layout, **over):
                 w_packed=p["w_packed"], base=p["base"], scale=p["scale"], gamma=p["gamma"],
                 iters=20, norm_eps=1e-6, hc_eps=1e-6, x_out=p["x_out"], y_out=p["y_out"],
                 pre_out=p["pre_out"], post_out=p["post_out"], comb_out=p["comb_out"],
-                mix_out=p["mix_out"], stream=None)
+                mix_out=p["mix_out"], workspace=None, workspace_bytes=0, stream=None)
     args.update(over)
     return binding.load().mhc_fused_step_n(*args.values())
 
@@ -263,15 +264,24 @@ def test_fused_step_n_stream_counts_and_zero_tokens():
         assert _call_n(n, tokens=0, x_out=_layout_n(n)["x"]) == binding.MHC_OK
 
 
+def test_fused_step_n_workspace_bytes_validation():
+    lib = binding.load()
+    for args in ((3, 100, 512, binding.MHC_BF16), (4, -1, 512, binding.MHC_BF16),
+                 (2, 100, 48, binding.MHC_BF16), (8, 100, 512, 7)):
+        assert lib.mhc_fused_step_n_workspace_bytes(*args) == -1
+        assert "bad" in binding.last_error()
+
+
 def test_mixes_n_sinkhorn_n_pack_n_validation():
     lib = binding.load()
     p = _layout_n(8)
     st = lib.mhc_mixes_n(8, p["x"], binding.MHC_BF16, T, D, p["w_packed"], p["base"], p["scale"],
-                         20, 1e-6, 1e-6, p["pre_out"], p["post_out"], p["comb_out"], None, None)
+                         20, 1e-6, 1e-6, p["pre_out"], p["post_out"], p["comb_out"], None, None, 0,
+                         None)
     assert st == binding.MHC_ERR_INVALID_ARG and "mix_out is NULL" in binding.last_error()
     st = lib.mhc_mixes_n(6, p["x"], binding.MHC_BF16, T, D, p["w_packed"], p["base"], p["scale"],
                          20, 1e-6, 1e-6, p["pre_out"], p["post_out"], p["comb_out"], p["mix_out"],
-                         None)
+                         None, 0, None)
     assert st == binding.MHC_ERR_UNSUPPORTED
     st = lib.mhc_sinkhorn_n(8, p["mix_out"], T, p["base"], p["scale"], 20, 1e-6, p["pre_out"],
                             p["pre_out"], p["comb_out"], None)

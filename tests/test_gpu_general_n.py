@@ -2,7 +2,10 @@
 
 Every case is checked against the float64 oracle with the rules of
 tests/parity.py (new streams as correct roundings, everything after them
-teacher-forced on the validated new streams). Cases cover n = 2, 4, 8, bf16
+teacher-forced on the validated new streams). Both kernels of the family
+are covered: the token-block kernel (path "block", every n and dtype) and
+the feature-split kernel (path "split", n = 2 and 4, bf16, slices of 64,
+128 and 256 features). Cases cover n = 2, 4, 8, bf16
 and f32 streams, widths from one 32-feature step to d = 5120, odd step counts,
 token counts from one token to several 128-token blocks with a ragged last
 block, in-place updates, guard bands around every output, and, at n = 4,
@@ -64,16 +67,124 @@ CASES = [
 
 @pytest.mark.parametrize("n,dtype,d,t", CASES)
 def test_general_n_parity(n, dtype, d, t):
+    """The token-block kernel (path "block")."""
     _log(f"general n={n} {dtype} d={d} T={t}")
     case = make_case(wl.Workload(700 + 10 * n + d % 7 + t % 5, "general_n", t, d, dtype, n=n))
-    out, _ = run_step_n(case, dtype)
+    out, _ = run_step_n(case, dtype, path="block")
     o = check_step(case, out, dtype)
     _log(f"  ties in new streams: {o['n_ties']}; comb sums {comb_sum_stats(out['comb'])}")
 
 
-def test_general_n4_matches_tuned_kernels():
+SPLIT_CASES = [
+    # n, d, tokens: slices of 64 * rounds features, 16 to 40 slices
+    (2, 5120, 300),     # 20 slices of 256 (4 rounds)
+    (2, 5120, 1),       # one token
+    (2, 4096, 1000),    # 16 slices of 256
+    (2, 2048, 129),     # 16 slices of 128
+    (2, 1024, 70),      # 16 slices of 64
+    (4, 5120, 257),     # 40 slices of 128
+    (4, 3072, 600),     # 24 slices of 128
+    (4, 2048, 130),     # 16 slices of 128
+    (4, 1024, 33),      # 16 slices of 64
+]
+
+
+@pytest.mark.parametrize("n,d,t", SPLIT_CASES)
+def test_general_n_split_parity(n, d, t):
+    """The feature-split kernel of the n-family (path "split"), and the new
+    streams identical to the block kernel's (same per-element arithmetic)."""
+    _log(f"general split n={n} d={d} T={t}")
+    case = make_case(wl.Workload(800 + 10 * n + d % 7 + t % 5, "general_n_split", t, d, "bf16",
+                                 n=n))
+    ws = torch.empty(mhc.fused_step_n_workspace_bytes(n, t, d, "bf16"), dtype=torch.uint8,
+                     device="cuda")
+    out, _ = run_step_n(case, "bf16", path="split", workspace=ws)
+    assert mhc.split_status(ws) == 0
+    o = check_step(case, out, "bf16")
+    blk, _ = run_step_n(case, "bf16", path="block")
+    assert torch.equal(out["x_out"], blk["x_out"])
+    np.testing.assert_allclose(out["mix"].numpy(), blk["mix"].numpy(), rtol=1e-5, atol=2e-5)
+    _log(f"  ties in new streams: {o['n_ties']}; comb sums {comb_sum_stats(out['comb'])}")
+
+
+def test_general_n_split_guard_bands_and_in_place():
+    """n = 2, d = 1024 (16 slices of 64) through the split kernel: nothing is
+    written outside the outputs, and x_out = x gives the same results."""
+    n, t, d, gpad = 2, 150, 1024, 64
+    case = make_case(wl.Workload(820, "general_n_split_guard", t, d, "bf16", n=n))
+    dev = _dev(case)
+    wp = mhc.pack_wmix_n(dev["w_mix"], "bf16")
+
+    def guarded(count, dtype):
+        buf = torch.full((count + 2 * gpad,), float("nan"), dtype=dtype, device="cuda")
+        return buf, buf[gpad:gpad + count]
+
+    nm = (2 + n) * n
+    bx, vx = guarded(t * n * d, torch.bfloat16)
+    by, vy = guarded(t * d, torch.bfloat16)
+    bp, vp = guarded(t * n, torch.float32)
+    bu, vu = guarded(t * n, torch.float32)
+    bc, vc = guarded(t * n * n, torch.float32)
+    bm, vm = guarded(t * nm, torch.float32)
+    out = mhc.fused_step_n(dev["x"], dev["f"], dev["pre"], dev["post"], dev["comb"], wp,
+                           dev["base"], dev["scale"], dev["gamma"], x_out=vx.view(t, n, d),
+                           y_out=vy.view(t, d), pre_out=vp.view(t, n), post_out=vu.view(t, n),
+                           comb_out=vc.view(t, n, n), mix_out=vm.view(t, nm), path="split")
+    torch.cuda.synchronize()
+    for buf, view in ((bx, vx), (by, vy), (bp, vp), (bu, vu), (bc, vc), (bm, vm)):
+        assert torch.isnan(buf[:gpad].float()).all() and torch.isnan(buf[-gpad:].float()).all()
+        assert not torch.isnan(view.float()).any()
+    ref = {k: v.cpu() for k, v in out.items()}
+    check_step(case, ref, "bf16")
+    x = dev["x"].clone()
+    again = mhc.fused_step_n(x, dev["f"], dev["pre"], dev["post"], dev["comb"], wp, dev["base"],
+                             dev["scale"], dev["gamma"], x_out=x, path="split")
+    torch.cuda.synchronize()
+    for k in ("x_out", "y", "pre", "post", "comb", "mix"):
+        assert torch.equal(again[k].cpu(), ref[k]), k
+
+
+@pytest.mark.parametrize("n,d,t", [(2, 5120, 700), (4, 2048, 260)])
+def test_mixes_n_split_parity(n, d, t):
+    w = wl.Workload(830 + n, "mixes_n_split", t, d, "bf16", n=n)
+    x = wl.streams(w)
+    p = wl.params(w)
+    out = mhc.mixes_n(to_dev(x), mhc.pack_wmix_n(to_dev(p["w_mix"]), "bf16"), to_dev(p["base"]),
+                      to_dev(p["scale"]), path="split")
+    torch.cuda.synchronize()
+    check_mixes(dict(x=x, **p), {k: v.cpu() for k, v in out.items()}, "bf16")
+
+
+@pytest.mark.timeout(900)
+def test_general_n2_throughput_shape_sampled():
+    """n = 2 at 65,536 tokens x d = 5120 through the feature-split kernel, as
+    the benchmark launches it; first and last blocks plus a seeded random
+    sample of tokens checked in full."""
+    w = wl.Workload(3, "large_prefill_n2", 65536, 5120, "bf16", batch=4, n=2)
+    t_start = time.time()
+    x = wl.streams(w)
+    f = wl.sublayer_out(w)
+    prev, cur = wl.params(w, prev=True), wl.params(w)
+    pre, post, comb = oracle_prior(x, prev)
+    _log(f"n2 large: inputs and oracle prior in {time.time() - t_start:.1f}s")
+    case = dict(x=x, f=f, pre=pre, post=post, comb=comb, iters=w.iters, norm_eps=w.norm_eps,
+                hc_eps=w.hc_eps, **cur)
+    out, _ = run_step_n(case, "bf16", path="split")
+    t = w.tokens
+    rng = np.random.default_rng(12345)
+    idx = np.unique(np.concatenate([np.arange(128), np.arange(t - 128, t),
+                                    rng.choice(t, 256, replace=False)]))
+    sub = dict(case)
+    for k in ("x", "f", "pre", "post", "comb"):
+        sub[k] = case[k][idx]
+    check_step(sub, {k: v[idx] for k, v in out.items()}, "bf16")
+    _log(f"n2 large: {len(idx)} sampled tokens match; comb sums {comb_sum_stats(out['comb'])}")
+
+
+@pytest.mark.parametrize("npath", ["block", "split"])
+def test_general_n4_matches_tuned_kernels(npath):
     case = make_case(wl.Workload(760, "general_n4", 700, 5120, "bf16"))
-    a, _ = run_step_n(case, "bf16")
+    a, _ = run_step_n(case, "bf16", path=npath)
     for path in ("split", "tile"):
         b, _ = run_step(case, path=path)
         assert torch.equal(a["x_out"], b["x_out"]), path
