@@ -31,10 +31,11 @@
 //     atomic per workgroup and batch).
 //   * One batch later each wave waits for all ns slices of the batch, sums the
 //     ns partial sums of h^2 of its 16 tokens and writes y for its slice from h
-//     kept in registers; four waves per workgroup (alternating halves) each sum
-//     the ns partial rows of one token of the batch (token c + ns*j), apply the
-//     RMS scaling and write its 24 mixes; tail_kernel then runs the split and
-//     the 4x4 Sinkhorn on all tokens (16 lanes per token).
+//     kept in registers; waves 0 .. ceil(128 / ns) - 1 each sum the ns partial
+//     rows of one token of the batch (token c + ns * wave), apply the RMS
+//     scaling and write its 24 mixes (alternating the wave halves from batch
+//     to batch was 0.6% slower); tail_kernel then runs the split and the 4x4
+//     Sinkhorn on all tokens (16 lanes per token).
 //
 // Cross-workgroup protocol (correct wherever the workgroups run; the group ->
 // XCD mapping only matters for speed):
@@ -438,12 +439,11 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
       p0 += bload_sc1(wsr, o1, 0);
       p1 += bload_sc1(wsr, o1, 16);
     }
-    // waves 4(i&1) + j, j = 0..3, take the batch's token c + ns*j (when it
-    // exists) for the split and Sinkhorn; their partial loads (lane: 16-byte
-    // chunk l&7 of the token row, slices l>>3 + 8k) follow at once so their
-    // latency hides behind the y work
-    const int tb = c + ns * (wave & 3);
-    const bool sk = (wave >> 2) == (i & 1) && tb < kBatch;
+    // wave w takes the batch's token c + ns*w (when it exists) for the mixes
+    // row; its partial loads (lane: 16-byte chunk l&7 of the token row, slices
+    // l>>3 + 8k) follow at once so their latency hides behind the y work
+    const int tb = c + ns * wave;
+    const bool sk = tb < kBatch;
     f32x4 sk_part[kMaxSlices / 8];
     {
       const uint32_t base = (uint32_t)(mp_off(G) + slot_id * mp_slot_bytes(ns)) +
