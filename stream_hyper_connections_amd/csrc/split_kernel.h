@@ -501,23 +501,15 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
         x += __shfl_xor(x, 16);
         v[e] = x + __shfl_xor(x, 32);
       }
-      // every lane now holds floats 4(l&7) .. 4(l&7)+3 of the token's row
-      const int e = lane & 15;
-      auto pick = [&](int chunk, int el) {
-        const float w0 = __shfl(v[0], chunk), w1 = __shfl(v[1], chunk);
-        const float w2 = __shfl(v[2], chunk), w3 = __shfl(v[3], chunk);
-        return el == 0 ? w0 : (el == 1 ? w1 : (el == 2 ? w2 : w3));
-      };
-      const float msum_c = pick(2 + (e >> 2), e & 3);   // mixes slot 8 + e
-      const float msum_p = pick((e & 7) >> 2, e & 3);   // mixes slot e (e < 8)
-      const float ssum = __shfl(v[0], 6);               // sum of x'^2
+      // every lane now holds floats 4(l&7) .. 4(l&7)+3 of the token's row:
+      // lanes 0..5 write mixes 4l .. 4l+3; float 24 (lane 6) is sum x'^2
+      const float ssum = __shfl(v[0], 6);
       const float rr = rsqrtf(ssum / (float)(kStreams * d) + a.norm_eps);
-      const float mc = msum_c * rr, mp = msum_p * rr;
       const int64_t t = (g + (int64_t)i * G) * kBatch + tb;
       // the mixes row; split and Sinkhorn run in tail_kernel
-      if (t < a.tokens && lane < 16) {
-        fs.mix[t * kMix + 8 + e] = mc;
-        if (e < 8) fs.mix[t * kMix + e] = mp;
+      if (t < a.tokens && lane < kMix / 4) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) fs.mix[t * kMix + 4 * lane + e] = v[e] * rr;
       }
     }
   };
