@@ -131,101 +131,77 @@ struct Args {
   float hc_eps;
 };
 
-// ----- split / Sinkhorn backward, one thread per token ---------------------------------
+// ----- split / Sinkhorn backward, n^2 lanes per token --------------------------------------
 
-// In-place normalisation of the NxN matrix c (rows when ROW, columns
-// otherwise) by (sum + eps); the divisors go to s.
-template <int N, bool ROW>
-__device__ __forceinline__ void normalise(float (&c)[N][N], float (&s)[N], float eps) {
-#pragma unroll
-  for (int a = 0; a < N; ++a) {
-    float sum = 0.f;
-#pragma unroll
-    for (int b = 0; b < N; ++b) sum += ROW ? c[a][b] : c[b][a];
-    s[a] = sum + eps;
-#pragma unroll
-    for (int b = 0; b < N; ++b) {
-      if (ROW)
-        c[a][b] = c[a][b] / s[a];
-      else
-        c[b][a] = c[b][a] / s[a];
-    }
-  }
-}
-
-// Step k of the comb's normalisations (k = 0: the first column division,
-// then rows at odd k and columns at even k).
+// Sums and maximum over the n lanes of an entry's row (lanes e with the same
+// e / n) and over the n lanes of its column (same e % n), within one DPP row
+// (n = 4: a token is one 16-lane row; n = 2: one quad).
 template <int N>
-__device__ __forceinline__ void sk_step(float (&c)[N][N], float (&s)[N], int k, float eps) {
-  if (k == 0 || (k & 1) == 0)
-    normalise<N, false>(c, s, eps);
-  else
-    normalise<N, true>(c, s, eps);
+__device__ __forceinline__ float row_sum(float v) {
+  if constexpr (N == 4) return pipe::quad_sum(v);
+  else return v + pipe::dpp<pipe::kQuadSwap1>(v);
+}
+template <int N>
+__device__ __forceinline__ float row_max(float v) {
+  if constexpr (N == 4) return pipe::quad_max(v);
+  else return fmaxf(v, pipe::dpp<pipe::kQuadSwap1>(v));
+}
+template <int N>
+__device__ __forceinline__ float col_sum(float v) {
+  if constexpr (N == 4) return pipe::col_sum(v);
+  else return v + pipe::dpp<pipe::kQuadSwap2>(v);
 }
 
-// The reverse pass recomputes the forward up to each normalisation from the
-// nearest of kCp checkpoints (the matrices entering every seg-th step), so
-// the state stays O(kCp N^2) registers and the work O(iters^2 / kCp). For Y = X / (sum + eps) along an axis,
-// dX = (dY - sum_axis(dY * Y)) / (sum + eps); for P = softmax(L) along rows,
-// dL = P * (dP - sum_row(dP * P)).
+// Gradient g at the split's pre-activations of (pre, post, comb) =
+// split_sinkhorn(m): lane e of a token's n^2 lanes holds comb entry
+// (e / n, e % n), and lanes e < 2n also the pre (e < n) or post slot.
+// Step k of the comb's normalisations divides the columns (k = 0 and even k)
+// or the rows (odd k) by (sum + eps), here as a product with the hardware
+// reciprocal, as the forward kernels do. The reverse pass recomputes each step's
+// output from the nearest of kCp checkpoints (the matrices entering every
+// seg-th step). For Y = X / (sum + eps) along an axis, dX = (dY - sum_axis(dY
+// * Y)) / (sum + eps); for P = softmax(L) along rows, dL = P * (dP -
+// sum_row(dP * P)). Every lane stays active (the sums are DPP lane
+// exchanges); lanes of tokens past the end compute on token 0 and store
+// nothing.
 template <int N>
 __global__ __launch_bounds__(256) void split_kernel(Args a) {
   constexpr int kMix = Dims<N>::kMix;
+  constexpr int kE = N * N;
   constexpr int kCp = 8;
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (t >= a.tokens) return;
-  const float* m = a.mix + t * kMix;
-  float* g = a.ws + t * kMix;   // region g at offset 0
-  const float s0 = a.scale[0], s1 = a.scale[1], s2 = a.scale[2];
-#pragma unroll
-  for (int j = 0; j < N; ++j) {
-    const float sp = sigmoidf(m[j] * s0 + a.base[j]);
-    g[j] = a.d_pre[t * N + j] * sp * (1.0f - sp);
-    const float sq = sigmoidf(m[N + j] * s1 + a.base[N + j]);
-    g[N + j] = a.d_post[t * N + j] * 2.0f * sq * (1.0f - sq);
+  static_assert(N == 2 || N == 4, "one DPP row or quad per token");
+  const int e = threadIdx.x % kE;
+  const int64_t t = (int64_t)blockIdx.x * (256 / kE) + threadIdx.x / kE;
+  const bool ok = t < a.tokens;
+  const int64_t tc = ok ? t : 0;
+  const float* m = a.mix + tc * kMix;
+  float* g = a.ws + tc * kMix;   // region g at offset 0
+  if (e < N) {
+    const float sp = sigmoidf(m[e] * a.scale[0] + a.base[e]);
+    if (ok) g[e] = a.d_pre[tc * N + e] * sp * (1.0f - sp);
+  } else if (e < 2 * N) {
+    const float sq = sigmoidf(m[e] * a.scale[1] + a.base[e]);
+    if (ok) g[e] = a.d_post[tc * N + (e - N)] * 2.0f * sq * (1.0f - sq);
   }
-  float p[N][N];
-#pragma unroll
-  for (int j = 0; j < N; ++j) {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int k = 0; k < N; ++k) {
-      p[j][k] = m[2 * N + N * j + k] * s2 + a.base[2 * N + N * j + k];
-      mx = fmaxf(mx, p[j][k]);
-    }
-    float rs = 0.f;
-#pragma unroll
-    for (int k = 0; k < N; ++k) {
-      p[j][k] = expf(p[j][k] - mx);
-      rs += p[j][k];
-    }
-#pragma unroll
-    for (int k = 0; k < N; ++k) p[j][k] = p[j][k] / rs;
-  }
-  float dc[N][N];
-#pragma unroll
-  for (int j = 0; j < N; ++j)
-#pragma unroll
-    for (int k = 0; k < N; ++k) dc[j][k] = a.d_comb[(t * N + j) * N + k];
+  // the row softmax of the comb logits
+  const float lg = m[2 * N + e] * a.scale[2] + a.base[2 * N + e];
+  const float ex = expf(lg - row_max<N>(lg));
+  const float p = ex / row_sum<N>(ex);
+  float dc = a.d_comb[tc * kE + e];
   const float eps = a.hc_eps;
-  // checkpoints: the input of step cp * seg, kept for kCp segments
+  auto axis_sum = [&](int q, float v) {
+    return (q == 0 || (q & 1) == 0) ? col_sum<N>(v) : row_sum<N>(v);
+  };
   const int nsteps = 2 * a.iters - 1;
   const int seg = (nsteps + kCp - 1) / kCp;
-  float ck[kCp][N][N];
+  float ck[kCp];
   {
-    float c[N][N], s[N];
-#pragma unroll
-    for (int j = 0; j < N; ++j)
-#pragma unroll
-      for (int k = 0; k < N; ++k) c[j][k] = p[j][k] + eps;
+    float c = p + eps;
 #pragma unroll
     for (int cp = 0; cp < kCp; ++cp) {
-#pragma unroll
-      for (int j = 0; j < N; ++j)
-#pragma unroll
-        for (int k = 0; k < N; ++k) ck[cp][j][k] = c[j][k];
+      ck[cp] = c;
       const int hi = (cp + 1) * seg < nsteps ? (cp + 1) * seg : nsteps;
-      for (int q = cp * seg; q < hi; ++q) sk_step<N>(c, s, q, eps);
+      for (int q = cp * seg; q < hi; ++q) c = c * __builtin_amdgcn_rcpf(axis_sum(q, c) + eps);
     }
   }
 #pragma unroll
@@ -233,36 +209,18 @@ __global__ __launch_bounds__(256) void split_kernel(Args a) {
     const int lo = cp * seg;
     const int hi = lo + seg < nsteps ? lo + seg : nsteps;
     for (int step = hi - 1; step >= lo; --step) {
-      float c[N][N], s[N];
-#pragma unroll
-      for (int j = 0; j < N; ++j)
-#pragma unroll
-        for (int k = 0; k < N; ++k) c[j][k] = ck[cp][j][k];
-      for (int q = lo; q <= step; ++q) sk_step<N>(c, s, q, eps);   // c = output of `step`
-      const bool row = step != 0 && (step & 1);
-#pragma unroll
-      for (int a2 = 0; a2 < N; ++a2) {
-        float dot = 0.f;
-#pragma unroll
-        for (int b = 0; b < N; ++b) dot += row ? dc[a2][b] * c[a2][b] : dc[b][a2] * c[b][a2];
-#pragma unroll
-        for (int b = 0; b < N; ++b) {
-          if (row)
-            dc[a2][b] = (dc[a2][b] - dot) / s[a2];
-          else
-            dc[b][a2] = (dc[b][a2] - dot) / s[a2];
-        }
+      float c = ck[cp], r = 1.f;
+      for (int q = lo; q <= step; ++q) {   // c = output of `step`, r = 1 / its divisor
+        r = __builtin_amdgcn_rcpf(axis_sum(q, c) + eps);
+        c = c * r;
       }
+      const float dot = axis_sum(step, dc * c);
+      dc = (dc - dot) * r;
     }
   }
-#pragma unroll
-  for (int j = 0; j < N; ++j) {
-    float dot = 0.f;
-#pragma unroll
-    for (int k = 0; k < N; ++k) dot += dc[j][k] * p[j][k];
-#pragma unroll
-    for (int k = 0; k < N; ++k) g[2 * N + N * j + k] = p[j][k] * (dc[j][k] - dot);
-  }
+  // dc is now the gradient of softmax + eps, i.e. of p
+  const float dot = row_sum<N>(dc * p);
+  if (ok) g[2 * N + e] = p * (dc - dot);
 }
 
 // ----- per-token statistics, one wave per token ----------------------------------------

@@ -1663,8 +1663,8 @@ mhc_status run_backward(const bwd::Args& args, hipStream_t st) {
   bwd::Args a = args;
   const int64_t block = rows ? bwd::kRowBlock : bwd::kBlock;
   a.dg_groups = (a.tokens + block - 1) / block;
-  const unsigned tok256 = (unsigned)((a.tokens + 255) / 256);
-  hipLaunchKernelGGL((bwd::split_kernel<N>), dim3(tok256), dim3(256), 0, st, a);
+  const unsigned tok_blocks = (unsigned)((a.tokens + 256 / (N * N) - 1) / (256 / (N * N)));
+  hipLaunchKernelGGL((bwd::split_kernel<N>), dim3(tok_blocks), dim3(256), 0, st, a);
   mhc_status s = launch_status("backward split/Sinkhorn kernel launch");
   if (s != MHC_OK) return s;
   hipLaunchKernelGGL((bwd::stats_kernel<N, DT>), dim3((unsigned)((a.tokens + 3) / 4)), dim3(256),
