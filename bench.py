@@ -240,7 +240,15 @@ def backward_bench(w, steps, warmup):
 CONFIG_NAMES = ("tiny", "prefill", "decode", "large_prefill", "chain")
 
 
-def all_configs_bench(reps_min=50, min_ms=200.0, flush_bytes=512 << 20):
+# the kernel that dominates each route of mhc_fused_step
+ROUTE_KERNELS = {
+    "split": "fsplit::split_kernel (feature-split fused step)",
+    "chunk": "pipe::chunk_kernel + pipe::chunk_finish_kernel (chunked fused step)",
+    "tile": "pipe::fused_bf16_kernel (tile fused step)",
+}
+
+
+def all_configs_bench(reps_min=50, min_ms=200.0, flush_bytes=512 << 20, path="auto"):
     """mhc_fused_step alone on each workload (the chain: its first step), with
     HIP events around the C-ABI call: warm (10 warm-up calls, then at least
     `reps_min` calls or `min_ms` of calls) and cache-flushed (a write of
@@ -255,6 +263,11 @@ def all_configs_bench(reps_min=50, min_ms=200.0, flush_bytes=512 << 20):
     scratch = torch.empty(flush_bytes, dtype=torch.uint8, device=dev)
     for name in CONFIG_NAMES:
         w = wl.WORKLOADS[name]
+        try:
+            route = mhc.fused_step_route(path, w.tokens, w.d, w.dtype)
+        except ValueError as e:
+            print(f"[bench] {name}: skipped ({e})", file=sys.stderr, flush=True)
+            continue
         dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
         elem = 2 if w.dtype == "bf16" else 4
         x = upload_tokens(w, wl.X, 0, dev, dt).view(w.tokens, N, w.d)
@@ -271,10 +284,12 @@ def all_configs_bench(reps_min=50, min_ms=200.0, flush_bytes=512 << 20):
 
         def call():
             mhc.fused_step(x, f, prior["pre"], prior["post"], prior["comb"], wp, cur["base"],
-                           cur["scale"], cur["gamma"], w.iters, w.norm_eps, w.hc_eps, **outs)
+                           cur["scale"], cur["gamma"], w.iters, w.norm_eps, w.hc_eps, path=path,
+                           **outs)
 
         line = {"metric": "fused mHC step latency per workload, n=4", "workload": name,
-                "tokens": w.tokens, "d": w.d, "dtype": w.dtype}
+                "tokens": w.tokens, "d": w.d, "dtype": w.dtype,
+                "route": route}
         alg = algorithmic_bytes(w.tokens, w.d, elem)
         for mode in ("warm", "flushed"):
             for _ in range(10):
@@ -312,6 +327,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="large_prefill")
+    ap.add_argument("--path", choices=("auto", "tile", "split", "chunk"), default="auto",
+                    help="kernel family of mhc_fused_step (auto: the library's choice by size)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="minimum oracle time for the cpu_baseline sample")
@@ -543,7 +560,7 @@ def main():
         backward_bench(w, args.steps, args.warmup)
         return
     if args.all_configs:
-        all_configs_bench()
+        all_configs_bench(path=args.path)
         return
     if args.copy_ceiling:
         copy_ceiling(w, args.steps, args.warmup)
@@ -563,10 +580,8 @@ def main():
     outs = dict(x_out=torch.empty_like(x), y_out=torch.empty_like(f),
                 pre_out=torch.empty_like(prior["pre"]), post_out=torch.empty_like(prior["post"]),
                 comb_out=torch.empty_like(prior["comb"]))
-    split = (w.tokens >= mhc.SPLIT_MIN_TOKENS and
-             mhc.fused_step_workspace_bytes(w.tokens, w.d, w.dtype) > 0)
-    kernel_name = ("fsplit::split_kernel (feature-split fused step)" if split
-                   else "pipe::fused_bf16_kernel (tile fused step)")
+    route = mhc.fused_step_route(args.path, w.tokens, w.d, w.dtype)
+    kernel_name = ROUTE_KERNELS[route]
     if args.form != "fused":
         kernel_name = "hc_post + hc_mixes + hc_pre + RMSNorm kernels (three-kernel form)"
     if args.sinkhorn_sweep:
@@ -586,7 +601,8 @@ def main():
         e1.record()
         if args.form == "fused":
             mhc.fused_step(x, f, prior["pre"], prior["post"], prior["comb"], wp, cur["base"],
-                           cur["scale"], cur["gamma"], w.iters, w.norm_eps, w.hc_eps, **outs)
+                           cur["scale"], cur["gamma"], w.iters, w.norm_eps, w.hc_eps,
+                           path=args.path, **outs)
         else:
             mhc.three_kernel_step(x, f, prior["pre"], prior["post"], prior["comb"], wp,
                                   cur["base"], cur["scale"], cur["gamma"], w.iters, w.norm_eps,
@@ -610,7 +626,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    if split:
+    if route != "tile" and args.form == "fused":
         ws = mhc.workspace_for(dev, mhc.fused_step_workspace_bytes(w.tokens, w.d, w.dtype))
         if mhc.split_status(ws) != 0:
             print("bench.py: a cross-workgroup wait of the feature-split kernel gave up; the "

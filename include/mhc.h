@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define MHC_ABI_VERSION 6
+#define MHC_ABI_VERSION 7
 #define MHC_N_STREAMS 4
 #define MHC_N_MIX 24
 
@@ -54,6 +54,26 @@ typedef enum mhc_status {
 } mhc_status;
 
 typedef enum mhc_dtype { MHC_F32 = 0, MHC_BF16 = 1 } mhc_dtype;
+
+/*
+ * Kernel family of mhc_fused_step and mhc_mixes:
+ *   MHC_PATH_AUTO   no workspace: the tile kernel. With a workspace: the
+ *                   chunked kernels up to MHC_CHUNK_AUTO_TOKENS (1024) tokens,
+ *                   the feature-split kernel above, each where it applies
+ *                   (else the other, else the tile kernel).
+ *   MHC_PATH_TILE   the tile kernel (one workgroup per 16 tokens, no
+ *                   workspace; the workspace argument is ignored).
+ *   MHC_PATH_SPLIT  the feature-split kernel (needs a workspace;
+ *                   MHC_ERR_UNSUPPORTED where it does not apply).
+ *   MHC_PATH_CHUNK  the chunked kernels (needs a workspace;
+ *                   MHC_ERR_UNSUPPORTED where they do not apply).
+ */
+typedef enum mhc_path {
+  MHC_PATH_AUTO = 0,
+  MHC_PATH_TILE = 1,
+  MHC_PATH_SPLIT = 2,
+  MHC_PATH_CHUNK = 3
+} mhc_path;
 
 typedef void* mhc_stream_t;
 
@@ -92,17 +112,30 @@ mhc_status mhc_pack_wmix(const float* w_mix, int32_t d, int32_t dtype, void* w_p
 
 /*
  * mhc_fused_step_workspace_bytes -- bytes of device workspace that
- * mhc_fused_step needs to run its feature-split kernel for these arguments on
- * the current device: 0 when that kernel does not apply (then the workspace
- * argument is ignored), -1 for bad arguments or a failing HIP query (see
- * mhc_last_error). The feature-split kernel applies to MHC_BF16 streams whose
- * width splits into ns slices of S features, ns in {32, 40, 48, 64} and S in
- * {64, 96, 128, 160} (d = 2048 ... 10240, e.g. 5120 = 40 x 128), on a device
- * with at least ns compute units and cooperative launch support. The size
- * depends on the device's compute unit count, d and tokens (about 17 MB for
- * d = 5120 on 256 CUs, plus 96 bytes per token for the mixes rows).
+ * mhc_fused_step and mhc_mixes need to run either of their workspace kernel
+ * families for these arguments on the current device (the larger of the two
+ * needs; 0 when neither applies, and then only the tile kernel runs), -1 for
+ * bad arguments or a failing HIP query (see mhc_last_error).
+ *   - Feature-split kernel: MHC_BF16 streams whose width splits into ns
+ *     slices of S features, ns in {32, 40, 48, 64} and S in {64, 96, 128, 160}
+ *     (d = 2048 ... 10240, e.g. 5120 = 40 x 128), on a device with at least ns
+ *     compute units and cooperative launch support. About 17 MB for d = 5120
+ *     on 256 CUs, plus 96 bytes per token for the mixes rows.
+ *   - Chunked kernels: MHC_BF16 streams, d a multiple of 64 up to 5120, at
+ *     most 8192 tokens. 256 bytes plus 128 bytes per token and chunk of 512
+ *     features (1,280 bytes per token at d = 5120).
  */
 int64_t mhc_fused_step_workspace_bytes(int64_t tokens, int32_t d, int32_t dtype);
+
+/*
+ * mhc_fused_step_route -- the kernel family (MHC_PATH_TILE, MHC_PATH_SPLIT or
+ * MHC_PATH_CHUNK) that mhc_fused_step and mhc_mixes run for `path`, these
+ * arguments and a workspace given (with_workspace != 0) or not, on the current
+ * device; -1 (see mhc_last_error) for bad arguments, a path that cannot run
+ * them, or a failing HIP query.
+ */
+int32_t mhc_fused_step_route(int32_t path, int64_t tokens, int32_t d, int32_t dtype,
+                             int32_t with_workspace);
 
 /*
  * mhc_fused_step -- one Single-Pass mHC step at the boundary between sublayer
@@ -126,20 +159,23 @@ int64_t mhc_fused_step_workspace_bytes(int64_t tokens, int32_t d, int32_t dtype)
  *          RMSNorm gain), sinkhorn_iters >= 1, norm_eps >= 0, hc_eps >= 0.
  * Outputs: x_out [T][4][d] (may be x), y_out [T][d], pre_out/post_out
  *          [T][4], comb_out [T][4][4], mix_out [T][24] (optional, NULL to skip).
+ * path:    mhc_path, the kernel family (MHC_PATH_AUTO picks by size).
  * Workspace (optional): NULL, or device memory of workspace_bytes bytes,
- *          256-byte aligned, overlapping no other argument. When it is given and
- *          mhc_fused_step_workspace_bytes() > 0, the step runs the feature-split
- *          kernel (each compute unit keeps one slice of the features and of W on
- *          chip; workgroups exchange per-token partial sums through the workspace),
- *          which needs the whole device: it is launched cooperatively, one
- *          workgroup per compute unit, and fails with MHC_ERR_HIP when that
- *          launch is refused. workspace_bytes below the required size is
- *          MHC_ERR_INVALID_ARG. Otherwise the tile kernel runs (no workspace).
- *          Calls that share a workspace must be ordered (same stream or
- *          synchronised). After the call has completed, the 32-bit word at
- *          workspace offset 0 is 0; it is 1 if a cross-workgroup wait gave up
- *          after its bounded number of polls, in which case the outputs are
- *          invalid.
+ *          256-byte aligned, overlapping no other argument, used by:
+ *          - the feature-split kernel: each compute unit keeps one slice of
+ *            the features and of W on chip; workgroups exchange per-token
+ *            partial sums through the workspace. It needs the whole device:
+ *            it is launched cooperatively, one workgroup per compute unit, and
+ *            fails with MHC_ERR_HIP when that launch is refused.
+ *          - the chunked kernels: workgroups of 16 tokens x 512 features write
+ *            per-token partial sums to the workspace, and a second kernel
+ *            finishes each token (two plain launches; for small calls).
+ *          workspace_bytes below the chosen route's need is
+ *          MHC_ERR_INVALID_ARG. Calls that share a workspace must be ordered
+ *          (same stream or synchronised). After the call has completed, the
+ *          32-bit word at workspace offset 0 is 0; the feature-split kernel
+ *          sets it to 1 if a cross-workgroup wait gave up after its bounded
+ *          number of polls, in which case the outputs are invalid.
  */
 mhc_status mhc_fused_step(const void* x, const void* f, int32_t dtype, int64_t tokens,
                           int32_t d, const float* pre_in, const float* post_in,
@@ -147,22 +183,23 @@ mhc_status mhc_fused_step(const void* x, const void* f, int32_t dtype, int64_t t
                           const float* scale, const float* gamma, int32_t sinkhorn_iters,
                           float norm_eps, float hc_eps, void* x_out, void* y_out,
                           float* pre_out, float* post_out, float* comb_out, float* mix_out,
-                          void* workspace, int64_t workspace_bytes, mhc_stream_t stream);
+                          int32_t path, void* workspace, int64_t workspace_bytes,
+                          mhc_stream_t stream);
 
 /*
  * mhc_mixes -- hc_mixes alone ([SW] Code, hc_mixes and "All 5 steps"): one RMS
  * statistic over the flattened 4*d streams, the 24-wide projection, then the
  * split and Sinkhorn of mhc_sinkhorn4. Reads x [T][4][d]; writes pre_out,
  * post_out [T][4], comb_out [T][4][4] and, if not NULL, mix_out [T][24].
- * w_packed as for mhc_fused_step. workspace / workspace_bytes as for
- * mhc_fused_step (same size, mhc_fused_step_workspace_bytes): with it, the
- * feature-split kernel runs in its mixes-only mode.
+ * w_packed as for mhc_fused_step. path, workspace and workspace_bytes as for
+ * mhc_fused_step (same size, mhc_fused_step_workspace_bytes): the
+ * feature-split and chunked kernels run in their mixes-only modes.
  */
 mhc_status mhc_mixes(const void* x, int32_t dtype, int64_t tokens, int32_t d,
                      const void* w_packed, const float* base, const float* scale,
                      int32_t sinkhorn_iters, float norm_eps, float hc_eps, float* pre_out,
-                     float* post_out, float* comb_out, float* mix_out, void* workspace,
-                     int64_t workspace_bytes, mhc_stream_t stream);
+                     float* post_out, float* comb_out, float* mix_out, int32_t path,
+                     void* workspace, int64_t workspace_bytes, mhc_stream_t stream);
 
 /*
  * The step as separate kernels, in the order of [RN] Code, Block.forward:

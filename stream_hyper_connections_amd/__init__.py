@@ -10,12 +10,13 @@ from .binding import (  # noqa: F401
     MhcError,
     abi_version,
     d_granule,
-    SPLIT_MIN_TOKENS,
+    PATHS,
     fused_step,
     fused_step_backward_n,
     fused_step_backward_workspace_bytes_n,
     fused_step_n,
     fused_step_n_workspace_bytes,
+    fused_step_route,
     fused_step_workspace_bytes,
     hc_post,
     hc_pre,

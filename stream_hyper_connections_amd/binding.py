@@ -34,9 +34,11 @@ _SIGS = {
     "mhc_fused_step": ([_c_void_p, _c_void_p, _i32, _i64, _i32, _c_void_p, _c_void_p, _c_void_p,
                         _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _f32, _f32,
                         _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
-                        _c_void_p, _i64, _c_void_p], _i32),
+                        _i32, _c_void_p, _i64, _c_void_p], _i32),
     "mhc_mixes": ([_c_void_p, _i32, _i64, _i32, _c_void_p, _c_void_p, _c_void_p, _i32, _f32, _f32,
-                   _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _c_void_p], _i32),
+                   _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _c_void_p, _i64, _c_void_p],
+                  _i32),
+    "mhc_fused_step_route": ([_i32, _i64, _i32, _i32, _i32], _i32),
     "mhc_hc_post": ([_c_void_p, _c_void_p, _i32, _i64, _i32, _c_void_p, _c_void_p, _c_void_p,
                      _c_void_p], _i32),
     "mhc_hc_pre": ([_c_void_p, _i32, _i64, _i32, _c_void_p, _c_void_p, _c_void_p], _i32),
@@ -161,18 +163,30 @@ def pack_wmix(w_mix: torch.Tensor, dtype, out: torch.Tensor | None = None) -> to
     return out
 
 
-# token count from which path="auto" takes the feature-split kernel (when it
-# applies to d and the dtype). Measured on 65,536-token down to 16-token calls
-# at d = 5120 it is faster than the tile kernel at every size (59 against 124
-# us at 256 tokens), so it is taken from the first token.
-SPLIT_MIN_TOKENS = 1
+# mhc_path codes by name
+PATHS = {"auto": 0, "tile": 1, "split": 2, "chunk": 3}
+_PATH_NAMES = {v: k for k, v in PATHS.items()}
 
 _workspaces = {}
 
 
+def fused_step_route(path: str, tokens: int, d: int, dtype, with_workspace=True) -> str:
+    """mhc_fused_step_route: the kernel family ("tile", "split" or "chunk") that
+    fused_step / mixes run for `path`; ValueError if that path cannot run these
+    arguments."""
+    if path not in PATHS:
+        raise ValueError(f"unknown path {path!r}")
+    r = load().mhc_fused_step_route(PATHS[path], tokens, d, _dtype_name_code(dtype),
+                                    1 if with_workspace else 0)
+    if r < 0:
+        raise ValueError(f"path {path!r}, d={d}, {dtype}: {last_error()}")
+    return _PATH_NAMES[r]
+
+
 def fused_step_workspace_bytes(tokens: int, d: int, dtype) -> int:
-    """mhc_fused_step_workspace_bytes: 0 when the feature-split kernel does not
-    apply to (d, dtype) on the current device."""
+    """mhc_fused_step_workspace_bytes: the workspace both workspace kernel
+    families need (0 when neither applies to (tokens, d, dtype) on the current
+    device)."""
     n = load().mhc_fused_step_workspace_bytes(tokens, d, _dtype_name_code(dtype))
     if n < 0:
         raise MhcError("mhc_fused_step_workspace_bytes", MHC_ERR_INVALID_ARG, last_error())
@@ -202,14 +216,14 @@ def fused_step(x, f, pre_in, post_in, comb_in, w_packed, base, scale, gamma, ite
     """mhc_fused_step on tensors. x [T,4,d], f [T,d] (bf16 or f32); coefficients
     and parameters float32. Returns dict(x_out, y, pre, post, comb, mix).
 
-    path: "tile" (no workspace), "split" (feature-split kernel; raises if it does
-    not apply), or "auto" (split for at least SPLIT_MIN_TOKENS tokens when it
-    applies). workspace: optional uint8 tensor for the split kernel (a cached
-    one is used otherwise)."""
+    path: "tile" (no workspace), "split" (feature-split kernel), "chunk" (chunked
+    kernels; both raise ValueError where they do not apply), or "auto" (the
+    library's choice by size, with a workspace where one applies). workspace:
+    optional uint8 tensor (a cached one is used otherwise)."""
     t, n, d = x.shape
     if n != N_STREAMS:
         raise ValueError("x must be [T, 4, d]")
-    ws_ptr, ws_bytes = _workspace_arg(x, t, d, path, workspace)
+    code, ws_ptr, ws_bytes = _workspace_arg(x, t, d, path, workspace)
     x_out = torch.empty_like(x) if x_out is None else x_out
     y_out = torch.empty_like(f) if y_out is None else y_out
     pre_out = _f32_out((t, N_STREAMS), x, pre_out)
@@ -221,26 +235,27 @@ def fused_step(x, f, pre_in, post_in, comb_in, w_packed, base, scale, gamma, ite
         _ptr(x), _ptr(f), _dtype_code(x), t, d, _ptr(pre_in), _ptr(post_in), _ptr(comb_in),
         _ptr(w_packed), _ptr(base), _ptr(scale), _ptr(gamma), iters, norm_eps, hc_eps,
         _ptr(x_out), _ptr(y_out), _ptr(pre_out), _ptr(post_out), _ptr(comb_out), _ptr(mix_out),
-        ws_ptr, ws_bytes, _stream())
+        code, ws_ptr, ws_bytes, _stream())
     _check("mhc_fused_step", st)
     return {"x_out": x_out, "y": y_out, "pre": pre_out, "post": post_out, "comb": comb_out,
             "mix": mix_out}
 
 
 def _workspace_arg(x, t, d, path, workspace):
-    """(pointer, bytes) of the workspace for path "tile" / "split" / "auto"."""
-    if path not in ("auto", "tile", "split"):
+    """(mhc_path code, workspace pointer, workspace bytes) for path "auto" /
+    "tile" / "split" / "chunk"."""
+    if path not in PATHS:
         raise ValueError(f"unknown path {path!r}")
     if path == "tile":
-        return None, 0
+        return PATHS["tile"], None, 0
+    if path != "auto":
+        fused_step_route(path, t, d, _dtype_code(x))   # raises where the path does not apply
     need = fused_step_workspace_bytes(t, d, _dtype_code(x))
-    if path == "split" and need == 0:
-        raise ValueError(f"the feature-split kernel does not apply to d={d}, {x.dtype}")
-    if need > 0 and (path == "split" or t >= SPLIT_MIN_TOKENS):
-        if workspace is None:
-            workspace = workspace_for(x.device, need)
-        return _ptr(workspace), workspace.numel() * workspace.element_size()
-    return None, 0
+    if need == 0:
+        return PATHS[path], None, 0
+    if workspace is None:
+        workspace = workspace_for(x.device, need)
+    return PATHS[path], _ptr(workspace), workspace.numel() * workspace.element_size()
 
 
 def mixes(x, w_packed, base, scale, iters=20, norm_eps=1e-6, hc_eps=1e-6, pre_out=None,
@@ -251,7 +266,7 @@ def mixes(x, w_packed, base, scale, iters=20, norm_eps=1e-6, hc_eps=1e-6, pre_ou
     t, n, d = x.shape
     if n != N_STREAMS:
         raise ValueError("x must be [T, 4, d]")
-    ws_ptr, ws_bytes = _workspace_arg(x, t, d, path, workspace)
+    code, ws_ptr, ws_bytes = _workspace_arg(x, t, d, path, workspace)
     pre_out = _f32_out((t, N_STREAMS), x, pre_out)
     post_out = _f32_out((t, N_STREAMS), x, post_out)
     comb_out = _f32_out((t, N_STREAMS, N_STREAMS), x, comb_out)
@@ -259,7 +274,7 @@ def mixes(x, w_packed, base, scale, iters=20, norm_eps=1e-6, hc_eps=1e-6, pre_ou
         mix_out = _f32_out((t, N_MIX), x, None)
     st = load().mhc_mixes(_ptr(x), _dtype_code(x), t, d, _ptr(w_packed), _ptr(base), _ptr(scale),
                           iters, norm_eps, hc_eps, _ptr(pre_out), _ptr(post_out), _ptr(comb_out),
-                          _ptr(mix_out), ws_ptr, ws_bytes, _stream())
+                          _ptr(mix_out), code, ws_ptr, ws_bytes, _stream())
     _check("mhc_mixes", st)
     return {"pre": pre_out, "post": post_out, "comb": comb_out, "mix": mix_out}
 

@@ -1,0 +1,232 @@
+// Chunked small-batch path (bf16 streams, d a multiple of 64, d <= 5120): the
+// fused step, or the mixes alone, as two plain kernel launches.
+//
+// Included by mhc.hip (one translation unit) after the pipelined tile kernel,
+// whose per-step pieces (stream and operand loads, hc_post / hc_pre / sums of
+// squares, the MFMA projection) it reuses.
+//
+// Why. For a few hundred tokens the feature-split kernel occupies only a few
+// of its 128-token batches, and the device-side cost of its cooperative launch
+// (about 11 us before and after it, against none between plain launches)
+// outweighs the kernel itself; the tile kernel, one workgroup per 16 tokens,
+// leaves most compute units idle. Here the features are cut into chunks as
+// well, and the per-token reduction moves to a second kernel:
+//
+//   * chunk_kernel: workgroup (tile, chunk) = 16 tokens x `cpairs` pairs of
+//     32-feature steps (64 * cpairs features of every row). Its 8 waves run the
+//     pipelined tile kernel's steps on them (wave w takes the pairs w, w + 8,
+//     ... of the chunk; W read from L2), store the new streams, store h into
+//     y_out (normalised in place later), and write one partial row of 32 floats
+//     per token: the 24 projection sums of the chunk (hi + mid + lo terms),
+//     sum x'^2 and sum h^2.
+//   * chunk_finish_kernel: one workgroup per token sums the token's partial
+//     rows over the chunks (in chunk order), forms the mixes
+//     (r * projection, [SW] Code, hc_mixes), runs the split and the Sinkhorn on
+//     16 lanes of wave 0 ([SW] Code, hc_split_sinkhorn), and rewrites y_out
+//     = S(gamma * (h * rh)) ([RN] RMSNorm).
+// No workgroup ever waits for another: the launch boundary orders the partial
+// rows. Workspace: a 256-byte header (word 0, the status word, is set to 0;
+// nothing in this path can fail after launch) and then the partial rows,
+// [chunk][token][32] float32.
+
+namespace pipe {
+
+constexpr int kPart = 32;                  // floats per partial row
+constexpr int64_t kChunkHeader = 256;      // bytes before the partial rows
+
+inline int64_t chunk_workspace_bytes(int nchunks, int64_t tokens) {
+  return kChunkHeader + (int64_t)nchunks * tokens * kPart * 4;
+}
+
+// One pair of steps (A = sa, B = sa + 1) of a chunk: the order of pair_body,
+// with h stored to y_out instead of LDS.
+template <int MODE>
+__device__ __forceinline__ void chunk_pair(int sa, int sn, Ctx& c, Half& ha, Half& hb) {
+  u32x4 w[4][kTiles];
+  u32x4 xa[4], xb[4];
+
+  load_w(w, c, sa);
+  __builtin_amdgcn_sched_barrier(0);
+  const u32x4 h_a = valu_core<MODE>(ha, xa, c);
+  __builtin_amdgcn_sched_barrier(0);
+  load_half<MODE>(ha, c, sn);
+  __builtin_amdgcn_sched_barrier(0);
+  mfma_step(xa, w, c);
+  __builtin_amdgcn_sched_barrier(0);
+
+  load_w(w, c, sa + 1);
+  __builtin_amdgcn_sched_barrier(0);
+  const u32x4 h_b = valu_core<MODE>(hb, xb, c);
+  __builtin_amdgcn_sched_barrier(0);
+  load_half<MODE>(hb, c, sn + 1);
+  if (MODE == kFused) {
+    const uint32_t col = (uint32_t)sa * 64;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      bstore<MHC_STORE_AUX>(c.xor_, c.xoff, col + (uint32_t)k * c.d2, xa[k]);
+      bstore<MHC_STORE_AUX>(c.xor_, c.xoff, col + 64 + (uint32_t)k * c.d2, xb[k]);
+    }
+    bstore<0>(c.yr, c.foff, col, h_a);
+    bstore<0>(c.yr, c.foff, col + 64, h_b);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  mfma_step(xb, w, c);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Grid: ceil(tokens / 16) * nchunks workgroups of kThreads; nchunks * cpairs
+// covers the d / 64 pairs of the row.
+template <int MODE>
+__global__ __launch_bounds__(kThreads) void chunk_kernel(StepArgs a, int nchunks, int cpairs,
+                                                         char* __restrict__ ws) {
+  __shared__ float acc_s[kWaves][kTok][kCols];
+  __shared__ float ss_s[kWaves][kTok];
+  __shared__ float hs_s[kWaves][kTok];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tr = lane & 15;
+  const int g = lane >> 4;
+  const int d = a.d;
+  const int nsteps = d / kStep;
+  const int npairs = nsteps / 2;
+  const int tile = blockIdx.x / nchunks;
+  const int chunk = blockIdx.x - tile * nchunks;
+  const int pair0 = chunk * cpairs;
+  const int np = min(cpairs, npairs - pair0);
+  const int cnt = wave < np ? (np - wave + kWaves - 1) / kWaves : 0;
+  if (blockIdx.x == 0 && tid == 0) *reinterpret_cast<uint32_t*>(ws) = 0u;
+
+  const int64_t t0 = (int64_t)tile * kTok;
+  const int ntok = (int)min((int64_t)kTok, a.tokens - t0);
+  const uint32_t rowx = (uint32_t)(kStreams * d * 2), rowf = (uint32_t)(d * 2);
+  Ctx c;
+  c.d2 = d * 2;
+  c.wr = make_rsrc(a.wpk, (uint32_t)nsteps * kStreams * kTiles * 1024);
+  c.woff = (uint32_t)lane * 16;
+  c.woff_last = (tr < kCols - 16 * (kTiles - 1)) ? (uint32_t)lane * 16 : kOutOfRange;
+  c.xr = make_rsrc(static_cast<const char*>(a.x) + t0 * rowx, ntok * rowx);
+  c.xoff = (uint32_t)tr * rowx + (uint32_t)g * 16;
+  c.foff = (uint32_t)tr * rowf + (uint32_t)g * 16;
+  if (MODE == kFused) {
+    c.fr = make_rsrc(static_cast<const char*>(a.f) + t0 * rowf, ntok * rowf);
+    c.xor_ = make_rsrc(static_cast<char*>(a.x_out) + t0 * rowx, ntok * rowx);
+    c.yr = make_rsrc(static_cast<char*>(a.y_out) + t0 * rowf, ntok * rowf);
+    const int64_t tc = t0 + min(tr, ntok - 1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 cv = *reinterpret_cast<const f32x4*>(a.comb_in + tc * 16 + 4 * j);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) c.C[j][k] = cv[k];
+    }
+    const f32x4 u = *reinterpret_cast<const f32x4*>(a.post_in + tc * 4);
+    const f32x4 p = *reinterpret_cast<const f32x4*>(a.pre_in + tc * 4);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      c.U[k] = u[k];
+      c.P[k] = p[k];
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < kTiles; ++q) c.acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  c.ss = 0.f;
+  c.hs = 0.f;
+
+  Half ha, hb;
+  if (cnt > 0) {
+    load_half<MODE>(ha, c, 2 * (pair0 + wave));
+    load_half<MODE>(hb, c, 2 * (pair0 + wave) + 1);
+  }
+  for (int p = 0; p < cnt; ++p) {
+    const int sa = 2 * (pair0 + wave + kWaves * p);
+    const int sn = p + 1 < cnt ? sa + 2 * kWaves : sa;   // next pair (clamped to this one)
+    chunk_pair<MODE>(sa, sn, c, ha, hb);
+  }
+
+  // sums of squares over the four lane groups, then the waves' partials to LDS
+  float ss = c.ss, hs = c.hs;
+  ss += __shfl_xor(ss, 16);
+  ss += __shfl_xor(ss, 32);
+  hs += __shfl_xor(hs, 16);
+  hs += __shfl_xor(hs, 32);
+  if (g == 0) {
+    ss_s[wave][tr] = ss;
+    hs_s[wave][tr] = hs;
+  }
+#pragma unroll
+  for (int q = 0; q < kTiles; ++q) {
+    const int col = 16 * q + tr;
+    if (col < kCols) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc_s[wave][4 * g + r][col] = c.acc[q][r];
+    }
+  }
+  __syncthreads();
+
+  // one partial row per token: thread (token tt, column j), 16 x 32 threads
+  const int tt = tid >> 5, j = tid & 31;
+  float v = 0.f;
+  if (j < kMix) {
+    float hi = 0.f, mid = 0.f, lo = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      hi += acc_s[w][tt][j];
+      mid += acc_s[w][tt][kMix + j];
+      lo += acc_s[w][tt][2 * kMix + j];
+    }
+    v = (hi + mid) + lo;
+  } else if (j == kMix || j == kMix + 1) {
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) v += j == kMix ? ss_s[w][tt] : hs_s[w][tt];
+  }
+  if (tt < ntok) {
+    float* part = reinterpret_cast<float*>(ws + kChunkHeader);
+    part[((int64_t)chunk * a.tokens + t0 + tt) * kPart + j] = v;
+  }
+}
+
+// Grid: tokens workgroups of 256 threads.
+template <int MODE>
+__global__ __launch_bounds__(256) void chunk_finish_kernel(StepArgs a, int nchunks,
+                                                           const char* __restrict__ ws) {
+  const int64_t t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const float* part = reinterpret_cast<const float*>(ws + kChunkHeader);
+  float v = 0.f;   // lane j < 32: column j of the token's partial rows, summed
+  if (lane < kPart)
+    for (int ch = 0; ch < nchunks; ++ch) v += part[((int64_t)ch * a.tokens + t) * kPart + lane];
+  const float ssum = __shfl(v, kMix);
+  const float hsum = __shfl(v, kMix + 1);
+  if (tid < 64) {
+    const float r = rsqrtf(ssum / (float)(kStreams * a.d) + a.norm_eps);
+    const int e = lane & 15;
+    const float mc = __shfl(v, 8 + e) * r;   // comb logit slot of (j, k) = (e/4, e%4)
+    const float mp = __shfl(v, e & 7) * r;   // pre / post slot for e < 8
+    if (lane < 16) {
+      if (a.mix_out != nullptr) {
+        a.mix_out[t * kMix + 8 + e] = mc;
+        if (e < 8) a.mix_out[t * kMix + e] = mp;
+      }
+      const float eps = a.hc_eps;
+      if (e < 4) a.pre_out[t * 4 + e] = sigmoidf(mp * a.scale[0] + a.base[e]) + eps;
+      if (e >= 4 && e < 8) a.post_out[t * 4 + (e - 4)] = 2.0f * sigmoidf(mp * a.scale[1] + a.base[e]);
+      float cv = mc * a.scale[2] + a.base[8 + e];
+      cv = expf(cv - quad_max(cv));
+      cv = cv / quad_sum(cv) + eps;
+      cv = cv * __builtin_amdgcn_rcpf(col_sum(cv) + eps);
+      for (int it = 1; it < a.iters; ++it) {
+        cv = cv * __builtin_amdgcn_rcpf(quad_sum(cv) + eps);
+        cv = cv * __builtin_amdgcn_rcpf(col_sum(cv) + eps);
+      }
+      a.comb_out[t * 16 + e] = cv;
+    }
+  }
+  if (MODE == kFused) {
+    const float rh = rsqrtf(hsum / (float)a.d + a.norm_eps);
+    u32x4* y = reinterpret_cast<u32x4*>(static_cast<char*>(a.y_out) + t * a.d * 2);
+    for (int u = tid; u < a.d / 8; u += 256) y[u] = norm_bf(y[u], a.gamma, 8 * u, rh);
+  }
+}
+
+}  // namespace pipe

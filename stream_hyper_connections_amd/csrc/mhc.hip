@@ -824,10 +824,9 @@ __device__ __forceinline__ void load_w(u32x4 (&w)[4][kTiles], const Ctx& c, int 
 }
 
 // hc_post, the sums of squares and hc_pre of one step (the arithmetic per
-// element is that of step_bf); h goes to LDS slot s (or a register).
+// element is that of step_bf); returns the lane's 8 values of h.
 template <int MODE>
-__device__ __forceinline__ void valu_step(const Half& in, u32x4 (&xo)[4], Ctx& c, Smem& sm, int s,
-                                          int lane, int half) {
+__device__ __forceinline__ u32x4 valu_core(const Half& in, u32x4 (&xo)[4], Ctx& c) {
   if (MODE == kFused) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -885,6 +884,14 @@ __device__ __forceinline__ void valu_step(const Half& in, u32x4 (&xo)[4], Ctx& c
   }
   c.ss += ssa + ssb;
   c.hs += hsa;
+  return hpk;
+}
+
+// valu_core, with h going to LDS slot s (or a register).
+template <int MODE>
+__device__ __forceinline__ void valu_step(const Half& in, u32x4 (&xo)[4], Ctx& c, Smem& sm, int s,
+                                          int lane, int half) {
+  const u32x4 hpk = valu_core<MODE>(in, xo, c);
   if (MODE == kFused) {
     if (s < kSlots) sm.u.h[s][lane] = hpk;
     else c.hlast[half] = hpk;
@@ -1108,6 +1115,7 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_kernel(StepArgs a, int nt
 }  // namespace pipe
 
 #include "split_kernel.h"
+#include "chunk_kernel.h"
 #include "unfused.h"
 #include "general_n.h"
 #include "split_n.h"
@@ -1255,6 +1263,19 @@ mhc_status check_spans(const Span* in, int nin, const Span* out, int nout, const
     }
   }
   return MHC_OK;
+}
+
+// A workspace of `given` bytes for a route that needs `need`: large enough,
+// 256-byte aligned and overlapping none of the call's other buffers.
+mhc_status check_workspace(const void* ws, int64_t given, int64_t need, const Span* others,
+                           int nothers) {
+  if (given < need)
+    return fail(MHC_ERR_INVALID_ARG, "workspace holds %lld bytes, %lld needed", (long long)given,
+                (long long)need);
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+    return fail(MHC_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+  const Span wsp[] = {{"workspace", ws, (uint64_t)need}};
+  return check_spans(others, nothers, wsp, 1, nullptr, nullptr);
 }
 
 mhc_status launch_status(const char* what) {
@@ -1414,6 +1435,127 @@ mhc_status launch_split(const StepArgs& a, void* ws, const SplitCfg& cfg, int mo
                      stream, mix, a.tokens, a.base, a.scale, a.iters, a.hc_eps, a.pre_out,
                      a.post_out, a.comb_out);
   return launch_status("split/Sinkhorn tail kernel launch");
+}
+
+// Chunked small-batch path: bf16 streams with an even number of 32-feature
+// steps, at most the pipelined kernel's 160, and at most kChunkMaxTokens
+// tokens (the partial rows take 128 bytes per token and chunk). Chunks of
+// MHC_CHUNK_PAIRS pairs of steps (one pair per wave).
+#ifndef MHC_CHUNK_PAIRS
+#define MHC_CHUNK_PAIRS 8
+#endif
+// Largest call that path "auto" runs on the chunked kernels (when a workspace
+// is given); larger calls take the feature-split kernel. At d = 5120 the two
+// kernels' device time (the split kernel with its cooperative-launch gaps)
+// is about 14 + 0.046 T and 42 + 0.022 T microseconds: equal near 1,150
+// tokens.
+#ifndef MHC_CHUNK_AUTO_TOKENS
+#define MHC_CHUNK_AUTO_TOKENS 1024
+#endif
+constexpr int64_t kChunkMaxTokens = 8192;
+
+struct ChunkCfg {
+  int nchunks = 0;
+  int cpairs = 0;
+};
+
+ChunkCfg chunk_config(int32_t dtype, int32_t d, int64_t tokens) {
+  const int nsteps = d / kStep;
+  if (dtype != MHC_BF16 || d % kStep != 0 || nsteps % 2 != 0 || nsteps > pipe::kMaxSteps ||
+      tokens > kChunkMaxTokens)
+    return ChunkCfg{};
+  const int npairs = nsteps / 2;
+  const int cp = std::min(MHC_CHUNK_PAIRS, npairs);
+  return ChunkCfg{(npairs + cp - 1) / cp, cp};
+}
+
+mhc_status launch_chunk(const StepArgs& a, void* ws, const ChunkCfg& cc, int mode,
+                        hipStream_t stream) {
+  const unsigned grid = (unsigned)(((a.tokens + kTok - 1) / kTok) * cc.nchunks);
+  char* w = static_cast<char*>(ws);
+  if (mode == kFused)
+    hipLaunchKernelGGL(pipe::chunk_kernel<kFused>, dim3(grid), dim3(pipe::kThreads), 0, stream, a,
+                       cc.nchunks, cc.cpairs, w);
+  else
+    hipLaunchKernelGGL(pipe::chunk_kernel<kMixesOnly>, dim3(grid), dim3(pipe::kThreads), 0, stream,
+                       a, cc.nchunks, cc.cpairs, w);
+  mhc_status s = launch_status("chunk kernel launch");
+  if (s != MHC_OK) return s;
+  if (mode == kFused)
+    hipLaunchKernelGGL(pipe::chunk_finish_kernel<kFused>, dim3((unsigned)a.tokens), dim3(256), 0,
+                       stream, a, cc.nchunks, w);
+  else
+    hipLaunchKernelGGL(pipe::chunk_finish_kernel<kMixesOnly>, dim3((unsigned)a.tokens), dim3(256),
+                       0, stream, a, cc.nchunks, w);
+  return launch_status("chunk finish kernel launch");
+}
+
+// Which kernel family runs a fused step or mixes call: the tile kernel (no
+// workspace), the feature-split kernel or the chunked kernels (workspace).
+enum class Route { kTile, kSplit, kChunk };
+
+// Workspace bytes each workspace route needs (0: the route does not apply).
+struct RouteNeeds {
+  SplitCfg split;
+  ChunkCfg chunk;
+  int64_t split_bytes = 0;
+  int64_t chunk_bytes = 0;
+};
+
+mhc_status route_needs(int32_t dtype, int32_t d, int64_t tokens, RouteNeeds* rn) {
+  *rn = RouteNeeds{};
+  mhc_status s = split_config(dtype, d, &rn->split);
+  if (s != MHC_OK) return s;
+  if (rn->split.groups > 0)
+    rn->split_bytes = fsplit::workspace_bytes(rn->split.groups, rn->split.ns, tokens);
+  rn->chunk = chunk_config(dtype, d, tokens);
+  if (rn->chunk.nchunks > 0) rn->chunk_bytes = pipe::chunk_workspace_bytes(rn->chunk.nchunks, tokens);
+  return MHC_OK;
+}
+
+// The route of a call with `path` and a workspace (or none), or an error for
+// a path that cannot run these arguments.
+mhc_status pick_route(int32_t path, const void* workspace, int64_t tokens, const RouteNeeds& rn,
+                      Route* r) {
+  switch (path) {
+    case MHC_PATH_TILE:
+      *r = Route::kTile;
+      return MHC_OK;
+    case MHC_PATH_AUTO:
+      if (workspace == nullptr) *r = Route::kTile;
+      else if (rn.chunk_bytes > 0 && (tokens <= MHC_CHUNK_AUTO_TOKENS || rn.split_bytes == 0))
+        *r = Route::kChunk;
+      else if (rn.split_bytes > 0) *r = Route::kSplit;
+      else *r = Route::kTile;
+      return MHC_OK;
+    case MHC_PATH_SPLIT:
+    case MHC_PATH_CHUNK: {
+      const bool split = path == MHC_PATH_SPLIT;
+      if ((split ? rn.split_bytes : rn.chunk_bytes) == 0)
+        return fail(MHC_ERR_UNSUPPORTED, "the %s kernel does not apply to these arguments",
+                    split ? "feature-split" : "chunked");
+      if (workspace == nullptr)
+        return fail(MHC_ERR_INVALID_ARG, "path %s needs a workspace", split ? "SPLIT" : "CHUNK");
+      *r = split ? Route::kSplit : Route::kChunk;
+      return MHC_OK;
+    }
+    default: return fail(MHC_ERR_INVALID_ARG, "unknown path %d", path);
+  }
+}
+
+// pick_route, querying the device only when a workspace route is possible.
+mhc_status choose_route(int32_t path, const void* workspace, int32_t dtype, int32_t d,
+                        int64_t tokens, RouteNeeds* rn, Route* r) {
+  *rn = RouteNeeds{};
+  if (path == MHC_PATH_TILE || (path == MHC_PATH_AUTO && workspace == nullptr)) {
+    *r = Route::kTile;
+    return MHC_OK;
+  }
+  if (path == MHC_PATH_AUTO || path == MHC_PATH_SPLIT || path == MHC_PATH_CHUNK) {
+    const mhc_status s = route_needs(dtype, d, tokens, rn);
+    if (s != MHC_OK) return s;
+  }
+  return pick_route(path, workspace, tokens, *rn, r);
 }
 
 mhc_status launch_step(const StepArgs& a, int32_t dtype, int mode, hipStream_t stream,
@@ -1732,9 +1874,23 @@ int64_t mhc_fused_step_workspace_bytes(int64_t tokens, int32_t d, int32_t dtype)
     fail(MHC_ERR_INVALID_ARG, "bad tokens (%lld), d (%d) or dtype (%d)", (long long)tokens, d, dtype);
     return -1;
   }
-  SplitCfg cfg;
-  if (split_config(dtype, d, &cfg) != MHC_OK) return -1;
-  return cfg.groups > 0 ? fsplit::workspace_bytes(cfg.groups, cfg.ns, tokens) : 0;
+  RouteNeeds rn;
+  if (route_needs(dtype, d, tokens, &rn) != MHC_OK) return -1;
+  return std::max(rn.split_bytes, rn.chunk_bytes);
+}
+
+int32_t mhc_fused_step_route(int32_t path, int64_t tokens, int32_t d, int32_t dtype,
+                             int32_t with_workspace) {
+  if (tokens < 0 || d <= 0 || d % kStep != 0 || elem_size(dtype) == 0) {
+    fail(MHC_ERR_INVALID_ARG, "bad tokens (%lld), d (%d) or dtype (%d)", (long long)tokens, d, dtype);
+    return -1;
+  }
+  RouteNeeds rn;
+  Route r;
+  static const char kDummy = 0;   // stands for a workspace; never dereferenced
+  if (choose_route(path, with_workspace ? &kDummy : nullptr, dtype, d, tokens, &rn, &r) != MHC_OK)
+    return -1;
+  return r == Route::kTile ? MHC_PATH_TILE : (r == Route::kSplit ? MHC_PATH_SPLIT : MHC_PATH_CHUNK);
 }
 
 mhc_status mhc_pack_wmix(const float* w_mix, int32_t d, int32_t dtype, void* w_packed,
@@ -1765,8 +1921,8 @@ mhc_status mhc_fused_step(const void* x, const void* f, int32_t dtype, int64_t t
                           const void* w_packed, const float* base, const float* scale,
                           const float* gamma, int32_t sinkhorn_iters, float norm_eps,
                           float hc_eps, void* x_out, void* y_out, float* pre_out,
-                          float* post_out, float* comb_out, float* mix_out, void* workspace,
-                          int64_t workspace_bytes, mhc_stream_t stream) {
+                          float* post_out, float* comb_out, float* mix_out, int32_t path,
+                          void* workspace, int64_t workspace_bytes, mhc_stream_t stream) {
   mhc_status s = check_common(dtype, tokens, d, sinkhorn_iters, norm_eps, hc_eps);
   if (s != MHC_OK) return s;
   if (tokens == 0) return ok();
@@ -1793,39 +1949,31 @@ mhc_status mhc_fused_step(const void* x, const void* f, int32_t dtype, int64_t t
     s = check_spans(all, 14, mo, 1, nullptr, nullptr);
     if (s != MHC_OK) return s;
   }
-  SplitCfg cfg;
-  if (workspace != nullptr) {
-    s = split_config(dtype, d, &cfg);
-    if (s != MHC_OK) return s;
-  }
-  if (cfg.groups > 0) {
-    const int64_t need = fsplit::workspace_bytes(cfg.groups, cfg.ns, tokens);
-    if (workspace_bytes < need)
-      return fail(MHC_ERR_INVALID_ARG, "workspace holds %lld bytes, %lld needed",
-                  (long long)workspace_bytes, (long long)need);
-    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-      return fail(MHC_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
-    const Span wsp[] = {{"workspace", workspace, (uint64_t)need}};
+  RouteNeeds rn;
+  Route route;
+  if ((s = choose_route(path, workspace, dtype, d, tokens, &rn, &route)) != MHC_OK) return s;
+  if (route != Route::kTile) {
+    const int64_t need = route == Route::kSplit ? rn.split_bytes : rn.chunk_bytes;
     Span all[15];
     for (int i = 0; i < 9; ++i) all[i] = in[i];
     for (int i = 0; i < 5; ++i) all[9 + i] = out[i];
     int nall = 14;
     if (mix_out != nullptr) all[nall++] = {"mix_out", mix_out, T * kMix * 4};
-    s = check_spans(all, nall, wsp, 1, nullptr, nullptr);
-    if (s != MHC_OK) return s;
+    if ((s = check_workspace(workspace, workspace_bytes, need, all, nall)) != MHC_OK) return s;
   }
   StepArgs a{x, f, pre_in, post_in, comb_in, w_packed, base, scale, gamma, x_out, y_out,
              pre_out, post_out, comb_out, mix_out, tokens, d, sinkhorn_iters, norm_eps, hc_eps};
-  if (cfg.groups > 0)
-    return launch_split(a, workspace, cfg, kFused, static_cast<hipStream_t>(stream));
-  return launch_step(a, dtype, kFused, static_cast<hipStream_t>(stream), "fused step kernel launch");
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (route == Route::kSplit) return launch_split(a, workspace, rn.split, kFused, st);
+  if (route == Route::kChunk) return launch_chunk(a, workspace, rn.chunk, kFused, st);
+  return launch_step(a, dtype, kFused, st, "fused step kernel launch");
 }
 
 mhc_status mhc_mixes(const void* x, int32_t dtype, int64_t tokens, int32_t d,
                      const void* w_packed, const float* base, const float* scale,
                      int32_t sinkhorn_iters, float norm_eps, float hc_eps, float* pre_out,
-                     float* post_out, float* comb_out, float* mix_out, void* workspace,
-                     int64_t workspace_bytes, mhc_stream_t stream) {
+                     float* post_out, float* comb_out, float* mix_out, int32_t path,
+                     void* workspace, int64_t workspace_bytes, mhc_stream_t stream) {
   mhc_status s = check_common(dtype, tokens, d, sinkhorn_iters, norm_eps, hc_eps);
   if (s != MHC_OK) return s;
   if (tokens == 0) return ok();
@@ -1842,31 +1990,24 @@ mhc_status mhc_mixes(const void* x, int32_t dtype, int64_t tokens, int32_t d,
   };
   s = check_spans(in, 4, out, mix_out ? 4 : 3, nullptr, nullptr);
   if (s != MHC_OK) return s;
-  SplitCfg cfg;
-  if (workspace != nullptr) {
-    s = split_config(dtype, d, &cfg);
-    if (s != MHC_OK) return s;
-  }
-  if (cfg.groups > 0) {
-    const int64_t need = fsplit::workspace_bytes(cfg.groups, cfg.ns, tokens);
-    if (workspace_bytes < need)
-      return fail(MHC_ERR_INVALID_ARG, "workspace holds %lld bytes, %lld needed",
-                  (long long)workspace_bytes, (long long)need);
-    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-      return fail(MHC_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
-    const Span wsp[] = {{"workspace", workspace, (uint64_t)need}};
+  RouteNeeds rn;
+  Route route;
+  if ((s = choose_route(path, workspace, dtype, d, tokens, &rn, &route)) != MHC_OK) return s;
+  if (route != Route::kTile) {
+    const int64_t need = route == Route::kSplit ? rn.split_bytes : rn.chunk_bytes;
     Span all[8];
     for (int i = 0; i < 4; ++i) all[i] = in[i];
     for (int i = 0; i < (mix_out ? 4 : 3); ++i) all[4 + i] = out[i];
-    s = check_spans(all, mix_out ? 8 : 7, wsp, 1, nullptr, nullptr);
-    if (s != MHC_OK) return s;
+    if ((s = check_workspace(workspace, workspace_bytes, need, all, mix_out ? 8 : 7)) != MHC_OK)
+      return s;
   }
   StepArgs a{x, nullptr, nullptr, nullptr, nullptr, w_packed, base, scale, nullptr, nullptr,
              nullptr, pre_out, post_out, comb_out, mix_out, tokens, d, sinkhorn_iters, norm_eps,
              hc_eps};
-  if (cfg.groups > 0)
-    return launch_split(a, workspace, cfg, kMixesOnly, static_cast<hipStream_t>(stream));
-  return launch_step(a, dtype, kMixesOnly, static_cast<hipStream_t>(stream), "mixes kernel launch");
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (route == Route::kSplit) return launch_split(a, workspace, rn.split, kMixesOnly, st);
+  if (route == Route::kChunk) return launch_chunk(a, workspace, rn.chunk, kMixesOnly, st);
+  return launch_step(a, dtype, kMixesOnly, st, "mixes kernel launch");
 }
 
 mhc_status mhc_hc_post(const void* x, const void* f, int32_t dtype, int64_t tokens, int32_t d,

@@ -30,7 +30,7 @@ def test_header_declares_the_entry_points():
                "mhc_abi_version", "mhc_d_granule", "mhc_fused_step_workspace_bytes",
                "mhc_hc_post", "mhc_hc_pre", "mhc_rmsnorm", "mhc_wmix_packed_bytes_n",
                "mhc_pack_wmix_n", "mhc_fused_step_n", "mhc_mixes_n", "mhc_sinkhorn_n",
-               "mhc_fused_step_n_workspace_bytes",
+               "mhc_fused_step_n_workspace_bytes", "mhc_fused_step_route",
                "mhc_fused_step_backward_n", "mhc_fused_step_backward_workspace_bytes_n"):
         assert fn in names
 
@@ -43,7 +43,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_granule_and_status_strings():
-    assert binding.abi_version() == 6
+    assert binding.abi_version() == 7
     assert binding.d_granule() == 32
     lib = binding.load()
     assert lib.mhc_status_string(0) == b"MHC_OK"
@@ -91,7 +91,7 @@ def _call(**over):
                 base=p["base"], scale=p["scale"], gamma=p["gamma"], iters=20, norm_eps=1e-6,
                 hc_eps=1e-6, x_out=p["x_out"], y_out=p["y_out"], pre_out=p["pre_out"],
                 post_out=p["post_out"], comb_out=p["comb_out"], mix_out=p["mix_out"],
-                workspace=None, workspace_bytes=0, stream=None)
+                path=binding.PATHS["auto"], workspace=None, workspace_bytes=0, stream=None)
     args.update(over)
     lib = binding.load()
     return lib.mhc_fused_step(*args.values())
@@ -121,6 +121,25 @@ def test_fused_step_rejects_bad_arguments(over, needle):
     assert needle in binding.last_error()
 
 
+def test_fused_step_rejects_unknown_path():
+    for path in (-1, 4, 9):
+        assert _call(path=path) == binding.MHC_ERR_INVALID_ARG
+        assert "unknown path" in binding.last_error()
+
+
+def test_route_query_without_a_device_query():
+    """Routes that need no device attribute: the tile kernel without a
+    workspace, and bad arguments."""
+    lib = binding.load()
+    for path in ("auto", "tile"):
+        assert lib.mhc_fused_step_route(binding.PATHS[path], 64, 5120, binding.MHC_BF16, 0) == 1
+    assert lib.mhc_fused_step_route(binding.PATHS["tile"], 64, 5120, binding.MHC_BF16, 1) == 1
+    assert lib.mhc_fused_step_route(7, 64, 5120, binding.MHC_BF16, 0) == -1
+    assert "unknown path" in binding.last_error()
+    assert lib.mhc_fused_step_route(0, -1, 5120, binding.MHC_BF16, 0) == -1
+    assert "bad tokens" in binding.last_error()
+
+
 def test_workspace_bytes_rejects_bad_arguments():
     lib = binding.load()
     for args in ((-1, 5120, binding.MHC_BF16), (64, 48, binding.MHC_BF16), (64, 5120, 9)):
@@ -142,10 +161,10 @@ def test_mixes_and_sinkhorn_validation():
     lib = binding.load()
     p = _layout()
     st = lib.mhc_mixes(p["x"], binding.MHC_BF16, T, D, p["w_packed"], p["base"], p["scale"], 0,
-                       1e-6, 1e-6, p["pre_out"], p["post_out"], p["comb_out"], None, None, 0, None)
+                       1e-6, 1e-6, p["pre_out"], p["post_out"], p["comb_out"], None, 0, None, 0, None)
     assert st == binding.MHC_ERR_INVALID_ARG
     st = lib.mhc_mixes(p["x"], binding.MHC_BF16, 0, D, p["w_packed"], p["base"], p["scale"], 20,
-                       1e-6, 1e-6, p["pre_out"], p["post_out"], p["comb_out"], None, None, 0, None)
+                       1e-6, 1e-6, p["pre_out"], p["post_out"], p["comb_out"], None, 0, None, 0, None)
     assert st == binding.MHC_OK
     st = lib.mhc_sinkhorn4(p["mix_out"], T, p["base"], p["scale"], 20, -1.0, p["pre_out"],
                            p["post_out"], p["comb_out"], None)

@@ -1,0 +1,193 @@
+"""GPU parity of the chunked small-batch kernels (path="chunk").
+
+Workgroups of 16 tokens x 512 features write per-token partial sums to the
+workspace; a second kernel finishes every token. The cases cover one token,
+ragged 16-token tiles, every chunk count from one (d = 64) to ten (d = 5120),
+a ragged last chunk (d = 5056: 79 pairs of steps in chunks of 8), the largest
+call the path takes (8,192 tokens), the mixes-only mode, in-place updates,
+guard bands, repeated calls on one workspace, agreement with the tile kernel
+(the new streams must match bit for bit: their arithmetic is the same) and the
+size limits. Every call's status word must read 0.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import stream_hyper_connections_amd as mhc
+from stream_hyper_connections_amd import workloads as wl
+from tests.cases import make_case, run_step, to_dev
+from tests.parity import check_mixes, check_step
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def _ws(t, d):
+    return torch.empty(mhc.fused_step_workspace_bytes(t, d, "bf16"), dtype=torch.uint8,
+                       device="cuda")
+
+
+def _run(case, **kw):
+    ws = _ws(len(case["x"]), case["x"].shape[2])
+    out, dev = run_step(case, path="chunk", workspace=ws, **kw)
+    assert mhc.split_status(ws) == 0
+    return out, dev
+
+
+CHUNK_CASES = [
+    (5120, 1),       # one token: one tile, 15 empty rows
+    (5120, 15),
+    (5120, 17),      # a second tile with one token
+    (5120, 256),     # the decode shape
+    (5120, 1000),
+    (5120, 8192),    # the largest call the path takes
+    (5056, 77),      # 79 pairs: nine chunks of 8 and one of 7
+    (64, 33),        # one pair of steps: one chunk, one busy wave
+    (192, 20),       # three pairs: one chunk, waves 3..7 idle
+    (1024, 100),     # two chunks
+    (2048, 513),
+    (2560, 130),     # five chunks
+    (3072, 257),
+    (4096, 300),
+]
+
+
+@pytest.mark.parametrize("d,t", CHUNK_CASES)
+def test_chunk_parity(d, t):
+    _log(f"chunk d={d} T={t}")
+    w = wl.Workload(700 + d % 83 + t % 5, "chunk", t, d, "bf16")
+    case = make_case(w)
+    out, _ = _run(case)
+    o = check_step(case, out, "bf16")
+    _log(f"  ties in new streams: {o['n_ties']}")
+
+
+def test_auto_route_by_size():
+    assert mhc.fused_step_route("auto", 256, 5120, "bf16") == "chunk"
+    assert mhc.fused_step_route("auto", 1024, 5120, "bf16") == "chunk"
+    assert mhc.fused_step_route("auto", 1025, 5120, "bf16") == "split"
+    assert mhc.fused_step_route("auto", 65536, 5120, "bf16") == "split"
+    assert mhc.fused_step_route("auto", 256, 5120, "bf16", with_workspace=False) == "tile"
+    assert mhc.fused_step_route("auto", 256, 5120, "f32") == "tile"
+    # d = 6144 has a slice geometry but is beyond the chunked kernels' 5120
+    assert mhc.fused_step_route("auto", 256, 6144, "bf16") == "split"
+    assert mhc.fused_step_route("chunk", 8192, 5120, "bf16") == "chunk"
+    for args in ((8193, 5120, "bf16"), (64, 6144, "bf16"), (64, 5120, "f32"), (64, 96, "bf16")):
+        with pytest.raises(ValueError, match="does not apply"):
+            mhc.fused_step_route("chunk", *args)
+
+
+def test_chunk_matches_tile_kernel():
+    w = wl.Workload(760, "chunk_vs_tile", 300, 5120, "bf16")
+    case = make_case(w)
+    a, _ = _run(case)
+    b, _ = run_step(case, path="tile")
+    assert torch.equal(a["x_out"], b["x_out"])
+    ya, yb = a["y"].float(), b["y"].float()
+    ulp = torch.maximum(ya.abs(), yb.abs()) * 2.0 ** -7 + 1e-30
+    assert ((ya - yb).abs() <= ulp).all()
+    for k in ("pre", "post", "comb", "mix"):
+        np.testing.assert_allclose(a[k].numpy(), b[k].numpy(), rtol=0, atol=2e-5)
+
+
+def test_chunk_in_place_and_deterministic():
+    t, d = 333, 5120
+    case = make_case(wl.Workload(761, "chunk_inplace", t, d, "bf16"))
+    ref, dev = _run(case)
+    again, _ = _run(case)
+    for k in ref:
+        if ref[k] is not None:
+            assert torch.equal(ref[k], again[k]), k
+    x_dev = dev["x"].clone()
+    wp = mhc.pack_wmix(dev["w_mix"], "bf16")
+    ws = _ws(t, d)
+    out = mhc.fused_step(x_dev, dev["f"], dev["pre"], dev["post"], dev["comb"], wp, dev["base"],
+                         dev["scale"], dev["gamma"], x_out=x_dev, want_mix=True, path="chunk",
+                         workspace=ws)
+    torch.cuda.synchronize()
+    assert mhc.split_status(ws) == 0
+    for k in ("x_out", "y", "pre", "post", "comb", "mix"):
+        assert torch.equal(out[k].cpu(), ref[k]), k
+
+
+def test_chunk_guard_bands_untouched():
+    t, d, gpad = 21, 1024, 64
+    case = make_case(wl.Workload(762, "chunk_guard", t, d, "bf16"))
+    dev = {k: to_dev(case[k]) for k in ("x", "f", "pre", "post", "comb", "w_mix", "base",
+                                        "scale", "gamma")}
+    wp = mhc.pack_wmix(dev["w_mix"], "bf16")
+
+    def guarded(n, dtype):
+        buf = torch.full((n + 2 * gpad,), float("nan"), dtype=dtype, device="cuda")
+        return buf, buf[gpad:gpad + n]
+
+    bx, vx = guarded(t * 4 * d, torch.bfloat16)
+    by, vy = guarded(t * d, torch.bfloat16)
+    bp, vp = guarded(t * 4, torch.float32)
+    bu, vu = guarded(t * 4, torch.float32)
+    bc, vc = guarded(t * 16, torch.float32)
+    bm, vm = guarded(t * 24, torch.float32)
+    ws = _ws(t, d)
+    out = mhc.fused_step(dev["x"], dev["f"], dev["pre"], dev["post"], dev["comb"], wp, dev["base"],
+                         dev["scale"], dev["gamma"], x_out=vx.view(t, 4, d), y_out=vy.view(t, d),
+                         pre_out=vp.view(t, 4), post_out=vu.view(t, 4), comb_out=vc.view(t, 4, 4),
+                         mix_out=vm.view(t, 24), path="chunk", workspace=ws)
+    torch.cuda.synchronize()
+    assert mhc.split_status(ws) == 0
+    for buf, view in ((bx, vx), (by, vy), (bp, vp), (bu, vu), (bc, vc), (bm, vm)):
+        assert torch.isnan(buf[:gpad].float()).all() and torch.isnan(buf[-gpad:].float()).all()
+        assert not torch.isnan(view.float()).any()
+    check_step(case, {k: (v.cpu() if v is not None else None) for k, v in out.items()}, "bf16")
+
+
+def test_chunk_repeated_calls_share_a_workspace():
+    """Two calls in a row on one workspace, the second smaller, then the split
+    kernel on the same workspace (its counters are cleared by its own call)."""
+    ws = _ws(3000, 5120)
+    for t, seed, path in ((2000, 763, "chunk"), (300, 764, "chunk"), (3000, 765, "split"),
+                          (100, 766, "chunk")):
+        case = make_case(wl.Workload(seed, "chunk_repeat", t, 5120, "bf16"))
+        out, _ = run_step(case, path=path, workspace=ws)
+        assert mhc.split_status(ws) == 0
+        check_step(case, out, "bf16")
+
+
+def test_chunk_workspace_validation():
+    t, d = 64, 1024
+    x = torch.zeros((t, 4, d), dtype=torch.bfloat16, device="cuda")
+    f = torch.zeros((t, d), dtype=torch.bfloat16, device="cuda")
+    wp = mhc.pack_wmix(torch.zeros((24, 4 * d), device="cuda"), "bf16")
+    z = torch.zeros((t, 4), device="cuda")
+    need = mhc.fused_step_workspace_bytes(t, d, "bf16")
+    assert need == 256 + 2 * t * 128
+    args = (x, f, z, z, torch.zeros((t, 4, 4), device="cuda"), wp, torch.zeros(24, device="cuda"),
+            torch.ones(3, device="cuda"), torch.ones(d, device="cuda"))
+    small = torch.empty(need - 4, dtype=torch.uint8, device="cuda")
+    with pytest.raises(mhc.MhcError, match="workspace holds"):
+        mhc.fused_step(*args, path="chunk", workspace=small)
+    big = torch.empty(need + 512, dtype=torch.uint8, device="cuda")
+    with pytest.raises(mhc.MhcError, match="256-byte aligned"):
+        mhc.fused_step(*args, path="chunk", workspace=big[16:])
+
+
+@pytest.mark.parametrize("d,t", [(5120, 256), (5120, 2000), (1024, 37), (5056, 19)])
+def test_mixes_chunk_mode_parity(d, t):
+    w = wl.Workload(770 + t % 11, "mixes_chunk", t, d, "bf16")
+    x = wl.streams(w)
+    p = wl.params(w)
+    wp = mhc.pack_wmix(to_dev(p["w_mix"]), "bf16")
+    ws = _ws(t, d)
+    dx = to_dev(x)
+    out = mhc.mixes(dx, wp, to_dev(p["base"]), to_dev(p["scale"]), want_mix=True, path="chunk",
+                    workspace=ws)
+    torch.cuda.synchronize()
+    assert mhc.split_status(ws) == 0
+    check_mixes(dict(x=x, **p), {k: v.cpu() for k, v in out.items()}, "bf16")
+    tile = mhc.mixes(dx, wp, to_dev(p["base"]), to_dev(p["scale"]), want_mix=True, path="tile")
+    for k in ("pre", "post", "comb", "mix"):
+        np.testing.assert_allclose(out[k].cpu().numpy(), tile[k].cpu().numpy(), rtol=0,
+                                   atol=2e-5)

@@ -162,5 +162,9 @@ def test_split_workspace_validation():
     with pytest.raises(mhc.MhcError, match="256-byte aligned"):
         mhc.fused_step(*args, path="split", workspace=big[16:])
     assert mhc.fused_step_workspace_bytes(t, 5120, "f32") == 0
-    assert mhc.fused_step_workspace_bytes(t, 1024, "bf16") == 0
     assert mhc.fused_step_workspace_bytes(t, 7168, "bf16") == 0
+    # d = 1024 has no slice geometry: only the chunked kernels take a workspace
+    assert mhc.fused_step_workspace_bytes(t, 1024, "bf16") == 256 + 2 * t * 128
+    with pytest.raises(ValueError, match="does not apply"):
+        mhc.fused_step_route("split", t, 1024, "bf16")
+    assert mhc.fused_step_route("auto", t, 1024, "bf16") == "chunk"
