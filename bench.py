@@ -32,19 +32,20 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 N = 4
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_step_large_prefill_traffic.txt")
+BACKWARD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "backward_large_prefill_traffic.txt")
 KERNEL_DIR = os.path.join(ROOT, "stream_hyper_connections_amd", "csrc")
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per launch of the fused kernel from the committed rocprofv3
-    FETCH_SIZE / WRITE_SIZE runs, scaled by the same counters on a plain copy
-    of known size; None unless they were taken on the current kernel source
-    and this workload."""
-    import hashlib
+def measured_traffic(workload: str, path=None, sources=None):
+    """HBM bytes per launch of the fused kernel (or, with the backward's record
+    and sources, per backward call) from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE runs, scaled by the same counters on a plain copy of known size;
+    None unless they were taken on the current kernel source and this
+    workload."""
     import json as _json
     try:
-        rec = _json.load(open(TRAFFIC_FILE))
-        src = kernel_source_hash()
+        rec = _json.load(open(path or TRAFFIC_FILE))
+        src = kernel_source_hash(sources or FUSED_SOURCES)
     except (OSError, ValueError):
         return None
     if rec.get("source_sha256") != src or rec.get("workload") != workload:
@@ -56,13 +57,16 @@ def measured_traffic(workload: str):
 # kernel, its clear and tail kernels, the packing kernel and their launch code);
 # the general-n, backward and three-kernel sources do not enter them
 FUSED_SOURCES = ("mhc.hip", "split_kernel.h")
+# the backward's kernels and their launch code
+BACKWARD_SOURCES = ("mhc.hip", "backward.h")
 
 
-def kernel_source_hash() -> str:
-    """sha256 over the fused-step kernel sources (names and contents)."""
+def kernel_source_hash(sources=FUSED_SOURCES) -> str:
+    """sha256 over kernel sources (names and contents), by default those of the
+    fused step."""
     import hashlib
     h = hashlib.sha256()
-    for name in FUSED_SOURCES:
+    for name in sources:
         h.update(name.encode())
         h.update(open(os.path.join(KERNEL_DIR, name), "rb").read())
     return h.hexdigest()
@@ -231,7 +235,9 @@ def backward_bench(w, steps, warmup):
         "call_ms_avg": round(float(ms.mean()), 5),
         "call_ms_p50": round(float(np.percentile(ms, 50)), 5),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": (measured_traffic(w.name, BACKWARD_TRAFFIC_FILE, BACKWARD_SOURCES)
+                                 if n == 4 else None),
                      "algorithmic_bytes_per_launch": alg,
                      "kernel": "bwd:: split + stats + stream + param + reductions"},
         "config": {"workload": w.name, "sinkhorn_iters": w.iters}}), flush=True)
