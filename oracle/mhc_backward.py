@@ -6,7 +6,7 @@ The pages give the forward step only; its gradient is derived here from the
 forward's definitions ("DeepSeek V4.1 · Stream weights for the feed-forward",
 "All 5 steps" and the Code excerpts; "DeepSeek V4.1 · MoE RMSNorm", formula and
 Code) by the chain rule, one forward operation at a time, in reverse order.
-Readings (also listed in the design doc):
+Readings:
 
 * The casts back to the stream dtype (``type_as`` in ``hc_post``, the casts in
   ``hc_pre`` and ``RMSNorm``) pass gradients through unchanged, as automatic

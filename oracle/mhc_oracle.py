@@ -9,8 +9,7 @@ weights ``post`` (u) and the stream combination ``comb`` (C, indexed ``[j, k]``)
 Every array argument is converted to float64 first; rounding to the stream
 dtype happens exactly where the code excerpts cast back (``round_to``).
 
-Readings taken where the pages are silent or disagree (each also listed in
-DESIGN.md):
+Readings taken where the pages are silent or disagree:
 
 * ``hc_post`` contracts ``comb`` on its FIRST index: new stream ``k`` is
   ``sum_j comb[j, k] * X_j + post[k] * F``. This is what the broadcasting in the
