@@ -191,3 +191,60 @@ def test_mixes_chunk_mode_parity(d, t):
     for k in ("pre", "post", "comb", "mix"):
         np.testing.assert_allclose(out[k].cpu().numpy(), tile[k].cpu().numpy(), rtol=0,
                                    atol=2e-5)
+
+
+def test_chunk_path_replays_from_a_hip_graph():
+    """The chunked kernels are plain launches with no memory set: a call
+    captured into a graph replays to the eager result, with eager work and
+    synchronisation between the replays, and the replays follow new inputs
+    copied into the captured buffers."""
+    t, d = 256, 5120
+    cases = [make_case(wl.Workload(780 + i, "chunk_graph", t, d, "bf16")) for i in range(2)]
+    dev = {k: to_dev(cases[0][k]) for k in ("x", "f", "pre", "post", "comb", "w_mix", "base",
+                                            "scale", "gamma")}
+    wp = mhc.pack_wmix(dev["w_mix"], "bf16")
+    ws = _ws(t, d)
+    outs = dict(x_out=torch.empty_like(dev["x"]), y_out=torch.empty_like(dev["f"]),
+                pre_out=torch.empty((t, 4), device="cuda"),
+                post_out=torch.empty((t, 4), device="cuda"),
+                comb_out=torch.empty((t, 4, 4), device="cuda"),
+                mix_out=torch.empty((t, 24), device="cuda"))
+
+    def call():
+        mhc.fused_step(dev["x"], dev["f"], dev["pre"], dev["post"], dev["comb"], wp, dev["base"],
+                       dev["scale"], dev["gamma"], path="chunk", workspace=ws, **outs)
+
+    def snapshot():
+        return {k: v.clone() for k, v in outs.items()}
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()                      # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for i in (0, 1, 0):
+        src = {k: to_dev(cases[i][k]) for k in ("x", "f", "pre", "post", "comb")}
+        for k, v in src.items():
+            dev[k].copy_(v)
+        torch.cuda.synchronize()
+        for o in outs.values():
+            o.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        got = snapshot()
+        junk = torch.randn(1 << 20, device="cuda").sum()   # eager work between replays
+        call()                                              # the eager reference
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
+        for k, v in snapshot().items():
+            assert torch.equal(got[k], v), (i, k)
+        assert mhc.split_status(ws) == 0
+        ref = dict(cases[0])   # the captured parameters, case i's streams and coefficients
+        ref.update({k: cases[i][k] for k in ("x", "f", "pre", "post", "comb")})
+        check_step(ref, {"x_out": got["x_out"].cpu(), "y": got["y_out"].cpu(),
+                              "pre": got["pre_out"].cpu(), "post": got["post_out"].cpu(),
+                              "comb": got["comb_out"].cpu(), "mix": got["mix_out"].cpu()}, "bf16")
