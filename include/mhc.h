@@ -58,7 +58,7 @@ typedef enum mhc_dtype { MHC_F32 = 0, MHC_BF16 = 1 } mhc_dtype;
 /*
  * Kernel family of mhc_fused_step and mhc_mixes:
  *   MHC_PATH_AUTO   no workspace: the tile kernel. With a workspace: the
- *                   chunked kernels up to MHC_CHUNK_AUTO_TOKENS (1024) tokens,
+ *                   chunked kernels up to MHC_CHUNK_AUTO_TOKENS (2048) tokens,
  *                   the feature-split kernel above, each where it applies
  *                   (else the other, else the tile kernel).
  *   MHC_PATH_TILE   the tile kernel (one workgroup per 16 tokens, no

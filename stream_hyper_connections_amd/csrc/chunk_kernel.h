@@ -39,9 +39,13 @@ inline int64_t chunk_workspace_bytes(int nchunks, int64_t tokens) {
 }
 
 // One pair of steps (A = sa, B = sa + 1) of a chunk: the order of pair_body,
-// with h stored to y_out instead of LDS.
+// with h stored to y_out instead of LDS, and the next pair's streams (pair
+// sn) loaded only when there is one (`more`, uniform across the wave: with
+// one pair per wave, as at d = 5120, a reload would only delay the in-order
+// wait on step B's operands).
 template <int MODE>
-__device__ __forceinline__ void chunk_pair(int sa, int sn, Ctx& c, Half& ha, Half& hb) {
+__device__ __forceinline__ void chunk_pair(int sa, int sn, bool more, Ctx& c, Half& ha,
+                                           Half& hb) {
   u32x4 w[4][kTiles];
   u32x4 xa[4], xb[4];
 
@@ -49,7 +53,7 @@ __device__ __forceinline__ void chunk_pair(int sa, int sn, Ctx& c, Half& ha, Hal
   __builtin_amdgcn_sched_barrier(0);
   const u32x4 h_a = valu_core<MODE>(ha, xa, c);
   __builtin_amdgcn_sched_barrier(0);
-  load_half<MODE>(ha, c, sn);
+  if (more) load_half<MODE>(ha, c, sn);
   __builtin_amdgcn_sched_barrier(0);
   mfma_step(xa, w, c);
   __builtin_amdgcn_sched_barrier(0);
@@ -58,7 +62,7 @@ __device__ __forceinline__ void chunk_pair(int sa, int sn, Ctx& c, Half& ha, Hal
   __builtin_amdgcn_sched_barrier(0);
   const u32x4 h_b = valu_core<MODE>(hb, xb, c);
   __builtin_amdgcn_sched_barrier(0);
-  load_half<MODE>(hb, c, sn + 1);
+  if (more) load_half<MODE>(hb, c, sn + 1);
   if (MODE == kFused) {
     const uint32_t col = (uint32_t)sa * 64;
 #pragma unroll
@@ -139,8 +143,7 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(StepArgs a, int nchunks
   }
   for (int p = 0; p < cnt; ++p) {
     const int sa = 2 * (pair0 + wave + kWaves * p);
-    const int sn = p + 1 < cnt ? sa + 2 * kWaves : sa;   // next pair (clamped to this one)
-    chunk_pair<MODE>(sa, sn, c, ha, hb);
+    chunk_pair<MODE>(sa, sa + 2 * kWaves, p + 1 < cnt, c, ha, hb);
   }
 
   // sums of squares over the four lane groups, then the waves' partials to LDS

@@ -910,12 +910,15 @@ __device__ __forceinline__ void mfma_step(const u32x4 (&xo)[4], const u32x4 (&w)
   }
 }
 
-// One pair of steps (A = 2P, B = 2P + 1), prefetching the next pair's streams.
+// One pair of steps (A = 2P, B = 2P + 1), prefetching the next pair's streams
+// when the wave has one in this tile (the branch is uniform across the wave;
+// the next tile's first pair is loaded by the tile set-up).
 template <int MODE>
 __device__ __forceinline__ void pair_body(int p, int cnt, int wave, Ctx& c, Smem& sm, int lane,
                                           Half& ha, Half& hb) {
   const int sa = 2 * (wave + kWaves * p);
-  const int sn = p + 1 < cnt ? sa + 2 * kWaves : sa;   // next pair (clamped to this one)
+  const bool more = p + 1 < cnt;
+  const int sn = sa + 2 * kWaves;   // the next pair
   u32x4 w[4][kTiles];
   u32x4 xa[4], xb[4];
 
@@ -923,7 +926,7 @@ __device__ __forceinline__ void pair_body(int p, int cnt, int wave, Ctx& c, Smem
   __builtin_amdgcn_sched_barrier(0);
   valu_step<MODE>(ha, xa, c, sm, sa, lane, 0);
   __builtin_amdgcn_sched_barrier(0);
-  load_half<MODE>(ha, c, sn);
+  if (more) load_half<MODE>(ha, c, sn);
   __builtin_amdgcn_sched_barrier(0);
   mfma_step(xa, w, c);
   __builtin_amdgcn_sched_barrier(0);
@@ -932,7 +935,7 @@ __device__ __forceinline__ void pair_body(int p, int cnt, int wave, Ctx& c, Smem
   __builtin_amdgcn_sched_barrier(0);
   valu_step<MODE>(hb, xb, c, sm, sa + 1, lane, 1);
   __builtin_amdgcn_sched_barrier(0);
-  load_half<MODE>(hb, c, sn + 1);
+  if (more) load_half<MODE>(hb, c, sn + 1);
   if (MODE == kFused) {
     const uint32_t col = (uint32_t)sa * 64;
 #pragma unroll
@@ -1445,12 +1448,12 @@ mhc_status launch_split(const StepArgs& a, void* ws, const SplitCfg& cfg, int mo
 #define MHC_CHUNK_PAIRS 8
 #endif
 // Largest call that path "auto" runs on the chunked kernels (when a workspace
-// is given); larger calls take the feature-split kernel. At d = 5120 the two
-// kernels' device time (the split kernel with its cooperative-launch gaps)
-// is about 14 + 0.046 T and 42 + 0.022 T microseconds: equal near 1,150
-// tokens.
+// is given); larger calls take the feature-split kernel. At d = 5120 the
+// two routes' call time (cache-flushed medians; the split route with its
+// cooperative-launch gaps) is about 16.5 + 0.0355 T and 45.6 + 0.0243 T
+// microseconds: equal near 2,600 tokens.
 #ifndef MHC_CHUNK_AUTO_TOKENS
-#define MHC_CHUNK_AUTO_TOKENS 1024
+#define MHC_CHUNK_AUTO_TOKENS 2048
 #endif
 constexpr int64_t kChunkMaxTokens = 8192;
 

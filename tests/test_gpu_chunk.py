@@ -68,8 +68,8 @@ def test_chunk_parity(d, t):
 
 def test_auto_route_by_size():
     assert mhc.fused_step_route("auto", 256, 5120, "bf16") == "chunk"
-    assert mhc.fused_step_route("auto", 1024, 5120, "bf16") == "chunk"
-    assert mhc.fused_step_route("auto", 1025, 5120, "bf16") == "split"
+    assert mhc.fused_step_route("auto", 2048, 5120, "bf16") == "chunk"
+    assert mhc.fused_step_route("auto", 2049, 5120, "bf16") == "split"
     assert mhc.fused_step_route("auto", 65536, 5120, "bf16") == "split"
     assert mhc.fused_step_route("auto", 256, 5120, "bf16", with_workspace=False) == "tile"
     assert mhc.fused_step_route("auto", 256, 5120, "f32") == "tile"
