@@ -154,8 +154,10 @@ STEP_CASES = [
 ]
 
 
-# path "tile" always runs the tile kernels; "auto" takes the feature-split
-# kernel where it applies (bf16, d = 5120 here) and the tile kernels otherwise
+# path "tile" always runs the tile kernels; "auto" (with a workspace) takes the
+# chunked kernels for these small bf16 calls where they apply (d <= 5120 with
+# an even number of 32-feature steps), the feature-split kernel for d = 6144,
+# and the tile kernels otherwise
 @pytest.mark.parametrize("path", ["tile", "auto"])
 @pytest.mark.parametrize("dtype,d,t", STEP_CASES)
 def test_fused_step_parity(dtype, d, t, path):
