@@ -58,9 +58,9 @@ typedef enum mhc_dtype { MHC_F32 = 0, MHC_BF16 = 1 } mhc_dtype;
 /*
  * Kernel family of mhc_fused_step and mhc_mixes:
  *   MHC_PATH_AUTO   no workspace: the tile kernel. With a workspace: the
- *                   chunked kernels up to MHC_CHUNK_AUTO_TOKENS (2048) tokens,
- *                   the feature-split kernel above, each where it applies
- *                   (else the other, else the tile kernel).
+ *                   chunked kernels up to MHC_CHUNK_AUTO_TOKENS (2048) tokens
+ *                   where they apply, else the feature-split kernel where it
+ *                   applies, else the tile kernel.
  *   MHC_PATH_TILE   the tile kernel (one workgroup per 16 tokens, no
  *                   workspace; the workspace argument is ignored).
  *   MHC_PATH_SPLIT  the feature-split kernel (needs a workspace;
@@ -121,9 +121,10 @@ mhc_status mhc_pack_wmix(const float* w_mix, int32_t d, int32_t dtype, void* w_p
  *     (d = 2048 ... 10240, e.g. 5120 = 40 x 128), on a device with at least ns
  *     compute units and cooperative launch support. About 17 MB for d = 5120
  *     on 256 CUs, plus 96 bytes per token for the mixes rows.
- *   - Chunked kernels: MHC_BF16 streams, d a multiple of 64 up to 5120, at
- *     most 8192 tokens. 256 bytes plus 128 bytes per token and chunk of 512
- *     features (1,280 bytes per token at d = 5120).
+ *   - Chunked kernels: at most 8192 tokens; MHC_BF16 streams with d a
+ *     multiple of 64 up to 5120, or MHC_F32 streams. 256 bytes plus 128
+ *     bytes per token and chunk of 512 features (1,280 bytes per token at
+ *     d = 5120).
  */
 int64_t mhc_fused_step_workspace_bytes(int64_t tokens, int32_t d, int32_t dtype);
 

@@ -1,5 +1,7 @@
-// Chunked small-batch path (bf16 streams, d a multiple of 64, d <= 5120): the
-// fused step, or the mixes alone, as two plain kernel launches.
+// Chunked small-batch path: the fused step, or the mixes alone, as two plain
+// kernel launches (bf16 streams with d a multiple of 64 up to 5120, on the
+// pipelined tile kernel's steps; f32 streams with any d, on the generic
+// kernel's steps).
 //
 // Included by mhc.hip (one translation unit) after the pipelined tile kernel,
 // whose per-step pieces (stream and operand loads, hc_post / hc_pre / sums of
@@ -188,8 +190,103 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(StepArgs a, int nchunks
   }
 }
 
-// Grid: tokens workgroups of 256 threads.
+// f32 streams: workgroup (tile, chunk) = 16 tokens x `csteps` 32-feature steps,
+// wave w taking the chunk's steps w, w + 8, ... with the generic kernel's step
+// (step_f: hc_post, the projection on v_mfma_f32_16x16x4_f32 from the float32
+// weights, sums of squares, hc_pre; h parked in y_out as float32), then the
+// same partial rows as chunk_kernel (one projection term).
+// Grid: ceil(tokens / 16) * nchunks workgroups of kThreads; nchunks * csteps
+// covers the d / 32 steps of the row.
 template <int MODE>
+__global__ __launch_bounds__(kThreads) void chunk_f32_kernel(StepArgs a, int nchunks, int csteps,
+                                                             char* __restrict__ ws) {
+  constexpr int kColsF = 16 * kTilesF;
+  __shared__ float acc_s[kWaves][kTok][kColsF];
+  __shared__ float ss_s[kWaves][kTok];
+  __shared__ float hs_s[kWaves][kTok];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tr = lane & 15;
+  const int g = lane >> 4;
+  const int d = a.d;
+  const int nsteps = d / kStep;
+  const int tile = blockIdx.x / nchunks;
+  const int chunk = blockIdx.x - tile * nchunks;
+  const int s0 = chunk * csteps;
+  const int ns = min(csteps, nsteps - s0);
+  const int cnt = wave < ns ? (ns - wave + kWaves - 1) / kWaves : 0;
+  if (blockIdx.x == 0 && tid == 0) *reinterpret_cast<uint32_t*>(ws) = 0u;
+
+  const int64_t t0 = (int64_t)tile * kTok;
+  const int64_t t = t0 + tr;
+  const bool valid = t < a.tokens;
+  const int64_t tc = valid ? t : 0;   // rows of tokens past the end are never read
+  LaneState<kTilesF> st;
+#pragma unroll
+  for (int q = 0; q < kTilesF; ++q) st.acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.ss = 0.f;
+  st.hs = 0.f;
+  if (MODE == kFused) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 c = *reinterpret_cast<const f32x4*>(a.comb_in + tc * 16 + 4 * j);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) st.C[j][k] = valid ? c[k] : 0.f;
+    }
+    const f32x4 u = *reinterpret_cast<const f32x4*>(a.post_in + tc * 4);
+    const f32x4 p = *reinterpret_cast<const f32x4*>(a.pre_in + tc * 4);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      st.U[k] = valid ? u[k] : 0.f;
+      st.P[k] = valid ? p[k] : 0.f;
+    }
+  }
+  const float* xrow = static_cast<const float*>(a.x) + tc * kStreams * (int64_t)d;
+  const float* frow = MODE == kFused ? static_cast<const float*>(a.f) + tc * (int64_t)d : nullptr;
+  float* xorow = MODE == kFused ? static_cast<float*>(a.x_out) + tc * kStreams * (int64_t)d : nullptr;
+  float* yrow = MODE == kFused ? static_cast<float*>(a.y_out) + tc * (int64_t)d : nullptr;
+  const u32x4* wpk = static_cast<const u32x4*>(a.wpk);
+  const size_t wstride = (size_t)kStreams * kTilesF * 64 * 2;   // u32x4 per step
+
+  InF cur, nxt;
+  if (cnt > 0) load_f<MODE>(cur, xrow, frow, d, (s0 + wave) * kStep + g * 8, valid);
+  for (int i = 0; i < cnt; ++i) {
+    const int s = s0 + wave + kWaves * i;
+    const int f0 = s * kStep + g * 8;
+    if (i + 1 < cnt) load_f<MODE>(nxt, xrow, frow, d, f0 + kWaves * kStep, valid);
+    step_f<MODE>(cur, st, wpk + (size_t)s * wstride, lane, xorow, yrow, d, f0, valid);
+    if (i + 1 < cnt) cur = nxt;
+  }
+
+  float ss = st.ss, hs = st.hs;
+  ss += __shfl_xor(ss, 16);
+  ss += __shfl_xor(ss, 32);
+  hs += __shfl_xor(hs, 16);
+  hs += __shfl_xor(hs, 32);
+  if (g == 0) {
+    ss_s[wave][tr] = ss;
+    hs_s[wave][tr] = hs;
+  }
+#pragma unroll
+  for (int q = 0; q < kTilesF; ++q)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc_s[wave][4 * g + r][16 * q + tr] = st.acc[q][r];
+  __syncthreads();
+
+  const int tt = tid >> 5, j = tid & 31;
+  float v = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w)
+    v += j < kMix ? acc_s[w][tt][j] : (j == kMix ? ss_s[w][tt] : (j == kMix + 1 ? hs_s[w][tt] : 0.f));
+  if (t0 + tt < a.tokens) {
+    float* part = reinterpret_cast<float*>(ws + kChunkHeader);
+    part[((int64_t)chunk * a.tokens + t0 + tt) * kPart + j] = v;
+  }
+}
+
+// Grid: tokens workgroups of 256 threads. DT: the stream dtype of h / y.
+template <int MODE, int DT>
 __global__ __launch_bounds__(256) void chunk_finish_kernel(StepArgs a, int nchunks,
                                                            const char* __restrict__ ws) {
   const int64_t t = blockIdx.x;
@@ -227,8 +324,20 @@ __global__ __launch_bounds__(256) void chunk_finish_kernel(StepArgs a, int nchun
   }
   if (MODE == kFused) {
     const float rh = rsqrtf(hsum / (float)a.d + a.norm_eps);
-    u32x4* y = reinterpret_cast<u32x4*>(static_cast<char*>(a.y_out) + t * a.d * 2);
-    for (int u = tid; u < a.d / 8; u += 256) y[u] = norm_bf(y[u], a.gamma, 8 * u, rh);
+    if (DT == MHC_BF16) {
+      u32x4* y = reinterpret_cast<u32x4*>(static_cast<char*>(a.y_out) + t * a.d * 2);
+      for (int u = tid; u < a.d / 8; u += 256) y[u] = norm_bf(y[u], a.gamma, 8 * u, rh);
+    } else {   // y = gamma * (h * rh), as the generic kernel
+      f32x4* y = reinterpret_cast<f32x4*>(static_cast<float*>(a.y_out) + t * a.d);
+      for (int u = tid; u < a.d / 4; u += 256) {
+        const f32x4 h = y[u];
+        const f32x4 gv = *reinterpret_cast<const f32x4*>(a.gamma + 4 * u);
+        f32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = gv[e] * (h[e] * rh);
+        y[u] = o;
+      }
+    }
   }
 }
 

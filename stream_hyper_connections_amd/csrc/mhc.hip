@@ -1440,10 +1440,11 @@ mhc_status launch_split(const StepArgs& a, void* ws, const SplitCfg& cfg, int mo
   return launch_status("split/Sinkhorn tail kernel launch");
 }
 
-// Chunked small-batch path: bf16 streams with an even number of 32-feature
-// steps, at most the pipelined kernel's 160, and at most kChunkMaxTokens
-// tokens (the partial rows take 128 bytes per token and chunk). Chunks of
-// MHC_CHUNK_PAIRS pairs of steps (one pair per wave).
+// Chunked small-batch path, at most kChunkMaxTokens tokens (the partial rows
+// take 128 bytes per token and chunk): bf16 streams with an even number of
+// 32-feature steps, at most the pipelined kernel's 160, in chunks of
+// MHC_CHUNK_PAIRS pairs of steps (one pair per wave); f32 streams with any
+// number of steps, in chunks of 16 steps (two per wave).
 #ifndef MHC_CHUNK_PAIRS
 #define MHC_CHUNK_PAIRS 8
 #endif
@@ -1457,39 +1458,59 @@ mhc_status launch_split(const StepArgs& a, void* ws, const SplitCfg& cfg, int mo
 #endif
 constexpr int64_t kChunkMaxTokens = 8192;
 
+constexpr int kChunkStepsF = 16;
+
 struct ChunkCfg {
   int nchunks = 0;
-  int cpairs = 0;
+  int per = 0;     // pairs of steps (bf16) or steps (f32) per chunk
+  int32_t dtype = MHC_BF16;
 };
 
 ChunkCfg chunk_config(int32_t dtype, int32_t d, int64_t tokens) {
   const int nsteps = d / kStep;
-  if (dtype != MHC_BF16 || d % kStep != 0 || nsteps % 2 != 0 || nsteps > pipe::kMaxSteps ||
-      tokens > kChunkMaxTokens)
-    return ChunkCfg{};
-  const int npairs = nsteps / 2;
-  const int cp = std::min(MHC_CHUNK_PAIRS, npairs);
-  return ChunkCfg{(npairs + cp - 1) / cp, cp};
+  if (d <= 0 || d % kStep != 0 || tokens > kChunkMaxTokens) return ChunkCfg{};
+  if (dtype == MHC_BF16) {
+    if (nsteps % 2 != 0 || nsteps > pipe::kMaxSteps) return ChunkCfg{};
+    const int npairs = nsteps / 2;
+    const int cp = std::min(MHC_CHUNK_PAIRS, npairs);
+    return ChunkCfg{(npairs + cp - 1) / cp, cp, dtype};
+  }
+  if (dtype == MHC_F32) {
+    const int cs = std::min(kChunkStepsF, nsteps);
+    return ChunkCfg{(nsteps + cs - 1) / cs, cs, dtype};
+  }
+  return ChunkCfg{};
 }
 
 mhc_status launch_chunk(const StepArgs& a, void* ws, const ChunkCfg& cc, int mode,
                         hipStream_t stream) {
   const unsigned grid = (unsigned)(((a.tokens + kTok - 1) / kTok) * cc.nchunks);
+  const dim3 blk(pipe::kThreads), tok((unsigned)a.tokens);
   char* w = static_cast<char*>(ws);
-  if (mode == kFused)
-    hipLaunchKernelGGL(pipe::chunk_kernel<kFused>, dim3(grid), dim3(pipe::kThreads), 0, stream, a,
-                       cc.nchunks, cc.cpairs, w);
+  const bool bf = cc.dtype == MHC_BF16, full = mode == kFused;
+  if (bf && full)
+    hipLaunchKernelGGL(pipe::chunk_kernel<kFused>, dim3(grid), blk, 0, stream, a, cc.nchunks,
+                       cc.per, w);
+  else if (bf)
+    hipLaunchKernelGGL(pipe::chunk_kernel<kMixesOnly>, dim3(grid), blk, 0, stream, a, cc.nchunks,
+                       cc.per, w);
+  else if (full)
+    hipLaunchKernelGGL(pipe::chunk_f32_kernel<kFused>, dim3(grid), blk, 0, stream, a, cc.nchunks,
+                       cc.per, w);
   else
-    hipLaunchKernelGGL(pipe::chunk_kernel<kMixesOnly>, dim3(grid), dim3(pipe::kThreads), 0, stream,
-                       a, cc.nchunks, cc.cpairs, w);
+    hipLaunchKernelGGL(pipe::chunk_f32_kernel<kMixesOnly>, dim3(grid), blk, 0, stream, a,
+                       cc.nchunks, cc.per, w);
   mhc_status s = launch_status("chunk kernel launch");
   if (s != MHC_OK) return s;
-  if (mode == kFused)
-    hipLaunchKernelGGL(pipe::chunk_finish_kernel<kFused>, dim3((unsigned)a.tokens), dim3(256), 0,
-                       stream, a, cc.nchunks, w);
+  if (bf && full)
+    hipLaunchKernelGGL((pipe::chunk_finish_kernel<kFused, MHC_BF16>), tok, dim3(256), 0, stream, a,
+                       cc.nchunks, w);
+  else if (full)
+    hipLaunchKernelGGL((pipe::chunk_finish_kernel<kFused, MHC_F32>), tok, dim3(256), 0, stream, a,
+                       cc.nchunks, w);
   else
-    hipLaunchKernelGGL(pipe::chunk_finish_kernel<kMixesOnly>, dim3((unsigned)a.tokens), dim3(256),
-                       0, stream, a, cc.nchunks, w);
+    hipLaunchKernelGGL((pipe::chunk_finish_kernel<kMixesOnly, MHC_BF16>), tok, dim3(256), 0,
+                       stream, a, cc.nchunks, w);
   return launch_status("chunk finish kernel launch");
 }
 
@@ -1526,8 +1547,7 @@ mhc_status pick_route(int32_t path, const void* workspace, int64_t tokens, const
       return MHC_OK;
     case MHC_PATH_AUTO:
       if (workspace == nullptr) *r = Route::kTile;
-      else if (rn.chunk_bytes > 0 && (tokens <= MHC_CHUNK_AUTO_TOKENS || rn.split_bytes == 0))
-        *r = Route::kChunk;
+      else if (rn.chunk_bytes > 0 && tokens <= MHC_CHUNK_AUTO_TOKENS) *r = Route::kChunk;
       else if (rn.split_bytes > 0) *r = Route::kSplit;
       else *r = Route::kTile;
       return MHC_OK;

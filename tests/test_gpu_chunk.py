@@ -26,9 +26,13 @@ def _log(msg):
     print(msg, flush=True)
 
 
-def _ws(t, d):
-    return torch.empty(mhc.fused_step_workspace_bytes(t, d, "bf16"), dtype=torch.uint8,
+def _ws_dt(t, d, dtype):
+    return torch.empty(mhc.fused_step_workspace_bytes(t, d, dtype), dtype=torch.uint8,
                        device="cuda")
+
+
+def _ws(t, d):
+    return _ws_dt(t, d, "bf16")
 
 
 def _run(case, **kw):
@@ -66,17 +70,54 @@ def test_chunk_parity(d, t):
     _log(f"  ties in new streams: {o['n_ties']}")
 
 
+# f32 streams: chunks of 16 steps, two per wave
+CHUNK_CASES_F32 = [
+    (5120, 64),      # the tiny workload's shape: ten chunks
+    (5120, 1),
+    (5120, 17),
+    (96, 10),        # three steps: one chunk, waves 3..7 idle
+    (544, 33),       # 17 steps: a chunk of 16 and a chunk of one
+    (2048, 300),
+]
+
+
+@pytest.mark.parametrize("d,t", CHUNK_CASES_F32)
+def test_chunk_parity_f32(d, t):
+    _log(f"chunk f32 d={d} T={t}")
+    w = wl.Workload(740 + d % 83 + t % 5, "chunk_f32", t, d, "f32")
+    case = make_case(w)
+    ws = _ws_dt(t, d, "f32")
+    out, _ = run_step(case, dtype="f32", path="chunk", workspace=ws)
+    assert mhc.split_status(ws) == 0
+    check_step(case, out, "f32")
+
+
+def test_chunk_f32_matches_tile_kernel():
+    t, d = 70, 1024
+    case = make_case(wl.Workload(747, "chunk_f32_vs_tile", t, d, "f32"))
+    a, _ = run_step(case, dtype="f32", path="chunk", workspace=_ws_dt(t, d, "f32"))
+    b, _ = run_step(case, dtype="f32", path="tile")
+    assert torch.equal(a["x_out"], b["x_out"])   # same per-element arithmetic
+    np.testing.assert_allclose(a["y"].numpy(), b["y"].numpy(), rtol=1e-5, atol=1e-6)
+    for k in ("pre", "post", "comb", "mix"):
+        np.testing.assert_allclose(a[k].numpy(), b[k].numpy(), rtol=0, atol=2e-5)
+
+
 def test_auto_route_by_size():
     assert mhc.fused_step_route("auto", 256, 5120, "bf16") == "chunk"
     assert mhc.fused_step_route("auto", 2048, 5120, "bf16") == "chunk"
     assert mhc.fused_step_route("auto", 2049, 5120, "bf16") == "split"
     assert mhc.fused_step_route("auto", 65536, 5120, "bf16") == "split"
     assert mhc.fused_step_route("auto", 256, 5120, "bf16", with_workspace=False) == "tile"
-    assert mhc.fused_step_route("auto", 256, 5120, "f32") == "tile"
+    assert mhc.fused_step_route("auto", 256, 5120, "f32") == "chunk"
+    assert mhc.fused_step_route("auto", 2049, 5120, "f32") == "tile"
+    assert mhc.fused_step_route("auto", 64, 96, "f32") == "chunk"
+    # bf16 widths without a slice geometry take the tile kernel above 2,048 tokens
+    assert mhc.fused_step_route("auto", 4096, 1024, "bf16") == "tile"
     # d = 6144 has a slice geometry but is beyond the chunked kernels' 5120
     assert mhc.fused_step_route("auto", 256, 6144, "bf16") == "split"
     assert mhc.fused_step_route("chunk", 8192, 5120, "bf16") == "chunk"
-    for args in ((8193, 5120, "bf16"), (64, 6144, "bf16"), (64, 5120, "f32"), (64, 96, "bf16")):
+    for args in ((8193, 5120, "bf16"), (64, 6144, "bf16"), (8193, 64, "f32"), (64, 96, "bf16")):
         with pytest.raises(ValueError, match="does not apply"):
             mhc.fused_step_route("chunk", *args)
 
@@ -174,19 +215,21 @@ def test_chunk_workspace_validation():
         mhc.fused_step(*args, path="chunk", workspace=big[16:])
 
 
-@pytest.mark.parametrize("d,t", [(5120, 256), (5120, 2000), (1024, 37), (5056, 19)])
-def test_mixes_chunk_mode_parity(d, t):
-    w = wl.Workload(770 + t % 11, "mixes_chunk", t, d, "bf16")
+@pytest.mark.parametrize("dtype,d,t", [("bf16", 5120, 256), ("bf16", 5120, 2000),
+                                        ("bf16", 1024, 37), ("bf16", 5056, 19),
+                                        ("f32", 5120, 64), ("f32", 544, 21)])
+def test_mixes_chunk_mode_parity(dtype, d, t):
+    w = wl.Workload(770 + t % 11, "mixes_chunk", t, d, dtype)
     x = wl.streams(w)
     p = wl.params(w)
-    wp = mhc.pack_wmix(to_dev(p["w_mix"]), "bf16")
-    ws = _ws(t, d)
+    wp = mhc.pack_wmix(to_dev(p["w_mix"]), dtype)
+    ws = _ws_dt(t, d, dtype)
     dx = to_dev(x)
     out = mhc.mixes(dx, wp, to_dev(p["base"]), to_dev(p["scale"]), want_mix=True, path="chunk",
                     workspace=ws)
     torch.cuda.synchronize()
     assert mhc.split_status(ws) == 0
-    check_mixes(dict(x=x, **p), {k: v.cpu() for k, v in out.items()}, "bf16")
+    check_mixes(dict(x=x, **p), {k: v.cpu() for k, v in out.items()}, dtype)
     tile = mhc.mixes(dx, wp, to_dev(p["base"]), to_dev(p["scale"]), want_mix=True, path="tile")
     for k in ("pre", "post", "comb", "mix"):
         np.testing.assert_allclose(out[k].cpu().numpy(), tile[k].cpu().numpy(), rtol=0,

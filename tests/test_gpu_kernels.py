@@ -155,9 +155,9 @@ STEP_CASES = [
 
 
 # path "tile" always runs the tile kernels; "auto" (with a workspace) takes the
-# chunked kernels for these small bf16 calls where they apply (d <= 5120 with
-# an even number of 32-feature steps), the feature-split kernel for d = 6144,
-# and the tile kernels otherwise
+# chunked kernels for these small calls where they apply (f32, and bf16 with
+# d <= 5120 and an even number of 32-feature steps), the feature-split kernel
+# for d = 6144, and the tile kernels otherwise
 @pytest.mark.parametrize("path", ["tile", "auto"])
 @pytest.mark.parametrize("dtype,d,t", STEP_CASES)
 def test_fused_step_parity(dtype, d, t, path):
