@@ -169,3 +169,45 @@ def test_split_workspace_validation():
     with pytest.raises(ValueError, match="does not apply"):
         mhc.fused_step_route("split", t, 1024, "bf16")
     assert mhc.fused_step_route("auto", t, 1024, "bf16") == "chunk"
+
+
+def test_split_calls_on_two_streams_in_flight_together():
+    """Two feature-split calls issued on two streams before either is waited
+    for (each with its own workspace): the cooperative launches keep every
+    workgroup of a call resident together, so both complete (status word 0)
+    and match the same calls run one after the other, bit for bit."""
+    t, d = 9000, 5120
+    cases = [make_case(wl.Workload(460 + i, "split_streams", t, d, "bf16")) for i in range(2)]
+    devs = [{k: to_dev(c[k]) for k in ("x", "f", "pre", "post", "comb", "w_mix", "base",
+                                       "scale", "gamma")} for c in cases]
+    wps = [mhc.pack_wmix(dv["w_mix"], "bf16") for dv in devs]
+    wss = [torch.empty(mhc.fused_step_workspace_bytes(t, d, "bf16"), dtype=torch.uint8,
+                       device="cuda") for _ in range(2)]
+
+    def call(i):
+        dv = devs[i]
+        return mhc.fused_step(dv["x"], dv["f"], dv["pre"], dv["post"], dv["comb"], wps[i],
+                              dv["base"], dv["scale"], dv["gamma"], want_mix=True,
+                              path="split", workspace=wss[i])
+
+    ref = []
+    for i in range(2):
+        ref.append({k: v.clone() for k, v in call(i).items()})
+        torch.cuda.synchronize()
+        assert mhc.split_status(wss[i]) == 0
+    streams = [torch.cuda.Stream() for _ in range(2)]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for _ in range(3):                      # a few rounds of overlapping pairs
+        for i in range(2):
+            with torch.cuda.stream(streams[i]):
+                outs.append((i, call(i)))
+    for s in streams:
+        torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for i in range(2):
+        assert mhc.split_status(wss[i]) == 0, "a cross-workgroup wait gave up"
+    for i, o in outs:
+        for k in ref[i]:
+            assert torch.equal(o[k], ref[i][k]), (i, k)
