@@ -366,3 +366,42 @@ def test_backward_rejects_bad_arguments(over, status, needle):
 
 def test_backward_zero_tokens():
     assert _call_bwd(tokens=0) == binding.MHC_OK
+
+
+C_PROGRAM = r"""
+#include <stdio.h>
+#include <string.h>
+#include "mhc.h"
+
+int main(void) {
+  if (mhc_abi_version() != MHC_ABI_VERSION) return 1;
+  if (strcmp(mhc_status_string(MHC_OK), "MHC_OK") != 0) return 2;
+  if (mhc_wmix_packed_bytes(5120, MHC_BF16) != 160LL * 4 * 5 * 64 * 16) return 3;
+  if (mhc_fused_step_workspace_bytes(-1, 5120, MHC_BF16) != -1) return 4;
+  if (strstr(mhc_last_error(), "bad tokens") == NULL) return 5;
+  mhc_path p = MHC_PATH_CHUNK;
+  if (mhc_fused_step_route(9, 64, 5120, MHC_BF16, 0) != -1 || p != 3) return 6;
+  printf("ok %d\n", mhc_abi_version());
+  return 0;
+}
+"""
+
+
+def test_header_is_c_and_links(tmp_path):
+    """include/mhc.h compiles as C99 and a C program linked against libmhc.so
+    calls the entry points that need no device."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "abi.c"
+    src.write_text(C_PROGRAM)
+    exe = tmp_path / "abi"
+    libdir = os.path.dirname(binding.LIB_PATH)
+    cmd = ["gcc", "-std=c99", "-Wall", "-Werror", "-pedantic", "-I", os.path.dirname(HEADER),
+           str(src), "-o", str(exe), "-L", libdir, "-l:libmhc.so", f"-Wl,-rpath,{libdir}"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
+    run = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert run.returncode == 0, (run.returncode, run.stderr)
+    assert run.stdout.strip() == f"ok {binding.abi_version()}"
