@@ -660,8 +660,8 @@ __global__ __launch_bounds__(256) void wt_pack_kernel(const float* __restrict__ 
     if (slot < kMix) split3(w[(int64_t)slot * N * d + col], t3[0], t3[1], t3[2]);
     h[e] = term == 0 ? t3[0] : t3[1];
   }
-  out[v] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
-                 h[6] | (h[7] << 16)};
+  st16(out + v, u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                      h[6] | (h[7] << 16)});
 }
 
 // Barrier for LDS traffic only: waits for the wave's LDS operations, not for

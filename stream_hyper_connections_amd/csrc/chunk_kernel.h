@@ -324,18 +324,19 @@ __global__ __launch_bounds__(256) void chunk_finish_kernel(StepArgs a, int nchun
   }
   if (MODE == kFused) {
     const float rh = rsqrtf(hsum / (float)a.d + a.norm_eps);
+    // 128-bit stores through st16 / st4f (followed by the store guard)
     if (DT == MHC_BF16) {
       u32x4* y = reinterpret_cast<u32x4*>(static_cast<char*>(a.y_out) + t * a.d * 2);
-      for (int u = tid; u < a.d / 8; u += 256) y[u] = norm_bf(y[u], a.gamma, 8 * u, rh);
+      for (int u = tid; u < a.d / 8; u += 256) st16(y + u, norm_bf(ld16(y + u), a.gamma, 8 * u, rh));
     } else {   // y = gamma * (h * rh), as the generic kernel
-      f32x4* y = reinterpret_cast<f32x4*>(static_cast<float*>(a.y_out) + t * a.d);
+      float* y = static_cast<float*>(a.y_out) + t * a.d;
       for (int u = tid; u < a.d / 4; u += 256) {
-        const f32x4 h = y[u];
+        const f32x4 h = *reinterpret_cast<const f32x4*>(y + 4 * u);
         const f32x4 gv = *reinterpret_cast<const f32x4*>(a.gamma + 4 * u);
         f32x4 o;
 #pragma unroll
         for (int e = 0; e < 4; ++e) o[e] = gv[e] * (h[e] * rh);
-        y[u] = o;
+        st4f(y + 4 * u, o);
       }
     }
   }

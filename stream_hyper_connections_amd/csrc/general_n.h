@@ -102,13 +102,13 @@ __global__ __launch_bounds__(256) void pack_kernel(const float* __restrict__ w, 
     }
   }
   if (DT == MHC_BF16) {
-    out[idx] = u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
-                     pack_bf16x2(v[6], v[7])};
+    st16(out + idx, u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                          pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])});
   } else {
-    out[2 * idx] = u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
-                         __float_as_uint(v[3])};
-    out[2 * idx + 1] = u32x4{__float_as_uint(v[4]), __float_as_uint(v[5]),
-                             __float_as_uint(v[6]), __float_as_uint(v[7])};
+    st16(out + 2 * idx, u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]),
+                              __float_as_uint(v[2]), __float_as_uint(v[3])});
+    st16(out + 2 * idx + 1, u32x4{__float_as_uint(v[4]), __float_as_uint(v[5]),
+                                  __float_as_uint(v[6]), __float_as_uint(v[7])});
   }
 }
 

@@ -1161,8 +1161,8 @@ __global__ __launch_bounds__(256) void pack_bf16_kernel(const float* __restrict_
       v[e] = part == 0 ? hi : (part == 1 ? mid : r2);
     }
   }
-  out[idx] = u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
-                   pack_bf16x2(v[6], v[7])};
+  st16(out + idx, u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                        pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])});
 }
 
 // f32: one thread per (s, k, q, lane) copies the lane's 8 float32 weights
@@ -1189,8 +1189,8 @@ __global__ __launch_bounds__(256) void pack_f32_kernel(const float* __restrict__
       o1[e] = __float_as_uint(src[4 + e]);
     }
   }
-  out[2 * idx] = o0;
-  out[2 * idx + 1] = o1;
+  st16(out + 2 * idx, o0);
+  st16(out + 2 * idx + 1, o1);
 }
 
 // ----- host side ------------------------------------------------------------------------
