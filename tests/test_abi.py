@@ -405,3 +405,84 @@ def test_header_is_c_and_links(tmp_path):
     run = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
     assert run.returncode == 0, (run.returncode, run.stderr)
     assert run.stdout.strip() == f"ok {binding.abi_version()}"
+
+
+# ---- property-based check of the validation (fake addresses, no device) --------------
+
+from hypothesis import given, settings, strategies as st  # noqa: E402
+
+_PTRS = ("x", "f", "pre_in", "post_in", "comb_in", "w_packed", "base", "scale", "gamma",
+         "x_out", "y_out", "pre_out", "post_out", "comb_out")
+_OUTS = ("x_out", "y_out", "pre_out", "post_out", "comb_out", "mix_out")
+
+
+def _defects():
+    """Each defect makes the call invalid on its own; (kind, key, value)."""
+    p = _layout()
+    out = [("dtype", "dtype", v) for v in (-1, 2, 5, 100)]
+    out += [("tokens", "tokens", v) for v in (-1, -(1 << 40))]
+    out += [("d", "d", v) for v in (0, -32, 31, 48, 100)]
+    out += [("iters", "iters", v) for v in (0, -5)]
+    for k in ("norm_eps", "hc_eps"):
+        out += [(k, k, v) for v in (-1e-3, float("nan"), float("inf"), float("-inf"))]
+    out += [("null", k, None) for k in _PTRS]
+    out += [("align", k, p[k] + off) for k in _PTRS for off in (4, 8)]
+    # an output that starts inside another buffer (never the exact in-place x_out == x)
+    out += [("overlap", o, p[b] + 16) for o in _OUTS for b in ("x", "f", "comb_in", "y_out")
+            if o != b]
+    out += [("path", "path", v) for v in (-1, 4, 99)]
+    return out
+
+
+DEFECTS = _defects()
+
+
+@settings(max_examples=300, deadline=None)
+@given(st.lists(st.sampled_from(range(len(DEFECTS))), min_size=1, max_size=3, unique=True))
+def test_fused_step_rejects_any_invalid_combination(picks):
+    over = {}
+    for i in picks:
+        _, key, value = DEFECTS[i]
+        if key not in over:   # the first defect on a field wins
+            over[key] = value
+    st_code = _call(**over)
+    assert st_code == binding.MHC_ERR_INVALID_ARG, (over, st_code, binding.last_error())
+    assert binding.last_error() != ""
+
+
+@settings(max_examples=100, deadline=None)
+@given(st.integers(min_value=(1 << 35) + 1, max_value=1 << 50))
+def test_fused_step_rejects_token_counts_beyond_the_limit(tokens):
+    assert _call(tokens=tokens) == binding.MHC_ERR_UNSUPPORTED
+    assert "2^35" in binding.last_error()
+
+
+def _defects_n(n):
+    p = _layout_n(n)
+    ptrs = _PTRS + ("mix_out",)
+    out = [("dtype", "dtype", v) for v in (-1, 2, 5)]
+    out += [("tokens", "tokens", v) for v in (-1, -(1 << 40))]
+    out += [("d", "d", v) for v in (0, 31, 48)]
+    out += [("iters", "iters", v) for v in (0, -5)]
+    for k in ("norm_eps", "hc_eps"):
+        out += [(k, k, v) for v in (-1.0, float("nan"), float("inf"))]
+    out += [("null", k, None) for k in ptrs]
+    out += [("align", k, p[k] + 8) for k in ptrs]
+    out += [("overlap", o, p[b] + 16) for o in _OUTS for b in ("x", "f", "comb_in", "y_out")
+            if o != b]
+    return out
+
+
+@settings(max_examples=150, deadline=None)
+@given(st.sampled_from([2, 4, 8]), st.data())
+def test_fused_step_n_rejects_any_invalid_combination(n, data):
+    defects = _defects_n(n)
+    picks = data.draw(st.lists(st.sampled_from(range(len(defects))), min_size=1, max_size=3,
+                               unique=True))
+    over = {}
+    for i in picks:
+        _, key, value = defects[i]
+        over.setdefault(key, value)
+    st_code = _call_n(n, **over)
+    assert st_code == binding.MHC_ERR_INVALID_ARG, (n, over, st_code, binding.last_error())
+    assert binding.last_error() != ""
