@@ -78,6 +78,7 @@ CHUNK_CASES_F32 = [
     (96, 10),        # three steps: one chunk, waves 3..7 idle
     (544, 33),       # 17 steps: a chunk of 16 and a chunk of one
     (2048, 300),
+    (5120, 8192),    # the largest call the path takes
 ]
 
 
