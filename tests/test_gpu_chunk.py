@@ -70,13 +70,13 @@ def test_chunk_parity(d, t):
     _log(f"  ties in new streams: {o['n_ties']}")
 
 
-# f32 streams: chunks of 16 steps, two per wave
+# f32 streams: chunks of 8 steps, one per wave
 CHUNK_CASES_F32 = [
-    (5120, 64),      # the tiny workload's shape: ten chunks
+    (5120, 64),      # the tiny workload's shape: twenty chunks
     (5120, 1),
     (5120, 17),
     (96, 10),        # three steps: one chunk, waves 3..7 idle
-    (544, 33),       # 17 steps: a chunk of 16 and a chunk of one
+    (544, 33),       # 17 steps: two chunks of 8 and a chunk of one
     (2048, 300),
     (5120, 8192),    # the largest call the path takes
 ]

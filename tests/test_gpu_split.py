@@ -161,8 +161,8 @@ def test_split_workspace_validation():
     big = torch.empty(need + 512, dtype=torch.uint8, device="cuda")
     with pytest.raises(mhc.MhcError, match="256-byte aligned"):
         mhc.fused_step(*args, path="split", workspace=big[16:])
-    # f32 streams: only the chunked kernels (chunks of 16 steps) take a workspace
-    assert mhc.fused_step_workspace_bytes(t, 5120, "f32") == 256 + 10 * t * 128
+    # f32 streams: only the chunked kernels (chunks of 8 steps) take a workspace
+    assert mhc.fused_step_workspace_bytes(t, 5120, "f32") == 256 + 20 * t * 128
     assert mhc.fused_step_workspace_bytes(t, 7168, "bf16") == 0
     # d = 1024 has no slice geometry: only the chunked kernels take a workspace
     assert mhc.fused_step_workspace_bytes(t, 1024, "bf16") == 256 + 2 * t * 128
