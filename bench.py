@@ -18,6 +18,7 @@ workload on the host cores.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -185,8 +186,9 @@ def algorithmic_bytes_backward(tokens: int, d: int, elem: int, n: int) -> int:
 
 
 def backward_bench(w, steps, warmup):
-    """mhc_fused_step_backward_n at the workload's shape (n = 4): one JSON
-    line, HIP events around the call (all backward kernels)."""
+    """mhc_fused_step_backward_n at the workload's shape (its stream count, 4
+    unless --n says otherwise): one JSON line, HIP events around the call (all
+    backward kernels)."""
     import torch
     import stream_hyper_connections_amd as mhc
     from stream_hyper_connections_amd import workloads as wl
@@ -378,6 +380,8 @@ def parse():
     ap.add_argument("--backward", action="store_true",
                     help="time the backward of the step (mhc_fused_step_backward_n) at the "
                          "workload's shape; one JSON line")
+    ap.add_argument("--n", type=int, choices=(2, 4), default=None,
+                    help="stream count of --backward (default: the workload's, 4)")
     ap.add_argument("--all-configs", action="store_true",
                     help="latency of the fused step alone on every workload, warm and "
                          "cache-flushed (p50/p95/p99); one JSON line per workload")
@@ -590,6 +594,8 @@ def main():
         general_n_bench(w, args.steps, args.warmup)
         return
     if args.backward:
+        if args.n is not None:
+            w = dataclasses.replace(w, n=args.n)
         backward_bench(w, args.steps, args.warmup)
         return
     if args.all_configs:
