@@ -74,6 +74,19 @@ def test_workload_large_prefill_sampled():
     stats = comb_sum_stats(out["comb"])
     assert stats["col_dev_max"] <= 1e-5
     _log(f"large_prefill: {len(idx)} sampled tokens match; comb sums {stats}")
+    # the same inputs cut to a ragged last batch (511 whole 128-token batches
+    # and 37 tokens), in the same launch configuration
+    t2 = 511 * 128 + 37
+    sub = dict(case, x=case["x"][:t2], f=case["f"][:t2], pre=pre[:t2], post=post[:t2],
+               comb=comb[:t2])
+    out2, _ = run_step(sub)
+    idx2 = np.unique(np.concatenate([np.arange(8), np.arange(t2 - 64, t2),
+                                     rng.choice(t2, 120, replace=False)]))
+    check_step(_sub(sub, idx2), {k: (v[idx2] if v is not None else None)
+                                 for k, v in out2.items()}, "bf16")
+    for k in ("x_out", "y", "pre", "post", "comb", "mix"):   # tokens before the cut unchanged
+        assert torch.equal(out2[k][:t2 - 37], out[k][:t2 - 37]), k
+    _log(f"large_prefill cut to {t2} tokens: {len(idx2)} sampled tokens match")
 
 
 @pytest.mark.timeout(900)
