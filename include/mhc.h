@@ -23,8 +23,10 @@
  *     [j][k]; mixes [T][24] with slots 0-3 pre, 4-7 post, 8+4j+k comb; w_mix
  *     float32 [24][4*d] whose column k*d+f multiplies stream k, feature f.
  *   - Errors: argument problems return MHC_ERR_INVALID_ARG and configurations
- *     the kernels do not cover return MHC_ERR_UNSUPPORTED, both before any HIP
- *     call. A failing HIP launch returns MHC_ERR_HIP. mhc_last_error() then
+ *     the kernels do not cover return MHC_ERR_UNSUPPORTED, both before any
+ *     launch (the argument checks come before any HIP call; choosing a kernel
+ *     family may query the device's attributes, whose failure is
+ *     MHC_ERR_HIP). A failing HIP launch returns MHC_ERR_HIP. mhc_last_error() then
  *     describes the failure (per calling thread). tokens == 0 returns MHC_OK
  *     after the scalar checks, without examining pointers and without
  *     launching anything. NaN/Inf in the data propagate; they are not
