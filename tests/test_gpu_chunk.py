@@ -292,3 +292,15 @@ def test_chunk_path_replays_from_a_hip_graph():
         check_step(ref, {"x_out": got["x_out"].cpu(), "y": got["y_out"].cpu(),
                               "pre": got["pre_out"].cpu(), "post": got["post_out"].cpu(),
                               "comb": got["comb_out"].cpu(), "mix": got["mix_out"].cpu()}, "bf16")
+
+
+def test_chunk_without_mix_out():
+    """mix_out is optional: without it the chunked route writes every other
+    output exactly as with it."""
+    t, d = 100, 5120
+    case = make_case(wl.Workload(790, "chunk_nomix", t, d, "bf16"))
+    a, _ = _run(case)
+    b, _ = _run(case, want_mix=False)
+    assert b["mix"] is None
+    for k in ("x_out", "y", "pre", "post", "comb"):
+        assert torch.equal(a[k], b[k]), k
