@@ -237,11 +237,12 @@ def test_mixes_chunk_mode_parity(dtype, d, t):
                                    atol=2e-5)
 
 
-def test_chunk_path_replays_from_a_hip_graph():
-    """The chunked kernels are plain launches with no memory set: a call
-    captured into a graph replays to the eager result, with eager work and
-    synchronisation between the replays, and the replays follow new inputs
-    copied into the captured buffers."""
+@pytest.mark.parametrize("path", ["chunk", "split"])
+def test_path_replays_from_a_hip_graph(path):
+    """Both workspace routes set no memory from the host (the split route's
+    counters are cleared by a kernel): a call captured into a graph replays to
+    the eager result, with eager work and synchronisation between the replays,
+    and the replays follow new inputs copied into the captured buffers."""
     t, d = 256, 5120
     cases = [make_case(wl.Workload(780 + i, "chunk_graph", t, d, "bf16")) for i in range(2)]
     dev = {k: to_dev(cases[0][k]) for k in ("x", "f", "pre", "post", "comb", "w_mix", "base",
@@ -256,7 +257,7 @@ def test_chunk_path_replays_from_a_hip_graph():
 
     def call():
         mhc.fused_step(dev["x"], dev["f"], dev["pre"], dev["post"], dev["comb"], wp, dev["base"],
-                       dev["scale"], dev["gamma"], path="chunk", workspace=ws, **outs)
+                       dev["scale"], dev["gamma"], path=path, workspace=ws, **outs)
 
     def snapshot():
         return {k: v.clone() for k, v in outs.items()}
