@@ -356,6 +356,54 @@ def all_configs_bench(reps_min=50, min_ms=200.0, flush_bytes=512 << 20, path="au
         torch.cuda.empty_cache()
 
 
+def crossover_bench(d=5120, sizes=(512, 1024, 1536, 2048, 2560, 3072, 4096), calls=40, runs=5):
+    """mhc_fused_step on the chunked and the feature-split route for a range of
+    token counts (seeded random bf16 inputs of width d): per route and size,
+    `calls` calls back to back between two events, median over `runs` runs.
+    One JSON line per size; the routes' crossing point is where path "auto"
+    should switch."""
+    import torch
+    import stream_hyper_connections_amd as mhc
+    for t in sizes:
+        g = torch.Generator(device="cuda").manual_seed(t)
+        x = torch.randn((t, N, d), device="cuda", generator=g).bfloat16()
+        f = torch.randn((t, d), device="cuda", generator=g).bfloat16()
+        pre = torch.rand((t, N), device="cuda", generator=g)
+        post = torch.rand((t, N), device="cuda", generator=g)
+        comb = torch.rand((t, N, N), device="cuda", generator=g)
+        comb = comb / comb.sum(1, keepdim=True)
+        wp = mhc.pack_wmix(0.02 * torch.randn((24, N * d), device="cuda", generator=g), "bf16")
+        base = 0.1 * torch.randn(24, device="cuda", generator=g)
+        scale, gamma = torch.ones(3, device="cuda"), torch.ones(d, device="cuda")
+        ws = torch.empty(mhc.fused_step_workspace_bytes(t, d, "bf16"), dtype=torch.uint8,
+                         device="cuda")
+        outs = dict(x_out=torch.empty_like(x), y_out=torch.empty_like(f),
+                    pre_out=torch.empty_like(pre), post_out=torch.empty_like(post),
+                    comb_out=torch.empty_like(comb))
+        line = {"metric": "fused step call time by route, back to back", "tokens": t, "d": d,
+                "unit": "us per call", "auto_route": mhc.fused_step_route("auto", t, d, "bf16")}
+        for path in ("chunk", "split"):
+            def call():
+                mhc.fused_step(x, f, pre, post, comb, wp, base, scale, gamma, path=path,
+                               workspace=ws, **outs)
+            for _ in range(5):
+                call()
+            torch.cuda.synchronize()
+            per = []
+            for _ in range(runs):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                for _ in range(calls):
+                    call()
+                b.record()
+                b.synchronize()
+                per.append(a.elapsed_time(b) * 1e3 / calls)
+            if mhc.split_status(ws) != 0:
+                raise RuntimeError("a cross-workgroup wait of the feature-split kernel gave up")
+            line[path] = round(float(np.median(per)), 1)
+        print(json.dumps(line), flush=True)
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -385,6 +433,9 @@ def parse():
     ap.add_argument("--all-configs", action="store_true",
                     help="latency of the fused step alone on every workload, warm and "
                          "cache-flushed (p50/p95/p99); one JSON line per workload")
+    ap.add_argument("--crossover", action="store_true",
+                    help="call time of the chunked and feature-split routes from 512 to 4,096 "
+                         "tokens, back to back; one JSON line per size")
     ap.add_argument("--copy-ceiling", action="store_true",
                     help="time plain copies in the access patterns of the step's kernels "
                          "(libmhc_probe.so) at the workload's shape; one JSON line")
@@ -600,6 +651,9 @@ def main():
         return
     if args.all_configs:
         all_configs_bench(path=args.path)
+        return
+    if args.crossover:
+        crossover_bench()
         return
     if args.copy_ceiling:
         copy_ceiling(w, args.steps, args.warmup)
