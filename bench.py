@@ -263,8 +263,8 @@ def all_configs_bench(reps_min=50, min_ms=200.0, flush_bytes=512 << 20, path="au
     `flush_bytes` between calls, outside the timed events, so that the inputs
     are not served from the 256 MB Infinity Cache). One JSON line per workload
     with p50 / p95 / p99 in microseconds and tokens/s, GB/s and % of peak at
-    the p50; for routes of plain launches (chunked, tile) also the time per call
-    of 200 back-to-back replays of the call captured in a graph."""
+    the p50, and the time per call of 200 calls back to back, eager and as
+    replays of the call captured in a graph."""
     import torch
     import stream_hyper_connections_amd as mhc
     from stream_hyper_connections_amd import workloads as wl
@@ -327,29 +327,39 @@ def all_configs_bench(reps_min=50, min_ms=200.0, flush_bytes=512 << 20, path="au
                           "tokens_per_s": round(w.tokens / (p50 / 1e6), 1),
                           "GBps": round(alg / (p50 / 1e6) / 1e9, 1),
                           "frac_of_peak": round(alg / (p50 / 1e6) / 1e9 / HBM_PEAK_GBS, 4)}
-        if route in ("chunk", "tile"):
-            # plain launches only: the call captured once into a graph, then
-            # replayed back to back (a serving loop's view, no host issue time)
-            side = torch.cuda.Stream()
-            side.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(side):
+        # eager calls back to back (no synchronisation between calls)
+        per_call = []
+        for _ in range(5):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(200):
                 call()
-            torch.cuda.current_stream().wait_stream(side)
-            torch.cuda.synchronize()
-            graph = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(graph):
-                call()
-            per_call = []
-            for _ in range(5):
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record()
-                for _ in range(200):
-                    graph.replay()
-                b.record()
-                b.synchronize()
-                per_call.append(a.elapsed_time(b) * 1e3 / 200)
-            line["graph_replay_us_per_call"] = round(float(np.median(per_call)), 2)
-            del graph
+            b.record()
+            b.synchronize()
+            per_call.append(a.elapsed_time(b) * 1e3 / 200)
+        line["back_to_back_us_per_call"] = round(float(np.median(per_call)), 2)
+        # the call captured once into a graph, then replayed back to back
+        # (a serving loop's view, no host issue time)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            call()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            call()
+        per_call = []
+        for _ in range(5):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(200):
+                graph.replay()
+            b.record()
+            b.synchronize()
+            per_call.append(a.elapsed_time(b) * 1e3 / 200)
+        line["graph_replay_us_per_call"] = round(float(np.median(per_call)), 2)
+        del graph
         line["algorithmic_bytes"] = alg
         print(json.dumps(line), flush=True)
         del x, f, outs, prior
