@@ -191,11 +191,11 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(StepArgs a, int nchunks
 }
 
 // f32 streams: workgroup (tile, chunk) = 16 tokens x `csteps` 32-feature steps
-// (8 by default),
-// wave w taking the chunk's steps w, w + 8, ... with the generic kernel's step
-// (step_f: hc_post, the projection on v_mfma_f32_16x16x4_f32 from the float32
-// weights, sums of squares, hc_pre; h parked in y_out as float32), then the
-// same partial rows as chunk_kernel (one projection term).
+// (8 by default), wave w taking the chunk's steps w, w + 8, ... with the
+// generic kernel's step (step_f: hc_post, the projection on
+// v_mfma_f32_16x16x4_f32 from the float32 weights, sums of squares, hc_pre; h
+// parked in y_out as float32), then the same partial rows as chunk_kernel (one
+// projection term).
 // Grid: ceil(tokens / 16) * nchunks workgroups of kThreads; nchunks * csteps
 // covers the d / 32 steps of the row.
 template <int MODE>
