@@ -110,8 +110,9 @@ N_SWEEP = (2, 4, 8)
 def general_n_bench(w0, steps, warmup):
     """mhc_fused_step_n at the workload's shape for n = 2, 4, 8: one JSON line
     per n and kernel (HIP events around the call): the token-block kernel
-    ("block") for every n, and the feature-split kernel ("split", with its
-    workspace) where it applies; each followed by the split/Sinkhorn kernel."""
+    ("block") for every n, and the feature-split kernel ("split") and the
+    chunked block kernel ("chunk", up to 8192 tokens) where they apply, with a
+    workspace; each followed by the split/Sinkhorn kernel."""
     import dataclasses
     import torch
     import stream_hyper_connections_amd as mhc
@@ -135,10 +136,16 @@ def general_n_bench(w0, steps, warmup):
                     mix_out=torch.empty_like(prior["mix"]))
 
         paths = ["block"]
-        if mhc.fused_step_n_workspace_bytes(n, w.tokens, w.d, w.dtype) > 0:
-            paths.append("split")
+        for p in ("split", "chunk"):
+            try:
+                mhc.fused_step_route_n(n, p, w.tokens, w.d, w.dtype)
+                paths.append(p)
+            except ValueError:
+                pass
         kernels = {"block": "gen::block_kernel + gen::sinkhorn_kernel",
-                   "split": "fsn::split_kernel + gen::sinkhorn_kernel (feature-split)"}
+                   "split": "fsn::split_kernel + gen::sinkhorn_kernel (feature-split)",
+                   "chunk": "gen::block_kernel (chunked) + gen::chunk_finish_kernel + "
+                            "gen::sinkhorn_kernel"}
         for path in paths:
             def call():
                 mhc.fused_step_n(x, f, prior["pre"], prior["post"], prior["comb"], wp,

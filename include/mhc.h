@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define MHC_ABI_VERSION 7
+#define MHC_ABI_VERSION 8
 #define MHC_N_STREAMS 4
 #define MHC_N_MIX 24
 
@@ -266,14 +266,28 @@ mhc_status mhc_pack_wmix_n(int32_t n, const float* w_mix, int32_t d, int32_t dty
                            void* w_packed, int64_t packed_bytes, mhc_stream_t stream);
 
 /*
- * Workspace bytes of the feature-split kernel of mhc_fused_step_n and
- * mhc_mixes_n for (n, tokens, d, dtype) on the current device; 0 when that
- * kernel does not apply (it covers n in {2, 4} with bf16 streams, d = ns * S
- * with S a multiple of 64 of at most 256 (n = 2) or 128 (n = 4) features and
- * 16 <= ns <= 64 slices, at most one per compute unit, on a device with
- * cooperative launch); -1 for a bad argument.
+ * Workspace bytes that cover every workspace route of mhc_fused_step_n and
+ * mhc_mixes_n for (n, tokens, d, dtype) on the current device (the larger of
+ * the two below); 0 when neither applies; -1 for a bad argument.
+ *   - the feature-split kernel: n in {2, 4} with bf16 streams, d = ns * S with
+ *     S a multiple of 64 of at most 256 (n = 2) or 128 (n = 4) features and
+ *     16 <= ns <= 64 slices, at most one per compute unit, on a device with
+ *     cooperative launch;
+ *   - the chunked block kernel: tokens <= 8192, any n and dtype; 256 bytes plus
+ *     4 * R bytes per token and chunk, R = (2+n)n + 2 rounded up to a multiple
+ *     of 4, with up to 80 chunks of whole units (64 features for bf16 at
+ *     n <= 4, else 32) across d.
  */
 int64_t mhc_fused_step_n_workspace_bytes(int32_t n, int64_t tokens, int32_t d, int32_t dtype);
+
+/*
+ * mhc_fused_step_route_n -- the kernel family that mhc_fused_step_n and
+ * mhc_mixes_n run for `path` and these arguments: MHC_PATH_TILE (standing for
+ * the token-block kernel), MHC_PATH_SPLIT or MHC_PATH_CHUNK; -1 (see
+ * mhc_last_error) as for mhc_fused_step_route.
+ */
+int32_t mhc_fused_step_route_n(int32_t n, int32_t path, int64_t tokens, int32_t d, int32_t dtype,
+                               int32_t with_workspace);
 
 /*
  * mhc_fused_step_n -- mhc_fused_step for n streams: the same six formulas with
@@ -282,14 +296,26 @@ int64_t mhc_fused_step_n_workspace_bytes(int32_t n, int64_t tokens, int32_t d, i
  * that writes the mixes to mix_out, then the split/Sinkhorn of
  * mhc_sinkhorn_n reading them back. mix_out [T][(2+n)n] is therefore
  * REQUIRED (NULL is MHC_ERR_INVALID_ARG).
- * Workspace (optional): NULL / 0 bytes, or device memory of at least
- * mhc_fused_step_n_workspace_bytes() bytes, 256-byte aligned, overlapping no
- * other argument. When it is given and that size is > 0, the pass over the
- * streams is the feature-split kernel (as for mhc_fused_step: each compute
- * unit keeps a slice of the features and of W; cooperative launch, one
- * workgroup per compute unit; a smaller workspace is MHC_ERR_INVALID_ARG;
- * the same status word at offset 0 and ordering rules). Otherwise, or with
- * no workspace, the token-block kernel runs.
+ * path: mhc_path, the kernel family of the pass over the streams:
+ *   MHC_PATH_TILE   the token-block kernel (one workgroup per 128 tokens, no
+ *                   workspace; the workspace argument is ignored);
+ *   MHC_PATH_SPLIT  the feature-split kernel (each compute unit keeps a slice
+ *                   of the features and of W; cooperative launch, one
+ *                   workgroup per compute unit; the same status word at
+ *                   offset 0 and ordering rules as mhc_fused_step);
+ *   MHC_PATH_CHUNK  the block kernel in chunks of the features (a workgroup
+ *                   per 128-token block and chunk writes partial sums to the
+ *                   workspace, h parked in y_out; a finishing kernel adds the
+ *                   chunks in order, writes the mixes and the RMSNorm);
+ *   MHC_PATH_AUTO   no workspace: the block kernel; with one: the chunks up to
+ *                   2048 tokens, else the feature-split kernel where it
+ *                   applies, else the chunks where they apply (up to 8192
+ *                   tokens), else the block kernel.
+ * SPLIT and CHUNK need a workspace and are MHC_ERR_UNSUPPORTED where they do
+ * not apply.
+ * Workspace: NULL / 0 bytes, or device memory of at least the chosen route's
+ * bytes (mhc_fused_step_n_workspace_bytes() covers both), 256-byte aligned,
+ * overlapping no other argument; a smaller one is MHC_ERR_INVALID_ARG.
  */
 mhc_status mhc_fused_step_n(int32_t n, const void* x, const void* f, int32_t dtype,
                             int64_t tokens, int32_t d, const float* pre_in,
@@ -297,16 +323,16 @@ mhc_status mhc_fused_step_n(int32_t n, const void* x, const void* f, int32_t dty
                             const float* base, const float* scale, const float* gamma,
                             int32_t sinkhorn_iters, float norm_eps, float hc_eps, void* x_out,
                             void* y_out, float* pre_out, float* post_out, float* comb_out,
-                            float* mix_out, void* workspace, int64_t workspace_bytes,
-                            mhc_stream_t stream);
+                            float* mix_out, int32_t path, void* workspace,
+                            int64_t workspace_bytes, mhc_stream_t stream);
 
-/* mhc_mixes_n -- mhc_mixes for n streams; mix_out is required and the
- * workspace optional (as above; same size). */
+/* mhc_mixes_n -- mhc_mixes for n streams; mix_out is required; path and
+ * workspace as above (same sizes). */
 mhc_status mhc_mixes_n(int32_t n, const void* x, int32_t dtype, int64_t tokens, int32_t d,
                        const void* w_packed, const float* base, const float* scale,
                        int32_t sinkhorn_iters, float norm_eps, float hc_eps, float* pre_out,
-                       float* post_out, float* comb_out, float* mix_out, void* workspace,
-                       int64_t workspace_bytes, mhc_stream_t stream);
+                       float* post_out, float* comb_out, float* mix_out, int32_t path,
+                       void* workspace, int64_t workspace_bytes, mhc_stream_t stream);
 
 /*
  * mhc_sinkhorn_n -- mhc_sinkhorn4 for n streams: mixes [T][(2+n)n] to pre,

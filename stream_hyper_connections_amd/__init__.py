@@ -11,12 +11,14 @@ from .binding import (  # noqa: F401
     abi_version,
     d_granule,
     PATHS,
+    PATHS_N,
     fused_step,
     fused_step_backward_n,
     fused_step_backward_workspace_bytes_n,
     fused_step_n,
     fused_step_n_workspace_bytes,
     fused_step_route,
+    fused_step_route_n,
     fused_step_workspace_bytes,
     hc_post,
     hc_pre,

@@ -51,10 +51,11 @@ _SIGS = {
     "mhc_fused_step_n": ([_i32, _c_void_p, _c_void_p, _i32, _i64, _i32, _c_void_p, _c_void_p,
                           _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _f32, _f32,
                           _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
-                          _c_void_p, _i64, _c_void_p], _i32),
+                          _i32, _c_void_p, _i64, _c_void_p], _i32),
     "mhc_mixes_n": ([_i32, _c_void_p, _i32, _i64, _i32, _c_void_p, _c_void_p, _c_void_p, _i32,
-                     _f32, _f32, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64,
-                     _c_void_p], _i32),
+                     _f32, _f32, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _c_void_p,
+                     _i64, _c_void_p], _i32),
+    "mhc_fused_step_route_n": ([_i32, _i32, _i64, _i32, _i32, _i32], _i32),
     "mhc_sinkhorn_n": ([_i32, _c_void_p, _i64, _c_void_p, _c_void_p, _i32, _f32, _c_void_p,
                         _c_void_p, _c_void_p, _c_void_p], _i32),
     "mhc_fused_step_backward_workspace_bytes_n": ([_i32, _i64, _i32], _i64),
@@ -362,30 +363,50 @@ def pack_wmix_n(w_mix: torch.Tensor, dtype, out: torch.Tensor | None = None) -> 
 
 
 def fused_step_n_workspace_bytes(n: int, tokens: int, d: int, dtype) -> int:
-    """mhc_fused_step_n_workspace_bytes: 0 when the feature-split kernel does
-    not apply to (n, d, dtype) on the current device."""
+    """mhc_fused_step_n_workspace_bytes: the workspace both workspace routes of
+    the n-family need (0 when neither applies to (n, tokens, d, dtype) on the
+    current device)."""
     b = load().mhc_fused_step_n_workspace_bytes(n, tokens, d, _dtype_name_code(dtype))
     if b < 0:
         raise MhcError("mhc_fused_step_n_workspace_bytes", MHC_ERR_INVALID_ARG, last_error())
     return b
 
 
+# path names of the n-family ("block" is the token-block kernel, MHC_PATH_TILE)
+PATHS_N = {"auto": 0, "block": 1, "split": 2, "chunk": 3}
+_PATH_NAMES_N = {v: k for k, v in PATHS_N.items()}
+
+
+def fused_step_route_n(n: int, path: str, tokens: int, d: int, dtype,
+                       with_workspace=True) -> str:
+    """mhc_fused_step_route_n: the kernel family ("block", "split" or "chunk")
+    that fused_step_n / mixes_n run for `path`; ValueError if that path cannot
+    run these arguments."""
+    if path not in PATHS_N:
+        raise ValueError(f"unknown path {path!r}")
+    r = load().mhc_fused_step_route_n(n, PATHS_N[path], tokens, d, _dtype_name_code(dtype),
+                                      1 if with_workspace else 0)
+    if r < 0:
+        raise ValueError(f"path {path!r}, n={n}, d={d}, {dtype}: {last_error()}")
+    return _PATH_NAMES_N[r]
+
+
 def _workspace_arg_n(x, n, t, d, path, workspace):
-    """(pointer, bytes) of the workspace of the n-family for path "block"
-    (token-block kernel) / "split" (feature-split kernel; raises if it does not
-    apply) / "auto" (split where it applies)."""
-    if path not in ("auto", "block", "split"):
+    """(mhc_path code, workspace pointer, workspace bytes) of the n-family for
+    path "block" / "split" / "chunk" (both raise ValueError where they do not
+    apply) / "auto"."""
+    if path not in PATHS_N:
         raise ValueError(f"unknown path {path!r}")
     if path == "block":
-        return None, 0
+        return PATHS_N["block"], None, 0
+    if path != "auto":
+        fused_step_route_n(n, path, t, d, _dtype_code(x))   # raises where it does not apply
     need = fused_step_n_workspace_bytes(n, t, d, _dtype_code(x))
-    if path == "split" and need == 0:
-        raise ValueError(f"the feature-split kernel does not apply to n={n}, d={d}, {x.dtype}")
-    if need > 0:
-        if workspace is None:
-            workspace = workspace_for(x.device, need)
-        return _ptr(workspace), workspace.numel() * workspace.element_size()
-    return None, 0
+    if need == 0:
+        return PATHS_N[path], None, 0
+    if workspace is None:
+        workspace = workspace_for(x.device, need)
+    return PATHS_N[path], _ptr(workspace), workspace.numel() * workspace.element_size()
 
 
 def fused_step_n(x, f, pre_in, post_in, comb_in, w_packed, base, scale, gamma, iters=20,
@@ -393,11 +414,12 @@ def fused_step_n(x, f, pre_in, post_in, comb_in, w_packed, base, scale, gamma, i
                  comb_out=None, mix_out=None, path="auto", workspace=None) -> dict:
     """mhc_fused_step_n on tensors: x [T,n,d], f [T,d]; w_packed from pack_wmix_n.
     Returns dict(x_out, y, pre, post, comb, mix) (mix is always produced).
-    path: "block", "split" or "auto" (the feature-split kernel where it
-    applies: n in {2, 4}, bf16); workspace: optional uint8 tensor for it (a
-    cached one is used otherwise)."""
+    path: "block" (no workspace), "split" (feature-split kernel: n in {2, 4},
+    bf16), "chunk" (the block kernel in chunks of the features, up to 8192
+    tokens) or "auto" (the library's choice by size); workspace: optional uint8
+    tensor (a cached one is used otherwise)."""
     t, n, d = x.shape
-    ws_ptr, ws_bytes = _workspace_arg_n(x, n, t, d, path, workspace)
+    code, ws_ptr, ws_bytes = _workspace_arg_n(x, n, t, d, path, workspace)
     x_out = torch.empty_like(x) if x_out is None else x_out
     y_out = torch.empty_like(f) if y_out is None else y_out
     pre_out = _f32_out((t, n), x, pre_out)
@@ -408,7 +430,7 @@ def fused_step_n(x, f, pre_in, post_in, comb_in, w_packed, base, scale, gamma, i
         n, _ptr(x), _ptr(f), _dtype_code(x), t, d, _ptr(pre_in), _ptr(post_in), _ptr(comb_in),
         _ptr(w_packed), _ptr(base), _ptr(scale), _ptr(gamma), iters, norm_eps, hc_eps,
         _ptr(x_out), _ptr(y_out), _ptr(pre_out), _ptr(post_out), _ptr(comb_out), _ptr(mix_out),
-        ws_ptr, ws_bytes, _stream())
+        code, ws_ptr, ws_bytes, _stream())
     _check("mhc_fused_step_n", st)
     return {"x_out": x_out, "y": y_out, "pre": pre_out, "post": post_out, "comb": comb_out,
             "mix": mix_out}
@@ -419,14 +441,15 @@ def mixes_n(x, w_packed, base, scale, iters=20, norm_eps=1e-6, hc_eps=1e-6, pre_
     """mhc_mixes_n on tensors: x [T,n,d]. Returns dict(pre, post, comb, mix).
     path and workspace as for fused_step_n."""
     t, n, d = x.shape
-    ws_ptr, ws_bytes = _workspace_arg_n(x, n, t, d, path, workspace)
+    code, ws_ptr, ws_bytes = _workspace_arg_n(x, n, t, d, path, workspace)
     pre_out = _f32_out((t, n), x, pre_out)
     post_out = _f32_out((t, n), x, post_out)
     comb_out = _f32_out((t, n, n), x, comb_out)
     mix_out = _f32_out((t, n_mix(n)), x, mix_out)
     st = load().mhc_mixes_n(n, _ptr(x), _dtype_code(x), t, d, _ptr(w_packed), _ptr(base),
                             _ptr(scale), iters, norm_eps, hc_eps, _ptr(pre_out), _ptr(post_out),
-                            _ptr(comb_out), _ptr(mix_out), ws_ptr, ws_bytes, _stream())
+                            _ptr(comb_out), _ptr(mix_out), code, ws_ptr, ws_bytes,
+                            _stream())
     _check("mhc_mixes_n", st)
     return {"pre": pre_out, "post": post_out, "comb": comb_out, "mix": mix_out}
 

@@ -319,12 +319,28 @@ __device__ __forceinline__ void next_part(u32x4* wl, u32x4* st, const u32x4* wne
   if (p + 1 < S::kParts) stage_load<N, DT, SPI>(st, wnext + (p + 1) * S::kPartVecs, tid);
 }
 
+// Chunked launches (small calls): workgroup (block, chunk) covers the units
+// [chunk * per, (chunk + 1) * per) of its 128-token block and writes, per
+// token, a partial row of kRowN floats to the workspace (after a 256-byte
+// header): the (2+n)n projection sums of its units (the three terms added),
+// sum x'^2 and sum h^2. h stays parked in y; chunk_finish_kernel completes the
+// tokens.
+struct ChunkN {
+  char* ws;       // workspace (nullptr: not chunked)
+  int per;        // units per chunk
+  int nchunks;    // chunks per row
+};
+constexpr int64_t kChunkHeaderN = 256;
+template <int N>
+__host__ __device__ constexpr int row_n() { return ((Dims<N>::kMix + 2 + 3) / 4) * 4; }
+
 // One pass over a 128-token block: hc_post (stored), the RMS statistic and the
 // (2+n)n-wide projection of the new streams (written to mix_out), hc_pre (h
 // parked in y) and, after the token's sum of h^2 is complete, RMSNorm over y.
-// MODE kMixesOnly reads x as the streams and writes mix_out only.
-template <int N, int DT, int MODE, int SPI>
-__global__ __launch_bounds__(kThreads) void block_kernel(StepArgs a) {
+// MODE kMixesOnly reads x as the streams and writes mix_out only. CH: one
+// chunk of the units, partial rows instead of the mixes and RMSNorm.
+template <int N, int DT, int MODE, int SPI, bool CH = false>
+__global__ __launch_bounds__(kThreads) void block_kernel(StepArgs a, ChunkN cn) {
   using Dm = Dims<N>;
   using S = Slice<N, DT, SPI>;
   constexpr bool kBf = DT == MHC_BF16;
@@ -342,17 +358,24 @@ __global__ __launch_bounds__(kThreads) void block_kernel(StepArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tr = lane & 15;
   const int g = lane >> 4;
-  const int64_t tb = (int64_t)blockIdx.x * kBlock;
+  const int blk = CH ? (int)(blockIdx.x / cn.nchunks) : (int)blockIdx.x;
+  const int chunk = CH ? (int)(blockIdx.x - (unsigned)blk * cn.nchunks) : 0;
+  const int64_t tb = (int64_t)blk * kBlock;
   const int64_t tw = tb + wave * kTok;
   const int64_t t = tw + tr;
   const bool valid = t < a.tokens;
   const int d = a.d;
   const int nsteps = d / kStep;
+  const int nunits_all = nsteps / SPI;
+  const int u0 = CH ? chunk * cn.per : 0;                       // this launch's units
+  const int u1 = CH ? min(u0 + cn.per, nunits_all) : nunits_all;
   const u32x4* wpk = static_cast<const u32x4*>(a.wpk);
+  const u32x4* wpk0 = wpk + (size_t)u0 * S::kVecs;
+  if (CH && blockIdx.x == 0 && tid == 0) *reinterpret_cast<uint32_t*>(cn.ws) = 0u;
 
-  // packed weights of unit 0, part 0 (the other parts follow below)
+  // packed weights of the first unit, part 0 (the other parts follow below)
   u32x4 wst[S::kStage];
-  stage_load<N, DT, SPI>(wst, wpk, tid);
+  stage_load<N, DT, SPI>(wst, wpk0, tid);
 
   Coef<N, kCL> cf;
   if (kFull) {
@@ -385,7 +408,7 @@ __global__ __launch_bounds__(kThreads) void block_kernel(StepArgs a) {
   stage_store<N, DT, SPI>(wl, wst, tid);
 #pragma unroll
   for (int p = 1; p < S::kParts; ++p) {
-    stage_load<N, DT, SPI>(wst, wpk + p * S::kPartVecs, tid);
+    stage_load<N, DT, SPI>(wst, wpk0 + p * S::kPartVecs, tid);
     stage_store<N, DT, SPI>(wl + p * S::kPartVecs, wst, tid);
   }
   __syncthreads();
@@ -400,16 +423,16 @@ __global__ __launch_bounds__(kThreads) void block_kernel(StepArgs a) {
   if constexpr (kBf) {
     // a unit of SPI steps; lane loads and stores of the SPI halves of a line
     // are issued back to back
-    const int nunits = nsteps / SPI;
     constexpr int kE = SPI * N;                 // stream-steps per unit
     InBf<N> cur[SPI];
 #pragma unroll
-    for (int h = 0; h < SPI; ++h) load_bf<N, MODE>(cur[h], rw, h * (kStep * 2));
-    for (int u = 0; u < nunits; ++u) {
+    for (int h = 0; h < SPI; ++h)
+      load_bf<N, MODE>(cur[h], rw, (uint32_t)u0 * (SPI * kStep * 2) + h * (kStep * 2));
+    for (int u = u0; u < u1; ++u) {
       const uint32_t col = (uint32_t)u * (SPI * kStep * 2);
       // the last unit reloads its own data instead of reading past the rows
       // (no branch around the loads, which the compiler would hoist)
-      const int un = u + 1 < nunits ? u + 1 : u;
+      const int un = u + 1 < u1 ? u + 1 : u;
       const u32x4* wnext = wpk + (size_t)un * S::kVecs;
       // Loads retire in issue order: the next unit's weights are issued before
       // its streams, so that the wait for the weights at the end of this unit
@@ -475,9 +498,9 @@ __global__ __launch_bounds__(kThreads) void block_kernel(StepArgs a) {
       if (S::kParts == 1) __syncthreads();
     }
   } else {
-    for (int s = 0; s < nsteps; ++s) {
+    for (int s = u0; s < u1; ++s) {
       const uint32_t col = (uint32_t)s * (kStep * 4);
-      const int sn = s + 1 < nsteps ? s + 1 : s;
+      const int sn = s + 1 < u1 ? s + 1 : s;
       const u32x4* wnext = wpk + (size_t)sn * S::kVecs;
       InF<N> in;
       load_f<N, MODE>(in, rw, col);
@@ -555,6 +578,30 @@ __global__ __launch_bounds__(kThreads) void block_kernel(StepArgs a) {
   ss += __shfl_xor(ss, 32);
   hs += __shfl_xor(hs, 16);
   hs += __shfl_xor(hs, 32);
+
+  if constexpr (CH) {
+    // partial row of this chunk: lane (c, g) holds rows 4g + i, column 16q + c
+    constexpr int kR = row_n<N>();
+    float* part = reinterpret_cast<float*>(cn.ws + kChunkHeaderN);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t tt = tw + 4 * g + i;
+      if (tt >= a.tokens) continue;
+      float* row = part + ((int64_t)chunk * a.tokens + tt) * kR;
+#pragma unroll
+      for (int q = 0; q < kT1; ++q) {
+        const int j = 16 * q + tr;
+        if (j < kMix)
+          row[j] = kBf ? (acc[q][i] + acc[kT1 + q][i]) + acc[2 * kT1 + q][i] : acc[q][i];
+      }
+    }
+    if (g == 0 && valid) {
+      float* row = part + ((int64_t)chunk * a.tokens + t) * kR;
+      row[kMix] = ss;
+      row[kMix + 1] = hs;
+    }
+    return;
+  }
   const float r = rsqrtf(ss / (float)(N * d) + a.norm_eps);
 
   // mixes: lane (c, g) holds rows 4g + i of the tile, column 16q + c of every
@@ -618,6 +665,80 @@ __global__ __launch_bounds__(kThreads) void block_kernel(StepArgs a) {
             pipe::bstore<0>(rw.y, rw.foff, col + 16 * v, y);
           }
         }
+      }
+    }
+  }
+}
+
+// Completes the tokens of a chunked launch: sums each token's partial rows,
+// writes the mixes (r * projection, [SW] Code, hc_mixes) to mix_out and
+// rewrites y = S(gamma * (h * rh)) over the parked h ([RN] RMSNorm), with the
+// block kernel's arithmetic per element. One workgroup of 256 threads per
+// token; sinkhorn_kernel then splits the mixes. The sums are split over kG
+// groups of kR threads, each adding a contiguous run of chunks eight loads at
+// a time, then added in group order (a fixed order: results repeat bit for
+// bit).
+template <int N, int DT, int MODE>
+__global__ __launch_bounds__(256) void chunk_finish_kernel(StepArgs a, ChunkN cn) {
+  constexpr int kMix = Dims<N>::kMix;
+  constexpr int kR = row_n<N>();
+  constexpr int kG = 256 / kR;
+  __shared__ float grp_sum[kG][kR];
+  __shared__ float sum[kR];
+  const int64_t t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const float* part = reinterpret_cast<const float*>(cn.ws + kChunkHeaderN);
+  const int grp = tid / kR;
+  const int col = tid - grp * kR;
+  if (grp < kG) {
+    const int cper = (cn.nchunks + kG - 1) / kG;
+    const int c1 = min((grp + 1) * cper, cn.nchunks);
+    float v = 0.f;
+    int c = grp * cper;
+    for (; c + 8 <= c1; c += 8) {
+      float b[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) b[e] = part[((int64_t)(c + e) * a.tokens + t) * kR + col];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v += b[e];
+    }
+    for (; c < c1; ++c) v += part[((int64_t)c * a.tokens + t) * kR + col];
+    grp_sum[grp][col] = v;
+  }
+  __syncthreads();
+  if (tid < kR) {
+    float v = 0.f;
+#pragma unroll
+    for (int g = 0; g < kG; ++g) v += grp_sum[g][tid];
+    sum[tid] = v;
+  }
+  __syncthreads();
+  const float r = rsqrtf(sum[kMix] / (float)(N * a.d) + a.norm_eps);
+  if (tid < kMix) a.mix_out[t * kMix + tid] = sum[tid] * r;
+  if (MODE == kFused) {
+    const float rh = rsqrtf(sum[kMix + 1] / (float)a.d + a.norm_eps);
+    if (DT == MHC_BF16) {
+      u32x4* y = reinterpret_cast<u32x4*>(static_cast<char*>(a.y_out) + t * a.d * 2);
+      for (int u = tid; u < a.d / 8; u += 256) {
+        const u32x4 h = ld16(y + u);
+        const f32x4 g0 = *reinterpret_cast<const f32x4*>(a.gamma + 8 * u);
+        const f32x4 g1 = *reinterpret_cast<const f32x4*>(a.gamma + 8 * u + 4);
+        const float gv[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
+        u32x4 o;
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          o[w] = pack_bf16x2(gv[2 * w] * (bf_lo(h[w]) * rh), gv[2 * w + 1] * (bf_hi(h[w]) * rh));
+        st16(y + u, o);
+      }
+    } else {
+      float* y = static_cast<float*>(a.y_out) + t * a.d;
+      for (int u = tid; u < a.d / 4; u += 256) {
+        const f32x4 h = *reinterpret_cast<const f32x4*>(y + 4 * u);
+        const f32x4 gv = *reinterpret_cast<const f32x4*>(a.gamma + 4 * u);
+        f32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = gv[e] * (h[e] * rh);
+        st4f(y + 4 * u, o);
       }
     }
   }

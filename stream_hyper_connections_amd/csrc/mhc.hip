@@ -1543,22 +1543,22 @@ mhc_status route_needs(int32_t dtype, int32_t d, int64_t tokens, RouteNeeds* rn)
 
 // The route of a call with `path` and a workspace (or none), or an error for
 // a path that cannot run these arguments.
-mhc_status pick_route(int32_t path, const void* workspace, int64_t tokens, const RouteNeeds& rn,
-                      Route* r) {
+mhc_status pick_route(int32_t path, const void* workspace, int64_t tokens, int64_t split_bytes,
+                      int64_t chunk_bytes, Route* r) {
   switch (path) {
     case MHC_PATH_TILE:
       *r = Route::kTile;
       return MHC_OK;
     case MHC_PATH_AUTO:
       if (workspace == nullptr) *r = Route::kTile;
-      else if (rn.chunk_bytes > 0 && tokens <= MHC_CHUNK_AUTO_TOKENS) *r = Route::kChunk;
-      else if (rn.split_bytes > 0) *r = Route::kSplit;
+      else if (chunk_bytes > 0 && tokens <= MHC_CHUNK_AUTO_TOKENS) *r = Route::kChunk;
+      else if (split_bytes > 0) *r = Route::kSplit;
       else *r = Route::kTile;
       return MHC_OK;
     case MHC_PATH_SPLIT:
     case MHC_PATH_CHUNK: {
       const bool split = path == MHC_PATH_SPLIT;
-      if ((split ? rn.split_bytes : rn.chunk_bytes) == 0)
+      if ((split ? split_bytes : chunk_bytes) == 0)
         return fail(MHC_ERR_UNSUPPORTED, "the %s kernel does not apply to these arguments",
                     split ? "feature-split" : "chunked");
       if (workspace == nullptr)
@@ -1582,7 +1582,7 @@ mhc_status choose_route(int32_t path, const void* workspace, int32_t dtype, int3
     const mhc_status s = route_needs(dtype, d, tokens, rn);
     if (s != MHC_OK) return s;
   }
-  return pick_route(path, workspace, tokens, *rn, r);
+  return pick_route(path, workspace, tokens, rn->split_bytes, rn->chunk_bytes, r);
 }
 
 mhc_status launch_step(const StepArgs& a, int32_t dtype, int mode, hipStream_t stream,
@@ -1644,12 +1644,13 @@ void launch_pack_n(const float* w, int d, int32_t dtype, int64_t total, void* ou
 template <int N, int DT, int SPI>
 void launch_block(const StepArgs& a, int mode, hipStream_t st) {
   const unsigned grid = (unsigned)((a.tokens + gen::kBlock - 1) / gen::kBlock);
+  const gen::ChunkN none{nullptr, 0, 1};
   if (mode == kFused)
     hipLaunchKernelGGL((gen::block_kernel<N, DT, kFused, SPI>), dim3(grid), dim3(gen::kThreads), 0,
-                       st, a);
+                       st, a, none);
   else
     hipLaunchKernelGGL((gen::block_kernel<N, DT, kMixesOnly, SPI>), dim3(grid),
-                       dim3(gen::kThreads), 0, st, a);
+                       dim3(gen::kThreads), 0, st, a, none);
 }
 
 // bf16 streams with n <= 4 and an even step count run two steps per unit
@@ -1794,21 +1795,127 @@ mhc_status launch_split_n(const StepArgs& a, void* ws, const SplitCfgN& cfg, int
 // Workspace argument of the n-family: (NULL or 0 bytes: the block kernel);
 // otherwise the feature-split kernel when it applies, after the checks of
 // mhc_fused_step.
-mhc_status pick_split_n(int32_t n, int32_t dtype, int64_t tokens, int32_t d, void* workspace,
-                        int64_t workspace_bytes, SplitCfgN* cfg, int64_t* need) {
-  *cfg = SplitCfgN{};
-  *need = 0;
-  if (workspace == nullptr || workspace_bytes <= 0) return MHC_OK;
-  mhc_status s = split_config_n(n, dtype, d, cfg);
+// Chunked launches of the general-n block kernel (at most kChunkMaxTokens
+// tokens): up to kChunksN chunks of whole units per row.
+constexpr int kChunksN = 80;
+
+struct ChunkCfgN {
+  int nchunks = 0;
+  int per = 0;   // units per chunk
+  int spi = 1;   // steps per unit
+};
+
+ChunkCfgN chunk_config_n(int32_t n, int32_t dtype, int32_t d, int64_t tokens) {
+  const int nsteps = d / kStep;
+  if (d <= 0 || d % kStep != 0 || tokens > kChunkMaxTokens || elem_size(dtype) == 0)
+    return ChunkCfgN{};
+  const int spi = (dtype == MHC_BF16 && n <= 4 && MHC_GEN_UNIT2 && nsteps % 2 == 0) ? 2 : 1;
+  const int nunits = nsteps / spi;
+  const int per = (nunits + kChunksN - 1) / kChunksN;
+  return ChunkCfgN{(nunits + per - 1) / per, per, spi};
+}
+
+int64_t chunk_n_workspace_bytes(int32_t n, const ChunkCfgN& c, int64_t tokens) {
+  const int row = n == 2 ? gen::row_n<2>() : (n == 4 ? gen::row_n<4>() : gen::row_n<8>());
+  return gen::kChunkHeaderN + (int64_t)c.nchunks * tokens * row * 4;
+}
+
+template <int N, int DT, int SPI>
+void launch_chunk_block(const StepArgs& a, const gen::ChunkN& cn, int mode, hipStream_t st) {
+  const unsigned grid =
+      (unsigned)(((a.tokens + gen::kBlock - 1) / gen::kBlock) * (int64_t)cn.nchunks);
+  if (mode == kFused)
+    hipLaunchKernelGGL((gen::block_kernel<N, DT, kFused, SPI, true>), dim3(grid),
+                       dim3(gen::kThreads), 0, st, a, cn);
+  else
+    hipLaunchKernelGGL((gen::block_kernel<N, DT, kMixesOnly, SPI, true>), dim3(grid),
+                       dim3(gen::kThreads), 0, st, a, cn);
+}
+
+template <int N>
+mhc_status launch_chunk_n(const StepArgs& a, void* ws, const ChunkCfgN& c, int32_t dtype,
+                          int mode, hipStream_t st) {
+  const gen::ChunkN cn{static_cast<char*>(ws), c.per, c.nchunks};
+  if (dtype == MHC_F32) {
+    launch_chunk_block<N, MHC_F32, 1>(a, cn, mode, st);
+  } else {
+    if constexpr (N <= 4) {
+      if (c.spi == 2) launch_chunk_block<N, MHC_BF16, 2>(a, cn, mode, st);
+      else launch_chunk_block<N, MHC_BF16, 1>(a, cn, mode, st);
+    } else {
+      launch_chunk_block<N, MHC_BF16, 1>(a, cn, mode, st);
+    }
+  }
+  mhc_status s = launch_status("general-n chunk kernel launch");
   if (s != MHC_OK) return s;
-  if (cfg->groups == 0) return MHC_OK;   // not applicable: the block kernel
-  *need = split_n_workspace_bytes(n, *cfg, tokens);
-  if (workspace_bytes < *need)
-    return fail(MHC_ERR_INVALID_ARG, "workspace holds %lld bytes, %lld needed",
-                (long long)workspace_bytes, (long long)*need);
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-    return fail(MHC_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+  const dim3 tok((unsigned)a.tokens);
+  if (mode == kFused && dtype == MHC_BF16)
+    hipLaunchKernelGGL((gen::chunk_finish_kernel<N, MHC_BF16, kFused>), tok, dim3(256), 0, st, a,
+                       cn);
+  else if (mode == kFused)
+    hipLaunchKernelGGL((gen::chunk_finish_kernel<N, MHC_F32, kFused>), tok, dim3(256), 0, st, a,
+                       cn);
+  else
+    hipLaunchKernelGGL((gen::chunk_finish_kernel<N, MHC_BF16, kMixesOnly>), tok, dim3(256), 0, st,
+                       a, cn);
+  if ((s = launch_status("general-n chunk finish kernel launch")) != MHC_OK) return s;
+  launch_sinkhorn_n<N>(a.mix_out, a.tokens, a.base, a.scale, a.iters, a.hc_eps, a.pre_out,
+                       a.post_out, a.comb_out, st);
+  return launch_status("general-n split/Sinkhorn kernel launch");
+}
+
+// Workspace routes of the n-family and what each needs (0: does not apply).
+struct RouteNeedsN {
+  SplitCfgN split;
+  ChunkCfgN chunk;
+  int64_t split_bytes = 0;
+  int64_t chunk_bytes = 0;
+};
+
+mhc_status route_needs_n(int32_t n, int32_t dtype, int32_t d, int64_t tokens, RouteNeedsN* rn) {
+  *rn = RouteNeedsN{};
+  mhc_status s = split_config_n(n, dtype, d, &rn->split);
+  if (s != MHC_OK) return s;
+  if (rn->split.groups > 0) rn->split_bytes = split_n_workspace_bytes(n, rn->split, tokens);
+  rn->chunk = chunk_config_n(n, dtype, d, tokens);
+  if (rn->chunk.nchunks > 0) rn->chunk_bytes = chunk_n_workspace_bytes(n, rn->chunk, tokens);
   return MHC_OK;
+}
+
+// The route of an n-family call (MHC_PATH_TILE names the block kernel here).
+mhc_status choose_route_n(int32_t path, const void* workspace, int32_t n, int32_t dtype,
+                          int32_t d, int64_t tokens, RouteNeedsN* rn, Route* r) {
+  *rn = RouteNeedsN{};
+  if (path == MHC_PATH_TILE || (path == MHC_PATH_AUTO && workspace == nullptr)) {
+    *r = Route::kTile;
+    return MHC_OK;
+  }
+  if (path == MHC_PATH_AUTO || path == MHC_PATH_SPLIT || path == MHC_PATH_CHUNK) {
+    const mhc_status s = route_needs_n(n, dtype, d, tokens, rn);
+    if (s != MHC_OK) return s;
+  }
+  const mhc_status s = pick_route(path, workspace, tokens, rn->split_bytes, rn->chunk_bytes, r);
+  // without a feature-split kernel the chunks beat the block kernel at every
+  // size they cover (a call of T tokens has only T / 128 blocks)
+  if (s == MHC_OK && path == MHC_PATH_AUTO && *r == Route::kTile && workspace != nullptr &&
+      rn->chunk_bytes > 0)
+    *r = Route::kChunk;
+  return s;
+}
+
+mhc_status launch_route_n(int32_t n, Route route, const RouteNeedsN& rn, const StepArgs& a,
+                          void* workspace, int32_t dtype, int mode, hipStream_t st) {
+  if (route == Route::kSplit)
+    return n == 2 ? launch_split_n<2>(a, workspace, rn.split, mode, st)
+                  : launch_split_n<4>(a, workspace, rn.split, mode, st);
+  if (route == Route::kChunk) {
+    switch (n) {
+      case 2: return launch_chunk_n<2>(a, workspace, rn.chunk, dtype, mode, st);
+      case 4: return launch_chunk_n<4>(a, workspace, rn.chunk, dtype, mode, st);
+      default: return launch_chunk_n<8>(a, workspace, rn.chunk, dtype, mode, st);
+    }
+  }
+  return run_n(n, a, dtype, mode, st);
 }
 
 // ----- backward ------------------------------------------------------------------------
@@ -2158,9 +2265,25 @@ int64_t mhc_fused_step_n_workspace_bytes(int32_t n, int64_t tokens, int32_t d, i
          (long long)tokens, d, dtype);
     return -1;
   }
-  SplitCfgN cfg;
-  if (split_config_n(n, dtype, d, &cfg) != MHC_OK) return -1;
-  return split_n_workspace_bytes(n, cfg, tokens);
+  RouteNeedsN rn;
+  if (route_needs_n(n, dtype, d, tokens, &rn) != MHC_OK) return -1;
+  return std::max(rn.split_bytes, rn.chunk_bytes);
+}
+
+int32_t mhc_fused_step_route_n(int32_t n, int32_t path, int64_t tokens, int32_t d, int32_t dtype,
+                               int32_t with_workspace) {
+  if (!n_supported(n) || tokens < 0 || d <= 0 || d % kStep != 0 || elem_size(dtype) == 0) {
+    fail(MHC_ERR_INVALID_ARG, "bad n (%d), tokens (%lld), d (%d) or dtype (%d)", n,
+         (long long)tokens, d, dtype);
+    return -1;
+  }
+  RouteNeedsN rn;
+  Route r;
+  static const char kDummy = 0;   // stands for a workspace; never dereferenced
+  if (choose_route_n(path, with_workspace ? &kDummy : nullptr, n, dtype, d, tokens, &rn, &r) !=
+      MHC_OK)
+    return -1;
+  return r == Route::kTile ? MHC_PATH_TILE : (r == Route::kSplit ? MHC_PATH_SPLIT : MHC_PATH_CHUNK);
 }
 
 mhc_status mhc_fused_step_n(int32_t n, const void* x, const void* f, int32_t dtype,
@@ -2169,16 +2292,12 @@ mhc_status mhc_fused_step_n(int32_t n, const void* x, const void* f, int32_t dty
                             const float* base, const float* scale, const float* gamma,
                             int32_t sinkhorn_iters, float norm_eps, float hc_eps, void* x_out,
                             void* y_out, float* pre_out, float* post_out, float* comb_out,
-                            float* mix_out, void* workspace, int64_t workspace_bytes,
-                            mhc_stream_t stream) {
+                            float* mix_out, int32_t path, void* workspace,
+                            int64_t workspace_bytes, mhc_stream_t stream) {
   if (!n_supported(n)) return fail(MHC_ERR_UNSUPPORTED, "n = %d streams (2, 4 or 8 supported)", n);
   mhc_status s = check_common(dtype, tokens, d, sinkhorn_iters, norm_eps, hc_eps);
   if (s != MHC_OK) return s;
   if (tokens == 0) return ok();
-  SplitCfgN cfg;
-  int64_t need = 0;
-  if ((s = pick_split_n(n, dtype, tokens, d, workspace, workspace_bytes, &cfg, &need)) != MHC_OK)
-    return s;
   const uint64_t es = elem_size(dtype), T = (uint64_t)tokens, nn = (uint64_t)n, nm = n_mix(n);
   const Span in[] = {
       {"x", x, T * nn * d * es},           {"f", f, T * d * es},
@@ -2192,32 +2311,34 @@ mhc_status mhc_fused_step_n(int32_t n, const void* x, const void* f, int32_t dty
       {"x_out", x_out, T * nn * d * es},   {"y_out", y_out, T * d * es},
       {"pre_out", pre_out, T * nn * 4},    {"post_out", post_out, T * nn * 4},
       {"comb_out", comb_out, T * nn * nn * 4}, {"mix_out", mix_out, T * nm * 4},
-      {"workspace", workspace, (uint64_t)need},
   };
-  s = check_spans(in, 9, out, cfg.groups > 0 ? 7 : 6, x_out, x);
+  s = check_spans(in, 9, out, 6, x_out, x);
   if (s != MHC_OK) return s;
+  RouteNeedsN rn;
+  Route route;
+  if ((s = choose_route_n(path, workspace, n, dtype, d, tokens, &rn, &route)) != MHC_OK) return s;
+  if (route != Route::kTile) {
+    const int64_t need = route == Route::kSplit ? rn.split_bytes : rn.chunk_bytes;
+    Span all[15];
+    for (int i = 0; i < 9; ++i) all[i] = in[i];
+    for (int i = 0; i < 6; ++i) all[9 + i] = out[i];
+    if ((s = check_workspace(workspace, workspace_bytes, need, all, 15)) != MHC_OK) return s;
+  }
   StepArgs a{x, f, pre_in, post_in, comb_in, w_packed, base, scale, gamma, x_out, y_out,
              pre_out, post_out, comb_out, mix_out, tokens, d, sinkhorn_iters, norm_eps, hc_eps};
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  if (cfg.groups > 0)
-    return n == 2 ? launch_split_n<2>(a, workspace, cfg, kFused, st)
-                  : launch_split_n<4>(a, workspace, cfg, kFused, st);
-  return run_n(n, a, dtype, kFused, st);
+  return launch_route_n(n, route, rn, a, workspace, dtype, kFused, st);
 }
 
 mhc_status mhc_mixes_n(int32_t n, const void* x, int32_t dtype, int64_t tokens, int32_t d,
                        const void* w_packed, const float* base, const float* scale,
                        int32_t sinkhorn_iters, float norm_eps, float hc_eps, float* pre_out,
-                       float* post_out, float* comb_out, float* mix_out, void* workspace,
-                       int64_t workspace_bytes, mhc_stream_t stream) {
+                       float* post_out, float* comb_out, float* mix_out, int32_t path,
+                       void* workspace, int64_t workspace_bytes, mhc_stream_t stream) {
   if (!n_supported(n)) return fail(MHC_ERR_UNSUPPORTED, "n = %d streams (2, 4 or 8 supported)", n);
   mhc_status s = check_common(dtype, tokens, d, sinkhorn_iters, norm_eps, hc_eps);
   if (s != MHC_OK) return s;
   if (tokens == 0) return ok();
-  SplitCfgN cfg;
-  int64_t need = 0;
-  if ((s = pick_split_n(n, dtype, tokens, d, workspace, workspace_bytes, &cfg, &need)) != MHC_OK)
-    return s;
   const uint64_t es = elem_size(dtype), T = (uint64_t)tokens, nn = (uint64_t)n, nm = n_mix(n);
   const Span in[] = {
       {"x", x, T * nn * d * es},
@@ -2228,18 +2349,24 @@ mhc_status mhc_mixes_n(int32_t n, const void* x, int32_t dtype, int64_t tokens, 
   const Span out[] = {
       {"pre_out", pre_out, T * nn * 4}, {"post_out", post_out, T * nn * 4},
       {"comb_out", comb_out, T * nn * nn * 4}, {"mix_out", mix_out, T * nm * 4},
-      {"workspace", workspace, (uint64_t)need},
   };
-  s = check_spans(in, 4, out, cfg.groups > 0 ? 5 : 4, nullptr, nullptr);
+  s = check_spans(in, 4, out, 4, nullptr, nullptr);
   if (s != MHC_OK) return s;
+  RouteNeedsN rn;
+  Route route;
+  if ((s = choose_route_n(path, workspace, n, dtype, d, tokens, &rn, &route)) != MHC_OK) return s;
+  if (route != Route::kTile) {
+    const int64_t need = route == Route::kSplit ? rn.split_bytes : rn.chunk_bytes;
+    Span all[8];
+    for (int i = 0; i < 4; ++i) all[i] = in[i];
+    for (int i = 0; i < 4; ++i) all[4 + i] = out[i];
+    if ((s = check_workspace(workspace, workspace_bytes, need, all, 8)) != MHC_OK) return s;
+  }
   StepArgs a{x, nullptr, nullptr, nullptr, nullptr, w_packed, base, scale, nullptr, nullptr,
              nullptr, pre_out, post_out, comb_out, mix_out, tokens, d, sinkhorn_iters, norm_eps,
              hc_eps};
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  if (cfg.groups > 0)
-    return n == 2 ? launch_split_n<2>(a, workspace, cfg, kMixesOnly, st)
-                  : launch_split_n<4>(a, workspace, cfg, kMixesOnly, st);
-  return run_n(n, a, dtype, kMixesOnly, st);
+  return launch_route_n(n, route, rn, a, workspace, dtype, kMixesOnly, st);
 }
 
 mhc_status mhc_sinkhorn_n(int32_t n, const float* mixes, int64_t tokens, const float* base,

@@ -31,6 +31,7 @@ def test_header_declares_the_entry_points():
                "mhc_hc_post", "mhc_hc_pre", "mhc_rmsnorm", "mhc_wmix_packed_bytes_n",
                "mhc_pack_wmix_n", "mhc_fused_step_n", "mhc_mixes_n", "mhc_sinkhorn_n",
                "mhc_fused_step_n_workspace_bytes", "mhc_fused_step_route",
+               "mhc_fused_step_route_n",
                "mhc_fused_step_backward_n", "mhc_fused_step_backward_workspace_bytes_n"):
         assert fn in names
 
@@ -43,7 +44,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_granule_and_status_strings():
-    assert binding.abi_version() == 7
+    assert binding.abi_version() == 8
     assert binding.d_granule() == 32
     lib = binding.load()
     assert lib.mhc_status_string(0) == b"MHC_OK"
@@ -138,6 +139,62 @@ def test_route_query_without_a_device_query():
     assert "unknown path" in binding.last_error()
     assert lib.mhc_fused_step_route(0, -1, 5120, binding.MHC_BF16, 0) == -1
     assert "bad tokens" in binding.last_error()
+
+
+def _chunk_n_bytes(n, tokens, chunks=80):
+    row = ((2 + n) * n + 2 + 3) // 4 * 4
+    return 256 + chunks * tokens * row * 4
+
+
+def test_route_query_n_family_without_a_device_query():
+    """n = 8 and float32 streams have no feature-split kernel, so their routes
+    need no device attribute: the chunks wherever they apply (up to 8192
+    tokens) under "auto" with a workspace, the block kernel otherwise."""
+    lib = binding.load()
+    route = lib.mhc_fused_step_route_n
+    bf, f32 = binding.MHC_BF16, binding.MHC_F32
+    assert route(8, 0, 256, 5120, bf, 1) == 3
+    assert route(8, 0, 2048, 5120, bf, 1) == 3
+    assert route(8, 0, 8192, 5120, bf, 1) == 3
+    assert route(8, 0, 8193, 5120, bf, 1) == 1
+    assert route(8, 0, 256, 5120, bf, 0) == 1
+    assert route(2, 0, 256, 5120, f32, 1) == 3
+    assert route(8, 1, 256, 5120, bf, 1) == 1
+    assert route(8, 3, 8192, 5120, bf, 1) == 3
+    assert route(8, 3, 8193, 5120, bf, 1) == -1
+    assert "chunked kernel does not apply" in binding.last_error()
+    assert route(8, 2, 256, 5120, bf, 1) == -1
+    assert "feature-split kernel does not apply" in binding.last_error()
+    assert route(8, 3, 256, 5120, bf, 0) == -1
+    assert "needs a workspace" in binding.last_error()
+    assert route(3, 0, 256, 5120, bf, 1) == -1
+    assert route(8, 5, 256, 5120, bf, 1) == -1
+    assert "unknown path" in binding.last_error()
+    # chunk workspace: 256-byte header, then 80 chunks of R floats per token
+    assert lib.mhc_fused_step_n_workspace_bytes(8, 256, 5120, bf) == _chunk_n_bytes(8, 256)
+    assert lib.mhc_fused_step_n_workspace_bytes(2, 100, 5120, f32) == _chunk_n_bytes(2, 100)
+    assert lib.mhc_fused_step_n_workspace_bytes(4, 64, 5120, f32) == _chunk_n_bytes(4, 64)
+    # 7 units of 32 features: one unit per chunk
+    assert lib.mhc_fused_step_n_workspace_bytes(8, 10, 224, bf) == _chunk_n_bytes(8, 10, 7)
+    assert lib.mhc_fused_step_n_workspace_bytes(8, 8193, 5120, bf) == 0
+
+
+def test_fused_step_n_chunk_path_checks_its_workspace():
+    need = _chunk_n_bytes(8, T, D // 32)
+    assert _call_n(8, path=3) == binding.MHC_ERR_INVALID_ARG
+    assert "needs a workspace" in binding.last_error()
+    ws = A + (1 << 34)
+    assert _call_n(8, path=3, workspace=ws, workspace_bytes=256) == binding.MHC_ERR_INVALID_ARG
+    assert "needed" in binding.last_error()
+    assert _call_n(8, path=3, workspace=ws + 64, workspace_bytes=1 << 30) == \
+        binding.MHC_ERR_INVALID_ARG
+    assert "aligned" in binding.last_error()
+    p = _layout_n(8)
+    assert _call_n(8, path=3, workspace=p["y_out"], workspace_bytes=1 << 30) == \
+        binding.MHC_ERR_INVALID_ARG
+    assert "overlap" in binding.last_error()
+    assert _call_n(8, path=2, workspace=ws, workspace_bytes=need) == binding.MHC_ERR_UNSUPPORTED
+    assert _call_n(8, path=6) == binding.MHC_ERR_INVALID_ARG
 
 
 def test_workspace_bytes_rejects_bad_arguments():
@@ -251,7 +308,7 @@ def _call_n(n_layout, **over):
                 w_packed=p["w_packed"], base=p["base"], scale=p["scale"], gamma=p["gamma"],
                 iters=20, norm_eps=1e-6, hc_eps=1e-6, x_out=p["x_out"], y_out=p["y_out"],
                 pre_out=p["pre_out"], post_out=p["post_out"], comb_out=p["comb_out"],
-                mix_out=p["mix_out"], workspace=None, workspace_bytes=0, stream=None)
+                mix_out=p["mix_out"], path=0, workspace=None, workspace_bytes=0, stream=None)
     args.update(over)
     return binding.load().mhc_fused_step_n(*args.values())
 
@@ -295,12 +352,12 @@ def test_mixes_n_sinkhorn_n_pack_n_validation():
     lib = binding.load()
     p = _layout_n(8)
     st = lib.mhc_mixes_n(8, p["x"], binding.MHC_BF16, T, D, p["w_packed"], p["base"], p["scale"],
-                         20, 1e-6, 1e-6, p["pre_out"], p["post_out"], p["comb_out"], None, None, 0,
-                         None)
+                         20, 1e-6, 1e-6, p["pre_out"], p["post_out"], p["comb_out"], None, 0, None,
+                         0, None)
     assert st == binding.MHC_ERR_INVALID_ARG and "mix_out is NULL" in binding.last_error()
     st = lib.mhc_mixes_n(6, p["x"], binding.MHC_BF16, T, D, p["w_packed"], p["base"], p["scale"],
                          20, 1e-6, 1e-6, p["pre_out"], p["post_out"], p["comb_out"], p["mix_out"],
-                         None, 0, None)
+                         0, None, 0, None)
     assert st == binding.MHC_ERR_UNSUPPORTED
     st = lib.mhc_sinkhorn_n(8, p["mix_out"], T, p["base"], p["scale"], 20, 1e-6, p["pre_out"],
                             p["pre_out"], p["comb_out"], None)

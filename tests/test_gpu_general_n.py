@@ -3,9 +3,10 @@
 Every case is checked against the float64 oracle with the rules of
 tests/parity.py (new streams as correct roundings, everything after them
 teacher-forced on the validated new streams). Both kernels of the family
-are covered: the token-block kernel (path "block", every n and dtype) and
-the feature-split kernel (path "split", n = 2 and 4, bf16, slices of 64,
-128 and 256 features). Cases cover n = 2, 4, 8, bf16
+are covered: the token-block kernel (path "block", every n and dtype), the
+feature-split kernel (path "split", n = 2 and 4, bf16, slices of 64,
+128 and 256 features) and the block kernel in chunks of the features (path
+"chunk", every n and dtype, up to 8192 tokens). Cases cover n = 2, 4, 8, bf16
 and f32 streams, widths from one 32-feature step to d = 5120, odd step counts,
 token counts from one token to several 128-token blocks with a ragged last
 block, in-place updates, guard bands around every output, and, at n = 4,
@@ -107,6 +108,67 @@ def test_general_n_split_parity(n, d, t):
     _log(f"  ties in new streams: {o['n_ties']}; comb sums {comb_sum_stats(out['comb'])}")
 
 
+CHUNK_CASES = [
+    # n, dtype, d, tokens
+    (2, "bf16", 5120, 300),     # 80 units of 64 features: one per chunk
+    (2, "f32", 64, 17),         # 2 units of 32
+    (2, "bf16", 2048, 2048),
+    (4, "bf16", 5120, 257),
+    (4, "bf16", 2080, 100),     # 65 steps: odd count, units of 32 features
+    (4, "bf16", 6400, 5),       # 100 units of 64: 2 per chunk, 50 chunks
+    (4, "f32", 96, 33),
+    (8, "bf16", 5120, 200),     # 160 units of 32: 2 per chunk
+    (8, "bf16", 32, 130),       # a single step
+    (8, "bf16", 1024, 1),       # one token
+    (8, "bf16", 224, 10),       # 7 units
+    (8, "f32", 128, 40),
+    (8, "bf16", 1024, 8192),    # the largest chunked call
+]
+
+
+@pytest.mark.parametrize("n,dtype,d,t", CHUNK_CASES)
+def test_general_n_chunk_parity(n, dtype, d, t):
+    """The chunked block kernel (path "chunk"): parity with the oracle, and
+    the new streams identical to the block kernel's (same per-element
+    arithmetic)."""
+    _log(f"general chunk n={n} {dtype} d={d} T={t}")
+    case = make_case(wl.Workload(900 + 10 * n + d % 7 + t % 5, "general_n_chunk", t, d, dtype,
+                                 n=n))
+    assert mhc.fused_step_route_n(n, "chunk", t, d, dtype) == "chunk"
+    ws = torch.empty(mhc.fused_step_n_workspace_bytes(n, t, d, dtype), dtype=torch.uint8,
+                     device="cuda")
+    out, _ = run_step_n(case, dtype, path="chunk", workspace=ws)
+    o = check_step(case, out, dtype)
+    blk, _ = run_step_n(case, dtype, path="block")
+    assert torch.equal(out["x_out"], blk["x_out"])
+    np.testing.assert_allclose(out["mix"].numpy(), blk["mix"].numpy(), rtol=1e-5, atol=2e-5)
+    _log(f"  ties in new streams: {o['n_ties']}; comb sums {comb_sum_stats(out['comb'])}")
+
+
+@pytest.mark.parametrize("n,dtype,d,t", [(8, "bf16", 2048, 300), (2, "f32", 64, 129),
+                                         (4, "bf16", 5120, 1000)])
+def test_mixes_n_chunk_parity(n, dtype, d, t):
+    w = wl.Workload(940 + n, "mixes_n_chunk", t, d, dtype, n=n)
+    x = wl.streams(w)
+    p = wl.params(w)
+    out = mhc.mixes_n(to_dev(x), mhc.pack_wmix_n(to_dev(p["w_mix"]), dtype), to_dev(p["base"]),
+                      to_dev(p["scale"]), path="chunk")
+    torch.cuda.synchronize()
+    check_mixes(dict(x=x, **p), {k: v.cpu() for k, v in out.items()}, dtype)
+
+
+def test_general_n_chunk_workspace_reused_for_a_smaller_call():
+    """One workspace, two calls in a row, the second with fewer tokens (the
+    partial rows are laid out by the call's own token count)."""
+    n, d = 8, 1024
+    ws = torch.empty(mhc.fused_step_n_workspace_bytes(n, 500, d, "bf16"), dtype=torch.uint8,
+                     device="cuda")
+    for t in (500, 77):
+        case = make_case(wl.Workload(960 + t, "general_n_chunk_reuse", t, d, "bf16", n=n))
+        out, _ = run_step_n(case, "bf16", path="chunk", workspace=ws)
+        check_step(case, out, "bf16")
+
+
 def test_general_n_split_guard_bands_and_in_place():
     """n = 2, d = 1024 (16 slices of 64) through the split kernel: nothing is
     written outside the outputs, and x_out = x gives the same results."""
@@ -181,7 +243,7 @@ def test_general_n2_throughput_shape_sampled():
     _log(f"n2 large: {len(idx)} sampled tokens match; comb sums {comb_sum_stats(out['comb'])}")
 
 
-@pytest.mark.parametrize("npath", ["block", "split"])
+@pytest.mark.parametrize("npath", ["block", "split", "chunk"])
 def test_general_n4_matches_tuned_kernels(npath):
     case = make_case(wl.Workload(760, "general_n4", 700, 5120, "bf16"))
     a, _ = run_step_n(case, "bf16", path=npath)
@@ -247,23 +309,25 @@ def test_sinkhorn_n_worked_example(n):
         np.testing.assert_allclose(out["comb"].cpu().numpy()[0], want, rtol=0, atol=2e-7)
 
 
-def test_general_n_in_place_and_repeatable():
+@pytest.mark.parametrize("path", ["block", "chunk"])
+def test_general_n_in_place_and_repeatable(path):
     case = make_case(wl.Workload(790, "general_n_inplace", 300, 1024, "bf16", n=8))
-    ref, dev = run_step_n(case, "bf16")
-    again, _ = run_step_n(case, "bf16")
+    ref, dev = run_step_n(case, "bf16", path=path)
+    again, _ = run_step_n(case, "bf16", path=path)
     for k in ref:
         assert torch.equal(ref[k], again[k]), k
     x = dev["x"].clone()
     wp = mhc.pack_wmix_n(dev["w_mix"], "bf16")
     out = mhc.fused_step_n(x, dev["f"], dev["pre"], dev["post"], dev["comb"], wp, dev["base"],
-                           dev["scale"], dev["gamma"], x_out=x)
+                           dev["scale"], dev["gamma"], x_out=x, path=path)
     torch.cuda.synchronize()
     for k in ("x_out", "y", "pre", "post", "comb", "mix"):
         assert torch.equal(out[k].cpu(), ref[k]), k
 
 
+@pytest.mark.parametrize("path", ["block", "chunk"])
 @pytest.mark.parametrize("n", [2, 8])
-def test_general_n_guard_bands_untouched(n):
+def test_general_n_guard_bands_untouched(n, path):
     t, d, gpad = 21, 256, 64
     case = make_case(wl.Workload(795 + n, "general_n_guard", t, d, "bf16", n=n))
     dev = _dev(case)
@@ -283,7 +347,7 @@ def test_general_n_guard_bands_untouched(n):
     out = mhc.fused_step_n(dev["x"], dev["f"], dev["pre"], dev["post"], dev["comb"], wp,
                            dev["base"], dev["scale"], dev["gamma"], x_out=vx.view(t, n, d),
                            y_out=vy.view(t, d), pre_out=vp.view(t, n), post_out=vu.view(t, n),
-                           comb_out=vc.view(t, n, n), mix_out=vm.view(t, nm))
+                           comb_out=vc.view(t, n, n), mix_out=vm.view(t, nm), path=path)
     torch.cuda.synchronize()
     for buf, view in ((bx, vx), (by, vy), (bp, vp), (bu, vu), (bc, vc), (bm, vm)):
         assert torch.isnan(buf[:gpad].float()).all() and torch.isnan(buf[-gpad:].float()).all()
