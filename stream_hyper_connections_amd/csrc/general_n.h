@@ -744,13 +744,23 @@ __global__ __launch_bounds__(256) void chunk_finish_kernel(StepArgs a, ChunkN cn
   }
 }
 
-// ----- split and Sinkhorn, one thread per token ----------------------------------------
+// ----- split and Sinkhorn, one lane per comb entry -------------------------------------
 
 // [SW] Code, the split/Sinkhorn kernel, for hc_mult = N: pre = sigmoid(s0 m +
 // b) + eps, post = 2 sigmoid(s1 m + b), comb = row softmax of s2 m + b plus eps,
 // a column division, then iters - 1 rounds of (row, column) divisions, every
 // divisor being (sum + eps). Each division is a multiplication by the
 // correctly rounded reciprocal of the divisor.
+//
+// A token owns kLanes = N*N consecutive lanes, lane e holding entry (j, k) =
+// (e / N, e % N); row j is N consecutive lanes and column k the lanes e with
+// e % N = k. Row and column sums (and the row maximum) are xor butterflies over
+// those lanes, so every lane of a row or column gets the same bits. Lanes
+// e < N also give pre[e], lanes N <= e < 2N post[e - N]. kSinkTokens tokens
+// per 256-thread workgroup.
+template <int N>
+constexpr int kSinkTokens = 256 / (N * N);
+
 template <int N>
 __global__ __launch_bounds__(256) void sinkhorn_kernel(const float* __restrict__ mix,
                                                        int64_t tokens,
@@ -760,70 +770,35 @@ __global__ __launch_bounds__(256) void sinkhorn_kernel(const float* __restrict__
                                                        float* __restrict__ post_out,
                                                        float* __restrict__ comb_out) {
   constexpr int kMix = Dims<N>::kMix;
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (t >= tokens) return;
-  float m[kMix];
+  constexpr int kLanes = N * N;
+  const int e = threadIdx.x % kLanes;
+  const int64_t t = (int64_t)blockIdx.x * kSinkTokens<N> + threadIdx.x / kLanes;
+  if (t >= tokens) return;   // whole tokens: the butterflies never reach a lane that left
+  const float* m = mix + t * kMix;
+  if (e < N) pre_out[t * N + e] = sigmoidf(m[e] * scale[0] + base[e]) + eps;
+  else if (e < 2 * N) post_out[t * N + e - N] = 2.0f * sigmoidf(m[e] * scale[1] + base[e]);
+  const auto row_sum = [](float v) {
 #pragma unroll
-  for (int i = 0; i < kMix / 4; ++i) {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(mix + t * kMix + 4 * i);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) m[4 * i + e] = v[e];
-  }
-  const float s0 = scale[0], s1 = scale[1], s2 = scale[2];
-  float pre[N], post[N], c[N][N];
-#pragma unroll
-  for (int j = 0; j < N; ++j) pre[j] = sigmoidf(m[j] * s0 + base[j]) + eps;
-#pragma unroll
-  for (int k = 0; k < N; ++k) post[k] = 2.0f * sigmoidf(m[N + k] * s1 + base[N + k]);
-#pragma unroll
-  for (int j = 0; j < N; ++j) {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int k = 0; k < N; ++k) {
-      c[j][k] = m[2 * N + N * j + k] * s2 + base[2 * N + N * j + k];
-      mx = fmaxf(mx, c[j][k]);
-    }
-    float rs = 0.f;
-#pragma unroll
-    for (int k = 0; k < N; ++k) {
-      c[j][k] = expf(c[j][k] - mx);
-      rs += c[j][k];
-    }
-    const float inv = 1.0f / rs;
-#pragma unroll
-    for (int k = 0; k < N; ++k) c[j][k] = c[j][k] * inv + eps;
-  }
-  auto colnorm = [&]() {
-#pragma unroll
-    for (int k = 0; k < N; ++k) {
-      float cs = 0.f;
-#pragma unroll
-      for (int j = 0; j < N; ++j) cs += c[j][k];
-      const float inv = 1.0f / (cs + eps);
-#pragma unroll
-      for (int j = 0; j < N; ++j) c[j][k] *= inv;
-    }
+    for (int o = 1; o < N; o <<= 1) v += __shfl_xor(v, o);
+    return v;
   };
-  colnorm();
+  const auto col_sum = [](float v) {
+#pragma unroll
+    for (int o = N; o < kLanes; o <<= 1) v += __shfl_xor(v, o);
+    return v;
+  };
+  float c = m[2 * N + e] * scale[2] + base[2 * N + e];
+  float mx = c;
+#pragma unroll
+  for (int o = 1; o < N; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  c = expf(c - mx);
+  c = c * (1.0f / row_sum(c)) + eps;
+  c *= 1.0f / (col_sum(c) + eps);
   for (int it = 1; it < iters; ++it) {
-#pragma unroll
-    for (int j = 0; j < N; ++j) {
-      float rs = 0.f;
-#pragma unroll
-      for (int k = 0; k < N; ++k) rs += c[j][k];
-      const float inv = 1.0f / (rs + eps);
-#pragma unroll
-      for (int k = 0; k < N; ++k) c[j][k] *= inv;
-    }
-    colnorm();
+    c *= 1.0f / (row_sum(c) + eps);
+    c *= 1.0f / (col_sum(c) + eps);
   }
-#pragma unroll
-  for (int j = 0; j < N; ++j) {
-    pre_out[t * N + j] = pre[j];
-    post_out[t * N + j] = post[j];
-#pragma unroll
-    for (int k = 0; k < N; ++k) comb_out[(t * N + j) * N + k] = c[j][k];
-  }
+  comb_out[t * kLanes + e] = c;
 }
 
 }  // namespace gen

@@ -1676,8 +1676,9 @@ void launch_block_n(const StepArgs& a, int32_t dtype, int mode, hipStream_t st) 
 template <int N>
 void launch_sinkhorn_n(const float* mix, int64_t tokens, const float* base, const float* scale,
                        int iters, float eps, float* pre, float* post, float* comb, hipStream_t st) {
-  hipLaunchKernelGGL(gen::sinkhorn_kernel<N>, dim3((unsigned)((tokens + 255) / 256)), dim3(256), 0,
-                     st, mix, tokens, base, scale, iters, eps, pre, post, comb);
+  constexpr int kTok = gen::kSinkTokens<N>;
+  hipLaunchKernelGGL(gen::sinkhorn_kernel<N>, dim3((unsigned)((tokens + kTok - 1) / kTok)),
+                     dim3(256), 0, st, mix, tokens, base, scale, iters, eps, pre, post, comb);
 }
 
 // The two kernels of the general step: one pass over the streams, then the
