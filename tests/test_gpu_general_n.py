@@ -395,3 +395,64 @@ def test_general_n8_throughput_shape_sampled():
     stats = comb_sum_stats(out["comb"])
     assert stats["col_dev_max"] <= 1e-5
     _log(f"n8 large: {len(idx)} sampled tokens match; comb sums {stats}")
+
+
+@pytest.mark.parametrize("n,path", [(8, "chunk"), (2, "chunk"), (4, "split"), (8, "block")])
+def test_general_n_replays_from_a_hip_graph(n, path):
+    """Every route of the n-family sets no memory from the host: a call
+    captured into a graph replays to the eager result, with eager work and
+    synchronisation between the replays, and the replays follow new inputs
+    copied into the captured buffers."""
+    t, d = 256, 1024
+    _log(f"general graph n={n} path={path}")
+    cases = [make_case(wl.Workload(980 + 10 * n + i, "general_n_graph", t, d, "bf16", n=n))
+             for i in range(2)]
+    dev = _dev(cases[0])
+    wp = mhc.pack_wmix_n(dev["w_mix"], "bf16")
+    ws = torch.empty(max(mhc.fused_step_n_workspace_bytes(n, t, d, "bf16"), 256),
+                     dtype=torch.uint8, device="cuda")
+    nm = (2 + n) * n
+    outs = dict(x_out=torch.empty_like(dev["x"]), y_out=torch.empty_like(dev["f"]),
+                pre_out=torch.empty((t, n), device="cuda"),
+                post_out=torch.empty((t, n), device="cuda"),
+                comb_out=torch.empty((t, n, n), device="cuda"),
+                mix_out=torch.empty((t, nm), device="cuda"))
+
+    def call():
+        mhc.fused_step_n(dev["x"], dev["f"], dev["pre"], dev["post"], dev["comb"], wp,
+                         dev["base"], dev["scale"], dev["gamma"], cases[0]["iters"],
+                         cases[0]["norm_eps"], cases[0]["hc_eps"], path=path, workspace=ws,
+                         **outs)
+
+    def snapshot():
+        return {k: v.clone() for k, v in outs.items()}
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()                      # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for i in (0, 1, 0):
+        for k in ("x", "f", "pre", "post", "comb"):
+            dev[k].copy_(to_dev(cases[i][k]))
+        torch.cuda.synchronize()
+        for o in outs.values():
+            o.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        got = snapshot()
+        junk = torch.randn(1 << 20, device="cuda").sum()   # eager work between replays
+        call()                                              # the eager reference
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
+        for k, v in snapshot().items():
+            assert torch.equal(got[k], v), (i, k)
+        ref = dict(cases[0])   # the captured parameters, case i's streams and coefficients
+        ref.update({k: cases[i][k] for k in ("x", "f", "pre", "post", "comb")})
+        check_step(ref, {"x_out": got["x_out"].cpu(), "y": got["y_out"].cpu(),
+                         "pre": got["pre_out"].cpu(), "post": got["post_out"].cpu(),
+                         "comb": got["comb_out"].cpu(), "mix": got["mix_out"].cpu()}, "bf16")
