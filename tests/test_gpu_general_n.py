@@ -309,6 +309,31 @@ def test_sinkhorn_n_worked_example(n):
         np.testing.assert_allclose(out["comb"].cpu().numpy()[0], want, rtol=0, atol=2e-7)
 
 
+def test_sinkhorn_n2_eps_quarter_hand_worked():
+    """The split kernel's schedule at n = 2 with eps = 1/4 ("Stream weights for
+    the feed-forward", Code, the split/Sinkhorn kernel), against fractions
+    worked by hand: every eps placement changes them."""
+    from fractions import Fraction
+    g = load_golden("sinkhorn_2x2_eps_quarter.txt")
+
+    def vals(key):
+        return np.array([float(Fraction(v)) for v in g[key]])
+
+    l3 = np.log(3.0)
+    m = np.zeros((1, 8), np.float32)
+    m[0, 0:4] = [l3, -l3, -l3, l3]
+    m[0, 4:8] = np.log(vals("input"))
+    eps = float(g["eps"])
+    for iters, key in ((1, "round1"), (2, "round2")):
+        out = mhc.sinkhorn_n(2, to_dev(m), to_dev(np.zeros(8, np.float32)),
+                             to_dev(np.ones(3, np.float32)), iters, eps)
+        torch.cuda.synchronize()
+        np.testing.assert_allclose(out["comb"].cpu().numpy()[0].reshape(-1), vals(key),
+                                   rtol=0, atol=3e-7)
+        np.testing.assert_allclose(out["pre"].cpu().numpy()[0], vals("pre"), rtol=0, atol=3e-7)
+        np.testing.assert_allclose(out["post"].cpu().numpy()[0], vals("post"), rtol=0, atol=3e-7)
+
+
 @pytest.mark.parametrize("path", ["block", "chunk"])
 def test_general_n_in_place_and_repeatable(path):
     case = make_case(wl.Workload(790, "general_n_inplace", 300, 1024, "bf16", n=8))

@@ -95,6 +95,44 @@ def test_worked_example_kronecker_20_rounds(n):
     assert np.all(np.abs(comb.sum(axis=2) - 1) < G["sum_tol_after_20"])
 
 
+# ---- the kernel's schedule with eps != 0, worked by hand ------------------------------
+
+GE = load_golden("sinkhorn_2x2_eps_quarter.txt")
+
+
+def _eps_case_m():
+    """n = 2 mixes: pre slots (log 3, -log 3), post slots (-log 3, log 3), comb
+    slots log A for the course page's A."""
+    a = _mat(GE["input"])
+    m = _logits_to_m(np.log(a)[None], 2)
+    l3 = np.log(3.0)
+    m[0, 0:4] = [l3, -l3, -l3, l3]
+    return m
+
+
+@pytest.mark.parametrize("iters,key", [(1, "round1"), (2, "round2")])
+def test_eps_quarter_schedule_hand_worked(iters, key):
+    """Every placement of eps in the schedule (after the softmax, in the first
+    column division, in each later row and column division) changes these
+    fractions; dropping or moving any one of them fails this test."""
+    eps = float(GE["eps"])
+    pre, post, comb = split_sinkhorn(_eps_case_m(), [1, 1, 1], np.zeros(8), iters=iters,
+                                     hc_eps=eps, n=2)
+    np.testing.assert_allclose(comb[0], _mat(GE[key]), rtol=0, atol=1e-15)
+    np.testing.assert_allclose(pre[0], [float(v) for v in GE["pre"]], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(post[0], [float(v) for v in GE["post"]], rtol=0, atol=1e-15)
+
+
+def test_eps_quarter_fractions_follow_from_each_other():
+    """The golden's intermediate lines are consistent: round 2's row step is
+    round 1 divided by (row sum + eps), elementwise in exact arithmetic."""
+    e = GE["eps"]
+    r1 = GE["round1"]
+    rows = [r1[0:2], r1[2:4]]
+    want = [v / (sum(r) + e) for r in rows for v in r]
+    assert want == GE["round2_rows"]
+
+
 # ---- invariants and closed forms --------------------------------------------------------
 
 def _random_m(t, seed, scale=2.86):
