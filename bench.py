@@ -392,7 +392,7 @@ def crossover_bench(d=5120, sizes=(512, 1024, 1536, 2048, 2560, 3072, 4096), cal
         wp = mhc.pack_wmix(0.02 * torch.randn((24, N * d), device="cuda", generator=g), "bf16")
         base = 0.1 * torch.randn(24, device="cuda", generator=g)
         scale, gamma = torch.ones(3, device="cuda"), torch.ones(d, device="cuda")
-        ws = torch.empty(mhc.fused_step_workspace_bytes(t, d, "bf16"), dtype=torch.uint8,
+        ws = torch.zeros(mhc.fused_step_workspace_bytes(t, d, "bf16"), dtype=torch.uint8,
                          device="cuda")
         outs = dict(x_out=torch.empty_like(x), y_out=torch.empty_like(f),
                     pre_out=torch.empty_like(pre), post_out=torch.empty_like(post),
@@ -415,7 +415,7 @@ def crossover_bench(d=5120, sizes=(512, 1024, 1536, 2048, 2560, 3072, 4096), cal
                 b.record()
                 b.synchronize()
                 per.append(a.elapsed_time(b) * 1e3 / calls)
-            if mhc.split_status(ws) != 0:
+            if mhc.split_status(ws) != 0:   # sticky: covers every call above
                 raise RuntimeError("a cross-workgroup wait of the feature-split kernel gave up")
             line[path] = round(float(np.median(per)), 1)
         print(json.dumps(line), flush=True)
@@ -453,9 +453,6 @@ def parse():
     ap.add_argument("--crossover", action="store_true",
                     help="call time of the chunked and feature-split routes from 512 to 4,096 "
                          "tokens, back to back; one JSON line per size")
-    ap.add_argument("--copy-ceiling", action="store_true",
-                    help="time plain copies in the access patterns of the step's kernels "
-                         "(libmhc_probe.so) at the workload's shape; one JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain device-to-device copy of 2 GiB instead (the reference "
                          "kernel for scaling the HBM byte counters)")
@@ -480,70 +477,6 @@ def copy_calibration(steps):
     ms = a.elapsed_time(b) / steps
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms_per_copy": round(ms, 4),
                       "GBps_read_plus_write": round(2 * n / ms / 1e6, 1)}), flush=True)
-
-
-COPY_PATTERNS = (
-    # name, probe pattern id, what it stands for
-    ("contiguous", 0, "flat copy of X and F, 1 KB contiguous per load instruction"),
-    ("slice_8x128", 1, "feature-split step kernel: 128-feature slices, 8 rows x 128 B"),
-    ("token_8x128", 2, "backward row kernel: 128-token blocks, 8 rows x 128 B"),
-    ("token_16x64", 3, "MFMA result order: 128-token blocks, 16 rows x 64 B"),
-    ("read_only", 4, "flat read of X and F"),
-    ("write_only", 5, "flat write of XO and Y"),
-)
-
-
-def copy_ceiling(w, steps, warmup):
-    """Plain copies (no arithmetic) in the access patterns of the step's
-    kernels, at the workload's shape (X [T][n][d] -> XO, F [T][d] -> Y, bf16):
-    the practical bandwidth each pattern reaches on this GPU. HIP events on
-    torch's current stream, around `steps` launches after `warmup`."""
-    import ctypes
-    import torch
-    from stream_hyper_connections_amd.build import PROBE_LIB
-    if not os.path.exists(PROBE_LIB):
-        raise RuntimeError(f"{PROBE_LIB} is not built; run python -m stream_hyper_connections_amd.build")
-    lib = ctypes.CDLL(PROBE_LIB)
-    fn = lib.mhc_probe_copy
-    fn.restype = ctypes.c_int
-    fn.argtypes = [ctypes.c_int] + [ctypes.c_void_p] * 4 + [ctypes.c_int64, ctypes.c_int,
-                                                            ctypes.c_int, ctypes.c_int,
-                                                            ctypes.c_void_p, ctypes.c_void_p]
-    t, n, d = w.tokens, w.n, w.d
-    x = torch.ones(t * n * d, dtype=torch.bfloat16, device="cuda")
-    f = torch.ones(t * d, dtype=torch.bfloat16, device="cuda")
-    xo, y = torch.empty_like(x), torch.empty_like(f)
-    sink = torch.empty(4096, dtype=torch.uint8, device="cuda")
-    cus = torch.cuda.get_device_properties(0).multi_processor_count
-    stream = torch.cuda.current_stream().cuda_stream
-    bx, bf = x.numel() * 2, f.numel() * 2
-    out = {}
-    for name, pid, what in COPY_PATTERNS:
-        def call():
-            rc = fn(pid, x.data_ptr(), f.data_ptr(), xo.data_ptr(), y.data_ptr(), t, n, d, cus,
-                    sink.data_ptr(), stream)
-            if rc != 0:
-                raise RuntimeError(f"mhc_probe_copy({name}) returned {rc}")
-        for _ in range(warmup):
-            call()
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(steps):
-            call()
-        b.record()
-        torch.cuda.synchronize()
-        ms = a.elapsed_time(b) / steps
-        moved = (bx + bf) * (1 if pid in (4, 5) else 2)
-        out[name] = {"ms": round(ms, 4), "bytes": moved, "GBps": round(moved / ms / 1e6, 1),
-                     "frac_of_8TBps": round(moved / ms / 1e6 / 8000.0, 4), "pattern": what}
-        print(f"  {name}: {ms:.3f} ms, {moved / ms / 1e6:.1f} GB/s", flush=True)
-    print(json.dumps({"metric": "plain-copy bandwidth per access pattern", "unit": "GB/s",
-                      "config": {"workload": w.name, "tokens": t, "n_streams": n, "d": d,
-                                 "dtype": "bf16"}, "cus": cus, "patterns": out}), flush=True)
-
-
-SWEEP_ITERS = (1, 2, 3, 5, 10, 20, 50, 100, 200)
 
 
 def sinkhorn_sweep(w, mix, base, scale, steps, warmup):
@@ -672,9 +605,6 @@ def main():
     if args.crossover:
         crossover_bench()
         return
-    if args.copy_ceiling:
-        copy_ceiling(w, args.steps, args.warmup)
-        return
     dev = torch.device("cuda:0")
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     elem = 2 if w.dtype == "bf16" else 4
@@ -737,6 +667,8 @@ def main():
     wall = time.perf_counter() - t0
 
     if route != "tile" and args.form == "fused":
+        # the status word is sticky (no call clears it), so this one read
+        # covers every warm-up and timed call on the workspace
         ws = mhc.workspace_for(dev, mhc.fused_step_workspace_bytes(w.tokens, w.d, w.dtype))
         if mhc.split_status(ws) != 0:
             print("bench.py: a cross-workgroup wait of the feature-split kernel gave up; the "

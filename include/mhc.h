@@ -13,8 +13,11 @@
  *
  * Conventions shared by every entry point
  *   - All data pointers are DEVICE pointers, contiguous, row-major, and must be
- *     16-byte aligned. The caller owns all memory; the library allocates
- *     nothing and keeps no state between calls.
+ *     16-byte aligned. The caller owns all memory and the library allocates
+ *     none. Its only state is a per-device cache of two device attributes
+ *     (compute-unit count, cooperative-launch support), filled on first use
+ *     with atomic stores, so calls from several host threads are safe; the
+ *     per-thread detail of mhc_last_error() is the other.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
  *     and the call returns without synchronising.
  *   - `dtype` (an mhc_dtype value) is the dtype of the stream tensors x, f,
@@ -44,7 +47,7 @@
 extern "C" {
 #endif
 
-#define MHC_ABI_VERSION 8
+#define MHC_ABI_VERSION 9
 #define MHC_N_STREAMS 4
 #define MHC_N_MIX 24
 
@@ -124,9 +127,9 @@ mhc_status mhc_pack_wmix(const float* w_mix, int32_t d, int32_t dtype, void* w_p
  *     compute units and cooperative launch support. About 17 MB for d = 5120
  *     on 256 CUs, plus 96 bytes per token for the mixes rows.
  *   - Chunked kernels: at most 8192 tokens; MHC_BF16 streams with d a
- *     multiple of 64 up to 5120, or MHC_F32 streams. 256 bytes plus 128
- *     bytes per token and chunk, a chunk being 512 features (bf16) or 256
- *     (f32): 1,280 or 2,560 bytes per token at d = 5120.
+ *     multiple of 64 up to 5120, or MHC_F32 streams. The 16,384-byte header
+ *     plus 128 bytes per token and chunk, a chunk being 512 features (bf16)
+ *     or 256 (f32): 1,280 or 2,560 bytes per token at d = 5120.
  */
 int64_t mhc_fused_step_workspace_bytes(int64_t tokens, int32_t d, int32_t dtype);
 
@@ -175,10 +178,16 @@ int32_t mhc_fused_step_route(int32_t path, int64_t tokens, int32_t d, int32_t dt
  *            finishes each token (two plain launches; for small calls).
  *          workspace_bytes below the chosen route's need is
  *          MHC_ERR_INVALID_ARG. Calls that share a workspace must be ordered
- *          (same stream or synchronised). After the call has completed, the
- *          32-bit word at workspace offset 0 is 0; the feature-split kernel
- *          sets it to 1 if a cross-workgroup wait gave up after its bounded
- *          number of polls, in which case the outputs are invalid.
+ *          (same stream or synchronised).
+ *          The first 16,384 bytes are a header that must be ZERO-FILLED
+ *          before the workspace is first used (e.g. hipMemset once after
+ *          allocating it); every call leaves the header as it found it, so
+ *          no clearing is needed between calls. The 32-bit word at offset 0
+ *          is the status word: the feature-split kernel sets it to 1 when a
+ *          cross-workgroup wait gave up after its bounded number of polls,
+ *          in which case that call's outputs are invalid. The library never
+ *          clears it: it reports every such call since the caller last wrote
+ *          0 there.
  */
 mhc_status mhc_fused_step(const void* x, const void* f, int32_t dtype, int64_t tokens,
                           int32_t d, const float* pre_in, const float* post_in,
@@ -273,10 +282,10 @@ mhc_status mhc_pack_wmix_n(int32_t n, const float* w_mix, int32_t d, int32_t dty
  *     S a multiple of 64 of at most 256 (n = 2) or 128 (n = 4) features and
  *     16 <= ns <= 64 slices, at most one per compute unit, on a device with
  *     cooperative launch;
- *   - the chunked block kernel: tokens <= 8192, any n and dtype; 256 bytes plus
- *     4 * R bytes per token and chunk, R = (2+n)n + 2 rounded up to a multiple
- *     of 4, with up to 80 chunks of whole units (64 features for bf16 at
- *     n <= 4, else 32) across d.
+ *   - the chunked block kernel: tokens <= 8192, any n and dtype; the
+ *     16,384-byte header plus 4 * R bytes per token and chunk, R = (2+n)n
+ *     + 2 rounded up to a multiple of 4, with up to 80 chunks of whole units
+ *     (64 features for bf16 at n <= 4, else 32) across d.
  */
 int64_t mhc_fused_step_n_workspace_bytes(int32_t n, int64_t tokens, int32_t d, int32_t dtype);
 
@@ -315,7 +324,9 @@ int32_t mhc_fused_step_route_n(int32_t n, int32_t path, int64_t tokens, int32_t 
  * not apply.
  * Workspace: NULL / 0 bytes, or device memory of at least the chosen route's
  * bytes (mhc_fused_step_n_workspace_bytes() covers both), 256-byte aligned,
- * overlapping no other argument; a smaller one is MHC_ERR_INVALID_ARG.
+ * overlapping no other argument; a smaller one is MHC_ERR_INVALID_ARG. Its
+ * 16,384-byte header must be zero-filled before first use and keeps the
+ * status word, as for mhc_fused_step.
  */
 mhc_status mhc_fused_step_n(int32_t n, const void* x, const void* f, int32_t dtype,
                             int64_t tokens, int32_t d, const float* pre_in,
@@ -365,7 +376,9 @@ mhc_status mhc_sinkhorn_n(int32_t n, const float* mixes, int64_t tokens, const f
  *   give identical results.
  * Workspace: REQUIRED, mhc_fused_step_backward_workspace_bytes_n() bytes,
  *   256-byte aligned, overlapping no other argument; calls sharing one must be
- *   ordered. Its contents need no initialisation.
+ *   ordered. The backward leaves the first 16,384 bytes (the forward kernels'
+ *   header) untouched, so one workspace can serve forward and backward calls;
+ *   the rest needs no initialisation.
  * Same conventions as above otherwise (no output may overlap an input).
  */
 int64_t mhc_fused_step_backward_workspace_bytes_n(int32_t n, int64_t tokens, int32_t d);

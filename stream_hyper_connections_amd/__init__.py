@@ -9,6 +9,7 @@ for torch tensors, and ``workloads`` holds the seeded synthetic inputs.
 from .binding import (  # noqa: F401
     MhcError,
     abi_version,
+    clear_split_status,
     d_granule,
     PATHS,
     PATHS_N,
@@ -26,6 +27,7 @@ from .binding import (  # noqa: F401
     load,
     mixes,
     mixes_n,
+    new_workspace,
     n_mix,
     pack_wmix,
     pack_wmix_n,

@@ -15,7 +15,9 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libmhc.so")
+# MHC_LIBRARY names another build of the same library (the CPU sanitizer test
+# loads an AddressSanitizer build this way); by default the in-tree one.
+LIB_PATH = os.environ.get("MHC_LIBRARY") or os.path.join(_PKG, "libmhc.so")
 
 MHC_OK, MHC_ERR_INVALID_ARG, MHC_ERR_UNSUPPORTED, MHC_ERR_HIP = 0, 1, 2, 3
 MHC_F32, MHC_BF16 = 0, 1
@@ -194,37 +196,60 @@ def fused_step_workspace_bytes(tokens: int, d: int, dtype) -> int:
     return n
 
 
+def new_workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    """A zero-filled workspace of nbytes (the library requires its header to
+    be zero before first use and leaves it so after every call)."""
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
+
+
 def workspace_for(device, nbytes: int) -> torch.Tensor:
     """A workspace of at least nbytes, cached per (device, current stream):
     calls that share it are ordered by their stream."""
     key = (torch.device(device).index, torch.cuda.current_stream(device).cuda_stream)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        ws = new_workspace(nbytes, device)
         _workspaces[key] = ws
     return ws
 
 
 def split_status(workspace: torch.Tensor) -> int:
-    """The status word of a feature-split call (synchronises): 0, or 1 if a
-    cross-workgroup wait gave up."""
+    """The status word of a workspace (synchronises): 0, or 1 if a
+    cross-workgroup wait of any feature-split call since the last
+    clear_split_status gave up (that call's outputs are invalid)."""
     return int(workspace[:4].view(torch.int32).item())
+
+
+def clear_split_status(workspace: torch.Tensor) -> None:
+    """Write 0 to the status word (on the current stream; the library never
+    clears it)."""
+    workspace[:4].zero_()
+
+
+def _raise_on_status(fn, workspace):
+    if workspace is not None and split_status(workspace) != 0:
+        clear_split_status(workspace)
+        raise MhcError(fn, MHC_ERR_HIP, "a cross-workgroup wait of the feature-split kernel "
+                       "gave up; the outputs of this call are invalid")
 
 
 def fused_step(x, f, pre_in, post_in, comb_in, w_packed, base, scale, gamma, iters=20,
                norm_eps=1e-6, hc_eps=1e-6, x_out=None, y_out=None, pre_out=None, post_out=None,
-               comb_out=None, mix_out=None, want_mix=False, path="auto", workspace=None) -> dict:
+               comb_out=None, mix_out=None, want_mix=False, path="auto", workspace=None,
+               check_status=False) -> dict:
     """mhc_fused_step on tensors. x [T,4,d], f [T,d] (bf16 or f32); coefficients
     and parameters float32. Returns dict(x_out, y, pre, post, comb, mix).
 
     path: "tile" (no workspace), "split" (feature-split kernel), "chunk" (chunked
     kernels; both raise ValueError where they do not apply), or "auto" (the
     library's choice by size, with a workspace where one applies). workspace:
-    optional uint8 tensor (a cached one is used otherwise)."""
+    optional zero-initialised uint8 tensor (new_workspace; a cached one is used
+    otherwise). check_status: synchronise after the call and raise MhcError if
+    the workspace's status word is set (it is cleared then)."""
     t, n, d = x.shape
     if n != N_STREAMS:
         raise ValueError("x must be [T, 4, d]")
-    code, ws_ptr, ws_bytes = _workspace_arg(x, t, d, path, workspace)
+    code, ws_ptr, ws_bytes, ws = _workspace_arg(x, t, d, path, workspace)
     x_out = torch.empty_like(x) if x_out is None else x_out
     y_out = torch.empty_like(f) if y_out is None else y_out
     pre_out = _f32_out((t, N_STREAMS), x, pre_out)
@@ -238,36 +263,39 @@ def fused_step(x, f, pre_in, post_in, comb_in, w_packed, base, scale, gamma, ite
         _ptr(x_out), _ptr(y_out), _ptr(pre_out), _ptr(post_out), _ptr(comb_out), _ptr(mix_out),
         code, ws_ptr, ws_bytes, _stream())
     _check("mhc_fused_step", st)
+    if check_status:
+        _raise_on_status("mhc_fused_step", ws)
     return {"x_out": x_out, "y": y_out, "pre": pre_out, "post": post_out, "comb": comb_out,
             "mix": mix_out}
 
 
 def _workspace_arg(x, t, d, path, workspace):
-    """(mhc_path code, workspace pointer, workspace bytes) for path "auto" /
-    "tile" / "split" / "chunk"."""
+    """(mhc_path code, workspace pointer, workspace bytes, workspace tensor or
+    None) for path "auto" / "tile" / "split" / "chunk"."""
     if path not in PATHS:
         raise ValueError(f"unknown path {path!r}")
     if path == "tile":
-        return PATHS["tile"], None, 0
+        return PATHS["tile"], None, 0, None
     if path != "auto":
         fused_step_route(path, t, d, _dtype_code(x))   # raises where the path does not apply
     need = fused_step_workspace_bytes(t, d, _dtype_code(x))
     if need == 0:
-        return PATHS[path], None, 0
+        return PATHS[path], None, 0, None
     if workspace is None:
         workspace = workspace_for(x.device, need)
-    return PATHS[path], _ptr(workspace), workspace.numel() * workspace.element_size()
+    return (PATHS[path], _ptr(workspace), workspace.numel() * workspace.element_size(),
+            workspace)
 
 
 def mixes(x, w_packed, base, scale, iters=20, norm_eps=1e-6, hc_eps=1e-6, pre_out=None,
           post_out=None, comb_out=None, mix_out=None, want_mix=False, path="auto",
-          workspace=None) -> dict:
-    """mhc_mixes on tensors. Returns dict(pre, post, comb, mix). path and
-    workspace as for fused_step."""
+          workspace=None, check_status=False) -> dict:
+    """mhc_mixes on tensors. Returns dict(pre, post, comb, mix). path,
+    workspace and check_status as for fused_step."""
     t, n, d = x.shape
     if n != N_STREAMS:
         raise ValueError("x must be [T, 4, d]")
-    code, ws_ptr, ws_bytes = _workspace_arg(x, t, d, path, workspace)
+    code, ws_ptr, ws_bytes, ws = _workspace_arg(x, t, d, path, workspace)
     pre_out = _f32_out((t, N_STREAMS), x, pre_out)
     post_out = _f32_out((t, N_STREAMS), x, post_out)
     comb_out = _f32_out((t, N_STREAMS, N_STREAMS), x, comb_out)
@@ -277,6 +305,8 @@ def mixes(x, w_packed, base, scale, iters=20, norm_eps=1e-6, hc_eps=1e-6, pre_ou
                           iters, norm_eps, hc_eps, _ptr(pre_out), _ptr(post_out), _ptr(comb_out),
                           _ptr(mix_out), code, ws_ptr, ws_bytes, _stream())
     _check("mhc_mixes", st)
+    if check_status:
+        _raise_on_status("mhc_mixes", ws)
     return {"pre": pre_out, "post": post_out, "comb": comb_out, "mix": mix_out}
 
 
@@ -392,34 +422,37 @@ def fused_step_route_n(n: int, path: str, tokens: int, d: int, dtype,
 
 
 def _workspace_arg_n(x, n, t, d, path, workspace):
-    """(mhc_path code, workspace pointer, workspace bytes) of the n-family for
-    path "block" / "split" / "chunk" (both raise ValueError where they do not
-    apply) / "auto"."""
+    """(mhc_path code, workspace pointer, workspace bytes, workspace tensor or
+    None) of the n-family for path "block" / "split" / "chunk" (both raise
+    ValueError where they do not apply) / "auto"."""
     if path not in PATHS_N:
         raise ValueError(f"unknown path {path!r}")
     if path == "block":
-        return PATHS_N["block"], None, 0
+        return PATHS_N["block"], None, 0, None
     if path != "auto":
         fused_step_route_n(n, path, t, d, _dtype_code(x))   # raises where it does not apply
     need = fused_step_n_workspace_bytes(n, t, d, _dtype_code(x))
     if need == 0:
-        return PATHS_N[path], None, 0
+        return PATHS_N[path], None, 0, None
     if workspace is None:
         workspace = workspace_for(x.device, need)
-    return PATHS_N[path], _ptr(workspace), workspace.numel() * workspace.element_size()
+    return (PATHS_N[path], _ptr(workspace), workspace.numel() * workspace.element_size(),
+            workspace)
 
 
 def fused_step_n(x, f, pre_in, post_in, comb_in, w_packed, base, scale, gamma, iters=20,
                  norm_eps=1e-6, hc_eps=1e-6, x_out=None, y_out=None, pre_out=None, post_out=None,
-                 comb_out=None, mix_out=None, path="auto", workspace=None) -> dict:
+                 comb_out=None, mix_out=None, path="auto", workspace=None,
+                 check_status=False) -> dict:
     """mhc_fused_step_n on tensors: x [T,n,d], f [T,d]; w_packed from pack_wmix_n.
     Returns dict(x_out, y, pre, post, comb, mix) (mix is always produced).
     path: "block" (no workspace), "split" (feature-split kernel: n in {2, 4},
     bf16), "chunk" (the block kernel in chunks of the features, up to 8192
-    tokens) or "auto" (the library's choice by size); workspace: optional uint8
-    tensor (a cached one is used otherwise)."""
+    tokens) or "auto" (the library's choice by size); workspace: optional
+    zero-initialised uint8 tensor (a cached one is used otherwise);
+    check_status as for fused_step."""
     t, n, d = x.shape
-    code, ws_ptr, ws_bytes = _workspace_arg_n(x, n, t, d, path, workspace)
+    code, ws_ptr, ws_bytes, ws = _workspace_arg_n(x, n, t, d, path, workspace)
     x_out = torch.empty_like(x) if x_out is None else x_out
     y_out = torch.empty_like(f) if y_out is None else y_out
     pre_out = _f32_out((t, n), x, pre_out)
@@ -432,16 +465,19 @@ def fused_step_n(x, f, pre_in, post_in, comb_in, w_packed, base, scale, gamma, i
         _ptr(x_out), _ptr(y_out), _ptr(pre_out), _ptr(post_out), _ptr(comb_out), _ptr(mix_out),
         code, ws_ptr, ws_bytes, _stream())
     _check("mhc_fused_step_n", st)
+    if check_status:
+        _raise_on_status("mhc_fused_step_n", ws)
     return {"x_out": x_out, "y": y_out, "pre": pre_out, "post": post_out, "comb": comb_out,
             "mix": mix_out}
 
 
 def mixes_n(x, w_packed, base, scale, iters=20, norm_eps=1e-6, hc_eps=1e-6, pre_out=None,
-            post_out=None, comb_out=None, mix_out=None, path="auto", workspace=None) -> dict:
+            post_out=None, comb_out=None, mix_out=None, path="auto", workspace=None,
+            check_status=False) -> dict:
     """mhc_mixes_n on tensors: x [T,n,d]. Returns dict(pre, post, comb, mix).
-    path and workspace as for fused_step_n."""
+    path, workspace and check_status as for fused_step_n."""
     t, n, d = x.shape
-    code, ws_ptr, ws_bytes = _workspace_arg_n(x, n, t, d, path, workspace)
+    code, ws_ptr, ws_bytes, ws = _workspace_arg_n(x, n, t, d, path, workspace)
     pre_out = _f32_out((t, n), x, pre_out)
     post_out = _f32_out((t, n), x, post_out)
     comb_out = _f32_out((t, n, n), x, comb_out)
@@ -451,6 +487,8 @@ def mixes_n(x, w_packed, base, scale, iters=20, norm_eps=1e-6, hc_eps=1e-6, pre_
                             _ptr(comb_out), _ptr(mix_out), code, ws_ptr, ws_bytes,
                             _stream())
     _check("mhc_mixes_n", st)
+    if check_status:
+        _raise_on_status("mhc_mixes_n", ws)
     return {"pre": pre_out, "post": post_out, "comb": comb_out, "mix": mix_out}
 
 

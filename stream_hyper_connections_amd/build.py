@@ -1,5 +1,4 @@
-"""Build libmhc.so (and libmhc_probe.so, the copy kernels bench.py uses for
-the memory system's practical ceilings) in-tree for gfx950 with hipcc.
+"""Build libmhc.so in-tree for gfx950 with hipcc.
 
 ``python -m stream_hyper_connections_amd.build`` or ``build()`` from Python.
 The flags disable packed-fp32 instruction selection on the device side.
@@ -16,8 +15,6 @@ ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "mhc.hip")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmhc.so")
-PROBE_SRC = os.path.join(PKG, "csrc", "copy_probe.hip")
-PROBE_LIB = os.path.join(PKG, "libmhc_probe.so")
 ARCH = "gfx950"
 
 
@@ -45,7 +42,6 @@ def _compile(src: str, lib: str, verbose: bool) -> None:
 
 def build(verbose: bool = False) -> str:
     _compile(SRC, LIB, verbose)
-    _compile(PROBE_SRC, PROBE_LIB, verbose)
     return LIB
 
 

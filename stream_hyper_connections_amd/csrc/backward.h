@@ -37,6 +37,21 @@
 
 namespace bwd {
 
+// Per-token coefficient gradients (M floats, M even), written in 16-byte
+// pieces through the guarded store where M fills whole pieces, else as 8-byte
+// stores (a store of up to 64 bits needs no guard).
+template <int M>
+__device__ __forceinline__ void put_coef(float* p, const float (&v)[M]) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  if constexpr (M % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < M; i += 4) st4f(p + i, f32x4{v[i], v[i + 1], v[i + 2], v[i + 3]});
+  } else {
+#pragma unroll
+    for (int i = 0; i < M; i += 2) *reinterpret_cast<f32x2_t*>(p + i) = f32x2_t{v[i], v[i + 1]};
+  }
+}
+
 constexpr int kTok = gen::kTok;
 constexpr int kWaves = gen::kWaves;
 constexpr int kThreads = gen::kThreads;
@@ -301,11 +316,9 @@ __global__ __launch_bounds__(256) void stats_kernel(Args a) {
   }
   if (lane == 0) {
     Ws<N> w{a.tokens, d};
-    float* st = a.ws + w.st_off() + t * 4;
-    st[0] = rsqrtf(sx / (float)(N * d) + a.norm_eps);
-    st[1] = rsqrtf(sh / (float)d + a.norm_eps);
-    st[2] = sd;
-    st[3] = 0.f;
+    st4f(a.ws + w.st_off() + t * 4,
+         f32x4{rsqrtf(sx / (float)(N * d) + a.norm_eps), rsqrtf(sh / (float)d + a.norm_eps), sd,
+               0.f});
   }
 }
 
@@ -584,13 +597,14 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(Args a) {
     }
   }
   if (valid && g == 0) {
+    put_coef<N>(a.d_pre_in + t * N, dp);
+    put_coef<N>(a.d_post_in + t * N, du);
+    float dcr[N * N];
 #pragma unroll
-    for (int k = 0; k < N; ++k) {
-      a.d_pre_in[t * N + k] = dp[k];
-      a.d_post_in[t * N + k] = du[k];
+    for (int j = 0; j < N; ++j)
 #pragma unroll
-      for (int j = 0; j < N; ++j) a.d_comb_in[(t * N + j) * N + k] = dC[j][k];
-    }
+      for (int k = 0; k < N; ++k) dcr[j * N + k] = dC[j][k];
+    put_coef<N * N>(a.d_comb_in + t * N * N, dcr);
   }
 }
 
@@ -991,13 +1005,14 @@ __global__ __launch_bounds__(kThreads) void row_kernel(Args a) {
     }
   }
   if (valid && x8 == 0) {
+    put_coef<N>(a.d_pre_in + t * N, dp);
+    put_coef<N>(a.d_post_in + t * N, du);
+    float dcr[N * N];
 #pragma unroll
-    for (int k = 0; k < N; ++k) {
-      a.d_pre_in[t * N + k] = dp[k];
-      a.d_post_in[t * N + k] = du[k];
+    for (int j = 0; j < N; ++j)
 #pragma unroll
-      for (int j = 0; j < N; ++j) a.d_comb_in[(t * N + j) * N + k] = dC[j][k];
-    }
+      for (int k = 0; k < N; ++k) dcr[j * N + k] = dC[j][k];
+    put_coef<N * N>(a.d_comb_in + t * N * N, dcr);
   }
 }
 
@@ -1301,12 +1316,11 @@ __global__ __launch_bounds__(64) void scale_kernel(Args a) {
     em[i] = s2;
   }
   __syncthreads();
-  if (i == 0) {
-    float s[3] = {0.f, 0.f, 0.f};
-    for (int j = 0; j < kMix; ++j) s[j < N ? 0 : (j < 2 * N ? 1 : 2)] += em[j];
-    a.d_scale[0] = s[0];
-    a.d_scale[1] = s[1];
-    a.d_scale[2] = s[2];
+  if (i < 3) {   // d scale[i]: the slots of pre (i = 0), post (1) or comb (2), in order
+    const int j0 = i == 0 ? 0 : (i == 1 ? N : 2 * N), j1 = i == 0 ? N : (i == 1 ? 2 * N : kMix);
+    float v = 0.f;
+    for (int j = j0; j < j1; ++j) v += em[j];
+    a.d_scale[i] = v;
   }
 }
 

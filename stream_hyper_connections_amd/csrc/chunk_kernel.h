@@ -27,14 +27,14 @@
 //     16 lanes of wave 0 ([SW] Code, hc_split_sinkhorn), and rewrites y_out
 //     = S(gamma * (h * rh)) ([RN] RMSNorm).
 // No workgroup ever waits for another: the launch boundary orders the partial
-// rows. Workspace: a 256-byte header (word 0, the status word, is set to 0;
-// nothing in this path can fail after launch) and then the partial rows,
-// [chunk][token][32] float32.
+// rows. Workspace: the step kernels' shared header (fsplit::kWsHeader bytes,
+// which this path leaves untouched: nothing in it can fail after launch) and
+// then the partial rows, [chunk][token][32] float32.
 
 namespace pipe {
 
 constexpr int kPart = 32;                  // floats per partial row
-constexpr int64_t kChunkHeader = 256;      // bytes before the partial rows
+constexpr int64_t kChunkHeader = fsplit::kWsHeader;   // bytes before the partial rows
 
 inline int64_t chunk_workspace_bytes(int nchunks, int64_t tokens) {
   return kChunkHeader + (int64_t)nchunks * tokens * kPart * 4;
@@ -69,8 +69,8 @@ __device__ __forceinline__ void chunk_pair(int sa, int sn, bool more, Ctx& c, Ha
     const uint32_t col = (uint32_t)sa * 64;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      bstore<MHC_STORE_AUX>(c.xor_, c.xoff, col + (uint32_t)k * c.d2, xa[k]);
-      bstore<MHC_STORE_AUX>(c.xor_, c.xoff, col + 64 + (uint32_t)k * c.d2, xb[k]);
+      bstore<kStoreAux>(c.xor_, c.xoff, col + (uint32_t)k * c.d2, xa[k]);
+      bstore<kStoreAux>(c.xor_, c.xoff, col + 64 + (uint32_t)k * c.d2, xb[k]);
     }
     bstore<0>(c.yr, c.foff, col, h_a);
     bstore<0>(c.yr, c.foff, col + 64, h_b);
@@ -101,7 +101,6 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(StepArgs a, int nchunks
   const int pair0 = chunk * cpairs;
   const int np = min(cpairs, npairs - pair0);
   const int cnt = wave < np ? (np - wave + kWaves - 1) / kWaves : 0;
-  if (blockIdx.x == 0 && tid == 0) *reinterpret_cast<uint32_t*>(ws) = 0u;
 
   const int64_t t0 = (int64_t)tile * kTok;
   const int ntok = (int)min((int64_t)kTok, a.tokens - t0);
@@ -217,7 +216,6 @@ __global__ __launch_bounds__(kThreads) void chunk_f32_kernel(StepArgs a, int nch
   const int s0 = chunk * csteps;
   const int ns = min(csteps, nsteps - s0);
   const int cnt = wave < ns ? (ns - wave + kWaves - 1) / kWaves : 0;
-  if (blockIdx.x == 0 && tid == 0) *reinterpret_cast<uint32_t*>(ws) = 0u;
 
   const int64_t t0 = (int64_t)tile * kTok;
   const int64_t t = t0 + tr;

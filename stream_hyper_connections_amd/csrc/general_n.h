@@ -330,7 +330,7 @@ struct ChunkN {
   int per;        // units per chunk
   int nchunks;    // chunks per row
 };
-constexpr int64_t kChunkHeaderN = 256;
+constexpr int64_t kChunkHeaderN = fsplit::kWsHeader;
 template <int N>
 __host__ __device__ constexpr int row_n() { return ((Dims<N>::kMix + 2 + 3) / 4) * 4; }
 
@@ -371,7 +371,6 @@ __global__ __launch_bounds__(kThreads) void block_kernel(StepArgs a, ChunkN cn) 
   const int u1 = CH ? min(u0 + cn.per, nunits_all) : nunits_all;
   const u32x4* wpk = static_cast<const u32x4*>(a.wpk);
   const u32x4* wpk0 = wpk + (size_t)u0 * S::kVecs;
-  if (CH && blockIdx.x == 0 && tid == 0) *reinterpret_cast<uint32_t*>(cn.ws) = 0u;
 
   // packed weights of the first unit, part 0 (the other parts follow below)
   u32x4 wst[S::kStage];

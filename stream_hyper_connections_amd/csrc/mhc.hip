@@ -32,6 +32,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "mhc.h"
@@ -58,30 +59,14 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// Two floats -> two bf16 (round to nearest even), `a` in the low half.
-// float -> bf16 bits, round to nearest even, placed in the HIGH half of the
-// returned word (low half is garbage); every NaN becomes the quiet NaN 0x7fc0.
-__device__ __forceinline__ uint32_t rne_bf16_hi(float x) {
-  const uint32_t u = __float_as_uint(x);
-  const uint32_t r = u + 0x7fffu + ((u >> 16) & 1u);
-  return x != x ? 0x7fc00000u : r;
-}
-
-#ifndef MHC_HW_BF16
-#define MHC_HW_BF16 1
-#endif
-
 // Two floats -> two bf16 (round to nearest even), `a` in the low half: the
 // packed hardware conversion (v_cvt_pk_bf16_f32, round to nearest even in the
-// default mode), or the integer form above.
+// default mode).
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  if (MHC_HW_BF16) {
-    typedef float f32x2_t __attribute__((ext_vector_type(2)));
-    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-    const f32x2_t v = {a, b};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
-  }
-  return __builtin_amdgcn_perm(rne_bf16_hi(b), rne_bf16_hi(a), 0x07060302u);
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // Every vector store of more than 64 bits is followed by this guard. On gfx950
@@ -89,15 +74,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 // instruction (no wait state), and such stores have written wrong data for
 // some lanes (lanes 12-15 of each 16-lane row, the words rewritten first,
 // intermittently). A few wait states right after the store, with the
-// scheduler kept from moving anything across, avoid it.
-#ifndef MHC_GUARD_NOP
-#define MHC_GUARD_NOP 4
-#endif
-#define MHC_STR2(x) #x
-#define MHC_STR(x) MHC_STR2(x)
-__device__ __forceinline__ void store_guard() {
+// scheduler kept from moving anything across, avoid it. The store's data is an
+// input of the wait-state asm, so its registers stay allocated to it until the
+// wait states have passed: no copy inserted after scheduling can land between
+// the store and the guard and overwrite them (a CPU test checks the compiled
+// code: every store wider than 64 bits is followed at once by s_nop 4).
+template <class T>
+__device__ __forceinline__ void store_guard(const T& data) {
   __builtin_amdgcn_sched_barrier(0);
-  __asm__ volatile("s_nop " MHC_STR(MHC_GUARD_NOP));
+  __asm__ volatile("s_nop 4" ::"v"(data));
   __builtin_amdgcn_sched_barrier(0);
 }
 // pins the store that follows in place (nothing is scheduled across it)
@@ -107,39 +92,23 @@ __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<
 __device__ __forceinline__ void st16(void* p, u32x4 v) {
   store_pin();
   *reinterpret_cast<u32x4*>(p) = v;
-  store_guard();
+  store_guard(v);
 }
 __device__ __forceinline__ void st4f(float* p, f32x4 v) {
   store_pin();
   *reinterpret_cast<f32x4*>(p) = v;
-  store_guard();
+  store_guard(v);
 }
 
-#ifndef MHC_STREAM_NT
-#define MHC_STREAM_NT 1
-#endif
-#ifndef MHC_SKIP_PAD
-#define MHC_SKIP_PAD 1
-#endif
-#ifndef MHC_FORCE_HMEM
-#define MHC_FORCE_HMEM 0
-#endif
-
-
-// Stream tensors are touched once: optionally load/store them non-temporally so
-// they do not push the packed projection out of L2.
+// Stream tensors are touched once: load/store them non-temporally so they do
+// not push the packed projection out of L2.
 __device__ __forceinline__ u32x4 lds16(const void* p) {
-  if (MHC_STREAM_NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-  return ld16(p);
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 __device__ __forceinline__ void sts16(void* p, u32x4 v) {
-  if (MHC_STREAM_NT) {
-    store_pin();
-    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
-    store_guard();
-  } else {
-    st16(p, v);
-  }
+  store_pin();
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+  store_guard(v);
 }
 
 __device__ __forceinline__ float sigmoidf(float z) { return 1.0f / (1.0f + expf(-z)); }
@@ -300,7 +269,7 @@ __device__ __forceinline__ u32x4 step_bf(const InBf& in, LaneState<kTilesBf>& st
 #pragma unroll
     for (int q = 0; q < kTilesBf; ++q) {
       // the last tile holds columns 64..79 of which 72..79 are padding
-      const bool pad = MHC_SKIP_PAD && q == kTilesBf - 1 && (lane & 15) >= 3 * kMix - 64;
+      const bool pad = q == kTilesBf - 1 && (lane & 15) >= 3 * kMix - 64;
       const u32x4 B = pad ? u32x4{0, 0, 0, 0} : wstep[(k * kTilesBf + q) * 64 + lane];
       st.acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8, B),
                                                           st.acc[q], 0, 0, 0);
@@ -734,9 +703,7 @@ constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw buffer, 32-bit data format
 constexpr int kNT = 2;                         // cache-policy bit: non-temporal
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
-#ifndef MHC_STORE_AUX
-#define MHC_STORE_AUX 0
-#endif
+constexpr int kStoreAux = 0;                   // cache policy of the tile kernels' stream stores
 
 struct __align__(16) Smem {
   union {
@@ -762,7 +729,7 @@ __device__ __forceinline__ void bstore(rsrc_t r, uint32_t voff, uint32_t soff, u
   __builtin_amdgcn_raw_buffer_store_b128(
       __builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b128(r, 0, 0, 0)), v), r,
       (int)voff, (int)soff, AUX);
-  store_guard();
+  store_guard(v);
 }
 
 template <int CTRL>
@@ -940,8 +907,8 @@ __device__ __forceinline__ void pair_body(int p, int cnt, int wave, Ctx& c, Smem
     const uint32_t col = (uint32_t)sa * 64;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      bstore<MHC_STORE_AUX>(c.xor_, c.xoff, col + (uint32_t)k * c.d2, xa[k]);
-      bstore<MHC_STORE_AUX>(c.xor_, c.xoff, col + 64 + (uint32_t)k * c.d2, xb[k]);
+      bstore<kStoreAux>(c.xor_, c.xoff, col + (uint32_t)k * c.d2, xa[k]);
+      bstore<kStoreAux>(c.xor_, c.xoff, col + 64 + (uint32_t)k * c.d2, xb[k]);
     }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -1299,7 +1266,7 @@ typedef void (*StepKernel)(StepArgs);
 
 StepKernel pick_step_kernel(int32_t dtype, int mode, int32_t d) {
   const int nsteps = d / kStep;
-  const bool hreg = !MHC_FORCE_HMEM && (nsteps + kWaves - 1) / kWaves <= kMaxSpw;
+  const bool hreg = (nsteps + kWaves - 1) / kWaves <= kMaxSpw;
   if (dtype == MHC_BF16) {
     if (mode == kMixesOnly) return step_kernel<MHC_BF16, kMixesOnly, false>;
     return hreg ? step_kernel<MHC_BF16, kFused, true> : step_kernel<MHC_BF16, kFused, false>;
@@ -1308,25 +1275,25 @@ StepKernel pick_step_kernel(int32_t dtype, int mode, int32_t d) {
   return step_kernel<MHC_F32, kFused, false>;
 }
 
-#ifndef MHC_FORCE_GENERIC
-#define MHC_FORCE_GENERIC 0
-#endif
-
-// Compute units of the current device (cached per device ordinal).
+// Compute units of the current device (cached per device ordinal; threads
+// that race here store the same value).
 mhc_status device_cu_count(int* out) {
-  static int cache[64];
+  static std::atomic<int> cache[64];
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return fail(MHC_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
-  if (dev >= 0 && dev < 64 && cache[dev] > 0) {
-    *out = cache[dev];
-    return MHC_OK;
+  if (dev >= 0 && dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *out = c;
+      return MHC_OK;
+    }
   }
   int n = 0;
   e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess || n <= 0)
     return fail(MHC_ERR_HIP, "hipDeviceGetAttribute(multiprocessor count): %s", hipGetErrorString(e));
-  if (dev >= 0 && dev < 64) cache[dev] = n;
+  if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
   *out = n;
   return MHC_OK;
 }
@@ -1338,9 +1305,6 @@ mhc_status device_cu_count(int* out) {
 // exchange traffic). groups = 0 when the kernel does not apply: bf16 streams,
 // S in {64, 96, 128, 160}, at least `ns` compute units and cooperative launch
 // support are required.
-#ifndef MHC_SPLIT_NS
-#define MHC_SPLIT_NS 0   // 0: choose; otherwise only this slice count is considered
-#endif
 
 struct SplitCfg {
   int groups = 0;
@@ -1351,17 +1315,20 @@ struct SplitCfg {
 // Cooperative-launch support of the current device, cached per device
 // ordinal (1 = no, 2 = yes).
 mhc_status coop_supported(bool* ok) {
-  static int coop_cache[64];
+  static std::atomic<int> coop_cache[64];
   int dev = 0, coop = 0;
   hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess && dev >= 0 && dev < 64 && coop_cache[dev] != 0) {
-    coop = coop_cache[dev] - 1;
+  const int cached = (e == hipSuccess && dev >= 0 && dev < 64)
+                         ? coop_cache[dev].load(std::memory_order_relaxed)
+                         : 0;
+  if (cached != 0) {
+    coop = cached - 1;
   } else {
     if (e == hipSuccess)
       e = hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev);
     if (e != hipSuccess)
       return fail(MHC_ERR_HIP, "cooperative-launch attribute: %s", hipGetErrorString(e));
-    if (dev >= 0 && dev < 64) coop_cache[dev] = coop ? 2 : 1;
+    if (dev >= 0 && dev < 64) coop_cache[dev].store(coop ? 2 : 1, std::memory_order_relaxed);
   }
   *ok = coop != 0;
   return MHC_OK;
@@ -1375,7 +1342,6 @@ mhc_status split_config(int32_t dtype, int32_t d, SplitCfg* cfg) {
   if (s != MHC_OK) return s;
   int best_score = -1;
   for (int ns : {32, 40, 48, 64}) {
-    if (MHC_SPLIT_NS != 0 && ns != MHC_SPLIT_NS) continue;
     if (d % ns != 0 || ns > cus) continue;
     const int S = d / ns;
     if (S % 32 != 0 || S < 64 || S > fsplit::kMaxS) continue;
@@ -1393,13 +1359,13 @@ mhc_status split_config(int32_t dtype, int32_t d, SplitCfg* cfg) {
   return MHC_OK;
 }
 
+// The feature-split kernel (cooperative; it leaves the workspace header as it
+// found it, see split_kernel.h), then the split/Sinkhorn of its mixes rows.
 mhc_status launch_split(const StepArgs& a, void* ws, const SplitCfg& cfg, int mode,
                         hipStream_t stream) {
-  const int words = (int)(fsplit::mp_off(cfg.groups) / 4);
-  hipLaunchKernelGGL(fsplit::clear_kernel, dim3(1), dim3(256), 0, stream,
-                     static_cast<uint32_t*>(ws), words);
-  mhc_status s = launch_status("workspace clear kernel launch");
-  if (s != MHC_OK) return s;
+  if (fsplit::ctr_off(cfg.groups, 0) > fsplit::kWsHeader)
+    return fail(MHC_ERR_UNSUPPORTED, "feature-split kernel: %d groups exceed the header", cfg.groups);
+  mhc_status s = MHC_OK;
   float* mix = a.mix_out != nullptr
                    ? a.mix_out
                    : reinterpret_cast<float*>(static_cast<char*>(ws) + fsplit::mix_off(cfg.groups, cfg.ns));
@@ -1443,26 +1409,19 @@ mhc_status launch_split(const StepArgs& a, void* ws, const SplitCfg& cfg, int mo
 // Chunked small-batch path, at most kChunkMaxTokens tokens (the partial rows
 // take 128 bytes per token and chunk): bf16 streams with an even number of
 // 32-feature steps, at most the pipelined kernel's 160, in chunks of
-// MHC_CHUNK_PAIRS pairs of steps (one pair per wave); f32 streams with any
-// number of steps, in chunks of MHC_CHUNK_STEPS_F steps (one per wave; 16
-// steps, two per wave, took 37.3 against 29.2 us on 64 tokens at d = 5120).
-#ifndef MHC_CHUNK_PAIRS
-#define MHC_CHUNK_PAIRS 8
-#endif
+// kChunkPairs pairs of steps (one pair per wave); f32 streams with any
+// number of steps, in chunks of kChunkStepsF steps (one per wave; 16 steps,
+// two per wave, took 37.3 against 29.2 us on 64 tokens at d = 5120).
+constexpr int kChunkPairs = 8;
 // Largest call that path "auto" runs on the chunked kernels (when a workspace
 // is given); larger calls take the feature-split kernel. At d = 5120 the
 // two routes' call time (cache-flushed medians; the split route with its
 // cooperative-launch gaps) is about 16.5 + 0.0355 T and 45.6 + 0.0243 T
 // microseconds: equal near 2,600 tokens.
-#ifndef MHC_CHUNK_AUTO_TOKENS
-#define MHC_CHUNK_AUTO_TOKENS 2048
-#endif
+constexpr int64_t kChunkAutoTokens = 2048;
 constexpr int64_t kChunkMaxTokens = 8192;
 
-#ifndef MHC_CHUNK_STEPS_F
-#define MHC_CHUNK_STEPS_F 8
-#endif
-constexpr int kChunkStepsF = MHC_CHUNK_STEPS_F;
+constexpr int kChunkStepsF = 8;
 
 struct ChunkCfg {
   int nchunks = 0;
@@ -1476,7 +1435,7 @@ ChunkCfg chunk_config(int32_t dtype, int32_t d, int64_t tokens) {
   if (dtype == MHC_BF16) {
     if (nsteps % 2 != 0 || nsteps > pipe::kMaxSteps) return ChunkCfg{};
     const int npairs = nsteps / 2;
-    const int cp = std::min(MHC_CHUNK_PAIRS, npairs);
+    const int cp = std::min(kChunkPairs, npairs);
     return ChunkCfg{(npairs + cp - 1) / cp, cp, dtype};
   }
   if (dtype == MHC_F32) {
@@ -1551,7 +1510,7 @@ mhc_status pick_route(int32_t path, const void* workspace, int64_t tokens, int64
       return MHC_OK;
     case MHC_PATH_AUTO:
       if (workspace == nullptr) *r = Route::kTile;
-      else if (chunk_bytes > 0 && tokens <= MHC_CHUNK_AUTO_TOKENS) *r = Route::kChunk;
+      else if (chunk_bytes > 0 && tokens <= kChunkAutoTokens) *r = Route::kChunk;
       else if (split_bytes > 0) *r = Route::kSplit;
       else *r = Route::kTile;
       return MHC_OK;
@@ -1589,7 +1548,7 @@ mhc_status launch_step(const StepArgs& a, int32_t dtype, int mode, hipStream_t s
                        const char* what) {
   const int nsteps = a.d / kStep;
   const int64_t ntiles = (a.tokens + kTok - 1) / kTok;
-  if (!MHC_FORCE_GENERIC && dtype == MHC_BF16 && nsteps <= pipe::kMaxSteps && nsteps % 2 == 0) {
+  if (dtype == MHC_BF16 && nsteps <= pipe::kMaxSteps && nsteps % 2 == 0) {
     int cus = 0;
     const mhc_status s = device_cu_count(&cus);
     if (s != MHC_OK) return s;
@@ -1655,9 +1614,6 @@ void launch_block(const StepArgs& a, int mode, hipStream_t st) {
 
 // bf16 streams with n <= 4 and an even step count run two steps per unit
 // (both halves of each 128-byte line of a token row loaded back to back)
-#ifndef MHC_GEN_UNIT2
-#define MHC_GEN_UNIT2 1
-#endif
 template <int N>
 void launch_block_n(const StepArgs& a, int32_t dtype, int mode, hipStream_t st) {
   if (dtype == MHC_F32) {
@@ -1665,7 +1621,7 @@ void launch_block_n(const StepArgs& a, int32_t dtype, int mode, hipStream_t st) 
     return;
   }
   if constexpr (N <= 4) {
-    if (MHC_GEN_UNIT2 && (a.d / kStep) % 2 == 0) {
+    if ((a.d / kStep) % 2 == 0) {
       launch_block<N, MHC_BF16, 2>(a, mode, st);
       return;
     }
@@ -1745,16 +1701,14 @@ int64_t split_n_workspace_bytes(int32_t n, const SplitCfgN& c, int64_t tokens) {
                 : fsn::workspace_bytes<4>(c.groups, c.ns, tokens);
 }
 
-// clear the workspace counters, the cooperative split kernel, then the
-// split/Sinkhorn of the mixes rows it wrote
+// the cooperative split kernel (it leaves the workspace header as it found
+// it), then the split/Sinkhorn of the mixes rows it wrote
 template <int N>
 mhc_status launch_split_n(const StepArgs& a, void* ws, const SplitCfgN& cfg, int mode,
                           hipStream_t stream) {
-  const int words = (int)(fsn::mp_off<N>(cfg.groups) / 4);
-  hipLaunchKernelGGL(fsplit::clear_kernel, dim3(1), dim3(256), 0, stream,
-                     static_cast<uint32_t*>(ws), words);
-  mhc_status s = launch_status("workspace clear kernel launch");
-  if (s != MHC_OK) return s;
+  if (fsn::ctr_off<N>(cfg.groups, 0) > fsplit::kWsHeader)
+    return fail(MHC_ERR_UNSUPPORTED, "feature-split kernel: %d groups exceed the header", cfg.groups);
+  mhc_status s = MHC_OK;
   float* mix = a.mix_out != nullptr
                    ? a.mix_out
                    : reinterpret_cast<float*>(static_cast<char*>(ws) +
@@ -1810,7 +1764,7 @@ ChunkCfgN chunk_config_n(int32_t n, int32_t dtype, int32_t d, int64_t tokens) {
   const int nsteps = d / kStep;
   if (d <= 0 || d % kStep != 0 || tokens > kChunkMaxTokens || elem_size(dtype) == 0)
     return ChunkCfgN{};
-  const int spi = (dtype == MHC_BF16 && n <= 4 && MHC_GEN_UNIT2 && nsteps % 2 == 0) ? 2 : 1;
+  const int spi = (dtype == MHC_BF16 && n <= 4 && nsteps % 2 == 0) ? 2 : 1;
   const int nunits = nsteps / spi;
   const int per = (nunits + kChunksN - 1) / kChunksN;
   return ChunkCfgN{(nunits + per - 1) / per, per, spi};
@@ -1928,9 +1882,12 @@ int64_t bwd_workspace_floats(int32_t n, int64_t tokens, int32_t d) {
   return bwd::Ws<4>{tokens, d}.floats();
 }
 
-#ifndef MHC_BWD_MFMA_DW
-#define MHC_BWD_MFMA_DW 1   // dW on bf16 MFMA for bf16 streams with d % 64 == 0
-#endif
+// The backward's regions start after the header the forward kernels keep at
+// the start of every workspace, so one workspace serves both directions.
+int64_t bwd_workspace_bytes(int32_t n, int64_t tokens, int32_t d) {
+  return fsplit::kWsHeader + bwd_workspace_floats(n, tokens, d) * 4;
+}
+
 
 template <int N, int DT>
 mhc_status run_backward(const bwd::Args& args, hipStream_t st) {
@@ -1960,7 +1917,7 @@ mhc_status run_backward(const bwd::Args& args, hipStream_t st) {
                        dim3(bwd::kThreads), 0, st, a);
   }
   if ((s = launch_status("backward stream kernel launch")) != MHC_OK) return s;
-  if (DT == MHC_BF16 && MHC_BWD_MFMA_DW && a.d % 64 == 0)
+  if (DT == MHC_BF16 && a.d % 64 == 0)
     hipLaunchKernelGGL((bwd::param_mfma_kernel<N>),
                        dim3((unsigned)((a.d / 64 + 3) / 4), N, bwd::kParamChunks), dim3(256), 0, st,
                        a);
@@ -2404,7 +2361,7 @@ int64_t mhc_fused_step_backward_workspace_bytes_n(int32_t n, int64_t tokens, int
     fail(MHC_ERR_INVALID_ARG, "bad n (%d), tokens (%lld) or d (%d)", n, (long long)tokens, d);
     return -1;
   }
-  return bwd_workspace_floats(n, tokens, d) * 4;
+  return bwd_workspace_bytes(n, tokens, d);
 }
 
 mhc_status mhc_fused_step_backward_n(
@@ -2422,7 +2379,7 @@ mhc_status mhc_fused_step_backward_n(
   if (s != MHC_OK) return s;
   if (tokens == 0) return ok();
   const uint64_t es = elem_size(dtype), T = (uint64_t)tokens, nn = (uint64_t)n, nm = n_mix(n);
-  const int64_t need = bwd_workspace_floats(n, tokens, d) * 4;
+  const int64_t need = bwd_workspace_bytes(n, tokens, d);
   if (workspace_bytes < need)
     return fail(MHC_ERR_INVALID_ARG, "workspace holds %lld bytes, %lld needed",
                 (long long)workspace_bytes, (long long)need);
@@ -2447,9 +2404,11 @@ mhc_status mhc_fused_step_backward_n(
   };
   s = check_spans(in, 16, out, 10, nullptr, nullptr);
   if (s != MHC_OK) return s;
+  // the backward's regions begin after the forward kernels' header
+  float* const bws = reinterpret_cast<float*>(static_cast<char*>(workspace) + fsplit::kWsHeader);
   bwd::Args a{x, f, pre_in, post_in, comb_in, x_out, mix, w_mix, base, scale, gamma, d_x_out,
               d_y, d_pre, d_post, d_comb, d_x, d_f, d_pre_in, d_post_in, d_comb_in, d_w_mix,
-              d_base, d_scale, d_gamma, static_cast<float*>(workspace), tokens, 0, d,
+              d_base, d_scale, d_gamma, bws, tokens, 0, d,
               sinkhorn_iters, norm_eps, hc_eps};
   const hipStream_t st = static_cast<hipStream_t>(stream);
   if (n == 2)

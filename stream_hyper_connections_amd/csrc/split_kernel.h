@@ -38,20 +38,37 @@
 //     Sinkhorn on all tokens (16 lanes per token).
 //
 // Cross-workgroup protocol (correct wherever the workgroups run; the group ->
-// XCD mapping only matters for speed):
-//   * writer: exchange stores carry sc1, so they are written through to the
-//     device-coherent level; s_waitcnt vmcnt makes them complete before the
-//     wave's LDS increment; the wave that completes the workgroup's count
-//     issues a device-scope atomic add on the counter.
-//   * reader: polls the counter with device-scope loads until it reaches
-//     ns * (generation + 1), then reads the exchange with sc1 loads.
+// XCD mapping only matters for speed). In the GFX942 memory model of the LLVM
+// AMDGPU backend (also applied to gfx950) an agent-scope relaxed atomic load
+// or store is a load or store with the sc1 bit, so every exchange access
+// below is, per dword, such an atomic: coherent across the XCDs' L2 caches.
+//   * writer: exchange stores carry sc1; s_waitcnt makes them complete (vmcnt
+//     counts loads and stores together and decrements in issue order on this
+//     architecture family, so waiting until only the loads issued after them
+//     remain outstanding suffices) before the wave's LDS increment; the wave
+//     that completes the workgroup's count issues an agent-scope atomic add
+//     on the counter. That is an agent-scope release minus the L2 write-back,
+//     which only stores without sc1 would need.
+//   * reader: polls the counter with agent-scope atomic loads until it
+//     reaches ns * (generation + 1); the value decides the loop exit, so the
+//     exchange loads (sc1, never served from a stale cache line) issue only
+//     after it: an agent-scope acquire minus the cache invalidation, which
+//     only loads without sc1 would need.
 //   * slots: a workgroup writes batch i's slot only after it has seen every
 //     workgroup of the group finish batch i-2, whose waves had all finished
 //     reading batch i-4 before that; four slots are therefore never read and
 //     written at once.
 //   * every wait is bounded: after kSpinLimit polls the wave sets the status
-//     word at workspace offset 0 and stops waiting (outputs are then invalid);
-//     later waits return at once once the status word is set.
+//     word (workspace offset 0) and the call's abort word (offset 4) and stops
+//     waiting (outputs are then invalid); later waits of the same call return
+//     at once once the abort word is set. The library never clears the status
+//     word: it reports every give-up since the caller last cleared it.
+//   * the workspace cleans up after itself: each workgroup, once all of its
+//     waves are done with the exchange, adds one to the done word (offset 8)
+//     with an acquire-release atomic; the workgroup that brings it to the
+//     grid size resets the counters, the abort word and the done word. The
+//     next call therefore finds the header as the caller first provided it
+//     (zero-filled), without a clearing launch.
 // All workgroups must be resident together: the host launches the kernel
 // cooperatively with one workgroup per CU.
 
@@ -81,36 +98,32 @@ constexpr int kStepBytes = kStreams * kTiles * 1024;   // packed bytes per 32 fe
 constexpr int kSC1 = 16;                       // cache-policy bit: device scope
 constexpr uint32_t kSpinLimit = 1u << 20;
 constexpr int kCtrStride = 128;                // bytes between counters
-constexpr int64_t kHdr = 256;                  // status word + padding
+constexpr int64_t kHdr = 256;                  // status, abort and done words + padding
+constexpr int64_t kAbortOff = 4;               // byte offset of the call's abort word
+constexpr int64_t kDoneOff = 8;                // byte offset of the done count
+// Bytes reserved at the start of every workspace of the step's kernels: the
+// counters of the largest group count (16 groups x kRing slots) fit, and the
+// chunked kernels' partial rows start here, so they never overwrite them.
+constexpr int64_t kWsHeader = 16384;
 
 constexpr int kRowRor2 = 0x122;                // DPP row rotate right by 2
 
-// raise a batch's count right after its exchange stores (1), or after the
-// next wait, whose loads were issued behind those stores (0)
-#ifndef FS_COUNT_EARLY
-#define FS_COUNT_EARLY 1
-#endif
-
-// cache policies: stream loads, new-stream stores, y stores
-#ifndef FS_LOAD_AUX
-#define FS_LOAD_AUX 2
-#endif
-#ifndef FS_XO_AUX
-#define FS_XO_AUX 0
-#endif
-#ifndef FS_Y_AUX
-#define FS_Y_AUX 2
-#endif
+// cache policies: stream loads and y stores non-temporal, new-stream stores
+// default (measured fastest of the combinations)
+constexpr int kLoadAux = kNT;
+constexpr int kXoAux = 0;
+constexpr int kYAux = kNT;
 
 // workspace layout for `groups` groups of `ns` slices: status word, one
-// counter per (group, slot), then per (group, slot) the mixes rows
-// [slice][token][kRow] and the h^2 partials [slice][token]
+// counter per (group, slot), then from the end of the 16 KB header per
+// (group, slot) the mixes rows [slice][token][kRow] and the h^2 partials
+// [slice][token]
 __host__ __device__ constexpr int64_t ctr_off(int g, int slot) {
   return kHdr + ((int64_t)g * kRing + slot) * kCtrStride;
 }
-__host__ __device__ constexpr int64_t mp_off(int groups) {
-  return kHdr + (((int64_t)groups * kRing * kCtrStride + 255) / 256) * 256;
-}
+// (the exchange rows begin after the whole header, whatever the group count,
+// so no call's data lands where another call's counters live)
+__host__ __device__ constexpr int64_t mp_off(int) { return kWsHeader; }
 __host__ __device__ constexpr int64_t mp_slot_bytes(int ns) { return (int64_t)ns * kBatch * kRow * 4; }
 __host__ __device__ constexpr int64_t hs_off(int groups, int ns) {
   return mp_off(groups) + (int64_t)groups * kRing * mp_slot_bytes(ns);
@@ -257,24 +270,50 @@ __device__ __forceinline__ void streams_only(const Items& in, u32x4 (&xo)[4], fl
 }
 
 // Bounded wait until the counter reaches `target`; false after a time-out or
-// when another wave has already timed out.
+// when another wave of the call has already timed out.
 __device__ __forceinline__ bool wait_count(char* ws, int64_t off, uint32_t target) {
   uint32_t* status = reinterpret_cast<uint32_t*>(ws);
+  uint32_t* abort_w = reinterpret_cast<uint32_t*>(ws + kAbortOff);
   const uint32_t* ctr = reinterpret_cast<const uint32_t*>(ws + off);
   for (uint32_t n = 0;; ++n) {
     const uint32_t v = __builtin_amdgcn_readfirstlane(
         __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
     if (v >= target) return true;
     if ((n & 31) == 31) {
-      const uint32_t st = __builtin_amdgcn_readfirstlane(
-          __hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-      if (st != 0) return false;
+      const uint32_t ab = __builtin_amdgcn_readfirstlane(
+          __hip_atomic_load(abort_w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      if (ab != 0) return false;
     }
     if (n >= kSpinLimit) {
       __hip_atomic_store(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(abort_w, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       return false;
     }
     __builtin_amdgcn_s_sleep(2);
+  }
+}
+
+// End of a cooperative split kernel: called by every thread of every
+// workgroup after its last exchange access. The workgroup that completes the
+// done count resets the `nctr` counters at `ctr0` (kCtrStride apart), the
+// abort word and the done word, leaving the header zero for the next call.
+__device__ __forceinline__ void release_workspace(char* ws, int64_t ctr0, int nctr) {
+  __syncthreads();
+  if (threadIdx.x >= 64) return;
+  uint32_t old = 0;
+  if (threadIdx.x == 0)
+    old = __hip_atomic_fetch_add(reinterpret_cast<uint32_t*>(ws + kDoneOff), 1u,
+                                 __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+  old = __builtin_amdgcn_readfirstlane(old);
+  if (old != gridDim.x - 1) return;
+  for (int i = threadIdx.x; i < nctr; i += 64)
+    __hip_atomic_store(reinterpret_cast<uint32_t*>(ws + ctr0 + (int64_t)i * kCtrStride), 0u,
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0) {
+    __hip_atomic_store(reinterpret_cast<uint32_t*>(ws + kAbortOff), 0u, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(reinterpret_cast<uint32_t*>(ws + kDoneOff), 0u, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -352,14 +391,14 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
   auto load_half = [&](Items& it, const Rs& r, int rr, int h) {
     const uint32_t col = 128u * rr;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) it.x[k] = bload<FS_LOAD_AUX>(r.x, vxh[h], col + k * d2);
-    if constexpr (kFull) it.f = bload<FS_LOAD_AUX>(r.f, vfh[h], col);
+    for (int k = 0; k < 4; ++k) it.x[k] = bload<kLoadAux>(r.x, vxh[h], col + k * d2);
+    if constexpr (kFull) it.f = bload<kLoadAux>(r.f, vfh[h], col);
     else it.f = u32x4{0, 0, 0, 0};
   };
   auto load_tail = [&](Items& it, const Rs& r) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) it.x[k] = bload<FS_LOAD_AUX>(r.x, vxt, k * d2);
-    if constexpr (kFull) it.f = bload<FS_LOAD_AUX>(r.f, vft, 0);
+    for (int k = 0; k < 4; ++k) it.x[k] = bload<kLoadAux>(r.x, vxt, k * d2);
+    if constexpr (kFull) it.f = bload<kLoadAux>(r.f, vft, 0);
     else it.f = u32x4{0, 0, 0, 0};
   };
   auto load_coef = [&](Cf& cf, const Rs& r) {
@@ -415,10 +454,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
 
-  // finish(i, ...) also counts batch i+1 (count_next): its exchange stores were
-  // issued before the loads of sum h^2 below, so once those loads have
-  // returned (vector memory retires in order) the stores are complete too.
-  auto finish = [&](int i, const Rs& r, const u32x4 (&hk)[NI], bool count_next) {
+  auto finish = [&](int i, const Rs& r, const u32x4 (&hk)[NI]) {
     const int slot = i % kRing;
     const uint32_t target = (uint32_t)ns * (uint32_t)(i / kRing + 1);
     wait_count(ws, ctr_off(g, slot), target);
@@ -456,14 +492,6 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    {
-      if (count_next) {
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(kMaxSlices / 8));
-        __builtin_amdgcn_sched_barrier(0);
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        count_batch(i + 1);
-      }
-    }
     if constexpr (kFull) {
       float rh[8];
 #pragma unroll
@@ -482,11 +510,11 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
         const int rr = j >> 1, h = j & 1;
         const float rhv = wsm.rh[8 * h + m8];
         const u32x4 y = norm_bf(hk[j], sm.gamma, fr0 + 64 * rr + 8 * x8, rhv);
-        bstore<FS_Y_AUX>(r.y, vfh[h], 128u * rr, y);
+        bstore<kYAux>(r.y, vfh[h], 128u * rr, y);
       }
       if (TAIL) {
         const u32x4 y = norm_bf(hk[NI - 1], sm.gamma, ftl + 8 * g16, wsm.rh[t16]);
-        bstore<FS_Y_AUX>(r.y, vft, 0, y);
+        bstore<kYAux>(r.y, vft, 0, y);
       }
     }
     // split + Sinkhorn of token tb of the batch
@@ -508,8 +536,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
       const int64_t t = (g + (int64_t)i * G) * kBatch + tb;
       // the mixes row; split and Sinkhorn run in tail_kernel
       if (t < a.tokens && lane < kMix / 4) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) fs.mix[t * kMix + 4 * lane + e] = v[e] * rr;
+        st4f(&fs.mix[t * kMix + 4 * lane], f32x4{v[0] * rr, v[1] * rr, v[2] * rr, v[3] * rr});
       }
     }
   };
@@ -545,7 +572,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
       else streams_only(bufA, xo0, ssA[0]);
 #pragma unroll
       for (int k = 0; k < 4; ++k)
-        if constexpr (kFull) bstore<FS_XO_AUX>(rcur.xo, vxh[0], 128u * rr + k * d2, xo0[k]);
+        if constexpr (kFull) bstore<kXoAux>(rcur.xo, vxh[0], 128u * rr + k * d2, xo0[k]);
       __builtin_amdgcn_sched_barrier(0);
       if (rr + 1 < NR) load_half(bufA, rcur, rr + 1, 0);
       else if (TAIL) load_tail(bufT, rcur);
@@ -555,7 +582,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
       else streams_only(bufB, xo1, ssA[1]);
 #pragma unroll
       for (int k = 0; k < 4; ++k)
-        if constexpr (kFull) bstore<FS_XO_AUX>(rcur.xo, vxh[1], 128u * rr + k * d2, xo1[k]);
+        if constexpr (kFull) bstore<kXoAux>(rcur.xo, vxh[1], 128u * rr + k * d2, xo1[k]);
       __builtin_amdgcn_sched_barrier(0);
       if (rr + 1 < NR) load_half(bufB, rcur, rr + 1, 1);
       __builtin_amdgcn_sched_barrier(0);
@@ -586,7 +613,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
       else streams_only(bufT, xot, ssT);
 #pragma unroll
       for (int k = 0; k < 4; ++k)
-        if constexpr (kFull) bstore<FS_XO_AUX>(rcur.xo, vxt, k * d2, xot[k]);
+        if constexpr (kFull) bstore<kXoAux>(rcur.xo, vxt, k * d2, xot[k]);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const bf16x8 A = __builtin_bit_cast(bf16x8, xot[k]);
@@ -681,7 +708,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
       load_half(bufA, rnext, 0, 0);
       load_half(bufB, rnext, 0, 1);
       __builtin_amdgcn_sched_barrier(0);
-      if (i == 0 || FS_COUNT_EARLY) {
+      {
         // wait for the exchange stores directly (13 loads were issued after
         // them) and count the batch now
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(kFull ? 13 : 8));
@@ -689,14 +716,15 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         count_batch(i);
       }
-      if (i > 0) finish(i - 1, rprev, hprev, !FS_COUNT_EARLY);
+      if (i > 0) finish(i - 1, rprev, hprev);
       rprev = rcur;
       rcur = rnext;
 #pragma unroll
       for (int j = 0; j < NI; ++j) hprev[j] = hcur[j];
     }
   }
-  if (nbg > 0) finish(nbg - 1, rprev, hprev, false);
+  if (nbg > 0) finish(nbg - 1, rprev, hprev);
+  release_workspace(ws, ctr_off(0, 0), G * kRing);
 }
 
 // Split and Sinkhorn of the mixes rows [T][24] the feature-split kernel wrote:
@@ -727,10 +755,6 @@ __global__ __launch_bounds__(256) void tail_kernel(const float* __restrict__ mix
     cv = cv * __builtin_amdgcn_rcpf(col_sum(cv) + eps);
   }
   if (ok) comb_out[t * 16 + e] = cv;
-}
-
-__global__ __launch_bounds__(256) void clear_kernel(uint32_t* p, int words) {
-  for (int i = threadIdx.x; i < words; i += 256) p[i] = 0u;
 }
 
 }  // namespace fsplit

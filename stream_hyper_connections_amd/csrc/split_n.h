@@ -21,8 +21,9 @@
 //     partial rows of one token of the batch (token c + ns * wave) and write
 //     its mixes row.
 //     gen::sinkhorn_kernel then runs the split and Sinkhorn on every token.
-// The cross-workgroup protocol, the bounded waits and the status word are
-// those of fsplit (see split_kernel.h). All workgroups must be resident
+// The cross-workgroup protocol, the bounded waits, the status and abort
+// words and the end-of-call reset of the header are those of fsplit (see
+// split_kernel.h). All workgroups must be resident
 // together: the host launches the kernel cooperatively, one workgroup per CU.
 
 namespace fsn {
@@ -62,17 +63,16 @@ template <int N>
 __host__ __device__ constexpr int max_rounds() { return N == 2 ? 4 : 2; }
 
 // workspace layout for `groups` groups of `ns` slices (as fsplit, with rows
-// of kRow floats): status word, one counter per (group, slot), the partial
-// rows [group][slot][slice][token][kRow], the h^2 partials
-// [group][slot][slice][token], then the mixes rows [T][(2+n)n]
+// of kRow floats): status word, one counter per (group, slot), then from the
+// end of the 16 KB header the partial rows [group][slot][slice][token][kRow],
+// the h^2 partials [group][slot][slice][token], then the mixes rows
+// [T][(2+n)n]
 template <int N>
 __host__ __device__ constexpr int64_t ctr_off(int g, int slot) {
   return kHdr + ((int64_t)g * kRing + slot) * kCtrStride;
 }
 template <int N>
-__host__ __device__ constexpr int64_t mp_off(int groups) {
-  return kHdr + (((int64_t)groups * kRing * kCtrStride + 255) / 256) * 256;
-}
+__host__ __device__ constexpr int64_t mp_off(int) { return fsplit::kWsHeader; }
 template <int N>
 __host__ __device__ constexpr int64_t mp_slot_bytes(int ns) {
   return (int64_t)ns * kBatch * Dims<N>::kRow * 4;
@@ -285,8 +285,8 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
   auto load_half = [&](Items<N>& it, const Rs& r, int rr, int h) {
     const uint32_t col = 128u * rr;
 #pragma unroll
-    for (int k = 0; k < N; ++k) it.x[k] = bload<FS_LOAD_AUX>(r.x, vxh[h], col + k * d2);
-    if constexpr (kFull) it.f = bload<FS_LOAD_AUX>(r.f, vfh[h], col);
+    for (int k = 0; k < N; ++k) it.x[k] = bload<fsplit::kLoadAux>(r.x, vxh[h], col + k * d2);
+    if constexpr (kFull) it.f = bload<fsplit::kLoadAux>(r.f, vfh[h], col);
     else it.f = u32x4{0, 0, 0, 0};
   };
   // coefficients of the wave's 16 tokens as 16-byte chunks: lane l loads
@@ -408,7 +408,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
         const int rr = j >> 1, h = j & 1;
         const float rhv = wsm.rh[8 * h + m8];
         const u32x4 y = norm_bf(hk[j], sm.gamma, 64 * rr + 8 * x8, rhv);
-        bstore<FS_Y_AUX>(r.y, vfh[h], 128u * rr, y);
+        bstore<fsplit::kYAux>(r.y, vfh[h], 128u * rr, y);
       }
     }
     if (sk) {
@@ -431,8 +431,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
       const float rr = rsqrtf(ssum / (float)(N * d) + a.norm_eps);
       const int64_t t = (g + (int64_t)i * G) * kBatch + tb;
       if (t < a.tokens && lane < kCH && 4 * lane < kMix) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) fs.mix[t * kMix + 4 * lane + e] = v[e] * rr;
+        st4f(&fs.mix[t * kMix + 4 * lane], f32x4{v[0] * rr, v[1] * rr, v[2] * rr, v[3] * rr});
       }
     }
   };
@@ -465,7 +464,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
       else streams_only<N>(bufA, xo0, ssA[0]);
 #pragma unroll
       for (int k = 0; k < N; ++k)
-        if constexpr (kFull) bstore<FS_XO_AUX>(rcur.xo, vxh[0], 128u * rr + k * d2, xo0[k]);
+        if constexpr (kFull) bstore<fsplit::kXoAux>(rcur.xo, vxh[0], 128u * rr + k * d2, xo0[k]);
       __builtin_amdgcn_sched_barrier(0);
       if (rr + 1 < NR) load_half(bufA, rcur, rr + 1, 0);
       __builtin_amdgcn_sched_barrier(0);
@@ -474,7 +473,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
       else streams_only<N>(bufB, xo1, ssA[1]);
 #pragma unroll
       for (int k = 0; k < N; ++k)
-        if constexpr (kFull) bstore<FS_XO_AUX>(rcur.xo, vxh[1], 128u * rr + k * d2, xo1[k]);
+        if constexpr (kFull) bstore<fsplit::kXoAux>(rcur.xo, vxh[1], 128u * rr + k * d2, xo1[k]);
       __builtin_amdgcn_sched_barrier(0);
       if (rr + 1 < NR) load_half(bufB, rcur, rr + 1, 1);
       __builtin_amdgcn_sched_barrier(0);
@@ -586,6 +585,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
     }
   }
   if (nbg > 0) finish(nbg - 1, rprev, hprev);
+  fsplit::release_workspace(ws, ctr_off<N>(0, 0), G * kRing);
 }
 
 }  // namespace fsn

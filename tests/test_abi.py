@@ -44,7 +44,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_granule_and_status_strings():
-    assert binding.abi_version() == 8
+    assert binding.abi_version() == 9
     assert binding.d_granule() == 32
     lib = binding.load()
     assert lib.mhc_status_string(0) == b"MHC_OK"
@@ -143,7 +143,7 @@ def test_route_query_without_a_device_query():
 
 def _chunk_n_bytes(n, tokens, chunks=80):
     row = ((2 + n) * n + 2 + 3) // 4 * 4
-    return 256 + chunks * tokens * row * 4
+    return 16384 + chunks * tokens * row * 4
 
 
 def test_route_query_n_family_without_a_device_query():
@@ -170,7 +170,7 @@ def test_route_query_n_family_without_a_device_query():
     assert route(3, 0, 256, 5120, bf, 1) == -1
     assert route(8, 5, 256, 5120, bf, 1) == -1
     assert "unknown path" in binding.last_error()
-    # chunk workspace: 256-byte header, then 80 chunks of R floats per token
+    # chunk workspace: 16,384-byte header, then 80 chunks of R floats per token
     assert lib.mhc_fused_step_n_workspace_bytes(8, 256, 5120, bf) == _chunk_n_bytes(8, 256)
     assert lib.mhc_fused_step_n_workspace_bytes(2, 100, 5120, f32) == _chunk_n_bytes(2, 100)
     assert lib.mhc_fused_step_n_workspace_bytes(4, 64, 5120, f32) == _chunk_n_bytes(4, 64)

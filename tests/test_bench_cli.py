@@ -23,6 +23,5 @@ def test_help_lists_the_modes():
     res = _run("--help")
     assert res.returncode == 0
     for flag in ("--gpus", "--steps", "--warmup", "--workload", "--path", "--form",
-                 "--sinkhorn-sweep", "--n-sweep", "--backward", "--all-configs", "--crossover",
-                 "--copy-ceiling"):
+                 "--sinkhorn-sweep", "--n-sweep", "--backward", "--all-configs", "--crossover"):
         assert flag in res.stdout, flag

@@ -27,7 +27,7 @@ def _log(msg):
 
 
 def _ws_dt(t, d, dtype):
-    return torch.empty(mhc.fused_step_workspace_bytes(t, d, dtype), dtype=torch.uint8,
+    return torch.zeros(mhc.fused_step_workspace_bytes(t, d, dtype), dtype=torch.uint8,
                        device="cuda")
 
 
@@ -205,13 +205,13 @@ def test_chunk_workspace_validation():
     wp = mhc.pack_wmix(torch.zeros((24, 4 * d), device="cuda"), "bf16")
     z = torch.zeros((t, 4), device="cuda")
     need = mhc.fused_step_workspace_bytes(t, d, "bf16")
-    assert need == 256 + 2 * t * 128
+    assert need == 16384 + 2 * t * 128
     args = (x, f, z, z, torch.zeros((t, 4, 4), device="cuda"), wp, torch.zeros(24, device="cuda"),
             torch.ones(3, device="cuda"), torch.ones(d, device="cuda"))
-    small = torch.empty(need - 4, dtype=torch.uint8, device="cuda")
+    small = torch.zeros(need - 4, dtype=torch.uint8, device="cuda")
     with pytest.raises(mhc.MhcError, match="workspace holds"):
         mhc.fused_step(*args, path="chunk", workspace=small)
-    big = torch.empty(need + 512, dtype=torch.uint8, device="cuda")
+    big = torch.zeros(need + 512, dtype=torch.uint8, device="cuda")
     with pytest.raises(mhc.MhcError, match="256-byte aligned"):
         mhc.fused_step(*args, path="chunk", workspace=big[16:])
 

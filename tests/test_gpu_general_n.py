@@ -97,7 +97,7 @@ def test_general_n_split_parity(n, d, t):
     _log(f"general split n={n} d={d} T={t}")
     case = make_case(wl.Workload(800 + 10 * n + d % 7 + t % 5, "general_n_split", t, d, "bf16",
                                  n=n))
-    ws = torch.empty(mhc.fused_step_n_workspace_bytes(n, t, d, "bf16"), dtype=torch.uint8,
+    ws = torch.zeros(mhc.fused_step_n_workspace_bytes(n, t, d, "bf16"), dtype=torch.uint8,
                      device="cuda")
     out, _ = run_step_n(case, "bf16", path="split", workspace=ws)
     assert mhc.split_status(ws) == 0
@@ -135,7 +135,7 @@ def test_general_n_chunk_parity(n, dtype, d, t):
     case = make_case(wl.Workload(900 + 10 * n + d % 7 + t % 5, "general_n_chunk", t, d, dtype,
                                  n=n))
     assert mhc.fused_step_route_n(n, "chunk", t, d, dtype) == "chunk"
-    ws = torch.empty(mhc.fused_step_n_workspace_bytes(n, t, d, dtype), dtype=torch.uint8,
+    ws = torch.zeros(mhc.fused_step_n_workspace_bytes(n, t, d, dtype), dtype=torch.uint8,
                      device="cuda")
     out, _ = run_step_n(case, dtype, path="chunk", workspace=ws)
     o = check_step(case, out, dtype)
@@ -161,7 +161,7 @@ def test_general_n_chunk_workspace_reused_for_a_smaller_call():
     """One workspace, two calls in a row, the second with fewer tokens (the
     partial rows are laid out by the call's own token count)."""
     n, d = 8, 1024
-    ws = torch.empty(mhc.fused_step_n_workspace_bytes(n, 500, d, "bf16"), dtype=torch.uint8,
+    ws = torch.zeros(mhc.fused_step_n_workspace_bytes(n, 500, d, "bf16"), dtype=torch.uint8,
                      device="cuda")
     for t in (500, 77):
         case = make_case(wl.Workload(960 + t, "general_n_chunk_reuse", t, d, "bf16", n=n))
@@ -215,6 +215,53 @@ def test_mixes_n_split_parity(n, d, t):
                       to_dev(p["scale"]), path="split")
     torch.cuda.synchronize()
     check_mixes(dict(x=x, **p), {k: v.cpu() for k, v in out.items()}, "bf16")
+
+
+def test_one_workspace_serves_every_route_in_turn():
+    """One zero-filled workspace shared, in turn, by the backward, the chunked
+    route and feature-split calls with 16, 6 and 12 groups (fused and
+    mixes-only): each route leaves the header (status, abort and done words,
+    the group counters) zero for the next, and keeps its own data out of it,
+    so every forward result matches the oracle."""
+    calls = [  # n, d, tokens, path, mixes only
+        (2, 1024, 150, "split", False),    # 16 slices of 64: 16 groups
+        (4, 5120, 300, "split", False),    # 40 slices of 128: 6 groups
+        (2, 5120, 700, "split", True),     # 20 slices of 256: 12 groups
+        (4, 5120, 200, "chunk", False),
+        (2, 1024, 150, "split", True),
+    ]
+    need = max(mhc.fused_step_n_workspace_bytes(n, t, d, "bf16") for n, d, t, _, _ in calls)
+    need = max(need, mhc.fused_step_backward_workspace_bytes_n(4, 64, 1024))
+    ws = mhc.new_workspace(need)
+    # a backward call first: its regions lie after the header
+    bc = make_case(wl.Workload(841, "ws_backward", 64, 1024, "bf16", n=4))
+    bo, bdev = run_step_n(bc, "bf16", path="block")
+    g = torch.Generator(device="cuda").manual_seed(5)
+    mhc.fused_step_backward_n(
+        bdev["x"], bdev["f"], bdev["pre"], bdev["post"], bdev["comb"], bo["x_out"].cuda(),
+        bo["mix"].cuda(), bdev["w_mix"], bdev["base"], bdev["scale"], bdev["gamma"],
+        torch.randn(bdev["x"].shape, device="cuda", generator=g).bfloat16(),
+        torch.randn(bdev["f"].shape, device="cuda", generator=g).bfloat16(),
+        torch.randn((64, 4), device="cuda", generator=g),
+        torch.randn((64, 4), device="cuda", generator=g),
+        torch.randn((64, 4, 4), device="cuda", generator=g), workspace=ws)
+    torch.cuda.synchronize()
+    for i, (n, d, t, path, mixes_only) in enumerate(calls):
+        case = make_case(wl.Workload(842 + i, "ws_shared", t, d, "bf16", n=n))
+        if mixes_only:
+            dev = _dev(case)
+            out = mhc.mixes_n(dev["x"], mhc.pack_wmix_n(dev["w_mix"], "bf16"), dev["base"],
+                              dev["scale"], path=path, workspace=ws)
+            torch.cuda.synchronize()
+            check_mixes(case, {k: v.cpu() for k, v in out.items()}, "bf16")
+        else:
+            out, _ = run_step_n(case, "bf16", path=path, workspace=ws)
+            check_step(case, out, "bf16")
+        assert mhc.split_status(ws) == 0
+        words = ws[:16384].view(torch.int32)
+        assert int(words[1:3].abs().sum().item()) == 0
+        assert int(words[64:].abs().sum().item()) == 0   # counters (bytes 256 on) are zero
+        _log(f"shared workspace: n={n} d={d} T={t} {path}{' mixes' if mixes_only else ''} ok")
 
 
 @pytest.mark.timeout(900)
@@ -434,7 +481,7 @@ def test_general_n_replays_from_a_hip_graph(n, path):
              for i in range(2)]
     dev = _dev(cases[0])
     wp = mhc.pack_wmix_n(dev["w_mix"], "bf16")
-    ws = torch.empty(max(mhc.fused_step_n_workspace_bytes(n, t, d, "bf16"), 256),
+    ws = torch.zeros(max(mhc.fused_step_n_workspace_bytes(n, t, d, "bf16"), 256),
                      dtype=torch.uint8, device="cuda")
     nm = (2 + n) * n
     outs = dict(x_out=torch.empty_like(dev["x"]), y_out=torch.empty_like(dev["f"]),

@@ -28,7 +28,7 @@ def _log(msg):
 
 
 def _run(case, **kw):
-    ws = torch.empty(mhc.fused_step_workspace_bytes(len(case["x"]), case["x"].shape[2], "bf16"),
+    ws = torch.zeros(mhc.fused_step_workspace_bytes(len(case["x"]), case["x"].shape[2], "bf16"),
                      dtype=torch.uint8, device="cuda")
     assert ws.numel() > 0
     out, dev = run_step(case, path="split", workspace=ws, **kw)
@@ -91,7 +91,7 @@ def test_split_in_place_and_deterministic():
             assert torch.equal(ref[k], again[k]), k
     x_dev = dev["x"].clone()
     wp = mhc.pack_wmix(dev["w_mix"], "bf16")
-    ws = torch.empty(mhc.fused_step_workspace_bytes(555, 5120, "bf16"), dtype=torch.uint8,
+    ws = torch.zeros(mhc.fused_step_workspace_bytes(555, 5120, "bf16"), dtype=torch.uint8,
                      device="cuda")
     out = mhc.fused_step(x_dev, dev["f"], dev["pre"], dev["post"], dev["comb"], wp, dev["base"],
                          dev["scale"], dev["gamma"], x_out=x_dev, want_mix=True, path="split",
@@ -120,7 +120,7 @@ def test_split_guard_bands_untouched():
     bu, vu = guarded(t * 4, torch.float32)
     bc, vc = guarded(t * 16, torch.float32)
     bm, vm = guarded(t * 24, torch.float32)
-    ws = torch.empty(mhc.fused_step_workspace_bytes(t, d, "bf16"), dtype=torch.uint8,
+    ws = torch.zeros(mhc.fused_step_workspace_bytes(t, d, "bf16"), dtype=torch.uint8,
                      device="cuda")
     out = mhc.fused_step(dev["x"], dev["f"], dev["pre"], dev["post"], dev["comb"], wp, dev["base"],
                          dev["scale"], dev["gamma"], x_out=vx.view(t, 4, d), y_out=vy.view(t, d),
@@ -135,15 +135,52 @@ def test_split_guard_bands_untouched():
 
 
 def test_split_repeated_calls_share_a_workspace():
-    """Two calls in a row on one workspace, the second smaller: counters and the
-    status word are reset by every call."""
-    ws = torch.empty(mhc.fused_step_workspace_bytes(3000, 5120, "bf16"), dtype=torch.uint8,
+    """Two calls in a row on one zero-filled workspace, the second smaller: each
+    call leaves the header's counters as it found them, with no clearing
+    launch in between."""
+    ws = torch.zeros(mhc.fused_step_workspace_bytes(3000, 5120, "bf16"), dtype=torch.uint8,
                      device="cuda")
     for t, seed in ((3000, 453), (200, 454)):
         case = make_case(wl.Workload(seed, "split_repeat", t, 5120, "bf16"))
         out, _ = run_step(case, path="split", workspace=ws)
         assert mhc.split_status(ws) == 0
         check_step(case, out, "bf16")
+
+
+def test_split_leaves_the_header_zero():
+    """After a feature-split call the abort word, the done count and every
+    (group, slot) counter are back to zero (the header layout of the kernel:
+    words at bytes 4 and 8, counters from byte 256, 128 bytes apart, four per
+    group; 40 slices of 128 features at d = 5120 make 6 groups on 256 CUs)."""
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("group count assumed for a 256-CU device")
+    ws = mhc.new_workspace(mhc.fused_step_workspace_bytes(1000, 5120, "bf16"))
+    case = make_case(wl.Workload(455, "split_header", 1000, 5120, "bf16"))
+    out, _ = run_step(case, path="split", workspace=ws)
+    words = ws[:16384].view(torch.int32).cpu().numpy()
+    assert words[0] == 0 and words[1] == 0 and words[2] == 0
+    counters = words[(256 + 128 * np.arange(6 * 4)) // 4]
+    assert (counters == 0).all(), counters
+    check_step(case, out, "bf16")
+
+
+def test_split_status_word_is_sticky():
+    """The library never clears the status word: a value written there stays
+    across calls (whose outputs are unaffected, since the waits read the
+    call's own abort word), check_status reports it, and clear_split_status
+    resets it. The word is set from the host; no wait is made to give up."""
+    t = 300
+    ws = mhc.new_workspace(mhc.fused_step_workspace_bytes(t, 5120, "bf16"))
+    case = make_case(wl.Workload(456, "split_sticky", t, 5120, "bf16"))
+    ws[:4].view(torch.int32).fill_(1)
+    out, _ = run_step(case, path="split", workspace=ws)
+    assert mhc.split_status(ws) == 1
+    check_step(case, out, "bf16")
+    with pytest.raises(mhc.MhcError, match="gave up"):
+        run_step(case, path="split", workspace=ws, check_status=True)
+    assert mhc.split_status(ws) == 0
+    out, _ = run_step(case, path="split", workspace=ws, check_status=True)
+    check_step(case, out, "bf16")
 
 
 def test_split_workspace_validation():
@@ -155,17 +192,17 @@ def test_split_workspace_validation():
     need = mhc.fused_step_workspace_bytes(t, d, "bf16")
     args = (x, f, z, z, torch.zeros((t, 4, 4), device="cuda"), wp, torch.zeros(24, device="cuda"),
             torch.ones(3, device="cuda"), torch.ones(d, device="cuda"))
-    small = torch.empty(need - 256, dtype=torch.uint8, device="cuda")
+    small = torch.zeros(need - 256, dtype=torch.uint8, device="cuda")
     with pytest.raises(mhc.MhcError, match="workspace holds"):
         mhc.fused_step(*args, path="split", workspace=small)
-    big = torch.empty(need + 512, dtype=torch.uint8, device="cuda")
+    big = torch.zeros(need + 512, dtype=torch.uint8, device="cuda")
     with pytest.raises(mhc.MhcError, match="256-byte aligned"):
         mhc.fused_step(*args, path="split", workspace=big[16:])
     # f32 streams: only the chunked kernels (chunks of 8 steps) take a workspace
-    assert mhc.fused_step_workspace_bytes(t, 5120, "f32") == 256 + 20 * t * 128
+    assert mhc.fused_step_workspace_bytes(t, 5120, "f32") == 16384 + 20 * t * 128
     assert mhc.fused_step_workspace_bytes(t, 7168, "bf16") == 0
     # d = 1024 has no slice geometry: only the chunked kernels take a workspace
-    assert mhc.fused_step_workspace_bytes(t, 1024, "bf16") == 256 + 2 * t * 128
+    assert mhc.fused_step_workspace_bytes(t, 1024, "bf16") == 16384 + 2 * t * 128
     with pytest.raises(ValueError, match="does not apply"):
         mhc.fused_step_route("split", t, 1024, "bf16")
     assert mhc.fused_step_route("auto", t, 1024, "bf16") == "chunk"
@@ -181,7 +218,7 @@ def test_split_calls_on_two_streams_in_flight_together():
     devs = [{k: to_dev(c[k]) for k in ("x", "f", "pre", "post", "comb", "w_mix", "base",
                                        "scale", "gamma")} for c in cases]
     wps = [mhc.pack_wmix(dv["w_mix"], "bf16") for dv in devs]
-    wss = [torch.empty(mhc.fused_step_workspace_bytes(t, d, "bf16"), dtype=torch.uint8,
+    wss = [torch.zeros(mhc.fused_step_workspace_bytes(t, d, "bf16"), dtype=torch.uint8,
                        device="cuda") for _ in range(2)]
 
     def call(i):

@@ -76,7 +76,7 @@ def test_mixes_split_mode_parity(d, t):
     x = wl.streams(w)
     p = wl.params(w)
     wp = mhc.pack_wmix(to_dev(p["w_mix"]), "bf16")
-    ws = torch.empty(mhc.fused_step_workspace_bytes(t, d, "bf16"), dtype=torch.uint8,
+    ws = torch.zeros(mhc.fused_step_workspace_bytes(t, d, "bf16"), dtype=torch.uint8,
                      device="cuda")
     dx = to_dev(x)
     out = mhc.mixes(dx, wp, to_dev(p["base"]), to_dev(p["scale"]), want_mix=True, path="split",

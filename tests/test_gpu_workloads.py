@@ -4,12 +4,13 @@
   every output of every token against the oracle;
 * prefill (4,096 tokens): every token;
 * large prefill (65,536 tokens, the throughput shape, launched exactly as the
-  benchmark launches it): sampled tokens (first and last tiles plus a seeded
-  random sample), each checked in full;
+  benchmark launches it): every token, in 1,024-token chunks;
 * chain (8,192 tokens x 80 sublayer steps, fresh parameters per step, each
-  step's outputs feeding the next): per step, sampled tokens against the
-  oracle carried alongside, comb column sums of every token, and drift
-  statistics of a free-running oracle chain (reported).
+  step's outputs feeding the next): at steps 1, 40 and 80 every token against
+  the oracle applied to exactly the inputs the GPU consumed; at every step
+  sampled tokens against the oracle carried alongside, comb column sums of
+  every token, the workspace status word, and drift statistics of a
+  free-running oracle chain (reported).
 """
 
 import time
@@ -51,8 +52,16 @@ def test_workload_full(name):
     _log(f"  comb sums: {comb_sum_stats(out['comb'])}")
 
 
+def _check_chunked(case, out, dtype, chunk=1024):
+    t = len(case["x"])
+    for t0 in range(0, t, chunk):
+        sl = slice(t0, min(t, t0 + chunk))
+        check_step(_sub(case, sl), {k: (v[sl] if v is not None else None) for k, v in out.items()},
+                   dtype)
+
+
 @pytest.mark.timeout(900)
-def test_workload_large_prefill_sampled():
+def test_workload_large_prefill_full():
     w = wl.WORKLOADS["large_prefill"]
     t = w.tokens
     t_start = time.time()
@@ -64,29 +73,31 @@ def test_workload_large_prefill_sampled():
     _log(f"large_prefill: oracle prior done at {time.time() - t_start:.1f}s")
     case = dict(x=x, f=f, pre=pre, post=post, comb=comb, iters=w.iters, norm_eps=w.norm_eps,
                 hc_eps=w.hc_eps, **cur)
-    out, _ = run_step(case)
+    ws = mhc.new_workspace(mhc.fused_step_workspace_bytes(t, w.d, "bf16"))
+    out, _ = run_step(case, workspace=ws)
+    assert mhc.split_status(ws) == 0, "a cross-workgroup wait gave up"
     _log(f"large_prefill: GPU step done at {time.time() - t_start:.1f}s")
-    rng = np.random.default_rng(12345)
-    idx = np.unique(np.concatenate([np.arange(16), np.arange(t - 16, t),
-                                    rng.choice(t, 480, replace=False)]))
-    check_step(_sub(case, idx), {k: (v[idx] if v is not None else None) for k, v in out.items()},
-               "bf16")
+    _check_chunked(case, out, "bf16")
     stats = comb_sum_stats(out["comb"])
     assert stats["col_dev_max"] <= 1e-5
-    _log(f"large_prefill: {len(idx)} sampled tokens match; comb sums {stats}")
+    _log(f"large_prefill: all {t} tokens match the oracle at {time.time() - t_start:.1f}s; "
+         f"comb sums {stats}")
     # the same inputs cut to a ragged last batch (511 whole 128-token batches
     # and 37 tokens), in the same launch configuration
     t2 = 511 * 128 + 37
     sub = dict(case, x=case["x"][:t2], f=case["f"][:t2], pre=pre[:t2], post=post[:t2],
                comb=comb[:t2])
-    out2, _ = run_step(sub)
+    out2, _ = run_step(sub, workspace=ws)
+    assert mhc.split_status(ws) == 0, "a cross-workgroup wait gave up"
+    rng = np.random.default_rng(12345)
     idx2 = np.unique(np.concatenate([np.arange(8), np.arange(t2 - 64, t2),
                                      rng.choice(t2, 120, replace=False)]))
     check_step(_sub(sub, idx2), {k: (v[idx2] if v is not None else None)
                                  for k, v in out2.items()}, "bf16")
     for k in ("x_out", "y", "pre", "post", "comb", "mix"):   # tokens before the cut unchanged
         assert torch.equal(out2[k][:t2 - 37], out[k][:t2 - 37]), k
-    _log(f"large_prefill cut to {t2} tokens: {len(idx2)} sampled tokens match")
+    _log(f"large_prefill cut to {t2} tokens: {len(idx2)} sampled tokens match, the whole "
+         "batches equal the full run bit for bit")
 
 
 @pytest.mark.timeout(900)
@@ -106,13 +117,24 @@ def test_workload_chain():
     free = {k: v.copy() for k, v in tf.items()}
     gap = np.zeros(len(idx))
     max_ties = 0
+    ws = mhc.new_workspace(mhc.fused_step_workspace_bytes(t, w.d, "bf16"))
+    full_steps = (0, 39, w.steps - 1)     # steps 1, 40 and 80: every token
     for s in range(w.steps):
         p = wl.params(w, s)
         f_cpu = wl.sublayer_out(w, s)
         wp = mhc.pack_wmix(to_dev(p["w_mix"]), "bf16")
+        if s in full_steps:   # exactly the inputs the GPU consumes at this step
+            consumed = dict(x=dev_x.cpu(), f=f_cpu, pre=dev_c["pre"].cpu().numpy(),
+                            post=dev_c["post"].cpu().numpy(), comb=dev_c["comb"].cpu().numpy(),
+                            iters=w.iters, norm_eps=w.norm_eps, hc_eps=w.hc_eps, **p)
         out = mhc.fused_step(dev_x, to_dev(f_cpu), dev_c["pre"], dev_c["post"], dev_c["comb"], wp,
                              to_dev(p["base"]), to_dev(p["scale"]), to_dev(p["gamma"]),
-                             w.iters, w.norm_eps, w.hc_eps, want_mix=True)
+                             w.iters, w.norm_eps, w.hc_eps, want_mix=True, workspace=ws)
+        assert mhc.split_status(ws) == 0, f"step {s}: a cross-workgroup wait gave up"
+        if s in full_steps:
+            _check_chunked(consumed, {k: (v.cpu() if v is not None else None)
+                                      for k, v in out.items()}, "bf16")
+            _log(f"chain step {s + 1}: all {t} tokens match the oracle on the inputs consumed")
         didx = torch.as_tensor(idx, device="cuda")
         g = {k: v.index_select(0, didx).cpu() for k, v in out.items() if v is not None}
         col = out["comb"].sum(dim=1)
