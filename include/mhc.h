@@ -199,6 +199,35 @@ mhc_status mhc_fused_step(const void* x, const void* f, int32_t dtype, int64_t t
                           mhc_stream_t stream);
 
 /*
+ * mhc_fused_step_noalloc -- mhc_fused_step for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops and
+ * harnesses that forbid allocation. Same arguments and rules as
+ * mhc_fused_step without the workspace pair; the library's own scratch
+ * serves as the workspace, and the call allocates nothing.
+ *   - Scratch: a static 32 MiB device array, one per GPU the library runs
+ *     on, held until the process ends. A call whose route needs more
+ *     (mhc_fused_step_workspace_bytes: on the feature-split route about
+ *     16.2 MB plus 96 bytes per token at d = 5120, i.e. up to about 180,000
+ *     tokens) returns MHC_ERR_INVALID_ARG before launching; MHC_PATH_TILE
+ *     needs none.
+ *   - Every call on a GPU shares that GPU's scratch: calls that overlap on
+ *     one GPU (different streams, or host threads without ordering) race on
+ *     it and must not be issued.
+ *   - The scratch's header starts zeroed and every call leaves it so (the
+ *     first call on a device also enqueues one small kernel that zeroes it).
+ *     Its status word is not reported: a feature-split wait that gave up
+ *     leaves that call's outputs invalid without an error code; callers that
+ *     must check it use mhc_fused_step with their own workspace.
+ */
+mhc_status mhc_fused_step_noalloc(const void* x, const void* f, int32_t dtype, int64_t tokens,
+                                  int32_t d, const float* pre_in, const float* post_in,
+                                  const float* comb_in, const void* w_packed, const float* base,
+                                  const float* scale, const float* gamma, int32_t sinkhorn_iters,
+                                  float norm_eps, float hc_eps, void* x_out, void* y_out,
+                                  float* pre_out, float* post_out, float* comb_out,
+                                  float* mix_out, int32_t path, mhc_stream_t stream);
+
+/*
  * mhc_mixes -- hc_mixes alone ([SW] Code, hc_mixes and "All 5 steps"): one RMS
  * statistic over the flattened 4*d streams, the 24-wide projection, then the
  * split and Sinkhorn of mhc_sinkhorn4. Reads x [T][4][d]; writes pre_out,

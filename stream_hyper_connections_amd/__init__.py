@@ -17,6 +17,7 @@ from .binding import (  # noqa: F401
     fused_step_backward_n,
     fused_step_backward_workspace_bytes_n,
     fused_step_n,
+    fused_step_noalloc,
     fused_step_n_workspace_bytes,
     fused_step_route,
     fused_step_route_n,

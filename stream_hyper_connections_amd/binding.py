@@ -37,6 +37,10 @@ _SIGS = {
                         _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _f32, _f32,
                         _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                         _i32, _c_void_p, _i64, _c_void_p], _i32),
+    "mhc_fused_step_noalloc": ([_c_void_p, _c_void_p, _i32, _i64, _i32, _c_void_p, _c_void_p,
+                                _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _f32,
+                                _f32, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                _c_void_p, _i32, _c_void_p], _i32),
     "mhc_mixes": ([_c_void_p, _i32, _i64, _i32, _c_void_p, _c_void_p, _c_void_p, _i32, _f32, _f32,
                    _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _c_void_p, _i64, _c_void_p],
                   _i32),
@@ -265,6 +269,35 @@ def fused_step(x, f, pre_in, post_in, comb_in, w_packed, base, scale, gamma, ite
     _check("mhc_fused_step", st)
     if check_status:
         _raise_on_status("mhc_fused_step", ws)
+    return {"x_out": x_out, "y": y_out, "pre": pre_out, "post": post_out, "comb": comb_out,
+            "mix": mix_out}
+
+
+def fused_step_noalloc(x, f, pre_in, post_in, comb_in, w_packed, base, scale, gamma, iters=20,
+                       norm_eps=1e-6, hc_eps=1e-6, x_out=None, y_out=None, pre_out=None,
+                       post_out=None, comb_out=None, mix_out=None, want_mix=False,
+                       path="auto") -> dict:
+    """mhc_fused_step_noalloc on tensors: fused_step with the library's static
+    scratch as the workspace (no device allocation by the library; outputs
+    not given are allocated here by torch)."""
+    t, n, d = x.shape
+    if n != N_STREAMS:
+        raise ValueError("x must be [T, 4, d]")
+    if path not in PATHS:
+        raise ValueError(f"unknown path {path!r}")
+    x_out = torch.empty_like(x) if x_out is None else x_out
+    y_out = torch.empty_like(f) if y_out is None else y_out
+    pre_out = _f32_out((t, N_STREAMS), x, pre_out)
+    post_out = _f32_out((t, N_STREAMS), x, post_out)
+    comb_out = _f32_out((t, N_STREAMS, N_STREAMS), x, comb_out)
+    if want_mix and mix_out is None:
+        mix_out = _f32_out((t, N_MIX), x, None)
+    st = load().mhc_fused_step_noalloc(
+        _ptr(x), _ptr(f), _dtype_code(x), t, d, _ptr(pre_in), _ptr(post_in), _ptr(comb_in),
+        _ptr(w_packed), _ptr(base), _ptr(scale), _ptr(gamma), iters, norm_eps, hc_eps,
+        _ptr(x_out), _ptr(y_out), _ptr(pre_out), _ptr(post_out), _ptr(comb_out), _ptr(mix_out),
+        PATHS[path], _stream())
+    _check("mhc_fused_step_noalloc", st)
     return {"x_out": x_out, "y": y_out, "pre": pre_out, "post": post_out, "comb": comb_out,
             "mix": mix_out}
 

@@ -1939,6 +1939,47 @@ mhc_status run_backward(const bwd::Args& args, hipStream_t st) {
   return launch_status("backward scale reduction launch");
 }
 
+
+// ----- scratch of the allocation-free entry point -------------------------------------
+//
+// mhc_fused_step_noalloc's workspace is `scratch`, a file-scope device array:
+// every GPU the library runs on holds one copy (at its own address) until the
+// process ends. On the host the array's name is only a stand-in symbol, never
+// a device address: the address is looked up once per device, with that
+// device current, and kept; kernels get that address.
+
+constexpr int64_t kScratchBytes = int64_t(32) << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+__global__ void zero_header_kernel(uint32_t* p, int words) {
+  for (int i = threadIdx.x; i < words; i += blockDim.x) p[i] = 0u;
+}
+
+// Device address of the current device's scratch. The first call on a device
+// also zeroes the workspace header on `stream` with a plain kernel (static
+// device memory starts zeroed when the code object is loaded; this makes the
+// header rule explicit for one launch per device); every call leaves it zero.
+mhc_status device_scratch(hipStream_t stream, void** out) {
+  static std::atomic<void*> ptrs[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MHC_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(MHC_ERR_UNSUPPORTED, "device ordinal %d", dev);
+  void* p = ptrs[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(MHC_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    hipLaunchKernelGGL(zero_header_kernel, dim3(1), dim3(256), 0, stream,
+                       static_cast<uint32_t*>(p), (int)(fsplit::kWsHeader / 4));
+    const mhc_status s = launch_status("scratch header clear launch");
+    if (s != MHC_OK) return s;
+    ptrs[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return MHC_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -2059,6 +2100,36 @@ mhc_status mhc_fused_step(const void* x, const void* f, int32_t dtype, int64_t t
   if (route == Route::kSplit) return launch_split(a, workspace, rn.split, kFused, st);
   if (route == Route::kChunk) return launch_chunk(a, workspace, rn.chunk, kFused, st);
   return launch_step(a, dtype, kFused, st, "fused step kernel launch");
+}
+
+mhc_status mhc_fused_step_noalloc(const void* x, const void* f, int32_t dtype, int64_t tokens,
+                                  int32_t d, const float* pre_in, const float* post_in,
+                                  const float* comb_in, const void* w_packed, const float* base,
+                                  const float* scale, const float* gamma, int32_t sinkhorn_iters,
+                                  float norm_eps, float hc_eps, void* x_out, void* y_out,
+                                  float* pre_out, float* post_out, float* comb_out,
+                                  float* mix_out, int32_t path, mhc_stream_t stream) {
+  mhc_status s = check_common(dtype, tokens, d, sinkhorn_iters, norm_eps, hc_eps);
+  if (s != MHC_OK) return s;
+  if (tokens == 0) return ok();
+  if (path != MHC_PATH_TILE) {
+    RouteNeeds rn;
+    Route r;
+    static const char kDummy = 0;   // stands for a workspace; never dereferenced
+    if ((s = choose_route(path, &kDummy, dtype, d, tokens, &rn, &r)) != MHC_OK) return s;
+    const int64_t need =
+        r == Route::kSplit ? rn.split_bytes : (r == Route::kChunk ? rn.chunk_bytes : 0);
+    if (need > kScratchBytes)
+      return fail(MHC_ERR_INVALID_ARG,
+                  "%lld tokens at d = %d need %lld bytes of scratch; the static scratch holds "
+                  "%lld (use mhc_fused_step with a workspace)",
+                  (long long)tokens, d, (long long)need, (long long)kScratchBytes);
+  }
+  void* ws = nullptr;
+  if ((s = device_scratch(static_cast<hipStream_t>(stream), &ws)) != MHC_OK) return s;
+  return mhc_fused_step(x, f, dtype, tokens, d, pre_in, post_in, comb_in, w_packed, base, scale,
+                        gamma, sinkhorn_iters, norm_eps, hc_eps, x_out, y_out, pre_out, post_out,
+                        comb_out, mix_out, path, ws, kScratchBytes, stream);
 }
 
 mhc_status mhc_mixes(const void* x, int32_t dtype, int64_t tokens, int32_t d,

@@ -32,7 +32,8 @@ def test_header_declares_the_entry_points():
                "mhc_pack_wmix_n", "mhc_fused_step_n", "mhc_mixes_n", "mhc_sinkhorn_n",
                "mhc_fused_step_n_workspace_bytes", "mhc_fused_step_route",
                "mhc_fused_step_route_n",
-               "mhc_fused_step_backward_n", "mhc_fused_step_backward_workspace_bytes_n"):
+               "mhc_fused_step_backward_n", "mhc_fused_step_backward_workspace_bytes_n",
+               "mhc_fused_step_noalloc"):
         assert fn in names
 
 
