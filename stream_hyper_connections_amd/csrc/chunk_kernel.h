@@ -40,6 +40,31 @@ inline int64_t chunk_workspace_bytes(int nchunks, int64_t tokens) {
   return kChunkHeader + (int64_t)nchunks * tokens * kPart * 4;
 }
 
+// XCD-aware work list of the chunked kernels. The hardware hands workgroup b
+// to XCD b % 8, and each XCD has its own L2. The (chunk, tile) work items are
+// listed chunk-major (every tile of chunk 0, then chunk 1, ...) and cut into
+// 8 contiguous ranges, one per XCD, so each XCD's L2 fetches the packed
+// weights of about nchunks / 8 chunks instead of all of them; workgroups past
+// the end of the list (grid padded to 8 ranges) do nothing.
+constexpr int kXcds = 8;
+inline int64_t chunk_grid(int64_t ntiles, int nchunks) {
+  return kXcds * ((ntiles * nchunks + kXcds - 1) / kXcds);
+}
+struct ChunkItem {
+  int tile, chunk;
+  bool live;
+};
+__device__ __forceinline__ ChunkItem chunk_item(int64_t ntiles, int nchunks) {
+  const int64_t total = ntiles * nchunks;
+  const int64_t per = (total + kXcds - 1) / kXcds;
+  const int64_t w = (int64_t)(blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
+  ChunkItem it;
+  it.live = w < total;
+  it.chunk = it.live ? (int)(w / ntiles) : 0;
+  it.tile = it.live ? (int)(w - (int64_t)it.chunk * ntiles) : 0;
+  return it;
+}
+
 // One pair of steps (A = sa, B = sa + 1) of a chunk: the order of pair_body,
 // with h stored to y_out instead of LDS, and the next pair's streams (pair
 // sn) loaded only when there is one (`more`, uniform across the wave: with
@@ -96,8 +121,10 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(StepArgs a, int nchunks
   const int d = a.d;
   const int nsteps = d / kStep;
   const int npairs = nsteps / 2;
-  const int tile = blockIdx.x / nchunks;
-  const int chunk = blockIdx.x - tile * nchunks;
+  const ChunkItem item = chunk_item((a.tokens + kTok - 1) / kTok, nchunks);
+  if (!item.live) return;
+  const int tile = item.tile;
+  const int chunk = item.chunk;
   const int pair0 = chunk * cpairs;
   const int np = min(cpairs, npairs - pair0);
   const int cnt = wave < np ? (np - wave + kWaves - 1) / kWaves : 0;
@@ -211,8 +238,10 @@ __global__ __launch_bounds__(kThreads) void chunk_f32_kernel(StepArgs a, int nch
   const int g = lane >> 4;
   const int d = a.d;
   const int nsteps = d / kStep;
-  const int tile = blockIdx.x / nchunks;
-  const int chunk = blockIdx.x - tile * nchunks;
+  const ChunkItem item = chunk_item((a.tokens + kTok - 1) / kTok, nchunks);
+  if (!item.live) return;
+  const int tile = item.tile;
+  const int chunk = item.chunk;
   const int s0 = chunk * csteps;
   const int ns = min(csteps, nsteps - s0);
   const int cnt = wave < ns ? (ns - wave + kWaves - 1) / kWaves : 0;

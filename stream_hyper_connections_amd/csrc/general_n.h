@@ -358,8 +358,12 @@ __global__ __launch_bounds__(kThreads) void block_kernel(StepArgs a, ChunkN cn) 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tr = lane & 15;
   const int g = lane >> 4;
-  const int blk = CH ? (int)(blockIdx.x / cn.nchunks) : (int)blockIdx.x;
-  const int chunk = CH ? (int)(blockIdx.x - (unsigned)blk * cn.nchunks) : 0;
+  // chunks: the XCD-aware work list of the chunked kernels (pipe::chunk_item)
+  pipe::ChunkItem item{(int)blockIdx.x, 0, true};
+  if constexpr (CH) item = pipe::chunk_item((a.tokens + kBlock - 1) / kBlock, cn.nchunks);
+  if (!item.live) return;
+  const int blk = item.tile;
+  const int chunk = item.chunk;
   const int64_t tb = (int64_t)blk * kBlock;
   const int64_t tw = tb + wave * kTok;
   const int64_t t = tw + tr;

@@ -1447,7 +1447,7 @@ ChunkCfg chunk_config(int32_t dtype, int32_t d, int64_t tokens) {
 
 mhc_status launch_chunk(const StepArgs& a, void* ws, const ChunkCfg& cc, int mode,
                         hipStream_t stream) {
-  const unsigned grid = (unsigned)(((a.tokens + kTok - 1) / kTok) * cc.nchunks);
+  const unsigned grid = (unsigned)pipe::chunk_grid((a.tokens + kTok - 1) / kTok, cc.nchunks);
   const dim3 blk(pipe::kThreads), tok((unsigned)a.tokens);
   char* w = static_cast<char*>(ws);
   const bool bf = cc.dtype == MHC_BF16, full = mode == kFused;
@@ -1778,7 +1778,7 @@ int64_t chunk_n_workspace_bytes(int32_t n, const ChunkCfgN& c, int64_t tokens) {
 template <int N, int DT, int SPI>
 void launch_chunk_block(const StepArgs& a, const gen::ChunkN& cn, int mode, hipStream_t st) {
   const unsigned grid =
-      (unsigned)(((a.tokens + gen::kBlock - 1) / gen::kBlock) * (int64_t)cn.nchunks);
+      (unsigned)pipe::chunk_grid((a.tokens + gen::kBlock - 1) / gen::kBlock, cn.nchunks);
   if (mode == kFused)
     hipLaunchKernelGGL((gen::block_kernel<N, DT, kFused, SPI, true>), dim3(grid),
                        dim3(gen::kThreads), 0, st, a, cn);
