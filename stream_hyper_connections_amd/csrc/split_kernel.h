@@ -564,6 +564,12 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
     // are fenced so every wait stays at its consumer (vmcnt retires in order).
 #pragma unroll
     for (int rr = 0; rr < NR; ++rr) {
+      // Wave priority: the two waves of a SIMD alternate between streaming
+      // phases (hc_post, stores, the refill loads) and the MFMA phase below.
+      // Giving the streaming phase the higher priority lets the other wave's
+      // loads and stores issue ahead of this wave's MFMAs: 1.514 -> 1.480 ms
+      // at 65,536 tokens.
+      __builtin_amdgcn_s_setprio(3);
       u32x4 xo0[4], xo1[4];
       float C[4][4], U[4], P[4];
       __builtin_amdgcn_sched_barrier(0);
@@ -586,6 +592,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
       __builtin_amdgcn_sched_barrier(0);
       if (rr + 1 < NR) load_half(bufB, rcur, rr + 1, 1);
       __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(0);
       // new streams of the two halves -> A operands, 2 K-steps x 4 streams
 #pragma unroll
       for (int k = 0; k < 4; ++k) {

@@ -456,6 +456,9 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
 
 #pragma unroll
     for (int rr = 0; rr < NR; ++rr) {
+      // streaming phase at high wave priority, the MFMA phase at the base one
+      // (as in fsplit::split_kernel)
+      __builtin_amdgcn_s_setprio(3);
       u32x4 xo0[N], xo1[N];
       float C[N][N], U[N], P[N];
       __builtin_amdgcn_sched_barrier(0);
@@ -477,6 +480,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
       __builtin_amdgcn_sched_barrier(0);
       if (rr + 1 < NR) load_half(bufB, rcur, rr + 1, 1);
       __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(0);
       // new streams of the two halves -> A operands, 2 K-steps per stream
 #pragma unroll
       for (int k = 0; k < N; ++k) {
