@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define MHC_ABI_VERSION 9
+#define MHC_ABI_VERSION 10
 #define MHC_N_STREAMS 4
 #define MHC_N_MIX 24
 
@@ -63,21 +63,41 @@ typedef enum mhc_dtype { MHC_F32 = 0, MHC_BF16 = 1 } mhc_dtype;
 /*
  * Kernel family of mhc_fused_step and mhc_mixes:
  *   MHC_PATH_AUTO   no workspace: the tile kernel. With a workspace: the
- *                   chunked kernels up to MHC_CHUNK_AUTO_TOKENS (2048) tokens
- *                   where they apply, else the feature-split kernel where it
- *                   applies, else the tile kernel.
+ *                   chunked kernels up to 2048 tokens (1024 with
+ *                   MHC_PATH_PLAIN_LAUNCH) where they apply, else the
+ *                   feature-split kernel where it applies, else the tile
+ *                   kernel.
  *   MHC_PATH_TILE   the tile kernel (one workgroup per 16 tokens, no
  *                   workspace; the workspace argument is ignored).
  *   MHC_PATH_SPLIT  the feature-split kernel (needs a workspace;
  *                   MHC_ERR_UNSUPPORTED where it does not apply).
  *   MHC_PATH_CHUNK  the chunked kernels (needs a workspace;
  *                   MHC_ERR_UNSUPPORTED where they do not apply).
+ * MHC_PATH_PLAIN_LAUNCH is a flag that may be OR-ed into any of them. It
+ * changes how the feature-split kernel is launched and nothing else: as an
+ * ordinary kernel instead of a cooperative one. A cooperative launch runs
+ * the kernel alone on the device, and the device idles for about 11 us
+ * before and after it. The plain launch avoids that idle and saves about
+ * 10 us per call. That kernel's workgroups (one per compute unit, at most
+ * the device's count) wait for one another, so all of them must run at
+ * once. With the flag the caller guarantees this: while the call runs, no
+ * other work may hold compute units indefinitely. That excludes a CU mask on
+ * the stream that leaves fewer compute units than the grid, and a kernel
+ * elsewhere on the device that waits for this call. Kernels that merely run
+ * alongside only delay it. If the guarantee fails, a wait gives up after
+ * 2^20 polls: the workspace status word is set and the outputs are invalid,
+ * as after any given-up wait. With MHC_PATH_AUTO the flag also lowers the
+ * switch from the chunked kernels to the feature-split kernel from 2048 to
+ * 1024 tokens, since the split route's fixed cost is then smaller.
+ * mhc_fused_step_route reports that choice. The n-family's switch stays at
+ * 2048 tokens.
  */
 typedef enum mhc_path {
   MHC_PATH_AUTO = 0,
   MHC_PATH_TILE = 1,
   MHC_PATH_SPLIT = 2,
-  MHC_PATH_CHUNK = 3
+  MHC_PATH_CHUNK = 3,
+  MHC_PATH_PLAIN_LAUNCH = 16
 } mhc_path;
 
 typedef void* mhc_stream_t;
@@ -165,7 +185,8 @@ int32_t mhc_fused_step_route(int32_t path, int64_t tokens, int32_t d, int32_t dt
  *          RMSNorm gain), sinkhorn_iters >= 1, norm_eps >= 0, hc_eps >= 0.
  * Outputs: x_out [T][4][d] (may be x), y_out [T][d], pre_out/post_out
  *          [T][4], comb_out [T][4][4], mix_out [T][24] (optional, NULL to skip).
- * path:    mhc_path, the kernel family (MHC_PATH_AUTO picks by size).
+ * path:    mhc_path, the kernel family (MHC_PATH_AUTO picks by size),
+ *          optionally with MHC_PATH_PLAIN_LAUNCH OR-ed in.
  * Workspace (optional): NULL, or device memory of workspace_bytes bytes,
  *          256-byte aligned, overlapping no other argument, used by:
  *          - the feature-split kernel: each compute unit keeps one slice of
@@ -350,7 +371,7 @@ int32_t mhc_fused_step_route_n(int32_t n, int32_t path, int64_t tokens, int32_t 
  *                   applies, else the chunks where they apply (up to 8192
  *                   tokens), else the block kernel.
  * SPLIT and CHUNK need a workspace and are MHC_ERR_UNSUPPORTED where they do
- * not apply.
+ * not apply. MHC_PATH_PLAIN_LAUNCH may be OR-ed in, as for mhc_fused_step.
  * Workspace: NULL / 0 bytes, or device memory of at least the chosen route's
  * bytes (mhc_fused_step_n_workspace_bytes() covers both), 256-byte aligned,
  * overlapping no other argument; a smaller one is MHC_ERR_INVALID_ARG. Its

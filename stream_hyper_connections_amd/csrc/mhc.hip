@@ -1359,9 +1359,19 @@ mhc_status split_config(int32_t dtype, int32_t d, SplitCfg* cfg) {
   return MHC_OK;
 }
 
-// The feature-split kernel (cooperative; it leaves the workspace header as it
-// found it, see split_kernel.h), then the split/Sinkhorn of its mixes rows.
-mhc_status launch_split(const StepArgs& a, void* ws, const SplitCfg& cfg, int mode,
+// Launch of a feature-split kernel, whose workgroups wait for one another:
+// cooperative (the runtime runs it alone on the device, so all workgroups are
+// resident), or, with MHC_PATH_PLAIN_LAUNCH, as an ordinary kernel, where the
+// caller guarantees that nothing holds compute units for the whole call.
+hipError_t launch_resident(const void* fn, unsigned grid, void** params, bool plain,
+                           hipStream_t stream) {
+  if (plain) return hipLaunchKernel(fn, dim3(grid), dim3(fsplit::kThreads), params, 0, stream);
+  return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(fsplit::kThreads), params, 0, stream);
+}
+
+// The feature-split kernel (it leaves the workspace header as it found it, see
+// split_kernel.h), then the split/Sinkhorn of its mixes rows.
+mhc_status launch_split(const StepArgs& a, void* ws, const SplitCfg& cfg, int mode, bool plain,
                         hipStream_t stream) {
   if (fsplit::ctr_off(cfg.groups, 0) > fsplit::kWsHeader)
     return fail(MHC_ERR_UNSUPPORTED, "feature-split kernel: %d groups exceed the header", cfg.groups);
@@ -1394,10 +1404,9 @@ mhc_status launch_split(const StepArgs& a, void* ws, const SplitCfg& cfg, int mo
       break;
     default: return fail(MHC_ERR_UNSUPPORTED, "feature-split kernel: slice of %d features", cfg.S);
   }
-  const hipError_t e = hipLaunchCooperativeKernel(fn, dim3((unsigned)(cfg.groups * cfg.ns)),
-                                                  dim3(fsplit::kThreads), params, 0, stream);
+  const hipError_t e = launch_resident(fn, (unsigned)(cfg.groups * cfg.ns), params, plain, stream);
   if (e != hipSuccess)
-    return fail(MHC_ERR_HIP, "feature-split kernel cooperative launch: %s", hipGetErrorString(e));
+    return fail(MHC_ERR_HIP, "feature-split kernel launch: %s", hipGetErrorString(e));
   s = launch_status("feature-split kernel launch");
   if (s != MHC_OK) return s;
   hipLaunchKernelGGL(fsplit::tail_kernel, dim3((unsigned)((a.tokens + 15) / 16)), dim3(256), 0,
@@ -1417,8 +1426,12 @@ constexpr int kChunkPairs = 8;
 // is given); larger calls take the feature-split kernel. At d = 5120 the
 // two routes' call time (cache-flushed medians; the split route with its
 // cooperative-launch gaps) is about 16.5 + 0.0355 T and 45.6 + 0.0243 T
-// microseconds: equal near 2,600 tokens.
+// microseconds: equal near 2,600 tokens. Launched as an ordinary kernel
+// (MHC_PATH_PLAIN_LAUNCH) the split route loses about 20 us per call; back to
+// back it then ties the chunks at 512 to 1,024 tokens (34.8 against 34.5 us,
+// 50.7 against 48.1) and wins from 1,536 (51.7 against 63.2).
 constexpr int64_t kChunkAutoTokens = 2048;
+constexpr int64_t kChunkAutoTokensPlain = 1024;
 constexpr int64_t kChunkMaxTokens = 8192;
 
 constexpr int kChunkStepsF = 8;
@@ -1503,14 +1516,14 @@ mhc_status route_needs(int32_t dtype, int32_t d, int64_t tokens, RouteNeeds* rn)
 // The route of a call with `path` and a workspace (or none), or an error for
 // a path that cannot run these arguments.
 mhc_status pick_route(int32_t path, const void* workspace, int64_t tokens, int64_t split_bytes,
-                      int64_t chunk_bytes, Route* r) {
+                      int64_t chunk_bytes, Route* r, int64_t chunk_auto = kChunkAutoTokens) {
   switch (path) {
     case MHC_PATH_TILE:
       *r = Route::kTile;
       return MHC_OK;
     case MHC_PATH_AUTO:
       if (workspace == nullptr) *r = Route::kTile;
-      else if (chunk_bytes > 0 && tokens <= kChunkAutoTokens) *r = Route::kChunk;
+      else if (chunk_bytes > 0 && tokens <= chunk_auto) *r = Route::kChunk;
       else if (split_bytes > 0) *r = Route::kSplit;
       else *r = Route::kTile;
       return MHC_OK;
@@ -1529,9 +1542,19 @@ mhc_status pick_route(int32_t path, const void* workspace, int64_t tokens, int64
   }
 }
 
+// The kernel family of `path` (the MHC_PATH_PLAIN_LAUNCH flag taken out) and
+// whether the flag was given.
+int32_t path_family(int32_t path, bool* plain) {
+  *plain = (path & MHC_PATH_PLAIN_LAUNCH) != 0;
+  return path & ~MHC_PATH_PLAIN_LAUNCH;
+}
+
 // pick_route, querying the device only when a workspace route is possible.
+// `path` may carry MHC_PATH_PLAIN_LAUNCH, which lowers auto's switch to the
+// feature-split kernel (*plain reports it).
 mhc_status choose_route(int32_t path, const void* workspace, int32_t dtype, int32_t d,
-                        int64_t tokens, RouteNeeds* rn, Route* r) {
+                        int64_t tokens, RouteNeeds* rn, Route* r, bool* plain) {
+  path = path_family(path, plain);
   *rn = RouteNeeds{};
   if (path == MHC_PATH_TILE || (path == MHC_PATH_AUTO && workspace == nullptr)) {
     *r = Route::kTile;
@@ -1541,7 +1564,9 @@ mhc_status choose_route(int32_t path, const void* workspace, int32_t dtype, int3
     const mhc_status s = route_needs(dtype, d, tokens, rn);
     if (s != MHC_OK) return s;
   }
-  return pick_route(path, workspace, tokens, rn->split_bytes, rn->chunk_bytes, r);
+  const bool lower = *plain && rn->split_bytes > 0;   // only where the split kernel runs
+  return pick_route(path, workspace, tokens, rn->split_bytes, rn->chunk_bytes, r,
+                    lower ? kChunkAutoTokensPlain : kChunkAutoTokens);
 }
 
 mhc_status launch_step(const StepArgs& a, int32_t dtype, int mode, hipStream_t stream,
@@ -1701,10 +1726,10 @@ int64_t split_n_workspace_bytes(int32_t n, const SplitCfgN& c, int64_t tokens) {
                 : fsn::workspace_bytes<4>(c.groups, c.ns, tokens);
 }
 
-// the cooperative split kernel (it leaves the workspace header as it found
-// it), then the split/Sinkhorn of the mixes rows it wrote
+// the split kernel (it leaves the workspace header as it found it), then the
+// split/Sinkhorn of the mixes rows it wrote
 template <int N>
-mhc_status launch_split_n(const StepArgs& a, void* ws, const SplitCfgN& cfg, int mode,
+mhc_status launch_split_n(const StepArgs& a, void* ws, const SplitCfgN& cfg, int mode, bool plain,
                           hipStream_t stream) {
   if (fsn::ctr_off<N>(cfg.groups, 0) > fsplit::kWsHeader)
     return fail(MHC_ERR_UNSUPPORTED, "feature-split kernel: %d groups exceed the header", cfg.groups);
@@ -1737,10 +1762,9 @@ mhc_status launch_split_n(const StepArgs& a, void* ws, const SplitCfgN& cfg, int
   }
   if (fn == nullptr)
     return fail(MHC_ERR_UNSUPPORTED, "feature-split kernel: n = %d, %d rounds", N, cfg.nr);
-  const hipError_t e = hipLaunchCooperativeKernel(fn, dim3((unsigned)(cfg.groups * cfg.ns)),
-                                                  dim3(fsplit::kThreads), params, 0, stream);
+  const hipError_t e = launch_resident(fn, (unsigned)(cfg.groups * cfg.ns), params, plain, stream);
   if (e != hipSuccess)
-    return fail(MHC_ERR_HIP, "feature-split kernel cooperative launch: %s", hipGetErrorString(e));
+    return fail(MHC_ERR_HIP, "feature-split kernel launch: %s", hipGetErrorString(e));
   if ((s = launch_status("feature-split kernel launch")) != MHC_OK) return s;
   launch_sinkhorn_n<N>(mix, a.tokens, a.base, a.scale, a.iters, a.hc_eps, a.pre_out, a.post_out,
                        a.comb_out, stream);
@@ -1859,10 +1883,10 @@ mhc_status choose_route_n(int32_t path, const void* workspace, int32_t n, int32_
 }
 
 mhc_status launch_route_n(int32_t n, Route route, const RouteNeedsN& rn, const StepArgs& a,
-                          void* workspace, int32_t dtype, int mode, hipStream_t st) {
+                          void* workspace, int32_t dtype, int mode, bool plain, hipStream_t st) {
   if (route == Route::kSplit)
-    return n == 2 ? launch_split_n<2>(a, workspace, rn.split, mode, st)
-                  : launch_split_n<4>(a, workspace, rn.split, mode, st);
+    return n == 2 ? launch_split_n<2>(a, workspace, rn.split, mode, plain, st)
+                  : launch_split_n<4>(a, workspace, rn.split, mode, plain, st);
   if (route == Route::kChunk) {
     switch (n) {
       case 2: return launch_chunk_n<2>(a, workspace, rn.chunk, dtype, mode, st);
@@ -2020,8 +2044,10 @@ int32_t mhc_fused_step_route(int32_t path, int64_t tokens, int32_t d, int32_t dt
   }
   RouteNeeds rn;
   Route r;
+  bool plain = false;
   static const char kDummy = 0;   // stands for a workspace; never dereferenced
-  if (choose_route(path, with_workspace ? &kDummy : nullptr, dtype, d, tokens, &rn, &r) != MHC_OK)
+  if (choose_route(path, with_workspace ? &kDummy : nullptr, dtype, d, tokens, &rn, &r,
+                   &plain) != MHC_OK)
     return -1;
   return r == Route::kTile ? MHC_PATH_TILE : (r == Route::kSplit ? MHC_PATH_SPLIT : MHC_PATH_CHUNK);
 }
@@ -2084,7 +2110,9 @@ mhc_status mhc_fused_step(const void* x, const void* f, int32_t dtype, int64_t t
   }
   RouteNeeds rn;
   Route route;
-  if ((s = choose_route(path, workspace, dtype, d, tokens, &rn, &route)) != MHC_OK) return s;
+  bool plain = false;
+  if ((s = choose_route(path, workspace, dtype, d, tokens, &rn, &route, &plain)) != MHC_OK)
+    return s;
   if (route != Route::kTile) {
     const int64_t need = route == Route::kSplit ? rn.split_bytes : rn.chunk_bytes;
     Span all[15];
@@ -2097,7 +2125,7 @@ mhc_status mhc_fused_step(const void* x, const void* f, int32_t dtype, int64_t t
   StepArgs a{x, f, pre_in, post_in, comb_in, w_packed, base, scale, gamma, x_out, y_out,
              pre_out, post_out, comb_out, mix_out, tokens, d, sinkhorn_iters, norm_eps, hc_eps};
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  if (route == Route::kSplit) return launch_split(a, workspace, rn.split, kFused, st);
+  if (route == Route::kSplit) return launch_split(a, workspace, rn.split, kFused, plain, st);
   if (route == Route::kChunk) return launch_chunk(a, workspace, rn.chunk, kFused, st);
   return launch_step(a, dtype, kFused, st, "fused step kernel launch");
 }
@@ -2112,11 +2140,12 @@ mhc_status mhc_fused_step_noalloc(const void* x, const void* f, int32_t dtype, i
   mhc_status s = check_common(dtype, tokens, d, sinkhorn_iters, norm_eps, hc_eps);
   if (s != MHC_OK) return s;
   if (tokens == 0) return ok();
-  if (path != MHC_PATH_TILE) {
+  bool plain = false;
+  if (path_family(path, &plain) != MHC_PATH_TILE) {
     RouteNeeds rn;
     Route r;
     static const char kDummy = 0;   // stands for a workspace; never dereferenced
-    if ((s = choose_route(path, &kDummy, dtype, d, tokens, &rn, &r)) != MHC_OK) return s;
+    if ((s = choose_route(path, &kDummy, dtype, d, tokens, &rn, &r, &plain)) != MHC_OK) return s;
     const int64_t need =
         r == Route::kSplit ? rn.split_bytes : (r == Route::kChunk ? rn.chunk_bytes : 0);
     if (need > kScratchBytes)
@@ -2155,7 +2184,9 @@ mhc_status mhc_mixes(const void* x, int32_t dtype, int64_t tokens, int32_t d,
   if (s != MHC_OK) return s;
   RouteNeeds rn;
   Route route;
-  if ((s = choose_route(path, workspace, dtype, d, tokens, &rn, &route)) != MHC_OK) return s;
+  bool plain = false;
+  if ((s = choose_route(path, workspace, dtype, d, tokens, &rn, &route, &plain)) != MHC_OK)
+    return s;
   if (route != Route::kTile) {
     const int64_t need = route == Route::kSplit ? rn.split_bytes : rn.chunk_bytes;
     Span all[8];
@@ -2168,7 +2199,8 @@ mhc_status mhc_mixes(const void* x, int32_t dtype, int64_t tokens, int32_t d,
              nullptr, pre_out, post_out, comb_out, mix_out, tokens, d, sinkhorn_iters, norm_eps,
              hc_eps};
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  if (route == Route::kSplit) return launch_split(a, workspace, rn.split, kMixesOnly, st);
+  if (route == Route::kSplit)
+    return launch_split(a, workspace, rn.split, kMixesOnly, plain, st);
   if (route == Route::kChunk) return launch_chunk(a, workspace, rn.chunk, kMixesOnly, st);
   return launch_step(a, dtype, kMixesOnly, st, "mixes kernel launch");
 }
@@ -2308,9 +2340,10 @@ int32_t mhc_fused_step_route_n(int32_t n, int32_t path, int64_t tokens, int32_t 
   }
   RouteNeedsN rn;
   Route r;
+  bool plain = false;
   static const char kDummy = 0;   // stands for a workspace; never dereferenced
-  if (choose_route_n(path, with_workspace ? &kDummy : nullptr, n, dtype, d, tokens, &rn, &r) !=
-      MHC_OK)
+  if (choose_route_n(path_family(path, &plain), with_workspace ? &kDummy : nullptr, n, dtype, d,
+                     tokens, &rn, &r) != MHC_OK)
     return -1;
   return r == Route::kTile ? MHC_PATH_TILE : (r == Route::kSplit ? MHC_PATH_SPLIT : MHC_PATH_CHUNK);
 }
@@ -2345,7 +2378,10 @@ mhc_status mhc_fused_step_n(int32_t n, const void* x, const void* f, int32_t dty
   if (s != MHC_OK) return s;
   RouteNeedsN rn;
   Route route;
-  if ((s = choose_route_n(path, workspace, n, dtype, d, tokens, &rn, &route)) != MHC_OK) return s;
+  bool plain = false;
+  if ((s = choose_route_n(path_family(path, &plain), workspace, n, dtype, d, tokens, &rn,
+                          &route)) != MHC_OK)
+    return s;
   if (route != Route::kTile) {
     const int64_t need = route == Route::kSplit ? rn.split_bytes : rn.chunk_bytes;
     Span all[15];
@@ -2356,7 +2392,7 @@ mhc_status mhc_fused_step_n(int32_t n, const void* x, const void* f, int32_t dty
   StepArgs a{x, f, pre_in, post_in, comb_in, w_packed, base, scale, gamma, x_out, y_out,
              pre_out, post_out, comb_out, mix_out, tokens, d, sinkhorn_iters, norm_eps, hc_eps};
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  return launch_route_n(n, route, rn, a, workspace, dtype, kFused, st);
+  return launch_route_n(n, route, rn, a, workspace, dtype, kFused, plain, st);
 }
 
 mhc_status mhc_mixes_n(int32_t n, const void* x, int32_t dtype, int64_t tokens, int32_t d,
@@ -2383,7 +2419,10 @@ mhc_status mhc_mixes_n(int32_t n, const void* x, int32_t dtype, int64_t tokens, 
   if (s != MHC_OK) return s;
   RouteNeedsN rn;
   Route route;
-  if ((s = choose_route_n(path, workspace, n, dtype, d, tokens, &rn, &route)) != MHC_OK) return s;
+  bool plain = false;
+  if ((s = choose_route_n(path_family(path, &plain), workspace, n, dtype, d, tokens, &rn,
+                          &route)) != MHC_OK)
+    return s;
   if (route != Route::kTile) {
     const int64_t need = route == Route::kSplit ? rn.split_bytes : rn.chunk_bytes;
     Span all[8];
@@ -2395,7 +2434,7 @@ mhc_status mhc_mixes_n(int32_t n, const void* x, int32_t dtype, int64_t tokens, 
              nullptr, pre_out, post_out, comb_out, mix_out, tokens, d, sinkhorn_iters, norm_eps,
              hc_eps};
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  return launch_route_n(n, route, rn, a, workspace, dtype, kMixesOnly, st);
+  return launch_route_n(n, route, rn, a, workspace, dtype, kMixesOnly, plain, st);
 }
 
 mhc_status mhc_sinkhorn_n(int32_t n, const float* mixes, int64_t tokens, const float* base,

@@ -23,5 +23,6 @@ def test_help_lists_the_modes():
     res = _run("--help")
     assert res.returncode == 0
     for flag in ("--gpus", "--steps", "--warmup", "--workload", "--path", "--form",
-                 "--sinkhorn-sweep", "--n-sweep", "--backward", "--all-configs", "--crossover"):
+                 "--sinkhorn-sweep", "--n-sweep", "--backward", "--all-configs", "--crossover",
+                 "--plain-launch"):
         assert flag in res.stdout, flag

@@ -248,3 +248,34 @@ def test_split_calls_on_two_streams_in_flight_together():
     for i, o in outs:
         for k in ref[i]:
             assert torch.equal(o[k], ref[i][k]), (i, k)
+
+
+@pytest.mark.parametrize("t", [1000, 9000])
+def test_plain_launch_matches_the_cooperative_launch(t):
+    """MHC_PATH_PLAIN_LAUNCH runs the same kernel as an ordinary launch (nothing
+    else runs on the device here, so its workgroups are resident together):
+    the fused step and the mixes-only mode give the cooperative launch's bits,
+    every wait completes (status word 0) and the whole header is zero again.
+    At 1,000 tokens every token is also checked against the oracle."""
+    d = 5120
+    case = make_case(wl.Workload(470 + t % 11, "split_plain", t, d, "bf16"))
+    ref, dev = _run(case)
+    ws = mhc.new_workspace(mhc.fused_step_workspace_bytes(t, d, "bf16"))
+    out, _ = run_step(case, path="split", workspace=ws, plain_launch=True)
+    assert mhc.split_status(ws) == 0, "a cross-workgroup wait gave up"
+    assert ws[:16384].count_nonzero().item() == 0
+    for k in ref:
+        if ref[k] is not None:
+            assert torch.equal(out[k], ref[k]), k
+    if t <= 1000:
+        check_step(case, out, "bf16")
+    wp = mhc.pack_wmix(dev["w_mix"], "bf16")
+    args = (dev["x"], wp, dev["base"], dev["scale"], case["iters"], case["norm_eps"],
+            case["hc_eps"])
+    m_coop = mhc.mixes(*args, want_mix=True, path="split", workspace=ws)
+    m_plain = mhc.mixes(*args, want_mix=True, path="split", workspace=ws, plain_launch=True)
+    torch.cuda.synchronize()
+    assert mhc.split_status(ws) == 0
+    assert ws[:16384].count_nonzero().item() == 0
+    for k in ("pre", "post", "comb", "mix"):
+        assert torch.equal(m_plain[k], m_coop[k]), k
