@@ -1299,12 +1299,14 @@ mhc_status device_cu_count(int* out) {
 }
 
 // Feature-split kernel geometry: `ns` workgroups per group, each owning S = d/ns
-// features, and `groups` groups (one workgroup per compute unit). Slices of a
-// multiple of 64 features (128-byte aligned rows, no 32-feature tail) are
-// preferred, then the most compute units in use, then fewer slices (less
-// exchange traffic). groups = 0 when the kernel does not apply: bf16 streams,
-// S in {64, 96, 128, 160}, at least `ns` compute units and cooperative launch
-// support are required.
+// features, and `groups` groups (one workgroup per compute unit). For large
+// calls, slices of a multiple of 64 features (128-byte aligned rows, no
+// 32-feature tail) are preferred, then the most compute units in use, then
+// fewer slices (less exchange traffic). Calls of at most kSplitCostBatches
+// 128-token batches take the geometry with the least estimated time
+// (split_cost_us), which may be another one. groups = 0 when the kernel does
+// not apply: bf16 streams, S in {64, 96, 128, 160}, at least `ns` compute
+// units and cooperative launch support are required.
 
 struct SplitCfg {
   int groups = 0;
@@ -1334,8 +1336,30 @@ mhc_status coop_supported(bool* ok) {
   return MHC_OK;
 }
 
-mhc_status split_config(int32_t dtype, int32_t d, SplitCfg* cfg) {
-  *cfg = SplitCfg{};
+// Estimated time of a feature-split call of `nbatch` 128-token batches, in
+// microseconds: a fixed part plus one batch time per round of `groups`
+// batches. Fitted to calls issued back to back at d = 5120 on the MI355X, up
+// to 40 batches: 40 slices of 128 features (6 groups) cost 38 + 15.4 per
+// round, 32 slices of 160 features (8 groups, all 256 CUs, the 32-feature
+// tail) 41.6 + 20.0. For example, at 4,096 tokens the two take 6 and 4
+// rounds: 130.5 against 121.6 us measured. A round's time grows with the
+// slice width, and by 4% more with the tail's 64-byte row pieces. With more
+// batches the rounds cost more as the device saturates (17.1 and 23.2 us at
+// 65,536 tokens), and the aligned geometry wins at every size measured
+// (8,192 tokens: 226 against 245 us).
+constexpr int64_t kSplitCostBatches = 40;
+
+double split_cost_us(const SplitCfg& c, int64_t nbatch) {
+  const bool tail = c.S % 64 != 0;
+  const double per_round = 15.4 * c.S / 128.0 * (tail ? 1.04 : 1.0);
+  return (tail ? 41.6 : 38.0) + per_round * (double)((nbatch + c.groups - 1) / c.groups);
+}
+
+// Every geometry the kernel can run for (dtype, d) on this device, the
+// preferred one for large calls first; none without cooperative launch
+// support.
+mhc_status split_candidates(int32_t dtype, int32_t d, SplitCfg (&out)[4], int* count) {
+  *count = 0;
   if (dtype != MHC_BF16) return MHC_OK;
   int cus = 0;
   mhc_status s = device_cu_count(&cus);
@@ -1347,15 +1371,38 @@ mhc_status split_config(int32_t dtype, int32_t d, SplitCfg* cfg) {
     if (S % 32 != 0 || S < 64 || S > fsplit::kMaxS) continue;
     const int used = (cus / ns) * ns;
     const int score = (S % 64 == 0 ? 1 << 20 : 0) + used * 64 + (64 - ns);
+    out[*count] = SplitCfg{cus / ns, ns, S};
     if (score > best_score) {
       best_score = score;
-      *cfg = SplitCfg{cus / ns, ns, S};
+      std::swap(out[0], out[*count]);
     }
+    ++*count;
   }
-  if (cfg->groups == 0) return MHC_OK;
+  if (*count == 0) return MHC_OK;
   bool coop = false;
   if ((s = coop_supported(&coop)) != MHC_OK) return s;
-  if (!coop) *cfg = SplitCfg{};
+  if (!coop) *count = 0;
+  return MHC_OK;
+}
+
+// The geometry of a call of `tokens` tokens, and the workspace bytes that
+// cover every candidate geometry at that size (so a workspace sized for T
+// tokens serves every call of at most T tokens, whichever geometry it takes).
+mhc_status split_config(int32_t dtype, int32_t d, int64_t tokens, SplitCfg* cfg,
+                        int64_t* bytes) {
+  *cfg = SplitCfg{};
+  *bytes = 0;
+  SplitCfg cand[4];
+  int count = 0;
+  const mhc_status s = split_candidates(dtype, d, cand, &count);
+  if (s != MHC_OK || count == 0) return s;
+  *cfg = cand[0];
+  const int64_t nbatch = (tokens + fsplit::kBatch - 1) / fsplit::kBatch;
+  for (int i = 0; i < count; ++i) {
+    *bytes = std::max(*bytes, fsplit::workspace_bytes(cand[i].groups, cand[i].ns, tokens));
+    if (nbatch <= kSplitCostBatches && split_cost_us(cand[i], nbatch) < split_cost_us(*cfg, nbatch))
+      *cfg = cand[i];
+  }
   return MHC_OK;
 }
 
@@ -1504,10 +1551,8 @@ struct RouteNeeds {
 
 mhc_status route_needs(int32_t dtype, int32_t d, int64_t tokens, RouteNeeds* rn) {
   *rn = RouteNeeds{};
-  mhc_status s = split_config(dtype, d, &rn->split);
+  mhc_status s = split_config(dtype, d, tokens, &rn->split, &rn->split_bytes);
   if (s != MHC_OK) return s;
-  if (rn->split.groups > 0)
-    rn->split_bytes = fsplit::workspace_bytes(rn->split.groups, rn->split.ns, tokens);
   rn->chunk = chunk_config(dtype, d, tokens);
   if (rn->chunk.nchunks > 0) rn->chunk_bytes = pipe::chunk_workspace_bytes(rn->chunk.nchunks, tokens);
   return MHC_OK;
