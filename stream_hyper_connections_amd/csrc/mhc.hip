@@ -1311,7 +1311,7 @@ mhc_status device_cu_count(int* out) {
 struct SplitCfg {
   int groups = 0;
   int ns = 0;
-  int S = 0;
+  int S = 0;      // 256: the two-term projection (hi + mid of W), else three terms
 };
 
 // Cooperative-launch support of the current device, cached per device
@@ -1358,13 +1358,22 @@ double split_cost_us(const SplitCfg& c, int64_t nbatch) {
 // Every geometry the kernel can run for (dtype, d) on this device, the
 // preferred one for large calls first; none without cooperative launch
 // support.
-mhc_status split_candidates(int32_t dtype, int32_t d, SplitCfg (&out)[4], int* count) {
+mhc_status split_candidates(int32_t dtype, int32_t d, SplitCfg (&out)[5], int* count) {
   *count = 0;
   if (dtype != MHC_BF16) return MHC_OK;
   int cus = 0;
   mhc_status s = device_cu_count(&cus);
   if (s != MHC_OK) return s;
   int best_score = -1;
+  // 256-feature slices on the two-term projection: 512-byte row segments per
+  // workgroup, half the exchange rows of 128-feature slices
+  if (d % fsplit::kMaxSW == 0) {
+    const int ns = d / fsplit::kMaxSW;
+    if (ns >= 16 && ns <= fsplit::kMaxSlicesW && ns <= cus) {
+      out[(*count)++] = SplitCfg{cus / ns, ns, fsplit::kMaxSW};
+      best_score = 1 << 30;
+    }
+  }
   for (int ns : {32, 40, 48, 64}) {
     if (d % ns != 0 || ns > cus) continue;
     const int S = d / ns;
@@ -1392,7 +1401,7 @@ mhc_status split_config(int32_t dtype, int32_t d, int64_t tokens, SplitCfg* cfg,
                         int64_t* bytes) {
   *cfg = SplitCfg{};
   *bytes = 0;
-  SplitCfg cand[4];
+  SplitCfg cand[5];
   int count = 0;
   const mhc_status s = split_candidates(dtype, d, cand, &count);
   if (s != MHC_OK || count == 0) return s;
@@ -1434,20 +1443,24 @@ mhc_status launch_split(const StepArgs& a, void* ws, const SplitCfg& cfg, int mo
   const bool full = mode == kFused;
   switch (cfg.S) {
     case 64:
-      fn = full ? reinterpret_cast<const void*>(fsplit::split_kernel<1, false, kFused>)
-                : reinterpret_cast<const void*>(fsplit::split_kernel<1, false, kMixesOnly>);
+      fn = full ? reinterpret_cast<const void*>(fsplit::split_kernel<1, false, kFused, 3>)
+                : reinterpret_cast<const void*>(fsplit::split_kernel<1, false, kMixesOnly, 3>);
       break;
     case 96:
-      fn = full ? reinterpret_cast<const void*>(fsplit::split_kernel<1, true, kFused>)
-                : reinterpret_cast<const void*>(fsplit::split_kernel<1, true, kMixesOnly>);
+      fn = full ? reinterpret_cast<const void*>(fsplit::split_kernel<1, true, kFused, 3>)
+                : reinterpret_cast<const void*>(fsplit::split_kernel<1, true, kMixesOnly, 3>);
       break;
     case 128:
-      fn = full ? reinterpret_cast<const void*>(fsplit::split_kernel<2, false, kFused>)
-                : reinterpret_cast<const void*>(fsplit::split_kernel<2, false, kMixesOnly>);
+      fn = full ? reinterpret_cast<const void*>(fsplit::split_kernel<2, false, kFused, 3>)
+                : reinterpret_cast<const void*>(fsplit::split_kernel<2, false, kMixesOnly, 3>);
       break;
     case 160:
-      fn = full ? reinterpret_cast<const void*>(fsplit::split_kernel<2, true, kFused>)
-                : reinterpret_cast<const void*>(fsplit::split_kernel<2, true, kMixesOnly>);
+      fn = full ? reinterpret_cast<const void*>(fsplit::split_kernel<2, true, kFused, 3>)
+                : reinterpret_cast<const void*>(fsplit::split_kernel<2, true, kMixesOnly, 3>);
+      break;
+    case fsplit::kMaxSW:
+      fn = full ? reinterpret_cast<const void*>(fsplit::split_kernel<4, false, kFused, 2>)
+                : reinterpret_cast<const void*>(fsplit::split_kernel<4, false, kMixesOnly, 2>);
       break;
     default: return fail(MHC_ERR_UNSUPPORTED, "feature-split kernel: slice of %d features", cfg.S);
   }

@@ -1,6 +1,7 @@
 // Feature-split fused step (bf16 streams, d = ns * S with S = 64 * NR + 32 * TAIL,
-// NR >= 1, S <= 160, ns <= 64 slices): the kernel behind mhc_fused_step when a
-// workspace is given.
+// NR >= 1; three-term projection: S <= 160, ns <= 64 slices; two-term
+// projection: S = 256, 16 <= ns <= 24): the kernel behind mhc_fused_step when
+// a workspace is given.
 //
 // Included by mhc.hip (one translation unit); uses its helpers and the pipe::
 // buffer-instruction wrappers.
@@ -13,11 +14,11 @@
 // x 128-256 bytes. Here every CU owns one slice of the features for good:
 //
 //   * Workgroup (group g, slice c): g = blockIdx % G, c = blockIdx / G, with G
-//     groups of ns workgroups (the host picks ns; d = 5120 runs 40 slices of
-//     128 features). Slice c is features [c*S, (c+1)*S) of every stream row,
-//     F row, new-stream row and y row; its W slice (S/32 packed steps, 80 KB
-//     for S = 128) is loaded into LDS once and used for every token the group
-//     processes. Groups take 128-token batches b = g, g+G, ...; wave w of a
+//     groups of ns workgroups (the host picks ns; d = 5120 runs 20 slices of
+//     256 features). Slice c is features [c*S, (c+1)*S) of every stream row,
+//     F row, new-stream row and y row; its W slice (S/32 packed steps: 96 KB
+//     for S = 256 with two terms, 80 KB for S = 128 with three) is loaded
+//     into LDS once and used for every token the group processes. Groups take 128-token batches b = g, g+G, ...; wave w of a
 //     workgroup owns tokens 16w .. 16w+15 of each batch.
 //   * Loads and stores move 8 token rows x 128 bytes per instruction ("half
 //     rounds" of 64 features); an S % 64 = 32 remainder ("tail", 16 rows x 64
@@ -94,6 +95,8 @@ constexpr int kRow = 32;                       // floats per token and slice: 24
 constexpr int kTiles = kTilesBf;
 constexpr int kCols = 3 * kMix;                // 72 packed columns in use
 constexpr int kMaxS = 160;                     // features per slice (d <= 5120)
+constexpr int kMaxSW = 256;                    // features per slice, two-term projection
+constexpr int kMaxSlicesW = 24;                // slices per group, two-term projection
 constexpr int kStepBytes = kStreams * kTiles * 1024;   // packed bytes per 32 features
 constexpr int kSC1 = 16;                       // cache-policy bit: device scope
 constexpr uint32_t kSpinLimit = 1u << 20;
@@ -155,7 +158,7 @@ struct __align__(16) WaveSmem {
 struct __align__(16) Smem {
   u32x4 w[kMaxS / 32 * kStepBytes / 16];   // W slice, packed B-operand order
   WaveSmem wv[kWaves];
-  float gamma[kMaxS];
+  float gamma[kMaxSW];
   float base[kMix];
   float scale[4];
   uint32_t lcount[kRing];
@@ -317,14 +320,22 @@ __device__ __forceinline__ void release_workspace(char* ws, int64_t ctr0, int nc
   }
 }
 
-template <int NR, bool TAIL, int MODE>
+// TERMS: bf16 terms of W in the projection. 3: hi + mid + lo = w exactly
+// (packed tiles 0..4 in LDS). 2: hi + mid (tiles 0..2 of the same packing),
+// |w - hi - mid| <= 2^-16 |w|, which leaves LDS room for 256-feature slices.
+template <int NR, bool TAIL, int MODE, int TERMS>
 __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
   constexpr bool kFull = MODE == kFused;   // else mixes only (hc_mixes)
   __shared__ Smem sm;
   constexpr int S = 64 * NR + (TAIL ? 32 : 0);   // features per slice
   constexpr int KS = S / 32;                      // packed steps per slice
   constexpr int NI = 2 * NR + (TAIL ? 1 : 0);     // load groups per wave and batch
-  static_assert(NR >= 1 && S <= kMaxS, "slice shape");
+  constexpr int kT = TERMS == 3 ? kTiles : 3;     // packed tiles in LDS per (step, stream)
+  constexpr int kC = TERMS * kMix;                // projection columns in use
+  constexpr int kSk = (TERMS == 3 ? kMaxSlices : kMaxSlicesW) / 8;   // slice loads per mixes row
+  static_assert(TERMS == 2 || TERMS == 3, "terms");
+  static_assert(NR >= 1 && S <= (TERMS == 3 ? kMaxS : kMaxSW), "slice shape");
+  static_assert(KS * kStreams * kT * 1024 <= (int)sizeof(sm.w), "W slice fits");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -347,7 +358,15 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
   {
     const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.wpk) +
                                                       (size_t)c * KS * kStepBytes);
-    for (int i = tid; i < KS * kStepBytes / 16; i += kThreads) sm.w[i] = src[i];
+    if constexpr (TERMS == 3) {
+      for (int i = tid; i < KS * kStepBytes / 16; i += kThreads) sm.w[i] = src[i];
+    } else {
+      // tiles 0 .. kT-1 of every (step, stream): the hi and mid columns
+      for (int i = tid; i < KS * kStreams * kT * 64; i += kThreads) {
+        const int sk = i / (kT * 64), q = (i / 64) % kT;
+        sm.w[i] = src[(sk * kTiles + q) * 64 + (i & 63)];
+      }
+    }
     if constexpr (kFull)
       for (int i = tid; i < S; i += kThreads) sm.gamma[i] = a.gamma[f0 + i];
     if (tid < kMix) sm.base[tid] = a.base[tid];
@@ -431,7 +450,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
     }
   };
   auto wlds = [&](int step, int k, int q) -> bf16x8 {
-    return __builtin_bit_cast(bf16x8, sm.w[((step * kStreams + k) * kTiles + q) * 64 + lane]);
+    return __builtin_bit_cast(bf16x8, sm.w[((step * kStreams + k) * kT + q) * 64 + lane]);
   };
   // staging index of (token, 16-byte chunk) with the XOR swizzle that keeps
   // both the row writes and the operand reads free of bank conflicts
@@ -480,12 +499,12 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
     // l>>3 + 8k) follow at once so their latency hides behind the y work
     const int tb = c + ns * wave;
     const bool sk = tb < kBatch;
-    f32x4 sk_part[kMaxSlices / 8];
+    f32x4 sk_part[kSk];
     {
       const uint32_t base = (uint32_t)(mp_off(G) + slot_id * mp_slot_bytes(ns)) +
                             (uint32_t)((tb * kRow + 4 * (lane & 7)) * 4);
 #pragma unroll
-      for (int j = 0; j < kMaxSlices / 8; ++j) {
+      for (int j = 0; j < kSk; ++j) {
         const int sl = (lane >> 3) + 8 * j;
         sk_part[j] = bload_sc1(
             wsr, sk && sl < ns ? base + (uint32_t)(sl * kBatch * kRow * 4) : kOutOfRange, 0);
@@ -521,7 +540,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
     if (sk) {
       f32x4 acc = sk_part[0];
 #pragma unroll
-      for (int j = 1; j < kMaxSlices / 8; ++j) acc += sk_part[j];
+      for (int j = 1; j < kSk; ++j) acc += sk_part[j];
       float v[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {   // sum over the 8 slice groups (lanes l ^ 8, 16, 32)
@@ -554,9 +573,9 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
   for (int i = 0; i < nbg; ++i) {
     store_coef(cf);
     __builtin_amdgcn_wave_barrier();
-    f32x4 acc[kTiles];
+    f32x4 acc[kT];
 #pragma unroll
-    for (int q = 0; q < kTiles; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < kT; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
     float ssA[2] = {0.f, 0.f}, hsA[2] = {0.f, 0.f}, ssT = 0.f, hsT = 0.f;
 
     // both halves of round rr are in flight on entry; each half's buffer is
@@ -605,7 +624,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
           const bf16x8 A = __builtin_bit_cast(bf16x8, buf[sidx(t16, 4 * q2 + g16)]);
           const int step = fr0 / 32 + 2 * rr + q2;
 #pragma unroll
-          for (int q = 0; q < kTiles; ++q)
+          for (int q = 0; q < kT; ++q)
             acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, wlds(step, k, q), acc[q], 0, 0, 0);
         }
         __builtin_amdgcn_wave_barrier();
@@ -625,7 +644,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
       for (int k = 0; k < 4; ++k) {
         const bf16x8 A = __builtin_bit_cast(bf16x8, xot[k]);
 #pragma unroll
-        for (int q = 0; q < kTiles; ++q)
+        for (int q = 0; q < kT; ++q)
           acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, wlds(ftl / 32, k, q), acc[q], 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -660,9 +679,9 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
       // projection partials -> per-token rows, hi + mid + lo
       __builtin_amdgcn_wave_barrier();
 #pragma unroll
-      for (int q = 0; q < kTiles; ++q) {
+      for (int q = 0; q < kT; ++q) {
         const int col = 16 * q + t16;
-        if (col < kCols) {
+        if (col < kC) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) wsm.u.cst[4 * g16 + e][col] = acc[q][e];
         }
@@ -672,7 +691,8 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
 #pragma unroll
       for (int jj = 0; jj < 6; ++jj) {
         const int row = 6 * (lane & 3) + jj;
-        mv[jj] = (wsm.u.cst[u][row] + wsm.u.cst[u][kMix + row]) + wsm.u.cst[u][2 * kMix + row];
+        mv[jj] = wsm.u.cst[u][row] + wsm.u.cst[u][kMix + row];
+        if constexpr (TERMS == 3) mv[jj] += wsm.u.cst[u][2 * kMix + row];
       }
       __builtin_amdgcn_wave_barrier();
       // assemble the 16 token rows (24 mixes, x'^2, h^2, zero pad) in LDS, then
