@@ -111,10 +111,14 @@ constexpr int64_t kWsHeader = 16384;
 
 constexpr int kRowRor2 = 0x122;                // DPP row rotate right by 2
 
-// cache policies: stream loads and y stores non-temporal, new-stream stores
-// default (measured fastest of the combinations)
+// cache policies: stream loads and y stores non-temporal; new-stream stores
+// non-temporal on 256-feature slices, default on the narrower ones (each the
+// fastest combination measured for its geometry: at 65,536 x 5120 on 256
+// features, non-temporal new streams 1.360 against 1.384 ms per call, default
+// loads 1.375, default y stores 1.386)
 constexpr int kLoadAux = kNT;
-constexpr int kXoAux = 0;
+constexpr int kXoAuxNarrow = 0;
+constexpr int kXoAuxWide = kNT;
 constexpr int kYAux = kNT;
 
 // workspace layout for `groups` groups of `ns` slices: status word, one
@@ -336,6 +340,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
   static_assert(TERMS == 2 || TERMS == 3, "terms");
   static_assert(NR >= 1 && S <= (TERMS == 3 ? kMaxS : kMaxSW), "slice shape");
   static_assert(KS * kStreams * kT * 1024 <= (int)sizeof(sm.w), "W slice fits");
+  constexpr int kXoAux = TERMS == 2 ? kXoAuxWide : kXoAuxNarrow;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
