@@ -264,7 +264,7 @@ ROUTE_KERNELS = {
 
 
 def all_configs_bench(reps_min=50, min_ms=200.0, flush_bytes=512 << 20, path="auto",
-                      plain_launch=False):
+                      cooperative=False):
     """mhc_fused_step alone on each workload (the chain: its first step), with
     HIP events around the C-ABI call: warm (10 warm-up calls, then at least
     `reps_min` calls or `min_ms` of calls) and cache-flushed (a write of
@@ -272,8 +272,9 @@ def all_configs_bench(reps_min=50, min_ms=200.0, flush_bytes=512 << 20, path="au
     are not served from the 256 MB Infinity Cache). One JSON line per workload
     with p50 / p95 / p99 in microseconds and tokens/s, GB/s and % of peak at
     the p50, and the time per call of 200 calls back to back, eager and as
-    replays of the call captured in a graph. plain_launch: the feature-split
-    kernel launched as an ordinary kernel (MHC_PATH_PLAIN_LAUNCH)."""
+    replays of the call captured in a graph. cooperative: the feature-split
+    kernel launched cooperatively (MHC_PATH_COOPERATIVE) instead of as an
+    ordinary kernel."""
     import torch
     import stream_hyper_connections_amd as mhc
     from stream_hyper_connections_amd import workloads as wl
@@ -282,7 +283,7 @@ def all_configs_bench(reps_min=50, min_ms=200.0, flush_bytes=512 << 20, path="au
     for name in CONFIG_NAMES:
         w = wl.WORKLOADS[name]
         try:
-            route = mhc.fused_step_route(path, w.tokens, w.d, w.dtype, plain_launch=plain_launch)
+            route = mhc.fused_step_route(path, w.tokens, w.d, w.dtype, cooperative=cooperative)
         except ValueError as e:
             print(f"[bench] {name}: skipped ({e})", file=sys.stderr, flush=True)
             continue
@@ -306,13 +307,13 @@ def all_configs_bench(reps_min=50, min_ms=200.0, flush_bytes=512 << 20, path="au
         def call():
             mhc.fused_step(x, f, prior["pre"], prior["post"], prior["comb"], wp, cur["base"],
                            cur["scale"], cur["gamma"], w.iters, w.norm_eps, w.hc_eps, path=path,
-                           workspace=ws, plain_launch=plain_launch, **outs)
+                           workspace=ws, cooperative=cooperative, **outs)
 
         line = {"metric": "fused mHC step latency per workload, n=4", "workload": name,
                 "tokens": w.tokens, "d": w.d, "dtype": w.dtype,
                 "route": route}
         if route == "split":
-            line["launch"] = "plain" if plain_launch else "cooperative"
+            line["launch"] = "cooperative" if cooperative else "plain"
         alg = algorithmic_bytes(w.tokens, w.d, elem)
         for mode in ("warm", "flushed"):
             for _ in range(10):
@@ -380,11 +381,11 @@ def all_configs_bench(reps_min=50, min_ms=200.0, flush_bytes=512 << 20, path="au
 def crossover_bench(d=5120, sizes=(256, 512, 768, 1024, 1536, 2048, 2560, 3072, 4096), calls=40,
                     runs=5):
     """mhc_fused_step on the chunked and the feature-split route (launched
-    cooperatively, and as an ordinary kernel: "split_plain") for a range of
-    token counts (seeded random bf16 inputs of width d): per route and size,
-    `calls` calls back to back between two events, median over `runs` runs.
-    One JSON line per size; the routes' crossing points are where path "auto"
-    should switch, with and without MHC_PATH_PLAIN_LAUNCH."""
+    as an ordinary kernel: "split", and cooperatively: "split_coop") for a
+    range of token counts (seeded random bf16 inputs of width d): per route
+    and size, `calls` calls back to back between two events, median over
+    `runs` runs. One JSON line per size; the routes' crossing points are where
+    path "auto" should switch, with and without MHC_PATH_COOPERATIVE."""
     import torch
     import stream_hyper_connections_amd as mhc
     for t in sizes:
@@ -405,11 +406,11 @@ def crossover_bench(d=5120, sizes=(256, 512, 768, 1024, 1536, 2048, 2560, 3072, 
                     comb_out=torch.empty_like(comb))
         line = {"metric": "fused step call time by route, back to back", "tokens": t, "d": d,
                 "unit": "us per call", "auto_route": mhc.fused_step_route("auto", t, d, "bf16")}
-        for name in ("chunk", "split", "split_plain"):
+        for name in ("chunk", "split", "split_coop"):
             def call():
                 mhc.fused_step(x, f, pre, post, comb, wp, base, scale, gamma,
                                path=name.split("_")[0], workspace=ws,
-                               plain_launch=name == "split_plain", **outs)
+                               cooperative=name == "split_coop", **outs)
             for _ in range(5):
                 call()
             torch.cuda.synchronize()
@@ -436,9 +437,9 @@ def parse():
     ap.add_argument("--workload", default="large_prefill")
     ap.add_argument("--path", choices=("auto", "tile", "split", "chunk"), default="auto",
                     help="kernel family of mhc_fused_step (auto: the library's choice by size)")
-    ap.add_argument("--plain-launch", action="store_true",
-                    help="launch the feature-split kernel as an ordinary kernel "
-                         "(MHC_PATH_PLAIN_LAUNCH) instead of a cooperative one")
+    ap.add_argument("--cooperative", action="store_true",
+                    help="launch the feature-split kernel cooperatively "
+                         "(MHC_PATH_COOPERATIVE) instead of as an ordinary kernel")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="minimum oracle time for the cpu_baseline sample")
@@ -610,7 +611,7 @@ def main():
         backward_bench(w, args.steps, args.warmup)
         return
     if args.all_configs:
-        all_configs_bench(path=args.path, plain_launch=args.plain_launch)
+        all_configs_bench(path=args.path, cooperative=args.cooperative)
         return
     if args.crossover:
         crossover_bench()
@@ -630,7 +631,7 @@ def main():
     outs = dict(x_out=torch.empty_like(x), y_out=torch.empty_like(f),
                 pre_out=torch.empty_like(prior["pre"]), post_out=torch.empty_like(prior["post"]),
                 comb_out=torch.empty_like(prior["comb"]))
-    route = mhc.fused_step_route(args.path, w.tokens, w.d, w.dtype, plain_launch=args.plain_launch)
+    route = mhc.fused_step_route(args.path, w.tokens, w.d, w.dtype, cooperative=args.cooperative)
     kernel_name = ROUTE_KERNELS[route]
     if args.form != "fused":
         kernel_name = "hc_post + hc_mixes + hc_pre + RMSNorm kernels (three-kernel form)"
@@ -652,7 +653,7 @@ def main():
         if args.form == "fused":
             mhc.fused_step(x, f, prior["pre"], prior["post"], prior["comb"], wp, cur["base"],
                            cur["scale"], cur["gamma"], w.iters, w.norm_eps, w.hc_eps,
-                           path=args.path, plain_launch=args.plain_launch, **outs)
+                           path=args.path, cooperative=args.cooperative, **outs)
         else:
             mhc.three_kernel_step(x, f, prior["pre"], prior["post"], prior["comb"], wp,
                                   cur["base"], cur["scale"], cur["gamma"], w.iters, w.norm_eps,
@@ -711,7 +712,7 @@ def main():
         "config": {"workload": w.name, "tokens": w.tokens, "batch": w.batch,
                    "seq_len": w.tokens // w.batch, "n_streams": N, "d": w.d,
                    "sinkhorn_iters": w.iters, "stream_dtype": w.dtype, "form": args.form,
-                   "split_launch": (("plain" if args.plain_launch else "cooperative")
+                   "split_launch": (("cooperative" if args.cooperative else "plain")
                                     if route == "split" else None)},
         "step_ms_p50": round(float(np.percentile(step_ms, 50)), 5),
         "step_ms_p95": round(float(np.percentile(step_ms, 95)), 5),

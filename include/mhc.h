@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define MHC_ABI_VERSION 10
+#define MHC_ABI_VERSION 11
 #define MHC_N_STREAMS 4
 #define MHC_N_MIX 24
 
@@ -63,8 +63,8 @@ typedef enum mhc_dtype { MHC_F32 = 0, MHC_BF16 = 1 } mhc_dtype;
 /*
  * Kernel family of mhc_fused_step and mhc_mixes:
  *   MHC_PATH_AUTO   no workspace: the tile kernel. With a workspace: the
- *                   chunked kernels up to 2048 tokens (1024 with
- *                   MHC_PATH_PLAIN_LAUNCH) where they apply, else the
+ *                   chunked kernels up to 896 tokens (2048 with
+ *                   MHC_PATH_COOPERATIVE) where they apply, else the
  *                   feature-split kernel where it applies, else the tile
  *                   kernel.
  *   MHC_PATH_TILE   the tile kernel (one workgroup per 16 tokens, no
@@ -73,31 +73,39 @@ typedef enum mhc_dtype { MHC_F32 = 0, MHC_BF16 = 1 } mhc_dtype;
  *                   MHC_ERR_UNSUPPORTED where it does not apply).
  *   MHC_PATH_CHUNK  the chunked kernels (needs a workspace;
  *                   MHC_ERR_UNSUPPORTED where they do not apply).
- * MHC_PATH_PLAIN_LAUNCH is a flag that may be OR-ed into any of them. It
- * changes how the feature-split kernel is launched and nothing else: as an
- * ordinary kernel instead of a cooperative one. A cooperative launch runs
- * the kernel alone on the device, and the device idles for about 11 us
- * before and after it. The plain launch avoids that idle and saves about
- * 10 us per call. That kernel's workgroups (one per compute unit, at most
- * the device's count) wait for one another, so all of them must run at
- * once. With the flag the caller guarantees this: while the call runs, no
- * other work may hold compute units indefinitely. That excludes a CU mask on
- * the stream that leaves fewer compute units than the grid, and a kernel
- * elsewhere on the device that waits for this call. Kernels that merely run
- * alongside only delay it. If the guarantee fails, a wait gives up after
- * 2^20 polls: the workspace status word is set and the outputs are invalid,
- * as after any given-up wait. With MHC_PATH_AUTO the flag also lowers the
- * switch from the chunked kernels to the feature-split kernel from 2048 to
- * 1024 tokens, since the split route's fixed cost is then smaller.
- * mhc_fused_step_route reports that choice. The n-family's switch stays at
- * 2048 tokens.
+ * MHC_PATH_COOPERATIVE is a flag that may be OR-ed into any of them. It
+ * changes how the feature-split kernel is launched and nothing else. That
+ * kernel runs one workgroup per compute unit (at most the device's count) in
+ * groups of ns workgroups that wait for one another. By default it is an
+ * ordinary launch: each workgroup takes its place in start order from a
+ * counter in the workspace, and groups are filled in that order, so only the
+ * one group still being filled can be waiting; every other group runs to its
+ * end and frees its compute units. The call therefore completes whenever the
+ * device can eventually hold one group (ns compute units, 20 at d = 5120) of
+ * it at once: kernels running alongside only delay it, and two calls in
+ * flight on two streams both finish. It cannot complete if other work holds
+ * all but fewer than ns compute units for good (a CU mask on the stream that
+ * leaves fewer than ns, a kernel elsewhere that waits for this call, or more
+ * than (compute units)/(ns - 1) such calls in flight at once); then a wait
+ * gives up after 2^20 polls, the workspace status word is set and the outputs
+ * are invalid, as after any given-up wait. With MHC_PATH_COOPERATIVE the
+ * kernel is launched cooperatively instead: the runtime runs it alone on the
+ * device with all workgroups resident, and the device idles for about 11 us
+ * before and after it (about 19 us per call issued back to back). With
+ * MHC_PATH_AUTO the flag also raises the switch from the chunked kernels to
+ * the feature-split kernel from 896 to 2048 tokens, since the split route's
+ * fixed cost is then larger. mhc_fused_step_route reports that choice. The
+ * n-family's switch is 2048 tokens either way. MHC_PATH_PLAIN_LAUNCH (the
+ * ordinary launch, the default since ABI 11) is still accepted and changes
+ * nothing; it may not be combined with MHC_PATH_COOPERATIVE.
  */
 typedef enum mhc_path {
   MHC_PATH_AUTO = 0,
   MHC_PATH_TILE = 1,
   MHC_PATH_SPLIT = 2,
   MHC_PATH_CHUNK = 3,
-  MHC_PATH_PLAIN_LAUNCH = 16
+  MHC_PATH_PLAIN_LAUNCH = 16,
+  MHC_PATH_COOPERATIVE = 32
 } mhc_path;
 
 typedef void* mhc_stream_t;
@@ -143,9 +151,11 @@ mhc_status mhc_pack_wmix(const float* w_mix, int32_t d, int32_t dtype, void* w_p
  * bad arguments or a failing HIP query (see mhc_last_error).
  *   - Feature-split kernel: MHC_BF16 streams whose width splits into ns
  *     slices of S features, ns in {32, 40, 48, 64} and S in {64, 96, 128, 160}
- *     (d = 2048 ... 10240, e.g. 5120 = 40 x 128), on a device with at least ns
- *     compute units and cooperative launch support. About 17 MB for d = 5120
- *     on 256 CUs, plus 96 bytes per token for the mixes rows.
+ *     (d = 2048 ... 10240), or S = 256 and 16 <= ns <= 24 (d a multiple of
+ *     256 from 4096 to 6144; e.g. 5120 = 20 x 256, the geometry of large
+ *     calls there), on a device with at least ns compute units and
+ *     cooperative launch support. About 17 MB for d = 5120 on 256 CUs, plus
+ *     96 bytes per token for the mixes rows.
  *   - Chunked kernels: at most 8192 tokens; MHC_BF16 streams with d a
  *     multiple of 64 up to 5120, or MHC_F32 streams. The 16,384-byte header
  *     plus 128 bytes per token and chunk, a chunk being 512 features (bf16)
@@ -186,14 +196,15 @@ int32_t mhc_fused_step_route(int32_t path, int64_t tokens, int32_t d, int32_t dt
  * Outputs: x_out [T][4][d] (may be x), y_out [T][d], pre_out/post_out
  *          [T][4], comb_out [T][4][4], mix_out [T][24] (optional, NULL to skip).
  * path:    mhc_path, the kernel family (MHC_PATH_AUTO picks by size),
- *          optionally with MHC_PATH_PLAIN_LAUNCH OR-ed in.
+ *          optionally with MHC_PATH_COOPERATIVE OR-ed in.
  * Workspace (optional): NULL, or device memory of workspace_bytes bytes,
  *          256-byte aligned, overlapping no other argument, used by:
  *          - the feature-split kernel: each compute unit keeps one slice of
  *            the features and of W on chip; workgroups exchange per-token
- *            partial sums through the workspace. It needs the whole device:
- *            it is launched cooperatively, one workgroup per compute unit, and
- *            fails with MHC_ERR_HIP when that launch is refused.
+ *            partial sums through the workspace. One workgroup per compute
+ *            unit, launched as an ordinary kernel, or cooperatively with
+ *            MHC_PATH_COOPERATIVE (MHC_ERR_HIP when that launch is refused);
+ *            see mhc_path for when it completes.
  *          - the chunked kernels: workgroups of 16 tokens x 512 features write
  *            per-token partial sums to the workspace, and a second kernel
  *            finishes each token (two plain launches; for small calls).
@@ -331,7 +342,7 @@ mhc_status mhc_pack_wmix_n(int32_t n, const float* w_mix, int32_t d, int32_t dty
  *   - the feature-split kernel: n in {2, 4} with bf16 streams, d = ns * S with
  *     S a multiple of 64 of at most 256 (n = 2) or 128 (n = 4) features and
  *     16 <= ns <= 64 slices, at most one per compute unit, on a device with
- *     cooperative launch;
+ *     cooperative launch support;
  *   - the chunked block kernel: tokens <= 8192, any n and dtype; the
  *     16,384-byte header plus 4 * R bytes per token and chunk, R = (2+n)n
  *     + 2 rounded up to a multiple of 4, with up to 80 chunks of whole units
@@ -359,9 +370,9 @@ int32_t mhc_fused_step_route_n(int32_t n, int32_t path, int64_t tokens, int32_t 
  *   MHC_PATH_TILE   the token-block kernel (one workgroup per 128 tokens, no
  *                   workspace; the workspace argument is ignored);
  *   MHC_PATH_SPLIT  the feature-split kernel (each compute unit keeps a slice
- *                   of the features and of W; cooperative launch, one
- *                   workgroup per compute unit; the same status word at
- *                   offset 0 and ordering rules as mhc_fused_step);
+ *                   of the features and of W; one workgroup per compute
+ *                   unit, launched as for mhc_fused_step; the same status
+ *                   word at offset 0 and ordering rules);
  *   MHC_PATH_CHUNK  the block kernel in chunks of the features (a workgroup
  *                   per 128-token block and chunk writes partial sums to the
  *                   workspace, h parked in y_out; a finishing kernel adds the
@@ -371,7 +382,7 @@ int32_t mhc_fused_step_route_n(int32_t n, int32_t path, int64_t tokens, int32_t 
  *                   applies, else the chunks where they apply (up to 8192
  *                   tokens), else the block kernel.
  * SPLIT and CHUNK need a workspace and are MHC_ERR_UNSUPPORTED where they do
- * not apply. MHC_PATH_PLAIN_LAUNCH may be OR-ed in, as for mhc_fused_step.
+ * not apply. MHC_PATH_COOPERATIVE may be OR-ed in, as for mhc_fused_step.
  * Workspace: NULL / 0 bytes, or device memory of at least the chosen route's
  * bytes (mhc_fused_step_n_workspace_bytes() covers both), 256-byte aligned,
  * overlapping no other argument; a smaller one is MHC_ERR_INVALID_ARG. Its

@@ -13,7 +13,7 @@ from .binding import (  # noqa: F401
     d_granule,
     PATHS,
     PATHS_N,
-    PLAIN_LAUNCH,
+    COOPERATIVE,
     fused_step,
     fused_step_backward_n,
     fused_step_backward_workspace_bytes_n,

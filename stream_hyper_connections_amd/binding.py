@@ -173,22 +173,23 @@ def pack_wmix(w_mix: torch.Tensor, dtype, out: torch.Tensor | None = None) -> to
 # mhc_path codes by name
 PATHS = {"auto": 0, "tile": 1, "split": 2, "chunk": 3}
 _PATH_NAMES = {v: k for k, v in PATHS.items()}
-# MHC_PATH_PLAIN_LAUNCH: OR-ed into a path code, the feature-split kernel is
-# launched as an ordinary kernel (the caller guarantees that nothing else
-# holds compute units for the whole call; see mhc.h)
+# MHC_PATH_COOPERATIVE: OR-ed into a path code, the feature-split kernel is
+# launched cooperatively instead of as an ordinary kernel (see mhc.h)
+COOPERATIVE = 32
+# MHC_PATH_PLAIN_LAUNCH: the ordinary launch, the default; accepted, changes nothing
 PLAIN_LAUNCH = 16
 
 _workspaces = {}
 
 
 def fused_step_route(path: str, tokens: int, d: int, dtype, with_workspace=True,
-                     plain_launch=False) -> str:
+                     cooperative=False) -> str:
     """mhc_fused_step_route: the kernel family ("tile", "split" or "chunk") that
-    fused_step / mixes run for `path` (and plain_launch); ValueError if that
+    fused_step / mixes run for `path` (and cooperative); ValueError if that
     path cannot run these arguments."""
     if path not in PATHS:
         raise ValueError(f"unknown path {path!r}")
-    r = load().mhc_fused_step_route(PATHS[path] | (PLAIN_LAUNCH if plain_launch else 0), tokens,
+    r = load().mhc_fused_step_route(PATHS[path] | (COOPERATIVE if cooperative else 0), tokens,
                                     d, _dtype_name_code(dtype), 1 if with_workspace else 0)
     if r < 0:
         raise ValueError(f"path {path!r}, d={d}, {dtype}: {last_error()}")
@@ -245,7 +246,7 @@ def _raise_on_status(fn, workspace):
 def fused_step(x, f, pre_in, post_in, comb_in, w_packed, base, scale, gamma, iters=20,
                norm_eps=1e-6, hc_eps=1e-6, x_out=None, y_out=None, pre_out=None, post_out=None,
                comb_out=None, mix_out=None, want_mix=False, path="auto", workspace=None,
-               check_status=False, plain_launch=False) -> dict:
+               check_status=False, cooperative=False) -> dict:
     """mhc_fused_step on tensors. x [T,4,d], f [T,d] (bf16 or f32); coefficients
     and parameters float32. Returns dict(x_out, y, pre, post, comb, mix).
 
@@ -254,15 +255,14 @@ def fused_step(x, f, pre_in, post_in, comb_in, w_packed, base, scale, gamma, ite
     library's choice by size, with a workspace where one applies). workspace:
     optional zero-initialised uint8 tensor (new_workspace; a cached one is used
     otherwise). check_status: synchronise after the call and raise MhcError if
-    the workspace's status word is set (it is cleared then). plain_launch: OR
-    MHC_PATH_PLAIN_LAUNCH into the path (an ordinary launch of the
-    feature-split kernel; the caller guarantees that nothing else holds
-    compute units for the whole call)."""
+    the workspace's status word is set (it is cleared then). cooperative: OR
+    MHC_PATH_COOPERATIVE into the path (a cooperative launch of the
+    feature-split kernel instead of an ordinary one)."""
     t, n, d = x.shape
     if n != N_STREAMS:
         raise ValueError("x must be [T, 4, d]")
     code, ws_ptr, ws_bytes, ws = _workspace_arg(x, t, d, path, workspace)
-    code |= PLAIN_LAUNCH if plain_launch else 0
+    code |= COOPERATIVE if cooperative else 0
     x_out = torch.empty_like(x) if x_out is None else x_out
     y_out = torch.empty_like(f) if y_out is None else y_out
     pre_out = _f32_out((t, N_STREAMS), x, pre_out)
@@ -285,10 +285,10 @@ def fused_step(x, f, pre_in, post_in, comb_in, w_packed, base, scale, gamma, ite
 def fused_step_noalloc(x, f, pre_in, post_in, comb_in, w_packed, base, scale, gamma, iters=20,
                        norm_eps=1e-6, hc_eps=1e-6, x_out=None, y_out=None, pre_out=None,
                        post_out=None, comb_out=None, mix_out=None, want_mix=False,
-                       path="auto", plain_launch=False) -> dict:
+                       path="auto", cooperative=False) -> dict:
     """mhc_fused_step_noalloc on tensors: fused_step with the library's static
     scratch as the workspace (no device allocation by the library; outputs
-    not given are allocated here by torch). plain_launch as for fused_step."""
+    not given are allocated here by torch). cooperative as for fused_step."""
     t, n, d = x.shape
     if n != N_STREAMS:
         raise ValueError("x must be [T, 4, d]")
@@ -305,7 +305,7 @@ def fused_step_noalloc(x, f, pre_in, post_in, comb_in, w_packed, base, scale, ga
         _ptr(x), _ptr(f), _dtype_code(x), t, d, _ptr(pre_in), _ptr(post_in), _ptr(comb_in),
         _ptr(w_packed), _ptr(base), _ptr(scale), _ptr(gamma), iters, norm_eps, hc_eps,
         _ptr(x_out), _ptr(y_out), _ptr(pre_out), _ptr(post_out), _ptr(comb_out), _ptr(mix_out),
-        PATHS[path] | (PLAIN_LAUNCH if plain_launch else 0), _stream())
+        PATHS[path] | (COOPERATIVE if cooperative else 0), _stream())
     _check("mhc_fused_step_noalloc", st)
     return {"x_out": x_out, "y": y_out, "pre": pre_out, "post": post_out, "comb": comb_out,
             "mix": mix_out}
@@ -331,14 +331,14 @@ def _workspace_arg(x, t, d, path, workspace):
 
 def mixes(x, w_packed, base, scale, iters=20, norm_eps=1e-6, hc_eps=1e-6, pre_out=None,
           post_out=None, comb_out=None, mix_out=None, want_mix=False, path="auto",
-          workspace=None, check_status=False, plain_launch=False) -> dict:
+          workspace=None, check_status=False, cooperative=False) -> dict:
     """mhc_mixes on tensors. Returns dict(pre, post, comb, mix). path,
-    workspace, check_status and plain_launch as for fused_step."""
+    workspace, check_status and cooperative as for fused_step."""
     t, n, d = x.shape
     if n != N_STREAMS:
         raise ValueError("x must be [T, 4, d]")
     code, ws_ptr, ws_bytes, ws = _workspace_arg(x, t, d, path, workspace)
-    code |= PLAIN_LAUNCH if plain_launch else 0
+    code |= COOPERATIVE if cooperative else 0
     pre_out = _f32_out((t, N_STREAMS), x, pre_out)
     post_out = _f32_out((t, N_STREAMS), x, post_out)
     comb_out = _f32_out((t, N_STREAMS, N_STREAMS), x, comb_out)
@@ -486,17 +486,17 @@ def _workspace_arg_n(x, n, t, d, path, workspace):
 def fused_step_n(x, f, pre_in, post_in, comb_in, w_packed, base, scale, gamma, iters=20,
                  norm_eps=1e-6, hc_eps=1e-6, x_out=None, y_out=None, pre_out=None, post_out=None,
                  comb_out=None, mix_out=None, path="auto", workspace=None,
-                 check_status=False, plain_launch=False) -> dict:
+                 check_status=False, cooperative=False) -> dict:
     """mhc_fused_step_n on tensors: x [T,n,d], f [T,d]; w_packed from pack_wmix_n.
     Returns dict(x_out, y, pre, post, comb, mix) (mix is always produced).
     path: "block" (no workspace), "split" (feature-split kernel: n in {2, 4},
     bf16), "chunk" (the block kernel in chunks of the features, up to 8192
     tokens) or "auto" (the library's choice by size); workspace: optional
     zero-initialised uint8 tensor (a cached one is used otherwise);
-    check_status and plain_launch as for fused_step."""
+    check_status and cooperative as for fused_step."""
     t, n, d = x.shape
     code, ws_ptr, ws_bytes, ws = _workspace_arg_n(x, n, t, d, path, workspace)
-    code |= PLAIN_LAUNCH if plain_launch else 0
+    code |= COOPERATIVE if cooperative else 0
     x_out = torch.empty_like(x) if x_out is None else x_out
     y_out = torch.empty_like(f) if y_out is None else y_out
     pre_out = _f32_out((t, n), x, pre_out)
@@ -517,12 +517,12 @@ def fused_step_n(x, f, pre_in, post_in, comb_in, w_packed, base, scale, gamma, i
 
 def mixes_n(x, w_packed, base, scale, iters=20, norm_eps=1e-6, hc_eps=1e-6, pre_out=None,
             post_out=None, comb_out=None, mix_out=None, path="auto", workspace=None,
-            check_status=False, plain_launch=False) -> dict:
+            check_status=False, cooperative=False) -> dict:
     """mhc_mixes_n on tensors: x [T,n,d]. Returns dict(pre, post, comb, mix).
-    path, workspace, check_status and plain_launch as for fused_step_n."""
+    path, workspace, check_status and cooperative as for fused_step_n."""
     t, n, d = x.shape
     code, ws_ptr, ws_bytes, ws = _workspace_arg_n(x, n, t, d, path, workspace)
-    code |= PLAIN_LAUNCH if plain_launch else 0
+    code |= COOPERATIVE if cooperative else 0
     pre_out = _f32_out((t, n), x, pre_out)
     post_out = _f32_out((t, n), x, post_out)
     comb_out = _f32_out((t, n, n), x, comb_out)

@@ -1415,10 +1415,12 @@ mhc_status split_config(int32_t dtype, int32_t d, int64_t tokens, SplitCfg* cfg,
   return MHC_OK;
 }
 
-// Launch of a feature-split kernel, whose workgroups wait for one another:
-// cooperative (the runtime runs it alone on the device, so all workgroups are
-// resident), or, with MHC_PATH_PLAIN_LAUNCH, as an ordinary kernel, where the
-// caller guarantees that nothing holds compute units for the whole call.
+// Launch of a feature-split kernel, whose workgroups wait for the others of
+// their group: as an ordinary kernel (the default: the groups are filled in
+// start order, so the kernel finishes whenever the device can eventually hold
+// one group at once), or, with MHC_PATH_COOPERATIVE, cooperatively (the
+// runtime runs it alone on the device, all workgroups resident, at the price
+// of about 11 us of device idle before and after it).
 hipError_t launch_resident(const void* fn, unsigned grid, void** params, bool plain,
                            hipStream_t stream) {
   if (plain) return hipLaunchKernel(fn, dim3(grid), dim3(fsplit::kThreads), params, 0, stream);
@@ -1486,12 +1488,12 @@ constexpr int kChunkPairs = 8;
 // is given); larger calls take the feature-split kernel. At d = 5120 the
 // two routes' call time (cache-flushed medians; the split route with its
 // cooperative-launch gaps) is about 16.5 + 0.0355 T and 45.6 + 0.0243 T
-// microseconds: equal near 2,600 tokens. Launched as an ordinary kernel
-// (MHC_PATH_PLAIN_LAUNCH) the split route loses about 20 us per call; back to
-// back it then ties the chunks at 512 to 1,024 tokens (34.8 against 34.5 us,
-// 50.7 against 48.1) and wins from 1,536 (51.7 against 63.2).
-constexpr int64_t kChunkAutoTokens = 2048;
-constexpr int64_t kChunkAutoTokensPlain = 1024;
+// microseconds: equal near 2,600 tokens. Launched as an ordinary kernel (the
+// default) the split route loses about 20 us per call; back to back the
+// chunks then win up to 768 tokens (37.3 against 39.8 us) and the split
+// kernel from 1,024 (46.0 against 48.2): equal near 900 tokens.
+constexpr int64_t kChunkAutoTokensCoop = 2048;
+constexpr int64_t kChunkAutoTokensPlain = 896;
 constexpr int64_t kChunkMaxTokens = 8192;
 
 constexpr int kChunkStepsF = 8;
@@ -1574,7 +1576,7 @@ mhc_status route_needs(int32_t dtype, int32_t d, int64_t tokens, RouteNeeds* rn)
 // The route of a call with `path` and a workspace (or none), or an error for
 // a path that cannot run these arguments.
 mhc_status pick_route(int32_t path, const void* workspace, int64_t tokens, int64_t split_bytes,
-                      int64_t chunk_bytes, Route* r, int64_t chunk_auto = kChunkAutoTokens) {
+                      int64_t chunk_bytes, Route* r, int64_t chunk_auto = kChunkAutoTokensCoop) {
   switch (path) {
     case MHC_PATH_TILE:
       *r = Route::kTile;
@@ -1600,16 +1602,18 @@ mhc_status pick_route(int32_t path, const void* workspace, int64_t tokens, int64
   }
 }
 
-// The kernel family of `path` (the MHC_PATH_PLAIN_LAUNCH flag taken out) and
-// whether the flag was given.
+// The kernel family of `path` (the launch flags taken out) and whether the
+// feature-split kernel is launched as an ordinary kernel (no
+// MHC_PATH_COOPERATIVE). Both launch flags at once: -1, an unknown path.
 int32_t path_family(int32_t path, bool* plain) {
-  *plain = (path & MHC_PATH_PLAIN_LAUNCH) != 0;
-  return path & ~MHC_PATH_PLAIN_LAUNCH;
+  *plain = (path & MHC_PATH_COOPERATIVE) == 0;
+  if ((path & MHC_PATH_COOPERATIVE) != 0 && (path & MHC_PATH_PLAIN_LAUNCH) != 0) return -1;
+  return path & ~(MHC_PATH_PLAIN_LAUNCH | MHC_PATH_COOPERATIVE);
 }
 
 // pick_route, querying the device only when a workspace route is possible.
-// `path` may carry MHC_PATH_PLAIN_LAUNCH, which lowers auto's switch to the
-// feature-split kernel (*plain reports it).
+// `path` may carry MHC_PATH_COOPERATIVE, which raises auto's switch to the
+// feature-split kernel (*plain reports the launch).
 mhc_status choose_route(int32_t path, const void* workspace, int32_t dtype, int32_t d,
                         int64_t tokens, RouteNeeds* rn, Route* r, bool* plain) {
   path = path_family(path, plain);
@@ -1624,7 +1628,7 @@ mhc_status choose_route(int32_t path, const void* workspace, int32_t dtype, int3
   }
   const bool lower = *plain && rn->split_bytes > 0;   // only where the split kernel runs
   return pick_route(path, workspace, tokens, rn->split_bytes, rn->chunk_bytes, r,
-                    lower ? kChunkAutoTokensPlain : kChunkAutoTokens);
+                    lower ? kChunkAutoTokensPlain : kChunkAutoTokensCoop);
 }
 
 mhc_status launch_step(const StepArgs& a, int32_t dtype, int mode, hipStream_t stream,

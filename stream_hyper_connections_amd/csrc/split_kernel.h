@@ -13,7 +13,8 @@
 // moves at most ~3 TB/s even as a plain copy, against 4.3-4.8 TB/s for 4-8 rows
 // x 128-256 bytes. Here every CU owns one slice of the features for good:
 //
-//   * Workgroup (group g, slice c): g = blockIdx % G, c = blockIdx / G, with G
+//   * Workgroup (group g, slice c): g = ticket / ns, c = ticket % ns, where the
+//     ticket is the workgroup's place in start order (take_ticket), with G
 //     groups of ns workgroups (the host picks ns; d = 5120 runs 20 slices of
 //     256 features). Slice c is features [c*S, (c+1)*S) of every stream row,
 //     F row, new-stream row and y row; its W slice (S/32 packed steps: 96 KB
@@ -70,8 +71,10 @@
 //     grid size resets the counters, the abort word and the done word. The
 //     next call therefore finds the header as the caller first provided it
 //     (zero-filled), without a clearing launch.
-// All workgroups must be resident together: the host launches the kernel
-// cooperatively with one workgroup per CU.
+// Residency: groups are filled in start order (take_ticket), so the kernel
+// completes whenever the device can eventually hold ns of its workgroups at
+// once. The host launches one workgroup per CU (at most), as an ordinary
+// kernel or, on request, cooperatively.
 
 namespace fsplit {
 
@@ -104,6 +107,7 @@ constexpr int kCtrStride = 128;                // bytes between counters
 constexpr int64_t kHdr = 256;                  // status, abort and done words + padding
 constexpr int64_t kAbortOff = 4;               // byte offset of the call's abort word
 constexpr int64_t kDoneOff = 8;                // byte offset of the done count
+constexpr int64_t kTicketOff = 12;             // byte offset of the start-order count
 // Bytes reserved at the start of every workspace of the step's kernels: the
 // counters of the largest group count (16 groups x kRing slots) fit, and the
 // chunked kernels' partial rows start here, so they never overwrite them.
@@ -166,6 +170,7 @@ struct __align__(16) Smem {
   float base[kMix];
   float scale[4];
   uint32_t lcount[kRing];
+  uint32_t ticket;
 };
 
 struct Args {
@@ -300,10 +305,27 @@ __device__ __forceinline__ bool wait_count(char* ws, int64_t off, uint32_t targe
   }
 }
 
-// End of a cooperative split kernel: called by every thread of every
-// workgroup after its last exchange access. The workgroup that completes the
-// done count resets the `nctr` counters at `ctr0` (kCtrStride apart), the
-// abort word and the done word, leaving the header zero for the next call.
+// The workgroup's place in the order in which the workgroups started (thread
+// 0 takes it with one agent-scope atomic; `slot` is LDS). Groups are filled in
+// that order: group = ticket / ns, slice = ticket % ns. A workgroup waits only
+// for workgroups of its own group, so at any time the only workgroups that
+// can be waiting are those of the one group still being filled; all others
+// belong to complete groups, which run to the end and free their compute
+// units. The kernel therefore finishes whenever the device can eventually
+// hold ns of its workgroups at once, launched cooperatively or not.
+__device__ __forceinline__ int take_ticket(char* ws, uint32_t* slot) {
+  if (threadIdx.x == 0)
+    *slot = __hip_atomic_fetch_add(reinterpret_cast<uint32_t*>(ws + kTicketOff), 1u,
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  return (int)__builtin_amdgcn_readfirstlane(*slot);
+}
+
+// End of a split kernel: called by every thread of every workgroup after its
+// last exchange access. The workgroup that completes the done count resets
+// the `nctr` counters at `ctr0` (kCtrStride apart), the abort word, the
+// start-order count and the done word, leaving the header zero for the next
+// call (every workgroup took its ticket before it counted itself done).
 __device__ __forceinline__ void release_workspace(char* ws, int64_t ctr0, int nctr) {
   __syncthreads();
   if (threadIdx.x >= 64) return;
@@ -318,6 +340,8 @@ __device__ __forceinline__ void release_workspace(char* ws, int64_t ctr0, int nc
                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (threadIdx.x == 0) {
     __hip_atomic_store(reinterpret_cast<uint32_t*>(ws + kAbortOff), 0u, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(reinterpret_cast<uint32_t*>(ws + kTicketOff), 0u, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(reinterpret_cast<uint32_t*>(ws + kDoneOff), 0u, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
@@ -346,8 +370,9 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = fs.groups;
-  const int g = blockIdx.x % G;
-  const int c = blockIdx.x / G;
+  const int ticket = take_ticket(fs.ws, &sm.ticket);
+  const int g = ticket / fs.ns;
+  const int c = ticket % fs.ns;
   const int d = a.d;
   const uint32_t d2 = (uint32_t)d * 2;
   const uint32_t rowx = kStreams * d2, rowf = d2;

@@ -5,7 +5,7 @@
 //
 // Included by mhc.hip after split_kernel.h and general_n.h; the design is
 // that of the n = 4 feature-split kernel (fsplit), written for any n:
-//   * Workgroup (group g, slice c) keeps slice c of the features of every
+//   * Workgroup (group g, slice c) = (ticket / ns, ticket % ns) keeps slice c of the features of every
 //     stream row and its part of the packed projection (S / 32 steps of n
 //     streams x 3 T1 tiles, T1 = ceil((2+n)n / 16); term-major hi | mid | lo)
 //     in LDS for the whole call, and takes 128-token batches b = g, g + G, ...
@@ -22,9 +22,10 @@
 //     its mixes row.
 //     gen::sinkhorn_kernel then runs the split and Sinkhorn on every token.
 // The cross-workgroup protocol, the bounded waits, the status and abort
-// words and the end-of-call reset of the header are those of fsplit (see
-// split_kernel.h). All workgroups must be resident
-// together: the host launches the kernel cooperatively, one workgroup per CU.
+// words, the start-order tickets that assign the groups and the end-of-call
+// reset of the header are those of fsplit (see split_kernel.h); the host
+// launches one workgroup per CU, as an ordinary kernel or, on request,
+// cooperatively.
 
 namespace fsn {
 
@@ -110,6 +111,7 @@ struct __align__(16) Smem {
   WaveSmem<N> wv[kWaves];
   float gamma[64 * NR];
   uint32_t lcount[kRing];
+  uint32_t ticket;
 };
 
 struct Args {
@@ -232,8 +234,9 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = fs.groups;
-  const int g = blockIdx.x % G;
-  const int c = blockIdx.x / G;
+  const int ticket = fsplit::take_ticket(fs.ws, &sm.ticket);
+  const int g = ticket / fs.ns;
+  const int c = ticket % fs.ns;
   const int d = a.d;
   const uint32_t d2 = (uint32_t)d * 2;
   const uint32_t rowx = N * d2, rowf = d2;

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_granule_and_status_strings():
-    assert binding.abi_version() == 10
+    assert binding.abi_version() == 11
     assert binding.d_granule() == 32
     lib = binding.load()
     assert lib.mhc_status_string(0) == b"MHC_OK"
@@ -124,7 +124,9 @@ def test_fused_step_rejects_bad_arguments(over, needle):
 
 
 def test_fused_step_rejects_unknown_path():
-    for path in (-1, 4, 9, 4 | binding.PLAIN_LAUNCH, 32):
+    both = binding.PLAIN_LAUNCH | binding.COOPERATIVE   # the two launch flags at once
+    for path in (-1, 4, 9, 4 | binding.PLAIN_LAUNCH, 4 | binding.COOPERATIVE, 64, both,
+                 2 | both):
         assert _call(path=path) == binding.MHC_ERR_INVALID_ARG
         assert "unknown path" in binding.last_error()
 
@@ -136,10 +138,11 @@ def test_route_query_without_a_device_query():
     for path in ("auto", "tile"):
         assert lib.mhc_fused_step_route(binding.PATHS[path], 64, 5120, binding.MHC_BF16, 0) == 1
     assert lib.mhc_fused_step_route(binding.PATHS["tile"], 64, 5120, binding.MHC_BF16, 1) == 1
-    # the plain-launch flag changes no route
+    # neither launch flag changes these routes
     for path in ("auto", "tile"):
-        code = binding.PATHS[path] | binding.PLAIN_LAUNCH
-        assert lib.mhc_fused_step_route(code, 64, 5120, binding.MHC_BF16, 0) == 1
+        for flag in (binding.PLAIN_LAUNCH, binding.COOPERATIVE):
+            code = binding.PATHS[path] | flag
+            assert lib.mhc_fused_step_route(code, 64, 5120, binding.MHC_BF16, 0) == 1
     assert lib.mhc_fused_step_route(7, 64, 5120, binding.MHC_BF16, 0) == -1
     assert "unknown path" in binding.last_error()
     assert lib.mhc_fused_step_route(0, -1, 5120, binding.MHC_BF16, 0) == -1
@@ -168,6 +171,8 @@ def test_route_query_n_family_without_a_device_query():
     assert route(8, 3, 8192, 5120, bf, 1) == 3
     assert route(8, 3 | binding.PLAIN_LAUNCH, 8192, 5120, bf, 1) == 3
     assert route(8, binding.PLAIN_LAUNCH, 8193, 5120, bf, 1) == 1
+    assert route(8, 3 | binding.COOPERATIVE, 8192, 5120, bf, 1) == 3
+    assert route(8, binding.COOPERATIVE, 8193, 5120, bf, 1) == 1
     assert route(8, 3, 8193, 5120, bf, 1) == -1
     assert "chunked kernel does not apply" in binding.last_error()
     assert route(8, 2, 256, 5120, bf, 1) == -1

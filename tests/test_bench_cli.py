@@ -24,5 +24,5 @@ def test_help_lists_the_modes():
     assert res.returncode == 0
     for flag in ("--gpus", "--steps", "--warmup", "--workload", "--path", "--form",
                  "--sinkhorn-sweep", "--n-sweep", "--backward", "--all-configs", "--crossover",
-                 "--plain-launch"):
+                 "--cooperative"):
         assert flag in res.stdout, flag

@@ -106,19 +106,19 @@ def test_chunk_f32_matches_tile_kernel():
 
 def test_auto_route_by_size():
     assert mhc.fused_step_route("auto", 256, 5120, "bf16") == "chunk"
-    assert mhc.fused_step_route("auto", 2048, 5120, "bf16") == "chunk"
-    assert mhc.fused_step_route("auto", 2049, 5120, "bf16") == "split"
+    assert mhc.fused_step_route("auto", 896, 5120, "bf16") == "chunk"
+    assert mhc.fused_step_route("auto", 897, 5120, "bf16") == "split"
     assert mhc.fused_step_route("auto", 65536, 5120, "bf16") == "split"
     assert mhc.fused_step_route("auto", 256, 5120, "bf16", with_workspace=False) == "tile"
     assert mhc.fused_step_route("auto", 256, 5120, "f32") == "chunk"
     assert mhc.fused_step_route("auto", 2049, 5120, "f32") == "tile"
     assert mhc.fused_step_route("auto", 64, 96, "f32") == "chunk"
-    # with the plain launch the feature-split route costs less per call, and
-    # auto switches to it above 1,024 tokens
-    assert mhc.fused_step_route("auto", 1024, 5120, "bf16", plain_launch=True) == "chunk"
-    assert mhc.fused_step_route("auto", 1025, 5120, "bf16", plain_launch=True) == "split"
-    assert mhc.fused_step_route("auto", 1025, 5120, "f32", plain_launch=True) == "chunk"
-    assert mhc.fused_step_route("split", 256, 5120, "bf16", plain_launch=True) == "split"
+    # launched cooperatively the feature-split route costs more per call, and
+    # auto switches to it above 2,048 tokens
+    assert mhc.fused_step_route("auto", 2048, 5120, "bf16", cooperative=True) == "chunk"
+    assert mhc.fused_step_route("auto", 2049, 5120, "bf16", cooperative=True) == "split"
+    assert mhc.fused_step_route("auto", 2049, 5120, "f32", cooperative=True) == "tile"
+    assert mhc.fused_step_route("split", 256, 5120, "bf16", cooperative=True) == "split"
     # bf16 widths without a slice geometry take the tile kernel above 2,048 tokens
     assert mhc.fused_step_route("auto", 4096, 1024, "bf16") == "tile"
     # d = 6144 has a slice geometry but is beyond the chunked kernels' 5120

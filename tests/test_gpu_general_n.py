@@ -109,14 +109,14 @@ def test_general_n_split_parity(n, d, t):
 
 
 @pytest.mark.parametrize("n,d,t", [(2, 5120, 3000), (4, 2048, 700)])
-def test_general_n_split_plain_launch(n, d, t):
-    """MHC_PATH_PLAIN_LAUNCH on the n-family's feature-split kernel: the
-    cooperative launch's bits, every wait completed, the header zero again,
-    and the oracle on every token."""
+def test_general_n_split_cooperative_launch(n, d, t):
+    """MHC_PATH_COOPERATIVE on the n-family's feature-split kernel: the
+    ordinary launch's bits, every wait completed, the header zero again, and
+    the oracle on every token."""
     case = make_case(wl.Workload(840 + n + t % 7, "general_n_plain", t, d, "bf16", n=n))
     ws = mhc.new_workspace(mhc.fused_step_n_workspace_bytes(n, t, d, "bf16"))
     ref, _ = run_step_n(case, "bf16", path="split", workspace=ws)
-    out, _ = run_step_n(case, "bf16", path="split", workspace=ws, plain_launch=True)
+    out, _ = run_step_n(case, "bf16", path="split", workspace=ws, cooperative=True)
     assert mhc.split_status(ws) == 0
     assert ws[:16384].count_nonzero().item() == 0
     for k in ref:

@@ -85,9 +85,11 @@ def test_mixes_split_mode_parity(d, t):
     assert mhc.split_status(ws) == 0
     check_mixes(dict(x=x, **p), {k: v.cpu() for k, v in out.items()}, "bf16")
     tile = mhc.mixes(dx, wp, to_dev(p["base"]), to_dev(p["scale"]), want_mix=True, path="tile")
+    # the two routes agree to the parity bar: on 256-feature slices the split
+    # route's projection uses the hi and mid terms of W (each product within
+    # 2^-16 of its magnitude), the tile route all three
     for k in ("pre", "post", "comb", "mix"):
-        np.testing.assert_allclose(out[k].cpu().numpy(), tile[k].cpu().numpy(), rtol=0,
-                                   atol=2e-5)
+        check_mix_like(k, out[k].cpu(), tile[k].cpu())
 
 
 @pytest.mark.parametrize("t", [700, 5000])
