@@ -1336,23 +1336,26 @@ mhc_status coop_supported(bool* ok) {
   return MHC_OK;
 }
 
-// Estimated time of a feature-split call of `nbatch` 128-token batches, in
-// microseconds: a fixed part plus one batch time per round of `groups`
-// batches. Fitted to calls issued back to back at d = 5120 on the MI355X, up
-// to 40 batches: 40 slices of 128 features (6 groups) cost 38 + 15.4 per
-// round, 32 slices of 160 features (8 groups, all 256 CUs, the 32-feature
-// tail) 41.6 + 20.0. For example, at 4,096 tokens the two take 6 and 4
-// rounds: 130.5 against 121.6 us measured. A round's time grows with the
-// slice width, and by 4% more with the tail's 64-byte row pieces. With more
-// batches the rounds cost more as the device saturates (17.1 and 23.2 us at
-// 65,536 tokens), and the aligned geometry wins at every size measured
-// (8,192 tokens: 226 against 245 us).
+// Estimated time of a feature-split call of `tokens` tokens, in microseconds:
+// a fixed part plus a round time per round of the call's batches (whole
+// rounds plus the last round's share of 128 tokens, see fsplit::BatchSpans),
+// the round time proportional to the slice width (plus 4% for the 32-feature
+// tail's 64-byte row pieces). Fitted to calls issued back to back (ordinary
+// launch) at d = 5120 on the MI355X, 256 to 5,120 tokens: 15.9 us per round
+// per 128 features; fixed 22.4 us, 25.5 us on 256-feature slices. For
+// example, at 4,096 tokens 20 x 256 (12 groups: 2 whole rounds + 96 tokens),
+// 32 x 160 (8 groups: 4 rounds) and 40 x 128 (6 groups: 5 rounds + 48)
+// measured 108.9, 104.7 and 109.2 us, estimated 113.0, 105.1 and 107.9. At
+// more tokens the rounds cost more as the device saturates, and the 256-
+// feature slices are the fastest at every size measured from 6,144 tokens
+// (8,192: 198.2 against 206.0 and 224.4 us).
 constexpr int64_t kSplitCostBatches = 40;
 
-double split_cost_us(const SplitCfg& c, int64_t nbatch) {
+double split_cost_us(const SplitCfg& c, int64_t tokens) {
+  const fsplit::BatchSpans sp = fsplit::BatchSpans::make(tokens, c.groups);
+  const double rounds = sp.full + sp.share / (double)fsplit::kBatch;
   const bool tail = c.S % 64 != 0;
-  const double per_round = 15.4 * c.S / 128.0 * (tail ? 1.04 : 1.0);
-  return (tail ? 41.6 : 38.0) + per_round * (double)((nbatch + c.groups - 1) / c.groups);
+  return (c.S == fsplit::kMaxSW ? 25.5 : 22.4) + 15.9 * c.S / 128.0 * (tail ? 1.04 : 1.0) * rounds;
 }
 
 // Every geometry the kernel can run for (dtype, d) on this device, the
@@ -1409,7 +1412,7 @@ mhc_status split_config(int32_t dtype, int32_t d, int64_t tokens, SplitCfg* cfg,
   const int64_t nbatch = (tokens + fsplit::kBatch - 1) / fsplit::kBatch;
   for (int i = 0; i < count; ++i) {
     *bytes = std::max(*bytes, fsplit::workspace_bytes(cand[i].groups, cand[i].ns, tokens));
-    if (nbatch <= kSplitCostBatches && split_cost_us(cand[i], nbatch) < split_cost_us(*cfg, nbatch))
+    if (nbatch <= kSplitCostBatches && split_cost_us(cand[i], tokens) < split_cost_us(*cfg, tokens))
       *cfg = cand[i];
   }
   return MHC_OK;
@@ -1438,7 +1441,7 @@ mhc_status launch_split(const StepArgs& a, void* ws, const SplitCfg& cfg, int mo
                    ? a.mix_out
                    : reinterpret_cast<float*>(static_cast<char*>(ws) + fsplit::mix_off(cfg.groups, cfg.ns));
   fsplit::Args fs{static_cast<char*>(ws), mix, cfg.groups, cfg.ns,
-                  (int)((a.tokens + fsplit::kBatch - 1) / fsplit::kBatch)};
+                  fsplit::BatchSpans::make(a.tokens, cfg.groups)};
   StepArgs args = a;
   void* params[] = {&args, &fs};
   const void* fn = nullptr;
@@ -1801,7 +1804,7 @@ mhc_status launch_split_n(const StepArgs& a, void* ws, const SplitCfgN& cfg, int
                    : reinterpret_cast<float*>(static_cast<char*>(ws) +
                                               fsn::mix_off<N>(cfg.groups, cfg.ns));
   fsn::Args fs{static_cast<char*>(ws), mix, cfg.groups, cfg.ns,
-               (int)((a.tokens + fsplit::kBatch - 1) / fsplit::kBatch)};
+               fsplit::BatchSpans::make(a.tokens, cfg.groups)};
   StepArgs args = a;
   void* params[] = {&args, &fs};
   const bool full = mode == kFused;

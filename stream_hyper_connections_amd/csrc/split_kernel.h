@@ -19,8 +19,10 @@
 //     256 features). Slice c is features [c*S, (c+1)*S) of every stream row,
 //     F row, new-stream row and y row; its W slice (S/32 packed steps: 96 KB
 //     for S = 256 with two terms, 80 KB for S = 128 with three) is loaded
-//     into LDS once and used for every token the group processes. Groups take 128-token batches b = g, g+G, ...; wave w of a
-//     workgroup owns tokens 16w .. 16w+15 of each batch.
+//     into LDS once and used for every token the group processes. Groups
+//     take 128-token batches b = g, g+G, ... while every group has one; the
+//     tokens after the last such round are shared out evenly (BatchSpans).
+//     Wave w of a workgroup owns tokens 16w .. 16w+15 of each batch.
 //   * Loads and stores move 8 token rows x 128 bytes per instruction ("half
 //     rounds" of 64 features); an S % 64 = 32 remainder ("tail", 16 rows x 64
 //     bytes) sits at the 128-byte-aligned end of the slice (first for odd c).
@@ -173,12 +175,64 @@ struct __align__(16) Smem {
   uint32_t ticket;
 };
 
+// A wave-uniform 64-bit value moved to scalar registers.
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  return (int64_t)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32)) << 32) |
+                   (uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)v));
+}
+
+// Token spans of a group's batches. While every group has a whole 128-token
+// batch left, group g takes batches b = g + i*G (tokens [128b, 128b + 128));
+// the tokens after the last such round (`full` rounds) are split over the
+// groups in equal shares of `share` tokens, rounded up to a multiple of 16
+// (one wave's rows). So the last round, and the only round of a call of fewer
+// than G batches, keeps every group busy on a shorter batch instead of
+// leaving groups idle.
+struct BatchSpans {
+  int64_t rest0;  // first token after the full rounds
+  int full;       // rounds of whole 128-token batches
+  int rest;       // tokens after them (< G * 128)
+  int share;      // tokens per group in the last round (0: none)
+
+  __host__ __device__ static BatchSpans make(int64_t tokens, int groups) {
+    const int64_t full = tokens / ((int64_t)groups * kBatch);
+    const int64_t rest0 = full * groups * kBatch;
+    const int rest = (int)(tokens - rest0);
+    return BatchSpans{rest0, (int)full, rest, ((rest + groups - 1) / groups + kTok - 1) / kTok * kTok};
+  }
+  // the fields as wave-uniform values (the kernel reads them from its
+  // argument struct through lambdas; without this the compiler cannot prove
+  // the buffer resources built from them uniform and loops over lanes)
+  __device__ BatchSpans uniform() const {
+    BatchSpans u;
+    u.rest0 = (int64_t)__builtin_amdgcn_readfirstlane((uint32_t)rest0) |
+              ((int64_t)__builtin_amdgcn_readfirstlane((uint32_t)(rest0 >> 32)) << 32);
+    u.full = __builtin_amdgcn_readfirstlane(full);
+    u.rest = __builtin_amdgcn_readfirstlane(rest);
+    u.share = __builtin_amdgcn_readfirstlane(share);
+    return u;
+  }
+  // batches of group g (32-bit comparisons: every quantity stays scalar)
+  __device__ int count(int g) const { return full + (g * share < rest ? 1 : 0); }
+  // first token and length of batch i of group g of G (length 0 past the last)
+  __device__ void span(int g, int i, int G, int64_t& t0, int& len) const {
+    if (i < full) {
+      t0 = (int64_t)(g + i * G) * kBatch;
+      len = kBatch;
+    } else {
+      const int off = i == full ? g * share : rest;
+      t0 = rest0 + off;
+      len = max(0, min(share, rest - off));
+    }
+  }
+};
+
 struct Args {
   char* ws;      // workspace (mhc_fused_step_workspace_bytes)
   float* mix;    // [T][24] mixes (mix_out, or a workspace region)
   int groups;    // G
   int ns;        // slices per group (d = ns * S)
-  int nbatch;    // ceil(tokens / 128)
+  BatchSpans spans;
 };
 
 struct Items {   // one load group: 4 stream rows + the F row, 16 B per lane each
@@ -188,7 +242,6 @@ struct Items {   // one load group: 4 stream rows + the F row, 16 B per lane eac
 
 struct Rs {      // buffer resources of one wave's 16 tokens of one batch
   rsrc_t x, f, xo, y, cb, po, pr;
-  int64_t t0;
 };
 
 struct Cf {      // raw coefficient loads of one batch (see store_coef)
@@ -305,6 +358,26 @@ __device__ __forceinline__ bool wait_count(char* ws, int64_t off, uint32_t targe
   }
 }
 
+// Copy kItems 16-byte items into LDS, item i from src[map(i)], with all of a
+// thread's loads issued before its first LDS write. (A plain strided loop
+// waits for each load before the next: 10 to 12 dependent global loads per
+// thread at kernel start.)
+template <int kItems, typename Map>
+__device__ __forceinline__ void stage_lds(u32x4* dst, const u32x4* src, Map map) {
+  constexpr int kPer = (kItems + kThreads - 1) / kThreads;
+  u32x4 v[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int i = (int)threadIdx.x + j * kThreads;
+    if (i < kItems) v[j] = src[map(i)];
+  }
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int i = (int)threadIdx.x + j * kThreads;
+    if (i < kItems) dst[i] = v[j];
+  }
+}
+
 // The workgroup's place in the order in which the workgroups started (thread
 // 0 takes it with one agent-scope atomic; `slot` is LDS). Groups are filled in
 // that order: group = ticket / ns, slice = ticket % ns. A workgroup waits only
@@ -373,6 +446,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
   const int ticket = take_ticket(fs.ws, &sm.ticket);
   const int g = ticket / fs.ns;
   const int c = ticket % fs.ns;
+  const BatchSpans spans = fs.spans.uniform();
   const int d = a.d;
   const uint32_t d2 = (uint32_t)d * 2;
   const uint32_t rowx = kStreams * d2, rowf = d2;
@@ -389,13 +463,13 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
     const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.wpk) +
                                                       (size_t)c * KS * kStepBytes);
     if constexpr (TERMS == 3) {
-      for (int i = tid; i < KS * kStepBytes / 16; i += kThreads) sm.w[i] = src[i];
+      stage_lds<KS * kStepBytes / 16>(sm.w, src, [](int i) { return i; });
     } else {
       // tiles 0 .. kT-1 of every (step, stream): the hi and mid columns
-      for (int i = tid; i < KS * kStreams * kT * 64; i += kThreads) {
+      stage_lds<KS * kStreams * kT * 64>(sm.w, src, [](int i) {
         const int sk = i / (kT * 64), q = (i / 64) % kT;
-        sm.w[i] = src[(sk * kTiles + q) * 64 + (i & 63)];
-      }
+        return (sk * kTiles + q) * 64 + (i & 63);
+      });
     }
     if constexpr (kFull)
       for (int i = tid; i < S; i += kThreads) sm.gamma[i] = a.gamma[f0 + i];
@@ -419,19 +493,23 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
   const uint32_t vft = (uint32_t)t16 * rowf + (uint32_t)(f0 + ftl) * 2 + 16u * g16;
 
   auto batch_rs = [&](int i) {
-    const int64_t b = g + (int64_t)i * G;
-    const int64_t t0 = b * kBatch + (int64_t)wave * kTok;
-    const int ntok = (int)max<int64_t>(0, min<int64_t>(kTok, a.tokens - t0));
+    int64_t bt0;
+    int blen;
+    spans.span(g, i, G, bt0, blen);
+    // wave-uniform by construction; said so explicitly, or the compiler keeps
+    // the buffer resources in vector registers and loops over lanes
+    const int64_t t0 = uniform64(bt0 + (int64_t)wave * kTok);
+    const int ntok = __builtin_amdgcn_readfirstlane(max(0, min(kTok, blen - wave * kTok)));
+    const int64_t tw = ntok > 0 ? t0 : 0;   // no base pointer past the arrays
     Rs r;
-    r.t0 = t0;
-    r.x = make_rsrc(static_cast<const char*>(a.x) + t0 * rowx, ntok * rowx);
+    r.x = make_rsrc(static_cast<const char*>(a.x) + tw * rowx, ntok * rowx);
     if constexpr (kFull) {
-      r.f = make_rsrc(static_cast<const char*>(a.f) + t0 * rowf, ntok * rowf);
-      r.xo = make_rsrc(static_cast<char*>(a.x_out) + t0 * rowx, ntok * rowx);
-      r.y = make_rsrc(static_cast<char*>(a.y_out) + t0 * rowf, ntok * rowf);
-      r.cb = make_rsrc(a.comb_in + t0 * 16, ntok * 64);
-      r.po = make_rsrc(a.post_in + t0 * 4, ntok * 16);
-      r.pr = make_rsrc(a.pre_in + t0 * 4, ntok * 16);
+      r.f = make_rsrc(static_cast<const char*>(a.f) + tw * rowf, ntok * rowf);
+      r.xo = make_rsrc(static_cast<char*>(a.x_out) + tw * rowx, ntok * rowx);
+      r.y = make_rsrc(static_cast<char*>(a.y_out) + tw * rowf, ntok * rowf);
+      r.cb = make_rsrc(a.comb_in + tw * 16, ntok * 64);
+      r.po = make_rsrc(a.post_in + tw * 4, ntok * 16);
+      r.pr = make_rsrc(a.pre_in + tw * 4, ntok * 16);
     } else {
       r.f = r.xo = r.y = r.cb = r.po = r.pr = r.x;   // unused
     }
@@ -486,7 +564,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
   // both the row writes and the operand reads free of bank conflicts
   auto sidx = [](int tok, int chunk) { return tok * 8 + (chunk ^ ((tok >> 1) & 7)); };
 
-  const int nbg = g < fs.nbatch ? (fs.nbatch - g + G - 1) / G : 0;
+  const int nbg = spans.count(g);
 
   // ---- finish batch i: y of the wave's tokens, Sinkhorn of 4 tokens ----
   // The wave's exchange stores of batch i are complete: count them in LDS; the
@@ -528,7 +606,10 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
     // row; its partial loads (lane: 16-byte chunk l&7 of the token row, slices
     // l>>3 + 8k) follow at once so their latency hides behind the y work
     const int tb = c + ns * wave;
-    const bool sk = tb < kBatch;
+    int64_t bt0;
+    int blen;
+    spans.span(g, i, G, bt0, blen);
+    const bool sk = tb < blen;
     f32x4 sk_part[kSk];
     {
       const uint32_t base = (uint32_t)(mp_off(G) + slot_id * mp_slot_bytes(ns)) +
@@ -582,9 +663,9 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
       // lanes 0..5 write mixes 4l .. 4l+3; float 24 (lane 6) is sum x'^2
       const float ssum = __shfl(v[0], 6);
       const float rr = rsqrtf(ssum / (float)(kStreams * d) + a.norm_eps);
-      const int64_t t = (g + (int64_t)i * G) * kBatch + tb;
+      const int64_t t = bt0 + tb;
       // the mixes row; split and Sinkhorn run in tail_kernel
-      if (t < a.tokens && lane < kMix / 4) {
+      if (lane < kMix / 4) {
         st4f(&fs.mix[t * kMix + 4 * lane], f32x4{v[0] * rr, v[1] * rr, v[2] * rr, v[3] * rr});
       }
     }

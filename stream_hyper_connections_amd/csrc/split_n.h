@@ -119,7 +119,7 @@ struct Args {
   float* mix;    // [T][(2+n)n] mixes rows (mix_out, or a workspace region)
   int groups;    // G
   int ns;        // slices per group (d = ns * S)
-  int nbatch;    // ceil(tokens / 128)
+  fsplit::BatchSpans spans;
 };
 
 template <int N>
@@ -237,6 +237,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
   const int ticket = fsplit::take_ticket(fs.ws, &sm.ticket);
   const int g = ticket / fs.ns;
   const int c = ticket % fs.ns;
+  const fsplit::BatchSpans spans = fs.spans.uniform();
   const int d = a.d;
   const uint32_t d2 = (uint32_t)d * 2;
   const uint32_t rowx = N * d2, rowf = d2;
@@ -249,7 +250,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
   {
     const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.wpk) +
                                                       (size_t)c * KS * D::kStepBytes);
-    for (int i = tid; i < KS * D::kStepBytes / 16; i += kThreads) sm.w[i] = src[i];
+    fsplit::stage_lds<KS * D::kStepBytes / 16>(sm.w, src, [](int i) { return i; });
     if constexpr (kFull)
       for (int i = tid; i < S; i += kThreads) sm.gamma[i] = a.gamma[f0 + i];
     if (tid < kRing) sm.lcount[tid] = 0;
@@ -267,9 +268,13 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
   }
 
   auto batch_rs = [&](int i) {
-    const int64_t b = g + (int64_t)i * G;
-    const int64_t t0 = b * kBatch + (int64_t)wave * kTok;
-    const int ntok = (int)max<int64_t>(0, min<int64_t>(kTok, a.tokens - t0));
+    int64_t bt0;
+    int blen;
+    spans.span(g, i, G, bt0, blen);
+    // wave-uniform by construction; said so explicitly, or the compiler keeps
+    // the buffer resources in vector registers and loops over lanes
+    const int64_t t0 = fsplit::uniform64(bt0 + (int64_t)wave * kTok);
+    const int ntok = __builtin_amdgcn_readfirstlane(max(0, min(kTok, blen - wave * kTok)));
     const int64_t tb = ntok > 0 ? t0 : 0;
     Rs r;
     r.x = make_rsrc(static_cast<const char*>(a.x) + tb * rowx, ntok * rowx);
@@ -340,7 +345,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
   };
   auto sidx = [](int tok, int chunk) { return tok * 8 + (chunk ^ ((tok >> 1) & 7)); };
 
-  const int nbg = g < fs.nbatch ? (fs.nbatch - g + G - 1) / G : 0;
+  const int nbg = spans.count(g);
 
   auto count_batch = [&](int i) {
     const int slot = i % kRing;
@@ -379,7 +384,10 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
     // the mixes row of token tb = c + ns * wave of the batch: lane l reads
     // 16-byte chunk l % kCH of the row of slices l / kCH + kGroupsPerWave * j
     const int tb = c + ns * wave;
-    const bool sk = tb < kBatch;
+    int64_t bt0;
+    int blen;
+    spans.span(g, i, G, bt0, blen);
+    const bool sk = tb < blen;
     constexpr int kSk = (kMaxSlices + kGroupsPerWave - 1) / kGroupsPerWave;
     f32x4 sk_part[kSk];
     {
@@ -432,8 +440,8 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
       // is the sum of x'^2
       const float ssum = __shfl(v[kMix % 4], kMix / 4);
       const float rr = rsqrtf(ssum / (float)(N * d) + a.norm_eps);
-      const int64_t t = (g + (int64_t)i * G) * kBatch + tb;
-      if (t < a.tokens && lane < kCH && 4 * lane < kMix) {
+      const int64_t t = bt0 + tb;
+      if (lane < kCH && 4 * lane < kMix) {
         st4f(&fs.mix[t * kMix + 4 * lane], f32x4{v[0] * rr, v[1] * rr, v[2] * rr, v[3] * rr});
       }
     }
