@@ -1474,8 +1474,9 @@ mhc_status launch_split(const StepArgs& a, void* ws, const SplitCfg& cfg, int mo
     return fail(MHC_ERR_HIP, "feature-split kernel launch: %s", hipGetErrorString(e));
   s = launch_status("feature-split kernel launch");
   if (s != MHC_OK) return s;
-  hipLaunchKernelGGL(fsplit::tail_kernel, dim3((unsigned)((a.tokens + 15) / 16)), dim3(256), 0,
-                     stream, mix, a.tokens, a.base, a.scale, a.iters, a.hc_eps, a.pre_out,
+  hipLaunchKernelGGL(fsplit::tail_kernel,
+                     dim3((unsigned)((a.tokens + fsplit::kTailThreads - 1) / fsplit::kTailThreads)),
+                     dim3(fsplit::kTailThreads), 0, stream, mix, a.tokens, a.base, a.scale, a.iters, a.hc_eps, a.pre_out,
                      a.post_out, a.comb_out);
   return launch_status("split/Sinkhorn tail kernel launch");
 }
@@ -2351,8 +2352,9 @@ mhc_status mhc_sinkhorn4(const float* mixes, int64_t tokens, const float* base,
                       {"comb_out", comb_out, T * 64}};
   mhc_status s = check_spans(in, 3, out, 3, nullptr, nullptr);
   if (s != MHC_OK) return s;
-  hipLaunchKernelGGL(fsplit::tail_kernel, dim3((unsigned)((tokens + 15) / 16)), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), mixes, tokens, base, scale, sinkhorn_iters,
+  hipLaunchKernelGGL(fsplit::tail_kernel,
+                     dim3((unsigned)((tokens + fsplit::kTailThreads - 1) / fsplit::kTailThreads)),
+                     dim3(fsplit::kTailThreads), 0, static_cast<hipStream_t>(stream), mixes, tokens, base, scale, sinkhorn_iters,
                      hc_eps, pre_out, post_out, comb_out);
   return launch_status("split/Sinkhorn kernel launch");
 }

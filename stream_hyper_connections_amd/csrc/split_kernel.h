@@ -865,34 +865,74 @@ __global__ __launch_bounds__(kThreads) void split_kernel(StepArgs a, Args fs) {
   release_workspace(ws, ctr_off(0, 0), G * kRing);
 }
 
-// Split and Sinkhorn of the mixes rows [T][24] the feature-split kernel wrote:
-// 16 lanes per token, lane e holds comb entry (e/4, e%4) and, for e < 8, the
-// pre (e < 4) or post slot e ([SW] Code, the split/Sinkhorn kernel; "All 5
-// steps"): row sums over quads, column sums over lanes e, e+4, e+8, e+12.
-__global__ __launch_bounds__(256) void tail_kernel(const float* __restrict__ mix, int64_t tokens,
-                                                   const float* __restrict__ base,
-                                                   const float* __restrict__ scale, int iters,
-                                                   float eps, float* __restrict__ pre_out,
-                                                   float* __restrict__ post_out,
-                                                   float* __restrict__ comb_out) {
-  const int e = threadIdx.x & 15;
-  const int64_t t = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-  const bool ok = t < tokens;
-  const int64_t tc = ok ? t : 0;
-  const float mc = mix[tc * kMix + 8 + e];
-  const float mp = mix[tc * kMix + (e & 7)];
-  const float s0 = scale[0], s1 = scale[1], s2 = scale[2];
-  if (ok && e < 4) pre_out[t * 4 + e] = sigmoidf(mp * s0 + base[e]) + eps;
-  if (ok && e >= 4 && e < 8) post_out[t * 4 + (e - 4)] = 2.0f * sigmoidf(mp * s1 + base[e]);
-  float cv = mc * s2 + base[8 + e];
-  cv = expf(cv - quad_max(cv));
-  cv = cv / quad_sum(cv) + eps;
-  cv = cv * __builtin_amdgcn_rcpf(col_sum(cv) + eps);
-  for (int it = 1; it < iters; ++it) {
-    cv = cv * __builtin_amdgcn_rcpf(quad_sum(cv) + eps);
-    cv = cv * __builtin_amdgcn_rcpf(col_sum(cv) + eps);
+// Split and Sinkhorn of the mixes rows [T][24] the feature-split kernel wrote,
+// one thread per token with the 4x4 in registers ([SW] Code, the
+// split/Sinkhorn kernel; "All 5 steps"). The sums are associated as the
+// 16-lane form's quad and column sums (DPP, in the tile and chunked kernels)
+// are (row: (c0 + c1) + (c2 + c3); column: (r0 + r2) + (r1 + r3)), and the
+// divisions after the softmax are multiplications by the hardware
+// reciprocal, as there; a token takes half the 16-lane form's arithmetic.
+constexpr int kTailThreads = 64;
+
+__global__ __launch_bounds__(kTailThreads) void tail_kernel(const float* __restrict__ mix,
+                                                           int64_t tokens,
+                                                           const float* __restrict__ base,
+                                                           const float* __restrict__ scale,
+                                                           int iters, float eps,
+                                                           float* __restrict__ pre_out,
+                                                           float* __restrict__ post_out,
+                                                           float* __restrict__ comb_out) {
+  const int64_t t = (int64_t)blockIdx.x * kTailThreads + threadIdx.x;
+  if (t >= tokens) return;
+  float m[kMix];
+  const f32x4* row = reinterpret_cast<const f32x4*>(mix + t * kMix);
+#pragma unroll
+  for (int q = 0; q < kMix / 4; ++q) {
+    const f32x4 v = row[q];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) m[4 * q + e] = v[e];
   }
-  if (ok) comb_out[t * 16 + e] = cv;
+  const float s0 = scale[0], s1 = scale[1], s2 = scale[2];
+  f32x4 pre, post;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    pre[k] = sigmoidf(m[k] * s0 + base[k]) + eps;
+    post[k] = 2.0f * sigmoidf(m[4 + k] * s1 + base[4 + k]);
+  }
+  float c[4][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) c[j][k] = m[8 + 4 * j + k] * s2 + base[8 + 4 * j + k];
+    const float mx = fmaxf(fmaxf(c[j][0], c[j][1]), fmaxf(c[j][2], c[j][3]));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) c[j][k] = expf(c[j][k] - mx);
+    const float rs = (c[j][0] + c[j][1]) + (c[j][2] + c[j][3]);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) c[j][k] = c[j][k] / rs + eps;
+  }
+  auto columns = [&]() {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float r = __builtin_amdgcn_rcpf(((c[0][k] + c[2][k]) + (c[1][k] + c[3][k])) + eps);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) c[j][k] = c[j][k] * r;
+    }
+  };
+  columns();
+  for (int it = 1; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float r = __builtin_amdgcn_rcpf(((c[j][0] + c[j][1]) + (c[j][2] + c[j][3])) + eps);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) c[j][k] = c[j][k] * r;
+    }
+    columns();
+  }
+  st4f(pre_out + t * 4, pre);
+  st4f(post_out + t * 4, post);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) st4f(comb_out + t * 16 + 4 * j, f32x4{c[j][0], c[j][1], c[j][2], c[j][3]});
 }
 
 }  // namespace fsplit
