@@ -284,3 +284,75 @@ def test_cooperative_launch_matches_the_ordinary_launch(t):
     assert ws[:16384].count_nonzero().item() == 0
     for k in ("pre", "post", "comb", "mix"):
         assert torch.equal(m_plain[k], m_coop[k]), k
+
+
+def test_two_term_projection_error_bound():
+    """On 256-feature slices (the large-call geometry at d = 5120) the
+    projection uses the hi and mid bf16 terms of W: |w - hi - mid| <=
+    2^-16 |w|. Every mix must then lie within r * sum_f |w_jf x'_f| *
+    (2^-16 + 64 * 2^-24) of the exact value on the validated new streams (the
+    dropped term, plus float32 accumulation over at most 64 sequential
+    roundings per output: the MFMA steps of a slice, the slices, the terms).
+    Reports the largest fraction of that bound used and of the 1e-4 parity
+    bar."""
+    t, d = 6000, 5120
+    assert mhc.fused_step_route("auto", t, d, "bf16") == "split"
+    w = wl.Workload(455, "two_term", t, d, "bf16")
+    case = make_case(w)
+    out, _ = _run(case)
+    o = check_step(case, out, "bf16")
+    xp = np.asarray(o["xprime"], dtype=np.float64).reshape(t, -1)
+    wabs = np.abs(np.asarray(case["w_mix"], dtype=np.float64))
+    r = 1.0 / np.sqrt(np.mean(xp * xp, axis=1) + case["norm_eps"])
+    err = np.abs(out["mix"].numpy().astype(np.float64) - o["m"])
+    worst, worst_bar = 0.0, 0.0
+    for t0 in range(0, t, 1000):
+        sl = slice(t0, t0 + 1000)
+        mag = (np.abs(xp[sl]) @ wabs.T) * r[sl, None]
+        bound = mag * (2.0 ** -16 + 64 * 2.0 ** -24)
+        assert (err[sl] <= bound).all(), "a mix outside the two-term error bound"
+        worst = max(worst, float((err[sl] / bound).max()))
+        worst_bar = max(worst_bar, float((err[sl] / (1e-4 * np.maximum(np.abs(o["m"][sl]), 1.0))).max()))
+    _log(f"  mixes error: at most {worst:.3f} of the two-term bound, {worst_bar:.3f} of the parity bar")
+
+
+def test_split_calls_on_four_streams_in_flight_together():
+    """Four ordinary-launch feature-split calls in flight on four streams (each
+    with its own workspace): every call's groups fill in start order, so all
+    complete however the device interleaves them (status word 0), with the
+    bits of the same calls run one after the other."""
+    t, d = 6000, 5120
+    cases = [make_case(wl.Workload(480 + i, "split_streams4", t, d, "bf16")) for i in range(4)]
+    devs = [{k: to_dev(c[k]) for k in ("x", "f", "pre", "post", "comb", "w_mix", "base",
+                                       "scale", "gamma")} for c in cases]
+    wps = [mhc.pack_wmix(dv["w_mix"], "bf16") for dv in devs]
+    wss = [torch.zeros(mhc.fused_step_workspace_bytes(t, d, "bf16"), dtype=torch.uint8,
+                       device="cuda") for _ in range(4)]
+
+    def call(i):
+        dv = devs[i]
+        return mhc.fused_step(dv["x"], dv["f"], dv["pre"], dv["post"], dv["comb"], wps[i],
+                              dv["base"], dv["scale"], dv["gamma"], want_mix=True,
+                              path="split", workspace=wss[i])
+
+    ref = []
+    for i in range(4):
+        ref.append({k: v.clone() for k, v in call(i).items()})
+        torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in range(4)]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for _ in range(2):
+        for i in range(4):
+            with torch.cuda.stream(streams[i]):
+                outs.append((i, call(i)))
+    for s in streams:
+        torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for i in range(4):
+        assert mhc.split_status(wss[i]) == 0, "a cross-workgroup wait gave up"
+        assert wss[i][:16384].count_nonzero().item() == 0
+    for i, o in outs:
+        for k in ref[i]:
+            assert torch.equal(o[k], ref[i][k]), (i, k)
