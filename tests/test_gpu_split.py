@@ -36,10 +36,14 @@ def _run(case, **kw):
     return out, dev
 
 
-# slice geometry chosen on a 256-CU device: d=5120 -> 40 slices of 128
-# features, 4096 -> 32 x 128, 3072 -> 48 x 64, 2048 -> 32 x 64, 2560 -> 40 x 64,
-# 6144 -> 48 x 128, 8192 -> 64 x 128; no 128-byte aligned choice exists for
-# 3840 (40 x 96) and 6400 (40 x 160), which take the 32-feature tail
+# slice geometry on a 256-CU device: calls of more than 40 batches of 128
+# tokens take 256-feature slices on the two-term projection where d allows
+# (d = 4096: 16, 5120: 20, 6144: 24 slices), else 128-byte aligned slices
+# (8192 -> 64 x 128, 3072 -> 48 x 64, 2048 -> 32 x 64, 2560 -> 40 x 64) or,
+# with no aligned choice, the 32-feature tail (3840 -> 40 x 96, 6400 -> 40 x
+# 160); smaller calls take the geometry with the least estimated time (at
+# d = 5120 32 x 160 on all 256 CUs). The tokens after the last whole round
+# are shared out over the groups, so every size below exercises it
 SPLIT_CASES = [
     (5120, 1),       # one token: one wave of one group works
     (5120, 37),      # ragged first batch
@@ -150,20 +154,17 @@ def test_split_repeated_calls_share_a_workspace():
         check_step(case, out, "bf16")
 
 
-def test_split_leaves_the_header_zero():
-    """After a feature-split call the abort word, the done count and every
-    (group, slot) counter are back to zero (the header layout of the kernel:
-    words at bytes 4 and 8, counters from byte 256, 128 bytes apart, four per
-    group; 40 slices of 128 features at d = 5120 make 6 groups on 256 CUs)."""
-    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
-        pytest.skip("group count assumed for a 256-CU device")
-    ws = mhc.new_workspace(mhc.fused_step_workspace_bytes(1000, 5120, "bf16"))
-    case = make_case(wl.Workload(455, "split_header", 1000, 5120, "bf16"))
+@pytest.mark.parametrize("t", [1000, 6000])   # 32 slices of 160 features; 20 of 256
+def test_split_leaves_the_header_zero(t):
+    """After a feature-split call the status word, the abort word, the done
+    count, the start-order ticket count (bytes 0, 4, 8, 12) and every (group,
+    slot) counter (from byte 256) are back to zero: the whole 16 KB header."""
+    ws = mhc.new_workspace(mhc.fused_step_workspace_bytes(t, 5120, "bf16"))
+    case = make_case(wl.Workload(455, "split_header", t, 5120, "bf16"))
     out, _ = run_step(case, path="split", workspace=ws)
     words = ws[:16384].view(torch.int32).cpu().numpy()
-    assert words[0] == 0 and words[1] == 0 and words[2] == 0
-    counters = words[(256 + 128 * np.arange(6 * 4)) // 4]
-    assert (counters == 0).all(), counters
+    assert (words[:4] == 0).all(), words[:4]
+    assert (words == 0).all(), np.flatnonzero(words)[:8]
     check_step(case, out, "bf16")
 
 
