@@ -244,7 +244,10 @@ __global__ __launch_bounds__(256) void split_kernel(Args a) {
 template <int DT>
 __device__ __forceinline__ void load8(const void* base, int64_t elem, float (&v)[8]) {
   if constexpr (DT == MHC_BF16) {
-    const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + elem);
+    // non-temporal: the statistics pass reads X' and dy once (with the dW
+    // kernel's loads also non-temporal: 3.411 -> 3.317 ms per backward call)
+    const u32x4 w = __builtin_nontemporal_load(
+        reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + elem));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       v[2 * i] = bf_lo(w[i]);
@@ -1111,7 +1114,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5, 5))) voi
     for (int e = 0; e < 8; ++e) {
       const int64_t t = tb + 8 * g + e;
       const int64_t tc = t < t1 ? t : t1 - 1;
-      xw[e] = *reinterpret_cast<const uint2*>(xo + (tc * N + k) * (int64_t)d + f0 + 4 * c);
+      typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+      const u32x2_t v2 = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x2_t*>(xo + (tc * N + k) * (int64_t)d + f0 + 4 * c));
+      xw[e] = make_uint2(v2[0], v2[1]);
     }
   };
   // V of one step (32 tokens x 32 slots, the workspace block) staged in LDS

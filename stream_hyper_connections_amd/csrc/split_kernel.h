@@ -39,7 +39,7 @@
 //     rows of one token of the batch (token c + ns * wave), apply the RMS
 //     scaling and write its 24 mixes (alternating the wave halves from batch
 //     to batch was 0.6% slower); tail_kernel then runs the split and the 4x4
-//     Sinkhorn on all tokens (16 lanes per token).
+//     Sinkhorn on all tokens (one thread per token).
 //
 // Cross-workgroup protocol (correct wherever the workgroups run; the group ->
 // XCD mapping only matters for speed). In the GFX942 memory model of the LLVM
@@ -70,7 +70,8 @@
 //   * the workspace cleans up after itself: each workgroup, once all of its
 //     waves are done with the exchange, adds one to the done word (offset 8)
 //     with an acquire-release atomic; the workgroup that brings it to the
-//     grid size resets the counters, the abort word and the done word. The
+//     grid size resets the counters, the abort word, the start-order ticket
+//     count (offset 12) and the done word. The
 //     next call therefore finds the header as the caller first provided it
 //     (zero-filled), without a clearing launch.
 // Residency: groups are filled in start order (take_ticket), so the kernel
