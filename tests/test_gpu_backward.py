@@ -143,6 +143,14 @@ def test_backward_deterministic():
 
 
 @pytest.mark.timeout(900)
+def test_backward_ragged_wide():
+    """d = 5312 (83 units of 64 features, not a multiple of 256) and 4,100
+    tokens (65 workgroups of the stream kernel, the last with 4 tokens):
+    every gradient checked in full."""
+    run_backward_case(4, "bf16", 5312, 4100, 970)
+
+
+@pytest.mark.timeout(900)
 def test_backward_many_blocks():
     """8,192 tokens x d = 5120 (64 workgroups of the stream kernel, every
     token chunk of the parameter kernel): every gradient checked in full."""
