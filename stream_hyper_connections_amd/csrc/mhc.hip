@@ -18,6 +18,8 @@
 //     feed the 24-wide projection without any reshuffle. The projection
 //     weights are pre-split into three exact bf16 terms (mhc_pack_wmix) and
 //     packed in B-operand order; 72 columns (3 x 24) padded to 5 tiles of 16.
+//     (This generic kernel and the narrow feature slices take all three
+//     terms; the pipelined tile, chunked and wide-slice kernels take hi + mid.)
 //   * The rounded hc_pre result h (bf16, 8 values per lane and step) stays in
 //     registers until the token's sum of squares is complete, then the
 //     normalised y is written: streams are read once and written once.
