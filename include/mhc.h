@@ -133,10 +133,7 @@ int64_t mhc_wmix_packed_bytes(int32_t d, int32_t dtype);
  * order of the gfx950 matrix instructions the step kernels use.
  *   - MHC_BF16: every weight is split into three bfloat16 terms hi + mid + lo
  *     whose sum is the float32 weight exactly; the 72 terms per column are
- *     padded to 80 rows. The feature-split kernel on 256-feature slices, the
- *     tile kernel and the chunked kernels take hi + mid only
- *     (|w - hi - mid| <= 2^-16 |w|); the narrower feature slices take all
- *     three.
+ *     padded to 80 rows.
  *   - MHC_F32: float32 copy, rows padded to 32.
  * The packed buffer depends only on (W, d, dtype): pack once per weight and
  * reuse it for every call of mhc_fused_step / mhc_mixes with that dtype.

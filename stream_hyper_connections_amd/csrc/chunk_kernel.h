@@ -19,8 +19,7 @@
 //     pipelined tile kernel's steps on them (wave w takes the pairs w, w + 8,
 //     ... of the chunk; W read from L2), store the new streams, store h into
 //     y_out (normalised in place later), and write one partial row of 32 floats
-//     per token: the 24 projection sums of the chunk (hi + mid terms of W, as
-//     in the pipelined tile kernel),
+//     per token: the 24 projection sums of the chunk (hi + mid + lo terms),
 //     sum x'^2 and sum h^2.
 //   * chunk_finish_kernel: one workgroup per token sums the token's partial
 //     rows over the chunks (in chunk order), forms the mixes
@@ -135,7 +134,7 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(StepArgs a, int nchunks
   const uint32_t rowx = (uint32_t)(kStreams * d * 2), rowf = (uint32_t)(d * 2);
   Ctx c;
   c.d2 = d * 2;
-  c.wr = make_rsrc(a.wpk, (uint32_t)nsteps * kStreams * kPackTiles * 1024);
+  c.wr = make_rsrc(a.wpk, (uint32_t)nsteps * kStreams * kTiles * 1024);
   c.woff = (uint32_t)lane * 16;
   c.woff_last = (tr < kCols - 16 * (kTiles - 1)) ? (uint32_t)lane * 16 : kOutOfRange;
   c.xr = make_rsrc(static_cast<const char*>(a.x) + t0 * rowx, ntok * rowx);
@@ -199,13 +198,14 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(StepArgs a, int nchunks
   const int tt = tid >> 5, j = tid & 31;
   float v = 0.f;
   if (j < kMix) {
-    float hi = 0.f, mid = 0.f;
+    float hi = 0.f, mid = 0.f, lo = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
       hi += acc_s[w][tt][j];
       mid += acc_s[w][tt][kMix + j];
+      lo += acc_s[w][tt][2 * kMix + j];
     }
-    v = hi + mid;
+    v = (hi + mid) + lo;
   } else if (j == kMix || j == kMix + 1) {
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) v += j == kMix ? ss_s[w][tt] : hs_s[w][tt];

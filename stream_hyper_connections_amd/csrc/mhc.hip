@@ -18,8 +18,6 @@
 //     feed the 24-wide projection without any reshuffle. The projection
 //     weights are pre-split into three exact bf16 terms (mhc_pack_wmix) and
 //     packed in B-operand order; 72 columns (3 x 24) padded to 5 tiles of 16.
-//     (This generic kernel and the narrow feature slices take all three
-//     terms; the pipelined tile, chunked and wide-slice kernels take hi + mid.)
 //   * The rounded hc_pre result h (bf16, 8 values per lane and step) stays in
 //     registers until the token's sum of squares is complete, then the
 //     normalised y is written: streams are read once and written once.
@@ -677,23 +675,20 @@ __global__ __launch_bounds__(kThreads) void step_kernel(StepArgs a) {
 // streams are software-pipelined by hand, because the vector-memory counter
 // retires in issue order and a wait on a late-issued load would otherwise drain
 // every earlier prefetch. Per pair (steps A and B):
-//   1. projection operands of A (12 loads, L2)
+//   1. projection operands of A (20 loads, L2)
 //   2. [wait streams of A] hc_post, sums of squares, hc_pre for A; h to LDS
 //   3. stream loads of the NEXT pair's A into the freed registers
-//   4. [wait operands of A] 12 MFMAs
+//   4. [wait operands of A] 20 MFMAs
 //   5. projection operands of B
 //   6. [wait streams of B] VALU work of B
 //   7. stream loads of the next pair's B; stores of A and B interleaved, so
 //      every 128-byte line of the new streams is written by two adjacent
 //      instructions
-//   8. [wait operands of B] 12 MFMAs
-// The projection takes two of the three packed bf16 terms of W (hi + mid, the
-// first three column tiles of each (step, stream) of the packing; |w - hi -
-// mid| <= 2^-16 |w|), as the feature-split kernel does on its 256-feature
-// slices: the operand loads from L2, 40% of the bytes a wave reads per step
-// with all three terms, shrink by that much, and so do the MFMAs.
+//   8. [wait operands of B] 20 MFMAs
 // Stream tensors use buffer instructions whose range check drops the lanes of
-// tokens past the end of the tensor (no branches). h is kept in LDS (one 1 KB slot per step; the steps beyond the
+// tokens past the end of the tensor (no branches), and the padding half of the
+// last operand tile is read from outside the range, which returns zeros without
+// memory traffic. h is kept in LDS (one 1 KB slot per step; the steps beyond the
 // LDS capacity stay in registers) until the token's sum of squares is known.
 
 namespace pipe {
@@ -702,9 +697,8 @@ constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kMaxSteps = 160;              // d <= 5120
 constexpr int kSlots = kMaxSteps - kWaves;  // LDS slots for h
-constexpr int kCols = 2 * kMix;             // packed columns used (hi/mid x 24)
-constexpr int kPackTiles = kTilesBf;        // column tiles per (step, stream) in the packing
-constexpr int kTiles = (kCols + 15) / 16;   // the tiles used: hi and mid
+constexpr int kCols = 3 * kMix;             // real packed columns (hi/mid/lo x 24)
+constexpr int kTiles = kTilesBf;
 constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw buffer, 32-bit data format (gfx9)
 constexpr int kNT = 2;                         // cache-policy bit: non-temporal
 constexpr uint32_t kOutOfRange = 0x80000000u;
@@ -787,13 +781,13 @@ __device__ __forceinline__ void load_half(Half& hf, const Ctx& c, int s) {
 }
 
 __device__ __forceinline__ void load_w(u32x4 (&w)[4][kTiles], const Ctx& c, int s) {
-  const uint32_t base = (uint32_t)s * (kStreams * kPackTiles * 1024);
+  const uint32_t base = (uint32_t)s * (kStreams * kTiles * 1024);
 #pragma unroll
   for (int k = 0; k < 4; ++k)
 #pragma unroll
     for (int q = 0; q < kTiles; ++q)
       w[k][q] = bload<0>(c.wr, q == kTiles - 1 ? c.woff_last : c.woff,
-                         base + (uint32_t)(k * kPackTiles + q) * 1024);
+                         base + (uint32_t)(k * kTiles + q) * 1024);
 }
 
 // hc_post, the sums of squares and hc_pre of one step (the arithmetic per
@@ -937,7 +931,7 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_kernel(StepArgs a, int nt
 
   Ctx c;
   c.d2 = d * 2;
-  c.wr = make_rsrc(a.wpk, (uint32_t)nsteps * kStreams * kPackTiles * 1024);
+  c.wr = make_rsrc(a.wpk, (uint32_t)nsteps * kStreams * kTiles * 1024);
   c.woff = (uint32_t)lane * 16;
   c.woff_last = (tr < kCols - 16 * (kTiles - 1)) ? (uint32_t)lane * 16 : kOutOfRange;
 
@@ -1052,13 +1046,14 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_kernel(StepArgs a, int nt
       for (int w = 0; w < kWaves; ++w) ssum += sm.ss[w][tt];
       const float r = rsqrtf(ssum / (float)(kStreams * d) + a.norm_eps);
       auto mix_at = [&](int j) {
-        float hi = 0.f, mid = 0.f;
+        float hi = 0.f, mid = 0.f, lo = 0.f;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
           hi += sm.u.acc[w][tt][j];
           mid += sm.u.acc[w][tt][kMix + j];
+          lo += sm.u.acc[w][tt][2 * kMix + j];
         }
-        return (hi + mid) * r;
+        return ((hi + mid) + lo) * r;
       };
       const float mc = mix_at(8 + e);                 // comb logit slot of (j, k) = (e/4, e%4)
       const float mp = mix_at(e < 8 ? e : 0);         // pre / post slot for e < 8

@@ -6,9 +6,9 @@
 // Included by mhc.hip (one translation unit); uses its helpers and the pipe::
 // buffer-instruction wrappers.
 //
-// Why a second kernel. The tile kernel re-reads the packed projection (hi and
-// mid of W, 12 KB per 32 features) from L2 for every 16-token tile: more than
-// the stream bytes through each CU's vector-memory path. Its lane layout
+// Why a second kernel. The tile kernel re-reads the packed projection (three
+// bf16 terms of W, 20 KB per 32 features) from L2 for every 16-token tile:
+// twice the stream bytes through each CU's vector-memory path. Its lane layout
 // (16 token rows x 64 bytes per load instruction, the MFMA operand order) also
 // moves at most ~3 TB/s even as a plain copy, against 4.3-4.8 TB/s for 4-8 rows
 // x 128-256 bytes. Here every CU owns one slice of the features for good:

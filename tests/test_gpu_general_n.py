@@ -315,10 +315,9 @@ def test_general_n4_matches_tuned_kernels(npath):
         assert torch.equal(a["x_out"], b["x_out"]), path
         ya, yb = a["y"].float(), b["y"].float()
         assert ((ya - yb).abs() <= torch.maximum(ya.abs(), yb.abs()) * 2.0 ** -7 + 1e-30).all()
-        # the mixes: summed in another order, and the tuned kernels may take
-        # the two-term projection (hi + mid of W): compared at the parity bar
+        # the mixes are summed in another order (|m| up to ~10 here)
         for k in ("pre", "post", "comb", "mix"):
-            check_mix_like(k, a[k], b[k])
+            np.testing.assert_allclose(a[k].numpy(), b[k].numpy(), rtol=1e-5, atol=2e-5)
 
 
 @pytest.mark.parametrize("n,dtype,d,t", [(2, "bf16", 5120, 1000), (8, "bf16", 2048, 300),
