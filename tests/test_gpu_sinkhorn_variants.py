@@ -132,5 +132,12 @@ def test_fused_step_one_round_on_wide_slices():
     slices and the other kernels take all three terms and pass at one round
     (test_fused_step_other_iteration_counts)."""
     case, out = _wide_step(1)
-    check_step(case, out, "bf16")
+    try:
+        check_step(case, out, "bf16")
+    except ParityError as e:
+        # only this deviation is expected: any other fails the test (a plain
+        # AssertionError is not the ParityError the mark accepts)
+        if not str(e).startswith("comb row sums"):
+            raise AssertionError(f"unexpected deviation: {e}") from e
+        raise
 
