@@ -155,7 +155,11 @@ mhc_status mhc_pack_wmix(const float* w_mix, int32_t d, int32_t dtype, void* w_p
  *     256 from 4096 to 6144; e.g. 5120 = 20 x 256, the geometry of large
  *     calls there), on a device with at least ns compute units and
  *     cooperative launch support. About 17 MB for d = 5120 on 256 CUs, plus
- *     96 bytes per token for the mixes rows.
+ *     96 bytes per token for the mixes rows. The 256-feature slices take
+ *     the hi + mid terms of the packed projection (|w - hi - mid| <=
+ *     2^-16 |w|), the others all three; a call with sinkhorn_iters == 1
+ *     takes a three-term geometry where d has one (after a single round the
+ *     comb's row sums are not normalised and would carry the two-term error).
  *   - Chunked kernels: at most 8192 tokens; MHC_BF16 streams with d a
  *     multiple of 64 up to 5120, or MHC_F32 streams. The 16,384-byte header
  *     plus 128 bytes per token and chunk, a chunk being 512 features (bf16)

@@ -1359,24 +1359,24 @@ double split_cost_us(const SplitCfg& c, int64_t tokens) {
 }
 
 // Every geometry the kernel can run for (dtype, d) on this device, the
-// preferred one for large calls first; none without cooperative launch
-// support.
+// preferred one for large calls first: the 256-feature slices where d allows,
+// then the best-scored narrow geometry, then the other narrow ones; none
+// without cooperative launch support.
 mhc_status split_candidates(int32_t dtype, int32_t d, SplitCfg (&out)[5], int* count) {
   *count = 0;
   if (dtype != MHC_BF16) return MHC_OK;
   int cus = 0;
   mhc_status s = device_cu_count(&cus);
   if (s != MHC_OK) return s;
-  int best_score = -1;
   // 256-feature slices on the two-term projection: 512-byte row segments per
   // workgroup, half the exchange rows of 128-feature slices
   if (d % fsplit::kMaxSW == 0) {
     const int ns = d / fsplit::kMaxSW;
-    if (ns >= 16 && ns <= fsplit::kMaxSlicesW && ns <= cus) {
+    if (ns >= 16 && ns <= fsplit::kMaxSlicesW && ns <= cus)
       out[(*count)++] = SplitCfg{cus / ns, ns, fsplit::kMaxSW};
-      best_score = 1 << 30;
-    }
   }
+  const int first_narrow = *count;
+  int best_score = -1;
   for (int ns : {32, 40, 48, 64}) {
     if (d % ns != 0 || ns > cus) continue;
     const int S = d / ns;
@@ -1386,7 +1386,7 @@ mhc_status split_candidates(int32_t dtype, int32_t d, SplitCfg (&out)[5], int* c
     out[*count] = SplitCfg{cus / ns, ns, S};
     if (score > best_score) {
       best_score = score;
-      std::swap(out[0], out[*count]);
+      std::swap(out[first_narrow], out[*count]);
     }
     ++*count;
   }
@@ -1400,19 +1400,28 @@ mhc_status split_candidates(int32_t dtype, int32_t d, SplitCfg (&out)[5], int* c
 // The geometry of a call of `tokens` tokens, and the workspace bytes that
 // cover every candidate geometry at that size (so a workspace sized for T
 // tokens serves every call of at most T tokens, whichever geometry it takes).
+// one_round: the call runs a single Sinkhorn round. After one round nothing
+// divides the comb's row sums back to 1, so the error of the two-term
+// projection (|w - hi - mid| <= 2^-16 |w|, within the mixes' tolerance)
+// reaches them undivided and put some of them just past the 1e-5 comb-sum
+// tolerance (up to 1.1e-5 at 6,000 tokens); such calls take a geometry on the
+// exact three-term projection where d has one. From two rounds on the row
+// normalisations absorb it.
 mhc_status split_config(int32_t dtype, int32_t d, int64_t tokens, SplitCfg* cfg,
-                        int64_t* bytes) {
+                        int64_t* bytes, bool one_round = false) {
   *cfg = SplitCfg{};
   *bytes = 0;
   SplitCfg cand[5];
   int count = 0;
   const mhc_status s = split_candidates(dtype, d, cand, &count);
   if (s != MHC_OK || count == 0) return s;
-  *cfg = cand[0];
+  const int first = one_round && count > 1 && cand[0].S == fsplit::kMaxSW ? 1 : 0;
+  *cfg = cand[first];
   const int64_t nbatch = (tokens + fsplit::kBatch - 1) / fsplit::kBatch;
   for (int i = 0; i < count; ++i) {
     *bytes = std::max(*bytes, fsplit::workspace_bytes(cand[i].groups, cand[i].ns, tokens));
-    if (nbatch <= kSplitCostBatches && split_cost_us(cand[i], tokens) < split_cost_us(*cfg, tokens))
+    if (i >= first && nbatch <= kSplitCostBatches &&
+        split_cost_us(cand[i], tokens) < split_cost_us(*cfg, tokens))
       *cfg = cand[i];
   }
   return MHC_OK;
@@ -1568,9 +1577,10 @@ struct RouteNeeds {
   int64_t chunk_bytes = 0;
 };
 
-mhc_status route_needs(int32_t dtype, int32_t d, int64_t tokens, RouteNeeds* rn) {
+mhc_status route_needs(int32_t dtype, int32_t d, int64_t tokens, RouteNeeds* rn,
+                       bool one_round = false) {
   *rn = RouteNeeds{};
-  mhc_status s = split_config(dtype, d, tokens, &rn->split, &rn->split_bytes);
+  mhc_status s = split_config(dtype, d, tokens, &rn->split, &rn->split_bytes, one_round);
   if (s != MHC_OK) return s;
   rn->chunk = chunk_config(dtype, d, tokens);
   if (rn->chunk.nchunks > 0) rn->chunk_bytes = pipe::chunk_workspace_bytes(rn->chunk.nchunks, tokens);
@@ -1617,9 +1627,11 @@ int32_t path_family(int32_t path, bool* plain) {
 
 // pick_route, querying the device only when a workspace route is possible.
 // `path` may carry MHC_PATH_COOPERATIVE, which raises auto's switch to the
-// feature-split kernel (*plain reports the launch).
+// feature-split kernel (*plain reports the launch). iters: the call's Sinkhorn
+// rounds (a single round picks a three-term slice geometry, see split_config).
 mhc_status choose_route(int32_t path, const void* workspace, int32_t dtype, int32_t d,
-                        int64_t tokens, RouteNeeds* rn, Route* r, bool* plain) {
+                        int64_t tokens, RouteNeeds* rn, Route* r, bool* plain,
+                        int32_t iters = 0) {
   path = path_family(path, plain);
   *rn = RouteNeeds{};
   if (path == MHC_PATH_TILE || (path == MHC_PATH_AUTO && workspace == nullptr)) {
@@ -1627,7 +1639,7 @@ mhc_status choose_route(int32_t path, const void* workspace, int32_t dtype, int3
     return MHC_OK;
   }
   if (path == MHC_PATH_AUTO || path == MHC_PATH_SPLIT || path == MHC_PATH_CHUNK) {
-    const mhc_status s = route_needs(dtype, d, tokens, rn);
+    const mhc_status s = route_needs(dtype, d, tokens, rn, iters == 1);
     if (s != MHC_OK) return s;
   }
   const bool lower = *plain && rn->split_bytes > 0;   // only where the split kernel runs
@@ -2177,7 +2189,8 @@ mhc_status mhc_fused_step(const void* x, const void* f, int32_t dtype, int64_t t
   RouteNeeds rn;
   Route route;
   bool plain = false;
-  if ((s = choose_route(path, workspace, dtype, d, tokens, &rn, &route, &plain)) != MHC_OK)
+  if ((s = choose_route(path, workspace, dtype, d, tokens, &rn, &route, &plain,
+                        sinkhorn_iters)) != MHC_OK)
     return s;
   if (route != Route::kTile) {
     const int64_t need = route == Route::kSplit ? rn.split_bytes : rn.chunk_bytes;
@@ -2211,7 +2224,9 @@ mhc_status mhc_fused_step_noalloc(const void* x, const void* f, int32_t dtype, i
     RouteNeeds rn;
     Route r;
     static const char kDummy = 0;   // stands for a workspace; never dereferenced
-    if ((s = choose_route(path, &kDummy, dtype, d, tokens, &rn, &r, &plain)) != MHC_OK) return s;
+    if ((s = choose_route(path, &kDummy, dtype, d, tokens, &rn, &r, &plain, sinkhorn_iters)) !=
+        MHC_OK)
+      return s;
     const int64_t need =
         r == Route::kSplit ? rn.split_bytes : (r == Route::kChunk ? rn.chunk_bytes : 0);
     if (need > kScratchBytes)
@@ -2251,7 +2266,8 @@ mhc_status mhc_mixes(const void* x, int32_t dtype, int64_t tokens, int32_t d,
   RouteNeeds rn;
   Route route;
   bool plain = false;
-  if ((s = choose_route(path, workspace, dtype, d, tokens, &rn, &route, &plain)) != MHC_OK)
+  if ((s = choose_route(path, workspace, dtype, d, tokens, &rn, &route, &plain,
+                        sinkhorn_iters)) != MHC_OK)
     return s;
   if (route != Route::kTile) {
     const int64_t need = route == Route::kSplit ? rn.split_bytes : rn.chunk_bytes;
