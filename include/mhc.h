@@ -163,7 +163,9 @@ mhc_status mhc_pack_wmix(const float* w_mix, int32_t d, int32_t dtype, void* w_p
  *   - Chunked kernels: at most 8192 tokens; MHC_BF16 streams with d a
  *     multiple of 64 up to 5120, or MHC_F32 streams. The 16,384-byte header
  *     plus 128 bytes per token and chunk, a chunk being 512 features (bf16)
- *     or 256 (f32): 1,280 or 2,560 bytes per token at d = 5120.
+ *     or 256 (f32): 1,280 or 2,560 bytes per token at d = 5120. On bf16
+ *     streams they take the hi + mid terms of the packed projection when
+ *     sinkhorn_iters >= 2 and all three for a single round.
  */
 int64_t mhc_fused_step_workspace_bytes(int64_t tokens, int32_t d, int32_t dtype);
 

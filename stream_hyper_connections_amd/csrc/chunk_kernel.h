@@ -19,7 +19,8 @@
 //     pipelined tile kernel's steps on them (wave w takes the pairs w, w + 8,
 //     ... of the chunk; W read from L2), store the new streams, store h into
 //     y_out (normalised in place later), and write one partial row of 32 floats
-//     per token: the 24 projection sums of the chunk (hi + mid + lo terms),
+//     per token: the 24 projection sums of the chunk (the hi + mid + lo terms
+//     of W, or hi + mid from two Sinkhorn rounds on, as in the tile kernel),
 //     sum x'^2 and sum h^2.
 //   * chunk_finish_kernel: one workgroup per token sums the token's partial
 //     rows over the chunks (in chunk order), forms the mixes
@@ -70,10 +71,10 @@ __device__ __forceinline__ ChunkItem chunk_item(int64_t ntiles, int nchunks) {
 // sn) loaded only when there is one (`more`, uniform across the wave: with
 // one pair per wave, as at d = 5120, a reload would only delay the in-order
 // wait on step B's operands).
-template <int MODE>
+template <int MODE, int T>
 __device__ __forceinline__ void chunk_pair(int sa, int sn, bool more, Ctx& c, Half& ha,
                                            Half& hb) {
-  u32x4 w[4][kTiles];
+  u32x4 w[4][T];
   u32x4 xa[4], xb[4];
 
   load_w(w, c, sa);
@@ -106,10 +107,12 @@ __device__ __forceinline__ void chunk_pair(int sa, int sn, bool more, Ctx& c, Ha
 }
 
 // Grid: ceil(tokens / 16) * nchunks workgroups of kThreads; nchunks * cpairs
-// covers the d / 64 pairs of the row.
-template <int MODE>
+// covers the d / 64 pairs of the row. T: the packed column tiles read (all
+// three terms of W, or hi + mid; see used_cols).
+template <int MODE, int T>
 __global__ __launch_bounds__(kThreads) void chunk_kernel(StepArgs a, int nchunks, int cpairs,
                                                          char* __restrict__ ws) {
+  constexpr int kC = used_cols(T);
   __shared__ float acc_s[kWaves][kTok][kCols];
   __shared__ float ss_s[kWaves][kTok];
   __shared__ float hs_s[kWaves][kTok];
@@ -136,7 +139,7 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(StepArgs a, int nchunks
   c.d2 = d * 2;
   c.wr = make_rsrc(a.wpk, (uint32_t)nsteps * kStreams * kTiles * 1024);
   c.woff = (uint32_t)lane * 16;
-  c.woff_last = (tr < kCols - 16 * (kTiles - 1)) ? (uint32_t)lane * 16 : kOutOfRange;
+  c.woff_last = (tr < kC - 16 * (T - 1)) ? (uint32_t)lane * 16 : kOutOfRange;
   c.xr = make_rsrc(static_cast<const char*>(a.x) + t0 * rowx, ntok * rowx);
   c.xoff = (uint32_t)tr * rowx + (uint32_t)g * 16;
   c.foff = (uint32_t)tr * rowf + (uint32_t)g * 16;
@@ -160,7 +163,7 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(StepArgs a, int nchunks
     }
   }
 #pragma unroll
-  for (int q = 0; q < kTiles; ++q) c.acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int q = 0; q < T; ++q) c.acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
   c.ss = 0.f;
   c.hs = 0.f;
 
@@ -171,7 +174,7 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(StepArgs a, int nchunks
   }
   for (int p = 0; p < cnt; ++p) {
     const int sa = 2 * (pair0 + wave + kWaves * p);
-    chunk_pair<MODE>(sa, sa + 2 * kWaves, p + 1 < cnt, c, ha, hb);
+    chunk_pair<MODE, T>(sa, sa + 2 * kWaves, p + 1 < cnt, c, ha, hb);
   }
 
   // sums of squares over the four lane groups, then the waves' partials to LDS
@@ -185,9 +188,9 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(StepArgs a, int nchunks
     hs_s[wave][tr] = hs;
   }
 #pragma unroll
-  for (int q = 0; q < kTiles; ++q) {
+  for (int q = 0; q < T; ++q) {
     const int col = 16 * q + tr;
-    if (col < kCols) {
+    if (col < kC) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc_s[wave][4 * g + r][col] = c.acc[q][r];
     }
@@ -203,9 +206,9 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(StepArgs a, int nchunks
     for (int w = 0; w < kWaves; ++w) {
       hi += acc_s[w][tt][j];
       mid += acc_s[w][tt][kMix + j];
-      lo += acc_s[w][tt][2 * kMix + j];
+      if constexpr (T == kTiles) lo += acc_s[w][tt][2 * kMix + j];
     }
-    v = (hi + mid) + lo;
+    v = T == kTiles ? (hi + mid) + lo : hi + mid;
   } else if (j == kMix || j == kMix + 1) {
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) v += j == kMix ? ss_s[w][tt] : hs_s[w][tt];

@@ -698,7 +698,14 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kMaxSteps = 160;              // d <= 5120
 constexpr int kSlots = kMaxSteps - kWaves;  // LDS slots for h
 constexpr int kCols = 3 * kMix;             // real packed columns (hi/mid/lo x 24)
-constexpr int kTiles = kTilesBf;
+constexpr int kTiles = kTilesBf;            // column tiles per (step, stream) in the packing
+// Tiles a chunked-kernel instance reads (the tile kernel reads all five):
+// all of them (three terms, hi + mid + lo = w exactly) or the first three
+// (hi + mid, |w - hi - mid| <= 2^-16 |w|, 40% fewer operand bytes from L2
+// and MFMAs). Calls with a single Sinkhorn round take three terms: the comb's
+// row sums are then not normalised and would carry the two-term error.
+constexpr int kTilesHiMid = 3;
+constexpr int used_cols(int T) { return T == kTiles ? 3 * kMix : 2 * kMix; }
 constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw buffer, 32-bit data format (gfx9)
 constexpr int kNT = 2;                         // cache-policy bit: non-temporal
 constexpr uint32_t kOutOfRange = 0x80000000u;
@@ -780,13 +787,14 @@ __device__ __forceinline__ void load_half(Half& hf, const Ctx& c, int s) {
   hf.f = MODE == kFused ? bload<kNT>(c.fr, c.foff, col) : u32x4{0, 0, 0, 0};
 }
 
-__device__ __forceinline__ void load_w(u32x4 (&w)[4][kTiles], const Ctx& c, int s) {
+template <int T>
+__device__ __forceinline__ void load_w(u32x4 (&w)[4][T], const Ctx& c, int s) {
   const uint32_t base = (uint32_t)s * (kStreams * kTiles * 1024);
 #pragma unroll
   for (int k = 0; k < 4; ++k)
 #pragma unroll
-    for (int q = 0; q < kTiles; ++q)
-      w[k][q] = bload<0>(c.wr, q == kTiles - 1 ? c.woff_last : c.woff,
+    for (int q = 0; q < T; ++q)
+      w[k][q] = bload<0>(c.wr, q == T - 1 ? c.woff_last : c.woff,
                          base + (uint32_t)(k * kTiles + q) * 1024);
 }
 
@@ -865,13 +873,14 @@ __device__ __forceinline__ void valu_step(const Half& in, u32x4 (&xo)[4], Ctx& c
   }
 }
 
-__device__ __forceinline__ void mfma_step(const u32x4 (&xo)[4], const u32x4 (&w)[4][kTiles],
+template <int T>
+__device__ __forceinline__ void mfma_step(const u32x4 (&xo)[4], const u32x4 (&w)[4][T],
                                           Ctx& c) {
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const bf16x8 A = __builtin_bit_cast(bf16x8, xo[k]);
 #pragma unroll
-    for (int q = 0; q < kTiles; ++q)
+    for (int q = 0; q < T; ++q)
       c.acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8, w[k][q]),
                                                          c.acc[q], 0, 0, 0);
   }
@@ -880,13 +889,13 @@ __device__ __forceinline__ void mfma_step(const u32x4 (&xo)[4], const u32x4 (&w)
 // One pair of steps (A = 2P, B = 2P + 1), prefetching the next pair's streams
 // when the wave has one in this tile (the branch is uniform across the wave;
 // the next tile's first pair is loaded by the tile set-up).
-template <int MODE>
+template <int MODE, int T>
 __device__ __forceinline__ void pair_body(int p, int cnt, int wave, Ctx& c, Smem& sm, int lane,
                                           Half& ha, Half& hb) {
   const int sa = 2 * (wave + kWaves * p);
   const bool more = p + 1 < cnt;
   const int sn = sa + 2 * kWaves;   // the next pair
-  u32x4 w[4][kTiles];
+  u32x4 w[4][T];
   u32x4 xa[4], xb[4];
 
   load_w(w, c, sa);
@@ -918,6 +927,7 @@ __device__ __forceinline__ void pair_body(int p, int cnt, int wave, Ctx& c, Smem
 
 template <int MODE>
 __global__ __launch_bounds__(kThreads) void fused_bf16_kernel(StepArgs a, int ntiles) {
+  constexpr int T = kTiles;   // all three terms of W
   __shared__ Smem sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -933,7 +943,7 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_kernel(StepArgs a, int nt
   c.d2 = d * 2;
   c.wr = make_rsrc(a.wpk, (uint32_t)nsteps * kStreams * kTiles * 1024);
   c.woff = (uint32_t)lane * 16;
-  c.woff_last = (tr < kCols - 16 * (kTiles - 1)) ? (uint32_t)lane * 16 : kOutOfRange;
+  c.woff_last = (tr < kCols - 16 * (T - 1)) ? (uint32_t)lane * 16 : kOutOfRange;
 
   Half ha, hb;
 
@@ -977,20 +987,20 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_kernel(StepArgs a, int nt
     const int64_t t0 = (int64_t)tile * kTok;
     const int ntok = (int)min((int64_t)kTok, a.tokens - t0);
 #pragma unroll
-    for (int q = 0; q < kTiles; ++q) c.acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < T; ++q) c.acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
     c.ss = 0.f;
     c.hs = 0.f;
     c.hlast[0] = c.hlast[1] = u32x4{0, 0, 0, 0};
 
-    for (int p = 0; p < cnt; ++p) pair_body<MODE>(p, cnt, wave, c, sm, lane, ha, hb);
+    for (int p = 0; p < cnt; ++p) pair_body<MODE, T>(p, cnt, wave, c, sm, lane, ha, hb);
 
     // keep what the tail needs; start the next tile's loads so they fly while
     // this tile's y, reductions and Sinkhorn run
     const rsrc_t yr = c.yr;
     const float hsum_part = c.hs, ssum_part = c.ss;
-    f32x4 acc[kTiles];
+    f32x4 acc[T];
 #pragma unroll
-    for (int q = 0; q < kTiles; ++q) acc[q] = c.acc[q];
+    for (int q = 0; q < T; ++q) acc[q] = c.acc[q];
     const u32x4 hlast0 = c.hlast[0], hlast1 = c.hlast[1];
     const uint32_t foff = c.foff;
     if (tile + (int)gridDim.x < ntiles) setup(tile + gridDim.x);
@@ -1028,7 +1038,7 @@ __global__ __launch_bounds__(kThreads) void fused_bf16_kernel(StepArgs a, int nt
 
     // ---- projection partials across waves ----
 #pragma unroll
-    for (int q = 0; q < kTiles; ++q) {
+    for (int q = 0; q < T; ++q) {
       const int col = 16 * q + tr;
       if (col < kCols) {
 #pragma unroll
@@ -1539,12 +1549,21 @@ mhc_status launch_chunk(const StepArgs& a, void* ws, const ChunkCfg& cc, int mod
   const dim3 blk(pipe::kThreads), tok((unsigned)a.tokens);
   char* w = static_cast<char*>(ws);
   const bool bf = cc.dtype == MHC_BF16, full = mode == kFused;
-  if (bf && full)
-    hipLaunchKernelGGL(pipe::chunk_kernel<kFused>, dim3(grid), blk, 0, stream, a, cc.nchunks,
-                       cc.per, w);
+  // three projection terms for a single Sinkhorn round, else hi + mid (pipe::used_cols)
+  const bool exact = a.iters == 1;
+  constexpr int T3 = pipe::kTiles, T2 = pipe::kTilesHiMid;
+  if (bf && full && exact)
+    hipLaunchKernelGGL((pipe::chunk_kernel<kFused, T3>), dim3(grid), blk, 0, stream, a,
+                       cc.nchunks, cc.per, w);
+  else if (bf && full)
+    hipLaunchKernelGGL((pipe::chunk_kernel<kFused, T2>), dim3(grid), blk, 0, stream, a,
+                       cc.nchunks, cc.per, w);
+  else if (bf && exact)
+    hipLaunchKernelGGL((pipe::chunk_kernel<kMixesOnly, T3>), dim3(grid), blk, 0, stream, a,
+                       cc.nchunks, cc.per, w);
   else if (bf)
-    hipLaunchKernelGGL(pipe::chunk_kernel<kMixesOnly>, dim3(grid), blk, 0, stream, a, cc.nchunks,
-                       cc.per, w);
+    hipLaunchKernelGGL((pipe::chunk_kernel<kMixesOnly, T2>), dim3(grid), blk, 0, stream, a,
+                       cc.nchunks, cc.per, w);
   else if (full)
     hipLaunchKernelGGL(pipe::chunk_f32_kernel<kFused>, dim3(grid), blk, 0, stream, a, cc.nchunks,
                        cc.per, w);

@@ -17,7 +17,7 @@ import torch
 import stream_hyper_connections_amd as mhc
 from stream_hyper_connections_amd import workloads as wl
 from tests.cases import make_case, run_step, to_dev
-from tests.parity import check_mixes, check_step
+from tests.parity import check_mix_like, check_mixes, check_step
 
 pytestmark = pytest.mark.gpu
 
@@ -138,8 +138,10 @@ def test_chunk_matches_tile_kernel():
     ya, yb = a["y"].float(), b["y"].float()
     ulp = torch.maximum(ya.abs(), yb.abs()) * 2.0 ** -7 + 1e-30
     assert ((ya - yb).abs() <= ulp).all()
+    # the chunked kernels take the hi + mid terms of W (20 Sinkhorn rounds
+    # here), the tile kernel all three: the mixes agree at the parity bar
     for k in ("pre", "post", "comb", "mix"):
-        np.testing.assert_allclose(a[k].numpy(), b[k].numpy(), rtol=0, atol=2e-5)
+        check_mix_like(k, a[k], b[k])
 
 
 def test_chunk_in_place_and_deterministic():
@@ -239,8 +241,11 @@ def test_mixes_chunk_mode_parity(dtype, d, t):
     check_mixes(dict(x=x, **p), {k: v.cpu() for k, v in out.items()}, dtype)
     tile = mhc.mixes(dx, wp, to_dev(p["base"]), to_dev(p["scale"]), want_mix=True, path="tile")
     for k in ("pre", "post", "comb", "mix"):
-        np.testing.assert_allclose(out[k].cpu().numpy(), tile[k].cpu().numpy(), rtol=0,
-                                   atol=2e-5)
+        if dtype == "bf16":   # two terms of W against three: at the parity bar
+            check_mix_like(k, out[k].cpu(), tile[k].cpu())
+        else:                 # the same f32 arithmetic in another order
+            np.testing.assert_allclose(out[k].cpu().numpy(), tile[k].cpu().numpy(), rtol=0,
+                                       atol=2e-5)
 
 
 @pytest.mark.parametrize("path", ["chunk", "split"])

@@ -93,11 +93,16 @@ def test_iteration_sweep_on_workload_logits():
                      f"{np.abs(got.sum(axis=1) - 1).max():.3e}")
 
 
+# the chunked route takes the hi + mid terms of W from two rounds on and all
+# three for a single round; the split route's narrow slices take all three
+@pytest.mark.parametrize("path", ["split", "chunk"])
 @pytest.mark.parametrize("iters", [1, 5, 50])
-def test_fused_step_other_iteration_counts(iters):
+def test_fused_step_other_iteration_counts(iters, path):
     w = wl.Workload(910 + iters, "sk_iters", 700, 5120, "bf16", iters=iters)
     case = make_case(w)
-    out, _ = run_step(case, path="split")
+    ws = mhc.new_workspace(mhc.fused_step_workspace_bytes(700, 5120, "bf16"))
+    out, _ = run_step(case, path=path, workspace=ws)
+    assert mhc.split_status(ws) == 0
     check_step(case, out, "bf16")
 
 
