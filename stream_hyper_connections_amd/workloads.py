@@ -19,7 +19,8 @@ id    name               tokens      dtype   notes
 4     chain              8192 x 80   bf16    80 sublayer steps, fresh params per step
 ====  =================  ==========  ======  =========================================
 
-Other stream counts n (2 or 8) use the same recipe with n streams and
+Id 5 is a test case past 4 GiB of streams (131,072 tokens, bf16), drawn the
+same way. Other stream counts n (2 or 8) use the same recipe with n streams and
 (2+n)*n mixes; at n = 4 the draws are those of the table above.
 
 Distributions: streams X and sublayer output F ~ N(0, 1); W_mix [(2+n)n, nd]

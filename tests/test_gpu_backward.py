@@ -46,6 +46,39 @@ def _check(what, got, want, mag, dtype=None):
     return float((extra / (mag + 1e-30)).max())
 
 
+def check_token_grads(case, got, up, xprime, iters, dtype):
+    """The per-token gradients (d_x, d_f, d_comb_in, d_post_in, d_pre_in) of
+    the tokens of ``case`` against the float64 backward oracle evaluated on
+    the validated new streams ``xprime``; ``up``: the upstream gradients of
+    those tokens (numpy). Returns the oracle's outputs and the share of each
+    tolerance used."""
+    xs, f = _np(case["x"]), _np(case["f"])
+    t, n, d = xs.shape
+    pre = np.asarray(case["pre"], np.float64)
+    post = np.asarray(case["post"], np.float64)
+    comb = np.asarray(case["comb"], np.float64)
+    want = oracle.fused_step_backward(xs, f, pre, post, comb, case["w_mix"], case["base"],
+                                      case["scale"], case["gamma"], up["d_xprime"], up["d_y"],
+                                      up["d_pre"], up["d_post"], up["d_comb"], iters,
+                                      case["norm_eps"], case["hc_eps"], dtype, xprime=xprime)
+    # magnitudes of the terms forming each gradient
+    xp, dh = want["xprime"], want["dh"]
+    mag_da = (np.abs(up["d_xprime"]) + np.abs(want["dx_mix"]).reshape(t, n, d)
+              + np.abs(pre)[:, :, None] * np.abs(dh)[:, None, :])
+    used = {}
+    used["d_x"] = _check("d_x", got["d_x"], want["d_x"],
+                         np.einsum("tjk,tkf->tjf", np.abs(comb), mag_da), dtype)
+    used["d_f"] = _check("d_f", got["d_f"], want["d_f"],
+                         np.einsum("tk,tkf->tf", np.abs(post), mag_da), dtype)
+    used["d_comb_in"] = _check("d_comb_in", got["d_comb_in"], want["d_comb_in"],
+           np.einsum("tjf,tkf->tjk", np.abs(xs), mag_da))
+    used["d_post_in"] = _check("d_post_in", got["d_post_in"], want["d_post_in"],
+           np.einsum("tf,tkf->tk", np.abs(f), mag_da))
+    used["d_pre_in"] = _check("d_pre_in", got["d_pre_in"], want["d_pre_in"],
+           np.einsum("tf,tkf->tk", np.abs(dh), np.abs(xp)))
+    return want, used
+
+
 def run_backward_case(n, dtype, d, t, seed, iters=20):
     case = make_case(wl.Workload(seed, "backward", t, d, dtype, n=n, iters=iters))
     rng = np.random.default_rng(seed + 1)
@@ -74,30 +107,8 @@ def run_backward_case(n, dtype, d, t, seed, iters=20):
                                     case["norm_eps"], case["hc_eps"])
     torch.cuda.synchronize()
     got = {k: v.cpu() for k, v in got.items()}
-    xs, f = _np(case["x"]), _np(case["f"])
-    pre = np.asarray(case["pre"], np.float64)
-    post = np.asarray(case["post"], np.float64)
-    comb = np.asarray(case["comb"], np.float64)
-    want = oracle.fused_step_backward(xs, f, pre, post, comb, case["w_mix"], case["base"],
-                                      case["scale"], case["gamma"], up["d_xprime"], up["d_y"],
-                                      up["d_pre"], up["d_post"], up["d_comb"], iters,
-                                      case["norm_eps"], case["hc_eps"], dtype,
-                                      xprime=o["xprime"])
-    # magnitudes of the terms forming each gradient
-    xp, h, dh = want["xprime"], want["h"], want["dh"]
-    mag_da = (np.abs(up["d_xprime"]) + np.abs(want["dx_mix"]).reshape(t, n, d)
-              + np.abs(pre)[:, :, None] * np.abs(dh)[:, None, :])
-    used = {}
-    used["d_x"] = _check("d_x", got["d_x"], want["d_x"],
-                         np.einsum("tjk,tkf->tjf", np.abs(comb), mag_da), dtype)
-    used["d_f"] = _check("d_f", got["d_f"], want["d_f"],
-                         np.einsum("tk,tkf->tf", np.abs(post), mag_da), dtype)
-    used["d_comb_in"] = _check("d_comb_in", got["d_comb_in"], want["d_comb_in"],
-           np.einsum("tjf,tkf->tjk", np.abs(xs), mag_da))
-    used["d_post_in"] = _check("d_post_in", got["d_post_in"], want["d_post_in"],
-           np.einsum("tf,tkf->tk", np.abs(f), mag_da))
-    used["d_pre_in"] = _check("d_pre_in", got["d_pre_in"], want["d_pre_in"],
-           np.einsum("tf,tkf->tk", np.abs(dh), np.abs(xp)))
+    want, used = check_token_grads(case, got, up, o["xprime"], iters, dtype)
+    xp, h = want["xprime"], want["h"]
     s_slot = np.concatenate([np.full(n, case["scale"][0]), np.full(n, case["scale"][1]),
                              np.full(n * n, case["scale"][2])]).astype(np.float64)
     dz = np.abs(want["g"] * s_slot * want["r"][:, None])
