@@ -12,7 +12,9 @@ path "auto" takes at that size (the feature-split kernel and its tail):
   batch boundary, so every token keeps its place in its batch): every output
   of those tokens equal bit for bit;
 * the comb column sums of every token;
-* hc_mixes on the input streams at the same size, sampled against the oracle.
+* hc_mixes on the input streams at the same size, sampled against the oracle;
+* the general-n entry point at n = 4 on the same inputs, sampled against the
+  oracle.
 
 Inputs: streams and sublayer output drawn as every workload's (id 5 of the
 seed tree), the prior coefficients from the oracle's mixes of the first 1,024
@@ -132,6 +134,18 @@ def test_step_beyond_4gib(big):
                 {k: v.index_select(0, didx).cpu() for k, v in mx.items()}, "bf16")
     _log(f"beyond_4gib: hc_mixes on the input streams matches the oracle on the "
          f"{len(idx)} sampled tokens ({time.time() - t_start:.1f}s)")
+    del mx
+
+    # the general-n entry point at n = 4 (its own feature-split kernel)
+    route = mhc.fused_step_route_n(4, "auto", t, d, "bf16")
+    wpn = mhc.pack_wmix_n(to_dev(p["w_mix"]), "bf16")
+    on = mhc.fused_step_n(x, f, pre, post, comb, wpn, base, scale, gamma, w.iters, w.norm_eps,
+                          w.hc_eps, check_status=True)
+    torch.cuda.synchronize()
+    check_step(_sampled_case(big, p), {k: v.index_select(0, didx).cpu() for k, v in on.items()},
+               "bf16")
+    _log(f"beyond_4gib: fused_step_n (n = 4, route {route}) matches the oracle on the "
+         f"{len(idx)} sampled tokens")
 
 
 @pytest.mark.timeout(900)
