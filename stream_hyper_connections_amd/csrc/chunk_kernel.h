@@ -19,9 +19,9 @@
 //     pipelined tile kernel's steps on them (wave w takes the pairs w, w + 8,
 //     ... of the chunk; W read from L2), store the new streams, store h into
 //     y_out (normalised in place later), and write one partial row of 32 floats
-//     per token: the 24 projection sums of the chunk (the hi + mid + lo terms
-//     of W, or hi + mid from two Sinkhorn rounds on, as in the tile kernel),
-//     sum x'^2 and sum h^2.
+//     per token: the 24 projection sums of the chunk (from the hi + mid + lo
+//     terms of W for a single Sinkhorn round, as the tile kernel always does,
+//     and from hi + mid from two rounds on), sum x'^2 and sum h^2.
 //   * chunk_finish_kernel: one workgroup per token sums the token's partial
 //     rows over the chunks (in chunk order), forms the mixes
 //     (r * projection, [SW] Code, hc_mixes), runs the split and the Sinkhorn on
