@@ -325,8 +325,20 @@ __global__ __launch_bounds__(256) void chunk_finish_kernel(StepArgs a, int nchun
   const int lane = tid & 63;
   const float* part = reinterpret_cast<const float*>(ws + kChunkHeader);
   float v = 0.f;   // lane j < 32: column j of the token's partial rows, summed
-  if (lane < kPart)
-    for (int ch = 0; ch < nchunks; ++ch) v += part[((int64_t)ch * a.tokens + t) * kPart + lane];
+  if (lane < kPart) {
+    // in chunk order, eight loads in flight at a time (one at a time, each
+    // waited for before the next, the loop cost a full memory latency per chunk)
+    const float* p = part + t * kPart + lane;
+    const int64_t stride = a.tokens * kPart;
+    for (int ch = 0; ch < nchunks; ch += 8) {
+      float x[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = ch + i < nchunks ? p[(ch + i) * stride] : 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (ch + i < nchunks) v += x[i];
+    }
+  }
   const float ssum = __shfl(v, kMix);
   const float hsum = __shfl(v, kMix + 1);
   if (tid < 64) {
