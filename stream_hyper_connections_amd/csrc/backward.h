@@ -1251,15 +1251,15 @@ __global__ __launch_bounds__(256) void gamma_reduce_kernel(Args a) {
   const float* pg = a.ws + wsl.pg_off();
   float s = 0.f;
   if (f < d) {
-    for (int64_t w0 = slice; w0 < groups; w0 += 32) {
-      float v[8];
+    for (int64_t w0 = slice; w0 < groups; w0 += 128) {
+      float v[32];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < 32; ++u) {
         const int64_t w = w0 + 4 * u;
         v[u] = w < groups ? pg[w * d + f] : 0.f;
       }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) s += v[u];
+      for (int u = 0; u < 32; ++u) s += v[u];
     }
   }
   part[slice][lane] = s;
@@ -1284,10 +1284,22 @@ __global__ __launch_bounds__(256) void slot_kernel(Args a) {
   const int i = threadIdx.x % kMix, r = threadIdx.x / kMix;
   float s1 = 0.f, s2 = 0.f;
   if (r < kRows) {
-    for (int64_t t = t0 + r; t < t1; t += kRows) {
-      const float gv = g[t * kMix + i];
-      s1 += gv;
-      s2 = fmaf(gv, a.mix[t * kMix + i], s2);
+    // eight rows in flight, added in row order
+    for (int64_t tb = t0 + r; tb < t1; tb += 8 * kRows) {
+      float gv[8], mv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t t = tb + (int64_t)u * kRows;
+        gv[u] = t < t1 ? g[t * kMix + i] : 0.f;
+        mv[u] = t < t1 ? a.mix[t * kMix + i] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (tb + (int64_t)u * kRows < t1) {
+          s1 += gv[u];
+          s2 = fmaf(gv[u], mv[u], s2);
+        }
+      }
     }
   }
   sg[threadIdx.x] = s1;
@@ -1316,9 +1328,19 @@ __global__ __launch_bounds__(64) void scale_kernel(Args a) {
   const int i = threadIdx.x;
   if (i < kMix) {
     float s1 = 0.f, s2 = 0.f;
-    for (int c = 0; c < kSlotChunks; ++c) {
-      s1 += e[(int64_t)c * 2 * kMix + i];
-      s2 += e[(int64_t)c * 2 * kMix + kMix + i];
+    static_assert(kSlotChunks % 64 == 0, "whole batches of chunks");
+    for (int c0 = 0; c0 < kSlotChunks; c0 += 64) {   // 64 chunks in flight, added in order
+      float v1[64], v2[64];
+#pragma unroll
+      for (int c = 0; c < 64; ++c) {
+        v1[c] = e[(int64_t)(c0 + c) * 2 * kMix + i];
+        v2[c] = e[(int64_t)(c0 + c) * 2 * kMix + kMix + i];
+      }
+#pragma unroll
+      for (int c = 0; c < 64; ++c) {
+        s1 += v1[c];
+        s2 += v2[c];
+      }
     }
     a.d_base[i] = s1;
     em[i] = s2;
